@@ -1,0 +1,376 @@
+"""CPU oracle for the DFlash drafter block pass -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, float64 NumPy.  Only the tests, the smoke check and the benchmark's
+cpu_baseline leg may import this module; the library never does, and this module
+imports nothing from the library.
+
+What it computes, and where the pages say so:
+
+* KV injection -- "Z Lab releases DFlash 2 for Qwen 3.8 27B" (llms.blog), section
+  "Persistent Conditioning Through Target KV Injection": tapped target hidden states
+  are concatenated, RMS-normalised, projected to the drafter width, and pushed
+  through every draft layer's own K and V projections into that layer's KV cache.
+  "Architecture" (kb.ekarisky.com, DFlash 2), Component Breakdown row "KV injection
+  path" and "Internals Worth Knowing": projection ahead of the draft pass, with norm
+  and RoPE applied to the projected keys.
+* Single-pass block draft -- "Architecture", Component Breakdown rows "DFlash drafter
+  backbone" (5 layers, sliding window 1024) and "Block attention mask" (slot 0 holds
+  the anchor, slots 1..K-1 start as MASK, attention non-causal inside the block).
+* Two-tap dynamic convolution -- "Architecture", section "Problem 2 -- Suffix decay
+  is local": Conv(x)_t = k_t0 * x_t + k_t1 * x_{t-1}, around every attention and MLP
+  sublayer, the first position reading the last verified token.
+* Shared lm_head and top-16 candidates -- "Architecture", flowchart "Drafter" and the
+  sequence diagram "One Cycle, Step by Step".
+* Path selector -- "Architecture", section "Problem 1 -- Independent picks are
+  incoherent": S_t(a, b) = U_t(b) + < A(a) * H(h_t), B(b) >.
+* Greedy verification -- "Architecture", section "Speculative Decoding Context" and the
+  sequence diagram: accept the longest valid prefix plus one bonus token.
+
+Readings taken where the pages are silent (each also listed in the design notes):
+RMSNorm over the whole concatenation then the fc projection, no bias; K/V of the
+context are W_k c and W_v c with no extra input norm; per-head RMSNorm on q and k
+then rotate-half RoPE (theta 10000) at absolute positions; context token j sits at
+position j, the anchor at L (the current length), slot t at L+t; every block query
+sees the last min(L, W) injected positions plus all K block slots; conv taps are
+per-position scalars k_t = sigmoid(W_c x_t + b_c) (the 2048 -> 2 sigmoid-gated form),
+slot 0 reads a zero predecessor; H(h) = sigmoid(W_H h) with h the final-normed
+hidden at the candidate's slot; A and B are [V][r] tables; logits only for slots
+1..K-1; top-16 ordered by (logit descending, id ascending).
+
+Rounding points ("mode"):
+  "exact"  -- everything float64.
+  "bf16"   -- the values a bf16 pipeline stores are rounded to bf16 (nearest, ties to
+              even): the normalised concatenation, the fc output, cached K/V, the
+              pre-projection conv outputs, q/k/v after norm+RoPE, the attention output,
+              the SwiGLU product and the final-normed hidden.  The residual stream,
+              accumulations, conv taps, softmax, logits and selector stay float64.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+
+F64 = np.float64
+
+
+# --------------------------------------------------------------------------------------
+# numeric helpers
+# --------------------------------------------------------------------------------------
+
+def bf16_round(x) -> np.ndarray:
+    """Nearest bfloat16 value (8 exponent bits, 7 stored mantissa bits), ties to even.
+
+    Works on the float64 bit pattern: drop the low 45 of the 52 mantissa bits with
+    round-to-nearest-even.  Valid for magnitudes in bf16's normal range, which is all
+    this oracle produces."""
+    x = np.ascontiguousarray(x, dtype=F64)
+    b = x.view(np.uint64)
+    drop = np.uint64(45)
+    half_minus_one = np.uint64((1 << 44) - 1)
+    lsb = (b >> drop) & np.uint64(1)
+    r = (b + half_minus_one + lsb) & ~np.uint64((1 << 45) - 1)
+    return r.view(F64)
+
+
+def _rounder(mode: str):
+    if mode == "bf16":
+        return bf16_round
+    if mode == "exact":
+        return lambda v: np.asarray(v, dtype=F64)
+    raise ValueError(mode)
+
+
+def as64(a) -> np.ndarray:
+    return np.asarray(a, dtype=F64)
+
+
+def rms_norm(x, gain, eps):
+    """RMSNorm: x / sqrt(mean(x^2) + eps) * gain over the last axis."""
+    x = as64(x)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * as64(gain)
+
+
+def sigmoid(x):
+    x = as64(x)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def silu(x):
+    x = as64(x)
+    return x * sigmoid(x)
+
+
+def rope(x, pos, theta):
+    """Rotate-half rotary embedding on the last axis (size d_h) at integer positions `pos`.
+
+    Pair (x_i, x_{i+d_h/2}) is rotated by angle pos * theta^(-2i/d_h)."""
+    x = as64(x)
+    dh = x.shape[-1]
+    half = dh // 2
+    inv = theta ** (-(np.arange(half, dtype=F64) * 2.0) / dh)
+    ang = as64(pos)[..., None] * inv
+    shape = ang.shape[:-1] + (1,) * (x.ndim - ang.ndim) + (half,)
+    ang = ang.reshape(shape)
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def two_tap_conv(x, w, b, use_conv=True):
+    """Conv(x)_t = k_t0 * x_t + k_t1 * x_{t-1} over the rows of one block (x: [K][d]).
+
+    k_t = sigmoid(W_c x_t + b_c) in R^2 (per-position taps from the current row).
+    Slot 0 has no predecessor inside the block: x_{-1} = 0."""
+    x = as64(x)
+    if not use_conv:
+        return x
+    k = sigmoid(x @ as64(w).T + as64(b))          # [K][2]
+    prev = np.zeros_like(x)
+    prev[1:] = x[:-1]
+    return k[:, 0:1] * x + k[:, 1:2] * prev
+
+
+def topk_desc(values, k):
+    """Indices of the k largest values, ordered by (value descending, index ascending)."""
+    values = as64(values)
+    order = np.lexsort((np.arange(values.size), -values))
+    return order[:k]
+
+
+# --------------------------------------------------------------------------------------
+# the drafter's KV cache: by absolute position, no ring
+# --------------------------------------------------------------------------------------
+
+class DraftCache:
+    """K/V of one sequence for every draft layer, keyed by absolute position."""
+
+    def __init__(self, n_layers):
+        self.k = [dict() for _ in range(n_layers)]
+        self.v = [dict() for _ in range(n_layers)]
+        self.length = 0          # anchor position of the next draft = one past the last injected
+
+    def positions(self):
+        return sorted(self.k[0].keys())
+
+
+def inject(cfg, W, cache: DraftCache, positions, states, mode="bf16"):
+    """Project target states of `positions` into every layer's cache.
+
+    u = concat of the tapped states (one row per position); u_bar = RMSNorm(u) * g_in;
+    c = W_fc u_bar; for each layer l: K_l = RoPE_p(RMSNorm_head(W_k^l c) * g_k^l),
+    V_l = W_v^l c.  The cache length becomes max(position) + 1."""
+    R = _rounder(mode)
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1)
+    if positions.size == 0:
+        return
+    u = as64(states).reshape(positions.size, cfg.concat_width)
+    u_bar = R(rms_norm(u, W["concat_norm"], cfg.rms_eps))
+    c = R(u_bar @ as64(W["fc"]).T)
+    nkv, dh = cfg.n_kv_heads, cfg.head_dim
+    for l, lw in enumerate(W["layers"]):
+        k = (c @ as64(lw["wk"]).T).reshape(-1, nkv, dh)
+        k = R(rope(rms_norm(k, lw["k_norm"], cfg.rms_eps), positions[:, None], cfg.rope_theta))
+        v = R((c @ as64(lw["wv"]).T).reshape(-1, nkv, dh))
+        for i, p in enumerate(positions):
+            cache.k[l][int(p)] = k[i]
+            cache.v[l][int(p)] = v[i]
+    cache.length = max(cache.length, int(positions.max()) + 1)
+
+
+def _attention(q, k, v, n_kv):
+    """Softmax attention of every query row over every key row, per head, with GQA.
+
+    q: [K][n_h][d_h]; k, v: [n_keys][n_kv][d_h].  Query head i reads kv head
+    floor(i * n_kv / n_h).  Scale 1/sqrt(d_h).  No mask: every query sees every key."""
+    K, nh, dh = q.shape
+    out = np.empty_like(q)
+    for i in range(nh):
+        j = (i * n_kv) // nh
+        s = q[:, i, :] @ k[:, j, :].T / math.sqrt(dh)     # [K][n_keys]
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, i, :] = p @ v[:, j, :]
+    return out
+
+
+def draft_block(cfg, W, cache: DraftCache, anchor, mode="bf16", block_ids=None, keep_logits=True):
+    """One forward pass over the block [anchor, MASK, ..., MASK] at positions L..L+K-1.
+
+    Returns dict with h_final [K][d], logits [K-1][V] (slots 1..K-1), topk_ids/topk_logits
+    [K-1][topk].  `block_ids` overrides the block's token ids (used by invariant tests)."""
+    R = _rounder(mode)
+    K, d, nh, nkv, dh = cfg.block_size, cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    L = cache.length
+    ids = np.full(K, cfg.mask_id, dtype=np.int64)
+    ids[0] = anchor
+    if block_ids is not None:
+        ids = np.asarray(block_ids, dtype=np.int64)
+    pos = L + np.arange(K)
+    ctx = [p for p in range(max(0, L - cfg.window), L) if p in cache.k[0]]
+    h = as64(W["embed"])[ids]                                   # residual stream [K][d]
+    for l, lw in enumerate(W["layers"]):
+        # attention sublayer
+        z = rms_norm(h, lw["attn_norm"], cfg.rms_eps)
+        y = R(two_tap_conv(z, lw["conv_attn_pre_w"], lw["conv_attn_pre_b"], cfg.use_conv))
+        q = (y @ as64(lw["wq"]).T).reshape(K, nh, dh)
+        k = (y @ as64(lw["wk"]).T).reshape(K, nkv, dh)
+        v = (y @ as64(lw["wv"]).T).reshape(K, nkv, dh)
+        q = R(rope(rms_norm(q, lw["q_norm"], cfg.rms_eps), pos[:, None], cfg.rope_theta))
+        k = R(rope(rms_norm(k, lw["k_norm"], cfg.rms_eps), pos[:, None], cfg.rope_theta))
+        v = R(v)
+        if ctx:
+            keys = np.concatenate([np.stack([cache.k[l][p] for p in ctx]), k])
+            vals = np.concatenate([np.stack([cache.v[l][p] for p in ctx]), v])
+        else:
+            keys, vals = k, v
+        o = R(_attention(q, keys, vals, nkv).reshape(K, nh * dh))
+        a = o @ as64(lw["wo"]).T
+        h = h + two_tap_conv(a, lw["conv_attn_post_w"], lw["conv_attn_post_b"], cfg.use_conv)
+        # feed-forward sublayer
+        z = rms_norm(h, lw["mlp_norm"], cfg.rms_eps)
+        y = R(two_tap_conv(z, lw["conv_mlp_pre_w"], lw["conv_mlp_pre_b"], cfg.use_conv))
+        s = R(silu(y @ as64(lw["w_gate"]).T) * (y @ as64(lw["w_up"]).T))
+        m = s @ as64(lw["w_down"]).T
+        h = h + two_tap_conv(m, lw["conv_mlp_post_w"], lw["conv_mlp_post_b"], cfg.use_conv)
+    h_final = R(rms_norm(h, W["final_norm"], cfg.rms_eps))
+    logits = h_final[1:] @ as64(W["lm_head"]).T                 # [K-1][V]
+    tk = cfg.topk
+    ids_out = np.stack([topk_desc(row, tk) for row in logits]).astype(np.int64)
+    vals_out = np.take_along_axis(logits, ids_out, axis=1)
+    out = dict(h_final=h_final, topk_ids=ids_out, topk_logits=vals_out, residual=h)
+    if keep_logits:
+        out["logits"] = logits
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# path selector
+# --------------------------------------------------------------------------------------
+
+def pair_scores(cfg, W, anchor, topk_ids, topk_logits, h_final):
+    """S_t(a, b) = U_t(b) + sum_j A[a, j] * H_t[j] * B[b, j] for t = 1..K-1.
+
+    H_t = sigmoid(W_H h_t), h_t the final-normed hidden of slot t.  Predecessors of slot 1
+    are just the anchor; of slot t >= 2 the candidates of slot t-1.
+    Returns a list: S[0] has shape [1][k], S[t-1] for t >= 2 has shape [k][k]."""
+    A, B, WH = as64(W["sel_A"]), as64(W["sel_B"]), as64(W["sel_WH"])
+    topk_ids = np.asarray(topk_ids, dtype=np.int64)
+    U = as64(topk_logits)
+    S = []
+    for t in range(1, cfg.block_size):
+        gate = sigmoid(WH @ as64(h_final[t]))
+        prev = np.array([anchor]) if t == 1 else topk_ids[t - 2]
+        pair = (A[prev] * gate) @ B[topk_ids[t - 1]].T
+        S.append(U[t - 1][None, :] + pair)
+    return S
+
+
+def _path_better(s1, p1, s2, p2):
+    """Total order on (score, candidate-index path): higher score first, then the
+    lexicographically smaller index path."""
+    return s1 > s2 or (s1 == s2 and tuple(p1) < tuple(p2))
+
+
+def viterbi_2best(S):
+    """Max-scoring path through the lattice, keeping the two best partial paths per state.
+
+    Returns (best_path_indices, best_score, second_score).  second_score is -inf when the
+    lattice has a single path."""
+    n = len(S)
+    k = S[0].shape[1]
+    # lists[b] = up to two (score, path) entries, best first
+    lists = [[(S[0][0, b], (b,))] for b in range(k)]
+    for t in range(1, n):
+        new = []
+        for b in range(k):
+            cands = []
+            for a in range(k):
+                for sc, path in lists[a]:
+                    cands.append((sc + S[t][a, b], path + (b,)))
+            best = []
+            for c in cands:
+                best.append(c)
+                best.sort(key=lambda e: (-e[0], e[1]))
+                best = best[:2]
+            new.append(best)
+        lists = new
+    final = [e for lst in lists for e in lst]
+    final.sort(key=lambda e: (-e[0], e[1]))
+    second = final[1][0] if len(final) > 1 else -np.inf
+    return list(final[0][1]), final[0][0], second
+
+
+def greedy_walk(S):
+    """Follow the best successor from the anchor; margin = smallest best-minus-second gap."""
+    path, score, margin = [], 0.0, np.inf
+    a = 0
+    for t in range(len(S)):
+        row = S[t][a]
+        order = topk_desc(row, row.size)
+        b = int(order[0])
+        if row.size > 1:
+            margin = min(margin, row[order[0]] - row[order[1]])
+        path.append(b)
+        score += row[b]
+        a = b
+    return path, score, margin
+
+
+def select_path(cfg, W, anchor, topk_ids, topk_logits, h_final, mode="viterbi"):
+    """Returns dict(path_idx, path_ids [K-1], score, margin)."""
+    S = pair_scores(cfg, W, anchor, topk_ids, topk_logits, h_final)
+    if mode == "viterbi":
+        idx, best, second = viterbi_2best(S)
+        margin = best - second
+    elif mode == "greedy":
+        idx, best, margin = greedy_walk(S)
+    else:
+        raise ValueError(mode)
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    path_ids = np.array([ids[t, idx[t]] for t in range(len(idx))], dtype=np.int64)
+    return dict(path_idx=np.array(idx), path_ids=path_ids, score=best, margin=margin)
+
+
+def brute_force_paths(S):
+    """Every path's score, best first (same total order as viterbi_2best).  Tiny lattices only."""
+    k = S[0].shape[1]
+    out = []
+    for path in itertools.product(range(k), repeat=len(S)):
+        sc = S[0][0, path[0]] + sum(S[t][path[t - 1], path[t]] for t in range(1, len(S)))
+        out.append((sc, path))
+    out.sort(key=lambda e: (-e[0], e[1]))
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# verification
+# --------------------------------------------------------------------------------------
+
+def verify_greedy(draft, target):
+    """Greedy longest-prefix verification of one block.
+
+    draft: d_1..d_{K-1}; target: g_0..g_{K-1}, g_i the target's argmax after slot i.
+    n = largest m with d_i == g_{i-1} for all i <= m; tau = n + 1 committed tokens
+    (the accepted drafts plus the bonus g_n).  Returns (n, committed [K] padded with -1,
+    next_anchor = g_n)."""
+    draft = [int(x) for x in draft]
+    target = [int(x) for x in target]
+    K = len(target)
+    n = 0
+    while n < K - 1 and draft[n] == target[n]:
+        n += 1
+    committed = draft[:n] + [target[n]] + [-1] * (K - 1 - n)
+    return n, np.array(committed, dtype=np.int64), target[n]
+
+
+def expected_tau(match_probs):
+    """E[tau] when draft i is accepted with conditional probability r_i given all earlier
+    ones were: 1 + sum_i prod_{j<=i} r_j (the bonus token always counts)."""
+    acc, total = 1.0, 1.0
+    for r in match_probs:
+        acc *= r
+        total += acc
+    return total
