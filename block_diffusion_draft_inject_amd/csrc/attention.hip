@@ -1,0 +1,318 @@
+// Block + sliding-window attention of the drafter ("Architecture", kb.ekarisky.com, Component
+// Breakdown rows "DFlash drafter backbone" and "Block attention mask"): every query slot of a
+// block sees the last min(L - base, window) injected context positions of its sequence (ring
+// slots slot0, slot0+1, ... mod window) and all K slots of its own block -- no causal mask.
+// Softmax is invariant to key order, so ring order does not matter.
+//
+// Grouped-query attention: the G = n_heads / n_kv_heads query heads that share a KV head are
+// processed together, so one workgroup owns R = G * K query rows (row r = g * K + t) and reads
+// each key/value row once.  Keys are split into `chunks` per (sequence, KV head) to fill the
+// chip at small batch; each chunk writes an unnormalised partial output with its running max
+// and sum, and attn_combine merges them (log-sum-exp).
+//
+// bf16 path: Q K^T and P V on v_mfma_f32_16x16x32_bf16 (each wave owns 16 query rows); P is
+// rounded to bf16 for the P V product, the running sums stay fp32.  fp32 path: VALU.
+#include "rowops.h"
+
+namespace dfl {
+
+constexpr int AT_MAXR = 64;   // query rows per workgroup
+constexpr int AT_MAXD = 128;  // head_dim
+
+template <typename T>
+__device__ __forceinline__ float ldt(const void* p, size_t i) {
+  return ldv(reinterpret_cast<const T*>(p), i);
+}
+
+__device__ __forceinline__ bf16x8 bits_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ------------------------------------------------------------------------------ bf16 / MFMA
+constexpr int MK = 64;          // keys per sub-tile
+constexpr int MDH = 128;        // head_dim of the MFMA path
+
+__global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 sk[MK][MDH + 8];
+  __shared__ __attribute__((aligned(16))) bf16 svt[MDH][MK + 8];
+  __shared__ __attribute__((aligned(16))) bf16 sp[4][16][MK + 8];
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, li = lane & 15, kg = lane >> 4;
+  const int K = a.K, G = a.nh / a.nkv, R = G * K;
+  const SeqCtx ctx = a.ctx[b];
+  const int n_keys = ctx.n_ctx + K;
+  const int ck = (n_keys + a.chunks - 1) / a.chunks;
+  const int k_begin = min(c * ck, n_keys), k_end = min(k_begin + ck, n_keys);
+  const size_t pidx = ((size_t)b * a.nkv + kvh) * a.chunks + c;
+  const bf16* q = reinterpret_cast<const bf16*>(a.q);
+  const bf16* kb = reinterpret_cast<const bf16*>(a.kb);
+  const bf16* vb = reinterpret_cast<const bf16*>(a.vb);
+  const bf16* kc = reinterpret_cast<const bf16*>(a.kcache);
+  const bf16* vc = reinterpret_cast<const bf16*>(a.vcache);
+  // this wave's 16 query rows as MFMA A fragments (row = 16w + li, dims ks*32 + kg*8 .. +8)
+  const int qrow = 16 * w + li;
+  u32x4 qa[4];
+  {
+    const int g = qrow / K, t = qrow % K;
+    const bf16* qp = q + ((size_t)(b * K + t) * a.nh + (kvh * G + g)) * MDH;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qa[ks] = (qrow < R) ? *reinterpret_cast<const u32x4*>(qp + ks * 32 + kg * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+  float m[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { m[j] = NEG_INF; l[j] = 0.f; }
+  f32x4 acc[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const size_t cache_base = (((size_t)a.layer * a.max_seqs + ctx.sid) * a.nkv + kvh) * (size_t)a.window;
+  for (int j0 = k_begin; j0 < k_end; j0 += MK) {
+    const int nk = min(MK, k_end - j0);
+    __syncthreads();
+    // K rows -> sk[key][dim]; V rows -> svt[dim][key] (transposed for the P V operand)
+#pragma unroll
+    for (int it = 0; it < (MK * MDH / 8) / 256; ++it) {
+      const int e = tid + it * 256;
+      const int key = e >> 4, part = e & 15;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (key < nk) {
+        const int gk = j0 + key;
+        size_t off;
+        const bf16 *ks, *vs;
+        if (gk < ctx.n_ctx) {
+          const int slot = (ctx.slot0 + gk) % a.window;
+          off = (cache_base + slot) * MDH + part * 8;
+          ks = kc;
+          vs = vc;
+        } else {
+          const int t = gk - ctx.n_ctx;
+          off = ((size_t)(b * K + t) * a.nkv + kvh) * MDH + part * 8;
+          ks = kb;
+          vs = vb;
+        }
+        kv = *reinterpret_cast<const u32x4*>(ks + off);
+        vv = *reinterpret_cast<const u32x4*>(vs + off);
+      }
+      *reinterpret_cast<u32x4*>(&sk[key][part * 8]) = kv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        svt[part * 8 + 2 * i][key] = (bf16)(vv[i] & 0xffffu);
+        svt[part * 8 + 2 * i + 1][key] = (bf16)(vv[i] >> 16);
+      }
+    }
+    __syncthreads();
+    // S = Q K^T for 16 rows x 64 keys (4 key fragments)
+    f32x4 s[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      s[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sk[16 * f + li][ks * 32 + kg * 8]);
+        s[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_bf16x8(qa[ks]), kf, s[f], 0, 0, 0);
+      }
+    }
+    // online softmax; lane holds rows 4*kg + j, key 16f + li
+    float alpha[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float mx = NEG_INF;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const float v = (16 * f + li < nk) ? s[f][j] * a.scale : NEG_INF;
+        s[f][j] = v;
+        mx = fmaxf(mx, v);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      const float mn = fmaxf(m[j], mx);
+      alpha[j] = (m[j] == NEG_INF) ? 0.f : __expf(m[j] - mn);
+      float sum = 0.f;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const float p = (s[f][j] == NEG_INF) ? 0.f : __expf(s[f][j] - mn);
+        s[f][j] = p;
+        sum += p;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+      l[j] = l[j] * alpha[j] + sum;
+      m[j] = mn;
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[n][j] *= alpha[j];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sp[w][4 * kg + j][16 * f + li] = f2bf(s[f][j]);
+    __syncthreads();
+    // O += P V : A = P [16 rows][64 keys], B = V^T rows (dims) x keys
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&sp[w][li][k2 * 32 + kg * 8]);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&svt[16 * n + li][k2 * 32 + kg * 8]);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vf, acc[n], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * w + 4 * kg + j;
+    if (r >= R) continue;
+    float* op = a.o_part + (pidx * R + r) * MDH;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) op[16 * n + li] = acc[n][j];
+    if (li == 0) {
+      a.m_part[pidx * R + r] = m[j];
+      a.l_part[pidx * R + r] = l[j];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ fp32 / VALU
+constexpr int VK = 32;
+
+__global__ __launch_bounds__(256) void attn_chunk_valu(AttnArgs a) {
+  __shared__ float sq[AT_MAXR][AT_MAXD + 1];
+  __shared__ float sk[VK][AT_MAXD + 1];
+  __shared__ float sv[VK][AT_MAXD];
+  __shared__ float sp[AT_MAXR][VK + 1];
+  __shared__ float s_m[AT_MAXR], s_l[AT_MAXR], s_alpha[AT_MAXR];
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int K = a.K, dh = a.dh, G = a.nh / a.nkv, R = G * K;
+  const SeqCtx ctx = a.ctx[b];
+  const int n_keys = ctx.n_ctx + K;
+  const int ck = (n_keys + a.chunks - 1) / a.chunks;
+  const int k_begin = min(c * ck, n_keys), k_end = min(k_begin + ck, n_keys);
+  const size_t pidx = ((size_t)b * a.nkv + kvh) * a.chunks + c;
+  const float* qg = reinterpret_cast<const float*>(a.q);
+  for (int e = tid; e < R * dh; e += 256) {
+    const int r = e / dh, dd = e % dh;
+    const int g = r / K, t = r % K;
+    sq[r][dd] = qg[((size_t)(b * K + t) * a.nh + kvh * G + g) * dh + dd];
+  }
+  if (tid < R) { s_m[tid] = NEG_INF; s_l[tid] = 0.f; }
+  const int TPR = 256 / R;
+  const int my_r = tid / TPR, my_c = tid % TPR;
+  const int nd = dh / TPR;
+  float o[AT_MAXD / 4];
+#pragma unroll
+  for (int i = 0; i < AT_MAXD / 4; ++i) o[i] = 0.f;
+  const size_t cache_base = (((size_t)a.layer * a.max_seqs + ctx.sid) * a.nkv + kvh) * (size_t)a.window;
+  const float* kc = reinterpret_cast<const float*>(a.kcache);
+  const float* vc = reinterpret_cast<const float*>(a.vcache);
+  const float* kbp = reinterpret_cast<const float*>(a.kb);
+  const float* vbp = reinterpret_cast<const float*>(a.vb);
+  const int kj = tid & 31, rg = tid >> 5;
+  for (int j0 = k_begin; j0 < k_end; j0 += VK) {
+    const int nk = min(VK, k_end - j0);
+    __syncthreads();
+    for (int e = tid; e < VK * dh; e += 256) {
+      const int j = e / dh, dd = e % dh;
+      float kv = 0.f, vv = 0.f;
+      if (j < nk) {
+        const int key = j0 + j;
+        if (key < ctx.n_ctx) {
+          const size_t off = (cache_base + (ctx.slot0 + key) % a.window) * dh + dd;
+          kv = kc[off];
+          vv = vc[off];
+        } else {
+          const size_t off = ((size_t)(b * K + key - ctx.n_ctx) * a.nkv + kvh) * dh + dd;
+          kv = kbp[off];
+          vv = vbp[off];
+        }
+      }
+      sk[j][dd] = kv;
+      sv[j][dd] = vv;
+    }
+    __syncthreads();
+    for (int r = rg; r < R; r += 8) {
+      float sc = NEG_INF;
+      if (kj < nk) {
+        float acc = 0.f;
+        for (int dd = 0; dd < dh; ++dd) acc = fmaf(sq[r][dd], sk[kj][dd], acc);
+        sc = acc * a.scale;
+      }
+      float mx = sc;
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+      const float m_old = s_m[r];
+      const float m_new = fmaxf(m_old, mx);
+      const float pv = (kj < nk) ? __expf(sc - m_new) : 0.f;
+      float sum = pv;
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 32);
+      sp[r][kj] = pv;
+      if (kj == 0) {
+        const float alpha = (m_old == NEG_INF) ? 0.f : __expf(m_old - m_new);
+        s_alpha[r] = alpha;
+        s_l[r] = s_l[r] * alpha + sum;
+        s_m[r] = m_new;
+      }
+    }
+    __syncthreads();
+    if (my_r < R) {
+      const float alpha = s_alpha[my_r];
+#pragma unroll
+      for (int i = 0; i < AT_MAXD / 4; ++i) {
+        if (i >= nd) break;
+        const int dd = my_c + i * TPR;
+        float acc = o[i] * alpha;
+        for (int j = 0; j < nk; ++j) acc = fmaf(sp[my_r][j], sv[j][dd], acc);
+        o[i] = acc;
+      }
+    }
+  }
+  __syncthreads();
+  if (my_r < R) {
+    float* op = a.o_part + (pidx * R + my_r) * dh;
+#pragma unroll
+    for (int i = 0; i < AT_MAXD / 4; ++i) {
+      if (i >= nd) break;
+      op[my_c + i * TPR] = o[i];
+    }
+  }
+  if (tid < R) {
+    a.m_part[pidx * R + tid] = s_m[tid];
+    a.l_part[pidx * R + tid] = s_l[tid];
+  }
+}
+
+// Merge the chunks of one (sequence, KV head): o = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c.
+template <typename T>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int K = a.K, dh = a.dh, G = a.nh / a.nkv, R = G * K;
+  const size_t base = ((size_t)b * a.nkv + kvh) * a.chunks;
+  for (int e = tid; e < R * dh; e += 256) {
+    const int r = e / dh, dd = e % dh;
+    float M = NEG_INF;
+    for (int c = 0; c < a.chunks; ++c) M = fmaxf(M, a.m_part[(base + c) * R + r]);
+    float num = 0.f, den = 0.f;
+    for (int c = 0; c < a.chunks; ++c) {
+      const float mc = a.m_part[(base + c) * R + r];
+      if (mc == NEG_INF) continue;
+      const float wgt = __expf(mc - M);
+      num += wgt * a.o_part[((base + c) * R + r) * dh + dd];
+      den += wgt * a.l_part[(base + c) * R + r];
+    }
+    const int g = r / K, t = r % K, h = kvh * G + g;
+    stv(reinterpret_cast<T*>(a.o), ((size_t)(b * K + t) * a.nh + h) * dh + dd, num / den);
+  }
+}
+
+hipError_t launch_attention(bool bf, const AttnArgs& a, int n_seq, hipStream_t st) {
+  const dim3 g1(a.chunks, a.nkv, n_seq), g2(a.nkv, n_seq);
+  if (bf) {
+    hipLaunchKernelGGL(attn_chunk_mfma, g1, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_combine_kernel<bf16>, g2, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(attn_chunk_valu, g1, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_combine_kernel<float>, g2, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dfl

@@ -1,0 +1,107 @@
+// Shared device helpers for libdflash (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dfl {
+
+typedef uint16_t bf16;   // bfloat16 storage (bit pattern)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float bf2f(bf16 b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bfloat16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ bf16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16)(u >> 16);
+}
+
+// Storage-type dispatch: float storage keeps fp32, bf16 storage rounds on store.
+__device__ __forceinline__ float ldv(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float ldv(const bf16* p, size_t i) { return bf2f(p[i]); }
+__device__ __forceinline__ void stv(float* p, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void stv(bf16* p, size_t i, float v) { p[i] = f2bf(v); }
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+// Block-wide sum of NV values at once for a 256-thread block; scratch must hold 4*NV floats.
+template <int NV>
+__device__ __forceinline__ void block_sum256(float (&v)[NV], float* scratch) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = wave_sum(v[i]);
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) scratch[w * NV + i] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = scratch[i] + scratch[NV + i] + scratch[2 * NV + i] + scratch[3 * NV + i];
+  __syncthreads();
+}
+
+// Candidate order for top-k: higher value first, then smaller id.
+__device__ __forceinline__ bool cand_better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// Wave-wide best candidate (value, id) under cand_better.
+__device__ __forceinline__ void wave_best(float& v, int& id) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float v2 = __shfl_xor(v, o, WAVE);
+    int i2 = __shfl_xor(id, o, WAVE);
+    if (cand_better(v2, i2, v, id)) { v = v2; id = i2; }
+  }
+}
+
+constexpr int TOPK = 16;
+constexpr float NEG_INF = -__builtin_huge_valf();
+constexpr int ID_NONE = 0x7fffffff;
+
+// A thread-private sorted top-16 list (best first) kept in registers.
+struct Top16 {
+  float v[TOPK];
+  int id[TOPK];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int i = 0; i < TOPK; ++i) { v[i] = NEG_INF; id[i] = ID_NONE; }
+  }
+  // Insert (val, idx) if it beats the current 16th entry; keeps the list sorted.
+  __device__ __forceinline__ void push(float val, int idx) {
+    if (!cand_better(val, idx, v[TOPK - 1], id[TOPK - 1])) return;
+    bool placed = false;
+#pragma unroll
+    for (int i = TOPK - 1; i >= 0; --i) {
+      const bool above = (i > 0) && cand_better(val, idx, v[i > 0 ? i - 1 : 0], id[i > 0 ? i - 1 : 0]);
+      if (above) {
+        v[i] = v[i - 1];
+        id[i] = id[i - 1];
+      } else if (!placed) {
+        v[i] = val;
+        id[i] = idx;
+        placed = true;
+      }
+    }
+  }
+};
+
+}  // namespace dfl

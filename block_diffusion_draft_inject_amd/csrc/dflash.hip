@@ -1,0 +1,730 @@
+// libdflash C ABI: argument validation, workspace layout and launch sequencing.
+// Every entry point checks its host-visible arguments before any HIP call, then only enqueues
+// kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "kernels.h"
+#include "rowops.h"
+
+using namespace dfl;
+
+static thread_local char g_err[512] = "";
+
+static dflash_status fail(dflash_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+#define HIP_TRY(call)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    if (e_ != hipSuccess) return fail(DFLASH_E_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+namespace {
+
+constexpr uint32_t HANDLE_MAGIC = 0xDF1A5401u;
+
+size_t esize(const dflash_config* c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
+
+// Workspace regions (byte offsets), a pure function of (config, max_batch, max_inject_rows).
+struct WsLayout {
+  size_t h0, h1, act_y, act_o, act_s, qb, kb, vb, ctx, part, o_part, m_part, l_part, tk_val, tk_id;
+  size_t ubar, cbuf, meta_seq, meta_pos, row_off, row_start, total;
+  size_t bytes;
+  size_t part_floats;
+  int chunks_max;
+};
+
+struct Handle {
+  uint32_t magic;
+  dflash_config cfg;
+  const void* g_embed;
+  const void* g_lm;
+  const void* g_cnorm;
+  const void* g_fc;
+  const void* g_fnorm;
+  const void* g_A;
+  const void* g_B;
+  const void* g_WH;
+  std::vector<const void*> layers;   // n_layers * DFLASH_LAYER_TENSORS
+  int max_seqs, max_batch, max_inject_rows;
+  char* kv;
+  dflash_kv_layout kvl;
+  char* ws;
+  WsLayout wl;
+  // timing
+  int t_cap, t_next, t_count;
+  std::vector<hipEvent_t> t_ev;
+};
+
+bool bf(const dflash_config* c) { return c->dtype == DFLASH_BF16; }
+
+int attn_chunks(const dflash_config* c, int n_seq) {
+  const int max_chunks = (c->window + c->block_size + 63) / 64;
+  int ch = 512 / (n_seq * c->n_kv_heads);
+  if (ch < 1) ch = 1;
+  if (ch > max_chunks) ch = max_chunks;
+  return ch;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Largest partial buffer (floats) any GEMM of a draft call with n_seq sequences, or an
+// injection pass of `rows` rows, needs.
+size_t draft_part_floats(const dflash_config* c, int n_seq) {
+  const bool b = bf(c);
+  const int M = n_seq * c->block_size, d = c->hidden, qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
+  size_t mx = 0;
+  auto upd = [&](int mode, int N, int K) {
+    GemmPlan pl = gemm_plan(b, mode, M, N, K);
+    size_t f = gemm_part_floats(pl, mode, M, N);
+    if (f > mx) mx = f;
+  };
+  upd(GEMM_PARTIAL, qw + 2 * kvw, d);
+  upd(GEMM_PARTIAL, d, qw);
+  if (b && M <= 64) upd(GEMM_SWIGLU, 2 * c->ffn, d);
+  else upd(GEMM_PARTIAL, 2 * c->ffn, d);
+  upd(GEMM_PARTIAL, d, c->ffn);
+  if (!b) {
+    size_t f = (size_t)M * c->vocab;   // fp32 path keeps full logits
+    if (f > mx) mx = f;
+  }
+  return mx;
+}
+
+size_t inject_part_floats(const dflash_config* c, int rows) {
+  const bool b = bf(c);
+  const int d = c->hidden, kvw = c->n_kv_heads * c->head_dim;
+  GemmPlan p1 = gemm_plan(b, GEMM_PARTIAL, rows, d, c->n_taps * c->target_hidden);
+  GemmPlan p2 = gemm_plan(b, GEMM_PARTIAL, rows, c->n_layers * 2 * kvw, d);
+  size_t a = gemm_part_floats(p1, GEMM_PARTIAL, rows, d);
+  size_t e = gemm_part_floats(p2, GEMM_PARTIAL, rows, c->n_layers * 2 * kvw);
+  return a > e ? a : e;
+}
+
+int topk_groups(const dflash_config* c, int n_seq) {
+  GemmPlan pl = gemm_plan(true, GEMM_TOPK, n_seq * c->block_size, c->vocab, c->hidden);
+  return pl.groups;
+}
+
+WsLayout ws_layout(const dflash_config* c, int max_batch, int max_inject_rows, int max_seqs) {
+  WsLayout L{};
+  const size_t es = esize(c);
+  const int K = c->block_size, d = c->hidden;
+  const size_t M = (size_t)max_batch * K;
+  const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
+  const int G = c->n_heads / c->n_kv_heads, R = G * K;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  L.h0 = take(M * d * 4);
+  L.h1 = take(M * d * 4);
+  L.act_y = take(M * d * es);
+  L.act_o = take(M * qw * es);
+  L.act_s = take(M * c->ffn * es);
+  L.qb = take(M * qw * es);
+  L.kb = take(M * kvw * es);
+  L.vb = take(M * kvw * es);
+  L.ctx = take((size_t)max_batch * sizeof(SeqCtx));
+  size_t pf = 0;
+  int chmax = 1;
+  size_t attn_f = 0, tk_f = 0;
+  for (int n = 1; n <= max_batch; ++n) {
+    size_t f = draft_part_floats(c, n);
+    if (f > pf) pf = f;
+    int ch = attn_chunks(c, n);
+    size_t af = (size_t)n * c->n_kv_heads * ch * R;
+    if (af > attn_f) attn_f = af;
+    if (ch > chmax) chmax = ch;
+    if (bf(c)) {
+      size_t tf = (size_t)n * K * topk_groups(c, n) * TOPK;
+      if (tf > tk_f) tk_f = tf;
+    }
+  }
+  for (int r = 1; r <= max_inject_rows; ++r) {
+    size_t f = inject_part_floats(c, r);
+    if (f > pf) pf = f;
+  }
+  L.part_floats = pf;
+  L.part = take(pf * 4);
+  L.o_part = take(attn_f * c->head_dim * 4);
+  L.m_part = take(attn_f * 4);
+  L.l_part = take(attn_f * 4);
+  L.chunks_max = chmax;
+  L.tk_val = take(tk_f * 4);
+  L.tk_id = take(tk_f * 4);
+  const size_t Ri = (size_t)max_inject_rows;
+  L.ubar = take(Ri * c->n_taps * c->target_hidden * es);
+  L.cbuf = take(Ri * d * es);
+  L.meta_seq = take(Ri * 4);
+  L.meta_pos = take(Ri * 4);
+  L.row_off = take(((size_t)max_seqs + 1) * 4);
+  L.row_start = take((size_t)max_seqs * 4);
+  L.total = take(4);
+  L.bytes = off;
+  return L;
+}
+
+dflash_status check_cfg(const dflash_config* c) {
+  if (!c) return fail(DFLASH_E_INVALID, "config is NULL");
+  if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return fail(DFLASH_E_INVALID, "dtype %d", (int)c->dtype);
+  if (c->n_layers < 1 || c->n_layers > MAX_LAYERS) return fail(DFLASH_E_UNSUPPORTED, "n_layers must be 1..%d", MAX_LAYERS);
+  if (c->hidden < 64 || c->hidden > 4096 || c->hidden % 64) return fail(DFLASH_E_UNSUPPORTED, "hidden must be a multiple of 64 in [64, 4096]");
+  if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads)
+    return fail(DFLASH_E_UNSUPPORTED, "n_heads must be a positive multiple of n_kv_heads");
+  if (c->head_dim < 2 || c->head_dim > 128 || c->head_dim % 2) return fail(DFLASH_E_UNSUPPORTED, "head_dim must be even and <= 128");
+  if (c->block_size < 2 || c->block_size > 32) return fail(DFLASH_E_UNSUPPORTED, "block_size must be 2..32");
+  const int R = (c->n_heads / c->n_kv_heads) * c->block_size;
+  if (R > 64) return fail(DFLASH_E_UNSUPPORTED, "(n_heads/n_kv_heads)*block_size must be <= 64");
+  if (c->topk != 16) return fail(DFLASH_E_UNSUPPORTED, "topk must be 16");
+  if (c->sel_rank < 1 || c->sel_rank > 256) return fail(DFLASH_E_UNSUPPORTED, "sel_rank must be 1..256");
+  if (c->window < 1) return fail(DFLASH_E_INVALID, "window must be >= 1");
+  if (c->vocab < 16) return fail(DFLASH_E_INVALID, "vocab must be >= 16");
+  if (c->mask_id < 0 || c->mask_id >= c->vocab) return fail(DFLASH_E_INVALID, "mask_id outside the vocabulary");
+  if (c->n_taps < 1 || c->target_hidden < 1) return fail(DFLASH_E_INVALID, "n_taps and target_hidden must be positive");
+  if (c->ffn < 1) return fail(DFLASH_E_INVALID, "ffn must be positive");
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 1.f)) return fail(DFLASH_E_INVALID, "rms_eps >= 0 and rope_theta > 1 required");
+  if (c->dtype == DFLASH_BF16) {
+    if (c->head_dim != 128) return fail(DFLASH_E_UNSUPPORTED, "bf16 attention needs head_dim 128");
+    const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
+    if (c->ffn % 64 || qw % 64 || (c->n_taps * c->target_hidden) % 64)
+      return fail(DFLASH_E_UNSUPPORTED, "bf16 GEMMs need ffn, n_heads*head_dim and the concat width to be multiples of 64");
+    if (qw % kvw) return fail(DFLASH_E_UNSUPPORTED, "n_heads*head_dim must be a multiple of n_kv_heads*head_dim");
+    if ((qw / kvw) + 2 > MAX_SEG || 2 * c->n_layers > MAX_SEG) return fail(DFLASH_E_UNSUPPORTED, "too many weight segments");
+  } else {
+    if (256 % R || c->head_dim % (256 / R)) return fail(DFLASH_E_UNSUPPORTED, "fp32 attention needs 256 %% R == 0 and head_dim %% (256/R) == 0");
+    const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
+    if ((qw / kvw) + 2 > MAX_SEG || 2 * c->n_layers > MAX_SEG) return fail(DFLASH_E_UNSUPPORTED, "too many weight segments");
+  }
+  return DFLASH_OK;
+}
+
+dflash_kv_layout kv_layout(const dflash_config* c, int max_seqs) {
+  dflash_kv_layout k{};
+  const size_t one = (size_t)c->n_layers * max_seqs * c->n_kv_heads * c->window * c->head_dim * esize(c);
+  k.k_offset = 0;
+  k.v_offset = align_up(one);
+  k.seq_len_offset = align_up(k.v_offset + one);
+  k.seq_base_offset = align_up(k.seq_len_offset + (size_t)max_seqs * 4);
+  k.device_error_offset = align_up(k.seq_base_offset + (size_t)max_seqs * 4);
+  k.total_bytes = align_up(k.device_error_offset + 4);
+  return k;
+}
+
+Handle* as_handle(dflash_handle* h) {
+  Handle* H = reinterpret_cast<Handle*>(h);
+  if (!H || H->magic != HANDLE_MAGIC) return nullptr;
+  return H;
+}
+
+template <typename P>
+P* wsp(Handle* H, size_t off) { return reinterpret_cast<P*>(H->ws + off); }
+
+const void* LW(Handle* H, int l, int t) { return H->layers[(size_t)l * DFLASH_LAYER_TENSORS + t]; }
+
+int* seq_len(Handle* H) { return reinterpret_cast<int*>(H->kv + H->kvl.seq_len_offset); }
+int* seq_base(Handle* H) { return reinterpret_cast<int*>(H->kv + H->kvl.seq_base_offset); }
+int* dev_err(Handle* H) { return reinterpret_cast<int*>(H->kv + H->kvl.device_error_offset); }
+
+GemmParams gemm_base(const void* A, int lda, int M, int N, int K) {
+  GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.A = A;
+  p.lda = lda;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.ldb = K;
+  p.block = 1;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_status_string(dflash_status s) {
+  switch (s) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_E_INVALID: return "invalid argument";
+    case DFLASH_E_SHAPE: return "size outside the handle's limits";
+    case DFLASH_E_UNSUPPORTED: return "unsupported configuration";
+    case DFLASH_E_HIP: return "HIP runtime error";
+    case DFLASH_E_STATE: return "invalid handle state";
+  }
+  return "unknown status";
+}
+
+const char* dflash_last_error(void) { return g_err; }
+
+dflash_status dflash_config_check(const dflash_config* cfg) { return check_cfg(cfg); }
+
+size_t dflash_kv_cache_bytes(const dflash_config* cfg, int32_t max_seqs) {
+  if (check_cfg(cfg) != DFLASH_OK || max_seqs < 1) return 0;
+  return kv_layout(cfg, max_seqs).total_bytes;
+}
+
+dflash_status dflash_kv_cache_layout(const dflash_config* cfg, int32_t max_seqs, dflash_kv_layout* out) {
+  dflash_status s = check_cfg(cfg);
+  if (s != DFLASH_OK) return s;
+  if (max_seqs < 1) return fail(DFLASH_E_INVALID, "max_seqs must be >= 1");
+  if (!out) return fail(DFLASH_E_INVALID, "out is NULL");
+  *out = kv_layout(cfg, max_seqs);
+  return DFLASH_OK;
+}
+
+size_t dflash_workspace_bytes(const dflash_config* cfg, int32_t max_seqs, int32_t max_batch, int32_t max_inject_rows) {
+  if (check_cfg(cfg) != DFLASH_OK || max_seqs < 1 || max_batch < 1 || max_inject_rows < 1) return 0;
+  if (max_batch > 4096 || max_seqs > (1 << 20) || max_inject_rows > (1 << 16)) return 0;
+  return ws_layout(cfg, max_batch, max_inject_rows, max_seqs).bytes;
+}
+
+dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, int32_t max_seqs, int32_t max_batch,
+                            int32_t max_inject_rows, void* kv_cache, size_t kv_bytes, void* workspace, size_t ws_bytes,
+                            dflash_handle** out) {
+  dflash_status s = check_cfg(cfg);
+  if (s != DFLASH_OK) return s;
+  if (!w || !out || !kv_cache || !workspace) return fail(DFLASH_E_INVALID, "NULL weights, output, kv_cache or workspace");
+  if (max_seqs < 1 || max_batch < 1 || max_inject_rows < 1) return fail(DFLASH_E_INVALID, "max_seqs, max_batch, max_inject_rows must be >= 1");
+  if (max_batch > 4096) return fail(DFLASH_E_UNSUPPORTED, "max_batch must be <= 4096");
+  if (max_seqs > 1 << 20) return fail(DFLASH_E_UNSUPPORTED, "max_seqs must be <= 2^20");
+  if (max_inject_rows > 1 << 16) return fail(DFLASH_E_UNSUPPORTED, "max_inject_rows must be <= 65536");
+  const void* globals[] = {w->embed, w->lm_head, w->concat_norm, w->fc, w->final_norm, w->sel_A, w->sel_B, w->sel_WH};
+  for (const void* p : globals)
+    if (!p) return fail(DFLASH_E_INVALID, "a global weight pointer is NULL");
+  if (!w->layers) return fail(DFLASH_E_INVALID, "layers is NULL");
+  for (int i = 0; i < cfg->n_layers * DFLASH_LAYER_TENSORS; ++i)
+    if (!w->layers[i]) return fail(DFLASH_E_INVALID, "layer tensor %d of layer %d is NULL", i % DFLASH_LAYER_TENSORS, i / DFLASH_LAYER_TENSORS);
+  const dflash_kv_layout kvl = kv_layout(cfg, max_seqs);
+  if (kv_bytes < kvl.total_bytes) return fail(DFLASH_E_SHAPE, "kv_cache has %zu bytes, needs %zu", kv_bytes, kvl.total_bytes);
+  // the workspace also holds per-sequence injection offsets, sized by max_seqs
+  const WsLayout wl = ws_layout(cfg, max_batch, max_inject_rows, max_seqs);
+  if (ws_bytes < wl.bytes) return fail(DFLASH_E_SHAPE, "workspace has %zu bytes, needs %zu", ws_bytes, wl.bytes);
+  Handle* H = new Handle();
+  H->magic = HANDLE_MAGIC;
+  H->cfg = *cfg;
+  H->g_embed = w->embed;
+  H->g_lm = w->lm_head;
+  H->g_cnorm = w->concat_norm;
+  H->g_fc = w->fc;
+  H->g_fnorm = w->final_norm;
+  H->g_A = w->sel_A;
+  H->g_B = w->sel_B;
+  H->g_WH = w->sel_WH;
+  H->layers.assign(w->layers, w->layers + (size_t)cfg->n_layers * DFLASH_LAYER_TENSORS);
+  H->max_seqs = max_seqs;
+  H->max_batch = max_batch;
+  H->max_inject_rows = max_inject_rows;
+  H->kv = reinterpret_cast<char*>(kv_cache);
+  H->kvl = kvl;
+  H->ws = reinterpret_cast<char*>(workspace);
+  H->wl = wl;
+  H->t_cap = H->t_next = H->t_count = 0;
+  *out = reinterpret_cast<dflash_handle*>(H);
+  return DFLASH_OK;
+}
+
+dflash_status dflash_destroy(dflash_handle* h) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  for (hipEvent_t e : H->t_ev) (void)hipEventDestroy(e);
+  H->magic = 0;
+  delete H;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_reset_seqs(dflash_handle* h, int32_t n_seq, const int32_t* seq_ids, void* stream) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  if (n_seq < 0 || n_seq > H->max_seqs) return fail(DFLASH_E_SHAPE, "n_seq %d outside [0, max_seqs=%d]", n_seq, H->max_seqs);
+  if (n_seq > 0 && !seq_ids) return fail(DFLASH_E_INVALID, "seq_ids is NULL");
+  ResetArgs a{n_seq, H->max_seqs, seq_ids, seq_len(H), seq_base(H), dev_err(H)};
+  HIP_TRY(launch_reset(a, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* seq_ids, const int32_t* start_pos,
+                               const int32_t* n_new, int32_t max_new, const void* target_hidden, void* stream) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  const dflash_config* c = &H->cfg;
+  if (n_seq < 0 || n_seq > H->max_seqs) return fail(DFLASH_E_SHAPE, "n_seq %d outside [0, max_seqs=%d]", n_seq, H->max_seqs);
+  if (max_new < 0) return fail(DFLASH_E_INVALID, "max_new must be >= 0");
+  if (n_seq == 0 || max_new == 0) return DFLASH_OK;
+  if (!seq_ids || !n_new || !target_hidden) return fail(DFLASH_E_INVALID, "NULL seq_ids, n_new or target_hidden");
+  if ((long long)n_seq * max_new > (1ll << 30)) return fail(DFLASH_E_SHAPE, "n_seq * max_new too large");
+  hipStream_t st = (hipStream_t)stream;
+  const bool b = bf(c);
+  const int d = c->hidden, concat = c->n_taps * c->target_hidden, kvw = c->n_kv_heads * c->head_dim;
+  const int Nkv = c->n_layers * 2 * kvw;
+  const int Ri = H->max_inject_rows;
+  InjectArgs ia{};
+  ia.n_seq = n_seq;
+  ia.max_new = max_new;
+  ia.max_seqs = H->max_seqs;
+  ia.concat = concat;
+  ia.eps = c->rms_eps;
+  ia.seq_ids = seq_ids;
+  ia.start_pos = start_pos;
+  ia.n_new = n_new;
+  ia.seq_len = seq_len(H);
+  ia.seq_base = seq_base(H);
+  ia.dev_err = dev_err(H);
+  ia.row_off = wsp<int>(H, H->wl.row_off);
+  ia.row_start = wsp<int>(H, H->wl.row_start);
+  ia.total = wsp<int>(H, H->wl.total);
+  ia.states = target_hidden;
+  ia.gain = H->g_cnorm;
+  ia.ubar = H->ws + H->wl.ubar;
+  ia.meta_seq = wsp<int>(H, H->wl.meta_seq);
+  ia.meta_pos = wsp<int>(H, H->wl.meta_pos);
+  HIP_TRY(launch_inject_plan(ia, st));
+  const long long max_rows = (long long)n_seq * max_new;
+  float* part = wsp<float>(H, H->wl.part);
+  for (long long r0 = 0; r0 < max_rows; r0 += Ri) {
+    const int rows = (int)((max_rows - r0) < Ri ? (max_rows - r0) : Ri);
+    ia.chunk0 = (int)r0;
+    HIP_TRY(launch_concat_norm(b, ia, rows, st));
+    // rows valid in this pass = clamp(total - r0, 0, rows): kernels read it from meta/total
+    // fc: c = u_bar W_fc^T
+    GemmParams g1 = gemm_base(H->ws + H->wl.ubar, concat, rows, d, concat);
+    g1.m_dev = ia.total;
+    g1.m_off = (int)r0;
+    g1.seg[0] = H->g_fc;
+    g1.seg_rows = d;
+    g1.part = part;
+    GemmPlan p1 = gemm_plan(b, GEMM_PARTIAL, rows, d, concat);
+    HIP_TRY(gemm_launch(b, p1, GEMM_PARTIAL, g1, st));
+    ReduceArgs ra{rows, d, p1.splits, rows, ia.total, (int)r0, part, H->ws + H->wl.cbuf};
+    HIP_TRY(launch_reduce_store(b, ra, st));
+    // layer-batched K/V projection of every layer
+    GemmParams g2 = gemm_base(H->ws + H->wl.cbuf, d, rows, Nkv, d);
+    g2.m_dev = ia.total;
+    g2.m_off = (int)r0;
+    for (int l = 0; l < c->n_layers; ++l) {
+      g2.seg[2 * l] = LW(H, l, DFLASH_L_WK);
+      g2.seg[2 * l + 1] = LW(H, l, DFLASH_L_WV);
+    }
+    g2.seg_rows = kvw;
+    g2.part = part;
+    GemmPlan p2 = gemm_plan(b, GEMM_PARTIAL, rows, Nkv, d);
+    HIP_TRY(gemm_launch(b, p2, GEMM_PARTIAL, g2, st));
+    KvPostArgs ka{};
+    ka.N = Nkv;
+    ka.splits = p2.splits;
+    ka.part_rows = rows;
+    ka.nkv = c->n_kv_heads;
+    ka.dh = c->head_dim;
+    ka.window = c->window;
+    ka.max_seqs = H->max_seqs;
+    ka.eps = c->rms_eps;
+    ka.log_theta = log((double)c->rope_theta);
+    ka.part = part;
+    ka.meta_seq = ia.meta_seq;
+    ka.meta_pos = ia.meta_pos;
+    for (int l = 0; l < c->n_layers; ++l) ka.k_gain[l] = LW(H, l, DFLASH_L_K_NORM);
+    ka.kcache = H->kv + H->kvl.k_offset;
+    ka.vcache = H->kv + H->kvl.v_offset;
+    HIP_TRY(launch_kv_post(b, ka, rows, c->n_layers * 2 * c->n_kv_heads, st));
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t* seq_ids, const int32_t* anchor_ids,
+                                 int32_t* topk_ids, float* topk_logits, void* h_final, float* logits, void* stream) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  const dflash_config* c = &H->cfg;
+  if (n_seq < 1 || n_seq > H->max_batch) return fail(DFLASH_E_SHAPE, "n_seq %d outside [1, max_batch=%d]", n_seq, H->max_batch);
+  if (!seq_ids || !anchor_ids || !topk_ids || !topk_logits || !h_final)
+    return fail(DFLASH_E_INVALID, "NULL seq_ids, anchor_ids, topk_ids, topk_logits or h_final");
+  hipStream_t st = (hipStream_t)stream;
+  const bool b = bf(c);
+  const int K = c->block_size, d = c->hidden, M = n_seq * K;
+  const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
+  const WsLayout& W = H->wl;
+  float* part = wsp<float>(H, W.part);
+  SeqCtx* ctx = wsp<SeqCtx>(H, W.ctx);
+  PlanArgs pa{n_seq, H->max_seqs, c->window, seq_ids, seq_len(H), seq_base(H), dev_err(H), ctx};
+  HIP_TRY(launch_draft_plan(pa, st));
+  float* hA = wsp<float>(H, W.h0);
+  float* hB = wsp<float>(H, W.h1);
+  char* act_y = H->ws + W.act_y;
+  char* act_o = H->ws + W.act_o;
+  char* act_s = H->ws + W.act_s;
+  RowArgs ra{};
+  ra.K = K;
+  ra.d = d;
+  ra.mask_id = c->mask_id;
+  ra.use_conv = c->use_conv;
+  ra.eps = c->rms_eps;
+  ra.anchor = anchor_ids;
+  ra.vocab = c->vocab;
+  ra.dev_err = dev_err(H);
+  ra.embed = H->g_embed;
+  ra.h_out = hA;
+  ra.pre_gain = LW(H, 0, DFLASH_L_ATTN_NORM);
+  ra.pre_w = LW(H, 0, DFLASH_L_CONV_ATTN_PRE_W);
+  ra.pre_b = LW(H, 0, DFLASH_L_CONV_ATTN_PRE_B);
+  ra.y = act_y;
+  ra.ldy = d;
+  HIP_TRY(launch_embed_pre(b, ra, M, st));
+  const int chunks = attn_chunks(c, n_seq);
+  for (int l = 0; l < c->n_layers; ++l) {
+    // q, k, v = y [W_q; W_k; W_v]^T
+    const int G = qw / kvw;
+    GemmParams gq = gemm_base(act_y, d, M, qw + 2 * kvw, d);
+    for (int i = 0; i < G; ++i)
+      gq.seg[i] = reinterpret_cast<const char*>(LW(H, l, DFLASH_L_WQ)) + (size_t)i * kvw * d * esize(c);
+    gq.seg[G] = LW(H, l, DFLASH_L_WK);
+    gq.seg[G + 1] = LW(H, l, DFLASH_L_WV);
+    gq.seg_rows = kvw;
+    gq.part = part;
+    GemmPlan pq = gemm_plan(b, GEMM_PARTIAL, M, qw + 2 * kvw, d);
+    HIP_TRY(gemm_launch(b, pq, GEMM_PARTIAL, gq, st));
+    QkvArgs qa{};
+    qa.K = K;
+    qa.nh = c->n_heads;
+    qa.nkv = c->n_kv_heads;
+    qa.dh = c->head_dim;
+    qa.N = qw + 2 * kvw;
+    qa.splits = pq.splits;
+    qa.part_rows = M;
+    qa.eps = c->rms_eps;
+    qa.log_theta = log((double)c->rope_theta);
+    qa.ctx = ctx;
+    qa.part = part;
+    qa.q_gain = LW(H, l, DFLASH_L_Q_NORM);
+    qa.k_gain = LW(H, l, DFLASH_L_K_NORM);
+    qa.q = H->ws + W.qb;
+    qa.k = H->ws + W.kb;
+    qa.v = H->ws + W.vb;
+    HIP_TRY(launch_qkv_post(b, qa, M, st));
+    AttnArgs aa{};
+    aa.K = K;
+    aa.nh = c->n_heads;
+    aa.nkv = c->n_kv_heads;
+    aa.dh = c->head_dim;
+    aa.window = c->window;
+    aa.max_seqs = H->max_seqs;
+    aa.chunks = chunks;
+    aa.layer = l;
+    aa.scale = 1.0f / sqrtf((float)c->head_dim);
+    aa.ctx = ctx;
+    aa.q = qa.q;
+    aa.kb = qa.k;
+    aa.vb = qa.v;
+    aa.kcache = H->kv + H->kvl.k_offset;
+    aa.vcache = H->kv + H->kvl.v_offset;
+    aa.o_part = wsp<float>(H, W.o_part);
+    aa.m_part = wsp<float>(H, W.m_part);
+    aa.l_part = wsp<float>(H, W.l_part);
+    aa.o = act_o;
+    HIP_TRY(launch_attention(b, aa, n_seq, st));
+    // a = o W_o^T
+    GemmParams go = gemm_base(act_o, qw, M, d, qw);
+    go.seg[0] = LW(H, l, DFLASH_L_WO);
+    go.seg_rows = d;
+    go.part = part;
+    GemmPlan po = gemm_plan(b, GEMM_PARTIAL, M, d, qw);
+    HIP_TRY(gemm_launch(b, po, GEMM_PARTIAL, go, st));
+    RowArgs rp = ra;
+    rp.h_in = hA;
+    rp.h_out = hB;
+    rp.part = part;
+    rp.splits = po.splits;
+    rp.part_rows = M;
+    rp.post_w = LW(H, l, DFLASH_L_CONV_ATTN_POST_W);
+    rp.post_b = LW(H, l, DFLASH_L_CONV_ATTN_POST_B);
+    rp.pre_gain = LW(H, l, DFLASH_L_MLP_NORM);
+    rp.pre_w = LW(H, l, DFLASH_L_CONV_MLP_PRE_W);
+    rp.pre_b = LW(H, l, DFLASH_L_CONV_MLP_PRE_B);
+    rp.final_norm = 0;
+    rp.y = act_y;
+    rp.ldy = d;
+    HIP_TRY(launch_post_pre(b, rp, M, st));
+    // s = silu(y W_gate^T) * (y W_up^T)
+    GemmParams gg = gemm_base(act_y, d, M, 2 * c->ffn, d);
+    gg.seg[0] = LW(H, l, DFLASH_L_W_GATE);
+    gg.seg[1] = LW(H, l, DFLASH_L_W_UP);
+    gg.seg_rows = c->ffn;
+    gg.half = c->ffn;
+    gg.out = act_s;
+    gg.part = part;
+    if (b && M <= 64) {
+      GemmPlan pg = gemm_plan(b, GEMM_SWIGLU, M, 2 * c->ffn, d);
+      HIP_TRY(gemm_launch(b, pg, GEMM_SWIGLU, gg, st));
+    } else {
+      gg.half = 0;
+      GemmPlan pg = gemm_plan(b, GEMM_PARTIAL, M, 2 * c->ffn, d);
+      HIP_TRY(gemm_launch(b, pg, GEMM_PARTIAL, gg, st));
+      SwigluArgs sa{M, c->ffn, pg.splits, M, part, act_s};
+      HIP_TRY(launch_swiglu(b, sa, st));
+    }
+    // m = s W_down^T
+    GemmParams gd = gemm_base(act_s, c->ffn, M, d, c->ffn);
+    gd.seg[0] = LW(H, l, DFLASH_L_W_DOWN);
+    gd.seg_rows = d;
+    gd.part = part;
+    GemmPlan pd = gemm_plan(b, GEMM_PARTIAL, M, d, c->ffn);
+    HIP_TRY(gemm_launch(b, pd, GEMM_PARTIAL, gd, st));
+    RowArgs rm = ra;
+    rm.h_in = hB;
+    rm.h_out = hA;
+    rm.part = part;
+    rm.splits = pd.splits;
+    rm.part_rows = M;
+    rm.post_w = LW(H, l, DFLASH_L_CONV_MLP_POST_W);
+    rm.post_b = LW(H, l, DFLASH_L_CONV_MLP_POST_B);
+    if (l + 1 < c->n_layers) {
+      rm.pre_gain = LW(H, l + 1, DFLASH_L_ATTN_NORM);
+      rm.pre_w = LW(H, l + 1, DFLASH_L_CONV_ATTN_PRE_W);
+      rm.pre_b = LW(H, l + 1, DFLASH_L_CONV_ATTN_PRE_B);
+      rm.final_norm = 0;
+      rm.y = act_y;
+      rm.ldy = d;
+    } else {
+      rm.pre_gain = H->g_fnorm;
+      rm.final_norm = 1;
+      rm.y = h_final;
+      rm.ldy = d;
+    }
+    HIP_TRY(launch_post_pre(b, rm, M, st));
+  }
+  // shared lm_head + top-16 per draft slot
+  GemmParams gl = gemm_base(h_final, d, M, c->vocab, d);
+  gl.seg[0] = H->g_lm;
+  gl.seg_rows = c->vocab;
+  gl.block = K;
+  MergeArgs ma{};
+  ma.K = K;
+  ma.out_ids = topk_ids;
+  ma.out_vals = topk_logits;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (H->t_cap > 0) {
+    ev0 = H->t_ev[2 * H->t_next];
+    ev1 = H->t_ev[2 * H->t_next + 1];
+    H->t_next = (H->t_next + 1) % H->t_cap;
+    if (H->t_count < H->t_cap) H->t_count++;
+    HIP_TRY(hipEventRecord(ev0, st));
+  }
+  if (b) {
+    gl.tk_val = wsp<float>(H, W.tk_val);
+    gl.tk_id = wsp<int>(H, W.tk_id);
+    gl.logits = logits;
+    GemmPlan pl = gemm_plan(b, GEMM_TOPK, M, c->vocab, d);
+    HIP_TRY(gemm_launch(b, pl, GEMM_TOPK, gl, st));
+    if (ev1) HIP_TRY(hipEventRecord(ev1, st));
+    ma.ncand = pl.groups * TOPK;
+    ma.vals = gl.tk_val;
+    ma.ids = gl.tk_id;
+  } else {
+    gl.part = part;
+    GemmPlan pl = gemm_plan(b, GEMM_PARTIAL, M, c->vocab, d);
+    HIP_TRY(gemm_launch(b, pl, GEMM_PARTIAL, gl, st));
+    if (ev1) HIP_TRY(hipEventRecord(ev1, st));
+    ma.ncand = c->vocab;
+    ma.vals = part;
+    ma.ids = nullptr;
+    ma.logits_out = logits;
+  }
+  HIP_TRY(launch_topk_merge(ma, n_seq * (K - 1), st));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t* anchor_ids, const int32_t* topk_ids,
+                                 const float* topk_logits, const void* h_final, dflash_select_mode mode,
+                                 int32_t* path_ids, float* path_score, float* margin, void* stream) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  const dflash_config* c = &H->cfg;
+  if (n_seq < 1 || n_seq > H->max_batch) return fail(DFLASH_E_SHAPE, "n_seq %d outside [1, max_batch=%d]", n_seq, H->max_batch);
+  if (mode != DFLASH_SELECT_VITERBI && mode != DFLASH_SELECT_GREEDY) return fail(DFLASH_E_INVALID, "mode %d", (int)mode);
+  if (!anchor_ids || !topk_ids || !topk_logits || !h_final || !path_ids)
+    return fail(DFLASH_E_INVALID, "NULL anchor_ids, topk_ids, topk_logits, h_final or path_ids");
+  SelectArgs sa{c->block_size, c->hidden, c->sel_rank, (int)mode, c->vocab, dev_err(H), anchor_ids, topk_ids,
+                topk_logits, h_final, H->g_A, H->g_B, H->g_WH, path_ids, path_score, margin};
+  HIP_TRY(launch_select(bf(c), sa, n_seq, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_verify_greedy(int32_t n_seq, int32_t block_size, const int32_t* draft_ids, const int32_t* target_argmax,
+                                   int32_t* n_accepted, int32_t* n_commit, int32_t* committed, int32_t* next_anchor,
+                                   void* stream) {
+  if (n_seq < 0) return fail(DFLASH_E_INVALID, "n_seq must be >= 0");
+  if (block_size < 2) return fail(DFLASH_E_INVALID, "block_size must be >= 2");
+  if (n_seq == 0) return DFLASH_OK;
+  if (!draft_ids || !target_argmax || !n_accepted || !committed || !next_anchor)
+    return fail(DFLASH_E_INVALID, "NULL draft_ids, target_argmax, n_accepted, committed or next_anchor");
+  VerifyArgs va{n_seq, block_size, draft_ids, target_argmax, n_accepted, n_commit, committed, next_anchor};
+  HIP_TRY(launch_verify(va, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_synth_target_argmax(int32_t n_seq, int32_t block_size, int32_t vocab, const int32_t* draft_ids,
+                                         float match_prob, uint64_t seed, int64_t* counter, int32_t* target_argmax,
+                                         void* stream) {
+  if (n_seq < 0 || n_seq > 1024) return fail(DFLASH_E_SHAPE, "n_seq must be 0..1024");
+  if (block_size < 2 || vocab < 2) return fail(DFLASH_E_INVALID, "block_size and vocab must be >= 2");
+  if (!(match_prob >= 0.f && match_prob <= 1.f)) return fail(DFLASH_E_INVALID, "match_prob must be in [0, 1]");
+  if (n_seq == 0) return DFLASH_OK;
+  if (!draft_ids || !counter || !target_argmax) return fail(DFLASH_E_INVALID, "NULL draft_ids, counter or target_argmax");
+  SynthArgs a{n_seq, block_size, vocab, match_prob, (unsigned long long)seed, reinterpret_cast<long long*>(counter),
+              draft_ids, target_argmax};
+  HIP_TRY(launch_synth(a, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_timing_enable(dflash_handle* h, int32_t capacity) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  if (capacity < 0 || capacity > 100000) return fail(DFLASH_E_INVALID, "capacity must be 0..100000");
+  for (hipEvent_t e : H->t_ev) (void)hipEventDestroy(e);
+  H->t_ev.clear();
+  H->t_cap = H->t_next = H->t_count = 0;
+  if (capacity == 0) return DFLASH_OK;
+  H->t_ev.resize(2 * (size_t)capacity, nullptr);
+  for (auto& e : H->t_ev) HIP_TRY(hipEventCreate(&e));
+  H->t_cap = capacity;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_timing_read(dflash_handle* h, double* total_ms, int32_t* count) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  if (!total_ms || !count) return fail(DFLASH_E_INVALID, "NULL output");
+  double tot = 0.0;
+  const int n = H->t_count;
+  for (int i = 0; i < n; ++i) {
+    HIP_TRY(hipEventSynchronize(H->t_ev[2 * i + 1]));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, H->t_ev[2 * i], H->t_ev[2 * i + 1]));
+    tot += ms;
+  }
+  *total_ms = tot;
+  *count = n;
+  H->t_count = 0;
+  H->t_next = 0;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_get_device_error(dflash_handle* h, int32_t* code) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  if (!code) return fail(DFLASH_E_INVALID, "code is NULL");
+  HIP_TRY(hipDeviceSynchronize());
+  HIP_TRY(hipMemcpy(code, dev_err(H), 4, hipMemcpyDeviceToHost));
+  return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,524 @@
+// Weight GEMMs of the drafter on gfx950: C = A * B^T with A = activations [M][K] and
+// B = a weight matrix [N][K] (one output row per line), fp32 accumulation.
+//
+//  * gemm_skinny  (bf16, M <= 64): weight streaming.  Every weight byte is used by at most 4
+//    row fragments, so weights go straight from HBM into VGPRs (no LDS), 32 contiguous bytes
+//    per lane per load.  The k index inside a 64-wide chunk is permuted so that a lane's two
+//    16-byte loads are adjacent; A and B use the same permutation, so the sum is unchanged.
+//    Waves of a workgroup split K and are reduced through LDS; workgroups split K again
+//    ("splits") into fp32 partials that the consumer kernel sums in a fixed order.
+//  * gemm_tiled   (bf16, M > 64): 128x128x64 tiles staged through double-buffered LDS,
+//    2x2 waves of 64x64, v_mfma_f32_16x16x32_bf16.
+//  * gemm_f32     (fp32 drafters): plain VALU dot products, for the small fp32 configuration.
+//  * TOPK mode: the lm_head epilogue keeps a running top-16 per row (thread-private sorted
+//    lists, merged at the end of the workgroup) over a contiguous range of column tiles and
+//    writes one partial list per (row, workgroup); the full-logit matrix is never stored
+//    unless requested for checking.
+#include "common.h"
+#include "kernels.h"
+
+namespace dfl {
+
+__device__ __forceinline__ const bf16* brow_ptr(const GemmParams& p, int n) {
+  const int s = n / p.seg_rows;
+  return reinterpret_cast<const bf16*>(p.seg[s]) + (size_t)(n - s * p.seg_rows) * p.ldb;
+}
+
+__device__ __forceinline__ int rows_valid(const GemmParams& p) {
+  return p.m_dev ? max(0, min(p.M, *p.m_dev - p.m_off)) : p.M;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+// ---------------------------------------------------------------------------------------
+// skinny: accumulate one wave tile of (16*MT rows) x (16*NF cols) over chunks
+// c = c0, c0 + cstep, ... < c1 (chunk = 64 k values).
+// ---------------------------------------------------------------------------------------
+template <int MT, int NF>
+__device__ __forceinline__ void skinny_acc(const bf16* const (&arow)[MT], const bf16* const (&brow)[NF], int kg,
+                                           int c0, int c1, int cstep, f32x4 (&acc)[MT][NF]) {
+  constexpr int U = 4;
+  int c = c0;
+  for (; c + (U - 1) * cstep < c1; c += U * cstep) {
+    u32x4 a[U][MT][2], b[U][NF][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (c + u * cstep) * 64 + kg * 16;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const u32x4* q = reinterpret_cast<const u32x4*>(brow[f] + k);
+        b[u][f][0] = q[0];
+        b[u][f][1] = q[1];
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const u32x4* q = reinterpret_cast<const u32x4*>(arow[m] + k);
+        a[u][m][0] = q[0];
+        a[u][m][1] = q[1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][m][0]), as_bf16x8(b[u][f][0]), acc[m][f], 0, 0, 0);
+          acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][m][1]), as_bf16x8(b[u][f][1]), acc[m][f], 0, 0, 0);
+        }
+  }
+  for (; c < c1; c += cstep) {
+    const int k = c * 64 + kg * 16;
+    u32x4 a[MT][2], b[NF][2];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const u32x4* q = reinterpret_cast<const u32x4*>(brow[f] + k);
+      b[f][0] = q[0];
+      b[f][1] = q[1];
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const u32x4* q = reinterpret_cast<const u32x4*>(arow[m] + k);
+      a[m][0] = q[0];
+      a[m][1] = q[1];
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[m][0]), as_bf16x8(b[f][0]), acc[m][f], 0, 0, 0);
+        acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[m][1]), as_bf16x8(b[f][1]), acc[m][f], 0, 0, 0);
+      }
+  }
+}
+
+// PARTIAL (NF=1) and SWIGLU (NF=2: gate and up fragment of the same 16 output columns).
+// grid: x = column tile (16 output columns), y = row tile (16*MT rows), z = k-split.
+template <int MT, int MODE>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
+  constexpr int NF = (MODE == GEMM_SWIGLU) ? 2 : 1;
+  __shared__ float red[3][MT][NF][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, kg = lane >> 4;
+  const int Mv = rows_valid(p);
+  const int m0 = blockIdx.y * 16 * MT;
+  if (m0 >= Mv) return;
+  const int ncol0 = blockIdx.x * 16;
+  const bf16* arow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int r = min(m0 + m * 16 + li, Mv - 1);
+    arow[m] = reinterpret_cast<const bf16*>(p.A) + (size_t)r * p.lda;
+  }
+  const bf16* brow[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    int n = ncol0 + li + f * p.half;     // SWIGLU: f=1 reads the up rows at offset `half`
+    n = min(n, p.N - 1);
+    brow[f] = brow_ptr(p, n);
+  }
+  const int nchunks = p.K / 64;
+  const int s = blockIdx.z;
+  const int c0 = (int)((long)nchunks * s / p.splits), c1 = (int)((long)nchunks * (s + 1) / p.splits);
+  f32x4 acc[MT][NF];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  skinny_acc<MT, NF>(arow, brow, kg, c0 + wave, c1, 4, acc);
+  // reduce the 4 waves' k-slices
+  if (wave > 0) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[wave - 1][m][f][j][lane] = acc[m][f][j];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[m][f][j] += red[0][m][f][j][lane] + red[1][m][f][j][lane] + red[2][m][f][j][lane];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = m0 + m * 16 + kg * 4 + j;
+      const int col = ncol0 + li;
+      if (row >= Mv) continue;
+      if (MODE == GEMM_PARTIAL) {
+        if (col < p.N) p.part[((size_t)s * p.M + row) * p.N + col] = acc[m][0][j];
+      } else {
+        if (col < p.half) {
+          const float v = silu_f(acc[m][0][j]) * acc[m][NF - 1][j];
+          reinterpret_cast<bf16*>(p.out)[(size_t)row * p.half + col] = f2bf(v);
+        }
+      }
+    }
+}
+
+// Writes one wave-tile of logits (rows of slot >= 1 only) when full logits are requested.
+__device__ __forceinline__ void store_logit(const GemmParams& p, int row, int col, float v) {
+  const int slot = row % p.block;
+  if (slot == 0 || col >= p.N) return;
+  const size_t orow = (size_t)(row / p.block) * (p.block - 1) + (slot - 1);
+  p.logits[orow * p.N + col] = v;
+}
+
+// Thread-pair or thread-group merge of Top16 lists through LDS, then store a partial.
+// `lists` holds nthr_per_row lists per row; the first thread of each row merges.
+__device__ __forceinline__ void store_partial(const GemmParams& p, int row, int group, const Top16& t) {
+  const size_t base = ((size_t)row * p.groups + group) * TOPK;
+#pragma unroll
+  for (int i = 0; i < TOPK; ++i) {
+    p.tk_val[base + i] = t.v[i];
+    p.tk_id[base + i] = t.id[i];
+  }
+}
+
+// TOPK (lm_head) skinny: 4 waves each own one 16-column fragment of a 64-column tile and run
+// over all of K.  Each row is scanned by 16 threads (4 columns of every tile each) holding a
+// private running top-16; at the end the 16 lists of a row are merged.
+// grid: x = group (contiguous range of 64-column tiles), y = row tile.
+template <int MT>
+__global__ __launch_bounds__(256) void lmhead_topk_skinny(GemmParams p) {
+  constexpr int R = 16 * MT;
+  constexpr int TPR = 256 / R;        // threads per row: 16 (MT=1), 8 (MT=2), 4 (MT=4)
+  constexpr int CPT = 64 / TPR;       // columns per thread per tile
+  __shared__ float tile[R][64 + 1];
+  __shared__ float mv[128][TOPK];   // R * TPR / 2 == 128 lists in flight during the merge
+  __shared__ int mi[128][TOPK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, kg = lane >> 4;
+  const int Mv = rows_valid(p);
+  const int m0 = blockIdx.y * R;
+  if (m0 >= Mv) return;
+  const int g = blockIdx.x, G = gridDim.x;
+  const int ntiles = (p.N + 63) / 64;
+  const int t0 = (int)((long)ntiles * g / G), t1 = (int)((long)ntiles * (g + 1) / G);
+  const bf16* arow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int r = min(m0 + m * 16 + li, Mv - 1);
+    arow[m] = reinterpret_cast<const bf16*>(p.A) + (size_t)r * p.lda;
+  }
+  const int my_row = tid / TPR, my_part = tid % TPR;
+  const bool row_live = (m0 + my_row < Mv) && ((m0 + my_row) % p.block != 0);
+  Top16 top;
+  top.init();
+  const int nchunks = p.K / 64;
+  for (int t = t0; t < t1; ++t) {
+    const int col = t * 64 + wave * 16 + li;
+    const bf16* brow[1] = {brow_ptr(p, min(col, p.N - 1))};
+    f32x4 acc[MT][1];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    skinny_acc<MT, 1>(arow, brow, kg, 0, nchunks, 1, acc);
+    __syncthreads();   // previous tile's readers are done
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = m * 16 + kg * 4 + j;
+        tile[r][wave * 16 + li] = acc[m][0][j];
+        if (p.logits && m0 + r < Mv) store_logit(p, m0 + r, col, acc[m][0][j]);
+      }
+    __syncthreads();
+    if (row_live) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int cc = c * TPR + my_part;
+        const int gcol = t * 64 + cc;
+        if (gcol < p.N) top.push(tile[my_row][cc], gcol);
+      }
+    }
+  }
+  // merge the TPR lists of each row: tree of pairwise merges through LDS; at step w the list of
+  // part p (p % 2w == w) goes to part p - w through slot my_row * TPR/2 + p / 2w.
+  for (int w = 1; w < TPR; w <<= 1) {
+    __syncthreads();
+    const int slot = my_row * (TPR / 2) + my_part / (2 * w);
+    if ((my_part & (2 * w - 1)) == w) {
+#pragma unroll
+      for (int i = 0; i < TOPK; ++i) { mv[slot][i] = top.v[i]; mi[slot][i] = top.id[i]; }
+    }
+    __syncthreads();
+    if ((my_part & (2 * w - 1)) == 0) {
+#pragma unroll
+      for (int i = 0; i < TOPK; ++i) top.push(mv[slot][i], mi[slot][i]);
+    }
+  }
+  if (my_part == 0 && m0 + my_row < Mv) store_partial(p, m0 + my_row, g, top);
+}
+
+// ---------------------------------------------------------------------------------------
+// tiled: 128 x 128 x 64, LDS double buffer, 2x2 waves of 64x64.
+// ---------------------------------------------------------------------------------------
+constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = TBK + 8;
+
+struct TiledSmem {
+  bf16 ab[2][2][TBM][TLD];   // [buffer][A or B][row][k]
+};
+
+__device__ __forceinline__ void tiled_load(const GemmParams& p, const bf16* const (&ap)[4], const bf16* const (&bp)[4], int kq,
+                                           int c, u32x4 (&ra)[4], u32x4 (&rb)[4]) {
+  const int k = c * TBK + kq;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + k);
+    rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k);
+  }
+}
+
+__device__ __forceinline__ void tiled_store(TiledSmem& sm, int buf, int r0, int kq, const u32x4 (&ra)[4], const u32x4 (&rb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    *reinterpret_cast<u32x4*>(&sm.ab[buf][0][r0 + 32 * i][kq]) = ra[i];
+    *reinterpret_cast<u32x4*>(&sm.ab[buf][1][r0 + 32 * i][kq]) = rb[i];
+  }
+}
+
+__device__ __forceinline__ void tiled_compute(const TiledSmem& sm, int buf, int wm, int wn, int li, int kg, f32x4 (&acc)[4][4]) {
+#pragma unroll
+  for (int ks = 0; ks < TBK / 32; ++ks) {
+    const int k = ks * 32 + kg * 8;
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = *reinterpret_cast<const bf16x8*>(&sm.ab[buf][0][wm * 64 + i * 16 + li][k]);
+      b[i] = *reinterpret_cast<const bf16x8*>(&sm.ab[buf][1][wn * 64 + i * 16 + li][k]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// One 128x128 output tile over k-chunks [c0, c1).
+__device__ __forceinline__ void tiled_tile(const GemmParams& p, TiledSmem& sm, int m0, int n0, int Mv, int c0, int c1,
+                                           f32x4 (&acc)[4][4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, li = lane & 15, kg = lane >> 4;
+  const int r0 = tid >> 3, kq = (tid & 7) * 8;
+  const bf16* ap[4];
+  const bf16* bp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = min(m0 + r0 + 32 * i, Mv - 1);
+    ap[i] = reinterpret_cast<const bf16*>(p.A) + (size_t)r * p.lda;
+    bp[i] = brow_ptr(p, min(n0 + r0 + 32 * i, p.N - 1));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (c0 >= c1) return;
+  u32x4 ra[4], rb[4];
+  tiled_load(p, ap, bp, kq, c0, ra, rb);
+  __syncthreads();   // LDS free (previous tile / epilogue done)
+  tiled_store(sm, 0, r0, kq, ra, rb);
+  __syncthreads();
+  int buf = 0;
+  for (int c = c0; c < c1; ++c) {
+    const bool more = c + 1 < c1;
+    if (more) tiled_load(p, ap, bp, kq, c + 1, ra, rb);
+    tiled_compute(sm, buf, wm, wn, li, kg, acc);
+    if (more) tiled_store(sm, buf ^ 1, r0, kq, ra, rb);
+    __syncthreads();
+    buf ^= 1;
+  }
+}
+
+// PARTIAL: grid x = column tile, y = row tile, z = k-split.
+__global__ __launch_bounds__(256, 2) void gemm_tiled_partial(GemmParams p) {
+  __shared__ TiledSmem sm;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, li = lane & 15, kg = lane >> 4;
+  const int Mv = rows_valid(p);
+  const int m0 = blockIdx.y * TBM, n0 = blockIdx.x * TBN;
+  if (m0 >= Mv) return;
+  const int nchunks = p.K / TBK, s = blockIdx.z;
+  const int c0 = (int)((long)nchunks * s / p.splits), c1 = (int)((long)nchunks * (s + 1) / p.splits);
+  f32x4 acc[4][4];
+  tiled_tile(p, sm, m0, n0, Mv, c0, c1, acc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * 64 + i * 16 + kg * 4 + r;
+        const int col = n0 + wn * 64 + j * 16 + li;
+        if (row < Mv && col < p.N) p.part[((size_t)s * p.M + row) * p.N + col] = acc[i][j][r];
+      }
+}
+
+// TOPK: grid x = group (contiguous range of 128-column tiles), y = row tile.  Each row of the
+// tile is scanned by 2 threads (64 columns each) with a private running top-16.
+__global__ __launch_bounds__(256, 2) void lmhead_topk_tiled(GemmParams p) {
+  __shared__ TiledSmem sm;
+  float (*ep)[TBN + 4] = reinterpret_cast<float (*)[TBN + 4]>(&sm.ab[0][0][0][0]);  // 64 x 132 floats
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, li = lane & 15, kg = lane >> 4;
+  const int Mv = rows_valid(p);
+  const int m0 = blockIdx.y * TBM;
+  if (m0 >= Mv) return;
+  const int g = blockIdx.x, G = gridDim.x;
+  const int ntiles = (p.N + TBN - 1) / TBN;
+  const int t0 = (int)((long)ntiles * g / G), t1 = (int)((long)ntiles * (g + 1) / G);
+  const int my_row = tid >> 1, my_half = tid & 1;
+  const bool row_live = (m0 + my_row < Mv) && ((m0 + my_row) % p.block != 0);
+  Top16 top;
+  top.init();
+  for (int t = t0; t < t1; ++t) {
+    const int n0 = t * TBN;
+    f32x4 acc[4][4];
+    tiled_tile(p, sm, m0, n0, Mv, 0, p.K / TBK, acc);
+    // epilogue in two halves of 64 rows (LDS holds 64 x 132 floats)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();
+      if (wm == half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int rl = i * 16 + kg * 4 + r;
+              const int cl = wn * 64 + j * 16 + li;
+              ep[rl][cl] = acc[i][j][r];
+              if (p.logits && m0 + half * 64 + rl < Mv) store_logit(p, m0 + half * 64 + rl, n0 + cl, acc[i][j][r]);
+            }
+      }
+      __syncthreads();
+      if (row_live && (my_row >> 6) == half) {
+        const int rl = my_row & 63;
+        for (int c = 0; c < 64; ++c) {
+          const int cl = my_half * 64 + c;
+          const int gcol = n0 + cl;
+          if (gcol < p.N) top.push(ep[rl][cl], gcol);
+        }
+      }
+    }
+  }
+  // merge the two lists of each row
+  __syncthreads();
+  float (*mv)[TOPK] = reinterpret_cast<float (*)[TOPK]>(&sm.ab[0][0][0][0]);
+  int (*mi)[TOPK] = reinterpret_cast<int (*)[TOPK]>(&sm.ab[1][0][0][0]);
+  if (my_half == 1) {
+#pragma unroll
+    for (int i = 0; i < TOPK; ++i) { mv[my_row][i] = top.v[i]; mi[my_row][i] = top.id[i]; }
+  }
+  __syncthreads();
+  if (my_half == 0) {
+#pragma unroll
+    for (int i = 0; i < TOPK; ++i) top.push(mv[my_row][i], mi[my_row][i]);
+    if (m0 + my_row < Mv) store_partial(p, m0 + my_row, g, top);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// fp32: plain dot products.  grid x = 64-column block, y = 4-row block.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
+  const int Mv = rows_valid(p);
+  const int col = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (row >= Mv || col >= p.N) return;
+  const float* a = reinterpret_cast<const float*>(p.A) + (size_t)row * p.lda;
+  const int s = col / p.seg_rows;
+  const float* b = reinterpret_cast<const float*>(p.seg[s]) + (size_t)(col - s * p.seg_rows) * p.ldb;
+  float acc = 0.f;
+  for (int k = 0; k < p.K; ++k) acc = fmaf(a[k], b[k], acc);
+  p.part[(size_t)row * p.N + col] = acc;
+}
+
+// ---------------------------------------------------------------------------------------
+// planning + launch
+// ---------------------------------------------------------------------------------------
+static int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
+  GemmPlan pl{};
+  pl.splits = 1;
+  pl.groups = 1;
+  if (!bf16) {
+    pl.kind = 2;
+    pl.grid = dim3((N + 63) / 64, (M + 3) / 4, 1);
+    return pl;
+  }
+  const int nchunks = K / 64;
+  if (M <= 64) {
+    pl.kind = 0;
+    pl.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    const int rt = (M + 16 * pl.mt - 1) / (16 * pl.mt);
+    if (mode == GEMM_TOPK) {
+      const int ntiles = (N + 63) / 64;
+      pl.groups = clampi(1024 / rt, 1, ntiles);
+      pl.grid = dim3(pl.groups, rt, 1);
+    } else {
+      const int ncols = (mode == GEMM_SWIGLU) ? N / 2 : N;
+      const int ct = (ncols + 15) / 16;
+      if (mode == GEMM_PARTIAL) pl.splits = clampi((768 + ct * rt - 1) / (ct * rt), 1, clampi(nchunks / 4, 1, 64));
+      pl.grid = dim3(ct, rt, pl.splits);
+    }
+  } else {
+    pl.kind = 1;
+    const int rt = (M + TBM - 1) / TBM;
+    const int ntiles = (N + TBN - 1) / TBN;
+    if (mode == GEMM_TOPK) {
+      pl.groups = clampi(512 / rt, 1, ntiles);
+      pl.grid = dim3(pl.groups, rt, 1);
+    } else {
+      pl.splits = clampi((512 + ntiles * rt - 1) / (ntiles * rt), 1, clampi(nchunks / 4, 1, 16));
+      pl.grid = dim3(ntiles, rt, pl.splits);
+    }
+  }
+  return pl;
+}
+
+size_t gemm_part_floats(const GemmPlan& pl, int mode, int M, int N) {
+  if (mode == GEMM_TOPK) return (size_t)M * pl.groups * TOPK;
+  if (mode == GEMM_SWIGLU) return 0;
+  return (size_t)pl.splits * M * N;
+}
+
+hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hipStream_t st) {
+  p.splits = pl.splits;
+  p.groups = pl.groups;
+  const dim3 blk(256);
+  if (pl.kind == 2) {
+    hipLaunchKernelGGL(gemm_f32_kernel, pl.grid, blk, 0, st, p);
+    return hipGetLastError();
+  }
+  if (pl.kind == 0) {
+    if (mode == GEMM_TOPK) {
+      if (pl.mt == 1) hipLaunchKernelGGL(lmhead_topk_skinny<1>, pl.grid, blk, 0, st, p);
+      else if (pl.mt == 2) hipLaunchKernelGGL(lmhead_topk_skinny<2>, pl.grid, blk, 0, st, p);
+      else hipLaunchKernelGGL(lmhead_topk_skinny<4>, pl.grid, blk, 0, st, p);
+    } else if (mode == GEMM_SWIGLU) {
+      if (pl.mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<1, GEMM_SWIGLU>), pl.grid, blk, 0, st, p);
+      else if (pl.mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<2, GEMM_SWIGLU>), pl.grid, blk, 0, st, p);
+      else hipLaunchKernelGGL((gemm_skinny_kernel<4, GEMM_SWIGLU>), pl.grid, blk, 0, st, p);
+    } else {
+      if (pl.mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<1, GEMM_PARTIAL>), pl.grid, blk, 0, st, p);
+      else if (pl.mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<2, GEMM_PARTIAL>), pl.grid, blk, 0, st, p);
+      else hipLaunchKernelGGL((gemm_skinny_kernel<4, GEMM_PARTIAL>), pl.grid, blk, 0, st, p);
+    }
+    return hipGetLastError();
+  }
+  if (mode == GEMM_TOPK) hipLaunchKernelGGL(lmhead_topk_tiled, pl.grid, blk, 0, st, p);
+  else hipLaunchKernelGGL(gemm_tiled_partial, pl.grid, blk, 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace dfl

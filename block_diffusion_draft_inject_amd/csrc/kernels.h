@@ -1,0 +1,53 @@
+// Internal launcher declarations for libdflash (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "common.h"
+
+namespace dfl {
+
+constexpr int MAX_SEG = 32;
+
+enum GemmMode { GEMM_PARTIAL = 0, GEMM_SWIGLU = 1, GEMM_TOPK = 2 };
+
+// C[m][n] = sum_k A[m][k] * B_n[k] where B_n is row n of a weight matrix split into
+// equal row segments: row n lives at seg[n / seg_rows] + (n % seg_rows) * ldb.
+struct GemmParams {
+  const void* A;          // [M][lda] activations (dtype)
+  int lda;
+  int M;                  // rows (allocation bound)
+  const int* m_dev;       // optional device row count: rows >= *m_dev - m_off are skipped
+  int m_off;
+  const void* seg[MAX_SEG];
+  int seg_rows;
+  int ldb;
+  int N, K;
+  int splits;             // k-splits (PARTIAL)
+  // PARTIAL: part[s][m][n], row stride N
+  float* part;
+  // SWIGLU: out[m][j] = silu(C[m][j]) * C[m][half + j], j < half
+  void* out;
+  int half;
+  // TOPK (lm_head): per (row, group) top-16 partials; rows whose slot (row % block) is 0 skipped
+  float* tk_val;
+  int* tk_id;
+  int groups;
+  int block;
+  float* logits;          // optional full logits [row/block][block-1][N] for slots >= 1
+};
+
+struct GemmPlan {
+  int kind;      // 0 = skinny, 1 = tiled, 2 = f32 simple
+  int mt;        // skinny row fragments (1,2,4)
+  int splits;
+  int groups;    // TOPK groups
+  dim3 grid;
+};
+
+// Chooses the launch shape; deterministic in (dtype, mode, M, N, K).
+GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K);
+// Bytes of partial output the plan writes (PARTIAL) or top-k partial entries (TOPK).
+size_t gemm_part_floats(const GemmPlan& pl, int mode, int M, int N);
+hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hipStream_t st);
+
+}  // namespace dfl

@@ -1,0 +1,183 @@
+// Argument structs and launchers of the non-GEMM kernels (internal).
+#pragma once
+#include "common.h"
+
+namespace dfl {
+
+// Per-sequence context of one draft call, written by draft_plan_kernel.
+struct SeqCtx {
+  int sid;     // sequence id (clamped into range)
+  int L;       // anchor position = current length
+  int n_ctx;   // number of context positions visible: min(L - base, window)
+  int slot0;   // ring slot of the oldest visible position
+};
+
+struct PlanArgs {
+  int n_seq, max_seqs, window;
+  const int* seq_ids;
+  const int* seq_len;
+  const int* seq_base;
+  int* dev_err;
+  SeqCtx* ctx;
+};
+
+struct RowArgs {
+  int K, d, mask_id, use_conv, final_norm, splits, part_rows, ldy, vocab;
+  int* dev_err;
+  float eps;
+  const int* anchor;
+  const void* embed;
+  const float* h_in;
+  float* h_out;
+  const float* part;
+  const void* post_w;
+  const void* post_b;
+  const void* pre_gain;
+  const void* pre_w;
+  const void* pre_b;
+  void* y;
+};
+
+struct QkvArgs {
+  int K, nh, nkv, dh, N, splits, part_rows;
+  float eps;
+  double log_theta;
+  const SeqCtx* ctx;
+  const float* part;
+  const void* q_gain;
+  const void* k_gain;
+  void* q;
+  void* k;
+  void* v;
+};
+
+struct SwigluArgs {
+  int M, f, splits, part_rows;
+  const float* part;
+  void* out;
+};
+
+struct ReduceArgs {
+  int M, N, splits, part_rows;
+  const int* m_dev;    // optional: rows valid = min(M, *m_dev - m_off)
+  int m_off;
+  const float* part;
+  void* out;
+};
+
+struct InjectArgs {
+  int n_seq, max_new, max_seqs, concat, chunk0;
+  float eps;
+  const int* seq_ids;
+  const int* start_pos;
+  const int* n_new;
+  int* seq_len;
+  int* seq_base;
+  int* dev_err;
+  int* row_off;     // [n_seq + 1]
+  int* row_start;   // [n_seq]
+  int* total;
+  const void* states;
+  const void* gain;
+  void* ubar;
+  int* meta_seq;
+  int* meta_pos;
+};
+
+constexpr int MAX_LAYERS = 16;
+
+struct KvPostArgs {
+  int N, splits, part_rows, nkv, dh, window, max_seqs;
+  float eps;
+  double log_theta;
+  const float* part;
+  const int* meta_seq;
+  const int* meta_pos;
+  const void* k_gain[MAX_LAYERS];
+  void* kcache;
+  void* vcache;
+};
+
+struct ResetArgs {
+  int n, max_seqs;
+  const int* seq_ids;
+  int* seq_len;
+  int* seq_base;
+  int* dev_err;
+};
+
+struct MergeArgs {
+  int K, ncand;
+  const float* vals;   // [n_seq*K][ncand]
+  const int* ids;      // same shape or nullptr (id = index)
+  int* out_ids;        // [n_seq][K-1][16]
+  float* out_vals;
+  float* logits_out;   // raw mode only: optional copy of the candidate row [n_seq][K-1][ncand]
+};
+
+struct AttnArgs {
+  int K, nh, nkv, dh, window, max_seqs, chunks, n_layers_stride, layer;
+  float scale;
+  const SeqCtx* ctx;
+  const void* q;       // [rows][nh*dh]
+  const void* kb;      // [rows][nkv*dh]
+  const void* vb;
+  const void* kcache;  // [layers][max_seqs][nkv][window][dh]
+  const void* vcache;
+  float* o_part;       // [n_seq][nkv][chunks][R][dh]
+  float* m_part;       // [n_seq][nkv][chunks][R]
+  float* l_part;
+  void* o;             // [rows][nh*dh]
+};
+
+struct SelectArgs {
+  int K, d, r, mode, vocab;
+  int* dev_err;
+  const int* anchor;
+  const int* topk_ids;
+  const float* topk_logits;
+  const void* h_final;
+  const void* A;
+  const void* B;
+  const void* WH;
+  int* path;
+  float* score;
+  float* margin;
+};
+
+struct VerifyArgs {
+  int n_seq, K;
+  const int* draft;
+  const int* target;
+  int* n_acc;
+  int* n_commit;
+  int* committed;
+  int* next_anchor;
+};
+
+struct SynthArgs {
+  int n_seq, K, vocab;
+  float p;
+  unsigned long long seed;
+  long long* counter;
+  const int* draft;
+  int* target;
+};
+
+hipError_t launch_draft_plan(const PlanArgs& a, hipStream_t st);
+hipError_t launch_embed_pre(bool bf, const RowArgs& a, int rows, hipStream_t st);
+hipError_t launch_post_pre(bool bf, const RowArgs& a, int rows, hipStream_t st);
+hipError_t launch_qkv_post(bool bf, const QkvArgs& a, int rows, hipStream_t st);
+hipError_t launch_swiglu(bool bf, const SwigluArgs& a, hipStream_t st);
+hipError_t launch_reduce_store(bool bf, const ReduceArgs& a, hipStream_t st);
+hipError_t launch_inject_plan(const InjectArgs& a, hipStream_t st);
+hipError_t launch_concat_norm(bool bf, const InjectArgs& a, int rows, hipStream_t st);
+hipError_t launch_kv_post(bool bf, const KvPostArgs& a, int rows, int heads, hipStream_t st);
+hipError_t launch_reset(const ResetArgs& a, hipStream_t st);
+hipError_t launch_topk_merge(const MergeArgs& a, int out_rows, hipStream_t st);
+hipError_t launch_attention(bool bf, const AttnArgs& a, int n_seq, hipStream_t st);
+hipError_t launch_select(bool bf, const SelectArgs& a, int n_seq, hipStream_t st);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
+hipError_t launch_synth(const SynthArgs& a, hipStream_t st);
+
+}  // namespace dfl

@@ -1,0 +1,230 @@
+/*
+ * libdflash -- the DFlash drafter's single-pass block draft on one AMD Instinct MI355X (gfx950).
+ *
+ * A cycle of block-diffusion speculative decoding, as the pages state it ("Architecture",
+ * kb.ekarisky.com, DFlash 2: sequence diagram "One Cycle, Step by Step" and flowchart
+ * "Draft-Verify Cycle"):
+ *   (1) inject target hidden states into the drafter's KV cache       -> dflash_inject_kv
+ *   (2) predict the whole block in one pass, top-16 per position      -> dflash_draft_block
+ *   (3) candidate lists + last verified token -> one coherent path    -> dflash_select_path
+ *   (4) accept the longest valid prefix plus one bonus token          -> dflash_verify_greedy
+ * The target model's own verify pass is not part of this library: step (4) takes the target's
+ * argmax tokens as input.
+ *
+ * Conventions for every call below
+ *   - Pointers are DEVICE pointers unless marked (host).  Arrays are dense, row-major.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls only
+ *     enqueue work; results are valid once the stream has been synchronised.  No call
+ *     synchronises, allocates or frees device memory; all scratch lives in the caller's
+ *     workspace buffer.  Calls on one handle must be serialised by the caller (one stream,
+ *     or explicit ordering); concurrent calls that share a handle race on its workspace.
+ *   - Ids are int32.  Logits, scores and margins are fp32.  Weights, target states and
+ *     the activations the library stores use the handle's dtype (fp32 or bf16).
+ *   - Linear weights are [out][in] (one output row per line).
+ *   - Errors: every check that the host can make (null pointers, sizes, counts above the
+ *     handle's maxima, unsupported shapes) returns a negative status BEFORE anything is
+ *     enqueued; dflash_last_error() then gives a message.  Nothing throws across this ABI.
+ *     Problems only the device can see (a sequence id or n_new out of range) are clamped
+ *     or skipped and recorded in a device error word (dflash_get_device_error).
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DFLASH_API __attribute__((visibility("default")))
+#else
+#define DFLASH_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_E_INVALID = -1,     /* null pointer, bad enum, inconsistent argument            */
+  DFLASH_E_SHAPE = -2,       /* a size outside what the handle was created for           */
+  DFLASH_E_UNSUPPORTED = -3, /* a configuration the kernels do not implement              */
+  DFLASH_E_HIP = -4,         /* a HIP runtime call failed (message has the HIP error)     */
+  DFLASH_E_STATE = -5        /* handle misuse (e.g. destroyed twice)                      */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+typedef enum { DFLASH_SELECT_VITERBI = 0, DFLASH_SELECT_GREEDY = 1 } dflash_select_mode;
+
+/* Drafter shape (host struct, copied by dflash_create).
+ *  - hidden d, n_heads x head_dim query heads, n_kv_heads KV heads (grouped-query attention:
+ *    query head i reads KV head floor(i * n_kv_heads / n_heads)), ffn = SwiGLU width, vocab V.
+ *  - n_taps tapped target layers of width target_hidden each; their concatenation
+ *    (n_taps * target_hidden wide) is RMS-normalised and projected to d ("Z Lab releases
+ *    DFlash 2 ...", section "Persistent Conditioning Through Target KV Injection").
+ *  - block_size K: slot 0 holds the anchor (last verified token), slots 1..K-1 hold MASK
+ *    ("Architecture", Component Breakdown row "Block attention mask").  K-1 drafts per block.
+ *  - window W: the block sees the last min(L, W) injected positions ("Architecture",
+ *    Component Breakdown row "DFlash drafter backbone": sliding window 1024).
+ *  - topk must be 16 ("Architecture", flowchart "Drafter": top-16 candidates per position).
+ *  - sel_rank r: width of the selector's A/B token tables and context gate.
+ *  - use_conv: 1 = two-tap dynamic convolution around every attention and MLP sublayer
+ *    ("Architecture", section "Problem 2 -- Suffix decay is local").
+ *  - rope_theta: rotary base for the rotate-half RoPE applied after the per-head q/k norm. */
+typedef struct {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  int32_t n_taps, target_hidden;
+  int32_t block_size, window, topk, sel_rank, mask_id, use_conv;
+  float rms_eps, rope_theta;
+  dflash_dtype dtype;
+} dflash_config;
+
+/* Per-layer weight tensors, in this order, in dflash_weights.layers[l * DFLASH_LAYER_TENSORS + i]. */
+typedef enum {
+  DFLASH_L_ATTN_NORM = 0,   /* [d]                 pre-attention RMSNorm gain               */
+  DFLASH_L_WQ,              /* [n_heads*head_dim][d]                                          */
+  DFLASH_L_WK,              /* [n_kv*head_dim][d]  also projects the injected context        */
+  DFLASH_L_WV,              /* [n_kv*head_dim][d]  also projects the injected context        */
+  DFLASH_L_Q_NORM,          /* [head_dim]          per-head q RMSNorm gain                   */
+  DFLASH_L_K_NORM,          /* [head_dim]          per-head k RMSNorm gain (block and ctx)   */
+  DFLASH_L_WO,              /* [d][n_heads*head_dim]                                          */
+  DFLASH_L_MLP_NORM,        /* [d]                                                            */
+  DFLASH_L_W_GATE,          /* [ffn][d]                                                       */
+  DFLASH_L_W_UP,            /* [ffn][d]                                                       */
+  DFLASH_L_W_DOWN,          /* [d][ffn]                                                       */
+  DFLASH_L_CONV_ATTN_PRE_W, /* [2][d]  conv taps k_t = sigmoid(W x_t + b): before attention   */
+  DFLASH_L_CONV_ATTN_PRE_B, /* [2]                                                            */
+  DFLASH_L_CONV_ATTN_POST_W,/* [2][d]  after attention (on the O-projection output)           */
+  DFLASH_L_CONV_ATTN_POST_B,/* [2]                                                            */
+  DFLASH_L_CONV_MLP_PRE_W,  /* [2][d]  before the MLP                                          */
+  DFLASH_L_CONV_MLP_PRE_B,  /* [2]                                                            */
+  DFLASH_L_CONV_MLP_POST_W, /* [2][d]  after the MLP                                           */
+  DFLASH_L_CONV_MLP_POST_B, /* [2]                                                            */
+  DFLASH_LAYER_TENSORS
+} dflash_layer_tensor;
+
+/* Borrowed device pointers (host struct, copied by dflash_create; the caller keeps the memory
+ * alive and unchanged for the handle's life).  embed and lm_head are [V][d] (shared with the
+ * target, "Architecture", Component Breakdown row "Target LLM"); sel_A / sel_B are [V][r]
+ * token tables and sel_WH is [r][d] (context gate) of the path selector. */
+typedef struct {
+  const void* embed;        /* [V][d]                       */
+  const void* lm_head;      /* [V][d]                       */
+  const void* concat_norm;  /* [n_taps*target_hidden]       */
+  const void* fc;           /* [d][n_taps*target_hidden]    */
+  const void* final_norm;   /* [d]                          */
+  const void* sel_A;        /* [V][r]                       */
+  const void* sel_B;        /* [V][r]                       */
+  const void* sel_WH;       /* [r][d]                       */
+  const void* const* layers;/* (host) n_layers*DFLASH_LAYER_TENSORS device pointers */
+} dflash_weights;
+
+/* Where things sit inside the caller's kv_cache buffer (byte offsets).
+ * K and V caches are [n_layers][max_seqs][n_kv_heads][window][head_dim] of dtype: position p
+ * of a sequence lives in ring slot p mod window.  seq_len[s] is one past the last injected
+ * position (= the anchor position of the next draft); seq_base[s] is the first position
+ * injected since the sequence was last (re)started.  device_error is one int32 word. */
+typedef struct {
+  size_t k_offset, v_offset, seq_len_offset, seq_base_offset, device_error_offset, total_bytes;
+} dflash_kv_layout;
+
+typedef struct dflash_handle dflash_handle;
+
+/* Validates a configuration; DFLASH_OK if the kernels support it. */
+DFLASH_API dflash_status dflash_config_check(const dflash_config* cfg);
+
+/* Size of the caller-owned KV cache buffer for `max_seqs` sequences (0 on invalid input). */
+DFLASH_API size_t dflash_kv_cache_bytes(const dflash_config* cfg, int32_t max_seqs);
+DFLASH_API dflash_status dflash_kv_cache_layout(const dflash_config* cfg, int32_t max_seqs, dflash_kv_layout* out /* host */);
+
+/* Size of the caller-owned workspace for up to `max_seqs` sequences, blocks of up to `max_batch`
+ * sequences and injection passes of up to `max_inject_rows` rows (an injection call with more
+ * rows is processed in several passes).  0 on invalid input. */
+DFLASH_API size_t dflash_workspace_bytes(const dflash_config* cfg, int32_t max_seqs, int32_t max_batch, int32_t max_inject_rows);
+
+/* Creates a handle.  kv_cache (kv_bytes) and workspace (ws_bytes) are caller-owned device
+ * buffers of at least the sizes above.  The caller must zero the seq_len/seq_base/device_error
+ * words of kv_cache before first use (or call dflash_reset_seqs).  Host-side only: enqueues
+ * nothing. */
+DFLASH_API dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, int32_t max_seqs,
+                            int32_t max_batch, int32_t max_inject_rows, void* kv_cache, size_t kv_bytes,
+                            void* workspace, size_t ws_bytes, dflash_handle** out /* host */);
+DFLASH_API dflash_status dflash_destroy(dflash_handle* h);   /* frees host state only */
+
+/* Marks n_seq sequences empty (seq_len = seq_base = 0) and clears the device error word. */
+DFLASH_API dflash_status dflash_reset_seqs(dflash_handle* h, int32_t n_seq, const int32_t* seq_ids, void* stream);
+
+/* (1) KV injection.  For each i < n_seq, appends n_new[i] (device, 0..max_new) target-state rows
+ * of sequence seq_ids[i] at absolute positions start_pos[i] .. start_pos[i]+n_new[i]-1.
+ * start_pos may be NULL: append at the sequence's current length.  A start position other
+ * than the current length restarts that sequence's context there.
+ * target_hidden: [n_seq][max_new][n_taps*target_hidden] (dtype): row (i, r) is the
+ * concatenation of the tapped target layers at that position.
+ * Computes u_bar = RMSNorm(row) * concat_norm, c = fc u_bar, then for every layer
+ * K = RoPE_p(RMSNorm_head(W_k c) * k_norm), V = W_v c into ring slot p mod window
+ * ("Z Lab releases DFlash 2 ...", section "Persistent Conditioning Through Target KV
+ * Injection"; "Architecture", section "Internals Worth Knowing": projection ahead of the
+ * draft pass with fused norm + RoPE). */
+DFLASH_API dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* seq_ids, const int32_t* start_pos,
+                               const int32_t* n_new, int32_t max_new, const void* target_hidden, void* stream);
+
+/* (2) One forward pass over the block [anchor_ids[i], MASK x (K-1)] of each sequence at
+ * positions L..L+K-1 (L = the sequence's current length): embed, then per layer
+ * h += Conv(Attn(Conv(RMSNorm h))), h += Conv(MLP(Conv(RMSNorm h))) with non-causal attention
+ * over the K block slots plus the last min(L - base, window) injected positions, final
+ * RMSNorm, shared lm_head, top-16 per draft slot ("Architecture", flowchart "Drafter" and
+ * Component Breakdown).  Outputs (slot t = 1..K-1 at index t-1):
+ *   topk_ids / topk_logits [n_seq][K-1][16], ordered by (logit desc, id asc);
+ *   h_final [n_seq][K][d] (dtype) -- final-normed hidden states, input of the selector;
+ *   logits  [n_seq][K-1][V] fp32 or NULL -- full logits for checking only (extra HBM writes). */
+DFLASH_API dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t* seq_ids, const int32_t* anchor_ids,
+                                 int32_t* topk_ids, float* topk_logits, void* h_final, float* logits, void* stream);
+
+/* (3) Path selection over the candidate lattice ("Architecture", section "Problem 1 --
+ * Independent picks are incoherent"): S_t(a, b) = U_t(b) + sum_j A[a,j] * H_t[j] * B[b,j] with
+ * U_t the drafter logit, H_t = sigmoid(W_H h_final[t]); slot 1's predecessor is the anchor.
+ * VITERBI: the max-scoring path (2-best list Viterbi; margin = best - second-best path score).
+ * GREEDY: follow the best successor from the anchor (margin = smallest best-minus-second gap).
+ * Ties go to the smaller candidate index.  path_ids [n_seq][K-1]; path_score, margin [n_seq]
+ * may be NULL. */
+DFLASH_API dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t* anchor_ids, const int32_t* topk_ids,
+                                 const float* topk_logits, const void* h_final, dflash_select_mode mode,
+                                 int32_t* path_ids, float* path_score, float* margin, void* stream);
+
+/* (4) Greedy longest-prefix verification ("Architecture", section "Speculative Decoding
+ * Context" and the sequence diagram's last step: accepted prefix + 1 bonus token).
+ * draft_ids [n_seq][K-1] = d_1..d_{K-1}; target_argmax [n_seq][K] = g_0..g_{K-1} (g_i is the
+ * target's choice after slot i).  n = largest m with d_i == g_{i-1} for all i <= m.
+ * Outputs: n_accepted [n_seq] = n; n_commit [n_seq] = n+1 (may be NULL; usable as the next
+ * call's n_new); committed [n_seq][K] = d_1..d_n, g_n, then -1; next_anchor [n_seq] = g_n. */
+DFLASH_API dflash_status dflash_verify_greedy(int32_t n_seq, int32_t block_size, const int32_t* draft_ids,
+                                   const int32_t* target_argmax, int32_t* n_accepted, int32_t* n_commit,
+                                   int32_t* committed, int32_t* next_anchor, void* stream);
+
+/* Benchmark workload helper, not part of the drafter: stands in for a target model's verify
+ * pass.  For i = 1..K-1, g_{i-1} = d_i with probability match_prob, else a different token;
+ * g_{K-1} is uniform.  Randomness: splitmix64 of (seed, *counter, sequence, slot); *counter
+ * (device int64) is incremented once per call.  Runs as one workgroup: n_seq <= 1024. */
+DFLASH_API dflash_status dflash_synth_target_argmax(int32_t n_seq, int32_t block_size, int32_t vocab, const int32_t* draft_ids,
+                                         float match_prob, uint64_t seed, int64_t* counter,
+                                         int32_t* target_argmax, void* stream);
+
+/* Kernel timing for measurement: while enabled, each dflash_draft_block records a pair of HIP
+ * events around its lm_head + top-16 kernel on the call's stream (pair index advances modulo
+ * capacity).  dflash_timing_read waits for the recorded pairs and returns their summed
+ * milliseconds and count, then starts a new accumulation.  capacity 0 disables. */
+DFLASH_API dflash_status dflash_timing_enable(dflash_handle* h, int32_t capacity);
+DFLASH_API dflash_status dflash_timing_read(dflash_handle* h, double* total_ms /* host */, int32_t* count /* host */);
+
+/* Reads (and keeps) the device error word; synchronises the device.  0 = none.
+ * Bits: 1 = sequence id out of range, 2 = n_new outside [0, max_new], 4 = negative start_pos,
+ * 8 = anchor token id outside [0, vocab). */
+DFLASH_API dflash_status dflash_get_device_error(dflash_handle* h, int32_t* code /* host */);
+
+DFLASH_API const char* dflash_status_string(dflash_status s);
+DFLASH_API const char* dflash_last_error(void);   /* thread-local message of the last failing call */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

@@ -1,0 +1,230 @@
+"""Shared GPU-vs-oracle parity machinery (test infrastructure: imports the oracle).
+
+Every comparison runs the oracle on the same seeded inputs as the HIP path; where a stage's
+input is itself a GPU output (the selector's candidate lists, the verifier's draft), the
+oracle stage is run on the GPU's own inputs (stage-wise parity)."""
+from __future__ import annotations
+
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from block_diffusion_draft_inject_amd import binding as B  # noqa: E402
+from block_diffusion_draft_inject_amd import synth  # noqa: E402
+from oracle import dflash_oracle as O  # noqa: E402
+
+# Tolerances.  Logits: max-abs 3e-2 for bf16 drafters (the stated bound), 1e-4 for fp32.
+LOGIT_TOL = {"bf16": 3e-2, "f32": 1e-4}
+TIE_BAND = 1e-3          # top-16 ids may differ only between candidates this close in value
+MARGIN_GATE = 1e-3       # paths must match exactly where the top-two margin exceeds this
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def weights64(w):
+    out = {k: v.values.astype(np.float64) for k, v in w.items() if k != "layers"}
+    out["layers"] = [{k: v.values.astype(np.float64) for k, v in lw.items()} for lw in w["layers"]]
+    return out
+
+
+def oracle_mode(cfg):
+    return "bf16" if cfg.dtype == "bf16" else "exact"
+
+
+class Case:
+    """One drafter on the GPU plus its oracle twin."""
+
+    def __init__(self, cfg, max_seqs, max_batch, max_inject_rows=1024, selector_stress=False, device="cuda"):
+        import torch
+        self.torch = torch
+        self.cfg = cfg
+        t0 = time.time()
+        self.w = synth.make_weights(cfg, selector_stress=selector_stress)
+        self.W64 = weights64(self.w)
+        self.dev_w = B.upload_weights(self.w, cfg.dtype, device)
+        self.d = B.Drafter(cfg, self.dev_w, max_seqs, max_batch, max_inject_rows, device)
+        self.caches = {}
+        self.device = device
+        log(f"[case] {cfg.name}: weights ready in {time.time() - t0:.1f}s")
+
+    def tensor(self, a, dtype=None):
+        t = self.torch.as_tensor(np.ascontiguousarray(a))
+        if dtype is not None:
+            t = t.to(dtype)
+        return t.to(self.device)
+
+    def states_tensor(self, per_seq_rows, max_new):
+        """[n_seq][max_new][concat] device tensor from per-sequence Tensor rows (padded)."""
+        cfg = self.cfg
+        n = len(per_seq_rows)
+        if cfg.dtype == "bf16":
+            buf = np.zeros((n, max_new, cfg.concat_width), dtype=np.uint16)
+        else:
+            buf = np.zeros((n, max_new, cfg.concat_width), dtype=np.float32)
+        for i, t in enumerate(per_seq_rows):
+            if t is not None and t.storage.shape[0]:
+                buf[i, : t.storage.shape[0]] = t.storage
+        if cfg.dtype == "bf16":
+            return self.torch.from_numpy(buf.view(np.int16)).to(self.device).view(self.torch.bfloat16)
+        return self.torch.from_numpy(buf).to(self.device)
+
+    def reset(self, seq_ids):
+        self.d.dflash_reset_seqs(self.tensor(np.asarray(seq_ids, dtype=np.int32)))
+        for s in seq_ids:
+            self.caches[int(s)] = O.DraftCache(self.cfg.n_layers)
+
+    def inject(self, seq_ids, positions_per_seq, start_pos=True, states_fn=None):
+        """Injects states of the given absolute positions (contiguous per sequence) on both sides."""
+        cfg = self.cfg
+        rows = []
+        for s, pos in zip(seq_ids, positions_per_seq):
+            pos = np.asarray(pos, dtype=np.int64)
+            st = (synth.target_states(cfg, int(s), pos) if states_fn is None else states_fn(int(s), pos))
+            rows.append(st)
+            if pos.size:
+                O.inject(cfg, self.W64, self.caches[int(s)], pos, st.values, oracle_mode(cfg))
+        n_new = np.array([len(p) for p in positions_per_seq], dtype=np.int32)
+        max_new = int(max(1, n_new.max()))
+        sp = np.array([int(p[0]) if len(p) else 0 for p in positions_per_seq], dtype=np.int32)
+        self.d.dflash_inject_kv(self.tensor(np.asarray(seq_ids, dtype=np.int32)), self.tensor(n_new), max_new,
+                                self.states_tensor(rows, max_new), start_pos=self.tensor(sp) if start_pos else None)
+
+    def draft(self, seq_ids, anchors, logits=True):
+        torch = self.torch
+        n = len(seq_ids)
+        out = self.d.outputs(n, logits=logits)
+        self.d.dflash_draft_block(self.tensor(np.asarray(seq_ids, dtype=np.int32)),
+                                  self.tensor(np.asarray(anchors, dtype=np.int32)),
+                                  out["topk_ids"], out["topk_logits"], out["h_final"], out["logits"])
+        torch.cuda.synchronize()
+        res = {k: (None if v is None else (v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy()))
+               for k, v in out.items()}
+        res["_dev"] = out
+        return res
+
+    def select(self, anchors, dev_out, mode):
+        torch = self.torch
+        n = len(anchors)
+        K = self.cfg.block_size
+        path = torch.empty((n, K - 1), dtype=torch.int32, device=self.device)
+        score = torch.empty(n, dtype=torch.float32, device=self.device)
+        margin = torch.empty(n, dtype=torch.float32, device=self.device)
+        self.d.dflash_select_path(self.tensor(np.asarray(anchors, dtype=np.int32)), dev_out["topk_ids"],
+                                  dev_out["topk_logits"], dev_out["h_final"], mode, path, score, margin)
+        torch.cuda.synchronize()
+        return path.cpu().numpy(), score.cpu().numpy(), margin.cpu().numpy()
+
+    def verify(self, draft, target):
+        torch = self.torch
+        n, km1 = draft.shape
+        K = km1 + 1
+        nacc = torch.empty(n, dtype=torch.int32, device=self.device)
+        ncom = torch.empty(n, dtype=torch.int32, device=self.device)
+        com = torch.empty((n, K), dtype=torch.int32, device=self.device)
+        nxt = torch.empty(n, dtype=torch.int32, device=self.device)
+        B.dflash_verify_greedy(n, K, self.tensor(draft.astype(np.int32)), self.tensor(target.astype(np.int32)),
+                               nacc, ncom, com, nxt)
+        torch.cuda.synchronize()
+        return nacc.cpu().numpy(), ncom.cpu().numpy(), com.cpu().numpy(), nxt.cpu().numpy()
+
+
+# ------------------------------------------------------------------------------ checks
+
+def check_kv(case, seq_ids, sample_layers=None, max_positions=64):
+    """Cache contents vs the oracle for (a sample of) the positions each ring holds."""
+    cfg = case.cfg
+    k, v, sl, sb = case.d.kv_views()
+    torch = case.torch
+    torch.cuda.synchronize()
+    sl = sl.cpu().numpy()
+    sb = sb.cpu().numpy()
+    worst = 0.0
+    same = tot = 0
+    layers = range(cfg.n_layers) if sample_layers is None else sample_layers
+    for s in seq_ids:
+        cache = case.caches[int(s)]
+        assert sl[s] == cache.length, (s, sl[s], cache.length)
+        held = [p for p in cache.positions() if p >= cache.length - cfg.window]
+        if len(held) > max_positions:
+            idx = np.linspace(0, len(held) - 1, max_positions).round().astype(int)
+            held = [held[i] for i in idx]
+        for l in layers:
+            kc = k[l, s].float().cpu().numpy()
+            vc = v[l, s].float().cpu().numpy()
+            for p in held:
+                slot = p % cfg.window
+                for got, ref in ((kc[:, slot], cache.k[l][p]), (vc[:, slot], cache.v[l][p])):
+                    scale = max(1e-30, float(np.sqrt(np.mean(ref * ref))))
+                    worst = max(worst, float(np.max(np.abs(got - ref))) / scale)
+                    same += int(np.sum(got == ref))
+                    tot += got.size
+    return worst, same / max(1, tot)
+
+
+def check_draft(case, seq_ids, anchors, res, band=TIE_BAND):
+    """Logits, top-16 (vs the GPU's own logits, exactly; vs the oracle, up to near-ties)."""
+    cfg = case.cfg
+    errs = []
+    o_all = []
+    for b, (s, a) in enumerate(zip(seq_ids, anchors)):
+        o = O.draft_block(cfg, case.W64, case.caches[int(s)], int(a), oracle_mode(cfg))
+        o_all.append(o)
+        if res.get("logits") is not None:
+            errs.append(float(np.max(np.abs(res["logits"][b] - o["logits"]))))
+            for t in range(cfg.block_size - 1):
+                lg = res["logits"][b, t].astype(np.float64)
+                ref = np.argsort(-lg, kind="stable")[:16]
+                assert np.array_equal(res["topk_ids"][b, t], ref), ("own-logit top-16", b, t)
+                assert np.array_equal(res["topk_logits"][b, t], res["logits"][b, t][ref])
+        for t in range(cfg.block_size - 1):
+            gset, oset = set(res["topk_ids"][b, t].tolist()), set(o["topk_ids"][t].tolist())
+            if gset != oset:
+                kth = o["topk_logits"][t][-1]
+                for i in gset ^ oset:
+                    assert abs(o["logits"][t][i] - kth) <= band, ("top-16 set", b, t, i, o["logits"][t][i] - kth)
+        hf_err = float(np.max(np.abs(res["h_final"][b] - o["h_final"])))
+        errs.append(0.0)
+        assert hf_err < 0.1, ("h_final", b, hf_err)
+    return (max(errs) if errs else 0.0), o_all
+
+
+def check_select(case, anchors, res, gpu_path, gpu_score, gpu_margin, mode_name):
+    """Selector on the GPU's own lattice: exact where the oracle margin exceeds the gate;
+    elsewhere the GPU path must be (near-)optimal under the oracle's scores."""
+    cfg = case.cfg
+    n_checked = 0
+    for b, a in enumerate(anchors):
+        ids = res["topk_ids"][b].astype(np.int64)
+        lg = res["topk_logits"][b].astype(np.float64)
+        hf = res["h_final"][b].astype(np.float64)
+        o = O.select_path(cfg, case.W64, int(a), ids, lg, hf, mode_name)
+        assert abs(o["score"] - gpu_score[b]) <= MARGIN_GATE, (b, o["score"], gpu_score[b])
+        if o["margin"] > MARGIN_GATE:
+            assert np.array_equal(o["path_ids"], gpu_path[b]), (b, o["path_ids"], gpu_path[b])
+            assert abs(o["margin"] - gpu_margin[b]) <= MARGIN_GATE
+            n_checked += 1
+        else:
+            # several paths are optimal within the band: the GPU's must score within it
+            S = O.pair_scores(cfg, case.W64, int(a), ids, lg, hf)
+            idx = [int(np.where(ids[t] == gpu_path[b][t])[0][0]) for t in range(cfg.block_size - 1)]
+            sc = S[0][0, idx[0]] + sum(S[t][idx[t - 1], idx[t]] for t in range(1, len(idx)))
+            assert sc >= o["score"] - 2 * MARGIN_GATE
+    return n_checked
+
+
+def check_verify(case, draft, target):
+    nacc, ncom, com, nxt = case.verify(draft, target)
+    for b in range(draft.shape[0]):
+        n, c, a = O.verify_greedy(draft[b], target[b])
+        assert nacc[b] == n and ncom[b] == n + 1 and nxt[b] == a, b
+        assert np.array_equal(com[b], c), b
+    return nacc

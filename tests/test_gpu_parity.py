@@ -1,0 +1,132 @@
+"""GPU parity: every libdflash entry point against the CPU oracle on the same seeded inputs.
+
+Small drafters here span several GEMM tiles, ragged contexts, ring wrap-around, restarted
+sequences, both GEMM paths (weight-streaming for <= 64 rows, LDS-tiled above) and both
+selector modes."""
+import numpy as np
+import pytest
+
+from block_diffusion_draft_inject_amd import binding as B
+from block_diffusion_draft_inject_amd import synth
+from oracle import dflash_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+MID = synth.DraftConfig(name="mid_bf16", n_layers=2, hidden=512, n_heads=8, n_kv_heads=2, head_dim=128, ffn=1024,
+                        vocab=8192, n_taps=2, target_hidden=512, block_size=16, sel_rank=16, mask_id=8191,
+                        dtype="bf16", batch=8, window=64)
+
+
+@pytest.fixture(scope="module")
+def H():
+    import parity_harness as H
+    return H
+
+
+def _prefill(case, seq_ids, spans):
+    """spans: per sequence (first, L).  Injects in two calls (explicit start, then append)."""
+    case.reset(seq_ids)
+    first = [np.arange(f, f + (L - f) // 2 + 1) for f, L in spans]
+    case.inject(seq_ids, first, start_pos=True)
+    rest = [np.arange(f + (L - f) // 2 + 1, L) for f, L in spans]
+    case.inject(seq_ids, rest, start_pos=False)
+
+
+def _full_check(H, case, seq_ids, spans, anchors, mode_names=("viterbi", "greedy")):
+    cfg = case.cfg
+    _prefill(case, seq_ids, spans)
+    worst, same = H.check_kv(case, seq_ids)
+    H.log(f"[kv] {cfg.name}: worst rel err {worst:.2e}, bit-equal {same:.4f}")
+    assert worst <= 1e-2 and same >= 0.99
+    res = case.draft(seq_ids, anchors, logits=True)
+    err, _ = H.check_draft(case, seq_ids, anchors, res)
+    H.log(f"[draft] {cfg.name}: max |logit err| {err:.2e}")
+    assert err <= H.LOGIT_TOL[cfg.dtype]
+    for mode_name in mode_names:
+        mode = B.SELECT_VITERBI if mode_name == "viterbi" else B.SELECT_GREEDY
+        path, score, margin = case.select(anchors, res["_dev"], mode)
+        n = H.check_select(case, anchors, res, path, score, margin, mode_name)
+        H.log(f"[select] {cfg.name} {mode_name}: {n}/{len(anchors)} above the margin gate")
+        match, alt, last = synth.match_draws(cfg.replace(batch=len(anchors)), 0)
+        tgt = synth.stand_in_target(path, match, alt, last, cfg.vocab)
+        nacc = H.check_verify(case, path.astype(np.int64), tgt)
+        H.log(f"[verify] {cfg.name} {mode_name}: accepted {nacc.tolist()}")
+    return res
+
+
+def test_mid_bf16_weight_streaming_path(H):
+    case = H.Case(MID, max_seqs=8, max_batch=8, max_inject_rows=48)
+    seq_ids = [5, 0, 3]
+    spans = [(0, 100), (0, 40), (1000, 1070)]     # ring wrap, short context, restarted at 1000
+    _full_check(H, case, seq_ids, spans, anchors=[17, 8000, 4095])
+
+
+def test_mid_bf16_tiled_path_and_ragged_batch(H):
+    case = H.Case(MID, max_seqs=8, max_batch=8, max_inject_rows=256)
+    seq_ids = list(range(8))
+    rng = np.random.default_rng(1)
+    Ls = rng.integers(1, 200, size=8)
+    Ls[2] = 1      # a single context token
+    spans = [(0, int(L)) for L in Ls]
+    anchors = rng.integers(0, MID.vocab - 1, size=8).tolist()
+    _full_check(H, case, seq_ids, spans, anchors)
+
+
+def test_mid_bf16_selector_stress(H):
+    """A, B ~ N(0,1): the pair term dominates, Viterbi != greedy != per-position argmax."""
+    case = H.Case(MID, max_seqs=4, max_batch=4, max_inject_rows=64, selector_stress=True)
+    _full_check(H, case, [0, 1, 2, 3], [(0, 70), (0, 20), (0, 64), (5, 90)], anchors=[1, 2, 3, 4])
+
+
+def test_tiny_fp32_drafter(H):
+    """2 layers, hidden 256, 4x64 heads, vocab 4096, 3x512 taps, context 128, K=8, batch 1."""
+    cfg = synth.WORKLOADS["tiny_fp32"]
+    case = H.Case(cfg, max_seqs=1, max_batch=1, max_inject_rows=128)
+    anchors = synth.anchors(cfg).tolist()
+    _full_check(H, case, [0], [(0, 128)], anchors)
+
+
+def test_tiny_fp32_no_conv_and_empty_context(H):
+    cfg = synth.WORKLOADS["tiny_fp32"].replace(use_conv=False)
+    case = H.Case(cfg, max_seqs=2, max_batch=2, max_inject_rows=16)
+    case.reset([0, 1])
+    case.inject([0, 1], [np.arange(0, 5), np.arange(0, 0)], start_pos=True)
+    res = case.draft([0, 1], [7, 9], logits=True)
+    err, _ = H.check_draft(case, [0, 1], [7, 9], res)
+    assert err <= H.LOGIT_TOL["f32"]
+
+
+def test_device_error_word(H):
+    case = H.Case(MID, max_seqs=2, max_batch=2, max_inject_rows=16)
+    case.reset([0, 1])
+    assert case.d.dflash_get_device_error() == 0
+    import torch
+    ids = torch.tensor([0, 7], dtype=torch.int32, device="cuda")          # 7 is out of range
+    n_new = torch.tensor([2, 2], dtype=torch.int32, device="cuda")
+    st = case.states_tensor([None, None], 2)
+    case.d.dflash_inject_kv(ids, n_new, 2, st)
+    assert case.d.dflash_get_device_error() & 1
+    case.reset([0, 1])
+    n_new = torch.tensor([5, 1], dtype=torch.int32, device="cuda")        # 5 > max_new
+    case.d.dflash_inject_kv(torch.tensor([0, 1], dtype=torch.int32, device="cuda"), n_new, 2, st)
+    assert case.d.dflash_get_device_error() & 2
+    _, _, sl, _ = case.d.kv_views()
+    assert sl[:2].cpu().tolist() == [2, 1]                                # clamped to max_new
+
+
+def test_synth_target_matches_rule(H):
+    import torch
+    K, V, n = 8, 1000, 512
+    d = torch.randint(0, V, (n, K - 1), dtype=torch.int32, device="cuda")
+    ctr = torch.zeros(1, dtype=torch.int64, device="cuda")
+    tgt = torch.empty((n, K), dtype=torch.int32, device="cuda")
+    B.dflash_synth_target_argmax(n, K, V, d, 0.7, 123, ctr, tgt)
+    torch.cuda.synchronize()
+    dn, tn = d.cpu().numpy(), tgt.cpu().numpy()
+    match = (tn[:, : K - 1] == dn)
+    assert abs(match.mean() - 0.7) < 0.03
+    assert tn.min() >= 0 and tn.max() < V
+    assert ctr.item() == 1
+    B.dflash_synth_target_argmax(n, K, V, d, 0.7, 123, ctr, tgt)
+    torch.cuda.synchronize()
+    assert ctr.item() == 2 and not np.array_equal(tgt.cpu().numpy(), tn)
