@@ -40,7 +40,7 @@ size_t esize(const dflash_config* c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 // Workspace regions (byte offsets), a pure function of (config, max_batch, max_inject_rows).
 struct WsLayout {
   size_t h0, h1, act_y, act_o, act_s, qb, kb, vb, ctx, part, o_part, m_part, l_part, tk_val, tk_id;
-  size_t ubar, cbuf, meta_seq, meta_pos, row_off, row_start, total;
+  size_t ubar, cbuf, meta_seq, meta_pos, row_off, row_start, row_skip, total;
   size_t bytes;
   size_t part_floats;
   int chunks_max;
@@ -170,6 +170,7 @@ WsLayout ws_layout(const dflash_config* c, int max_batch, int max_inject_rows, i
   L.meta_pos = take(Ri * 4);
   L.row_off = take(((size_t)max_seqs + 1) * 4);
   L.row_start = take((size_t)max_seqs * 4);
+  L.row_skip = take((size_t)max_seqs * 4);
   L.total = take(4);
   L.bytes = off;
   return L;
@@ -382,6 +383,8 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
   ia.dev_err = dev_err(H);
   ia.row_off = wsp<int>(H, H->wl.row_off);
   ia.row_start = wsp<int>(H, H->wl.row_start);
+  ia.row_skip = wsp<int>(H, H->wl.row_skip);
+  ia.window = c->window;
   ia.total = wsp<int>(H, H->wl.total);
   ia.states = target_hidden;
   ia.gain = H->g_cnorm;

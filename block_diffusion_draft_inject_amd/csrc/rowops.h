@@ -66,7 +66,7 @@ struct ReduceArgs {
 };
 
 struct InjectArgs {
-  int n_seq, max_new, max_seqs, concat, chunk0;
+  int n_seq, max_new, max_seqs, concat, chunk0, window;
   float eps;
   const int* seq_ids;
   const int* start_pos;
@@ -75,7 +75,8 @@ struct InjectArgs {
   int* seq_base;
   int* dev_err;
   int* row_off;     // [n_seq + 1]
-  int* row_start;   // [n_seq]
+  int* row_start;   // [n_seq] absolute position of the first projected row
+  int* row_skip;    // [n_seq] leading rows not projected (they would leave the window)
   int* total;
   const void* states;
   const void* gain;

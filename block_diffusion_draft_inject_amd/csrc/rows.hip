@@ -294,8 +294,10 @@ __global__ __launch_bounds__(256) void reduce_store_kernel(ReduceArgs a) {
 }
 
 // ------------------------------------------------------------------------ injection
-// One workgroup: per-sequence row offsets of this call (exclusive scan of the clamped n_new),
-// and the sequences' length update.
+// One workgroup: per-sequence row offsets of this call (exclusive scan of the projected row
+// counts), and the sequences' length update.  Of n rows for one sequence only the last
+// min(n, window) are projected: earlier ones are outside the window once the call completes,
+// and their ring slots would collide with the later rows'.
 __global__ __launch_bounds__(256) void inject_plan_kernel(InjectArgs a) {
   __shared__ int scan[256];
   __shared__ int carry;
@@ -316,13 +318,17 @@ __global__ __launch_bounds__(256) void inject_plan_kernel(InjectArgs a) {
         sp = a.start_pos ? a.start_pos[i] : a.seq_len[sid];
         if (sp < 0) { err |= 4; n = 0; }
       }
+      int skip = 0;
       if (n > 0) {
         const int len = a.seq_len[sid];
         if (len == 0 || sp != len) a.seq_base[sid] = sp;   // fresh or restarted
         a.seq_len[sid] = sp + n;
+        if (n > a.window) skip = n - a.window;
       }
       if (err) atomicOr(a.dev_err, err);
-      a.row_start[i] = sp;      // absolute position of row 0 of sequence i
+      a.row_start[i] = sp + skip;
+      a.row_skip[i] = skip;
+      n -= skip;
     }
     scan[tid] = n;
     __syncthreads();
@@ -365,7 +371,7 @@ __global__ __launch_bounds__(256) void concat_norm_kernel(InjectArgs a) {
   const int r = j - a.row_off[i];
   if (tid == 0) { a.meta_seq[lr] = a.seq_ids[i]; a.meta_pos[lr] = a.row_start[i] + r; }
   const int W = a.concat;
-  const T* src = reinterpret_cast<const T*>(a.states) + ((size_t)i * a.max_new + r) * W;
+  const T* src = reinterpret_cast<const T*>(a.states) + ((size_t)i * a.max_new + r + a.row_skip[i]) * W;
   float ss[1] = {0.f};
   for (int k = tid; k < W; k += 256) {
     const float v = ldv(src, k);

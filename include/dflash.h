@@ -157,7 +157,9 @@ DFLASH_API dflash_status dflash_reset_seqs(dflash_handle* h, int32_t n_seq, cons
 /* (1) KV injection.  For each i < n_seq, appends n_new[i] (device, 0..max_new) target-state rows
  * of sequence seq_ids[i] at absolute positions start_pos[i] .. start_pos[i]+n_new[i]-1.
  * start_pos may be NULL: append at the sequence's current length.  A start position other
- * than the current length restarts that sequence's context there.
+ * than the current length restarts that sequence's context there.  seq_ids within one call
+ * must be distinct.  Only the last `window` rows of a sequence in one call are projected (the
+ * earlier ones fall outside the window by the end of the call).
  * target_hidden: [n_seq][max_new][n_taps*target_hidden] (dtype): row (i, r) is the
  * concatenation of the tapped target layers at that position.
  * Computes u_bar = RMSNorm(row) * concat_norm, c = fc u_bar, then for every layer

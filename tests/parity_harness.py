@@ -140,7 +140,14 @@ class Case:
 # ------------------------------------------------------------------------------ checks
 
 def check_kv(case, seq_ids, sample_layers=None, max_positions=64):
-    """Cache contents vs the oracle for (a sample of) the positions each ring holds."""
+    """Cache contents vs the oracle for (a sample of) the positions each ring holds.
+
+    Returns (worst error in units of the allowed bound, fraction of bit-identical elements).
+    Allowed per element: bf16 drafters one bf16 ulp of the value (2^-7 |x|: the two sides
+    round an fp32 vs an fp64 value, so a value next to a rounding boundary can land on either
+    neighbour) plus 1e-2 rms for rounding flips upstream -- one flip of a large element of
+    c = W_fc u_bar moves K/V by |w| * ulp(c), about 3e-3 rms with N(0, 0.02) weights;
+    fp32 drafters 1e-5 rms."""
     cfg = case.cfg
     k, v, sl, sb = case.d.kv_views()
     torch = case.torch
@@ -149,6 +156,7 @@ def check_kv(case, seq_ids, sample_layers=None, max_positions=64):
     sb = sb.cpu().numpy()
     worst = 0.0
     same = tot = 0
+    offenders = []
     layers = range(cfg.n_layers) if sample_layers is None else sample_layers
     for s in seq_ids:
         cache = case.caches[int(s)]
@@ -162,39 +170,69 @@ def check_kv(case, seq_ids, sample_layers=None, max_positions=64):
             vc = v[l, s].float().cpu().numpy()
             for p in held:
                 slot = p % cfg.window
-                for got, ref in ((kc[:, slot], cache.k[l][p]), (vc[:, slot], cache.v[l][p])):
-                    scale = max(1e-30, float(np.sqrt(np.mean(ref * ref))))
-                    worst = max(worst, float(np.max(np.abs(got - ref))) / scale)
+                for kind, got, ref in (("K", kc[:, slot], cache.k[l][p]), ("V", vc[:, slot], cache.v[l][p])):
+                    rms = max(1e-30, float(np.sqrt(np.mean(ref * ref))))
+                    if cfg.dtype == "bf16":
+                        bound = 2.0 ** -7 * np.abs(ref) + 1e-2 * rms
+                    else:
+                        bound = np.full(ref.shape, 1e-5 * rms)
+                    ratio = np.abs(got - ref) / bound
+                    if float(np.max(ratio)) > 1.0:
+                        i = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+                        offenders.append((float(ratio[i]), int(s), l, kind, p, tuple(int(x) for x in i),
+                                          float(got[i]), float(ref[i]), rms))
+                    worst = max(worst, float(np.max(ratio)))
                     same += int(np.sum(got == ref))
                     tot += got.size
+    if offenders:
+        offenders.sort(reverse=True)
+        for o in offenders[:8]:
+            log("[kv offender] ratio %.2f seq %d layer %d %s pos %d elem %s got %.6g ref %.6g rms %.3g" % o)
+        log(f"[kv] {len(offenders)} (position, layer, K/V) entries exceed the bound")
     return worst, same / max(1, tot)
 
 
-def check_draft(case, seq_ids, anchors, res, band=TIE_BAND):
-    """Logits, top-16 (vs the GPU's own logits, exactly; vs the oracle, up to near-ties)."""
+def check_draft(case, seq_ids, anchors, res, band=TIE_BAND, oracles=None):
+    """Logits, then top-16: bitwise equal to the exact top-16 of the GPU's own logits, and equal
+    as a set to the oracle's up to near-ties.  A candidate may enter or leave the set only if its
+    oracle logit is within `band` + 2 * (that row's max |GPU - oracle| logit error) of the
+    oracle's 16th value: two candidates closer than the logit error can legitimately swap."""
     cfg = case.cfg
     errs = []
     o_all = []
+    swaps = 0
     for b, (s, a) in enumerate(zip(seq_ids, anchors)):
-        o = O.draft_block(cfg, case.W64, case.caches[int(s)], int(a), oracle_mode(cfg))
+        o = oracles[b] if oracles is not None else O.draft_block(cfg, case.W64, case.caches[int(s)], int(a),
+                                                                  oracle_mode(cfg))
         o_all.append(o)
+        row_err = np.full(cfg.block_size - 1, np.inf)
         if res.get("logits") is not None:
-            errs.append(float(np.max(np.abs(res["logits"][b] - o["logits"]))))
+            row_err = np.max(np.abs(res["logits"][b] - o["logits"]), axis=1)
+            errs.append(float(row_err.max()))
             for t in range(cfg.block_size - 1):
                 lg = res["logits"][b, t].astype(np.float64)
                 ref = np.argsort(-lg, kind="stable")[:16]
                 assert np.array_equal(res["topk_ids"][b, t], ref), ("own-logit top-16", b, t)
                 assert np.array_equal(res["topk_logits"][b, t], res["logits"][b, t][ref])
+        else:
+            # no full logits: the GPU's top-16 values vs the oracle's logits of the same ids
+            for t in range(cfg.block_size - 1):
+                ids = res["topk_ids"][b, t]
+                row_err[t] = float(np.max(np.abs(res["topk_logits"][b, t] - o["logits"][t][ids])))
+            errs.append(float(row_err.max()))
         for t in range(cfg.block_size - 1):
             gset, oset = set(res["topk_ids"][b, t].tolist()), set(o["topk_ids"][t].tolist())
             if gset != oset:
+                swaps += 1
                 kth = o["topk_logits"][t][-1]
                 for i in gset ^ oset:
-                    assert abs(o["logits"][t][i] - kth) <= band, ("top-16 set", b, t, i, o["logits"][t][i] - kth)
+                    gap = abs(o["logits"][t][i] - kth)
+                    assert gap <= band + 2 * row_err[t], ("top-16 set", b, t, i, gap, row_err[t])
         hf_err = float(np.max(np.abs(res["h_final"][b] - o["h_final"])))
-        errs.append(0.0)
         assert hf_err < 0.1, ("h_final", b, hf_err)
-    return (max(errs) if errs else 0.0), o_all
+    err = max(errs) if errs else 0.0
+    log(f"[draft] {cfg.name}: max |logit err| {err:.3e}, rows with a near-tie swap in the top-16 set: {swaps}")
+    return err, o_all
 
 
 def check_select(case, anchors, res, gpu_path, gpu_score, gpu_margin, mode_name):
