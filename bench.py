@@ -1,0 +1,343 @@
+"""Drafter block-pass benchmark on one MI355X.
+
+A step is one full cycle of the hot path for every sequence of the batch, all on the device:
+    inject(tau_prev target states) -> draft_block -> select_path (Viterbi) ->
+    stand-in target argmax (0.7 match rule) -> verify_greedy (-> tau, next anchor)
+Inputs (weights, target states, context) are synthetic, seeded and resident in HBM before the
+timed region.  The headline workload is the 5-layer bf16 drafter at batch 1, K=16, 1024-token
+context; the batch-32 K=8 drafter with ragged 512..4096 contexts is reported beside it.
+
+Prints one JSON line.  `python bench.py --gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+METRIC = "draft blocks/sec + draft tokens/sec at B=1 and B=32; % HBM/MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- workload setup
+
+def device_weights(cfg, seed, torch):
+    """Random-init drafter on the device: matrices/embeddings/conv/selector ~ N(0, 0.02),
+    norm gains ~ 1 + N(0, 0.02); same shapes as the synthetic generator's."""
+    from block_diffusion_draft_inject_amd import synth
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def draw(name, shape):
+        x = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * cfg.weight_std
+        if name.endswith("norm"):
+            x += 1.0
+        return x.to(dt)
+
+    w = {n: draw(n, s) for n, s in synth.global_shapes(cfg).items()}
+    w["layers"] = [{n: draw(n, s) for n, s in synth.layer_shapes(cfg).items()} for _ in range(cfg.n_layers)]
+    return w
+
+
+class Cycle:
+    """Device buffers and the per-step call sequence of one workload."""
+
+    def __init__(self, cfg, seed, torch, B):
+        from block_diffusion_draft_inject_amd import binding as Bd
+        self.torch, self.cfg, self.Bd = torch, cfg, B
+        self.Bd = Bd
+        self.n = cfg.batch
+        K = cfg.block_size
+        t0 = time.time()
+        self.w = device_weights(cfg, seed, torch)
+        self.d = Bd.Drafter(cfg, self.w, max_seqs=self.n, max_batch=self.n, max_inject_rows=1024)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed + 1)
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        # context: only the last `window` positions of each sequence are injected (older
+        # positions never reach the block, and injection keeps only the last window rows)
+        from block_diffusion_draft_inject_amd import synth
+        L = synth.context_lengths(cfg)
+        self.L0 = L
+        first = [max(0, int(l) - cfg.window) for l in L]
+        nrow = [int(l) - f for l, f in zip(L, first)]
+        maxn = max(nrow)
+        self.prefill_states = (torch.randn((self.n, maxn, cfg.concat_width), generator=g, device="cuda") * 1.0).to(dt)
+        self.pool = torch.randn((self.n, K, cfg.concat_width), generator=g, device="cuda").to(dt)
+        self.seq_ids = torch.arange(self.n, dtype=torch.int32, device="cuda")
+        self.d.dflash_reset_seqs(self.seq_ids)
+        self.d.dflash_inject_kv(self.seq_ids, torch.tensor(nrow, dtype=torch.int32, device="cuda"), maxn,
+                                self.prefill_states,
+                                start_pos=torch.tensor(first, dtype=torch.int32, device="cuda"))
+        self.anchor = torch.randint(0, cfg.vocab - 1, (self.n,), generator=g, device="cuda", dtype=torch.int32)
+        self.tau = torch.zeros(self.n, dtype=torch.int32, device="cuda")      # nothing to inject at step 0
+        self.out = self.d.outputs(self.n, logits=False)
+        self.path = torch.empty((self.n, K - 1), dtype=torch.int32, device="cuda")
+        self.score = torch.empty(self.n, dtype=torch.float32, device="cuda")
+        self.margin = torch.empty(self.n, dtype=torch.float32, device="cuda")
+        self.target = torch.empty((self.n, K), dtype=torch.int32, device="cuda")
+        self.nacc = torch.empty(self.n, dtype=torch.int32, device="cuda")
+        self.committed = torch.empty((self.n, K), dtype=torch.int32, device="cuda")
+        self.counter = torch.zeros(1, dtype=torch.int64, device="cuda")
+        torch.cuda.synchronize()
+        log(f"[bench] {cfg.name}: setup {time.time() - t0:.1f}s")
+
+    def step(self, stream):
+        cfg, d, Bd = self.cfg, self.d, self.Bd
+        K = cfg.block_size
+        d.dflash_inject_kv(self.seq_ids, self.tau, K, self.pool, start_pos=None, stream=stream)
+        o = self.out
+        d.dflash_draft_block(self.seq_ids, self.anchor, o["topk_ids"], o["topk_logits"], o["h_final"], None,
+                             stream=stream)
+        d.dflash_select_path(self.anchor, o["topk_ids"], o["topk_logits"], o["h_final"], Bd.SELECT_VITERBI,
+                             self.path, self.score, self.margin, stream=stream)
+        Bd.dflash_synth_target_argmax(self.n, K, cfg.vocab, self.path, 0.7, 12345, self.counter, self.target,
+                                      stream=stream)
+        Bd.dflash_verify_greedy(self.n, K, self.path, self.target, self.nacc, self.tau, self.committed,
+                                self.anchor, stream=stream)
+
+
+def algorithmic(cfg, tau_mean, n_ctx):
+    """Bytes and flops one step must move/do at minimum: every weight once, the visible KV,
+    the injected states, and the math of the pass (lm_head only for the K-1 draft slots)."""
+    d, f, V, K, B = cfg.hidden, cfg.ffn, cfg.vocab, cfg.block_size, cfg.batch
+    qw, kvw = cfg.q_width, cfg.kv_width
+    es = 2 if cfg.dtype == "bf16" else 4
+    layer_w = (qw * d + 2 * kvw * d + d * qw + 3 * f * d)
+    w_block = cfg.n_layers * layer_w + V * d            # backbone + lm_head
+    w_inject = d * cfg.concat_width + cfg.n_layers * 2 * kvw * d
+    rows_inj = B * tau_mean
+    kv_read = cfg.n_layers * B * 2 * n_ctx * kvw * es
+    bytes_ = (w_block + w_inject) * es + kv_read + rows_inj * cfg.concat_width * es
+    M = B * K
+    fl = 2 * M * cfg.n_layers * layer_w + 2 * B * (K - 1) * V * d
+    fl += cfg.n_layers * B * cfg.n_heads * K * (n_ctx + K) * cfg.head_dim * 4   # QK^T and PV
+    fl += 2 * rows_inj * w_inject
+    lm_bytes = V * d * es + M * d * es
+    return dict(bytes=bytes_, flops=fl, lm_head_bytes=lm_bytes, lm_head_flops=2 * B * (K - 1) * V * d)
+
+
+def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10):
+    """Times `steps` steps twice on one stream: (1) replays of a HIP graph holding
+    `graph_steps` steps (the headline rate; no events inside the graph), (2) the same number of
+    steps launched eagerly, each lm_head launch bracketed by HIP events on that stream (the
+    kernel's duration; the eager step rate is reported too)."""
+    cyc = Cycle(cfg, seed, torch, cfg.batch)
+    stream = torch.cuda.Stream()
+    G = max(1, min(graph_steps, steps))
+    while steps % G:
+        G -= 1
+    with torch.cuda.stream(stream):
+        raw = stream.cuda_stream
+        for _ in range(3):                     # eager warm-up (also loads every kernel)
+            cyc.step(raw)
+        stream.synchronize()
+        cyc.d.dflash_timing_enable(0)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(G):
+                cyc.step(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(max(1, math.ceil(warmup / G))):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps // G):
+        graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # eager pass with HIP events around every lm_head launch
+    cyc.d.dflash_timing_enable(steps)
+    with torch.cuda.stream(stream):
+        raw = stream.cuda_stream
+        stream.synchronize()
+        te0 = time.perf_counter()
+        for _ in range(steps):
+            cyc.step(raw)
+        stream.synchronize()
+        eager = time.perf_counter() - te0
+    lm_ms, lm_n = cyc.d.dflash_timing_read()
+    cyc.d.dflash_timing_enable(0)
+    tau_mean = float(cyc.tau.float().mean().item())
+    err = cyc.d.dflash_get_device_error()
+    if err:
+        raise RuntimeError(f"device error word {err}")
+    ms_step = elapsed * 1e3 / steps
+    L = cyc.L0
+    n_ctx = float(sum(min(int(l), cfg.window) for l in L)) / len(L)
+    alg = algorithmic(cfg, tau_mean if tau_mean > 0 else 1.0, n_ctx)
+    res = dict(
+        blocks_per_s=cfg.batch * steps / elapsed,
+        draft_tokens_per_s=cfg.batch * (cfg.block_size - 1) * steps / elapsed,
+        ms_per_step=ms_step,
+        eager_ms_per_step=eager * 1e3 / steps,
+        graph_steps=G,
+        tau_last=tau_mean,
+        lm_head_ms=lm_ms / max(1, lm_n),
+        lm_head_launches=lm_n,
+        alg=alg,
+    )
+    res["hbm_frac"] = alg["bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS
+    res["mfma_frac"] = alg["flops"] / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+    res["cycle"] = cyc
+    return res
+
+
+# ----------------------------------------------------------------------------- cpu baseline
+
+def cpu_baseline(cyc, budget_s=20.0, max_cycles=20):
+    """The CPU oracle (as it stands) running the same drafter cycle on the host cores, on a
+    bounded sample: prefill of the same context, then cycles until the time budget is spent."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import dflash_oracle as O
+    from block_diffusion_draft_inject_amd import synth
+    cfg = cyc.cfg
+    t_setup = time.time()
+
+    def host(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    W = {k: host(v) for k, v in cyc.w.items() if k != "layers"}
+    W["layers"] = [{k: host(v) for k, v in lw.items()} for lw in cyc.w["layers"]]
+    seq = 0
+    L = int(cyc.L0[seq])
+    first = max(0, L - cfg.window)
+    cache = O.DraftCache(cfg.n_layers)
+    O.inject(cfg, W, cache, np.arange(first, L), host(cyc.prefill_states[seq, : L - first]), "exact")
+    pool = host(cyc.pool[seq])
+    anchor = int(cyc.anchor[seq].item())
+    log(f"[cpu] oracle setup {time.time() - t_setup:.1f}s")
+    t0 = time.perf_counter()
+    n = 0
+    tau = 0
+    while n < max_cycles:
+        if tau:
+            O.inject(cfg, W, cache, np.arange(cache.length, cache.length + tau), pool[:tau], "exact")
+        r = O.draft_block(cfg, W, cache, anchor, "exact", keep_logits=False)
+        sel = O.select_path(cfg, W, anchor, r["topk_ids"], r["topk_logits"], r["h_final"], "viterbi")
+        match, alt, last = synth.match_draws(cfg.replace(batch=1), n)
+        tgt = synth.stand_in_target(sel["path_ids"][None], match, alt, last, cfg.vocab)
+        nacc, _, anchor = O.verify_greedy(sel["path_ids"], tgt[0])
+        tau = nacc + 1
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return dict(value=n / el, unit="blocks/s", cores=int(threads), kind="oracle",
+                sample=f"{cfg.name}: one sequence (context {L}), {n} full cycles (inject tau, draft, Viterbi "
+                       f"select, verify) in {el:.1f}s, float64 NumPy, BLAS threads {threads}")
+
+
+# ----------------------------------------------------------------------------- traffic record
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h", "kernels.h"):
+        h.update(open(os.path.join(ROOT, "block_diffusion_draft_inject_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per lm_head launch from the committed rocprofv3 counter summary, or None when
+    the kernel source changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"lmhead_topk_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-b32", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the drafter pass shards by sequence with no exchange, "
+              "so this build measures one GPU's share (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from block_diffusion_draft_inject_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = synth.WORKLOADS["b1_k16"]
+    r = run_workload(cfg, args.steps, args.warmup, torch)
+    alg = r["alg"]
+    lm_gbps = alg["lm_head_bytes"] / (r["lm_head_ms"] * 1e-3) / 1e9
+    traffic = recorded_traffic(cfg.name)
+    out = {
+        "metric": METRIC,
+        "value": round(r["blocks_per_s"], 2),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init drafter and target states)",
+        "config": {"workload": "b1_k16: 5-layer bf16 drafter, hidden 2048, 16/4 heads x 128, SwiGLU 6144, "
+                               "vocab 151936, 5 taps x 5120, K=16, batch 1, context 1024 (window 1024)",
+                   "batch": 1, "block_size": 16, "context": 1024, "graph_steps": r["graph_steps"]},
+        "eager_ms_per_step": round(r["eager_ms_per_step"], 4),
+        "draft_tokens_per_s": round(r["draft_tokens_per_s"], 1),
+        "cycle_hbm_frac": round(r["hbm_frac"], 4),
+        "cycle_algorithmic_bytes": int(alg["bytes"]),
+        "roofline": {"kernel": "lm_head GEMM + fused top-16 (lmhead_topk_skinny<1>)", "bound": "hbm",
+                     "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "avg_launch_ms": round(r["lm_head_ms"], 5), "launches_timed": r["lm_head_launches"],
+                     "bytes_per_launch": int(alg["lm_head_bytes"])},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(r["cycle"], budget_s=args.cpu_budget)
+    del r["cycle"]
+    if not args.no_b32:
+        c3 = synth.WORKLOADS["b32_k8_conv"]
+        torch.cuda.empty_cache()
+        r3 = run_workload(c3, args.steps, args.warmup, torch)
+        out["b32"] = {"workload": "b32_k8_conv: same drafter, K=8, batch 32, contexts U[512,4096] (window 1024), "
+                                  "two-tap conv, 0.7 match rule",
+                      "blocks_per_s": round(r3["blocks_per_s"], 1),
+                      "draft_tokens_per_s": round(r3["draft_tokens_per_s"], 1),
+                      "ms_per_step": round(r3["ms_per_step"], 4),
+                      "eager_ms_per_step": round(r3["eager_ms_per_step"], 4),
+                      "mfma_frac": round(r3["mfma_frac"], 4), "hbm_frac": round(r3["hbm_frac"], 4),
+                      "algorithmic_tflop_per_step": round(r3["alg"]["flops"] / 1e12, 4),
+                      "lm_head_avg_ms": round(r3["lm_head_ms"], 5)}
+        del r3["cycle"]
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -280,37 +280,67 @@ __global__ __launch_bounds__(256) void attn_chunk_valu(AttnArgs a) {
   }
 }
 
-// Merge the chunks of one (sequence, KV head): o = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c.
+// Merge the chunks of one query row: o = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c.
+// One workgroup of 128 threads per (row, KV head, sequence); chunk maxima and sums are read by
+// one thread each, and every thread then issues its chunk loads eight at a time.
 template <typename T>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float wgt[256];
+  __shared__ float red[2];
+  __shared__ float s_den;
+  const int r = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int K = a.K, dh = a.dh, G = a.nh / a.nkv, R = G * K;
   const size_t base = ((size_t)b * a.nkv + kvh) * a.chunks;
-  for (int e = tid; e < R * dh; e += 256) {
-    const int r = e / dh, dd = e % dh;
-    float M = NEG_INF;
-    for (int c = 0; c < a.chunks; ++c) M = fmaxf(M, a.m_part[(base + c) * R + r]);
-    float num = 0.f, den = 0.f;
-    for (int c = 0; c < a.chunks; ++c) {
-      const float mc = a.m_part[(base + c) * R + r];
-      if (mc == NEG_INF) continue;
-      const float wgt = __expf(mc - M);
-      num += wgt * a.o_part[((base + c) * R + r) * dh + dd];
-      den += wgt * a.l_part[(base + c) * R + r];
-    }
-    const int g = r / K, t = r % K, h = kvh * G + g;
-    stv(reinterpret_cast<T*>(a.o), ((size_t)(b * K + t) * a.nh + h) * dh + dd, num / den);
+  const int nc = a.chunks;
+  float mc[2], lc[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = tid + 128 * u;
+    mc[u] = c < nc ? a.m_part[(base + c) * R + r] : NEG_INF;
+    lc[u] = c < nc ? a.l_part[(base + c) * R + r] : 0.f;
   }
+  float M = wave_max(fmaxf(mc[0], mc[1]));
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  float den = 0.f;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = tid + 128 * u;
+    const float w = (mc[u] == NEG_INF) ? 0.f : __expf(mc[u] - M);
+    if (c < nc) wgt[c] = w;
+    den += w * lc[u];
+  }
+  den = wave_sum(den);
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = den;
+  __syncthreads();
+  if (tid == 0) s_den = red[0] + red[1];
+  __syncthreads();
+  if (tid >= dh) return;
+  const float* op = a.o_part + (base * R + r) * dh + tid;
+  const size_t cstride = (size_t)R * dh;
+  float num = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = (c0 + u < nc) ? op[(size_t)(c0 + u) * cstride] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) num += (c0 + u < nc) ? wgt[c0 + u] * x[u] : 0.f;
+  }
+  const int g = r / K, t = r % K, h = kvh * G + g;
+  stv(reinterpret_cast<T*>(a.o), ((size_t)(b * K + t) * a.nh + h) * dh + tid, num / s_den);
 }
 
 hipError_t launch_attention(bool bf, const AttnArgs& a, int n_seq, hipStream_t st) {
-  const dim3 g1(a.chunks, a.nkv, n_seq), g2(a.nkv, n_seq);
+  const int R = (a.nh / a.nkv) * a.K;
+  const dim3 g1(a.chunks, a.nkv, n_seq), g2(R, a.nkv, n_seq);
   if (bf) {
     hipLaunchKernelGGL(attn_chunk_mfma, g1, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(attn_combine_kernel<bf16>, g2, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_combine_kernel<bf16>, g2, dim3(128), 0, st, a);
   } else {
     hipLaunchKernelGGL(attn_chunk_valu, g1, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(attn_combine_kernel<float>, g2, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_combine_kernel<float>, g2, dim3(128), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -41,9 +41,10 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Block-wide sum of NV values at once for a 256-thread block; scratch must hold 4*NV floats.
-template <int NV>
-__device__ __forceinline__ void block_sum256(float (&v)[NV], float* scratch) {
+// Block-wide sum of NV values at once for a block of NT threads; scratch holds (NT/64)*NV floats.
+template <int NV, int NT = 256>
+__device__ __forceinline__ void block_sum(float (&v)[NV], float* scratch) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < NV; ++i) v[i] = wave_sum(v[i]);
@@ -54,8 +55,18 @@ __device__ __forceinline__ void block_sum256(float (&v)[NV], float* scratch) {
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < NV; ++i) v[i] = scratch[i] + scratch[NV + i] + scratch[2 * NV + i] + scratch[3 * NV + i];
+  for (int i = 0; i < NV; ++i) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) t += scratch[k * NV + i];
+    v[i] = t;
+  }
   __syncthreads();
+}
+
+template <int NV>
+__device__ __forceinline__ void block_sum256(float (&v)[NV], float* scratch) {
+  block_sum<NV, 256>(v, scratch);
 }
 
 // Candidate order for top-k: higher value first, then smaller id.

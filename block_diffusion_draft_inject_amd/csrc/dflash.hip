@@ -40,7 +40,7 @@ size_t esize(const dflash_config* c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 // Workspace regions (byte offsets), a pure function of (config, max_batch, max_inject_rows).
 struct WsLayout {
   size_t h0, h1, act_y, act_o, act_s, qb, kb, vb, ctx, part, o_part, m_part, l_part, tk_val, tk_id;
-  size_t ubar, cbuf, meta_seq, meta_pos, row_off, row_start, row_skip, total;
+  size_t ubar, cbuf, meta_seq, meta_pos, row_off, row_start, row_skip, total, gate, counters;
   size_t bytes;
   size_t part_floats;
   int chunks_max;
@@ -75,6 +75,7 @@ int attn_chunks(const dflash_config* c, int n_seq) {
   int ch = 512 / (n_seq * c->n_kv_heads);
   if (ch < 1) ch = 1;
   if (ch > max_chunks) ch = max_chunks;
+  if (ch > 256) ch = 256;
   return ch;
 }
 
@@ -172,6 +173,8 @@ WsLayout ws_layout(const dflash_config* c, int max_batch, int max_inject_rows, i
   L.row_start = take((size_t)max_seqs * 4);
   L.row_skip = take((size_t)max_seqs * 4);
   L.total = take(4);
+  L.gate = take((size_t)max_batch * (K - 1) * c->sel_rank * 4);
+  L.counters = take(64);
   L.bytes = off;
   return L;
 }
@@ -188,12 +191,14 @@ dflash_status check_cfg(const dflash_config* c) {
   const int R = (c->n_heads / c->n_kv_heads) * c->block_size;
   if (R > 64) return fail(DFLASH_E_UNSUPPORTED, "(n_heads/n_kv_heads)*block_size must be <= 64");
   if (c->topk != 16) return fail(DFLASH_E_UNSUPPORTED, "topk must be 16");
-  if (c->sel_rank < 1 || c->sel_rank > 256) return fail(DFLASH_E_UNSUPPORTED, "sel_rank must be 1..256");
+  if (c->sel_rank < 8 || c->sel_rank > 256 || c->sel_rank % 8)
+    return fail(DFLASH_E_UNSUPPORTED, "sel_rank must be a multiple of 8 in [8, 256]");
   if (c->window < 1) return fail(DFLASH_E_INVALID, "window must be >= 1");
   if (c->vocab < 16) return fail(DFLASH_E_INVALID, "vocab must be >= 16");
   if (c->mask_id < 0 || c->mask_id >= c->vocab) return fail(DFLASH_E_INVALID, "mask_id outside the vocabulary");
   if (c->n_taps < 1 || c->target_hidden < 1) return fail(DFLASH_E_INVALID, "n_taps and target_hidden must be positive");
   if (c->ffn < 1) return fail(DFLASH_E_INVALID, "ffn must be positive");
+  if ((c->n_taps * c->target_hidden) % 8) return fail(DFLASH_E_UNSUPPORTED, "n_taps*target_hidden must be a multiple of 8");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 1.f)) return fail(DFLASH_E_INVALID, "rms_eps >= 0 and rope_theta > 1 required");
   if (c->dtype == DFLASH_BF16) {
     if (c->head_dim != 128) return fail(DFLASH_E_UNSUPPORTED, "bf16 attention needs head_dim 128");
@@ -458,7 +463,8 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
   const WsLayout& W = H->wl;
   float* part = wsp<float>(H, W.part);
   SeqCtx* ctx = wsp<SeqCtx>(H, W.ctx);
-  PlanArgs pa{n_seq, H->max_seqs, c->window, seq_ids, seq_len(H), seq_base(H), dev_err(H), ctx};
+  int* counters = wsp<int>(H, W.counters);
+  PlanArgs pa{n_seq, H->max_seqs, c->window, seq_ids, seq_len(H), seq_base(H), dev_err(H), ctx, counters};
   HIP_TRY(launch_draft_plan(pa, st));
   float* hA = wsp<float>(H, W.h0);
   float* hB = wsp<float>(H, W.h1);
@@ -625,6 +631,7 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
     gl.tk_val = wsp<float>(H, W.tk_val);
     gl.tk_id = wsp<int>(H, W.tk_id);
     gl.logits = logits;
+    gl.counter = counters;
     GemmPlan pl = gemm_plan(b, GEMM_TOPK, M, c->vocab, d);
     HIP_TRY(gemm_launch(b, pl, GEMM_TOPK, gl, st));
     if (ev1) HIP_TRY(hipEventRecord(ev1, st));
@@ -641,6 +648,7 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
     ma.ids = nullptr;
     ma.logits_out = logits;
   }
+  ma.counters = counters;
   HIP_TRY(launch_topk_merge(ma, n_seq * (K - 1), st));
   return DFLASH_OK;
 }
@@ -655,7 +663,10 @@ dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t*
   if (mode != DFLASH_SELECT_VITERBI && mode != DFLASH_SELECT_GREEDY) return fail(DFLASH_E_INVALID, "mode %d", (int)mode);
   if (!anchor_ids || !topk_ids || !topk_logits || !h_final || !path_ids)
     return fail(DFLASH_E_INVALID, "NULL anchor_ids, topk_ids, topk_logits, h_final or path_ids");
-  SelectArgs sa{c->block_size, c->hidden, c->sel_rank, (int)mode, c->vocab, dev_err(H), anchor_ids, topk_ids,
+  float* gate = wsp<float>(H, H->wl.gate);
+  GateArgs ga{c->block_size, c->hidden, c->sel_rank, h_final, H->g_WH, gate};
+  HIP_TRY(launch_sel_gate(bf(c), ga, n_seq, (hipStream_t)stream));
+  SelectArgs sa{c->block_size, c->hidden, c->sel_rank, (int)mode, c->vocab, dev_err(H), gate, anchor_ids, topk_ids,
                 topk_logits, h_final, H->g_A, H->g_B, H->g_WH, path_ids, path_score, margin};
   HIP_TRY(launch_select(bf(c), sa, n_seq, (hipStream_t)stream));
   return DFLASH_OK;
@@ -716,8 +727,6 @@ dflash_status dflash_timing_read(dflash_handle* h, double* total_ms, int32_t* co
   }
   *total_ms = tot;
   *count = n;
-  H->t_count = 0;
-  H->t_next = 0;
   return DFLASH_OK;
 }
 

@@ -34,63 +34,73 @@ __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)
 
 // ---------------------------------------------------------------------------------------
 // skinny: accumulate one wave tile of (16*MT rows) x (16*NF cols) over chunks
-// c = c0, c0 + cstep, ... < c1 (chunk = 64 k values).
+// c = c0, c0 + cstep, ... < c1 (chunk = 64 k values).  Software-pipelined: the loads of the
+// next pair of chunks are issued before the MFMAs of the current pair, so a wave always has
+// one batch of weight loads in flight while it computes.
 // ---------------------------------------------------------------------------------------
 template <int MT, int NF>
-__device__ __forceinline__ void skinny_acc(const bf16* const (&arow)[MT], const bf16* const (&brow)[NF], int kg,
-                                           int c0, int c1, int cstep, f32x4 (&acc)[MT][NF]) {
-  constexpr int U = 4;
-  int c = c0;
-  for (; c + (U - 1) * cstep < c1; c += U * cstep) {
-    u32x4 a[U][MT][2], b[U][NF][2];
+struct SkinnyBatch {
+  u32x4 a[2][MT][2];
+  u32x4 b[2][NF][2];
+};
+
+// Loads chunks c and c + cstep; both indices are clamped to clast so the loads are always
+// issued (no branch around them: the compiler then keeps exact vmcnt counts and the next
+// batch stays in flight while the current one is multiplied).
+template <int MT, int NF>
+__device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NF>& x, const bf16* const (&arow)[MT],
+                                            const bf16* const (&brow)[NF], int kg, int c, int cstep, int clast) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = (c + u * cstep) * 64 + kg * 16;
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const u32x4* q = reinterpret_cast<const u32x4*>(brow[f] + k);
-        b[u][f][0] = q[0];
-        b[u][f][1] = q[1];
-      }
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const u32x4* q = reinterpret_cast<const u32x4*>(arow[m] + k);
-        a[u][m][0] = q[0];
-        a[u][m][1] = q[1];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][m][0]), as_bf16x8(b[u][f][0]), acc[m][f], 0, 0, 0);
-          acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][m][1]), as_bf16x8(b[u][f][1]), acc[m][f], 0, 0, 0);
-        }
-  }
-  for (; c < c1; c += cstep) {
-    const int k = c * 64 + kg * 16;
-    u32x4 a[MT][2], b[NF][2];
+  for (int u = 0; u < 2; ++u) {
+    const int k = min(c + u * cstep, clast) * 64 + kg * 16;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const u32x4* q = reinterpret_cast<const u32x4*>(brow[f] + k);
-      b[f][0] = q[0];
-      b[f][1] = q[1];
+      x.b[u][f][0] = q[0];
+      x.b[u][f][1] = q[1];
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const u32x4* q = reinterpret_cast<const u32x4*>(arow[m] + k);
-      a[m][0] = q[0];
-      a[m][1] = q[1];
+      x.a[u][m][0] = q[0];
+      x.a[u][m][1] = q[1];
     }
+  }
+}
+
+template <int MT, int NF>
+__device__ __forceinline__ void skinny_mma(const SkinnyBatch<MT, NF>& x, bool two, f32x4 (&acc)[MT][NF]) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (u == 1 && !two) break;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[m][0]), as_bf16x8(b[f][0]), acc[m][f], 0, 0, 0);
-        acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[m][1]), as_bf16x8(b[f][1]), acc[m][f], 0, 0, 0);
+        acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.a[u][m][0]), as_bf16x8(x.b[u][f][0]), acc[m][f], 0, 0, 0);
+        acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.a[u][m][1]), as_bf16x8(x.b[u][f][1]), acc[m][f], 0, 0, 0);
       }
+  }
+}
+
+template <int MT, int NF>
+__device__ __forceinline__ void skinny_acc(const bf16* const (&arow)[MT], const bf16* const (&brow)[NF], int kg,
+                                           int c0, int c1, int cstep, f32x4 (&acc)[MT][NF]) {
+  if (c0 >= c1) return;
+  const int clast = c0 + (c1 - 1 - c0) / cstep * cstep;   // last chunk this wave owns
+  SkinnyBatch<MT, NF> x, y;
+  int c = c0;
+  skinny_load(x, arow, brow, kg, c, cstep, clast);
+  while (true) {
+    const int cy = c + 2 * cstep;
+    skinny_load(y, arow, brow, kg, cy, cstep, clast);
+    skinny_mma(x, c + cstep < c1, acc);
+    if (cy >= c1) break;
+    const int cx = cy + 2 * cstep;
+    skinny_load(x, arow, brow, kg, cx, cstep, clast);
+    skinny_mma(y, cy + cstep < c1, acc);
+    if (cx >= c1) break;
+    c = cx;
   }
 }
 
@@ -183,79 +193,104 @@ __device__ __forceinline__ void store_partial(const GemmParams& p, int row, int 
   }
 }
 
-// TOPK (lm_head) skinny: 4 waves each own one 16-column fragment of a 64-column tile and run
-// over all of K.  Each row is scanned by 16 threads (4 columns of every tile each) holding a
-// private running top-16; at the end the 16 lists of a row are merged.
-// grid: x = group (contiguous range of 64-column tiles), y = row tile.
+// TOPK (lm_head) skinny, persistent with work stealing: each wave repeatedly takes the next
+// 16-column fragment from a device counter (reset to 0 by the draft's plan kernel) and
+// streams that fragment's weights over all of K.  Waves therefore finish together however the
+// 9496 fragments of a 151936-word vocabulary divide.  Each row's candidates are kept by
+// 64/(16*MT) lanes in private sorted top-16 lists, merged at the end of the workgroup; one
+// partial list per (row, workgroup) is written.  grid: x = workgroups, y = row tile.
 template <int MT>
 __global__ __launch_bounds__(256) void lmhead_topk_skinny(GemmParams p) {
   constexpr int R = 16 * MT;
-  constexpr int TPR = 256 / R;        // threads per row: 16 (MT=1), 8 (MT=2), 4 (MT=4)
-  constexpr int CPT = 64 / TPR;       // columns per thread per tile
-  __shared__ float tile[R][64 + 1];
-  __shared__ float mv[128][TOPK];   // R * TPR / 2 == 128 lists in flight during the merge
-  __shared__ int mi[128][TOPK];
+  constexpr int LPR = 64 / R;          // lanes per row within a wave: 4, 2, 1
+  constexpr int VPL = 16 / LPR;        // fragment values each of those lanes scans: 4, 8, 16
+  constexpr int NSLOT = R * (LPR > 1 ? LPR / 2 : 1);
+  __shared__ float fb[4][R][17];
+  __shared__ float mv[4][NSLOT][TOPK];
+  __shared__ int mi[4][NSLOT][TOPK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, kg = lane >> 4;
   const int Mv = rows_valid(p);
   const int m0 = blockIdx.y * R;
   if (m0 >= Mv) return;
-  const int g = blockIdx.x, G = gridDim.x;
-  const int ntiles = (p.N + 63) / 64;
-  const int t0 = (int)((long)ntiles * g / G), t1 = (int)((long)ntiles * (g + 1) / G);
   const bf16* arow[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int r = min(m0 + m * 16 + li, Mv - 1);
     arow[m] = reinterpret_cast<const bf16*>(p.A) + (size_t)r * p.lda;
   }
-  const int my_row = tid / TPR, my_part = tid % TPR;
+  const int my_row = lane / LPR, my_sub = lane % LPR;
   const bool row_live = (m0 + my_row < Mv) && ((m0 + my_row) % p.block != 0);
   Top16 top;
   top.init();
+  const int nfrag = (p.N + 15) / 16;
   const int nchunks = p.K / 64;
-  for (int t = t0; t < t1; ++t) {
-    const int col = t * 64 + wave * 16 + li;
+  int* ctr = p.counter + blockIdx.y;
+  while (true) {
+    int f = 0;
+    if (lane == 0) f = atomicAdd(ctr, 1);
+    f = __shfl(f, 0, WAVE);
+    if (f >= nfrag) break;
+    const int col = f * 16 + li;
     const bf16* brow[1] = {brow_ptr(p, min(col, p.N - 1))};
     f32x4 acc[MT][1];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
     skinny_acc<MT, 1>(arow, brow, kg, 0, nchunks, 1, acc);
-    __syncthreads();   // previous tile's readers are done
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = m * 16 + kg * 4 + j;
-        tile[r][wave * 16 + li] = acc[m][0][j];
+        fb[wave][r][li] = acc[m][0][j];
         if (p.logits && m0 + r < Mv) store_logit(p, m0 + r, col, acc[m][0][j]);
       }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (row_live) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int cc = c * TPR + my_part;
-        const int gcol = t * 64 + cc;
-        if (gcol < p.N) top.push(tile[my_row][cc], gcol);
+      for (int v = 0; v < VPL; ++v) {
+        const int c = my_sub * VPL + v;
+        const int gcol = f * 16 + c;
+        if (gcol < p.N) top.push(fb[wave][my_row][c], gcol);
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  // merge the TPR lists of each row: tree of pairwise merges through LDS; at step w the list of
-  // part p (p % 2w == w) goes to part p - w through slot my_row * TPR/2 + p / 2w.
-  for (int w = 1; w < TPR; w <<= 1) {
-    __syncthreads();
-    const int slot = my_row * (TPR / 2) + my_part / (2 * w);
-    if ((my_part & (2 * w - 1)) == w) {
+  // merge the LPR lane lists of each row inside the wave
+  for (int w = 1; w < LPR; w <<= 1) {
+    const int slot = my_row * (LPR / 2) + my_sub / (2 * w);
+    if ((my_sub & (2 * w - 1)) == w) {
 #pragma unroll
-      for (int i = 0; i < TOPK; ++i) { mv[slot][i] = top.v[i]; mi[slot][i] = top.id[i]; }
+      for (int i = 0; i < TOPK; ++i) { mv[wave][slot][i] = top.v[i]; mi[wave][slot][i] = top.id[i]; }
     }
-    __syncthreads();
-    if ((my_part & (2 * w - 1)) == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if ((my_sub & (2 * w - 1)) == 0) {
 #pragma unroll
-      for (int i = 0; i < TOPK; ++i) top.push(mv[slot][i], mi[slot][i]);
+      for (int i = 0; i < TOPK; ++i) top.push(mv[wave][slot][i], mi[wave][slot][i]);
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  if (my_part == 0 && m0 + my_row < Mv) store_partial(p, m0 + my_row, g, top);
+  // merge across the four waves (every wave has left its loop)
+  __syncthreads();
+  if (my_sub == 0 && wave > 0) {
+#pragma unroll
+    for (int i = 0; i < TOPK; ++i) { mv[wave][my_row][i] = top.v[i]; mi[wave][my_row][i] = top.id[i]; }
+  }
+  __syncthreads();
+  if (my_sub == 0 && wave == 0) {
+    for (int w = 1; w < 4; ++w)
+#pragma unroll
+      for (int i = 0; i < TOPK; ++i) top.push(mv[w][my_row][i], mi[w][my_row][i]);
+    if (m0 + my_row < Mv) store_partial(p, m0 + my_row, blockIdx.x, top);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -328,10 +363,10 @@ __device__ __forceinline__ void tiled_tile(const GemmParams& p, TiledSmem& sm, i
   __syncthreads();
   int buf = 0;
   for (int c = c0; c < c1; ++c) {
-    const bool more = c + 1 < c1;
-    if (more) tiled_load(p, ap, bp, kq, c + 1, ra, rb);
+    // prefetch the next k-tile (clamped, so the load is issued unconditionally)
+    tiled_load(p, ap, bp, kq, min(c + 1, c1 - 1), ra, rb);
     tiled_compute(sm, buf, wm, wn, li, kg, acc);
-    if (more) tiled_store(sm, buf ^ 1, r0, kq, ra, rb);
+    tiled_store(sm, buf ^ 1, r0, kq, ra, rb);
     __syncthreads();
     buf ^= 1;
   }
@@ -462,13 +497,13 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
     pl.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     const int rt = (M + 16 * pl.mt - 1) / (16 * pl.mt);
     if (mode == GEMM_TOPK) {
-      const int ntiles = (N + 63) / 64;
-      pl.groups = clampi(1024 / rt, 1, ntiles);
+      const int nfrag = (N + 15) / 16;
+      pl.groups = clampi(512 / rt, 1, (nfrag + 3) / 4);   // = resident workgroups (2 per CU)
       pl.grid = dim3(pl.groups, rt, 1);
     } else {
       const int ncols = (mode == GEMM_SWIGLU) ? N / 2 : N;
       const int ct = (ncols + 15) / 16;
-      if (mode == GEMM_PARTIAL) pl.splits = clampi((768 + ct * rt - 1) / (ct * rt), 1, clampi(nchunks / 4, 1, 64));
+      if (mode == GEMM_PARTIAL) pl.splits = clampi((768 + ct * rt - 1) / (ct * rt), 1, clampi(nchunks / 4, 1, 8));
       pl.grid = dim3(ct, rt, pl.splits);
     }
   } else {
@@ -479,7 +514,7 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
       pl.groups = clampi(512 / rt, 1, ntiles);
       pl.grid = dim3(pl.groups, rt, 1);
     } else {
-      pl.splits = clampi((512 + ntiles * rt - 1) / (ntiles * rt), 1, clampi(nchunks / 4, 1, 16));
+      pl.splits = clampi((512 + ntiles * rt - 1) / (ntiles * rt), 1, clampi(nchunks / 4, 1, 8));
       pl.grid = dim3(ntiles, rt, pl.splits);
     }
   }

@@ -34,6 +34,7 @@ struct GemmParams {
   int groups;
   int block;
   float* logits;          // optional full logits [row/block][block-1][N] for slots >= 1
+  int* counter;           // TOPK skinny: per-row-tile fragment counters, zero before the launch
 };
 
 struct GemmPlan {

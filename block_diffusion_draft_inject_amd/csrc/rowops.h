@@ -19,6 +19,7 @@ struct PlanArgs {
   const int* seq_base;
   int* dev_err;
   SeqCtx* ctx;
+  int* counters;       // lm_head work-stealing counters, zeroed here
 };
 
 struct RowArgs {
@@ -114,6 +115,7 @@ struct MergeArgs {
   int* out_ids;        // [n_seq][K-1][16]
   float* out_vals;
   float* logits_out;   // raw mode only: optional copy of the candidate row [n_seq][K-1][ncand]
+  int* counters;       // lm_head work-stealing counters, zeroed here for the next call
 };
 
 struct AttnArgs {
@@ -131,9 +133,17 @@ struct AttnArgs {
   void* o;             // [rows][nh*dh]
 };
 
+struct GateArgs {
+  int K, d, r;
+  const void* h_final;
+  const void* WH;
+  float* gate;         // [n_seq][K-1][r]
+};
+
 struct SelectArgs {
   int K, d, r, mode, vocab;
   int* dev_err;
+  const float* gate;   // [n_seq][K-1][r] from sel_gate_kernel
   const int* anchor;
   const int* topk_ids;
   const float* topk_logits;
@@ -177,6 +187,7 @@ hipError_t launch_kv_post(bool bf, const KvPostArgs& a, int rows, int heads, hip
 hipError_t launch_reset(const ResetArgs& a, hipStream_t st);
 hipError_t launch_topk_merge(const MergeArgs& a, int out_rows, hipStream_t st);
 hipError_t launch_attention(bool bf, const AttnArgs& a, int n_seq, hipStream_t st);
+hipError_t launch_sel_gate(bool bf, const GateArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_select(bool bf, const SelectArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_synth(const SynthArgs& a, hipStream_t st);

@@ -34,6 +34,7 @@ __device__ __forceinline__ void rope_cs(long pos, int i, int dh, double log_thet
 // slots (mod window) starting at slot0.
 __global__ __launch_bounds__(256) void draft_plan_kernel(PlanArgs a) {
   const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b < 4 && a.counters) a.counters[b] = 0;   // lm_head work-stealing counters of this call
   if (b >= a.n_seq) return;
   int sid = a.seq_ids[b];
   if (sid < 0 || sid >= a.max_seqs) {
@@ -110,104 +111,142 @@ __global__ __launch_bounds__(256) void embed_pre_kernel(RowArgs a) {
 // ------------------------------------------------------------------------ post + pre
 // h_out[t] = h_in[t] + Conv_post(a)_t with a = sum of `splits` partials of the sublayer output,
 // then y[t] = Conv_pre(RMSNorm(h_out))_t  (or, final: y[t] = RMSNorm(h_out[t]) * final gain).
+// Row t needs a_{t-2}, a_{t-1}, a_t (the taps of row t-1 read a_{t-2}) and h_{t-1}, h_t.
+// 512 threads, 4 consecutive elements each per 2048-wide slice (16-byte loads); every global
+// load of the row -- residuals, all partials of the three rows, conv and norm weights -- is
+// issued before the first use, so the kernel pays about one memory round trip.
+constexpr int PP_T = 512;
+constexpr int PP_MAXS = 8;   // k-splits of the producing GEMM (the planner keeps it <= 8)
+
+__device__ __forceinline__ f32x4 ld4f(const float* p, size_t i) { return *reinterpret_cast<const f32x4*>(p + i); }
 template <typename T>
-__global__ __launch_bounds__(256) void post_pre_kernel(RowArgs a) {
-  __shared__ float red[4 * 4];
+__device__ __forceinline__ f32x4 ld4w(const void* p, size_t i) {
+  if constexpr (sizeof(T) == 4) {
+    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + i);
+  } else {
+    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16*>(p) + i);
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+  }
+}
+template <typename T>
+__device__ __forceinline__ void st4(void* p, size_t i, f32x4 v) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p) + i) = v;
+  } else {
+    uint2 u;
+    u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16*>(p) + i) = u;
+  }
+}
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
+
+template <typename T, int NV>
+__global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
+  __shared__ float red[8 * 4];
   const int row = blockIdx.x, tid = threadIdx.x;
   const int t = row % a.K;
   const int d = a.d;
   const bool conv = a.use_conv != 0;
-  // rows t-2, t-1, t of the sublayer output (index 0, 1, 2)
-  float s[3][MAXV];
-  float hv[2][MAXV];
+  const bool fin = a.final_norm != 0;
+  const int q0 = conv ? max(0, 2 - t) : 2;       // first of rows t-2, t-1, t that exists
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 hv[2][NV], pw[2][NV], qw[2][NV], g[NV];
+  f32x4 pv[PP_MAXS][3][NV];
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int k = i * 256 + tid;
+  for (int i = 0; i < NV; ++i) {
+    const int k = (i * PP_T + tid) * 4;
+    const bool in = k < d;
+    hv[1][i] = in ? ld4f(a.h_in, (size_t)row * d + k) : z4;
+    hv[0][i] = (in && conv && t >= 1) ? ld4f(a.h_in, (size_t)(row - 1) * d + k) : z4;
+    pw[0][i] = (in && conv) ? ld4w<T>(a.post_w, k) : z4;
+    pw[1][i] = (in && conv) ? ld4w<T>(a.post_w, d + k) : z4;
+    qw[0][i] = (in && conv && !fin) ? ld4w<T>(a.pre_w, k) : z4;
+    qw[1][i] = (in && conv && !fin) ? ld4w<T>(a.pre_w, d + k) : z4;
+    g[i] = in ? ld4w<T>(a.pre_gain, k) : z4;
+  }
 #pragma unroll
-    for (int q = 0; q < 3; ++q) s[q][i] = 0.f;
-    hv[0][i] = hv[1][i] = 0.f;
-    if (k >= d) continue;
+  for (int sp = 0; sp < PP_MAXS; ++sp)
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int tt = t - 2 + q;
-      if (tt < 0 || (!conv && q < 2)) continue;
-      const int rr = row - 2 + q;
-      float acc = 0.f;
-      for (int sp = 0; sp < a.splits; ++sp) acc += a.part[((size_t)sp * a.part_rows + rr) * d + k];
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int k = (i * PP_T + tid) * 4;
+        pv[sp][q][i] = (sp < a.splits && q >= q0 && k < d)
+                           ? ld4f(a.part, ((size_t)sp * a.part_rows + (row - 2 + q)) * d + k) : z4;
+      }
+  const float pb0 = conv ? ldw<T>(a.post_b, 0) : 0.f, pb1 = conv ? ldw<T>(a.post_b, 1) : 0.f;
+  const float qb0 = (conv && !fin) ? ldw<T>(a.pre_b, 0) : 0.f, qb1 = (conv && !fin) ? ldw<T>(a.pre_b, 1) : 0.f;
+  f32x4 s[3][NV];
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      f32x4 acc = pv[0][q][i];
+#pragma unroll
+      for (int sp = 1; sp < PP_MAXS; ++sp) acc += pv[sp][q][i];
       s[q][i] = acc;
     }
-    if (t >= 1 && conv) hv[0][i] = a.h_in[(size_t)(row - 1) * d + k];
-    hv[1][i] = a.h_in[(size_t)row * d + k];
-  }
   // post-conv taps of rows t-1 and t
-  float kp[2][2] = {{1.f, 0.f}, {1.f, 0.f}};
+  float kp00 = 1.f, kp01 = 0.f, kp10 = 1.f, kp11 = 0.f;
   if (conv) {
     float dot[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-      const int k = i * 256 + tid;
-      if (k >= d) continue;
-      const float w0 = ldw<T>(a.post_w, k), w1 = ldw<T>(a.post_w, d + k);
-      dot[0] += w0 * s[1][i];
-      dot[1] += w1 * s[1][i];
-      dot[2] += w0 * s[2][i];
-      dot[3] += w1 * s[2][i];
+    for (int i = 0; i < NV; ++i) {
+      dot[0] += dot4(pw[0][i], s[1][i]);
+      dot[1] += dot4(pw[1][i], s[1][i]);
+      dot[2] += dot4(pw[0][i], s[2][i]);
+      dot[3] += dot4(pw[1][i], s[2][i]);
     }
-    block_sum256<4>(dot, red);
-    const float b0 = ldw<T>(a.post_b, 0), b1 = ldw<T>(a.post_b, 1);
-    kp[0][0] = sigmoidf_(dot[0] + b0);
-    kp[0][1] = sigmoidf_(dot[1] + b1);
-    kp[1][0] = sigmoidf_(dot[2] + b0);
-    kp[1][1] = sigmoidf_(dot[3] + b1);
+    block_sum<4, PP_T>(dot, red);
+    kp00 = sigmoidf_(dot[0] + pb0);
+    kp01 = sigmoidf_(dot[1] + pb1);
+    kp10 = sigmoidf_(dot[2] + pb0);
+    kp11 = sigmoidf_(dot[3] + pb1);
   }
   float ss[2] = {0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int k = i * 256 + tid;
-    if (k >= d) continue;
+  for (int i = 0; i < NV; ++i) {
+    const int k = (i * PP_T + tid) * 4;
     if (conv) {
-      hv[0][i] += kp[0][0] * s[1][i] + kp[0][1] * s[0][i];   // row t-1 (s[0] is t-2, zero if absent)
-      hv[1][i] += kp[1][0] * s[2][i] + kp[1][1] * s[1][i];
+      hv[0][i] += kp00 * s[1][i] + kp01 * s[0][i];   // row t-1 (s[0] is row t-2, zero if absent)
+      hv[1][i] += kp10 * s[2][i] + kp11 * s[1][i];
     } else {
       hv[1][i] += s[2][i];
     }
-    a.h_out[(size_t)row * d + k] = hv[1][i];
-    ss[0] += hv[0][i] * hv[0][i];
-    ss[1] += hv[1][i] * hv[1][i];
+    if (k < d) *reinterpret_cast<f32x4*>(a.h_out + (size_t)row * d + k) = hv[1][i];
+    ss[0] += dot4(hv[0][i], hv[0][i]);
+    ss[1] += dot4(hv[1][i], hv[1][i]);
   }
-  block_sum256<2>(ss, red);
+  block_sum<2, PP_T>(ss, red);
   const float r0 = rsqrtf(ss[0] / d + a.eps), r1 = rsqrtf(ss[1] / d + a.eps);
-  if (a.final_norm) {
+  if (fin) {
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-      const int k = i * 256 + tid;
-      if (k < d) stv(reinterpret_cast<T*>(a.y), (size_t)row * a.ldy + k, hv[1][i] * r1 * ldw<T>(a.pre_gain, k));
+    for (int i = 0; i < NV; ++i) {
+      const int k = (i * PP_T + tid) * 4;
+      if (k < d) st4<T>(a.y, (size_t)row * a.ldy + k, hv[1][i] * r1 * g[i]);
     }
     return;
   }
   float dot[2] = {0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int k = i * 256 + tid;
-    if (k >= d) continue;
-    const float g = ldw<T>(a.pre_gain, k);
-    hv[0][i] = (t >= 1) ? hv[0][i] * r0 * g : 0.f;
-    hv[1][i] = hv[1][i] * r1 * g;
-    if (conv) {
-      dot[0] += ldw<T>(a.pre_w, k) * hv[1][i];
-      dot[1] += ldw<T>(a.pre_w, d + k) * hv[1][i];
-    }
+  for (int i = 0; i < NV; ++i) {
+    hv[0][i] = (t >= 1) ? hv[0][i] * r0 * g[i] : z4;
+    hv[1][i] = hv[1][i] * r1 * g[i];
+    dot[0] += dot4(qw[0][i], hv[1][i]);
+    dot[1] += dot4(qw[1][i], hv[1][i]);
   }
   float k0 = 1.f, k1 = 0.f;
   if (conv) {
-    block_sum256<2>(dot, red);
-    k0 = sigmoidf_(dot[0] + ldw<T>(a.pre_b, 0));
-    k1 = sigmoidf_(dot[1] + ldw<T>(a.pre_b, 1));
+    block_sum<2, PP_T>(dot, red);
+    k0 = sigmoidf_(dot[0] + qb0);
+    k1 = sigmoidf_(dot[1] + qb1);
   }
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int k = i * 256 + tid;
-    if (k < d) stv(reinterpret_cast<T*>(a.y), (size_t)row * a.ldy + k, k0 * hv[1][i] + k1 * hv[0][i]);
+  for (int i = 0; i < NV; ++i) {
+    const int k = (i * PP_T + tid) * 4;
+    if (k < d) st4<T>(a.y, (size_t)row * a.ldy + k, k0 * hv[1][i] + k1 * hv[0][i]);
   }
 }
 
@@ -372,15 +411,36 @@ __global__ __launch_bounds__(256) void concat_norm_kernel(InjectArgs a) {
   if (tid == 0) { a.meta_seq[lr] = a.seq_ids[i]; a.meta_pos[lr] = a.row_start[i] + r; }
   const int W = a.concat;
   const T* src = reinterpret_cast<const T*>(a.states) + ((size_t)i * a.max_new + r + a.row_skip[i]) * W;
+  T* dst = reinterpret_cast<T*>(a.ubar) + (size_t)lr * W;
+  constexpr int VE = 16 / sizeof(T);          // elements per 16-byte vector
+  const int nv = W / VE;                      // W % VE == 0 (checked on the host)
+  const u32x4* sv = reinterpret_cast<const u32x4*>(src);
   float ss[1] = {0.f};
-  for (int k = tid; k < W; k += 256) {
-    const float v = ldv(src, k);
-    ss[0] += v * v;
+#pragma unroll 4
+  for (int v = tid; v < nv; v += 256) {
+    const u32x4 x = sv[v];
+    const T* e = reinterpret_cast<const T*>(&x);
+#pragma unroll
+    for (int j = 0; j < VE; ++j) {
+      const float f = ldv(e, j);
+      ss[0] += f * f;
+    }
   }
   block_sum256<1>(ss, red);
   const float rs = rsqrtf(ss[0] / W + a.eps);
-  T* dst = reinterpret_cast<T*>(a.ubar) + (size_t)lr * W;
-  for (int k = tid; k < W; k += 256) stv(dst, k, ldv(src, k) * rs * ldw<T>(a.gain, k));
+  const u32x4* gv = reinterpret_cast<const u32x4*>(a.gain);
+  u32x4* dv = reinterpret_cast<u32x4*>(dst);
+#pragma unroll 4
+  for (int v = tid; v < nv; v += 256) {
+    const u32x4 x = sv[v], g = gv[v];
+    u32x4 o;
+    const T* e = reinterpret_cast<const T*>(&x);
+    const T* ge = reinterpret_cast<const T*>(&g);
+    T* oe = reinterpret_cast<T*>(&o);
+#pragma unroll
+    for (int j = 0; j < VE; ++j) stv(oe, j, ldv(e, j) * rs * ldv(ge, j));
+    dv[v] = o;
+  }
 }
 
 // K/V of every layer from the fused projection [rows][n_layers * 2 * kv_width]; one wave per
@@ -438,49 +498,131 @@ __global__ void reset_seqs_kernel(ResetArgs a) {
 }
 
 // ------------------------------------------------------------------------ top-16 merge
-// One workgroup per output row: candidates are `ncand` (value, id) pairs of input row
-// in_row = seq * K + slot; ids == nullptr means the id is the candidate's index.
+// One workgroup per output row (seq, slot >= 1).  Candidates are either sorted lists of 16
+// (ids != nullptr: one list per lm_head workgroup) or raw values with id = index (fp32 path,
+// first reduced to one sorted list per thread).  Lists are then reduced pairwise in LDS by
+// merge-path: an entry's position in the merged list is its own index plus the number of
+// entries of the other list that beat it (the order is total: ids are distinct), so 32 lanes
+// merge two lists in one step.
+// Number of entries of a 16-entry LDS list that beat (x, xi); the list is read with 128-bit
+// LDS loads issued together (scalar reads would each wait out the LDS latency).
+__device__ __forceinline__ int count_better(const float* lv, const int* li, float x, int xi) {
+  f32x4 v[4];
+  u32x4 d[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[q] = reinterpret_cast<const f32x4*>(lv)[q];
+    d[q] = reinterpret_cast<const u32x4*>(li)[q];
+  }
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) n += cand_better(v[q][j], (int)d[q][j], x, xi) ? 1 : 0;
+  return n;
+}
+
 __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
-  __shared__ float sv[256 * 4];
-  __shared__ int si[256 * 4];
+  __shared__ __attribute__((aligned(16))) float sv[2][256][TOPK];
+  __shared__ __attribute__((aligned(16))) int si[2][256][TOPK];
   const int orow = blockIdx.x, tid = threadIdx.x;
   const int b = orow / (a.K - 1), t = orow % (a.K - 1) + 1;
+  if (orow == 0 && tid < 4 && a.counters) a.counters[tid] = 0;
   const size_t in_row = (size_t)b * a.K + t;
   const float* v = a.vals + in_row * a.ncand;
   const int* id = a.ids ? a.ids + in_row * a.ncand : nullptr;
-  if (!id && a.logits_out) {
-    float* lo = a.logits_out + (size_t)orow * a.ncand;
-    for (int c = tid; c < a.ncand; c += 256) lo[c] = v[c];
+  int have = 0;        // lists already in sv[0] (a carried partial result)
+  int nl;
+  if (!id) {
+    if (a.logits_out) {
+      float* lo = a.logits_out + (size_t)orow * a.ncand;
+      for (int c = tid; c < a.ncand; c += 256) lo[c] = v[c];
+    }
+    Top16 top;
+    top.init();
+#pragma unroll 1
+    for (int c = tid; c < a.ncand; c += 256) top.push(v[c], c);
+#pragma unroll
+    for (int j = 0; j < TOPK; ++j) { sv[0][tid][j] = top.v[j]; si[0][tid][j] = top.id[j]; }
+    nl = 0;
+    have = 256;
+  } else {
+    nl = a.ncand / TOPK;
   }
-  Top16 top;
-  top.init();
-  for (int c = tid; c < a.ncand; c += 256) top.push(v[c], id ? id[c] : c);
-  // tree merge of 256 lists: 4 lists per round written to LDS
-  for (int w = 1; w < 256; w <<= 1) {
+  int g0 = 0;
+  do {
+    const int take = min(nl - g0, 256 - have);
+    if (tid < take) {
+      const f32x4* pv = reinterpret_cast<const f32x4*>(v + (size_t)(g0 + tid) * TOPK);
+      const u32x4* pi = reinterpret_cast<const u32x4*>(id + (size_t)(g0 + tid) * TOPK);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 x = pv[q];
+        const u32x4 y = pi[q];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { sv[0][have + tid][4 * q + j] = x[j]; si[0][have + tid][4 * q + j] = (int)y[j]; }
+      }
+    }
     __syncthreads();
-    const bool writer = (tid & (2 * w - 1)) == w;
-    const int slot = tid / (2 * w);          // < 128 / w
-    // LDS holds 1024 entries: 64 lists of 16; rounds with more writers go in two passes
-    const int nwriters = 256 / (2 * w);
-    for (int base = 0; base < nwriters; base += 64) {
-      if (writer && slot >= base && slot < base + 64) {
-#pragma unroll
-        for (int i = 0; i < TOPK; ++i) { sv[(slot - base) * TOPK + i] = top.v[i]; si[(slot - base) * TOPK + i] = top.id[i]; }
+    int n = have + take, cur = 0;
+    while (n > 1) {
+      const int pairs = n / 2;
+      for (int p0 = 0; p0 < pairs; p0 += 8) {
+        const int pr = p0 + (tid >> 5), e = tid & 31;
+        if (pr < pairs) {
+          const int A = 2 * pr, Bl = 2 * pr + 1;
+          const int own = e < TOPK ? A : Bl, oth = e < TOPK ? Bl : A, ei = e & (TOPK - 1);
+          const float x = sv[cur][own][ei];
+          const int xi = si[cur][own][ei];
+          const int rank = ei + count_better(sv[cur][oth], si[cur][oth], x, xi);
+          if (rank < TOPK) { sv[cur ^ 1][pr][rank] = x; si[cur ^ 1][pr][rank] = xi; }
+        }
+      }
+      if ((n & 1) && tid < TOPK) {
+        sv[cur ^ 1][pairs][tid] = sv[cur][n - 1][tid];
+        si[cur ^ 1][pairs][tid] = si[cur][n - 1][tid];
       }
       __syncthreads();
-      if ((tid & (2 * w - 1)) == 0 && slot >= base && slot < base + 64) {
-#pragma unroll
-        for (int i = 0; i < TOPK; ++i) top.push(sv[(slot - base) * TOPK + i], si[(slot - base) * TOPK + i]);
-      }
-      __syncthreads();
+      n = pairs + (n & 1);
+      cur ^= 1;
     }
+    if (cur == 1 && tid < TOPK) { sv[0][0][tid] = sv[1][0][tid]; si[0][0][tid] = si[1][0][tid]; }
+    __syncthreads();
+    have = 1;
+    g0 += take;
+  } while (g0 < nl);
+  if (tid < TOPK) {
+    a.out_ids[(size_t)orow * TOPK + tid] = si[0][0][tid];
+    a.out_vals[(size_t)orow * TOPK + tid] = sv[0][0][tid];
   }
-  if (tid == 0) {
+}
+
+// ------------------------------------------------------------------------ selector context gate
+// gate[b][t-1][j] = sigmoid(W_H[j] . h_final[b][t]) for draft slots t >= 1.  One workgroup per
+// (sequence, slot); each wave computes whole dot products (lanes stride over the row with
+// 16-byte loads), so the code stays short and the loads of one dot are issued together.
+template <typename T>
+__global__ __launch_bounds__(256) void sel_gate_kernel(GateArgs a) {
+  const int idx = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = idx / (a.K - 1), t = idx % (a.K - 1) + 1;
+  const int d = a.d;
+  constexpr int VE = 16 / sizeof(T);
+  const T* h = reinterpret_cast<const T*>(a.h_final) + ((size_t)b * a.K + t) * d;
+  const int nv = d / VE;                   // d % 64 == 0 on the host
+  for (int j = w; j < a.r; j += 4) {
+    const T* wr = reinterpret_cast<const T*>(a.WH) + (size_t)j * d;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int v = lane; v < nv; v += 64) {
+      const u32x4 x = reinterpret_cast<const u32x4*>(h)[v];
+      const u32x4 y = reinterpret_cast<const u32x4*>(wr)[v];
+      const T* xe = reinterpret_cast<const T*>(&x);
+      const T* ye = reinterpret_cast<const T*>(&y);
 #pragma unroll
-    for (int i = 0; i < TOPK; ++i) {
-      a.out_ids[(size_t)orow * TOPK + i] = top.id[i];
-      a.out_vals[(size_t)orow * TOPK + i] = top.v[i];
+      for (int e = 0; e < VE; ++e) acc += ldv(xe, e) * ldv(ye, e);
     }
+    acc = wave_sum(acc);
+    if (lane == 0) a.gate[(size_t)idx * a.r + j] = sigmoidf_(acc);
   }
 }
 
@@ -499,8 +641,17 @@ hipError_t launch_embed_pre(bool bf, const RowArgs& a, int rows, hipStream_t st)
   DFL_T_DISPATCH(bf, embed_pre_kernel, dim3(rows), dim3(256), st, a);
   return hipGetLastError();
 }
+template <int NV>
+static void launch_pp(bool bf, const RowArgs& a, int rows, hipStream_t st) {
+  if (bf) hipLaunchKernelGGL((post_pre_kernel<bf16, NV>), dim3(rows), dim3(PP_T), 0, st, a);
+  else hipLaunchKernelGGL((post_pre_kernel<float, NV>), dim3(rows), dim3(PP_T), 0, st, a);
+}
 hipError_t launch_post_pre(bool bf, const RowArgs& a, int rows, hipStream_t st) {
-  DFL_T_DISPATCH(bf, post_pre_kernel, dim3(rows), dim3(256), st, a);
+  if (a.splits > PP_MAXS || a.d % 4) return hipErrorInvalidValue;
+  const int v = (a.d + 4 * PP_T - 1) / (4 * PP_T);
+  if (v <= 1) launch_pp<1>(bf, a, rows, st);
+  else if (v <= 2) launch_pp<2>(bf, a, rows, st);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 hipError_t launch_qkv_post(bool bf, const QkvArgs& a, int rows, hipStream_t st) {
@@ -532,6 +683,10 @@ hipError_t launch_kv_post(bool bf, const KvPostArgs& a, int rows, int heads, hip
 hipError_t launch_reset(const ResetArgs& a, hipStream_t st) {
   const int n = a.n > 0 ? a.n : 1;
   hipLaunchKernelGGL(reset_seqs_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_sel_gate(bool bf, const GateArgs& a, int n_seq, hipStream_t st) {
+  DFL_T_DISPATCH(bf, sel_gate_kernel, dim3(n_seq * (a.K - 1)), dim3(256), st, a);
   return hipGetLastError();
 }
 hipError_t launch_topk_merge(const MergeArgs& a, int out_rows, hipStream_t st) {

@@ -11,7 +11,7 @@
 namespace dfl {
 
 constexpr int SEL_KMAX = 32;    // block size
-constexpr int SEL_RMAX = 256;   // selector rank
+constexpr int SEL_RC = 16;      // selector-rank chunk staged in LDS at a time
 
 template <typename T>
 __device__ __forceinline__ float ldsel(const void* p, size_t i) {
@@ -25,60 +25,94 @@ __device__ __forceinline__ bool vit_better(float s1, int c1, float s2, int c2) {
 
 template <typename T>
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
+  constexpr int NP = (SEL_KMAX - 2) * TOPK + 1;    // predecessor rows: anchor + candidates of slots 1..K-2
+  constexpr int NC = (SEL_KMAX - 1) * TOPK;        // candidate rows of slots 1..K-1
+  constexpr int VE = 16 / sizeof(T);               // table elements per 16-byte load
   __shared__ int cid[SEL_KMAX][TOPK];
   __shared__ float cu[SEL_KMAX][TOPK];
-  __shared__ float gate[SEL_RMAX];
-  __shared__ float sa[TOPK][SEL_RMAX + 1];
-  __shared__ float sb[TOPK][SEL_RMAX + 1];
-  __shared__ float S[SEL_KMAX][TOPK][TOPK];        // S[t-1][a][b]
-  __shared__ float d1[2][TOPK], d2[2][TOPK];
+  __shared__ __attribute__((aligned(16))) float S[SEL_KMAX][TOPK][TOPK];   // S[t-1][b][a] (successor-major)
+  __shared__ __attribute__((aligned(16))) float ta[NP][SEL_RC + 4];
+  __shared__ __attribute__((aligned(16))) float tb[NC][SEL_RC + 4];
+  __shared__ __attribute__((aligned(16))) float tg[SEL_KMAX][SEL_RC];
+  __shared__ __attribute__((aligned(16))) float d1[2][TOPK];
+  __shared__ __attribute__((aligned(16))) float d2[2][TOPK];
   __shared__ unsigned char bp1[SEL_KMAX][TOPK], bp2[SEL_KMAX][TOPK];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int K = a.K, d = a.d, r = a.r;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int K = a.K, r = a.r;
   int anchor = a.anchor[b];
   if (anchor < 0 || anchor >= a.vocab) {   // out-of-range token: record and read row 0
     if (tid == 0) atomicOr(a.dev_err, 8);
     anchor = 0;
   }
-  for (int e = tid; e < (K - 1) * TOPK; e += 256) {
-    cid[e / TOPK][e % TOPK] = a.topk_ids[(size_t)b * (K - 1) * TOPK + e];
-    cu[e / TOPK][e % TOPK] = a.topk_logits[(size_t)b * (K - 1) * TOPK + e];
+  const int ncand = (K - 1) * TOPK, npred = (K - 2) * TOPK + 1;
+  for (int e = tid; e < ncand; e += 256) {
+    cid[e / TOPK][e % TOPK] = a.topk_ids[(size_t)b * ncand + e];
+    cu[e / TOPK][e % TOPK] = a.topk_logits[(size_t)b * ncand + e];
+  }
+  for (int e = tid; e < (K - 1) * TOPK * TOPK; e += 256) (&S[0][0][0])[e] = 0.f;
+  __syncthreads();
+  // pair term, accumulated over rank chunks of SEL_RC
+  for (int r0 = 0; r0 < r; r0 += SEL_RC) {
+    const int rc = min(SEL_RC, r - r0), nvr = rc / VE;   // r % VE == 0 (checked on the host)
+    const int nload = (npred + ncand) * nvr;
+    for (int e0 = tid; e0 < nload; e0 += 4 * 256) {
+      u32x4 x[4];
+      int rowi[4], vi[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * 256;
+        const int rr = e / nvr;
+        vi[u] = e % nvr;
+        rowi[u] = e < nload ? rr : -1;
+        int tok = 0;
+        const void* tab = a.A;
+        if (rr < npred) {
+          tok = rr == 0 ? anchor : cid[(rr - 1) / TOPK][(rr - 1) % TOPK];
+        } else if (rr < npred + ncand) {
+          tok = cid[(rr - npred) / TOPK][(rr - npred) % TOPK];
+          tab = a.B;
+        }
+        x[u] = e < nload ? reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(tab) + (size_t)tok * r + r0)[vi[u]]
+                         : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (rowi[u] < 0) continue;
+        const int rr = rowi[u];
+        float* dst = rr < npred ? &ta[rr][vi[u] * VE] : &tb[rr - npred][vi[u] * VE];
+        const T* xe = reinterpret_cast<const T*>(&x[u]);
+#pragma unroll
+        for (int j = 0; j < VE; ++j) dst[j] = ldv(xe, j);
+      }
+    }
+    for (int e = tid; e < (K - 1) * rc; e += 256)
+      tg[e / rc][e % rc] = a.gate[((size_t)b * (K - 1) + e / rc) * r + r0 + e % rc];
+    __syncthreads();
+    const int npairs = TOPK + (K - 2) * TOPK * TOPK;
+    for (int e = tid; e < npairs; e += 256) {
+      int t, ai, bi;
+      if (e < TOPK) { t = 1; ai = 0; bi = e; }
+      else { const int f = e - TOPK; t = 2 + f / (TOPK * TOPK); ai = (f / TOPK) % TOPK; bi = f % TOPK; }
+      const f32x4* pa = reinterpret_cast<const f32x4*>(ta[t == 1 ? 0 : 1 + (t - 2) * TOPK + ai]);
+      const f32x4* pb = reinterpret_cast<const f32x4*>(tb[(t - 1) * TOPK + bi]);
+      const f32x4* pg = reinterpret_cast<const f32x4*>(tg[t - 1]);
+      f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < SEL_RC / 4; ++q)
+        if (4 * q < rc) acc4 += pa[q] * pg[q] * pb[q];
+      S[t - 1][bi][ai] += acc4[0] + acc4[1] + acc4[2] + acc4[3];
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < (K - 1) * TOPK * TOPK; e += 256) {
+    const int t1 = e / (TOPK * TOPK), bi = (e / TOPK) % TOPK;
+    (&S[0][0][0])[e] += cu[t1][bi];
   }
   __syncthreads();
-  for (int t = 1; t < K; ++t) {
-    // context gate of slot t: one wave per output j
-    for (int j = w; j < r; j += 4) {
-      float acc = 0.f;
-      for (int k = lane; k < d; k += 64)
-        acc += ldsel<T>(a.WH, (size_t)j * d + k) * ldsel<T>(a.h_final, ((size_t)b * K + t) * d + k);
-      acc = wave_sum(acc);
-      if (lane == 0) gate[j] = sigmoidf_(acc);
-    }
-    // predecessor (A) rows and candidate (B) rows
-    const int npred = (t == 1) ? 1 : TOPK;
-    for (int e = tid; e < TOPK * r; e += 256) {
-      const int i = e / r, j = e % r;
-      sb[i][j] = ldsel<T>(a.B, (size_t)cid[t - 1][i] * r + j);
-      if (i < npred) {
-        const int pid = (t == 1) ? anchor : cid[t - 2][i];
-        sa[i][j] = ldsel<T>(a.A, (size_t)pid * r + j);
-      }
-    }
-    __syncthreads();
-    {
-      const int ai = tid / TOPK, bi = tid % TOPK;
-      if (ai < npred) {
-        float acc = 0.f;
-        for (int j = 0; j < r; ++j) acc += sa[ai][j] * gate[j] * sb[bi][j];
-        S[t - 1][ai][bi] = cu[t - 1][bi] + acc;
-      }
-    }
-    __syncthreads();
-  }
   // walk
   if (a.mode == 0) {
     if (tid < TOPK) {
-      d1[0][tid] = S[0][0][tid];
+      d1[0][tid] = S[0][tid][0];
       d2[0][tid] = NEG_INF;
     }
     __syncthreads();
@@ -88,12 +122,22 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
         const int bi = tid;
         float s1 = NEG_INF, s2 = NEG_INF;
         int c1 = 255, c2 = 255;
+        float p1[TOPK], p2[TOPK], sa_[TOPK];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 x1 = reinterpret_cast<const f32x4*>(d1[cur])[q];
+          const f32x4 x2 = reinterpret_cast<const f32x4*>(d2[cur])[q];
+          const f32x4 xs = reinterpret_cast<const f32x4*>(S[t - 1][bi])[q];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { p1[4 * q + j] = x1[j]; p2[4 * q + j] = x2[j]; sa_[4 * q + j] = xs[j]; }
+        }
+#pragma unroll
         for (int ai = 0; ai < TOPK; ++ai) {
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
-            const float prev = k == 0 ? d1[cur][ai] : d2[cur][ai];
+            const float prev = k == 0 ? p1[ai] : p2[ai];
             if (prev == NEG_INF) continue;
-            const float sc = prev + S[t - 1][ai][bi];
+            const float sc = prev + sa_[ai];
             const int code = ai * 2 + k;
             if (vit_better(sc, code, s1, c1)) {
               s2 = s1; c2 = c1;
@@ -146,7 +190,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
         float s1 = NEG_INF, s2 = NEG_INF;
         int c1 = 0;
         for (int bi = 0; bi < TOPK; ++bi) {
-          const float sc = S[t - 1][ai][bi];
+          const float sc = S[t - 1][bi][ai];
           if (sc > s1) { s2 = s1; s1 = sc; c1 = bi; }
           else if (sc > s2) { s2 = sc; }
         }
