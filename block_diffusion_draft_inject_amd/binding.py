@@ -260,7 +260,7 @@ class Drafter:
         out = dict(
             topk_ids=torch.empty((n_seq, K - 1, 16), dtype=torch.int32, device=dev),
             topk_logits=torch.empty((n_seq, K - 1, 16), dtype=torch.float32, device=dev),
-            h_final=torch.empty((n_seq, K, c.hidden), dtype=dt, device=dev),
+            h_final=torch.empty((n_seq, K, c.hidden), dtype=torch.float32, device=dev),
             logits=torch.empty((n_seq, K - 1, c.vocab), dtype=torch.float32, device=dev) if logits else None,
         )
         return out

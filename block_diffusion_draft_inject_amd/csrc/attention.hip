@@ -10,8 +10,9 @@
 // chip at small batch; each chunk writes an unnormalised partial output with its running max
 // and sum, and attn_combine merges them (log-sum-exp).
 //
-// bf16 path: Q K^T and P V on v_mfma_f32_16x16x32_bf16 (each wave owns 16 query rows); P is
-// rounded to bf16 for the P V product, the running sums stay fp32.  fp32 path: VALU.
+// bf16 path: Q K^T and P V on v_mfma_f32_16x16x32_bf16 (each wave owns 16 query rows); Q and P
+// enter as sums of two bf16 terms (hi + lo), K and V are the bf16 cache values, running sums
+// stay fp32.  fp32 path: VALU.
 #include "rowops.h"
 
 namespace dfl {
@@ -34,6 +35,7 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sk[MK][MDH + 8];
   __shared__ __attribute__((aligned(16))) bf16 svt[MDH][MK + 8];
   __shared__ __attribute__((aligned(16))) bf16 sp[4][16][MK + 8];
+  __shared__ __attribute__((aligned(16))) bf16 sl[4][16][MK + 8];
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, li = lane & 15, kg = lane >> 4;
   const int K = a.K, G = a.nh / a.nkv, R = G * K;
@@ -47,15 +49,18 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
   const bf16* vb = reinterpret_cast<const bf16*>(a.vb);
   const bf16* kc = reinterpret_cast<const bf16*>(a.kcache);
   const bf16* vc = reinterpret_cast<const bf16*>(a.vcache);
-  // this wave's 16 query rows as MFMA A fragments (row = 16w + li, dims ks*32 + kg*8 .. +8)
+  // this wave's 16 query rows as MFMA A fragments (row = 16w + li, dims ks*32 + kg*8 .. +8),
+  // hi and lo planes
   const int qrow = 16 * w + li;
-  u32x4 qa[4];
+  u32x4 qa[4], ql[4];
   {
     const int g = qrow / K, t = qrow % K;
     const bf16* qp = q + ((size_t)(b * K + t) * a.nh + (kvh * G + g)) * MDH;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 4; ++ks) {
       qa[ks] = (qrow < R) ? *reinterpret_cast<const u32x4*>(qp + ks * 32 + kg * 8) : u32x4{0u, 0u, 0u, 0u};
+      ql[ks] = (qrow < R) ? *reinterpret_cast<const u32x4*>(qp + a.q_plane + ks * 32 + kg * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   float m[4], l[4];
 #pragma unroll
@@ -108,6 +113,7 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sk[16 * f + li][ks * 32 + kg * 8]);
         s[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_bf16x8(qa[ks]), kf, s[f], 0, 0, 0);
+        s[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_bf16x8(ql[ks]), kf, s[f], 0, 0, 0);
       }
     }
     // online softmax; lane holds rows 4*kg + j, key 16f + li
@@ -141,19 +147,27 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
     for (int n = 0; n < 8; ++n)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[n][j] *= alpha[j];
+    // P is split into two bf16 terms, P = hi + lo with hi = bf16(P), lo = bf16(P - hi), and both
+    // are multiplied with V: the product then carries ~16 mantissa bits of P instead of 8.
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sp[w][4 * kg + j][16 * f + li] = f2bf(s[f][j]);
+      for (int j = 0; j < 4; ++j) {
+        const bf16 hi = f2bf(s[f][j]);
+        sp[w][4 * kg + j][16 * f + li] = hi;
+        sl[w][4 * kg + j][16 * f + li] = f2bf(s[f][j] - bf2f(hi));
+      }
     __syncthreads();
     // O += P V : A = P [16 rows][64 keys], B = V^T rows (dims) x keys
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&sp[w][li][k2 * 32 + kg * 8]);
+      const bf16x8 pl = *reinterpret_cast<const bf16x8*>(&sl[w][li][k2 * 32 + kg * 8]);
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
         const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&svt[16 * n + li][k2 * 32 + kg * 8]);
         acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vf, acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf, acc[n], 0, 0, 0);
       }
     }
   }
@@ -329,7 +343,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
     for (int u = 0; u < 8; ++u) num += (c0 + u < nc) ? wgt[c0 + u] * x[u] : 0.f;
   }
   const int g = r / K, t = r % K, h = kvh * G + g;
-  stv(reinterpret_cast<T*>(a.o), ((size_t)(b * K + t) * a.nh + h) * dh + tid, num / s_den);
+  st_act(reinterpret_cast<T*>(a.o), ((size_t)(b * K + t) * a.nh + h) * dh + tid, a.o_plane, num / s_den);
 }
 
 hipError_t launch_attention(bool bf, const AttnArgs& a, int n_seq, hipStream_t st) {

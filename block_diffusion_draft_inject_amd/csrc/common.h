@@ -28,6 +28,18 @@ __device__ __forceinline__ float ldv(const bf16* p, size_t i) { return bf2f(p[i]
 __device__ __forceinline__ void stv(float* p, size_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void stv(bf16* p, size_t i, float v) { p[i] = f2bf(v); }
 
+// Activations are carried in fp32.  For bf16 drafters an activation buffer holds two bf16
+// planes, hi = bf16(x) at index i and lo = bf16(x - hi) at index i + plane, so that a bf16 MFMA
+// can consume it as hi*w + lo*w (about 16 mantissa bits); for fp32 drafters it is plain fp32.
+__device__ __forceinline__ void st_act(bf16* p, size_t i, size_t plane, float v) {
+  const bf16 hi = f2bf(v);
+  p[i] = hi;
+  p[i + plane] = f2bf(v - bf2f(hi));
+}
+__device__ __forceinline__ void st_act(float* p, size_t i, size_t, float v) { p[i] = v; }
+__device__ __forceinline__ float ld_act(const bf16* p, size_t i, size_t plane) { return bf2f(p[i]) + bf2f(p[i + plane]); }
+__device__ __forceinline__ float ld_act(const float* p, size_t i, size_t) { return p[i]; }
+
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
 __device__ __forceinline__ float wave_sum(float v) {

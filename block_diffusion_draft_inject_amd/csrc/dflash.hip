@@ -39,7 +39,7 @@ size_t esize(const dflash_config* c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 
 // Workspace regions (byte offsets), a pure function of (config, max_batch, max_inject_rows).
 struct WsLayout {
-  size_t h0, h1, act_y, act_o, act_s, qb, kb, vb, ctx, part, o_part, m_part, l_part, tk_val, tk_id;
+  size_t h0, h1, act_y, act_o, act_s, qb, hsplit, kb, vb, ctx, part, o_part, m_part, l_part, tk_val, tk_id;
   size_t ubar, cbuf, meta_seq, meta_pos, row_off, row_start, row_skip, total, gate, counters;
   size_t bytes;
   size_t part_floats;
@@ -130,10 +130,12 @@ WsLayout ws_layout(const dflash_config* c, int max_batch, int max_inject_rows, i
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   L.h0 = take(M * d * 4);
   L.h1 = take(M * d * 4);
-  L.act_y = take(M * d * es);
-  L.act_o = take(M * qw * es);
-  L.act_s = take(M * c->ffn * es);
-  L.qb = take(M * qw * es);
+  // activations: fp32, or two bf16 planes (hi, lo) -- 4 bytes per element either way
+  L.act_y = take(M * d * 4);
+  L.act_o = take(M * qw * 4);
+  L.act_s = take(M * c->ffn * 4);
+  L.qb = take(M * qw * 4);
+  L.hsplit = take(M * d * 4);
   L.kb = take(M * kvw * es);
   L.vb = take(M * kvw * es);
   L.ctx = take((size_t)max_batch * sizeof(SeqCtx));
@@ -165,8 +167,8 @@ WsLayout ws_layout(const dflash_config* c, int max_batch, int max_inject_rows, i
   L.tk_val = take(tk_f * 4);
   L.tk_id = take(tk_f * 4);
   const size_t Ri = (size_t)max_inject_rows;
-  L.ubar = take(Ri * c->n_taps * c->target_hidden * es);
-  L.cbuf = take(Ri * d * es);
+  L.ubar = take(Ri * c->n_taps * c->target_hidden * 4);
+  L.cbuf = take(Ri * d * 4);
   L.meta_seq = take(Ri * 4);
   L.meta_pos = take(Ri * 4);
   L.row_off = take(((size_t)max_seqs + 1) * 4);
@@ -394,6 +396,7 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
   ia.states = target_hidden;
   ia.gain = H->g_cnorm;
   ia.ubar = H->ws + H->wl.ubar;
+  ia.ubar_plane = (size_t)H->max_inject_rows * concat;
   ia.meta_seq = wsp<int>(H, H->wl.meta_seq);
   ia.meta_pos = wsp<int>(H, H->wl.meta_pos);
   HIP_TRY(launch_inject_plan(ia, st));
@@ -406,6 +409,7 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
     // rows valid in this pass = clamp(total - r0, 0, rows): kernels read it from meta/total
     // fc: c = u_bar W_fc^T
     GemmParams g1 = gemm_base(H->ws + H->wl.ubar, concat, rows, d, concat);
+    g1.a_plane = ia.ubar_plane;
     g1.m_dev = ia.total;
     g1.m_off = (int)r0;
     g1.seg[0] = H->g_fc;
@@ -413,10 +417,12 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
     g1.part = part;
     GemmPlan p1 = gemm_plan(b, GEMM_PARTIAL, rows, d, concat);
     HIP_TRY(gemm_launch(b, p1, GEMM_PARTIAL, g1, st));
-    ReduceArgs ra{rows, d, p1.splits, rows, ia.total, (int)r0, part, H->ws + H->wl.cbuf};
+    const size_t c_plane = (size_t)H->max_inject_rows * d;
+    ReduceArgs ra{rows, d, p1.splits, rows, c_plane, ia.total, (int)r0, part, H->ws + H->wl.cbuf};
     HIP_TRY(launch_reduce_store(b, ra, st));
     // layer-batched K/V projection of every layer
     GemmParams g2 = gemm_base(H->ws + H->wl.cbuf, d, rows, Nkv, d);
+    g2.a_plane = c_plane;
     g2.m_dev = ia.total;
     g2.m_off = (int)r0;
     for (int l = 0; l < c->n_layers; ++l) {
@@ -449,7 +455,7 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
 }
 
 dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t* seq_ids, const int32_t* anchor_ids,
-                                 int32_t* topk_ids, float* topk_logits, void* h_final, float* logits, void* stream) {
+                                 int32_t* topk_ids, float* topk_logits, float* h_final, float* logits, void* stream) {
   Handle* H = as_handle(h);
   if (!H) return fail(DFLASH_E_STATE, "not a live handle");
   const dflash_config* c = &H->cfg;
@@ -466,6 +472,7 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
   int* counters = wsp<int>(H, W.counters);
   PlanArgs pa{n_seq, H->max_seqs, c->window, seq_ids, seq_len(H), seq_base(H), dev_err(H), ctx, counters};
   HIP_TRY(launch_draft_plan(pa, st));
+  const size_t Mmax = (size_t)H->max_batch * K;   // rows of every activation plane
   float* hA = wsp<float>(H, W.h0);
   float* hB = wsp<float>(H, W.h1);
   char* act_y = H->ws + W.act_y;
@@ -487,12 +494,14 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
   ra.pre_b = LW(H, 0, DFLASH_L_CONV_ATTN_PRE_B);
   ra.y = act_y;
   ra.ldy = d;
+  ra.y_plane = Mmax * d;
   HIP_TRY(launch_embed_pre(b, ra, M, st));
   const int chunks = attn_chunks(c, n_seq);
   for (int l = 0; l < c->n_layers; ++l) {
     // q, k, v = y [W_q; W_k; W_v]^T
     const int G = qw / kvw;
     GemmParams gq = gemm_base(act_y, d, M, qw + 2 * kvw, d);
+    gq.a_plane = Mmax * d;
     for (int i = 0; i < G; ++i)
       gq.seg[i] = reinterpret_cast<const char*>(LW(H, l, DFLASH_L_WQ)) + (size_t)i * kvw * d * esize(c);
     gq.seg[G] = LW(H, l, DFLASH_L_WK);
@@ -516,6 +525,7 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
     qa.q_gain = LW(H, l, DFLASH_L_Q_NORM);
     qa.k_gain = LW(H, l, DFLASH_L_K_NORM);
     qa.q = H->ws + W.qb;
+    qa.q_plane = Mmax * qw;
     qa.k = H->ws + W.kb;
     qa.v = H->ws + W.vb;
     HIP_TRY(launch_qkv_post(b, qa, M, st));
@@ -539,9 +549,12 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
     aa.m_part = wsp<float>(H, W.m_part);
     aa.l_part = wsp<float>(H, W.l_part);
     aa.o = act_o;
+    aa.q_plane = Mmax * qw;
+    aa.o_plane = Mmax * qw;
     HIP_TRY(launch_attention(b, aa, n_seq, st));
     // a = o W_o^T
     GemmParams go = gemm_base(act_o, qw, M, d, qw);
+    go.a_plane = Mmax * qw;
     go.seg[0] = LW(H, l, DFLASH_L_WO);
     go.seg_rows = d;
     go.part = part;
@@ -564,11 +577,13 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
     HIP_TRY(launch_post_pre(b, rp, M, st));
     // s = silu(y W_gate^T) * (y W_up^T)
     GemmParams gg = gemm_base(act_y, d, M, 2 * c->ffn, d);
+    gg.a_plane = Mmax * d;
     gg.seg[0] = LW(H, l, DFLASH_L_W_GATE);
     gg.seg[1] = LW(H, l, DFLASH_L_W_UP);
     gg.seg_rows = c->ffn;
     gg.half = c->ffn;
     gg.out = act_s;
+    gg.out_plane = Mmax * c->ffn;
     gg.part = part;
     if (b && M <= 64) {
       GemmPlan pg = gemm_plan(b, GEMM_SWIGLU, M, 2 * c->ffn, d);
@@ -577,11 +592,12 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
       gg.half = 0;
       GemmPlan pg = gemm_plan(b, GEMM_PARTIAL, M, 2 * c->ffn, d);
       HIP_TRY(gemm_launch(b, pg, GEMM_PARTIAL, gg, st));
-      SwigluArgs sa{M, c->ffn, pg.splits, M, part, act_s};
+      SwigluArgs sa{M, c->ffn, pg.splits, M, Mmax * c->ffn, part, act_s};
       HIP_TRY(launch_swiglu(b, sa, st));
     }
     // m = s W_down^T
     GemmParams gd = gemm_base(act_s, c->ffn, M, d, c->ffn);
+    gd.a_plane = Mmax * c->ffn;
     gd.seg[0] = LW(H, l, DFLASH_L_W_DOWN);
     gd.seg_rows = d;
     gd.part = part;
@@ -606,12 +622,14 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
       rm.pre_gain = H->g_fnorm;
       rm.final_norm = 1;
       rm.y = h_final;
+      rm.y2 = H->ws + W.hsplit;
       rm.ldy = d;
     }
     HIP_TRY(launch_post_pre(b, rm, M, st));
   }
   // shared lm_head + top-16 per draft slot
-  GemmParams gl = gemm_base(h_final, d, M, c->vocab, d);
+  GemmParams gl = gemm_base(b ? (const void*)(H->ws + W.hsplit) : (const void*)h_final, d, M, c->vocab, d);
+  gl.a_plane = Mmax * d;
   gl.seg[0] = H->g_lm;
   gl.seg_rows = c->vocab;
   gl.block = K;
@@ -654,7 +672,7 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
 }
 
 dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t* anchor_ids, const int32_t* topk_ids,
-                                 const float* topk_logits, const void* h_final, dflash_select_mode mode,
+                                 const float* topk_logits, const float* h_final, dflash_select_mode mode,
                                  int32_t* path_ids, float* path_score, float* margin, void* stream) {
   Handle* H = as_handle(h);
   if (!H) return fail(DFLASH_E_STATE, "not a live handle");
@@ -664,7 +682,7 @@ dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t*
   if (!anchor_ids || !topk_ids || !topk_logits || !h_final || !path_ids)
     return fail(DFLASH_E_INVALID, "NULL anchor_ids, topk_ids, topk_logits, h_final or path_ids");
   float* gate = wsp<float>(H, H->wl.gate);
-  GateArgs ga{c->block_size, c->hidden, c->sel_rank, h_final, H->g_WH, gate};
+  GateArgs ga{c->block_size, c->hidden, c->sel_rank, reinterpret_cast<const float*>(h_final), H->g_WH, gate};
   HIP_TRY(launch_sel_gate(bf(c), ga, n_seq, (hipStream_t)stream));
   SelectArgs sa{c->block_size, c->hidden, c->sel_rank, (int)mode, c->vocab, dev_err(H), gate, anchor_ids, topk_ids,
                 topk_logits, h_final, H->g_A, H->g_B, H->g_WH, path_ids, path_score, margin};

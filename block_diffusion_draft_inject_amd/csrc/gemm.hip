@@ -7,8 +7,10 @@
 //    16-byte loads are adjacent; A and B use the same permutation, so the sum is unchanged.
 //    Waves of a workgroup split K and are reduced through LDS; workgroups split K again
 //    ("splits") into fp32 partials that the consumer kernel sums in a fixed order.
-//  * gemm_tiled   (bf16, M > 64): 128x128x64 tiles staged through double-buffered LDS,
+//  * gemm_tiled   (bf16, M > 64): 128x128x32 tiles staged through double-buffered LDS,
 //    2x2 waves of 64x64, v_mfma_f32_16x16x32_bf16.
+//  * Activations (A) come as two bf16 planes, hi and lo (x = hi + lo to ~16 mantissa bits);
+//    every A fragment is multiplied twice, A_hi * W + A_lo * W, with bf16 weights.
 //  * gemm_f32     (fp32 drafters): plain VALU dot products, for the small fp32 configuration.
 //  * TOPK mode: the lm_head epilogue keeps a running top-16 per row (thread-private sorted
 //    lists, merged at the end of the workgroup) over a contiguous range of column tiles and
@@ -40,7 +42,8 @@ __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)
 // ---------------------------------------------------------------------------------------
 template <int MT, int NF>
 struct SkinnyBatch {
-  u32x4 a[2][MT][2];
+  u32x4 ah[2][MT][2];   // activation hi plane
+  u32x4 al[2][MT][2];   // activation lo plane
   u32x4 b[2][NF][2];
 };
 
@@ -48,7 +51,7 @@ struct SkinnyBatch {
 // issued (no branch around them: the compiler then keeps exact vmcnt counts and the next
 // batch stays in flight while the current one is multiplied).
 template <int MT, int NF>
-__device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NF>& x, const bf16* const (&arow)[MT],
+__device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NF>& x, const bf16* const (&arow)[MT], size_t a_plane,
                                             const bf16* const (&brow)[NF], int kg, int c, int cstep, int clast) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -62,8 +65,11 @@ __device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NF>& x, const bf16* 
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const u32x4* q = reinterpret_cast<const u32x4*>(arow[m] + k);
-      x.a[u][m][0] = q[0];
-      x.a[u][m][1] = q[1];
+      const u32x4* ql = reinterpret_cast<const u32x4*>(arow[m] + a_plane + k);
+      x.ah[u][m][0] = q[0];
+      x.ah[u][m][1] = q[1];
+      x.al[u][m][0] = ql[0];
+      x.al[u][m][1] = ql[1];
     }
   }
 }
@@ -76,28 +82,30 @@ __device__ __forceinline__ void skinny_mma(const SkinnyBatch<MT, NF>& x, bool tw
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.a[u][m][0]), as_bf16x8(x.b[u][f][0]), acc[m][f], 0, 0, 0);
-        acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.a[u][m][1]), as_bf16x8(x.b[u][f][1]), acc[m][f], 0, 0, 0);
-      }
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.ah[u][m][h]), as_bf16x8(x.b[u][f][h]), acc[m][f], 0, 0, 0);
+          acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.al[u][m][h]), as_bf16x8(x.b[u][f][h]), acc[m][f], 0, 0, 0);
+        }
   }
 }
 
 template <int MT, int NF>
-__device__ __forceinline__ void skinny_acc(const bf16* const (&arow)[MT], const bf16* const (&brow)[NF], int kg,
-                                           int c0, int c1, int cstep, f32x4 (&acc)[MT][NF]) {
+__device__ __forceinline__ void skinny_acc(const bf16* const (&arow)[MT], size_t a_plane, const bf16* const (&brow)[NF],
+                                           int kg, int c0, int c1, int cstep, f32x4 (&acc)[MT][NF]) {
   if (c0 >= c1) return;
   const int clast = c0 + (c1 - 1 - c0) / cstep * cstep;   // last chunk this wave owns
   SkinnyBatch<MT, NF> x, y;
   int c = c0;
-  skinny_load(x, arow, brow, kg, c, cstep, clast);
+  skinny_load(x, arow, a_plane, brow, kg, c, cstep, clast);
   while (true) {
     const int cy = c + 2 * cstep;
-    skinny_load(y, arow, brow, kg, cy, cstep, clast);
+    skinny_load(y, arow, a_plane, brow, kg, cy, cstep, clast);
     skinny_mma(x, c + cstep < c1, acc);
     if (cy >= c1) break;
     const int cx = cy + 2 * cstep;
-    skinny_load(x, arow, brow, kg, cx, cstep, clast);
+    skinny_load(x, arow, a_plane, brow, kg, cx, cstep, clast);
     skinny_mma(y, cy + cstep < c1, acc);
     if (cx >= c1) break;
     c = cx;
@@ -137,7 +145,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  skinny_acc<MT, NF>(arow, brow, kg, c0 + wave, c1, 4, acc);
+  skinny_acc<MT, NF>(arow, p.a_plane, brow, kg, c0 + wave, c1, 4, acc);
   // reduce the 4 waves' k-slices
   if (wave > 0) {
 #pragma unroll
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
       } else {
         if (col < p.half) {
           const float v = silu_f(acc[m][0][j]) * acc[m][NF - 1][j];
-          reinterpret_cast<bf16*>(p.out)[(size_t)row * p.half + col] = f2bf(v);
+          st_act(reinterpret_cast<bf16*>(p.out), (size_t)row * p.half + col, p.out_plane, v);
         }
       }
     }
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(256) void lmhead_topk_skinny(GemmParams p) {
     f32x4 acc[MT][1];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    skinny_acc<MT, 1>(arow, brow, kg, 0, nchunks, 1, acc);
+    skinny_acc<MT, 1>(arow, p.a_plane, brow, kg, 0, nchunks, 1, acc);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -296,77 +304,84 @@ __global__ __launch_bounds__(256) void lmhead_topk_skinny(GemmParams p) {
 // ---------------------------------------------------------------------------------------
 // tiled: 128 x 128 x 64, LDS double buffer, 2x2 waves of 64x64.
 // ---------------------------------------------------------------------------------------
-constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = TBK + 8;
+constexpr int TBM = 128, TBN = 128, TBK = 32, TLD = TBK + 8;
 
 struct TiledSmem {
-  bf16 ab[2][2][TBM][TLD];   // [buffer][A or B][row][k]
+  bf16 ab[2][3][TBM][TLD];   // [buffer][A hi, A lo, B][row][k]
 };
 
-__device__ __forceinline__ void tiled_load(const GemmParams& p, const bf16* const (&ap)[4], const bf16* const (&bp)[4], int kq,
-                                           int c, u32x4 (&ra)[4], u32x4 (&rb)[4]) {
+struct TiledRegs {
+  u32x4 ah[2], al[2], b[2];
+};
+
+__device__ __forceinline__ void tiled_load(const GemmParams& p, const bf16* const (&ap)[2], const bf16* const (&bp)[2], int kq,
+                                           int c, TiledRegs& r) {
   const int k = c * TBK + kq;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + k);
-    rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k);
+  for (int i = 0; i < 2; ++i) {
+    r.ah[i] = *reinterpret_cast<const u32x4*>(ap[i] + k);
+    r.al[i] = *reinterpret_cast<const u32x4*>(ap[i] + p.a_plane + k);
+    r.b[i] = *reinterpret_cast<const u32x4*>(bp[i] + k);
   }
 }
 
-__device__ __forceinline__ void tiled_store(TiledSmem& sm, int buf, int r0, int kq, const u32x4 (&ra)[4], const u32x4 (&rb)[4]) {
+__device__ __forceinline__ void tiled_store(TiledSmem& sm, int buf, int r0, int kq, const TiledRegs& r) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<u32x4*>(&sm.ab[buf][0][r0 + 32 * i][kq]) = ra[i];
-    *reinterpret_cast<u32x4*>(&sm.ab[buf][1][r0 + 32 * i][kq]) = rb[i];
+  for (int i = 0; i < 2; ++i) {
+    *reinterpret_cast<u32x4*>(&sm.ab[buf][0][r0 + 64 * i][kq]) = r.ah[i];
+    *reinterpret_cast<u32x4*>(&sm.ab[buf][1][r0 + 64 * i][kq]) = r.al[i];
+    *reinterpret_cast<u32x4*>(&sm.ab[buf][2][r0 + 64 * i][kq]) = r.b[i];
   }
 }
 
 __device__ __forceinline__ void tiled_compute(const TiledSmem& sm, int buf, int wm, int wn, int li, int kg, f32x4 (&acc)[4][4]) {
+  const int k = kg * 8;
+  bf16x8 ah[4], al[4], b[4];
 #pragma unroll
-  for (int ks = 0; ks < TBK / 32; ++ks) {
-    const int k = ks * 32 + kg * 8;
-    bf16x8 a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = *reinterpret_cast<const bf16x8*>(&sm.ab[buf][0][wm * 64 + i * 16 + li][k]);
-      b[i] = *reinterpret_cast<const bf16x8*>(&sm.ab[buf][1][wn * 64 + i * 16 + li][k]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  for (int i = 0; i < 4; ++i) {
+    ah[i] = *reinterpret_cast<const bf16x8*>(&sm.ab[buf][0][wm * 64 + i * 16 + li][k]);
+    al[i] = *reinterpret_cast<const bf16x8*>(&sm.ab[buf][1][wm * 64 + i * 16 + li][k]);
+    b[i] = *reinterpret_cast<const bf16x8*>(&sm.ab[buf][2][wn * 64 + i * 16 + li][k]);
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], b[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], b[j], acc[i][j], 0, 0, 0);
+    }
 }
 
-// One 128x128 output tile over k-chunks [c0, c1).
+// One 128x128 output tile over k-chunks [c0, c1) of TBK.
 __device__ __forceinline__ void tiled_tile(const GemmParams& p, TiledSmem& sm, int m0, int n0, int Mv, int c0, int c1,
                                            f32x4 (&acc)[4][4]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, li = lane & 15, kg = lane >> 4;
-  const int r0 = tid >> 3, kq = (tid & 7) * 8;
-  const bf16* ap[4];
-  const bf16* bp[4];
+  const int r0 = tid >> 2, kq = (tid & 3) * 8;
+  const bf16* ap[2];
+  const bf16* bp[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = min(m0 + r0 + 32 * i, Mv - 1);
+  for (int i = 0; i < 2; ++i) {
+    const int r = min(m0 + r0 + 64 * i, Mv - 1);
     ap[i] = reinterpret_cast<const bf16*>(p.A) + (size_t)r * p.lda;
-    bp[i] = brow_ptr(p, min(n0 + r0 + 32 * i, p.N - 1));
+    bp[i] = brow_ptr(p, min(n0 + r0 + 64 * i, p.N - 1));
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (c0 >= c1) return;
-  u32x4 ra[4], rb[4];
-  tiled_load(p, ap, bp, kq, c0, ra, rb);
+  TiledRegs r;
+  tiled_load(p, ap, bp, kq, c0, r);
   __syncthreads();   // LDS free (previous tile / epilogue done)
-  tiled_store(sm, 0, r0, kq, ra, rb);
+  tiled_store(sm, 0, r0, kq, r);
   __syncthreads();
   int buf = 0;
   for (int c = c0; c < c1; ++c) {
     // prefetch the next k-tile (clamped, so the load is issued unconditionally)
-    tiled_load(p, ap, bp, kq, min(c + 1, c1 - 1), ra, rb);
+    tiled_load(p, ap, bp, kq, min(c + 1, c1 - 1), r);
     tiled_compute(sm, buf, wm, wn, li, kg, acc);
-    tiled_store(sm, buf ^ 1, r0, kq, ra, rb);
+    tiled_store(sm, buf ^ 1, r0, kq, r);
     __syncthreads();
     buf ^= 1;
   }
@@ -400,7 +415,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_partial(GemmParams p) {
 // tile is scanned by 2 threads (64 columns each) with a private running top-16.
 __global__ __launch_bounds__(256, 2) void lmhead_topk_tiled(GemmParams p) {
   __shared__ TiledSmem sm;
-  float (*ep)[TBN + 4] = reinterpret_cast<float (*)[TBN + 4]>(&sm.ab[0][0][0][0]);  // 64 x 132 floats
+  float (*ep)[TBN + 4] = reinterpret_cast<float (*)[TBN + 4]>(&sm.ab[0][0][0][0]);  // 64 x 132 floats (33.8 KB)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, li = lane & 15, kg = lane >> 4;
   const int Mv = rows_valid(p);
@@ -448,7 +463,7 @@ __global__ __launch_bounds__(256, 2) void lmhead_topk_tiled(GemmParams p) {
   // merge the two lists of each row
   __syncthreads();
   float (*mv)[TOPK] = reinterpret_cast<float (*)[TOPK]>(&sm.ab[0][0][0][0]);
-  int (*mi)[TOPK] = reinterpret_cast<int (*)[TOPK]>(&sm.ab[1][0][0][0]);
+  int (*mi)[TOPK] = reinterpret_cast<int (*)[TOPK]>(&sm.ab[1][0][0][0]);   // 8 KB after the 30 KB first buffer
   if (my_half == 1) {
 #pragma unroll
     for (int i = 0; i < TOPK; ++i) { mv[my_row][i] = top.v[i]; mi[my_row][i] = top.id[i]; }

@@ -13,8 +13,9 @@ enum GemmMode { GEMM_PARTIAL = 0, GEMM_SWIGLU = 1, GEMM_TOPK = 2 };
 // C[m][n] = sum_k A[m][k] * B_n[k] where B_n is row n of a weight matrix split into
 // equal row segments: row n lives at seg[n / seg_rows] + (n % seg_rows) * ldb.
 struct GemmParams {
-  const void* A;          // [M][lda] activations (dtype)
+  const void* A;          // [M][lda] activations: bf16 hi plane (lo plane a_plane elements later) or fp32
   int lda;
+  size_t a_plane;         // elements from the hi plane to the lo plane (bf16 drafters)
   int M;                  // rows (allocation bound)
   const int* m_dev;       // optional device row count: rows >= *m_dev - m_off are skipped
   int m_off;
@@ -25,8 +26,10 @@ struct GemmParams {
   int splits;             // k-splits (PARTIAL)
   // PARTIAL: part[s][m][n], row stride N
   float* part;
-  // SWIGLU: out[m][j] = silu(C[m][j]) * C[m][half + j], j < half
+  // SWIGLU: out[m][j] = silu(C[m][j]) * C[m][half + j], j < half; bf16 hi plane, lo plane
+  // out_plane elements later
   void* out;
+  size_t out_plane;
   int half;
   // TOPK (lm_head): per (row, group) top-16 partials; rows whose slot (row % block) is 0 skipped
   float* tk_val;

@@ -24,6 +24,8 @@ struct PlanArgs {
 
 struct RowArgs {
   int K, d, mask_id, use_conv, final_norm, splits, part_rows, ldy, vocab;
+  size_t y_plane;      // activation planes of y (bf16 drafters)
+  void* y2;            // final norm only: split copy of the output for the lm_head GEMM
   int* dev_err;
   float eps;
   const int* anchor;
@@ -41,6 +43,7 @@ struct RowArgs {
 
 struct QkvArgs {
   int K, nh, nkv, dh, N, splits, part_rows;
+  size_t q_plane;
   float eps;
   double log_theta;
   const SeqCtx* ctx;
@@ -54,12 +57,14 @@ struct QkvArgs {
 
 struct SwigluArgs {
   int M, f, splits, part_rows;
+  size_t out_plane;
   const float* part;
   void* out;
 };
 
 struct ReduceArgs {
   int M, N, splits, part_rows;
+  size_t out_plane;
   const int* m_dev;    // optional: rows valid = min(M, *m_dev - m_off)
   int m_off;
   const float* part;
@@ -68,6 +73,7 @@ struct ReduceArgs {
 
 struct InjectArgs {
   int n_seq, max_new, max_seqs, concat, chunk0, window;
+  size_t ubar_plane;
   float eps;
   const int* seq_ids;
   const int* start_pos;
@@ -120,6 +126,7 @@ struct MergeArgs {
 
 struct AttnArgs {
   int K, nh, nkv, dh, window, max_seqs, chunks, n_layers_stride, layer;
+  size_t q_plane, o_plane;
   float scale;
   const SeqCtx* ctx;
   const void* q;       // [rows][nh*dh]
@@ -135,7 +142,7 @@ struct AttnArgs {
 
 struct GateArgs {
   int K, d, r;
-  const void* h_final;
+  const float* h_final;
   const void* WH;
   float* gate;         // [n_seq][K-1][r]
 };

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void embed_pre_kernel(RowArgs a) {
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int k = i * 256 + tid;
-    if (k < d) stv(reinterpret_cast<T*>(a.y), (size_t)row * a.ldy + k, k0 * e[0][i] + k1 * e[1][i]);
+    if (k < d) st_act(reinterpret_cast<T*>(a.y), (size_t)row * a.ldy + k, a.y_plane, k0 * e[0][i] + k1 * e[1][i]);
   }
 }
 
@@ -129,15 +129,25 @@ __device__ __forceinline__ f32x4 ld4w(const void* p, size_t i) {
                  __uint_as_float(u.y & 0xffff0000u)};
   }
 }
+// Four activations at i (16-byte aligned): fp32, or the hi and lo bf16 planes.
 template <typename T>
-__device__ __forceinline__ void st4(void* p, size_t i, f32x4 v) {
+__device__ __forceinline__ void st4_act(void* p, size_t i, size_t plane, f32x4 v) {
   if constexpr (sizeof(T) == 4) {
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p) + i) = v;
   } else {
-    uint2 u;
-    u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-    *reinterpret_cast<uint2*>(reinterpret_cast<bf16*>(p) + i) = u;
+    bf16 h[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h[j] = f2bf(v[j]);
+      l[j] = f2bf(v[j] - bf2f(h[j]));
+    }
+    uint2 uh, ul;
+    uh.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+    uh.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+    ul.x = (uint32_t)l[0] | ((uint32_t)l[1] << 16);
+    ul.y = (uint32_t)l[2] | ((uint32_t)l[3] << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16*>(p) + i) = uh;
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16*>(p) + i + plane) = ul;
   }
 }
 __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
@@ -225,7 +235,11 @@ __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int k = (i * PP_T + tid) * 4;
-      if (k < d) st4<T>(a.y, (size_t)row * a.ldy + k, hv[1][i] * r1 * g[i]);
+      if (k < d) {
+        const f32x4 o = hv[1][i] * r1 * g[i];
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.y) + (size_t)row * a.ldy + k) = o;
+        st4_act<T>(a.y2, (size_t)row * a.ldy + k, a.y_plane, o);
+      }
     }
     return;
   }
@@ -246,7 +260,7 @@ __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int k = (i * PP_T + tid) * 4;
-    if (k < d) st4<T>(a.y, (size_t)row * a.ldy + k, k0 * hv[1][i] + k1 * hv[0][i]);
+    if (k < d) st4_act<T>(a.y, (size_t)row * a.ldy + k, a.y_plane, k0 * hv[1][i] + k1 * hv[0][i]);
   }
 }
 
@@ -301,8 +315,13 @@ __global__ __launch_bounds__(64) void qkv_post_kernel(QkvArgs a) {
     }
   }
   if (act) {
-    stv(dst, off + lane, x0);
-    stv(dst, off + lane + half, x1);
+    if (gain_kind == 0) {
+      st_act(dst, off + lane, a.q_plane, x0);
+      st_act(dst, off + lane + half, a.q_plane, x1);
+    } else {
+      stv(dst, off + lane, x0);
+      stv(dst, off + lane + half, x1);
+    }
   }
 }
 
@@ -318,7 +337,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(SwigluArgs a) {
     g += pr[j];
     u += pr[a.f + j];
   }
-  stv(reinterpret_cast<T*>(a.out), m * a.f + j, g / (1.f + __expf(-g)) * u);
+  st_act(reinterpret_cast<T*>(a.out), m * a.f + j, a.out_plane, g / (1.f + __expf(-g)) * u);
 }
 
 // ------------------------------------------------------------------------ sum partials -> T
@@ -329,7 +348,7 @@ __global__ __launch_bounds__(256) void reduce_store_kernel(ReduceArgs a) {
   if (i >= (size_t)Mv * a.N) return;
   float acc = 0.f;
   for (int sp = 0; sp < a.splits; ++sp) acc += a.part[(size_t)sp * a.part_rows * a.N + i];
-  stv(reinterpret_cast<T*>(a.out), i, acc);
+  st_act(reinterpret_cast<T*>(a.out), i, a.out_plane, acc);
 }
 
 // ------------------------------------------------------------------------ injection
@@ -429,17 +448,16 @@ __global__ __launch_bounds__(256) void concat_norm_kernel(InjectArgs a) {
   block_sum256<1>(ss, red);
   const float rs = rsqrtf(ss[0] / W + a.eps);
   const u32x4* gv = reinterpret_cast<const u32x4*>(a.gain);
-  u32x4* dv = reinterpret_cast<u32x4*>(dst);
-#pragma unroll 4
+#pragma unroll 2
   for (int v = tid; v < nv; v += 256) {
     const u32x4 x = sv[v], g = gv[v];
-    u32x4 o;
     const T* e = reinterpret_cast<const T*>(&x);
     const T* ge = reinterpret_cast<const T*>(&g);
-    T* oe = reinterpret_cast<T*>(&o);
 #pragma unroll
-    for (int j = 0; j < VE; ++j) stv(oe, j, ldv(e, j) * rs * ldv(ge, j));
-    dv[v] = o;
+    for (int j = 0; j < VE; j += 4)
+      st4_act<T>(dst, (size_t)v * VE + j, a.ubar_plane,
+                 f32x4{ldv(e, j) * rs * ldv(ge, j), ldv(e, j + 1) * rs * ldv(ge, j + 1),
+                       ldv(e, j + 2) * rs * ldv(ge, j + 2), ldv(e, j + 3) * rs * ldv(ge, j + 3)});
   }
 }
 
@@ -606,20 +624,21 @@ __global__ __launch_bounds__(256) void sel_gate_kernel(GateArgs a) {
   const int idx = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = idx / (a.K - 1), t = idx % (a.K - 1) + 1;
   const int d = a.d;
-  constexpr int VE = 16 / sizeof(T);
-  const T* h = reinterpret_cast<const T*>(a.h_final) + ((size_t)b * a.K + t) * d;
+  constexpr int VE = 16 / sizeof(T);      // weight elements per 16-byte load
+  const float* h = a.h_final + ((size_t)b * a.K + t) * d;
   const int nv = d / VE;                   // d % 64 == 0 on the host
   for (int j = w; j < a.r; j += 4) {
     const T* wr = reinterpret_cast<const T*>(a.WH) + (size_t)j * d;
     float acc = 0.f;
-#pragma unroll 4
+#pragma unroll 2
     for (int v = lane; v < nv; v += 64) {
-      const u32x4 x = reinterpret_cast<const u32x4*>(h)[v];
       const u32x4 y = reinterpret_cast<const u32x4*>(wr)[v];
-      const T* xe = reinterpret_cast<const T*>(&x);
       const T* ye = reinterpret_cast<const T*>(&y);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) acc += ldv(xe, e) * ldv(ye, e);
+      for (int e = 0; e < VE; e += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(h + (size_t)v * VE + e);
+        acc += x[0] * ldv(ye, e) + x[1] * ldv(ye, e + 1) + x[2] * ldv(ye, e + 2) + x[3] * ldv(ye, e + 3);
+      }
     }
     acc = wave_sum(acc);
     if (lane == 0) a.gate[(size_t)idx * a.r + j] = sigmoidf_(acc);

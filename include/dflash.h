@@ -18,8 +18,11 @@
  *     synchronises, allocates or frees device memory; all scratch lives in the caller's
  *     workspace buffer.  Calls on one handle must be serialised by the caller (one stream,
  *     or explicit ordering); concurrent calls that share a handle race on its workspace.
- *   - Ids are int32.  Logits, scores and margins are fp32.  Weights, target states and
- *     the activations the library stores use the handle's dtype (fp32 or bf16).
+ *   - Ids are int32.  Logits, scores, margins and hidden states are fp32.  Weights, target
+ *     states and the KV cache use the handle's dtype (fp32 or bf16).  Activations are carried
+ *     in fp32; for bf16 drafters every activation that feeds a bf16 matrix core operation is
+ *     split into two bf16 terms (hi + lo, about 16 mantissa bits), so the only bf16 rounding
+ *     of computed values is the K/V written to (or read as) the cache.
  *   - Linear weights are [out][in] (one output row per line).
  *   - Errors: every check that the host can make (null pointers, sizes, counts above the
  *     handle's maxima, unsupported shapes) returns a negative status BEFORE anything is
@@ -177,10 +180,10 @@ DFLASH_API dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const
  * RMSNorm, shared lm_head, top-16 per draft slot ("Architecture", flowchart "Drafter" and
  * Component Breakdown).  Outputs (slot t = 1..K-1 at index t-1):
  *   topk_ids / topk_logits [n_seq][K-1][16], ordered by (logit desc, id asc);
- *   h_final [n_seq][K][d] (dtype) -- final-normed hidden states, input of the selector;
+ *   h_final [n_seq][K][d] fp32 -- final-normed hidden states, input of the selector;
  *   logits  [n_seq][K-1][V] fp32 or NULL -- full logits for checking only (extra HBM writes). */
 DFLASH_API dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t* seq_ids, const int32_t* anchor_ids,
-                                 int32_t* topk_ids, float* topk_logits, void* h_final, float* logits, void* stream);
+                                 int32_t* topk_ids, float* topk_logits, float* h_final, float* logits, void* stream);
 
 /* (3) Path selection over the candidate lattice ("Architecture", section "Problem 1 --
  * Independent picks are incoherent"): S_t(a, b) = U_t(b) + sum_j A[a,j] * H_t[j] * B[b,j] with
@@ -190,7 +193,7 @@ DFLASH_API dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, con
  * Ties go to the smaller candidate index.  path_ids [n_seq][K-1]; path_score, margin [n_seq]
  * may be NULL. */
 DFLASH_API dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t* anchor_ids, const int32_t* topk_ids,
-                                 const float* topk_logits, const void* h_final, dflash_select_mode mode,
+                                 const float* topk_logits, const float* h_final, dflash_select_mode mode,
                                  int32_t* path_ids, float* path_score, float* margin, void* stream);
 
 /* (4) Greedy longest-prefix verification ("Architecture", section "Speculative Decoding

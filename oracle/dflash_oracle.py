@@ -39,11 +39,11 @@ hidden at the candidate's slot; A and B are [V][r] tables; logits only for slots
 
 Rounding points ("mode"):
   "exact"  -- everything float64.
-  "bf16"   -- the values a bf16 pipeline stores are rounded to bf16 (nearest, ties to
-              even): the normalised concatenation, the fc output, cached K/V, the
-              pre-projection conv outputs, q/k/v after norm+RoPE, the attention output,
-              the SwiGLU product and the final-normed hidden.  The residual stream,
-              accumulations, conv taps, softmax, logits and selector stay float64.
+  "bf16"   -- the drafter stores its KV cache in bf16: the context K/V written by
+              injection and the block's own k/v (after per-head norm and RoPE) are rounded
+              to bf16 (nearest, ties to even).  Weights and target states are bf16 inputs;
+              every other value (activations, accumulations, softmax, logits, selector)
+              stays float64.
 """
 from __future__ import annotations
 
@@ -166,8 +166,8 @@ def inject(cfg, W, cache: DraftCache, positions, states, mode="bf16"):
     if positions.size == 0:
         return
     u = as64(states).reshape(positions.size, cfg.concat_width)
-    u_bar = R(rms_norm(u, W["concat_norm"], cfg.rms_eps))
-    c = R(u_bar @ as64(W["fc"]).T)
+    u_bar = rms_norm(u, W["concat_norm"], cfg.rms_eps)
+    c = u_bar @ as64(W["fc"]).T
     nkv, dh = cfg.n_kv_heads, cfg.head_dim
     for l, lw in enumerate(W["layers"]):
         k = (c @ as64(lw["wk"]).T).reshape(-1, nkv, dh)
@@ -214,11 +214,11 @@ def draft_block(cfg, W, cache: DraftCache, anchor, mode="bf16", block_ids=None, 
     for l, lw in enumerate(W["layers"]):
         # attention sublayer
         z = rms_norm(h, lw["attn_norm"], cfg.rms_eps)
-        y = R(two_tap_conv(z, lw["conv_attn_pre_w"], lw["conv_attn_pre_b"], cfg.use_conv))
+        y = two_tap_conv(z, lw["conv_attn_pre_w"], lw["conv_attn_pre_b"], cfg.use_conv)
         q = (y @ as64(lw["wq"]).T).reshape(K, nh, dh)
         k = (y @ as64(lw["wk"]).T).reshape(K, nkv, dh)
         v = (y @ as64(lw["wv"]).T).reshape(K, nkv, dh)
-        q = R(rope(rms_norm(q, lw["q_norm"], cfg.rms_eps), pos[:, None], cfg.rope_theta))
+        q = rope(rms_norm(q, lw["q_norm"], cfg.rms_eps), pos[:, None], cfg.rope_theta)
         k = R(rope(rms_norm(k, lw["k_norm"], cfg.rms_eps), pos[:, None], cfg.rope_theta))
         v = R(v)
         if ctx:
@@ -226,16 +226,16 @@ def draft_block(cfg, W, cache: DraftCache, anchor, mode="bf16", block_ids=None, 
             vals = np.concatenate([np.stack([cache.v[l][p] for p in ctx]), v])
         else:
             keys, vals = k, v
-        o = R(_attention(q, keys, vals, nkv).reshape(K, nh * dh))
+        o = _attention(q, keys, vals, nkv).reshape(K, nh * dh)
         a = o @ as64(lw["wo"]).T
         h = h + two_tap_conv(a, lw["conv_attn_post_w"], lw["conv_attn_post_b"], cfg.use_conv)
         # feed-forward sublayer
         z = rms_norm(h, lw["mlp_norm"], cfg.rms_eps)
-        y = R(two_tap_conv(z, lw["conv_mlp_pre_w"], lw["conv_mlp_pre_b"], cfg.use_conv))
-        s = R(silu(y @ as64(lw["w_gate"]).T) * (y @ as64(lw["w_up"]).T))
+        y = two_tap_conv(z, lw["conv_mlp_pre_w"], lw["conv_mlp_pre_b"], cfg.use_conv)
+        s = silu(y @ as64(lw["w_gate"]).T) * (y @ as64(lw["w_up"]).T)
         m = s @ as64(lw["w_down"]).T
         h = h + two_tap_conv(m, lw["conv_mlp_post_w"], lw["conv_mlp_post_b"], cfg.use_conv)
-    h_final = R(rms_norm(h, W["final_norm"], cfg.rms_eps))
+    h_final = rms_norm(h, W["final_norm"], cfg.rms_eps)
     logits = h_final[1:] @ as64(W["lm_head"]).T                 # [K-1][V]
     tk = cfg.topk
     ids_out = np.stack([topk_desc(row, tk) for row in logits]).astype(np.int64)

@@ -1,0 +1,270 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark uses.
+
+The four large workloads share one seeded 5-layer bf16 drafter (hidden 2048, 16/4 heads x 128,
+SwiGLU 6144, vocab 151936, 5 taps x 5120).  The oracle (float64 NumPy) runs on a sample of
+the sequences of each batch -- outputs of one sequence do not depend on the others -- while
+every sequence of the batch is checked through properties (top-16 equals the exact top-16 of
+the GPU's own logits, selector and verifier against the oracle on the GPU's inputs, length
+bookkeeping, the device error word).  Context positions older than the window never reach a
+block (pinned on the oracle), so only the last `window` positions of each context are
+injected."""
+import numpy as np
+import pytest
+
+from block_diffusion_draft_inject_amd import binding as B
+from block_diffusion_draft_inject_amd import synth
+from oracle import dflash_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def H():
+    import parity_harness as H
+    return H
+
+
+@pytest.fixture(scope="module")
+def big(H):
+    """numpy weights, their float64 oracle copy, and device copies of the 5-layer drafter."""
+    import time
+    t0 = time.time()
+    cfg = synth.WORKLOADS["b1_k16"]
+    w = synth.make_weights(cfg)
+    W64 = H.weights64(w)
+    dev = B.upload_weights(w, "bf16")
+    H.log(f"[big] drafter weights ready in {time.time() - t0:.1f}s")
+    return dict(w=w, W64=W64, dev=dev)
+
+
+class Run:
+    """A Drafter over the shared weights plus oracle caches for sampled sequences."""
+
+    def __init__(self, H, big, cfg, max_seqs, max_batch, max_inject_rows, sampled):
+        import torch
+        self.H, self.cfg, self.torch = H, cfg, torch
+        self.W64 = big["W64"]
+        self.d = B.Drafter(cfg, big["dev"], max_seqs, max_batch, max_inject_rows)
+        import parity_harness
+        parity_harness.poison(self.d)
+        self.sampled = list(sampled)
+        self.caches = {s: O.DraftCache(cfg.n_layers) for s in self.sampled}
+        self.gen = torch.Generator(device="cuda")
+        self.gen.manual_seed(1234)
+
+    def t(self, a, dt=None):
+        x = self.torch.as_tensor(np.ascontiguousarray(a))
+        return (x.to(dt) if dt is not None else x).cuda()
+
+    def inject(self, seq_ids, positions, start=True):
+        """Injects the given absolute positions for each sequence.  Sampled sequences get the
+        seeded synthetic states on both sides; the others get device-generated N(0,1) states."""
+        torch, cfg = self.torch, self.cfg
+        n = len(seq_ids)
+        n_new = np.array([len(p) for p in positions], dtype=np.int32)
+        mx = int(max(1, n_new.max()))
+        st = torch.empty((n, mx, cfg.concat_width), dtype=torch.bfloat16, device="cuda")
+        for i, (s, pos) in enumerate(zip(seq_ids, positions)):
+            if len(pos) == 0:
+                continue
+            if s in self.caches:
+                rows = synth.target_states(cfg, int(s), pos)
+                st[i, : len(pos)] = torch.from_numpy(rows.storage.view(np.int16)).cuda().view(torch.bfloat16)
+                O.inject(cfg, self.W64, self.caches[s], np.asarray(pos), rows.values, "bf16")
+            else:
+                st[i, : len(pos)] = torch.randn((len(pos), cfg.concat_width), generator=self.gen,
+                                                device="cuda").to(torch.bfloat16)
+        sp = np.array([int(p[0]) if len(p) else 0 for p in positions], dtype=np.int32)
+        self.d.dflash_inject_kv(self.t(np.asarray(seq_ids, dtype=np.int32)), self.t(n_new), mx, st,
+                                start_pos=self.t(sp) if start else None)
+
+    def draft(self, seq_ids, anchors, logits=True):
+        torch = self.torch
+        out = self.d.outputs(len(seq_ids), logits=logits)
+        self.d.dflash_draft_block(self.t(np.asarray(seq_ids, dtype=np.int32)), self.t(np.asarray(anchors, dtype=np.int32)),
+                                  out["topk_ids"], out["topk_logits"], out["h_final"], out["logits"])
+        torch.cuda.synchronize()
+        res = {"topk_ids": out["topk_ids"].cpu().numpy(), "topk_logits": out["topk_logits"].cpu().numpy(),
+               "h_final": out["h_final"].float().cpu().numpy(), "_dev": out}
+        return res
+
+    def own_logit_topk(self, res):
+        """Every row's top-16 equals the exact top-16 of the GPU's own full logits."""
+        torch = self.torch
+        lg = res["_dev"]["logits"]
+        n, km1, V = lg.shape
+        for b in range(n):
+            x = lg[b].double()
+            vals, idx = torch.sort(x, dim=1, descending=True, stable=True)
+            assert torch.equal(idx[:, :16].int().cpu(), torch.from_numpy(res["topk_ids"][b])), b
+            assert torch.equal(vals[:, :16].float().cpu(), torch.from_numpy(res["topk_logits"][b])), b
+
+    def compare_sampled(self, seq_ids, anchors, res):
+        H, cfg = self.H, self.cfg
+        errs = []
+        for b, (s, a) in enumerate(zip(seq_ids, anchors)):
+            if s not in self.caches:
+                continue
+            o = O.draft_block(cfg, self.W64, self.caches[s], int(a), "bf16")
+            lg = res["_dev"]["logits"][b].cpu().numpy()
+            row_err = np.max(np.abs(lg - o["logits"]), axis=1)
+            errs.append(float(row_err.max()))
+            for t in range(cfg.block_size - 1):
+                gset, oset = set(res["topk_ids"][b, t].tolist()), set(o["topk_ids"][t].tolist())
+                kth = o["topk_logits"][t][-1]
+                for i in gset ^ oset:
+                    assert abs(o["logits"][t][i] - kth) <= H.TIE_BAND + 2 * row_err[t], (s, t, i)
+        err = max(errs) if errs else 0.0
+        H.log(f"[{cfg.name}] sampled sequences {self.sampled}: max |logit err| {err:.3e}")
+        assert err <= H.LOGIT_TOL["bf16"]
+        return err
+
+    def select_verify(self, anchors, res, mode_name, target_fn):
+        """GPU selector and verifier vs the oracle on the GPU's own inputs, every sequence."""
+        H, cfg, torch = self.H, self.cfg, self.torch
+        mode = B.SELECT_VITERBI if mode_name == "viterbi" else B.SELECT_GREEDY
+        n = len(anchors)
+        K = cfg.block_size
+        path = torch.empty((n, K - 1), dtype=torch.int32, device="cuda")
+        score = torch.empty(n, dtype=torch.float32, device="cuda")
+        margin = torch.empty(n, dtype=torch.float32, device="cuda")
+        self.d.dflash_select_path(self.t(np.asarray(anchors, dtype=np.int32)), res["_dev"]["topk_ids"],
+                                  res["_dev"]["topk_logits"], res["_dev"]["h_final"], mode, path, score, margin)
+        torch.cuda.synchronize()
+        path, score, margin = path.cpu().numpy(), score.cpu().numpy(), margin.cpu().numpy()
+        for b, a in enumerate(anchors):
+            o = O.select_path(cfg, self.W64, int(a), res["topk_ids"][b].astype(np.int64),
+                              res["topk_logits"][b].astype(np.float64), res["h_final"][b].astype(np.float64),
+                              mode_name)
+            assert abs(o["score"] - score[b]) <= H.MARGIN_GATE, (b, o["score"], score[b])
+            if o["margin"] > H.MARGIN_GATE:
+                assert np.array_equal(o["path_ids"], path[b]), b
+        tgt = target_fn(path)
+        nacc, ncom, com, nxt = self.verify(path, tgt)
+        for b in range(n):
+            nn, c, a = O.verify_greedy(path[b], tgt[b])
+            assert nacc[b] == nn and ncom[b] == nn + 1 and nxt[b] == a and np.array_equal(com[b], c), b
+        return path, ncom
+
+    def verify(self, draft, target):
+        torch = self.torch
+        n, km1 = draft.shape
+        K = km1 + 1
+        nacc = torch.empty(n, dtype=torch.int32, device="cuda")
+        ncom = torch.empty(n, dtype=torch.int32, device="cuda")
+        com = torch.empty((n, K), dtype=torch.int32, device="cuda")
+        nxt = torch.empty(n, dtype=torch.int32, device="cuda")
+        B.dflash_verify_greedy(n, K, self.t(draft.astype(np.int32)), self.t(target.astype(np.int32)), nacc, ncom, com, nxt)
+        torch.cuda.synchronize()
+        return nacc.cpu().numpy(), ncom.cpu().numpy(), com.cpu().numpy(), nxt.cpu().numpy()
+
+    def lengths(self, seq_ids):
+        _, _, sl, _ = self.d.kv_views()
+        self.torch.cuda.synchronize()
+        return sl.cpu().numpy()[np.asarray(seq_ids)]
+
+
+def _window(L, W):
+    return np.arange(max(0, L - W), L)
+
+
+def test_b1_k16_full_window_two_cycles(H, big):
+    """Batch 1, K=16, 1024-token context; injection checked against the oracle, then two
+    draft -> select -> verify cycles on a fixed schedule (tau from the 0.7 rule)."""
+    cfg = synth.WORKLOADS["b1_k16"]
+    run = Run(H, big, cfg, max_seqs=1, max_batch=1, max_inject_rows=1024, sampled=[0])
+    run.d.dflash_reset_seqs(run.t(np.array([0], dtype=np.int32)))
+    run.inject([0], [np.arange(0, 1024)])
+    # injected K/V of sampled positions, every layer
+    k, v, _, _ = run.d.kv_views()
+    run.torch.cuda.synchronize()
+    cache = run.caches[0]
+    for l in range(cfg.n_layers):
+        kc, vc = k[l, 0].float().cpu().numpy(), v[l, 0].float().cpu().numpy()
+        for p in (0, 1, 511, 1023):
+            for got, ref in ((kc[:, p], cache.k[l][p]), (vc[:, p], cache.v[l][p])):
+                rms = float(np.sqrt(np.mean(ref * ref)))
+                assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-2 * rms), (l, p)
+    L = 1024
+    for cyc in range(2):
+        anchor = synth.anchors(cfg.replace(batch=1), cyc).tolist()
+        res = run.draft([0], anchor)
+        run.own_logit_topk(res)
+        run.compare_sampled([0], anchor, res)
+        match, alt, last = synth.match_draws(cfg.replace(batch=1), cyc)
+        _, ncom = run.select_verify(anchor, res, "viterbi",
+                                    lambda p: synth.stand_in_target(p, match, alt, last, cfg.vocab))
+        run.select_verify(anchor, res, "greedy", lambda p: synth.stand_in_target(p, match, alt, last, cfg.vocab))
+        tau = int(ncom[0])
+        run.inject([0], [np.arange(L, L + tau)], start=False)
+        L += tau
+        assert run.lengths([0])[0] == L
+    assert run.d.dflash_get_device_error() == 0
+
+
+def test_b32_k8_conv_ragged_contexts(H, big):
+    """Batch 32, K=8, contexts U[512, 4096] (window 1024), two-tap conv, 0.7 match rule."""
+    cfg = synth.WORKLOADS["b32_k8_conv"]
+    Ls = synth.context_lengths(cfg)
+    sampled = [int(np.argmin(Ls)), int(np.argmax(Ls)), 17]
+    run = Run(H, big, cfg, max_seqs=32, max_batch=32, max_inject_rows=4096, sampled=sampled)
+    ids = list(range(32))
+    run.d.dflash_reset_seqs(run.t(np.arange(32, dtype=np.int32)))
+    run.inject(ids, [_window(int(L), cfg.window) for L in Ls])
+    assert np.array_equal(run.lengths(ids), Ls)
+    anchors = synth.anchors(cfg).tolist()
+    res = run.draft(ids, anchors)
+    run.own_logit_topk(res)
+    run.compare_sampled(ids, anchors, res)
+    match, alt, last = synth.match_draws(cfg, 0)
+    for mode in ("viterbi", "greedy"):
+        run.select_verify(anchors, res, mode, lambda p: synth.stand_in_target(p, match, alt, last, cfg.vocab))
+    assert run.d.dflash_get_device_error() == 0
+
+
+def test_b32_k16_incremental_64_cycles(H, big):
+    """Batch 32, K=16, 2048-token prefixes, 64 cycles of draft -> select -> verify -> inject
+    tau ~ U{1..16} new states into the ring; oracle comparison at cycles 0, 31 and 63."""
+    cfg = synth.WORKLOADS["b32_k16_incremental"]
+    sampled = [0, 21]
+    run = Run(H, big, cfg, max_seqs=32, max_batch=32, max_inject_rows=4096, sampled=sampled)
+    ids = list(range(32))
+    run.d.dflash_reset_seqs(run.t(np.arange(32, dtype=np.int32)))
+    Ls = np.full(32, 2048)
+    run.inject(ids, [_window(2048, cfg.window) for _ in ids])
+    for cyc in range(cfg.cycles):
+        anchors = synth.anchors(cfg, cyc).tolist()
+        check = cyc in (0, 31, cfg.cycles - 1)
+        res = run.draft(ids, anchors, logits=check)
+        if check:
+            run.own_logit_topk(res)
+            run.compare_sampled(ids, anchors, res)
+        tau = synth.tau_draws(cfg, cyc)
+        _, alt, last = synth.match_draws(cfg, cyc)
+        _, ncom = run.select_verify(anchors, res, "viterbi",
+                                    lambda p: synth.target_for_tau(p, tau, alt, last, cfg.vocab))
+        assert np.array_equal(ncom, tau)
+        run.inject(ids, [np.arange(L, L + t) for L, t in zip(Ls, tau)], start=False)
+        Ls = Ls + tau
+        assert np.array_equal(run.lengths(ids), Ls)
+    assert run.d.dflash_get_device_error() == 0
+
+
+def test_b64_k16_long_context(H, big):
+    """Batch 64, context 32768 each (only the last 1024 positions attended), K=16; RoPE angles
+    at positions past 32k."""
+    cfg = synth.WORKLOADS["b64_k16_long"]
+    sampled = [0, 63]
+    run = Run(H, big, cfg, max_seqs=64, max_batch=64, max_inject_rows=4096, sampled=sampled)
+    ids = list(range(64))
+    run.d.dflash_reset_seqs(run.t(np.arange(64, dtype=np.int32)))
+    L = 32768
+    run.inject(ids, [_window(L, cfg.window) for _ in ids])
+    assert np.all(run.lengths(ids) == L)
+    anchors = synth.anchors(cfg).tolist()
+    res = run.draft(ids, anchors)
+    run.own_logit_topk(res)
+    run.compare_sampled(ids, anchors, res)
+    match, alt, last = synth.match_draws(cfg, 0)
+    run.select_verify(anchors, res, "viterbi", lambda p: synth.stand_in_target(p, match, alt, last, cfg.vocab))
+    assert run.d.dflash_get_device_error() == 0
