@@ -127,7 +127,7 @@ def algorithmic(cfg, tau_mean, n_ctx):
     fl = 2 * M * cfg.n_layers * layer_w + 2 * B * (K - 1) * V * d
     fl += cfg.n_layers * B * cfg.n_heads * K * (n_ctx + K) * cfg.head_dim * 4   # QK^T and PV
     fl += 2 * rows_inj * w_inject
-    lm_bytes = V * d * es + M * d * es
+    lm_bytes = V * d * es + M * d * 4                  # weights + fp32-precision hidden rows
     return dict(bytes=bytes_, flops=fl, lm_head_bytes=lm_bytes, lm_head_flops=2 * B * (K - 1) * V * d)
 
 
@@ -267,6 +267,64 @@ def recorded_traffic(workload):
     return rec.get("bytes_per_launch")
 
 
+# ----------------------------------------------------------------------------- counter passes
+
+COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
+
+
+def traffic_probe(steps, torch):
+    """Workload for one rocprofv3 counter pass: `steps` eager cycles of the headline workload,
+    then a plain elementwise copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES) three
+    times.  The copy's FETCH_SIZE / WRITE_SIZE readings give the counters' scale."""
+    from block_diffusion_draft_inject_amd import synth
+    cfg = synth.WORKLOADS["b1_k16"]
+    cyc = Cycle(cfg, 0, torch, cfg.batch)
+    raw = torch.cuda.current_stream().cuda_stream
+    for _ in range(steps):
+        cyc.step(raw)
+    torch.cuda.synchronize()
+    src = torch.full((COPY_BYTES // 4,), 1.5, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"[traffic-probe] {steps} cycles + 3 copies of {COPY_BYTES} bytes done")
+
+
+def _counter_rows(path):
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    out = []
+    for r in rows:
+        out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def traffic_record(fetch_csv, write_csv, workload="b1_k16"):
+    """Per-launch HBM bytes of the lm_head kernel from two counter-collection CSVs (one pass
+    with FETCH_SIZE, one with WRITE_SIZE; values in KiB per dispatch), each scaled so that the
+    calibration copy reads (writes) exactly COPY_BYTES."""
+    res = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r[2] == name]
+        lm = [v for _, k, _, v in rows if "lmhead_topk" in k]
+        copies = sorted([(i, v) for i, k, _, v in rows if "elementwise" in k])[-3:]
+        if not lm or len(copies) < 3:
+            raise SystemExit(f"{path}: no lm_head dispatches or fewer than 3 copy dispatches")
+        copy_kib = sum(v for _, v in copies) / 3
+        scale = COPY_BYTES / (copy_kib * 1024.0)
+        res[name] = dict(kib_per_launch=sum(lm) / len(lm), launches=len(lm), copy_kib=copy_kib, scale=scale)
+    f, w = res["FETCH_SIZE"], res["WRITE_SIZE"]
+    rec = dict(kernel="lmhead_topk_skinny<1>", workload=workload, kernel_hash=kernel_hash(),
+               fetch=f, write=w, copy_bytes=COPY_BYTES,
+               bytes_per_launch=int(round(f["kib_per_launch"] * 1024 * f["scale"]
+                                          + w["kib_per_launch"] * 1024 * w["scale"])))
+    out = os.path.join(ROOT, "profiles", f"lmhead_topk_{workload}_traffic.json")
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps(rec))
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -276,8 +334,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-b32", action="store_true")
+    ap.add_argument("--no-b1", action="store_true", help="skip the headline workload (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run the workload of one rocprofv3 counter pass (eager cycles + calibration copy)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the lm_head traffic record from two counter-collection CSVs (no GPU)")
     args = ap.parse_args()
+    if args.traffic_record:
+        traffic_record(*args.traffic_record)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the drafter pass shards by sequence with no exchange, "
               "so this build measures one GPU's share (--gpus 1).", file=sys.stderr)
@@ -288,40 +354,45 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    cfg = synth.WORKLOADS["b1_k16"]
-    r = run_workload(cfg, args.steps, args.warmup, torch)
-    alg = r["alg"]
-    lm_gbps = alg["lm_head_bytes"] / (r["lm_head_ms"] * 1e-3) / 1e9
-    traffic = recorded_traffic(cfg.name)
-    out = {
-        "metric": METRIC,
-        "value": round(r["blocks_per_s"], 2),
-        "unit": "blocks/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(r["ms_per_step"], 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded random-init drafter and target states)",
-        "config": {"workload": "b1_k16: 5-layer bf16 drafter, hidden 2048, 16/4 heads x 128, SwiGLU 6144, "
-                               "vocab 151936, 5 taps x 5120, K=16, batch 1, context 1024 (window 1024)",
-                   "batch": 1, "block_size": 16, "context": 1024, "graph_steps": r["graph_steps"]},
-        "eager_ms_per_step": round(r["eager_ms_per_step"], 4),
-        "draft_tokens_per_s": round(r["draft_tokens_per_s"], 1),
-        "cycle_hbm_frac": round(r["hbm_frac"], 4),
-        "cycle_algorithmic_bytes": int(alg["bytes"]),
-        "roofline": {"kernel": "lm_head GEMM + fused top-16 (lmhead_topk_skinny<1>)", "bound": "hbm",
-                     "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "avg_launch_ms": round(r["lm_head_ms"], 5), "launches_timed": r["lm_head_launches"],
-                     "bytes_per_launch": int(alg["lm_head_bytes"])},
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(r["cycle"], budget_s=args.cpu_budget)
-    del r["cycle"]
+    if args.traffic_probe:
+        traffic_probe(args.steps, torch)
+        return
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup}
+    if not args.no_b1:
+        cfg = synth.WORKLOADS["b1_k16"]
+        r = run_workload(cfg, args.steps, args.warmup, torch)
+        alg = r["alg"]
+        lm_gbps = alg["lm_head_bytes"] / (r["lm_head_ms"] * 1e-3) / 1e9
+        traffic = recorded_traffic(cfg.name)
+        out.update({
+            "metric": METRIC,
+            "value": round(r["blocks_per_s"], 2),
+            "unit": "blocks/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(r["ms_per_step"], 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic (seeded random-init drafter and target states)",
+            "config": {"workload": "b1_k16: 5-layer bf16 drafter, hidden 2048, 16/4 heads x 128, SwiGLU 6144, "
+                                   "vocab 151936, 5 taps x 5120, K=16, batch 1, context 1024 (window 1024)",
+                       "batch": 1, "block_size": 16, "context": 1024, "graph_steps": r["graph_steps"]},
+            "eager_ms_per_step": round(r["eager_ms_per_step"], 4),
+            "draft_tokens_per_s": round(r["draft_tokens_per_s"], 1),
+            "cycle_hbm_frac": round(r["hbm_frac"], 4),
+            "cycle_algorithmic_bytes": int(alg["bytes"]),
+            "roofline": {"kernel": "lm_head GEMM + fused top-16 (lmhead_topk_skinny<1>)", "bound": "hbm",
+                         "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                         "avg_launch_ms": round(r["lm_head_ms"], 5), "launches_timed": r["lm_head_launches"],
+                         "bytes_per_launch": int(alg["lm_head_bytes"])},
+        })
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(r["cycle"], budget_s=args.cpu_budget)
+        del r["cycle"]
     if not args.no_b32:
         c3 = synth.WORKLOADS["b32_k8_conv"]
         torch.cuda.empty_cache()

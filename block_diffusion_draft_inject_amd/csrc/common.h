@@ -40,6 +40,14 @@ __device__ __forceinline__ void st_act(float* p, size_t i, size_t, float v) { p[
 __device__ __forceinline__ float ld_act(const bf16* p, size_t i, size_t plane) { return bf2f(p[i]) + bf2f(p[i + plane]); }
 __device__ __forceinline__ float ld_act(const float* p, size_t i, size_t) { return p[i]; }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS operations, not for its
+// global loads, so prefetches stay in flight across it (__syncthreads() carries a release fence
+// that waits for every outstanding global load).  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -83,7 +91,7 @@ __device__ __forceinline__ void block_sum256(float (&v)[NV], float* scratch) {
 
 // Candidate order for top-k: higher value first, then smaller id.
 __device__ __forceinline__ bool cand_better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+  return (va > vb) | ((va == vb) & (ia < ib));   // bitwise: no short-circuit branches
 }
 
 // Wave-wide best candidate (value, id) under cand_better.
@@ -108,21 +116,22 @@ struct Top16 {
 #pragma unroll
     for (int i = 0; i < TOPK; ++i) { v[i] = NEG_INF; id[i] = ID_NONE; }
   }
-  // Insert (val, idx) if it beats the current 16th entry; keeps the list sorted.
+  // Insert (val, idx) if it beats the current 16th entry; keeps the list sorted.  Branch-free
+  // apart from the threshold test: better[] is monotone along the sorted list, so entry i
+  // takes its upper neighbour if the candidate beats that neighbour, else the candidate if it
+  // beats entry i, else stays.
   __device__ __forceinline__ void push(float val, int idx) {
     if (!cand_better(val, idx, v[TOPK - 1], id[TOPK - 1])) return;
-    bool placed = false;
+    bool b[TOPK];
+#pragma unroll
+    for (int i = 0; i < TOPK; ++i) b[i] = cand_better(val, idx, v[i], id[i]);
 #pragma unroll
     for (int i = TOPK - 1; i >= 0; --i) {
-      const bool above = (i > 0) && cand_better(val, idx, v[i > 0 ? i - 1 : 0], id[i > 0 ? i - 1 : 0]);
-      if (above) {
-        v[i] = v[i - 1];
-        id[i] = id[i - 1];
-      } else if (!placed) {
-        v[i] = val;
-        id[i] = idx;
-        placed = true;
-      }
+      const bool up = i > 0 && b[i > 0 ? i - 1 : 0];
+      const float vu = v[i > 0 ? i - 1 : 0];
+      const int iu = id[i > 0 ? i - 1 : 0];
+      v[i] = up ? vu : (b[i] ? val : v[i]);
+      id[i] = up ? iu : (b[i] ? idx : id[i]);
     }
   }
 };

@@ -40,7 +40,7 @@ size_t esize(const dflash_config* c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 // Workspace regions (byte offsets), a pure function of (config, max_batch, max_inject_rows).
 struct WsLayout {
   size_t h0, h1, act_y, act_o, act_s, qb, hsplit, kb, vb, ctx, part, o_part, m_part, l_part, tk_val, tk_id;
-  size_t ubar, cbuf, meta_seq, meta_pos, row_off, row_start, row_skip, total, gate, counters;
+  size_t ubar, cbuf, meta_seq, meta_pos, row_off, row_start, row_skip, total, counters;
   size_t bytes;
   size_t part_floats;
   int chunks_max;
@@ -175,7 +175,6 @@ WsLayout ws_layout(const dflash_config* c, int max_batch, int max_inject_rows, i
   L.row_start = take((size_t)max_seqs * 4);
   L.row_skip = take((size_t)max_seqs * 4);
   L.total = take(4);
-  L.gate = take((size_t)max_batch * (K - 1) * c->sel_rank * 4);
   L.counters = take(64);
   L.bytes = off;
   return L;
@@ -681,10 +680,7 @@ dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t*
   if (mode != DFLASH_SELECT_VITERBI && mode != DFLASH_SELECT_GREEDY) return fail(DFLASH_E_INVALID, "mode %d", (int)mode);
   if (!anchor_ids || !topk_ids || !topk_logits || !h_final || !path_ids)
     return fail(DFLASH_E_INVALID, "NULL anchor_ids, topk_ids, topk_logits, h_final or path_ids");
-  float* gate = wsp<float>(H, H->wl.gate);
-  GateArgs ga{c->block_size, c->hidden, c->sel_rank, reinterpret_cast<const float*>(h_final), H->g_WH, gate};
-  HIP_TRY(launch_sel_gate(bf(c), ga, n_seq, (hipStream_t)stream));
-  SelectArgs sa{c->block_size, c->hidden, c->sel_rank, (int)mode, c->vocab, dev_err(H), gate, anchor_ids, topk_ids,
+  SelectArgs sa{c->block_size, c->hidden, c->sel_rank, (int)mode, c->vocab, dev_err(H), anchor_ids, topk_ids,
                 topk_logits, h_final, H->g_A, H->g_B, H->g_WH, path_ids, path_score, margin};
   HIP_TRY(launch_select(bf(c), sa, n_seq, (hipStream_t)stream));
   return DFLASH_OK;

@@ -30,7 +30,6 @@ __device__ __forceinline__ int rows_valid(const GemmParams& p) {
   return p.m_dev ? max(0, min(p.M, *p.m_dev - p.m_off)) : p.M;
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
@@ -302,6 +301,181 @@ __global__ __launch_bounds__(256) void lmhead_topk_skinny(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
+// stream: at most 16 rows.  The SW waves of a workgroup split K: each wave keeps its K-slice
+// of the activations (hi and lo planes) in registers for the whole launch and streams only
+// weight rows, two 16-byte loads per lane per 64-wide chunk.  Per 16-column fragment the
+// waves' 16x16 partial tiles are summed through LDS (double-buffered, one barrier per
+// fragment) and waves 0..3 run the epilogue, each for the rows 4*g + wave.  The weight loads
+// of the next fragment are in flight during the MFMAs, the reduction and the epilogue of the
+// current one.  grid: x = fragment stride (fragments x, x + gridDim.x, ...), y = k-split.
+// ---------------------------------------------------------------------------------------
+constexpr int SW = 8;
+
+template <int SLC, int NF>
+struct StreamBuf {
+  u32x4 b[SLC][NF][2];
+};
+
+template <int SLC, int NF>
+__device__ __forceinline__ void stream_load(StreamBuf<SLC, NF>& x, const GemmParams& p, int ncols, int f, int kw,
+                                            int kg, int li) {
+#pragma unroll
+  for (int nf = 0; nf < NF; ++nf) {
+    // the 16 rows of a fragment lie in one weight segment (segment sizes and `half` are
+    // multiples of 16): its index is wave-uniform, so the segment pointer is a scalar load and
+    // never joins the vector-memory queue that the prefetches wait in
+    const int seg = __builtin_amdgcn_readfirstlane((f * 16 + nf * p.half) / p.seg_rows);
+    const int n = min(f * 16 + li, ncols - 1) + nf * p.half - seg * p.seg_rows;
+    const bf16* row = reinterpret_cast<const bf16*>(p.seg[seg]) + (size_t)n * p.ldb;
+#pragma unroll
+    for (int c = 0; c < SLC; ++c) {
+      // half h of the chunk: k = 32 h + 8 kg .. +7, so one load instruction covers 64
+      // contiguous bytes of each of the 16 rows; chunks past K carry zero activations
+      const int k = min(kw + c * 64, p.K - 64) + kg * 8;
+      x.b[c][nf][0] = *reinterpret_cast<const u32x4*>(row + k);
+      x.b[c][nf][1] = *reinterpret_cast<const u32x4*>(row + k + 32);
+    }
+  }
+}
+
+template <int SLC, int NF>
+__device__ __forceinline__ void stream_mma(const StreamBuf<SLC, NF>& x, const u32x4 (&ah)[SLC][2],
+                                           const u32x4 (&al)[SLC][2], f32x4 (&acc)[NF]) {
+#pragma unroll
+  for (int nf = 0; nf < NF; ++nf) acc[nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < SLC; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) {
+        acc[nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah[c][h]), as_bf16x8(x.b[c][nf][h]), acc[nf], 0, 0, 0);
+        acc[nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al[c][h]), as_bf16x8(x.b[c][nf][h]), acc[nf], 0, 0, 0);
+      }
+}
+
+template <int SLC, int MODE, bool LOOP>
+__global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
+  constexpr int NF = (MODE == GEMM_SWIGLU) ? 2 : 1;
+  constexpr int RED_FLOATS = 2 * NF * SW * 4 * 64;
+  constexpr int MRG = (MODE == GEMM_TOPK) ? 4 * 64 * (TOPK + 1) : 0;   // lane lists for the final merge
+  __shared__ __align__(16) float smem[RED_FLOATS + 2 * MRG];
+  float (*red)[NF][SW][4][64] = reinterpret_cast<float (*)[NF][SW][4][64]>(smem);
+  float (*mv)[64][TOPK + 1] = reinterpret_cast<float (*)[64][TOPK + 1]>(smem + RED_FLOATS);
+  int (*mi)[64][TOPK + 1] = reinterpret_cast<int (*)[64][TOPK + 1]>(smem + RED_FLOATS + MRG);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, kg = lane >> 4;
+  const int Mv = rows_valid(p);
+  const int ncols = (MODE == GEMM_SWIGLU) ? p.half : p.N;
+  const int nfrag = (ncols + 15) / 16;
+  if (Mv <= 0 || (int)blockIdx.x >= nfrag) return;    // uniform over the workgroup
+  const int s = blockIdx.y;
+  const int kw = (s * SW + wave) * SLC * 64;
+  // this wave's K-slice of the activations: lane (li, kg) holds row li, k = chunk + 16 kg .. +15
+  u32x4 ah[SLC][2], al[SLC][2];
+  {
+    const bf16* arow = reinterpret_cast<const bf16*>(p.A) + (size_t)min(li, Mv - 1) * p.lda;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < SLC; ++c) {
+      const bool ok = li < Mv && kw + c * 64 < p.K;
+      const int k = min(kw + c * 64, p.K - 64) + kg * 8;
+      const bf16* qh = arow + k;
+      const bf16* ql = arow + p.a_plane + k;
+      ah[c][0] = ok ? *reinterpret_cast<const u32x4*>(qh) : z;
+      ah[c][1] = ok ? *reinterpret_cast<const u32x4*>(qh + 32) : z;
+      al[c][0] = ok ? *reinterpret_cast<const u32x4*>(ql) : z;
+      al[c][1] = ok ? *reinterpret_cast<const u32x4*>(ql + 32) : z;
+    }
+  }
+  const int row = 4 * kg + wave;                        // epilogue row of waves 0..3
+  const bool epi = wave < 4;
+  const bool row_live = epi && row < Mv && (MODE != GEMM_TOPK || row % p.block != 0);
+  Top16 top;
+  top.init();
+  auto finish = [&](const f32x4 (&acc)[NF], int buf, int f) {
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[buf][nf][wave][j][lane] = acc[nf][j];
+    lds_barrier();
+    if (!epi) return;
+    float v[NF];
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < SW; ++w) t += red[buf][nf][w][wave][lane];
+      v[nf] = t;
+    }
+    const int col = f * 16 + li;
+    if (row >= Mv || col >= ncols) return;
+    if (MODE == GEMM_PARTIAL) {
+      p.part[((size_t)s * p.M + row) * p.N + col] = v[0];
+    } else if (MODE == GEMM_SWIGLU) {
+      st_act(reinterpret_cast<bf16*>(p.out), (size_t)row * p.half + col, p.out_plane, silu_f(v[0]) * v[NF - 1]);
+    } else {
+      if (p.logits) store_logit(p, row, col, v[0]);
+      if (row_live) top.push(v[0], col);
+    }
+  };
+  f32x4 acc[NF];
+  int f = blockIdx.x;
+  if (!LOOP) {
+    // one fragment for this workgroup
+    StreamBuf<SLC, NF> x;
+    stream_load(x, p, ncols, f, kw, kg, li);
+    stream_mma(x, ah, al, acc);
+    finish(acc, 0, f);
+  } else {
+    // ping-pong: the next fragment's loads are issued before this one's MFMAs (the scheduling
+    // barrier keeps the compiler from sinking them towards their use); loads past the last
+    // fragment are clamped to it and never used
+    const int G = gridDim.x;
+    StreamBuf<SLC, NF> x, y;
+    int buf = 0;
+    stream_load(x, p, ncols, f, kw, kg, li);
+    while (true) {
+      const int fy = f + G;
+      stream_load(y, p, ncols, min(fy, nfrag - 1), kw, kg, li);
+      __builtin_amdgcn_sched_barrier(0);
+      stream_mma(x, ah, al, acc);
+      finish(acc, buf, f);
+      if (fy >= nfrag) break;
+      f = fy;
+      buf ^= 1;
+      const int fx = f + G;
+      stream_load(x, p, ncols, min(fx, nfrag - 1), kw, kg, li);
+      __builtin_amdgcn_sched_barrier(0);
+      stream_mma(y, ah, al, acc);
+      finish(acc, buf, f);
+      if (fx >= nfrag) break;
+      f = fx;
+      buf ^= 1;
+    }
+  }
+  if (MODE != GEMM_TOPK || !epi) return;
+  // merge the 16 lane lists of each row (lanes li = 0..15 of one kg group) inside the wave
+  for (int w = 1; w < 16; w <<= 1) {
+    if ((li & (2 * w - 1)) == w) {
+#pragma unroll
+      for (int i = 0; i < TOPK; ++i) { mv[wave][lane][i] = top.v[i]; mi[wave][lane][i] = top.id[i]; }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if ((li & (2 * w - 1)) == 0) {
+#pragma unroll
+      for (int i = 0; i < TOPK; ++i) top.push(mv[wave][lane + w][i], mi[wave][lane + w][i]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  if (li == 0 && row < Mv) store_partial(p, row, blockIdx.x, top);
+}
+
+// ---------------------------------------------------------------------------------------
 // tiled: 128 x 128 x 64, LDS double buffer, 2x2 waves of 64x64.
 // ---------------------------------------------------------------------------------------
 constexpr int TBM = 128, TBN = 128, TBK = 32, TLD = TBK + 8;
@@ -507,6 +681,43 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
     return pl;
   }
   const int nchunks = K / 64;
+  if (M <= 16) {
+    // stream kernel: slice = SW waves x slc chunks of 64; full K in one workgroup for the
+    // nonlinear epilogues, k-splits for PARTIAL
+    const int ncols = (mode == GEMM_SWIGLU) ? N / 2 : N;
+    const int nfrag = (ncols + 15) / 16;
+    // workgroups loop over fragments: halve the fragment stride while it stays a divisor of
+    // the fragment count and the launch keeps more than 256 workgroups (one per CU is enough
+    // to stream; fewer, longer-lived workgroups load their activation slice fewer times)
+    auto stride = [&](int splits) {
+      int gx = nfrag;
+      while (gx % 2 == 0 && (gx / 2) * splits >= 128 && gx * splits > 256) gx /= 2;
+      return gx;
+    };
+    if (mode == GEMM_PARTIAL) {
+      pl.slc = 1;
+      while (pl.slc < 4 && (K + SW * 64 * pl.slc - 1) / (SW * 64 * pl.slc) > 8) pl.slc *= 2;
+      pl.splits = (K + SW * 64 * pl.slc - 1) / (SW * 64 * pl.slc);
+      pl.grid = dim3(stride(pl.splits), 1, 1);
+      pl.kind = 3;
+    } else {
+      pl.slc = 1;
+      while (pl.slc < 4 && SW * 64 * pl.slc < K) pl.slc *= 2;
+      if (SW * 64 * pl.slc >= K) {
+        pl.kind = 3;
+        if (mode == GEMM_TOPK) {
+          pl.groups = clampi(256, 1, nfrag);
+          pl.grid = dim3(pl.groups, 1, 1);
+        } else {
+          pl.grid = dim3(stride(1), 1, 1);
+        }
+      }
+    }
+    if (pl.kind == 3) {
+      pl.grid.y = pl.splits;
+      return pl;
+    }
+  }
   if (M <= 64) {
     pl.kind = 0;
     pl.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -548,6 +759,27 @@ hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hi
   const dim3 blk(256);
   if (pl.kind == 2) {
     hipLaunchKernelGGL(gemm_f32_kernel, pl.grid, blk, 0, st, p);
+    return hipGetLastError();
+  }
+  if (pl.kind == 3) {
+    if ((p.seg_rows % 16 && p.seg_rows < p.N) || p.half % 16) return hipErrorInvalidValue;
+    const dim3 sb(SW * 64);
+    const int ncols = (mode == GEMM_SWIGLU) ? p.half : p.N;
+    const bool loop = (int)pl.grid.x < (ncols + 15) / 16;
+#define DFL_STREAM_MODE(SLC, MODE)                                                                    \
+  if (loop) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, true>), pl.grid, sb, 0, st, p);         \
+  else hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, false>), pl.grid, sb, 0, st, p);
+#define DFL_STREAM(SLC)                                                                               \
+  if (pl.slc == SLC) {                                                                                \
+    if (mode == GEMM_TOPK) { DFL_STREAM_MODE(SLC, GEMM_TOPK) }                                        \
+    else if (mode == GEMM_SWIGLU) { DFL_STREAM_MODE(SLC, GEMM_SWIGLU) }                               \
+    else { DFL_STREAM_MODE(SLC, GEMM_PARTIAL) }                                                       \
+  }
+    DFL_STREAM(1)
+    DFL_STREAM(2)
+    DFL_STREAM(4)
+#undef DFL_STREAM
+#undef DFL_STREAM_MODE
     return hipGetLastError();
   }
   if (pl.kind == 0) {

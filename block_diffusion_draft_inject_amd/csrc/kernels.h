@@ -41,7 +41,8 @@ struct GemmParams {
 };
 
 struct GemmPlan {
-  int kind;      // 0 = skinny, 1 = tiled, 2 = f32 simple
+  int kind;      // 0 = skinny, 1 = tiled, 2 = f32 simple, 3 = stream (<= 16 rows)
+  int slc;       // stream: 64-wide chunks per wave
   int mt;        // skinny row fragments (1,2,4)
   int splits;
   int groups;    // TOPK groups

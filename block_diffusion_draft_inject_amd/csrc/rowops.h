@@ -140,21 +140,13 @@ struct AttnArgs {
   void* o;             // [rows][nh*dh]
 };
 
-struct GateArgs {
-  int K, d, r;
-  const float* h_final;
-  const void* WH;
-  float* gate;         // [n_seq][K-1][r]
-};
-
 struct SelectArgs {
   int K, d, r, mode, vocab;
   int* dev_err;
-  const float* gate;   // [n_seq][K-1][r] from sel_gate_kernel
   const int* anchor;
   const int* topk_ids;
   const float* topk_logits;
-  const void* h_final;
+  const float* h_final;   // [n_seq][K][d]
   const void* A;
   const void* B;
   const void* WH;
@@ -194,7 +186,6 @@ hipError_t launch_kv_post(bool bf, const KvPostArgs& a, int rows, int heads, hip
 hipError_t launch_reset(const ResetArgs& a, hipStream_t st);
 hipError_t launch_topk_merge(const MergeArgs& a, int out_rows, hipStream_t st);
 hipError_t launch_attention(bool bf, const AttnArgs& a, int n_seq, hipStream_t st);
-hipError_t launch_sel_gate(bool bf, const GateArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_select(bool bf, const SelectArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_synth(const SynthArgs& a, hipStream_t st);

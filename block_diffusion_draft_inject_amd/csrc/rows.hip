@@ -616,35 +616,6 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
 }
 
 // ------------------------------------------------------------------------ selector context gate
-// gate[b][t-1][j] = sigmoid(W_H[j] . h_final[b][t]) for draft slots t >= 1.  One workgroup per
-// (sequence, slot); each wave computes whole dot products (lanes stride over the row with
-// 16-byte loads), so the code stays short and the loads of one dot are issued together.
-template <typename T>
-__global__ __launch_bounds__(256) void sel_gate_kernel(GateArgs a) {
-  const int idx = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int b = idx / (a.K - 1), t = idx % (a.K - 1) + 1;
-  const int d = a.d;
-  constexpr int VE = 16 / sizeof(T);      // weight elements per 16-byte load
-  const float* h = a.h_final + ((size_t)b * a.K + t) * d;
-  const int nv = d / VE;                   // d % 64 == 0 on the host
-  for (int j = w; j < a.r; j += 4) {
-    const T* wr = reinterpret_cast<const T*>(a.WH) + (size_t)j * d;
-    float acc = 0.f;
-#pragma unroll 2
-    for (int v = lane; v < nv; v += 64) {
-      const u32x4 y = reinterpret_cast<const u32x4*>(wr)[v];
-      const T* ye = reinterpret_cast<const T*>(&y);
-#pragma unroll
-      for (int e = 0; e < VE; e += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(h + (size_t)v * VE + e);
-        acc += x[0] * ldv(ye, e) + x[1] * ldv(ye, e + 1) + x[2] * ldv(ye, e + 2) + x[3] * ldv(ye, e + 3);
-      }
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) a.gate[(size_t)idx * a.r + j] = sigmoidf_(acc);
-  }
-}
-
 // ------------------------------------------------------------------------ launchers
 #define DFL_T_DISPATCH(bf, KERNEL, grid, block, st, arg)                          \
   do {                                                                           \
@@ -702,10 +673,6 @@ hipError_t launch_kv_post(bool bf, const KvPostArgs& a, int rows, int heads, hip
 hipError_t launch_reset(const ResetArgs& a, hipStream_t st) {
   const int n = a.n > 0 ? a.n : 1;
   hipLaunchKernelGGL(reset_seqs_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-hipError_t launch_sel_gate(bool bf, const GateArgs& a, int n_seq, hipStream_t st) {
-  DFL_T_DISPATCH(bf, sel_gate_kernel, dim3(n_seq * (a.K - 1)), dim3(256), st, a);
   return hipGetLastError();
 }
 hipError_t launch_topk_merge(const MergeArgs& a, int out_rows, hipStream_t st) {

@@ -11,33 +11,133 @@
 namespace dfl {
 
 constexpr int SEL_KMAX = 32;    // block size
-constexpr int SEL_RC = 16;      // selector-rank chunk staged in LDS at a time
+constexpr int SEL_RMAX = 256;   // selector rank
+constexpr int SEL_RC = 16;      // rank chunk of the predecessor rows staged in LDS
+constexpr int SEL_NP = (SEL_KMAX - 2) * TOPK + 1;   // predecessor rows: anchor + candidates of slots 1..K-2
 
-template <typename T>
-__device__ __forceinline__ float ldsel(const void* p, size_t i) {
-  return ldv(reinterpret_cast<const T*>(p), i);
-}
-
-// order of Viterbi candidates: higher score, then smaller predecessor index, then rank
+// order of Viterbi candidates: higher score, then smaller code (2 * predecessor + rank)
 __device__ __forceinline__ bool vit_better(float s1, int c1, float s2, int c2) {
-  return s1 > s2 || (s1 == s2 && c1 < c2);
+  return (s1 > s2) | ((s1 == s2) & (c1 < c2));
 }
 
+// (s1,c1) >= (s2,c2) are a sorted best-two list; insert candidate (s,c)
+__device__ __forceinline__ void top2_push(float& s1, int& c1, float& s2, int& c2, float s, int c) {
+  const bool b1 = vit_better(s, c, s1, c1), b2 = vit_better(s, c, s2, c2);
+  s2 = b1 ? s1 : (b2 ? s : s2);
+  c2 = b1 ? c1 : (b2 ? c : c2);
+  s1 = b1 ? s : s1;
+  c1 = b1 ? c : c1;
+}
+
+// DPP quad permutation (lanes l ^ 1 for 0xB1, l ^ 2 for 0x4E inside each group of four)
+template <int CTRL>
+__device__ __forceinline__ int quad_perm_i(int v) { return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false); }
+template <int CTRL>
+__device__ __forceinline__ float quad_perm_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// merge the best-two lists of the lanes of a quad (DPP, no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ void top2_quad(float& s1, int& c1, float& s2, int& c2) {
+  const float o1 = quad_perm_f<CTRL>(s1), o2 = quad_perm_f<CTRL>(s2);
+  const int p1 = quad_perm_i<CTRL>(c1), p2 = quad_perm_i<CTRL>(c2);
+  top2_push(s1, c1, s2, c2, o1, p1);
+  top2_push(s1, c1, s2, c2, o2, p2);
+}
+
+// merge the best-two lists of this lane and lane ^ m
+__device__ __forceinline__ void top2_xor(float& s1, int& c1, float& s2, int& c2, int m) {
+  const float o1 = __shfl_xor(s1, m, WAVE), o2 = __shfl_xor(s2, m, WAVE);
+  const int p1 = __shfl_xor(c1, m, WAVE), p2 = __shfl_xor(c2, m, WAVE);
+  top2_push(s1, c1, s2, c2, o1, p1);
+  top2_push(s1, c1, s2, c2, o2, p2);
+}
+
+// gate[t-1][j] = sigmoid(W_H[j] . h_final[b][t]) for slots t = 1..K-1, into LDS.
+// bf16 tables: one 16x16 MFMA tile per (slot tile, rank tile); the four waves split the hidden
+// dimension, h enters as bf16 hi + lo planes (two MFMAs), partial tiles are summed through LDS.
+template <typename T>
+__device__ __forceinline__ void sel_gates(const SelectArgs& a, int b, float (*gt)[SEL_RMAX], float (*red)[64][4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, r = a.r, d = a.d;
+  const float* hb = a.h_final + (size_t)b * K * d;
+  if constexpr (sizeof(T) == 2) {
+    const int li = lane & 15, kg = lane >> 4;
+    const int nch = d / 32;                 // 32-wide k chunks; the waves take every 4th
+    constexpr int BATCH = 16;
+    for (int mt = 0; mt < (K + 15) / 16; ++mt)
+      for (int nt = 0; nt < (r + 15) / 16; ++nt) {
+        const float* hr = hb + (size_t)min(mt * 16 + li, K - 1) * d + kg * 8;
+        const bf16* wr = reinterpret_cast<const bf16*>(a.WH) + (size_t)min(nt * 16 + li, r - 1) * d + kg * 8;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int c0 = wave; c0 < nch; c0 += 4 * BATCH) {
+          f32x4 h0[BATCH], h1[BATCH];
+          u32x4 w[BATCH];
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {     // all loads of the batch first
+            const int c = min(c0 + 4 * u, nch - 1);
+            h0[u] = *reinterpret_cast<const f32x4*>(hr + c * 32);
+            h1[u] = *reinterpret_cast<const f32x4*>(hr + c * 32 + 4);
+            w[u] = *reinterpret_cast<const u32x4*>(wr + c * 32);
+          }
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            if (c0 + 4 * u >= nch) break;
+            u32x4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x0 = e < 2 ? h0[u][2 * e] : h1[u][2 * e - 4];
+              const float x1 = e < 2 ? h0[u][2 * e + 1] : h1[u][2 * e - 3];
+              const bf16 a0 = f2bf(x0), a1 = f2bf(x1);
+              hi[e] = (unsigned)a0 | ((unsigned)a1 << 16);
+              lo[e] = (unsigned)f2bf(x0 - bf2f(a0)) | ((unsigned)f2bf(x1 - bf2f(a1)) << 16);
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(hi), as_bf16x8(w[u]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lo), as_bf16x8(w[u]), acc, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[wave][lane][j] = acc[j];
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float g = red[0][lane][j] + red[1][lane][j] + red[2][lane][j] + red[3][lane][j];
+            const int t = mt * 16 + kg * 4 + j, jj = nt * 16 + li;   // D layout: row 4 kg + j, column li
+            if (t >= 1 && t < K && jj < r) gt[t - 1][jj] = sigmoidf_(g);
+          }
+        }
+        __syncthreads();
+      }
+  } else {
+    // fp32 tables: one wave per dot product
+    const float* wh = reinterpret_cast<const float*>(a.WH);
+    for (int e = wave; e < (K - 1) * r; e += 4) {
+      const int t = e / r + 1, j = e % r;
+      float acc = 0.f;
+      for (int k = lane; k < d; k += 64) acc += hb[(size_t)t * d + k] * wh[(size_t)j * d + k];
+      acc = wave_sum(acc);
+      if (lane == 0) gt[t - 1][j] = sigmoidf_(acc);
+    }
+    __syncthreads();
+  }
+}
+
+// Path selector for one sequence per workgroup.  Phases: candidates -> gates (in-kernel) ->
+// pair scores S_t(a, b) for all slots at once (one thread per (slot, successor), predecessor
+// rows staged in LDS by rank chunks) -> the sequential walk in one wave with shuffles only.
 template <typename T>
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
-  constexpr int NP = (SEL_KMAX - 2) * TOPK + 1;    // predecessor rows: anchor + candidates of slots 1..K-2
-  constexpr int NC = (SEL_KMAX - 1) * TOPK;        // candidate rows of slots 1..K-1
-  constexpr int VE = 16 / sizeof(T);               // table elements per 16-byte load
   __shared__ int cid[SEL_KMAX][TOPK];
   __shared__ float cu[SEL_KMAX][TOPK];
-  __shared__ __attribute__((aligned(16))) float S[SEL_KMAX][TOPK][TOPK];   // S[t-1][b][a] (successor-major)
-  __shared__ __attribute__((aligned(16))) float ta[NP][SEL_RC + 4];
-  __shared__ __attribute__((aligned(16))) float tb[NC][SEL_RC + 4];
-  __shared__ __attribute__((aligned(16))) float tg[SEL_KMAX][SEL_RC];
-  __shared__ __attribute__((aligned(16))) float d1[2][TOPK];
-  __shared__ __attribute__((aligned(16))) float d2[2][TOPK];
+  __shared__ __attribute__((aligned(16))) float gt[SEL_KMAX][SEL_RMAX];
+  __shared__ __attribute__((aligned(16))) float red[4][64][4];
+  __shared__ __attribute__((aligned(16))) float ta[SEL_NP][SEL_RC + 4];
+  __shared__ __attribute__((aligned(16))) float S[SEL_KMAX][TOPK][TOPK];   // S[t-1][b][a]
   __shared__ unsigned char bp1[SEL_KMAX][TOPK], bp2[SEL_KMAX][TOPK];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) float dv[2][TOPK];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K, r = a.r;
   int anchor = a.anchor[b];
   if (anchor < 0 || anchor >= a.vocab) {   // out-of-range token: record and read row 0
@@ -46,130 +146,159 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   }
   const int ncand = (K - 1) * TOPK, npred = (K - 2) * TOPK + 1;
   for (int e = tid; e < ncand; e += 256) {
-    cid[e / TOPK][e % TOPK] = a.topk_ids[(size_t)b * ncand + e];
+    int id = a.topk_ids[(size_t)b * ncand + e];
+    if (id < 0 || id >= a.vocab) {         // out-of-range candidate: record and read row 0
+      atomicOr(a.dev_err, 16);
+      id = 0;
+    }
+    cid[e / TOPK][e % TOPK] = id;
     cu[e / TOPK][e % TOPK] = a.topk_logits[(size_t)b * ncand + e];
   }
-  for (int e = tid; e < (K - 1) * TOPK * TOPK; e += 256) (&S[0][0][0])[e] = 0.f;
   __syncthreads();
-  // pair term, accumulated over rank chunks of SEL_RC
-  for (int r0 = 0; r0 < r; r0 += SEL_RC) {
-    const int rc = min(SEL_RC, r - r0), nvr = rc / VE;   // r % VE == 0 (checked on the host)
-    const int nload = (npred + ncand) * nvr;
-    for (int e0 = tid; e0 < nload; e0 += 4 * 256) {
-      u32x4 x[4];
-      int rowi[4], vi[4];
+  // pair scores: thread (t, bi) for t = 1..K-1 (two passes cover K up to 32), accumulated over
+  // rank chunks of SEL_RC.  The first chunk's table loads are issued before the gate phase so
+  // that their latency overlaps it.
+  constexpr int VE = 16 / sizeof(T);
+  constexpr int VPR = SEL_RC / VE;                      // 16-byte vectors per row chunk
+  constexpr int XA = (SEL_NP * VPR + 255) / 256;        // predecessor vectors per thread
+  float acc[2][TOPK];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * 256;
-        const int rr = e / nvr;
-        vi[u] = e % nvr;
-        rowi[u] = e < nload ? rr : -1;
-        int tok = 0;
-        const void* tab = a.A;
-        if (rr < npred) {
-          tok = rr == 0 ? anchor : cid[(rr - 1) / TOPK][(rr - 1) % TOPK];
-        } else if (rr < npred + ncand) {
-          tok = cid[(rr - npred) / TOPK][(rr - npred) % TOPK];
-          tab = a.B;
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int i = 0; i < TOPK; ++i) acc[q][i] = 0.f;
+  u32x4 xa[XA], xb[2][VPR];
+  auto issue = [&](int r0) {
+    const int nv = min(SEL_RC, r - r0) / VE;           // rank is a multiple of 8
+#pragma unroll
+    for (int u = 0; u < XA; ++u) {
+      const int e = tid + 256 * u, row = e / VPR, v = e % VPR;
+      const bool ok = row < npred && v < nv;
+      const int ci = max(min(row, npred - 1) - 1, 0);  // candidate index of predecessor row >= 1
+      const int tok = row == 0 ? anchor : cid[ci / TOPK][ci % TOPK];
+      xa[u] = ok ? reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.A) + (size_t)tok * r + r0)[v]
+                 : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = min(tid + 256 * q, ncand - 1);
+      const u32x4* brow = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.B) +
+                                                         (size_t)cid[e / TOPK][e % TOPK] * r + r0);
+#pragma unroll
+      for (int v = 0; v < VPR; ++v) xb[q][v] = v < nv ? brow[v] : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto consume = [&](int r0) {
+    const int rc = min(SEL_RC, r - r0);
+#pragma unroll
+    for (int u = 0; u < XA; ++u) {
+      const int e = tid + 256 * u, row = e / VPR, v = e % VPR;
+      if (row < npred) {
+        const T* xe = reinterpret_cast<const T*>(&xa[u]);
+#pragma unroll
+        for (int j = 0; j < VE; ++j) ta[row][v * VE + j] = v * VE < rc ? ldv(xe, j) : 0.f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid + 256 * q;
+      if (e >= ncand) break;
+      const int t = e / TOPK + 1;
+      float gb[SEL_RC];
+#pragma unroll
+      for (int j = 0; j < SEL_RC; ++j)
+        gb[j] = j < rc ? ldv(reinterpret_cast<const T*>(&xb[q][j / VE]), j % VE) * gt[t - 1][r0 + j] : 0.f;
+      const int p0 = t == 1 ? 0 : 1 + (t - 2) * TOPK;
+      const int na = t == 1 ? 1 : TOPK;
+#pragma unroll
+      for (int ai = 0; ai < TOPK; ++ai) {
+        if (ai >= na) break;
+        const f32x4* pa = reinterpret_cast<const f32x4*>(ta[p0 + ai]);
+        float sacc = 0.f;
+#pragma unroll
+        for (int j4 = 0; j4 < SEL_RC / 4; ++j4) {
+          const f32x4 x = pa[j4];
+          sacc += x[0] * gb[4 * j4] + x[1] * gb[4 * j4 + 1] + x[2] * gb[4 * j4 + 2] + x[3] * gb[4 * j4 + 3];
         }
-        x[u] = e < nload ? reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(tab) + (size_t)tok * r + r0)[vi[u]]
-                         : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (rowi[u] < 0) continue;
-        const int rr = rowi[u];
-        float* dst = rr < npred ? &ta[rr][vi[u] * VE] : &tb[rr - npred][vi[u] * VE];
-        const T* xe = reinterpret_cast<const T*>(&x[u]);
-#pragma unroll
-        for (int j = 0; j < VE; ++j) dst[j] = ldv(xe, j);
+        acc[q][ai] += sacc;
       }
     }
-    for (int e = tid; e < (K - 1) * rc; e += 256)
-      tg[e / rc][e % rc] = a.gate[((size_t)b * (K - 1) + e / rc) * r + r0 + e % rc];
     __syncthreads();
-    const int npairs = TOPK + (K - 2) * TOPK * TOPK;
-    for (int e = tid; e < npairs; e += 256) {
-      int t, ai, bi;
-      if (e < TOPK) { t = 1; ai = 0; bi = e; }
-      else { const int f = e - TOPK; t = 2 + f / (TOPK * TOPK); ai = (f / TOPK) % TOPK; bi = f % TOPK; }
-      const f32x4* pa = reinterpret_cast<const f32x4*>(ta[t == 1 ? 0 : 1 + (t - 2) * TOPK + ai]);
-      const f32x4* pb = reinterpret_cast<const f32x4*>(tb[(t - 1) * TOPK + bi]);
-      const f32x4* pg = reinterpret_cast<const f32x4*>(tg[t - 1]);
-      f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < SEL_RC / 4; ++q)
-        if (4 * q < rc) acc4 += pa[q] * pg[q] * pb[q];
-      S[t - 1][bi][ai] += acc4[0] + acc4[1] + acc4[2] + acc4[3];
-    }
-    __syncthreads();
+  };
+  issue(0);
+  sel_gates<T>(a, b, gt, red);              // ends with a barrier: gt visible
+  consume(0);
+  for (int r0 = SEL_RC; r0 < r; r0 += SEL_RC) {
+    issue(r0);
+    consume(r0);
   }
-  for (int e = tid; e < (K - 1) * TOPK * TOPK; e += 256) {
-    const int t1 = e / (TOPK * TOPK), bi = (e / TOPK) % TOPK;
-    (&S[0][0][0])[e] += cu[t1][bi];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = tid + 256 * q;
+    if (e >= ncand) break;
+    const int t = e / TOPK + 1, bi = e % TOPK;
+#pragma unroll
+    for (int ai = 0; ai < TOPK; ++ai) S[t - 1][bi][ai] = acc[q][ai] + cu[t - 1][bi];
   }
   __syncthreads();
-  // walk
+  if (wave != 0) return;
+  // ---- the walk: one wave; lane = 4 * bi + qa holds predecessors a = 4 qa .. 4 qa + 3 of state bi
+  const int bi = lane >> 2, qa = lane & 3;
   if (a.mode == 0) {
-    if (tid < TOPK) {
-      d1[0][tid] = S[0][tid][0];
-      d2[0][tid] = NEG_INF;
+    // partial-path scores of the previous slot live in LDS (dv[0][a] = best, dv[1][a] = second);
+    // each lane reads its four predecessors with two 16-byte reads, the quad merges by DPP
+    if (lane < TOPK) {
+      dv[0][lane] = S[0][lane][0];           // slot 1: the single path anchor -> lane
+      dv[1][lane] = NEG_INF;
     }
-    __syncthreads();
-    int cur = 0;
+    float d1 = 0.f, d2 = 0.f;
     for (int t = 2; t < K; ++t) {
-      if (tid < TOPK) {
-        const int bi = tid;
-        float s1 = NEG_INF, s2 = NEG_INF;
-        int c1 = 255, c2 = 255;
-        float p1[TOPK], p2[TOPK], sa_[TOPK];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const f32x4 p1v = *reinterpret_cast<const f32x4*>(&dv[0][4 * qa]);
+      const f32x4 p2v = *reinterpret_cast<const f32x4*>(&dv[1][4 * qa]);
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(&S[t - 1][bi][4 * qa]);
+      float s1 = NEG_INF, s2 = NEG_INF;
+      int c1 = 255, c2 = 255;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 x1 = reinterpret_cast<const f32x4*>(d1[cur])[q];
-          const f32x4 x2 = reinterpret_cast<const f32x4*>(d2[cur])[q];
-          const f32x4 xs = reinterpret_cast<const f32x4*>(S[t - 1][bi])[q];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) { p1[4 * q + j] = x1[j]; p2[4 * q + j] = x2[j]; sa_[4 * q + j] = xs[j]; }
-        }
-#pragma unroll
-        for (int ai = 0; ai < TOPK; ++ai) {
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const float prev = k == 0 ? p1[ai] : p2[ai];
-            if (prev == NEG_INF) continue;
-            const float sc = prev + sa_[ai];
-            const int code = ai * 2 + k;
-            if (vit_better(sc, code, s1, c1)) {
-              s2 = s1; c2 = c1;
-              s1 = sc; c1 = code;
-            } else if (vit_better(sc, code, s2, c2)) {
-              s2 = sc; c2 = code;
-            }
-          }
-        }
-        d1[cur ^ 1][bi] = s1;
-        d2[cur ^ 1][bi] = s2;
+      for (int i = 0; i < 4; ++i) {
+        const int ai = 4 * qa + i;
+        // candidates in code order 2 ai (rank 1), 2 ai + 1 (rank 2); an absent path enters as
+        // (-inf, 255), which never beats a list entry, i.e. it is skipped
+        top2_push(s1, c1, s2, c2, p1v[i] + sv[i], p1v[i] != NEG_INF ? 2 * ai : 255);
+        top2_push(s1, c1, s2, c2, p2v[i] + sv[i], p2v[i] != NEG_INF ? 2 * ai + 1 : 255);
+      }
+      top2_quad<0xB1>(s1, c1, s2, c2);
+      top2_quad<0x4E>(s1, c1, s2, c2);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (qa == 0) {
+        dv[0][bi] = s1;
+        dv[1][bi] = s2;
         bp1[t - 1][bi] = (unsigned char)c1;
         bp2[t - 1][bi] = (unsigned char)c2;
       }
-      __syncthreads();
-      cur ^= 1;
+      d1 = s1;
+      d2 = s2;
     }
-    if (tid == 0) {
-      float s1 = NEG_INF, s2 = NEG_INF;
-      int c1 = 255, c2 = 255;
-      for (int bi = 0; bi < TOPK; ++bi)
-        for (int k = 0; k < 2; ++k) {
-          const float sc = k == 0 ? d1[cur][bi] : d2[cur][bi];
-          if (sc == NEG_INF) continue;
-          const int code = bi * 2 + k;
-          if (vit_better(sc, code, s1, c1)) {
-            s2 = s1; c2 = c1;
-            s1 = sc; c1 = code;
-          } else if (vit_better(sc, code, s2, c2)) {
-            s2 = sc; c2 = code;
-          }
-        }
+    if (K == 2) {
+      d1 = S[0][bi][0];
+      d2 = NEG_INF;
+    }
+    // best two complete paths over the states of slot K-1 (code 2 bi + rank)
+    float s1 = NEG_INF, s2 = NEG_INF;
+    int c1 = 255, c2 = 255;
+    if (qa == 0) {
+      if (d1 != NEG_INF) top2_push(s1, c1, s2, c2, d1, 2 * bi);
+      if (d2 != NEG_INF) top2_push(s1, c1, s2, c2, d2, 2 * bi + 1);
+    }
+    for (int m = 4; m < 64; m <<= 1) top2_xor(s1, c1, s2, c2, m);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane == 0) {
       int st = c1 >> 1, rank = c1 & 1;
       for (int t = K - 1; t >= 1; --t) {
         a.path[(size_t)b * (K - 1) + t - 1] = cid[t - 1][st];
@@ -183,22 +312,31 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
       if (a.margin) a.margin[b] = s1 - s2;
     }
   } else {
-    if (tid == 0) {
-      int ai = 0;
-      float total = 0.f, margin = __builtin_huge_valf();
-      for (int t = 1; t < K; ++t) {
-        float s1 = NEG_INF, s2 = NEG_INF;
-        int c1 = 0;
-        for (int bi = 0; bi < TOPK; ++bi) {
-          const float sc = S[t - 1][bi][ai];
-          if (sc > s1) { s2 = s1; s1 = sc; c1 = bi; }
-          else if (sc > s2) { s2 = sc; }
-        }
-        margin = fminf(margin, s1 - s2);
-        total += s1;
-        a.path[(size_t)b * (K - 1) + t - 1] = cid[t - 1][c1];
-        ai = c1;
+    // greedy: from the current candidate, the best successor (ties to the smaller index)
+    int ai = 0;
+    float total = 0.f, margin = __builtin_huge_valf();
+    for (int t = 1; t < K; ++t) {
+      const float v = lane < TOPK ? S[t - 1][lane][ai] : NEG_INF;
+      float m1 = v;
+      int i1 = lane < TOPK ? lane : 255;
+      for (int m = 1; m < TOPK; m <<= 1) {
+        const float ov = __shfl_xor(m1, m, WAVE);
+        const int oi = __shfl_xor(i1, m, WAVE);
+        const bool take = (ov > m1) | ((ov == m1) & (oi < i1));
+        m1 = take ? ov : m1;
+        i1 = take ? oi : i1;
       }
+      m1 = __shfl(m1, 0, WAVE);
+      i1 = __shfl(i1, 0, WAVE);
+      float sec = (lane < TOPK && lane != i1) ? v : NEG_INF;
+      for (int m = 1; m < TOPK; m <<= 1) sec = fmaxf(sec, __shfl_xor(sec, m, WAVE));
+      sec = __shfl(sec, 0, WAVE);
+      margin = fminf(margin, m1 - sec);
+      total += m1;
+      if (lane == 0) a.path[(size_t)b * (K - 1) + t - 1] = cid[t - 1][i1];
+      ai = i1;
+    }
+    if (lane == 0) {
       if (a.score) a.score[b] = total;
       if (a.margin) a.margin[b] = margin;
     }

@@ -225,7 +225,8 @@ DFLASH_API dflash_status dflash_timing_read(dflash_handle* h, double* total_ms /
 
 /* Reads (and keeps) the device error word; synchronises the device.  0 = none.
  * Bits: 1 = sequence id out of range, 2 = n_new outside [0, max_new], 4 = negative start_pos,
- * 8 = anchor token id outside [0, vocab). */
+ * 8 = anchor token id outside [0, vocab), 16 = candidate id (dflash_select_path's topk_ids)
+ * outside [0, vocab): the selector reads row 0 of A and B for it and still reports that id. */
 DFLASH_API dflash_status dflash_get_device_error(dflash_handle* h, int32_t* code /* host */);
 
 DFLASH_API const char* dflash_status_string(dflash_status s);

@@ -33,8 +33,12 @@ def _prefill(case, seq_ids, spans):
 
 
 def _full_check(H, case, seq_ids, spans, anchors, mode_names=("viterbi", "greedy")):
-    cfg = case.cfg
     _prefill(case, seq_ids, spans)
+    return _check(H, case, seq_ids, anchors, mode_names)
+
+
+def _check(H, case, seq_ids, anchors, mode_names=("viterbi", "greedy")):
+    cfg = case.cfg
     worst, same = H.check_kv(case, seq_ids)
     H.log(f"[kv] {cfg.name}: worst rel err {worst:.2e}, bit-equal {same:.4f}")
     assert worst <= 1.0
@@ -132,3 +136,30 @@ def test_mid_bf16_selector_stress(H):
     """A, B ~ N(0,1): the pair term dominates, Viterbi != greedy != per-position argmax."""
     case = H.Case(MID, max_seqs=4, max_batch=4, max_inject_rows=64, selector_stress=True)
     _full_check(H, case, [0, 1, 2, 3], [(0, 70), (0, 20), (0, 64), (5, 90)], anchors=[1, 2, 3, 4])
+
+
+def test_mid_bf16_single_block_16_rows(H):
+    """One sequence at K=16: every draft GEMM has 16 rows (k-split kernels with the activation
+    slice held in registers), and injections of at most 16 rows per call, ragged, so the
+    injection GEMMs run with a device-side row count."""
+    case = H.Case(MID, max_seqs=2, max_batch=1, max_inject_rows=16)
+    case.reset([1])
+    L = 0
+    for n in (16, 5, 1, 16, 9, 16, 16):       # 79 rows: the 64-slot ring wraps
+        case.inject([1], [np.arange(L, L + n)], start_pos=(L == 0))
+        L += n
+    _check(H, case, [1], anchors=[4242])
+
+
+def test_mid_bf16_two_blocks_k8_ragged_inject(H):
+    """K=8, two sequences (16 rows), injected together with ragged row counts per call."""
+    cfg = MID.replace(block_size=8, name="mid_bf16_k8")
+    case = H.Case(cfg, max_seqs=4, max_batch=2, max_inject_rows=16)
+    seq_ids = [3, 1]
+    case.reset(seq_ids)
+    Ls = [0, 0]
+    for n0, n1 in ((7, 1), (1, 8), (8, 0), (3, 5)):
+        pos = [np.arange(Ls[0], Ls[0] + n0), np.arange(Ls[1], Ls[1] + n1)]
+        case.inject(seq_ids, pos, start_pos=(Ls == [0, 0]))
+        Ls = [Ls[0] + n0, Ls[1] + n1]
+    _check(H, case, seq_ids, anchors=[12, 8190])
