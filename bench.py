@@ -199,7 +199,7 @@ def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10):
 
 # ----------------------------------------------------------------------------- cpu baseline
 
-def cpu_baseline(cyc, budget_s=20.0, max_cycles=20):
+def cpu_baseline(cyc, budget_s=20.0, max_cycles=10000):
     """The CPU oracle (as it stands) running the same drafter cycle on the host cores, on a
     bounded sample: prefill of the same context, then cycles until the time budget is spent."""
     import numpy as np
@@ -270,6 +270,7 @@ def recorded_traffic(workload):
 # ----------------------------------------------------------------------------- counter passes
 
 COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
+LM_KERNEL = "gemm_stream_kernel<4, 2, true>"   # lm_head + top-16 at batch 1 (k-slice 4, TOPK mode, looping)
 
 
 def traffic_probe(steps, torch):
@@ -308,7 +309,7 @@ def traffic_record(fetch_csv, write_csv, workload="b1_k16"):
     res = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = [r for r in _counter_rows(path) if r[2] == name]
-        lm = [v for _, k, _, v in rows if "lmhead_topk" in k]
+        lm = [v for _, k, _, v in rows if LM_KERNEL in k]
         copies = sorted([(i, v) for i, k, _, v in rows if "elementwise" in k])[-3:]
         if not lm or len(copies) < 3:
             raise SystemExit(f"{path}: no lm_head dispatches or fewer than 3 copy dispatches")
@@ -316,10 +317,11 @@ def traffic_record(fetch_csv, write_csv, workload="b1_k16"):
         scale = COPY_BYTES / (copy_kib * 1024.0)
         res[name] = dict(kib_per_launch=sum(lm) / len(lm), launches=len(lm), copy_kib=copy_kib, scale=scale)
     f, w = res["FETCH_SIZE"], res["WRITE_SIZE"]
-    rec = dict(kernel="lmhead_topk_skinny<1>", workload=workload, kernel_hash=kernel_hash(),
+    rec = dict(kernel=LM_KERNEL, workload=workload, kernel_hash=kernel_hash(),
                fetch=f, write=w, copy_bytes=COPY_BYTES,
                bytes_per_launch=int(round(f["kib_per_launch"] * 1024 * f["scale"]
                                           + w["kib_per_launch"] * 1024 * w["scale"])))
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     out = os.path.join(ROOT, "profiles", f"lmhead_topk_{workload}_traffic.json")
     json.dump(rec, open(out, "w"), indent=1)
     print(json.dumps(rec))
@@ -384,7 +386,7 @@ def main():
             "draft_tokens_per_s": round(r["draft_tokens_per_s"], 1),
             "cycle_hbm_frac": round(r["hbm_frac"], 4),
             "cycle_algorithmic_bytes": int(alg["bytes"]),
-            "roofline": {"kernel": "lm_head GEMM + fused top-16 (lmhead_topk_skinny<1>)", "bound": "hbm",
+            "roofline": {"kernel": f"lm_head GEMM + fused top-16 ({LM_KERNEL})", "bound": "hbm",
                          "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                          "avg_launch_ms": round(r["lm_head_ms"], 5), "launches_timed": r["lm_head_launches"],
