@@ -216,10 +216,10 @@ DFLASH_API dflash_status dflash_synth_target_argmax(int32_t n_seq, int32_t block
 
 /* Kernel timing for measurement: while enabled, each dflash_draft_block records a pair of HIP
  * events around its lm_head + top-16 kernel on the call's stream (pair index advances modulo
- * capacity; under stream capture the event records become graph nodes and are re-recorded on
- * every replay).  dflash_timing_read waits for the pairs recorded so far (at most capacity)
- * and returns their summed milliseconds and count.  dflash_timing_enable re-creates the
- * events and clears the count; capacity 0 disables. */
+ * capacity).  Disable it (capacity 0) before capturing a graph: events recorded inside a
+ * captured graph cannot be read back.  dflash_timing_read waits for the pairs recorded so far
+ * (at most capacity) and returns their summed milliseconds and count.  dflash_timing_enable
+ * re-creates the events and clears the count; capacity 0 disables. */
 DFLASH_API dflash_status dflash_timing_enable(dflash_handle* h, int32_t capacity);
 DFLASH_API dflash_status dflash_timing_read(dflash_handle* h, double* total_ms /* host */, int32_t* count /* host */);
 
