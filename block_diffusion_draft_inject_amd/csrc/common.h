@@ -50,15 +50,34 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// Cross-lane data movement with DPP (no LDS round trip).  Controls used: quad_perm [1,0,3,2]
+// (0xB1), quad_perm [2,3,0,1] (0x4E), row_half_mirror (0x141: lane i <- lane 7-i within 8),
+// row_mirror (0x140: lane i <- lane 15-i within 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Wave-wide sum / max, the same value in every lane.  Needs all 64 lanes active.  Within each
+// row of 16 lanes the four symmetric DPP steps leave every lane with the row total (a + b is
+// evaluated as b + a in the partner lane: identical rounding); the four row totals are then
+// combined in lane order, so the result is deterministic.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return ((lane_f(v, 0) + lane_f(v, 16)) + lane_f(v, 32)) + lane_f(v, 48);
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // Block-wide sum of NV values at once for a block of NT threads; scratch holds (NT/64)*NV floats.
@@ -68,12 +87,12 @@ __device__ __forceinline__ void block_sum(float (&v)[NV], float* scratch) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < NV; ++i) v[i] = wave_sum(v[i]);
-  __syncthreads();
+  lds_barrier();
   if (lane == 0) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) scratch[w * NV + i] = v[i];
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     float t = 0.f;
@@ -81,7 +100,7 @@ __device__ __forceinline__ void block_sum(float (&v)[NV], float* scratch) {
     for (int k = 0; k < NW; ++k) t += scratch[k * NV + i];
     v[i] = t;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 template <int NV>
@@ -104,6 +123,7 @@ __device__ __forceinline__ void wave_best(float& v, int& id) {
   }
 }
 
+constexpr int NCOUNTERS = 64;   // lm_head work counters (one per 128-row tile), zeroed by the draft plan
 constexpr int TOPK = 16;
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr int ID_NONE = 0x7fffffff;

@@ -175,7 +175,7 @@ WsLayout ws_layout(const dflash_config* c, int max_batch, int max_inject_rows, i
   L.row_start = take((size_t)max_seqs * 4);
   L.row_skip = take((size_t)max_seqs * 4);
   L.total = take(4);
-  L.counters = take(64);
+  L.counters = take(NCOUNTERS * 4);
   L.bytes = off;
   return L;
 }
@@ -200,12 +200,14 @@ dflash_status check_cfg(const dflash_config* c) {
   if (c->n_taps < 1 || c->target_hidden < 1) return fail(DFLASH_E_INVALID, "n_taps and target_hidden must be positive");
   if (c->ffn < 1) return fail(DFLASH_E_INVALID, "ffn must be positive");
   if ((c->n_taps * c->target_hidden) % 8) return fail(DFLASH_E_UNSUPPORTED, "n_taps*target_hidden must be a multiple of 8");
+  if (c->n_taps * c->target_hidden > (c->dtype == DFLASH_BF16 ? 65536 : 32768))
+    return fail(DFLASH_E_UNSUPPORTED, "n_taps*target_hidden must be <= 65536 (bf16) or 32768 (fp32)");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 1.f)) return fail(DFLASH_E_INVALID, "rms_eps >= 0 and rope_theta > 1 required");
   if (c->dtype == DFLASH_BF16) {
     if (c->head_dim != 128) return fail(DFLASH_E_UNSUPPORTED, "bf16 attention needs head_dim 128");
     const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
-    if (c->ffn % 64 || qw % 64 || (c->n_taps * c->target_hidden) % 64)
-      return fail(DFLASH_E_UNSUPPORTED, "bf16 GEMMs need ffn, n_heads*head_dim and the concat width to be multiples of 64");
+    if (c->ffn % 128 || qw % 64 || (c->n_taps * c->target_hidden) % 64)
+      return fail(DFLASH_E_UNSUPPORTED, "bf16 GEMMs need ffn a multiple of 128, n_heads*head_dim and the concat width multiples of 64");
     if (qw % kvw) return fail(DFLASH_E_UNSUPPORTED, "n_heads*head_dim must be a multiple of n_kv_heads*head_dim");
     if ((qw / kvw) + 2 > MAX_SEG || 2 * c->n_layers > MAX_SEG) return fail(DFLASH_E_UNSUPPORTED, "too many weight segments");
   } else {

@@ -10,7 +10,6 @@
 
 namespace dfl {
 
-constexpr int MAXV = 16;   // hidden <= 16 * 256
 
 template <typename T>
 __device__ __forceinline__ float ldw(const void* p, size_t i) {
@@ -34,7 +33,7 @@ __device__ __forceinline__ void rope_cs(long pos, int i, int dh, double log_thet
 // slots (mod window) starting at slot0.
 __global__ __launch_bounds__(256) void draft_plan_kernel(PlanArgs a) {
   const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b < 4 && a.counters) a.counters[b] = 0;   // lm_head work-stealing counters of this call
+  if (b < NCOUNTERS && a.counters) a.counters[b] = 0;   // lm_head work counters of this call
   if (b >= a.n_seq) return;
   int sid = a.seq_ids[b];
   if (sid < 0 || sid >= a.max_seqs) {
@@ -52,62 +51,6 @@ __global__ __launch_bounds__(256) void draft_plan_kernel(PlanArgs a) {
 }
 
 // ------------------------------------------------------------------------ embed + pre
-template <typename T>
-__global__ __launch_bounds__(256) void embed_pre_kernel(RowArgs a) {
-  __shared__ float red[4 * 4];
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const int b = row / a.K, t = row % a.K;
-  const int d = a.d;
-  int anchor = a.anchor[b];
-  if (anchor < 0 || anchor >= a.vocab) {   // out-of-range token: record and read row 0
-    if (tid == 0 && t == 0) atomicOr(a.dev_err, 8);
-    anchor = 0;
-  }
-  const int id_t = (t == 0) ? anchor : a.mask_id;
-  const int id_p = (t <= 1) ? anchor : a.mask_id;
-  float e[2][MAXV];
-  float ss[2] = {0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int k = i * 256 + tid;
-    e[0][i] = e[1][i] = 0.f;
-    if (k < d) {
-      e[0][i] = ldw<T>(a.embed, (size_t)id_t * d + k);
-      e[1][i] = (t > 0) ? ldw<T>(a.embed, (size_t)id_p * d + k) : 0.f;
-      ss[0] += e[0][i] * e[0][i];
-      ss[1] += e[1][i] * e[1][i];
-      a.h_out[(size_t)row * d + k] = e[0][i];
-    }
-  }
-  block_sum256<2>(ss, red);
-  const float r0 = rsqrtf(ss[0] / d + a.eps), r1 = rsqrtf(ss[1] / d + a.eps);
-  float dot[2] = {0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int k = i * 256 + tid;
-    if (k < d) {
-      const float g = ldw<T>(a.pre_gain, k);
-      e[0][i] *= r0 * g;
-      e[1][i] *= r1 * g;
-      if (a.use_conv) {
-        dot[0] += ldw<T>(a.pre_w, k) * e[0][i];
-        dot[1] += ldw<T>(a.pre_w, d + k) * e[0][i];
-      }
-    }
-  }
-  float k0 = 1.f, k1 = 0.f;
-  if (a.use_conv) {
-    block_sum256<2>(dot, red);
-    k0 = sigmoidf_(dot[0] + ldw<T>(a.pre_b, 0));
-    k1 = sigmoidf_(dot[1] + ldw<T>(a.pre_b, 1));
-  }
-#pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int k = i * 256 + tid;
-    if (k < d) st_act(reinterpret_cast<T*>(a.y), (size_t)row * a.ldy + k, a.y_plane, k0 * e[0][i] + k1 * e[1][i]);
-  }
-}
-
 // ------------------------------------------------------------------------ post + pre
 // h_out[t] = h_in[t] + Conv_post(a)_t with a = sum of `splits` partials of the sublayer output,
 // then y[t] = Conv_pre(RMSNorm(h_out))_t  (or, final: y[t] = RMSNorm(h_out[t]) * final gain).
@@ -119,6 +62,27 @@ constexpr int PP_T = 512;
 constexpr int PP_MAXS = 8;   // k-splits of the producing GEMM (the planner keeps it <= 8)
 
 __device__ __forceinline__ f32x4 ld4f(const float* p, size_t i) { return *reinterpret_cast<const f32x4*>(p + i); }
+// Four consecutive weights as raw storage (loaded now, converted later).
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<float> {
+  using type = f32x4;
+  __device__ static type zero() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ static type load(const void* p, size_t i) { return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + i); }
+  __device__ static f32x4 cvt(type v) { return v; }
+};
+template <>
+struct Raw4<bf16> {
+  using type = uint2;
+  __device__ static type zero() { return uint2{0u, 0u}; }
+  __device__ static type load(const void* p, size_t i) { return *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16*>(p) + i); }
+  __device__ static f32x4 cvt(type u) {
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+  }
+};
+
 template <typename T>
 __device__ __forceinline__ f32x4 ld4w(const void* p, size_t i) {
   if constexpr (sizeof(T) == 4) {
@@ -162,20 +126,35 @@ __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
   const bool fin = a.final_norm != 0;
   const int q0 = conv ? max(0, 2 - t) : 2;       // first of rows t-2, t-1, t that exists
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  // Every load is issued, unconditionally and before any value is used, at an address that is
+  // always valid (clamped index; the gain vector stands in for absent conv weights); values
+  // that do not apply are masked afterwards.  A load under a condition makes the compiler wait
+  // for it inside the condition, which would serialise the loads.
+  using W4 = typename Raw4<T>::type;
   f32x4 hv[2][NV], pw[2][NV], qw[2][NV], g[NV];
+  W4 rpw[2][NV], rqw[2][NV], rg[NV];
   f32x4 pv[PP_MAXS][3][NV];
+  const bool pre = conv && !fin;
+  const void* pwp = conv ? a.post_w : a.pre_gain;
+  const void* qwp = pre ? a.pre_w : a.pre_gain;
+  const int wd = conv ? d : 0, qd = pre ? d : 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int k = (i * PP_T + tid) * 4;
-    const bool in = k < d;
-    hv[1][i] = in ? ld4f(a.h_in, (size_t)row * d + k) : z4;
-    hv[0][i] = (in && conv && t >= 1) ? ld4f(a.h_in, (size_t)(row - 1) * d + k) : z4;
-    pw[0][i] = (in && conv) ? ld4w<T>(a.post_w, k) : z4;
-    pw[1][i] = (in && conv) ? ld4w<T>(a.post_w, d + k) : z4;
-    qw[0][i] = (in && conv && !fin) ? ld4w<T>(a.pre_w, k) : z4;
-    qw[1][i] = (in && conv && !fin) ? ld4w<T>(a.pre_w, d + k) : z4;
-    g[i] = in ? ld4w<T>(a.pre_gain, k) : z4;
+    const int kc = k < d ? k : 0;
+    hv[1][i] = ld4f(a.h_in, (size_t)row * d + kc);
+    hv[0][i] = ld4f(a.h_in, (size_t)(t >= 1 ? row - 1 : row) * d + kc);
+    rpw[0][i] = Raw4<T>::load(pwp, kc);
+    rpw[1][i] = Raw4<T>::load(pwp, wd + kc);
+    rqw[0][i] = Raw4<T>::load(qwp, kc);
+    rqw[1][i] = Raw4<T>::load(qwp, qd + kc);
+    rg[i] = Raw4<T>::load(a.pre_gain, kc);
   }
+  // conv biases: raw, in the same burst (the gain stands in when absent)
+  const T* pbp = reinterpret_cast<const T*>(conv ? a.post_b : a.pre_gain);
+  const T* qbp = reinterpret_cast<const T*>(pre ? a.pre_b : a.pre_gain);
+  const T rpb0 = pbp[0], rpb1 = pbp[1], rqb0 = qbp[0], rqb1 = qbp[1];
+  const int nsp = max(a.splits, 1);
 #pragma unroll
   for (int sp = 0; sp < PP_MAXS; ++sp)
 #pragma unroll
@@ -183,11 +162,32 @@ __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int k = (i * PP_T + tid) * 4;
-        pv[sp][q][i] = (sp < a.splits && q >= q0 && k < d)
-                           ? ld4f(a.part, ((size_t)sp * a.part_rows + (row - 2 + q)) * d + k) : z4;
+        const int kc = k < d ? k : 0;
+        const int spc = min(sp, nsp - 1), qc = max(q, q0);
+        pv[sp][q][i] = ld4f(a.part, ((size_t)spc * a.part_rows + (row - 2 + qc)) * d + kc);
       }
-  const float pb0 = conv ? ldw<T>(a.post_b, 0) : 0.f, pb1 = conv ? ldw<T>(a.post_b, 1) : 0.f;
-  const float qb0 = (conv && !fin) ? ldw<T>(a.pre_b, 0) : 0.f, qb1 = (conv && !fin) ? ldw<T>(a.pre_b, 1) : 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const bool in = (i * PP_T + tid) * 4 < d;
+    if (!(in && conv && t >= 1)) hv[0][i] = z4;
+    if (!in) hv[1][i] = z4;
+#pragma unroll
+    for (int sp = 0; sp < PP_MAXS; ++sp)
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        if (!(in && sp < a.splits && q >= q0)) pv[sp][q][i] = z4;
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const bool in = (i * PP_T + tid) * 4 < d;
+    pw[0][i] = (in && conv) ? Raw4<T>::cvt(rpw[0][i]) : z4;
+    pw[1][i] = (in && conv) ? Raw4<T>::cvt(rpw[1][i]) : z4;
+    qw[0][i] = (in && pre) ? Raw4<T>::cvt(rqw[0][i]) : z4;
+    qw[1][i] = (in && pre) ? Raw4<T>::cvt(rqw[1][i]) : z4;
+    g[i] = in ? Raw4<T>::cvt(rg[i]) : z4;
+  }
+  const float pb0 = conv ? ldv(&rpb0, 0) : 0.f, pb1 = conv ? ldv(&rpb1, 0) : 0.f;
+  const float qb0 = pre ? ldv(&rqb0, 0) : 0.f, qb1 = pre ? ldv(&rqb1, 0) : 0.f;
   f32x4 s[3][NV];
 #pragma unroll
   for (int q = 0; q < 3; ++q)
@@ -408,56 +408,144 @@ __global__ __launch_bounds__(256) void inject_plan_kernel(InjectArgs a) {
 }
 
 // u_bar = RMSNorm(concatenated states) * gain for compacted rows [chunk0, chunk0 + rows).
-template <typename T>
-__global__ __launch_bounds__(256) void concat_norm_kernel(InjectArgs a) {
-  __shared__ float red[4];
-  __shared__ int s_i;
+// ū = RMSNorm(u) * g over the concatenated tapped states of one injected row.  One workgroup
+// per row: the row's sequence is found by every thread testing one sequence's row range (all
+// bookkeeping loads at once), then the whole row (NVC 16-byte vectors per thread) and the gain
+// are loaded in one burst and kept in registers for the scaling pass.
+constexpr int CN_T = 512;
+template <typename T, int NVC>
+__global__ __launch_bounds__(CN_T) void concat_norm_kernel(InjectArgs a) {
+  __shared__ float red[(CN_T / 64) * 1];
+  __shared__ int s_i, s_r, s_skip;
   const int j = a.chunk0 + blockIdx.x, tid = threadIdx.x;
-  const int total = *a.total;
   const int lr = blockIdx.x;
+  const int total = *a.total;
+  for (int i = tid; i < a.n_seq; i += CN_T) {
+    const int o0 = a.row_off[i], o1 = a.row_off[i + 1], sk = a.row_skip[i], st0 = a.row_start[i], sid = a.seq_ids[i];
+    if (o0 <= j && j < o1) {
+      s_i = i;
+      s_r = j - o0;
+      s_skip = sk;
+      a.meta_seq[lr] = sid;
+      a.meta_pos[lr] = st0 + (j - o0);
+    }
+  }
   if (j >= total) {
     if (tid == 0) { a.meta_seq[lr] = -1; a.meta_pos[lr] = 0; }
     return;
   }
-  if (tid == 0) {
-    int i = 0;
-    while (a.row_off[i + 1] <= j) ++i;
-    s_i = i;
-  }
   __syncthreads();
-  const int i = s_i;
-  const int r = j - a.row_off[i];
-  if (tid == 0) { a.meta_seq[lr] = a.seq_ids[i]; a.meta_pos[lr] = a.row_start[i] + r; }
+  const int i = s_i, r = s_r, skip = s_skip;
   const int W = a.concat;
-  const T* src = reinterpret_cast<const T*>(a.states) + ((size_t)i * a.max_new + r + a.row_skip[i]) * W;
-  T* dst = reinterpret_cast<T*>(a.ubar) + (size_t)lr * W;
   constexpr int VE = 16 / sizeof(T);          // elements per 16-byte vector
   const int nv = W / VE;                      // W % VE == 0 (checked on the host)
-  const u32x4* sv = reinterpret_cast<const u32x4*>(src);
-  float ss[1] = {0.f};
-#pragma unroll 4
-  for (int v = tid; v < nv; v += 256) {
-    const u32x4 x = sv[v];
-    const T* e = reinterpret_cast<const T*>(&x);
+  const u32x4* sv = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.states) + ((size_t)i * a.max_new + r + skip) * W);
+  const u32x4* gv = reinterpret_cast<const u32x4*>(a.gain);
+  u32x4 x[NVC], g[NVC];
 #pragma unroll
-    for (int j = 0; j < VE; ++j) {
-      const float f = ldv(e, j);
+  for (int u = 0; u < NVC; ++u) {
+    const int v = min(u * CN_T + tid, nv - 1);
+    x[u] = sv[v];
+    g[u] = gv[v];
+  }
+  float ss[1] = {0.f};
+#pragma unroll
+  for (int u = 0; u < NVC; ++u) {
+    if (u * CN_T + tid >= nv) continue;
+    const T* e = reinterpret_cast<const T*>(&x[u]);
+#pragma unroll
+    for (int q = 0; q < VE; ++q) {
+      const float f = ldv(e, q);
       ss[0] += f * f;
     }
   }
-  block_sum256<1>(ss, red);
+  block_sum<1, CN_T>(ss, red);
   const float rs = rsqrtf(ss[0] / W + a.eps);
-  const u32x4* gv = reinterpret_cast<const u32x4*>(a.gain);
-#pragma unroll 2
-  for (int v = tid; v < nv; v += 256) {
-    const u32x4 x = sv[v], g = gv[v];
-    const T* e = reinterpret_cast<const T*>(&x);
-    const T* ge = reinterpret_cast<const T*>(&g);
+  T* dst = reinterpret_cast<T*>(a.ubar) + (size_t)lr * W;
 #pragma unroll
-    for (int j = 0; j < VE; j += 4)
-      st4_act<T>(dst, (size_t)v * VE + j, a.ubar_plane,
-                 f32x4{ldv(e, j) * rs * ldv(ge, j), ldv(e, j + 1) * rs * ldv(ge, j + 1),
-                       ldv(e, j + 2) * rs * ldv(ge, j + 2), ldv(e, j + 3) * rs * ldv(ge, j + 3)});
+  for (int u = 0; u < NVC; ++u) {
+    const int v = u * CN_T + tid;
+    if (v >= nv) continue;
+    const T* e = reinterpret_cast<const T*>(&x[u]);
+    const T* ge = reinterpret_cast<const T*>(&g[u]);
+#pragma unroll
+    for (int q = 0; q < VE; q += 4)
+      st4_act<T>(dst, (size_t)v * VE + q, a.ubar_plane,
+                 f32x4{ldv(e, q) * rs * ldv(ge, q), ldv(e, q + 1) * rs * ldv(ge, q + 1),
+                       ldv(e, q + 2) * rs * ldv(ge, q + 2), ldv(e, q + 3) * rs * ldv(ge, q + 3)});
+  }
+}
+
+// Block embed + layer 0's attention pre-norm and pre-conv: h = E[x] with x = [anchor, MASK, ...];
+// z = RMSNorm(h) * g; y_t = k_t0 z_t + k_t1 z_{t-1}, k_t = sigmoid(W_c z_t + b_c) (z_{-1} = 0).
+// PP_T threads, 4 elements each; all loads (two embedding rows, gain, conv weights) in one burst.
+template <typename T, int NV>
+__global__ __launch_bounds__(PP_T) void embed_pre_kernel(RowArgs a) {
+  __shared__ float red[(PP_T / 64) * 2];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int b = row / a.K, t = row % a.K;
+  const int d = a.d;
+  int anchor = a.anchor[b];
+  if (anchor < 0 || anchor >= a.vocab) {   // out-of-range token: record and read row 0
+    if (tid == 0 && t == 0) atomicOr(a.dev_err, 8);
+    anchor = 0;
+  }
+  const int id_t = (t == 0) ? anchor : a.mask_id;
+  const int id_p = (t <= 1) ? anchor : a.mask_id;
+  const bool conv = a.use_conv != 0;
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  using W4 = typename Raw4<T>::type;
+  W4 re[2][NV], rg[NV], rw[2][NV];
+  const void* wp = conv ? a.pre_w : a.pre_gain;   // the gain stands in for absent conv weights
+  const int wd = conv ? d : 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int k = (i * PP_T + tid) * 4;
+    const int kc = k < d ? k : 0;
+    re[0][i] = Raw4<T>::load(a.embed, (size_t)id_t * d + kc);
+    re[1][i] = Raw4<T>::load(a.embed, (size_t)id_p * d + kc);
+    rg[i] = Raw4<T>::load(a.pre_gain, kc);
+    rw[0][i] = Raw4<T>::load(wp, kc);
+    rw[1][i] = Raw4<T>::load(wp, wd + kc);
+  }
+  const float pb0 = conv ? ldw<T>(a.pre_b, 0) : 0.f, pb1 = conv ? ldw<T>(a.pre_b, 1) : 0.f;
+  f32x4 e[2][NV], g[NV];
+  float ss[2] = {0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int k = (i * PP_T + tid) * 4;
+    const bool in = k < d;
+    e[0][i] = in ? Raw4<T>::cvt(re[0][i]) : z4;
+    e[1][i] = (in && t > 0) ? Raw4<T>::cvt(re[1][i]) : z4;
+    g[i] = in ? Raw4<T>::cvt(rg[i]) : z4;
+    ss[0] += dot4(e[0][i], e[0][i]);
+    ss[1] += dot4(e[1][i], e[1][i]);
+    if (in) *reinterpret_cast<f32x4*>(a.h_out + (size_t)row * d + k) = e[0][i];
+  }
+  block_sum<2, PP_T>(ss, red);
+  const float r0 = rsqrtf(ss[0] / d + a.eps), r1 = rsqrtf(ss[1] / d + a.eps);
+  float dot[2] = {0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int k = (i * PP_T + tid) * 4;
+    const bool in = k < d;
+    e[0][i] = e[0][i] * r0 * g[i];
+    e[1][i] = e[1][i] * r1 * g[i];
+    if (conv && in) {
+      dot[0] += dot4(Raw4<T>::cvt(rw[0][i]), e[0][i]);
+      dot[1] += dot4(Raw4<T>::cvt(rw[1][i]), e[0][i]);
+    }
+  }
+  float k0 = 1.f, k1 = 0.f;
+  if (conv) {
+    block_sum<2, PP_T>(dot, red);
+    k0 = sigmoidf_(dot[0] + pb0);
+    k1 = sigmoidf_(dot[1] + pb1);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int k = (i * PP_T + tid) * 4;
+    if (k < d) st4_act<T>(a.y, (size_t)row * a.ldy + k, a.y_plane, k0 * e[0][i] + k1 * e[1][i]);
   }
 }
 
@@ -545,7 +633,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
   __shared__ __attribute__((aligned(16))) int si[2][256][TOPK];
   const int orow = blockIdx.x, tid = threadIdx.x;
   const int b = orow / (a.K - 1), t = orow % (a.K - 1) + 1;
-  if (orow == 0 && tid < 4 && a.counters) a.counters[tid] = 0;
+  if (orow == 0 && tid < NCOUNTERS && a.counters) a.counters[tid] = 0;
   const size_t in_row = (size_t)b * a.K + t;
   const float* v = a.vals + in_row * a.ncand;
   const int* id = a.ids ? a.ids + in_row * a.ncand : nullptr;
@@ -628,7 +716,17 @@ hipError_t launch_draft_plan(const PlanArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 hipError_t launch_embed_pre(bool bf, const RowArgs& a, int rows, hipStream_t st) {
-  DFL_T_DISPATCH(bf, embed_pre_kernel, dim3(rows), dim3(256), st, a);
+  if (a.d % 4) return hipErrorInvalidValue;
+  const int v = (a.d + 4 * PP_T - 1) / (4 * PP_T);
+  if (v <= 1) {
+    if (bf) hipLaunchKernelGGL((embed_pre_kernel<bf16, 1>), dim3(rows), dim3(PP_T), 0, st, a);
+    else hipLaunchKernelGGL((embed_pre_kernel<float, 1>), dim3(rows), dim3(PP_T), 0, st, a);
+  } else if (v <= 2) {
+    if (bf) hipLaunchKernelGGL((embed_pre_kernel<bf16, 2>), dim3(rows), dim3(PP_T), 0, st, a);
+    else hipLaunchKernelGGL((embed_pre_kernel<float, 2>), dim3(rows), dim3(PP_T), 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 template <int NV>
@@ -662,8 +760,20 @@ hipError_t launch_inject_plan(const InjectArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(inject_plan_kernel, dim3(1), dim3(256), 0, st, a);
   return hipGetLastError();
 }
+template <int NVC>
+static void launch_cn(bool bf, const InjectArgs& a, int rows, hipStream_t st) {
+  if (bf) hipLaunchKernelGGL((concat_norm_kernel<bf16, NVC>), dim3(rows), dim3(CN_T), 0, st, a);
+  else hipLaunchKernelGGL((concat_norm_kernel<float, NVC>), dim3(rows), dim3(CN_T), 0, st, a);
+}
 hipError_t launch_concat_norm(bool bf, const InjectArgs& a, int rows, hipStream_t st) {
-  DFL_T_DISPATCH(bf, concat_norm_kernel, dim3(rows), dim3(256), st, a);
+  const int nv = a.concat / (bf ? 8 : 4);
+  const int per = (nv + CN_T - 1) / CN_T;
+  if (per <= 1) launch_cn<1>(bf, a, rows, st);
+  else if (per <= 2) launch_cn<2>(bf, a, rows, st);
+  else if (per <= 4) launch_cn<4>(bf, a, rows, st);
+  else if (per <= 8) launch_cn<8>(bf, a, rows, st);
+  else if (per <= 16) launch_cn<16>(bf, a, rows, st);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 hipError_t launch_kv_post(bool bf, const KvPostArgs& a, int rows, int heads, hipStream_t st) {

@@ -133,7 +133,13 @@ typedef struct {
 
 typedef struct dflash_handle dflash_handle;
 
-/* Validates a configuration; DFLASH_OK if the kernels support it. */
+/* Validates a configuration; DFLASH_OK if the kernels support it, else DFLASH_E_UNSUPPORTED or
+ * DFLASH_E_INVALID with the reason in dflash_last_error().  Supported: 1..16 layers; hidden a
+ * multiple of 64 up to 4096; n_heads a multiple of n_kv_heads with (n_heads/n_kv_heads) *
+ * block_size <= 64; block_size 2..32; topk 16; sel_rank a multiple of 8 in [8, 256]; the concat
+ * width n_taps*target_hidden a multiple of 8 (of 64 for bf16) and at most 65536 (bf16) or 32768
+ * (fp32); bf16 drafters need head_dim 128, ffn a multiple of 128 and n_heads*head_dim a multiple
+ * of 64. */
 DFLASH_API dflash_status dflash_config_check(const dflash_config* cfg);
 
 /* Size of the caller-owned KV cache buffer for `max_seqs` sequences (0 on invalid input). */
