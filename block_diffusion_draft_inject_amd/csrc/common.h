@@ -61,6 +61,11 @@ __device__ __forceinline__ float lane_f(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+
 // Wave-wide sum / max, the same value in every lane.  Needs all 64 lanes active.  Within each
 // row of 16 lanes the four symmetric DPP steps leave every lane with the row total (a + b is
 // evaluated as b + a in the partner lane: identical rounding); the four row totals are then

@@ -735,13 +735,15 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
     // nonlinear epilogues, k-splits for PARTIAL
     const int ncols = (mode == GEMM_SWIGLU) ? N / 2 : N;
     const int nfrag = (ncols + 15) / 16;
-    // workgroups loop over fragments: halve the fragment stride while it stays a divisor of
-    // the fragment count and the launch keeps more than 256 workgroups (one per CU is enough
-    // to stream; fewer, longer-lived workgroups load their activation slice fewer times)
+    // workgroups loop over fragments: the fragment stride is the largest divisor of the
+    // fragment count that keeps the launch at most 256 workgroups (one per CU is enough to
+    // stream; every workgroup then has the same number of fragments and loads its activation
+    // slice once)
     auto stride = [&](int splits) {
-      int gx = nfrag;
-      while (gx % 2 == 0 && (gx / 2) * splits >= 128 && gx * splits > 256) gx /= 2;
-      return gx;
+      if (nfrag * splits <= 256) return nfrag;
+      for (int gx = 256 / splits; gx >= 1; --gx)
+        if (nfrag % gx == 0 && gx * splits >= 128) return gx;
+      return max(1, 256 / splits);
     };
     if (mode == GEMM_PARTIAL) {
       pl.slc = 1;

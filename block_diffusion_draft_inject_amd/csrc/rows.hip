@@ -628,6 +628,94 @@ __device__ __forceinline__ int count_better(const float* lv, const int* li, floa
   return n;
 }
 
+// Best (value, id) candidate of the wave under cand_better, the same in every lane (all 64
+// lanes active).  DPP steps inside each row of 16 lanes, then the four row winners are compared
+// through readlane.
+__device__ __forceinline__ void wave_best_dpp(float& v, int& id) {
+  auto step = [&](float ov, int oi) {
+    const bool take = cand_better(ov, oi, v, id);
+    v = take ? ov : v;
+    id = take ? oi : id;
+  };
+  step(dpp_f<0xB1>(v), dpp_i<0xB1>(id));
+  step(dpp_f<0x4E>(v), dpp_i<0x4E>(id));
+  step(dpp_f<0x141>(v), dpp_i<0x141>(id));
+  step(dpp_f<0x140>(v), dpp_i<0x140>(id));
+  float bv = lane_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(id, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) {
+    const float ov = lane_f(v, r);
+    const int oi = __builtin_amdgcn_readlane(id, r);
+    const bool take = cand_better(ov, oi, bv, bi);
+    bv = take ? ov : bv;
+    bi = take ? oi : bi;
+  }
+  v = bv;
+  id = bi;
+}
+
+// List mode with at most 256 lists: thread t holds list t (sorted).  Each wave extracts its
+// own best 16 in 16 rounds of a wave-wide arg-best (the winning lane shifts its list by one),
+// the four wave results go through LDS, and wave 0 extracts the final 16 from those 64.
+__global__ __launch_bounds__(256) void topk_merge_lists_kernel(MergeArgs a) {
+  __shared__ float wv[4][TOPK];
+  __shared__ int wi[4][TOPK];
+  const int orow = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = orow / (a.K - 1), t = orow % (a.K - 1) + 1;
+  if (orow == 0 && tid < NCOUNTERS && a.counters) a.counters[tid] = 0;
+  const size_t in_row = (size_t)b * a.K + t;
+  const int nl = a.ncand / TOPK;
+  float v[TOPK];
+  int id[TOPK];
+  {
+    const int l = min(tid, nl - 1);
+    const f32x4* pv = reinterpret_cast<const f32x4*>(a.vals + in_row * a.ncand + (size_t)l * TOPK);
+    const u32x4* pi = reinterpret_cast<const u32x4*>(a.ids + in_row * a.ncand + (size_t)l * TOPK);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 x = pv[q];
+      const u32x4 y = pi[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[4 * q + j] = tid < nl ? x[j] : NEG_INF;
+        id[4 * q + j] = tid < nl ? (int)y[j] : ID_NONE;
+      }
+    }
+  }
+#pragma unroll 1
+  for (int r = 0; r < TOPK; ++r) {
+    float bv = v[0];
+    int bi = id[0];
+    wave_best_dpp(bv, bi);
+    if (lane == r) { wv[w][r] = bv; wi[w][r] = bi; }
+    if (id[0] == bi && v[0] == bv) {           // the winning lane (ids are distinct)
+#pragma unroll
+      for (int i = 0; i + 1 < TOPK; ++i) { v[i] = v[i + 1]; id[i] = id[i + 1]; }
+      v[TOPK - 1] = NEG_INF;
+      id[TOPK - 1] = ID_NONE;
+    }
+  }
+  __syncthreads();
+  if (w != 0) return;
+  float cv = wv[lane >> 4][lane & 15];
+  int ci = wi[lane >> 4][lane & 15];
+  float ov = NEG_INF;
+  int oi = ID_NONE;
+#pragma unroll 1
+  for (int r = 0; r < TOPK; ++r) {
+    float bv = cv;
+    int bi = ci;
+    wave_best_dpp(bv, bi);
+    if (lane == r) { ov = bv; oi = bi; }
+    if (ci == bi && cv == bv) { cv = NEG_INF; ci = ID_NONE; }
+  }
+  if (lane < TOPK) {
+    a.out_ids[(size_t)orow * TOPK + lane] = oi;
+    a.out_vals[(size_t)orow * TOPK + lane] = ov;
+  }
+}
+
 __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
   __shared__ __attribute__((aligned(16))) float sv[2][256][TOPK];
   __shared__ __attribute__((aligned(16))) int si[2][256][TOPK];
@@ -786,7 +874,8 @@ hipError_t launch_reset(const ResetArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 hipError_t launch_topk_merge(const MergeArgs& a, int out_rows, hipStream_t st) {
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(out_rows), dim3(256), 0, st, a);
+  if (a.ids && a.ncand / TOPK <= 256) hipLaunchKernelGGL(topk_merge_lists_kernel, dim3(out_rows), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(topk_merge_kernel, dim3(out_rows), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
