@@ -476,6 +476,214 @@ __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
+// lm_head + top-16, at most 16 rows, K <= 2048 (K a multiple of 512): independent waves.
+// The workgroup copies the activation rows (hi and lo planes) into LDS once; then every wave
+// streams whole 16-column fragments (wave w of the grid takes fragments w, w + waves, ...) over
+// all of K in batches of 4 chunks of 64, three batches in rotation, the prefetch running on
+// into the next fragment.  No workgroup barrier in the main loop: a wave waits only for its own
+// loads.  (Handing fragments out through one device-wide counter was far slower: the ~13k
+// increments of one address serialise.)  Each wave keeps, per row, 4 lane lists of the
+// running top-16 (one per column quarter); at the end a row's 32 lists are merged by one
+// half-wave into one partial list per (row, workgroup).
+// ---------------------------------------------------------------------------------------
+constexpr int LW_W = 8;             // waves per workgroup
+constexpr int LW_KMAX = 2048;
+constexpr int LW_LD = LW_KMAX + 8;  // LDS row stride (bf16): rows fall in distinct bank groups
+
+constexpr size_t LW_SMEM = (size_t)2 * 16 * LW_LD * 2 + (size_t)LW_W * 16 * 17 * 4;   // 137 KiB
+
+struct LwBatch {
+  u32x4 b[4][2];                    // 4 chunks x (k halves 0..31 / 32..63 of the chunk)
+};
+
+__device__ __forceinline__ void lw_load(LwBatch& x, const bf16* row, int k0, int kg) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const bf16* q = row + k0 + c * 64 + kg * 8;
+    x.b[c][0] = *reinterpret_cast<const u32x4*>(q);
+    x.b[c][1] = *reinterpret_cast<const u32x4*>(q + 32);
+  }
+}
+
+// hi and lo activation planes accumulate separately: two independent MFMA chains
+__device__ __forceinline__ void lw_mma(const LwBatch& x, const bf16 (*sa)[16][LW_LD], int k0, int li, int kg,
+                                       f32x4& acc_h, f32x4& acc_l) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + c * 64 + h * 32 + kg * 8;
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sa[0][li][k]);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&sa[1][li][k]);
+      acc_h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(x.b[c][h]), acc_h, 0, 0, 0);
+      acc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, as_bf16x8(x.b[c][h]), acc_l, 0, 0, 0);
+    }
+}
+
+// LOGITS: the full logits are written too (a global store in the fragment loop; kept out of
+// the instantiation without them, where it would make the compiler's load waits coarser)
+template <bool LOGITS>
+__global__ __launch_bounds__(LW_W * 64) void lmhead_topk_wave(GemmParams p) {
+  __shared__ __align__(16) unsigned char lw_smem[LW_SMEM];
+  bf16 (*sa)[16][LW_LD] = reinterpret_cast<bf16 (*)[16][LW_LD]>(lw_smem);                 // [plane][row][k]
+  float (*fb)[16][17] = reinterpret_cast<float (*)[16][17]>(lw_smem + 2 * 16 * LW_LD * 2);   // [wave][row][col]
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, kg = lane >> 4;
+  const int Mv = rows_valid(p);
+  const int K = p.K;
+  if (Mv <= 0) return;   // uniform
+  // activation rows -> LDS (rows >= Mv zero), 16-byte pieces, all loads issued in one burst at
+  // always-valid addresses and masked afterwards
+  // thread t copies the 16-byte piece t % 256 of plane-rows t / 256, t / 256 + 2, ... (32 plane-rows)
+  {
+    static_assert(LW_KMAX / 8 == 256 && LW_W * 64 == 512, "piece mapping assumes 256 pieces a row, 512 threads");
+    const int v = tid & 255, q0 = tid >> 8;
+    const bool vok = v < K / 8;
+    const int vc = min(v, K / 8 - 1);
+    u32x4 x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = q0 + 2 * i, pl = q >> 4, r = q & 15;
+      x[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(p.A) + (pl ? p.a_plane : 0) +
+                                             (size_t)min(r, Mv - 1) * p.lda + vc * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = q0 + 2 * i, pl = q >> 4, r = q & 15;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      if (vok) *reinterpret_cast<u32x4*>(&sa[pl][r][v * 8]) = r < Mv ? x[i] : z;
+    }
+  }
+  __syncthreads();
+  const int nfrag = (p.N + 15) / 16;
+  const int ncb = K / 256;                        // batches of 4 chunks per fragment (even)
+  const int TW = gridDim.x * LW_W;
+  const int my_row = lane >> 2, my_sub = lane & 3;   // epilogue: lane handles row my_row, cols 4 sub..+3
+  const bool row_live = my_row < Mv && (my_row % p.block) != 0;
+  Top16 top;
+  top.init();
+  auto rowp = [&](int frag) {
+    const int n = min(min(frag, nfrag - 1) * 16 + li, p.N - 1);
+    return reinterpret_cast<const bf16*>(p.seg[0]) + (size_t)n * p.ldb;
+  };
+  // epilogue of one fragment: the wave's 16 x 16 tile through its own LDS slot; lane (row,
+  // quarter) scans 4 columns into its list
+  auto epilogue = [&](int f, const f32x4& acc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      fb[wave][kg * 4 + j][li] = acc[j];
+      if (LOGITS && kg * 4 + j < Mv) store_logit(p, kg * 4 + j, f * 16 + li, acc[j]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (row_live) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int col = f * 16 + my_sub * 4 + c;
+        if (col < p.N) top.push(fb[wave][my_row][my_sub * 4 + c], col);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // this wave's batches, fragment by fragment; the load cursor runs two batches ahead of the
+  // compute cursor, over fragment boundaries (loads past the end read clamped, valid rows)
+  const int f0 = blockIdx.x * LW_W + wave;
+  // rounded up to whole rotations: a padded batch belongs to a fragment this wave never
+  // finishes (or to one past the end, whose columns the epilogue skips), so it changes nothing
+  const int T = ((f0 < nfrag ? (nfrag - 1 - f0) / TW + 1 : 0) * ncb + 2) / 3 * 3;
+  int lf = f0, lcb = 0;
+  auto issue = [&](LwBatch& b) {
+    lw_load(b, rowp(lf), lcb * 256, kg);
+    if (++lcb == ncb) { lcb = 0; lf += TW; }
+  };
+  int cf = f0, ccb = 0;
+  f32x4 acc_h = {0.f, 0.f, 0.f, 0.f}, acc_l = {0.f, 0.f, 0.f, 0.f};
+  auto step = [&](const LwBatch& b) {
+    lw_mma(b, sa, ccb * 256, li, kg, acc_h, acc_l);
+    if (++ccb == ncb) {
+      epilogue(cf, acc_h + acc_l);
+      acc_h = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc_l = f32x4{0.f, 0.f, 0.f, 0.f};
+      ccb = 0;
+      cf += TW;
+    }
+  };
+  LwBatch b0, b1, b2;
+  issue(b0);
+  __builtin_amdgcn_sched_barrier(0);   // b0's loads strictly before b1's: the in-order wait counts rely on it
+  issue(b1);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int t = 0; t < T; t += 3) {
+    issue(b2);
+    __builtin_amdgcn_sched_barrier(0);
+    step(b0);
+    issue(b0);
+    __builtin_amdgcn_sched_barrier(0);
+    step(b1);
+    issue(b1);
+    __builtin_amdgcn_sched_barrier(0);
+    step(b2);
+  }
+  // merge: a row's 32 lane lists (4 lanes x 8 waves) go through LDS to one half-wave (wave w
+  // takes rows 2w and 2w + 1), which extracts the row's best 16 in 16 rounds of a 32-lane
+  // arg-best; the winning lane shifts its sorted list by one.
+  float (*lv)[32][TOPK + 1] = reinterpret_cast<float (*)[32][TOPK + 1]>(lw_smem);
+  int (*lid)[32][TOPK + 1] = reinterpret_cast<int (*)[32][TOPK + 1]>(lw_smem + 16 * 32 * (TOPK + 1) * 4);
+  __syncthreads();   // every wave is done with the activation rows (the lists overlay them)
+  {
+    const int src = wave * 4 + my_sub;
+#pragma unroll
+    for (int i = 0; i < TOPK; ++i) { lv[my_row][src][i] = top.v[i]; lid[my_row][src][i] = top.id[i]; }
+  }
+  __syncthreads();
+  const int hr = lane >> 5, s = lane & 31, row = wave * 2 + hr;
+  float v[TOPK];
+  int id[TOPK];
+#pragma unroll
+  for (int i = 0; i < TOPK; ++i) { v[i] = lv[row][s][i]; id[i] = lid[row][s][i]; }
+  float ov = NEG_INF;
+  int oi = ID_NONE;
+#pragma unroll 1
+  for (int r = 0; r < TOPK; ++r) {
+    float bv = v[0];
+    int bi = id[0];
+    auto step = [&](float cv, int ci) {
+      const bool take = cand_better(cv, ci, bv, bi);
+      bv = take ? cv : bv;
+      bi = take ? ci : bi;
+    };
+    // every lane ends with the best of its 16-lane row, then the two rows of each half combine
+    step(dpp_f<0xB1>(bv), dpp_i<0xB1>(bi));
+    step(dpp_f<0x4E>(bv), dpp_i<0x4E>(bi));
+    step(dpp_f<0x141>(bv), dpp_i<0x141>(bi));
+    step(dpp_f<0x140>(bv), dpp_i<0x140>(bi));
+    const float u0 = lane_f(bv, 0), u1 = lane_f(bv, 16), u2 = lane_f(bv, 32), u3 = lane_f(bv, 48);
+    const int j0 = __builtin_amdgcn_readlane(bi, 0), j1 = __builtin_amdgcn_readlane(bi, 16);
+    const int j2 = __builtin_amdgcn_readlane(bi, 32), j3 = __builtin_amdgcn_readlane(bi, 48);
+    const float x0 = hr ? u2 : u0, x1 = hr ? u3 : u1;   // (readlane takes a uniform lane index)
+    const int y0 = hr ? j2 : j0, y1 = hr ? j3 : j1;
+    const bool second = cand_better(x1, y1, x0, y0);
+    bv = second ? x1 : x0;
+    bi = second ? y1 : y0;
+    if (s == r) { ov = bv; oi = bi; }
+    if (id[0] == bi && v[0] == bv) {   // the winning lane (ids are distinct, unless all are empty)
+#pragma unroll
+      for (int i = 0; i + 1 < TOPK; ++i) { v[i] = v[i + 1]; id[i] = id[i + 1]; }
+      v[TOPK - 1] = NEG_INF;
+      id[TOPK - 1] = ID_NONE;
+    }
+  }
+  if (s < TOPK && row < Mv) {
+    const size_t base = ((size_t)row * p.groups + blockIdx.x) * TOPK;
+    p.tk_val[base + s] = ov;
+    p.tk_id[base + s] = oi;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // tiled (more than 16 rows): 128 x 128 output tiles, 64-wide k-steps, one workgroup of 4 waves
 // per CU (2 x 2 waves of 64 x 64).  Per k-step a wave multiplies its 4 x 4 MFMA tiles twice
 // (k halves) for each activation plane: 64 MFMAs per step.  Operands go global -> registers
@@ -754,6 +962,12 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
     } else {
       pl.slc = 1;
       while (pl.slc < 4 && SW * 64 * pl.slc < K) pl.slc *= 2;
+      if (mode == GEMM_TOPK && K >= 512 && K % 512 == 0 && K <= LW_KMAX) {
+        pl.kind = 4;
+        pl.groups = 256;
+        pl.grid = dim3(pl.groups, 1, 1);
+        return pl;
+      }
       if (SW * 64 * pl.slc >= K) {
         pl.kind = 3;
         if (mode == GEMM_TOPK) {
@@ -812,6 +1026,12 @@ hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hi
   const dim3 blk(256);
   if (pl.kind == 2) {
     hipLaunchKernelGGL(gemm_f32_kernel, pl.grid, blk, 0, st, p);
+    return hipGetLastError();
+  }
+  if (pl.kind == 4) {
+    if (p.seg_rows < p.N) return hipErrorInvalidValue;   // one weight segment
+    if (p.logits) hipLaunchKernelGGL(lmhead_topk_wave<true>, pl.grid, dim3(LW_W * 64), 0, st, p);
+    else hipLaunchKernelGGL(lmhead_topk_wave<false>, pl.grid, dim3(LW_W * 64), 0, st, p);
     return hipGetLastError();
   }
   if (pl.kind == 3) {

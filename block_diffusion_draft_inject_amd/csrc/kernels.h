@@ -41,7 +41,7 @@ struct GemmParams {
 };
 
 struct GemmPlan {
-  int kind;      // 0 = skinny, 1 = tiled, 2 = f32 simple, 3 = stream (<= 16 rows)
+  int kind;      // 0 = skinny, 1 = tiled, 2 = f32 simple, 3 = stream (<= 16 rows), 4 = lm_head waves
   int slc;       // stream: 64-wide chunks per wave
   int mt;        // skinny row fragments (1,2,4)
   int splits;
