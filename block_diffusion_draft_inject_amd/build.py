@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdflash.so")
-SOURCES = ["dflash.hip", "gemm.hip", "rows.hip", "attention.hip", "select.hip"]
+SOURCES = ["dflash.hip", "gemm.hip", "gemm_tile.hip", "rows.hip", "attention.hip", "select.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMPILE_FLAGS = [

@@ -21,14 +21,7 @@
 
 namespace dfl {
 
-__device__ __forceinline__ const bf16* brow_ptr(const GemmParams& p, int n) {
-  const int s = n / p.seg_rows;
-  return reinterpret_cast<const bf16*>(p.seg[s]) + (size_t)(n - s * p.seg_rows) * p.ldb;
-}
 
-__device__ __forceinline__ int rows_valid(const GemmParams& p) {
-  return p.m_dev ? max(0, min(p.M, *p.m_dev - p.m_off)) : p.M;
-}
 
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
@@ -179,25 +172,6 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
         }
       }
     }
-}
-
-// Writes one wave-tile of logits (rows of slot >= 1 only) when full logits are requested.
-__device__ __forceinline__ void store_logit(const GemmParams& p, int row, int col, float v) {
-  const int slot = row % p.block;
-  if (slot == 0 || col >= p.N) return;
-  const size_t orow = (size_t)(row / p.block) * (p.block - 1) + (slot - 1);
-  p.logits[orow * p.N + col] = v;
-}
-
-// Thread-pair or thread-group merge of Top16 lists through LDS, then store a partial.
-// `lists` holds nthr_per_row lists per row; the first thread of each row merges.
-__device__ __forceinline__ void store_partial(const GemmParams& p, int row, int group, const Top16& t) {
-  const size_t base = ((size_t)row * p.groups + group) * TOPK;
-#pragma unroll
-  for (int i = 0; i < TOPK; ++i) {
-    p.tk_val[base + i] = t.v[i];
-    p.tk_id[base + i] = t.id[i];
-  }
 }
 
 // TOPK (lm_head) skinny, persistent with work stealing: each wave repeatedly takes the next
@@ -684,230 +658,6 @@ __global__ __launch_bounds__(LW_W * 64) void lmhead_topk_wave(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// tiled (more than 16 rows): 128 x 128 output tiles, 64-wide k-steps, one workgroup of 4 waves
-// per CU (2 x 2 waves of 64 x 64).  Per k-step a wave multiplies its 4 x 4 MFMA tiles twice
-// (k halves) for each activation plane: 64 MFMAs per step.  Operands go global -> registers
-// -> LDS; three register sets rotate so the loads of step c+2 are issued before step c is
-// multiplied.  Barriers are LDS-only.
-// LDS rows are padded to 72 elements so the 16 rows read by one ds_read_b128 pass fall in
-// distinct banks.
-// ---------------------------------------------------------------------------------------
-constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = TBK + 8, TNR = 3;
-
-struct TiledSmem {
-  bf16 ab[2][3][TBM][TLD];   // [stage][A hi, A lo, B][row][k]: 110,592 bytes
-};
-
-struct TiledRegs {
-  u32x4 ah[4], al[4], b[4];  // thread t: rows (t >> 3) + 32 i, k = 8 (t & 7) .. +7
-};
-
-// Operands are read with raw buffer loads: one resource per operand (A hi plane, A lo plane,
-// the tile's weight segment), a fixed per-lane byte offset for each of the thread's rows, and
-// the k-step as a uniform scalar offset, so a step needs no address arithmetic.  A load beyond
-// a resource's extent returns zero instead of faulting.
-struct TiledCtx {
-  __amdgpu_buffer_rsrc_t rah, ral, rb;
-  int oa[4], ob[4];          // per-lane byte offsets of the thread's 4 A rows and 4 B rows
-};
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tiled_rsrc(const void* base, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           (int)(bytes < 0x7fffffffu ? bytes : 0x7fffffffu), 0x00020000);
-}
-
-__device__ __forceinline__ void tiled_load(const TiledCtx& x, int c, TiledRegs& r) {
-  const int so = c * TBK * 2;   // byte offset of the k-step
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r.ah[i] = __builtin_amdgcn_raw_buffer_load_b128(x.rah, x.oa[i], so, 0);
-    r.al[i] = __builtin_amdgcn_raw_buffer_load_b128(x.ral, x.oa[i], so, 0);
-    r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(x.rb, x.ob[i], so, 0);
-  }
-}
-
-__device__ __forceinline__ void tiled_store(TiledSmem& sm, int buf, const TiledRegs& r) {
-  const int r0 = threadIdx.x >> 3, kq = (threadIdx.x & 7) * 8;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<u32x4*>(&sm.ab[buf][0][r0 + 32 * i][kq]) = r.ah[i];
-    *reinterpret_cast<u32x4*>(&sm.ab[buf][1][r0 + 32 * i][kq]) = r.al[i];
-    *reinterpret_cast<u32x4*>(&sm.ab[buf][2][r0 + 32 * i][kq]) = r.b[i];
-  }
-}
-
-__device__ __forceinline__ void tiled_compute(const TiledSmem& sm, int buf, int wm, int wn, int li, int kg,
-                                              f32x4 (&acc)[4][4]) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int k = h * 32 + kg * 8;
-    bf16x8 ah[4], al[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ah[i] = *reinterpret_cast<const bf16x8*>(&sm.ab[buf][0][wm * 64 + i * 16 + li][k]);
-      al[i] = *reinterpret_cast<const bf16x8*>(&sm.ab[buf][1][wm * 64 + i * 16 + li][k]);
-      b[i] = *reinterpret_cast<const bf16x8*>(&sm.ab[buf][2][wn * 64 + i * 16 + li][k]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], b[j], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], b[j], acc[i][j], 0, 0, 0);
-      }
-  }
-}
-
-// One 128x128 output tile over k-steps [c0, c1) of TBK.
-__device__ __forceinline__ void tiled_tile(const GemmParams& p, TiledSmem& sm, int m0, int n0, int Mv, int c0, int c1,
-                                           f32x4 (&acc)[4][4]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, li = lane & 15, kg = lane >> 4;
-  TiledCtx x;
-  {
-    // the 128 weight rows of the tile lie in one segment (segment sizes are multiples of 128
-    // or the matrix has one segment), so the segment index is workgroup-uniform
-    const int seg = __builtin_amdgcn_readfirstlane(n0 / p.seg_rows);
-    const int nbase = seg * p.seg_rows;
-    const int nseg = min(p.seg_rows, p.N - nbase);
-    const size_t abytes = ((size_t)(Mv - 1) * p.lda + p.K) * 2;
-    x.rah = tiled_rsrc(p.A, abytes);
-    x.ral = tiled_rsrc(reinterpret_cast<const bf16*>(p.A) + p.a_plane, abytes);
-    x.rb = tiled_rsrc(p.seg[seg], ((size_t)(nseg - 1) * p.ldb + p.K) * 2);
-    const int kq = (tid & 7) * 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = (tid >> 3) + 32 * i;
-      x.oa[i] = (min(m0 + rr, Mv - 1) * p.lda + kq) * 2;
-      x.ob[i] = ((min(n0 + rr, p.N - 1) - nbase) * p.ldb + kq) * 2;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (c0 >= c1) return;
-  const int cl = c1 - 1;
-  TiledRegs r[TNR];
-#pragma unroll
-  for (int q = 0; q < TNR - 1; ++q) tiled_load(x, min(c0 + q, cl), r[q]);
-  lds_barrier();   // LDS free (previous tile / epilogue done)
-  tiled_store(sm, 0, r[0]);
-  lds_barrier();
-  int buf = 0;
-  // step c: load step c+2 into the register set whose data went to LDS one step ago, multiply
-  // `buf` (step c), store step c+1 (loaded one step ago) into the other buffer
-  for (int c = c0; c < c1; c += TNR) {
-#pragma unroll
-    for (int q = 0; q < TNR; ++q) {
-      if (c + q >= c1) break;
-      tiled_load(x, min(c + q + TNR - 1, cl), r[(q + TNR - 1) % TNR]);
-      __builtin_amdgcn_sched_barrier(0);
-      tiled_compute(sm, buf, wm, wn, li, kg, acc);
-      tiled_store(sm, buf ^ 1, r[(q + 1) % TNR]);
-      lds_barrier();
-      buf ^= 1;
-    }
-  }
-}
-
-// PARTIAL: grid x = column tile, y = row tile, z = k-split.
-__global__ __launch_bounds__(256, 1) void gemm_tiled_partial(GemmParams p) {
-  __shared__ TiledSmem sm;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, li = lane & 15, kg = lane >> 4;
-  const int Mv = rows_valid(p);
-  const int m0 = blockIdx.y * TBM, n0 = blockIdx.x * TBN;
-  if (m0 >= Mv) return;
-  const int nsteps = p.K / TBK, s = blockIdx.z;
-  const int c0 = (int)((long)nsteps * s / p.splits), c1 = (int)((long)nsteps * (s + 1) / p.splits);
-  f32x4 acc[4][4];
-  tiled_tile(p, sm, m0, n0, Mv, c0, c1, acc);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * 64 + i * 16 + kg * 4 + r;
-        const int col = n0 + wn * 64 + j * 16 + li;
-        if (row < Mv && col < p.N) p.part[((size_t)s * p.M + row) * p.N + col] = acc[i][j][r];
-      }
-}
-
-// TOPK (lm_head with more than 16 rows): grid x = workgroups per row tile, y = row tile.  Each
-// workgroup takes column tiles from the row tile's work counter (zeroed by the draft plan);
-// after a tile, its logits go through LDS and every row is scanned by two threads (64
-// columns each) into private running top-16 lists, merged at the end into one partial list
-// per (row, workgroup).
-__global__ __launch_bounds__(256, 1) void lmhead_topk_tiled(GemmParams p) {
-  __shared__ TiledSmem sm;
-  __shared__ int s_tile;
-  float (*ep)[TBN + 4] = reinterpret_cast<float (*)[TBN + 4]>(&sm.ab[0][0][0][0]);   // 128 x 132 floats
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, li = lane & 15, kg = lane >> 4;
-  const int Mv = rows_valid(p);
-  const int m0 = blockIdx.y * TBM;
-  if (m0 >= Mv) return;
-  const int ntiles = (p.N + TBN - 1) / TBN;
-  const int my_row = tid >> 1, my_half = tid & 1;
-  const bool row_live = (m0 + my_row < Mv) && ((m0 + my_row) % p.block != 0);
-  int* ctr = p.counter + blockIdx.y;
-  Top16 top;
-  top.init();
-  while (true) {
-    if (tid == 0) s_tile = atomicAdd(ctr, 1);
-    lds_barrier();
-    const int t = s_tile;
-    if (t >= ntiles) break;
-    const int n0 = t * TBN;
-    f32x4 acc[4][4];
-    tiled_tile(p, sm, m0, n0, Mv, 0, p.K / TBK, acc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rl = wm * 64 + i * 16 + kg * 4 + r;
-          const int cl = wn * 64 + j * 16 + li;
-          ep[rl][cl] = acc[i][j][r];
-          if (p.logits && m0 + rl < Mv) store_logit(p, m0 + rl, n0 + cl, acc[i][j][r]);
-        }
-    lds_barrier();
-    if (row_live) {
-      // compact scan (one insertion site, so the code stays small): a vector of four is
-      // skipped when none of it beats the current 16th entry
-#pragma unroll 1
-      for (int c4 = 0; c4 < 16; ++c4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&ep[my_row][my_half * 64 + c4 * 4]);
-        const float thr = top.v[TOPK - 1];
-        if (fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])) < thr) continue;
-#pragma unroll 1
-        for (int q = 0; q < 4; ++q) {
-          const int gcol = n0 + my_half * 64 + c4 * 4 + q;
-          if (gcol < p.N) top.push(v[q], gcol);
-        }
-      }
-    }
-    lds_barrier();   // ep (stage 0) is reused by the next tile's loads
-  }
-  // merge the two lists of each row
-  float (*mv)[TOPK] = reinterpret_cast<float (*)[TOPK]>(&sm.ab[0][0][0][0]);
-  int (*mi)[TOPK] = reinterpret_cast<int (*)[TOPK]>(&sm.ab[1][0][0][0]);
-  if (my_half == 1) {
-#pragma unroll
-    for (int i = 0; i < TOPK; ++i) { mv[my_row][i] = top.v[i]; mi[my_row][i] = top.id[i]; }
-  }
-  lds_barrier();
-  if (my_half == 0) {
-#pragma unroll
-    for (int i = 0; i < TOPK; ++i) top.push(mv[my_row][i], mi[my_row][i]);
-    if (m0 + my_row < Mv) store_partial(p, m0 + my_row, blockIdx.x, top);
-  }
-}
-
-// ---------------------------------------------------------------------------------------
 // fp32: plain dot products.  grid x = 64-column block, y = 4-row block.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
@@ -998,16 +748,25 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
       pl.grid = dim3(ct, rt, pl.splits);
     }
   } else {
-    // one workgroup per CU: k-splits bring a PARTIAL launch to about 256 workgroups
-    pl.kind = 1;
-    const int rt = (M + TBM - 1) / TBM;
-    const int ntiles = (N + TBN - 1) / TBN;
-    const int nsteps = K / TBK;
+    // MFMA tiles with LDS-DMA operands (K is a multiple of 32 for every bf16 drafter).  TOPK:
+    // 256 x 256 tiles (one workgroup per CU) once there are more than 128 rows, else 128 x 128
+    // (two per CU); the workgroups resident at once split the column tiles statically.
+    // PARTIAL: 128 x 128 tiles, k-splits bring the launch to about two workgroups per CU, each
+    // split at least 8 k-steps of 32.
+    pl.kind = 5;
     if (mode == GEMM_TOPK) {
-      pl.groups = clampi(256 / rt, 1, ntiles);
+      pl.mt = M > 128 ? 1 : 0;
+      const int bt = pl.mt ? 256 : 128;
+      const int rt = (M + bt - 1) / bt;
+      const int ntiles = (N + bt - 1) / bt;
+      pl.groups = clampi((pl.mt ? 256 : 512) / rt, 1, ntiles);
       pl.grid = dim3(pl.groups, rt, 1);
     } else {
-      pl.splits = clampi(256 / (ntiles * rt), 1, clampi(nsteps / 2, 1, 8));
+      pl.mt = 0;
+      const int rt = (M + 127) / 128;
+      const int ntiles = (N + 127) / 128;
+      const int nk = K / 32;
+      pl.splits = clampi(512 / (ntiles * rt), 1, clampi(nk / 8, 1, 8));
       pl.grid = dim3(ntiles, rt, pl.splits);
     }
   }
@@ -1071,11 +830,8 @@ hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hi
     }
     return hipGetLastError();
   }
-  if (p.seg_rows % TBN && p.seg_rows < p.N) return hipErrorInvalidValue;   // a tile spans one segment
-  if (mode == GEMM_TOPK && pl.grid.y > (unsigned)NCOUNTERS) return hipErrorInvalidValue;
-  if (mode == GEMM_TOPK) hipLaunchKernelGGL(lmhead_topk_tiled, pl.grid, blk, 0, st, p);
-  else hipLaunchKernelGGL(gemm_tiled_partial, pl.grid, blk, 0, st, p);
-  return hipGetLastError();
+  if (pl.kind == 5) return tile_launch(pl, mode, p, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dfl

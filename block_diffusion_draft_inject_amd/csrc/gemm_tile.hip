@@ -1,0 +1,314 @@
+// Tiled MFMA GEMM for many rows (more than 64): C = A_hi W^T + A_lo W^T over bf16 operands.
+//
+// A workgroup of WGM x WGN waves computes a BM x BN output tile (each wave BM/WGM x BN/WGN)
+// over k-steps of 32.  Operands travel global -> LDS by the LDS-DMA form of the global load
+// (16 bytes per lane, one 1 KiB block of 16 rows x 32 k per wave instruction), with no VGPR
+// staging; S stages rotate, so the loads of step c + S - 1 are in flight while step c is
+// multiplied.  Inside a 1 KiB block the four 16-byte k-chunks of a row are stored in a
+// row-dependent XOR order, so that the 16 lanes that read one chunk column of 16 rows for an
+// MFMA operand fall in distinct LDS banks (for both 8- and 16-lane bank groups).
+//
+// Synchronisation per k-step: each wave waits for its own loads of the step (vmcnt) and
+// for its LDS reads of the previous step (lgkmcnt), then all waves meet at s_barrier; after
+// it the stage read one step earlier is free and is refilled.  The LDS-DMA loads are issued
+// from inline assembly (the compiler does not know they write LDS; the explicit waits above
+// replace its own), so the k-loop contains no other global memory access.
+#include "kernels.h"
+
+namespace dfl {
+namespace {
+
+constexpr int MK = 32;   // k per step
+
+// chunk order inside a row of a 16-row block: logical chunk c of row r sits in slot c ^ swz(r)
+__device__ __forceinline__ int tile_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+template <int BM, int BN, int WGM, int WGN, int S>
+struct TileCfg {
+  static constexpr int NW = WGM * WGN, NT = NW * 64; // waves, threads
+  static constexpr int WM = BM / WGM, WN = BN / WGN; // wave tile
+  static constexpr int FM = WM / 16, FN = WN / 16;   // MFMA fragments per wave
+  static constexpr int BA = BM / 16, BB = BN / 16;   // 1 KiB blocks per stage: A hi, A lo (BA each), B (BB)
+  static constexpr int NBLK = 2 * BA + BB;
+  static constexpr int STAGE = NBLK * 1024;
+  static constexpr int D = NBLK / NW;                // LDS-DMA instructions per wave per stage
+  static constexpr int LDS = S * STAGE;
+  static constexpr int BMc = BM, BNc = BN, Sc = S, WGNc = WGN;
+  static_assert(BA % NW == 0 && BB % NW == 0, "blocks per operand must split evenly over the waves");
+};
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// one LDS-DMA load: 64 lanes x 16 bytes from base + voff[lane] to LDS [lds, lds + 1024)
+__device__ __forceinline__ void dma16(unsigned lds, unsigned voff, const void* base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+// the same from a per-lane 64-bit address
+__device__ __forceinline__ void dma16v(unsigned lds, const void* addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(addr) : "memory", "m0");
+}
+
+// wait until at most N of this wave's loads are outstanding and its LDS reads are done, then
+// meet the other waves
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// The per-workgroup operand streams of one tile: for DMA slot q (block NW q + wave of a stage)
+// the lane's source at k-step 0 -- activation slots as a uniform base and a per-lane offset,
+// weight slots as a per-lane address (a tile's weight rows may lie in different segments).
+template <class T>
+struct TileSrc {
+  const char* base[T::D];
+  unsigned voff[T::D];
+  const char* addr[T::D];
+};
+
+template <class T>
+__device__ __forceinline__ void tile_src(const GemmParams& p, int m0, int n0, int Mv, int wave, int lane,
+                                         TileSrc<T>& s) {
+  const int r16 = lane >> 2;
+  const int kc = (lane & 3) ^ tile_swz(r16);
+  const char* ahi = reinterpret_cast<const char*>(p.A);
+  const char* alo = reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.A) + p.a_plane);
+#pragma unroll
+  for (int q = 0; q < T::D; ++q) {
+    const int b = T::NW * q + wave;                // block of the stage
+    if (T::NW * q < T::BA) {                       // A hi (compile-time per q: NW q < BA <=> b < BA)
+      const int r = min(m0 + b * 16 + r16, Mv - 1);
+      s.base[q] = ahi;
+      s.voff[q] = (unsigned)(((size_t)r * p.lda + kc * 8) * 2);
+    } else if (T::NW * q < 2 * T::BA) {            // A lo
+      const int r = min(m0 + (b - T::BA) * 16 + r16, Mv - 1);
+      s.base[q] = alo;
+      s.voff[q] = (unsigned)(((size_t)r * p.lda + kc * 8) * 2);
+    } else {                                       // weight rows
+      const int n = min(n0 + (b - 2 * T::BA) * 16 + r16, p.N - 1);
+      s.addr[q] = reinterpret_cast<const char*>(brow_ptr(p, n) + kc * 8);
+    }
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void tile_issue(const TileSrc<T>& s, unsigned lds_stage, int wave, int c) {
+#pragma unroll
+  for (int q = 0; q < T::D; ++q) {
+    const unsigned lds = lds_stage + (T::NW * q + wave) * 1024;
+    if (T::NW * q < 2 * T::BA) dma16(lds, s.voff[q], s.base[q] + (size_t)c * MK * 2);
+    else dma16v(lds, s.addr[q] + (size_t)c * MK * 2);
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void tile_mma(const unsigned char* stage, int wm, int wn, unsigned lo,
+                                         f32x4 (&acc)[T::FM][T::FN]) {
+  bf16x8 b[T::FN];
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j)
+    b[j] = *reinterpret_cast<const bf16x8*>(stage + (2 * T::BA + wn * T::FN + j) * 1024 + lo);
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(stage + (wm * T::FM + i) * 1024 + lo);
+    const bf16x8 al = *reinterpret_cast<const bf16x8*>(stage + (T::BA + wm * T::FM + i) * 1024 + lo);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// wait for stage `it` with `pend` later stages allowed to stay in flight (0 <= pend <= S - 2)
+template <class T, int S>
+__device__ __forceinline__ void tile_wait(int pend) {
+  static_assert(S >= 2 && S <= 6, "stage count");
+  if (S >= 6 && pend >= 4) wait_barrier<4 * T::D>();
+  else if (S >= 5 && pend >= 3) wait_barrier<3 * T::D>();
+  else if (S >= 4 && pend >= 2) wait_barrier<2 * T::D>();
+  else if (S >= 3 && pend >= 1) wait_barrier<T::D>();
+  else wait_barrier<0>();
+}
+
+// One output tile over k-steps [c0, c1): acc = the tile's partial products.
+template <class T>
+__device__ __forceinline__ void tile_run(const GemmParams& p, unsigned char* smem, int m0, int n0, int Mv, int c0,
+                                         int c1, f32x4 (&acc)[T::FM][T::FN]) {
+  constexpr int S = T::Sc;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / T::WGNc, wn = wave % T::WGNc, li = lane & 15, kg = lane >> 4;
+  TileSrc<T> src;
+  tile_src<T>(p, m0, n0, Mv, wave, lane, src);
+  const unsigned lo = li * 64 + ((kg ^ tile_swz(li)) << 4);
+  const unsigned sbase = lds_addr(smem);
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int n = c1 - c0;
+#pragma unroll
+  for (int q = 0; q + 1 < S; ++q)
+    if (q < n) tile_issue<T>(src, sbase + q * T::STAGE, wave, c0 + q);
+  int st = 0;            // stage of step it
+  int sl = S - 1;        // stage that step it + S - 1 goes to
+  for (int it = 0; it < n; ++it) {
+    tile_wait<T, S>(min(S - 2, n - 1 - it));
+    if (it + S - 1 < n) tile_issue<T>(src, sbase + sl * T::STAGE, wave, c0 + it + S - 1);
+    tile_mma<T>(smem + st * T::STAGE, wm, wn, lo, acc);
+    st = (st + 1 == S) ? 0 : st + 1;
+    sl = (sl + 1 == S) ? 0 : sl + 1;
+  }
+}
+
+// PARTIAL: grid x = column tile, y = row tile, z = k-split; part[z][row][col].
+template <class T, int OCC>
+__global__ __launch_bounds__(T::NT, OCC) void gemm_tile_partial(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / T::WGNc, wn = wave % T::WGNc, li = lane & 15, kg = lane >> 4;
+  const int Mv = rows_valid(p);
+  const int m0 = blockIdx.y * T::BMc, n0 = blockIdx.x * T::BNc;
+  if (m0 >= Mv) return;
+  const int nk = p.K / MK, s = blockIdx.z;
+  const int c0 = (int)((long)nk * s / p.splits), c1 = (int)((long)nk * (s + 1) / p.splits);
+  f32x4 acc[T::FM][T::FN];
+  tile_run<T>(p, smem, m0, n0, Mv, c0, c1, acc);
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * T::WM + i * 16 + kg * 4 + r;
+        const int col = n0 + wn * T::WN + j * 16 + li;
+        if (row < Mv && col < p.N) p.part[((size_t)s * p.M + row) * p.N + col] = acc[i][j][r];
+      }
+}
+
+// TOPK (lm_head): grid x = workgroups per row tile (static tile split: tiles x, x + gridDim.x,
+// ...), y = row tile.  After each tile its logits pass through LDS 64 columns at a time; TPR
+// threads share a row (64 / TPR columns each) and keep running top-16 lists: a thread first
+// marks the columns that beat its list's 16th entry, then inserts only those.  The lists of a
+// row are merged at the end into one partial list per (row, workgroup).
+template <class T, int OCC, bool LOGITS>
+__global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
+  constexpr int BM = T::BMc, BN = T::BNc;
+  constexpr int TPR = T::NT / BM;                 // threads per row
+  constexpr int CPT = 64 / TPR;                   // columns per thread in a 64-column pass
+  static_assert(T::NT % BM == 0 && CPT % 4 == 0, "row split");
+  static_assert(T::LDS >= BM * 68 * 4, "epilogue buffer must fit in the stages");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS];
+  float (*ep)[68] = reinterpret_cast<float (*)[68]>(smem);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WGNc, wn = wave % T::WGNc, li = lane & 15, kg = lane >> 4;
+  const int Mv = rows_valid(p);
+  const int m0 = blockIdx.y * BM;
+  if (m0 >= Mv) return;
+  const int ntiles = (p.N + BN - 1) / BN;
+  const int nk = p.K / MK;
+  const int lrow = tid / TPR, part = tid % TPR;
+  const int my_row = m0 + lrow;
+  const bool row_live = my_row < Mv && (my_row % p.block) != 0;
+  Top16 top;
+  top.init();
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int n0 = t * BN;
+    f32x4 acc[T::FM][T::FN];
+    tile_run<T>(p, smem, m0, n0, Mv, 0, nk, acc);
+    wait_barrier<0>();   // every wave is done reading the stages; the epilogue buffer overlays them
+#pragma unroll
+    for (int q = 0; q < BN / 64; ++q) {
+      const int owner = (q * 64) / T::WN;        // wave column holding these 64 columns
+      const int j0 = ((q * 64) % T::WN) / 16;
+      static_assert(T::WN % 64 == 0, "a 64-column pass lies in one wave column");
+      if (wn == owner) {
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ep[wm * T::WM + i * 16 + kg * 4 + r][jj * 16 + li] = acc[i][j0 + jj][r];
+      }
+      wait_barrier<0>();
+      const int cb = part * CPT;
+      if (LOGITS && my_row < Mv) {
+        for (int c = 0; c < CPT; ++c) store_logit(p, my_row, n0 + q * 64 + cb + c, ep[lrow][cb + c]);
+      }
+      if (row_live) {
+        // which of the thread's columns beat its current 16th entry; then one push per such
+        // column, so a wave runs as many pushes as its busiest lane needs (not one per column
+        // that any lane needs)
+        const int cg = n0 + q * 64 + cb;         // global column of the thread's first value
+        const float tv = top.v[TOPK - 1];
+        const int ti = top.id[TOPK - 1];
+        unsigned mask = 0;
+#pragma unroll
+        for (int c4 = 0; c4 < CPT / 4; ++c4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&ep[lrow][cb + c4 * 4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int col = cg + c4 * 4 + e;
+            mask |= (unsigned)(col < p.N && cand_better(v[e], col, tv, ti)) << (c4 * 4 + e);
+          }
+        }
+        while (mask) {
+          const int c = __builtin_ctz(mask);
+          mask &= mask - 1;
+          top.push(ep[lrow][cb + c], cg + c);
+        }
+      }
+      wait_barrier<0>();
+    }
+  }
+  // merge the TPR lists of each row through LDS (pairwise halving)
+  float (*mv)[TOPK + 1] = reinterpret_cast<float (*)[TOPK + 1]>(smem);
+  int (*mi)[TOPK + 1] = reinterpret_cast<int (*)[TOPK + 1]>(smem + T::NT * (TOPK + 1) * 4);
+#pragma unroll
+  for (int w = 1; w < TPR; w <<= 1) {
+    if ((part & (2 * w - 1)) == w) {
+#pragma unroll
+      for (int i = 0; i < TOPK; ++i) { mv[tid][i] = top.v[i]; mi[tid][i] = top.id[i]; }
+    }
+    wait_barrier<0>();
+    if ((part & (2 * w - 1)) == 0) {
+#pragma unroll
+      for (int i = 0; i < TOPK; ++i) top.push(mv[tid + w][i], mi[tid + w][i]);
+    }
+    wait_barrier<0>();
+  }
+  if (part == 0 && my_row < Mv) store_partial(p, my_row, blockIdx.x, top);
+}
+
+}  // namespace
+
+// Tile configurations: 0 = 128 x 128 (2 x 2 waves, 3 stages, two workgroups per CU),
+// 1 = 256 x 256 (4 x 2 waves of 64 x 128, two waves per SIMD, 3 stages, one workgroup per CU).
+using TileSmall = TileCfg<128, 128, 2, 2, 3>;
+using TileBig = TileCfg<256, 256, 4, 2, 3>;
+
+hipError_t tile_launch(const GemmPlan& pl, int mode, const GemmParams& p, hipStream_t st) {
+  if (p.K % MK) return hipErrorInvalidValue;
+  if (mode == GEMM_TOPK) {
+    if (pl.mt) {
+      const dim3 blk(TileBig::NT);
+      if (p.logits) hipLaunchKernelGGL((lmhead_topk_tile<TileBig, 1, true>), pl.grid, blk, 0, st, p);
+      else hipLaunchKernelGGL((lmhead_topk_tile<TileBig, 1, false>), pl.grid, blk, 0, st, p);
+    } else {
+      const dim3 blk(TileSmall::NT);
+      if (p.logits) hipLaunchKernelGGL((lmhead_topk_tile<TileSmall, 2, true>), pl.grid, blk, 0, st, p);
+      else hipLaunchKernelGGL((lmhead_topk_tile<TileSmall, 2, false>), pl.grid, blk, 0, st, p);
+    }
+  } else if (mode == GEMM_PARTIAL) {
+    if (pl.mt) hipLaunchKernelGGL((gemm_tile_partial<TileBig, 1>), pl.grid, dim3(TileBig::NT), 0, st, p);
+    else hipLaunchKernelGGL((gemm_tile_partial<TileSmall, 2>), pl.grid, dim3(TileSmall::NT), 0, st, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dfl

@@ -37,22 +37,54 @@ struct GemmParams {
   int groups;
   int block;
   float* logits;          // optional full logits [row/block][block-1][N] for slots >= 1
-  int* counter;           // TOPK skinny: per-row-tile fragment counters, zero before the launch
+  int* counter;           // TOPK skinny (17..64 rows): per-row-tile fragment counters, zero before the launch
 };
 
 struct GemmPlan {
-  int kind;      // 0 = skinny, 1 = tiled, 2 = f32 simple, 3 = stream (<= 16 rows), 4 = lm_head waves
+  int kind;      // 0 = skinny (17..64 rows), 2 = f32 simple, 3 = stream (<= 16 rows), 4 = lm_head
+                 // waves (<= 16 rows), 5 = MFMA tiles with LDS-DMA operands (more than 64 rows)
   int slc;       // stream: 64-wide chunks per wave
-  int mt;        // skinny row fragments (1,2,4)
+  int mt;        // skinny: row fragments (1,2,4); MFMA tiles: 0 = 128 x 128, 1 = 256 x 256
   int splits;
   int groups;    // TOPK groups
   dim3 grid;
 };
+
+// Row n of the segmented weight matrix.
+__device__ __forceinline__ const bf16* brow_ptr(const GemmParams& p, int n) {
+  const int s = n / p.seg_rows;
+  return reinterpret_cast<const bf16*>(p.seg[s]) + (size_t)(n - s * p.seg_rows) * p.ldb;
+}
+
+// Rows the launch computes: M, or the device row count when one is given.
+__device__ __forceinline__ int rows_valid(const GemmParams& p) {
+  return p.m_dev ? max(0, min(p.M, *p.m_dev - p.m_off)) : p.M;
+}
+
+// Writes one wave-tile of logits (rows of slot >= 1 only) when full logits are requested.
+__device__ __forceinline__ void store_logit(const GemmParams& p, int row, int col, float v) {
+  const int slot = row % p.block;
+  if (slot == 0 || col >= p.N) return;
+  const size_t orow = (size_t)(row / p.block) * (p.block - 1) + (slot - 1);
+  p.logits[orow * p.N + col] = v;
+}
+
+// Stores one (row, group) partial top-16 list.
+__device__ __forceinline__ void store_partial(const GemmParams& p, int row, int group, const Top16& t) {
+  const size_t base = ((size_t)row * p.groups + group) * TOPK;
+#pragma unroll
+  for (int i = 0; i < TOPK; ++i) {
+    p.tk_val[base + i] = t.v[i];
+    p.tk_id[base + i] = t.id[i];
+  }
+}
 
 // Chooses the launch shape; deterministic in (dtype, mode, M, N, K).
 GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K);
 // Bytes of partial output the plan writes (PARTIAL) or top-k partial entries (TOPK).
 size_t gemm_part_floats(const GemmPlan& pl, int mode, int M, int N);
 hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hipStream_t st);
+// Tiled MFMA kernels for more than 64 rows (pl.kind 5; pl.mt selects the tile shape).
+hipError_t tile_launch(const GemmPlan& pl, int mode, const GemmParams& p, hipStream_t st);
 
 }  // namespace dfl
