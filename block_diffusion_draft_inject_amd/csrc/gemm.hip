@@ -290,17 +290,31 @@ struct StreamBuf {
   u32x4 b[SLC][NF][2];
 };
 
-template <int SLC, int NF>
+// SWIGLU fragments interleave the two halves: lanes li < 8 take gate rows 8f .. 8f + 7, lanes
+// li >= 8 the matching up rows half + 8f .. (so the epilogue pairs lane li with lane li + 8).
+template <int SLC, int NF, bool GLU>
 __device__ __forceinline__ void stream_load(StreamBuf<SLC, NF>& x, const GemmParams& p, int ncols, int f, int kw,
                                             int kg, int li) {
 #pragma unroll
   for (int nf = 0; nf < NF; ++nf) {
-    // the 16 rows of a fragment lie in one weight segment (segment sizes and `half` are
-    // multiples of 16): its index is wave-uniform, so the segment pointer is a scalar load and
-    // never joins the vector-memory queue that the prefetches wait in
-    const int seg = __builtin_amdgcn_readfirstlane((f * 16 + nf * p.half) / p.seg_rows);
-    const int n = min(f * 16 + li, ncols - 1) + nf * p.half - seg * p.seg_rows;
-    const bf16* row = reinterpret_cast<const bf16*>(p.seg[seg]) + (size_t)n * p.ldb;
+    // the rows of a fragment (of each half for SWIGLU) lie in one weight segment (segment
+    // sizes and `half` are multiples of 16, of 8 for SWIGLU): the segment index is
+    // wave-uniform, so the segment pointer is a scalar load and never joins the vector-memory
+    // queue that the prefetches wait in
+    const bf16* row;
+    if (GLU) {
+      const int g0 = f * 8, u0 = p.half + f * 8;
+      const int sg = __builtin_amdgcn_readfirstlane(g0 / p.seg_rows);
+      const int su = __builtin_amdgcn_readfirstlane(u0 / p.seg_rows);
+      const int j = min(g0 + (li & 7), ncols - 1) - g0;
+      const bf16* bg = reinterpret_cast<const bf16*>(p.seg[sg]) + (size_t)(g0 - sg * p.seg_rows) * p.ldb;
+      const bf16* bu = reinterpret_cast<const bf16*>(p.seg[su]) + (size_t)(u0 - su * p.seg_rows) * p.ldb;
+      row = (li < 8 ? bg : bu) + (size_t)j * p.ldb;
+    } else {
+      const int seg = __builtin_amdgcn_readfirstlane((f * 16 + nf * p.half) / p.seg_rows);
+      const int n = min(f * 16 + li, ncols - 1) + nf * p.half - seg * p.seg_rows;
+      row = reinterpret_cast<const bf16*>(p.seg[seg]) + (size_t)n * p.ldb;
+    }
 #pragma unroll
     for (int c = 0; c < SLC; ++c) {
       // half h of the chunk: k = 32 h + 8 kg .. +7, so one load instruction covers 64
@@ -330,7 +344,8 @@ __device__ __forceinline__ void stream_mma(const StreamBuf<SLC, NF>& x, const u3
 
 template <int SLC, int MODE, bool LOOP>
 __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
-  constexpr int NF = (MODE == GEMM_SWIGLU) ? 2 : 1;
+  constexpr int NF = 1;
+  constexpr bool GLU = MODE == GEMM_SWIGLU;
   constexpr int RED_FLOATS = 2 * NF * SW * 4 * 64;
   constexpr int MRG = (MODE == GEMM_TOPK) ? 4 * 64 * (TOPK + 1) : 0;   // lane lists for the final merge
   __shared__ __align__(16) float smem[RED_FLOATS + 2 * MRG];
@@ -340,8 +355,8 @@ __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, kg = lane >> 4;
   const int Mv = rows_valid(p);
-  const int ncols = (MODE == GEMM_SWIGLU) ? p.half : p.N;
-  const int nfrag = (ncols + 15) / 16;
+  const int ncols = GLU ? p.half : p.N;
+  const int nfrag = GLU ? (ncols + 7) / 8 : (ncols + 15) / 16;
   if (Mv <= 0 || (int)blockIdx.x >= nfrag) return;    // uniform over the workgroup
   const int s = blockIdx.y;
   const int kw = (s * SW + wave) * SLC * 64;
@@ -374,23 +389,24 @@ __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
       for (int j = 0; j < 4; ++j) red[buf][nf][wave][j][lane] = acc[nf][j];
     lds_barrier();
     if (!epi) return;
-    float v[NF];
+    float v = 0.f;
 #pragma unroll
-    for (int nf = 0; nf < NF; ++nf) {
-      float t = 0.f;
-#pragma unroll
-      for (int w = 0; w < SW; ++w) t += red[buf][nf][w][wave][lane];
-      v[nf] = t;
+    for (int w = 0; w < SW; ++w) v += red[buf][0][w][wave][lane];
+    if (GLU) {
+      // lane li < 8 holds gate column 8f + li, lane li + 8 the matching up column
+      const float up = dpp_f<0x128>(v);   // row_ror:8 -- lane li reads lane li ^ 8 of its row
+      const int col = f * 8 + li;
+      if (li < 8 && row < Mv && col < ncols)
+        st_act(reinterpret_cast<bf16*>(p.out), (size_t)row * p.half + col, p.out_plane, silu_f(v) * up);
+      return;
     }
     const int col = f * 16 + li;
     if (row >= Mv || col >= ncols) return;
     if (MODE == GEMM_PARTIAL) {
-      p.part[((size_t)s * p.M + row) * p.N + col] = v[0];
-    } else if (MODE == GEMM_SWIGLU) {
-      st_act(reinterpret_cast<bf16*>(p.out), (size_t)row * p.half + col, p.out_plane, silu_f(v[0]) * v[NF - 1]);
+      p.part[((size_t)s * p.M + row) * p.N + col] = v;
     } else {
-      if (p.logits) store_logit(p, row, col, v[0]);
-      if (row_live) top.push(v[0], col);
+      if (p.logits) store_logit(p, row, col, v);
+      if (row_live) top.push(v, col);
     }
   };
   f32x4 acc[NF];
@@ -398,7 +414,7 @@ __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
   if (!LOOP) {
     // one fragment for this workgroup
     StreamBuf<SLC, NF> x;
-    stream_load(x, p, ncols, f, kw, kg, li);
+    stream_load<SLC, NF, GLU>(x, p, ncols, f, kw, kg, li);
     stream_mma(x, ah, al, acc);
     finish(acc, 0, f);
   } else {
@@ -408,10 +424,10 @@ __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
     const int G = gridDim.x;
     StreamBuf<SLC, NF> x, y;
     int buf = 0;
-    stream_load(x, p, ncols, f, kw, kg, li);
+    stream_load<SLC, NF, GLU>(x, p, ncols, f, kw, kg, li);
     while (true) {
       const int fy = f + G;
-      stream_load(y, p, ncols, min(fy, nfrag - 1), kw, kg, li);
+      stream_load<SLC, NF, GLU>(y, p, ncols, min(fy, nfrag - 1), kw, kg, li);
       __builtin_amdgcn_sched_barrier(0);
       stream_mma(x, ah, al, acc);
       finish(acc, buf, f);
@@ -419,7 +435,7 @@ __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
       f = fy;
       buf ^= 1;
       const int fx = f + G;
-      stream_load(x, p, ncols, min(fx, nfrag - 1), kw, kg, li);
+      stream_load<SLC, NF, GLU>(x, p, ncols, min(fx, nfrag - 1), kw, kg, li);
       __builtin_amdgcn_sched_barrier(0);
       stream_mma(y, ah, al, acc);
       finish(acc, buf, f);
@@ -692,7 +708,7 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
     // stream kernel: slice = SW waves x slc chunks of 64; full K in one workgroup for the
     // nonlinear epilogues, k-splits for PARTIAL
     const int ncols = (mode == GEMM_SWIGLU) ? N / 2 : N;
-    const int nfrag = (ncols + 15) / 16;
+    const int nfrag = (mode == GEMM_SWIGLU) ? (ncols + 7) / 8 : (ncols + 15) / 16;   // SWIGLU: 8 + 8 columns
     // workgroups loop over fragments: the fragment stride is the largest divisor of the
     // fragment count that keeps the launch at most 256 workgroups (one per CU is enough to
     // stream; every workgroup then has the same number of fragments and loads its activation
@@ -794,10 +810,11 @@ hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hi
     return hipGetLastError();
   }
   if (pl.kind == 3) {
-    if ((p.seg_rows % 16 && p.seg_rows < p.N) || p.half % 16) return hipErrorInvalidValue;
+    if ((p.seg_rows % 16 && p.seg_rows < p.N) || p.half % 8) return hipErrorInvalidValue;
     const dim3 sb(SW * 64);
     const int ncols = (mode == GEMM_SWIGLU) ? p.half : p.N;
-    const bool loop = (int)pl.grid.x < (ncols + 15) / 16;
+    const int nfrag = (mode == GEMM_SWIGLU) ? (ncols + 7) / 8 : (ncols + 15) / 16;
+    const bool loop = (int)pl.grid.x < nfrag;
 #define DFL_STREAM_MODE(SLC, MODE)                                                                    \
   if (loop) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, true>), pl.grid, sb, 0, st, p);         \
   else hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, false>), pl.grid, sb, 0, st, p);
