@@ -306,12 +306,20 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int K = a.K, dh = a.dh, G = a.nh / a.nkv, R = G * K;
   const size_t base = ((size_t)b * a.nkv + kvh) * a.chunks;
   const int nc = a.chunks;
+  // the first CB chunks' partial outputs are loaded in the same burst as the maxima and sums
+  constexpr int CB = 32;
+  const size_t cstride = (size_t)R * dh;
+  const float* op = a.o_part + (base * R + r) * dh + min(tid, dh - 1);
+  float x[CB];
+#pragma unroll
+  for (int u = 0; u < CB; ++u) x[u] = op[(size_t)min(u, nc - 1) * cstride];
   float mc[2], lc[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int c = tid + 128 * u;
-    mc[u] = c < nc ? a.m_part[(base + c) * R + r] : NEG_INF;
-    lc[u] = c < nc ? a.l_part[(base + c) * R + r] : 0.f;
+    const int c = min(tid + 128 * u, nc - 1);
+    mc[u] = a.m_part[(base + c) * R + r];
+    lc[u] = a.l_part[(base + c) * R + r];
+    if (tid + 128 * u >= nc) { mc[u] = NEG_INF; lc[u] = 0.f; }
   }
   float M = wave_max(fmaxf(mc[0], mc[1]));
   if ((tid & 63) == 0) red[tid >> 6] = M;
@@ -332,15 +340,15 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   if (tid == 0) s_den = red[0] + red[1];
   __syncthreads();
   if (tid >= dh) return;
-  const float* op = a.o_part + (base * R + r) * dh + tid;
-  const size_t cstride = (size_t)R * dh;
   float num = 0.f;
-  for (int c0 = 0; c0 < nc; c0 += 8) {
-    float x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = (c0 + u < nc) ? op[(size_t)(c0 + u) * cstride] : 0.f;
+  for (int u = 0; u < CB; ++u) num += (u < nc) ? wgt[u] * x[u] : 0.f;
+  for (int c0 = CB; c0 < nc; c0 += 8) {
+    float y[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) num += (c0 + u < nc) ? wgt[c0 + u] * x[u] : 0.f;
+    for (int u = 0; u < 8; ++u) y[u] = (c0 + u < nc) ? op[(size_t)(c0 + u) * cstride] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) num += (c0 + u < nc) ? wgt[c0 + u] * y[u] : 0.f;
   }
   const int g = r / K, t = r % K, h = kvh * G + g;
   st_act(reinterpret_cast<T*>(a.o), ((size_t)(b * K + t) * a.nh + h) * dh + tid, a.o_plane, num / s_den);

@@ -116,7 +116,9 @@ __device__ __forceinline__ void st4_act(void* p, size_t i, size_t plane, f32x4 v
 }
 __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
 
-template <typename T, int NV>
+// MS: the largest k-split count the launch allows for (the loads of absent splits are not
+// issued at all)
+template <typename T, int NV, int MS>
 __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
   __shared__ float red[8 * 4];
   const int row = blockIdx.x, tid = threadIdx.x;
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
   using W4 = typename Raw4<T>::type;
   f32x4 hv[2][NV], pw[2][NV], qw[2][NV], g[NV];
   W4 rpw[2][NV], rqw[2][NV], rg[NV];
-  f32x4 pv[PP_MAXS][3][NV];
+  f32x4 pv[MS][3][NV];
   const bool pre = conv && !fin;
   const void* pwp = conv ? a.post_w : a.pre_gain;
   const void* qwp = pre ? a.pre_w : a.pre_gain;
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
   const T rpb0 = pbp[0], rpb1 = pbp[1], rqb0 = qbp[0], rqb1 = qbp[1];
   const int nsp = max(a.splits, 1);
 #pragma unroll
-  for (int sp = 0; sp < PP_MAXS; ++sp)
+  for (int sp = 0; sp < MS; ++sp)
 #pragma unroll
     for (int q = 0; q < 3; ++q)
 #pragma unroll
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
     if (!(in && conv && t >= 1)) hv[0][i] = z4;
     if (!in) hv[1][i] = z4;
 #pragma unroll
-    for (int sp = 0; sp < PP_MAXS; ++sp)
+    for (int sp = 0; sp < MS; ++sp)
 #pragma unroll
       for (int q = 0; q < 3; ++q)
         if (!(in && sp < a.splits && q >= q0)) pv[sp][q][i] = z4;
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
     for (int i = 0; i < NV; ++i) {
       f32x4 acc = pv[0][q][i];
 #pragma unroll
-      for (int sp = 1; sp < PP_MAXS; ++sp) acc += pv[sp][q][i];
+      for (int sp = 1; sp < MS; ++sp) acc += pv[sp][q][i];
       s[q][i] = acc;
     }
   // post-conv taps of rows t-1 and t
@@ -276,12 +278,25 @@ __global__ __launch_bounds__(64) void qkv_post_kernel(QkvArgs a) {
   const int col0 = head * dh;   // column in the fused [q | k | v] output
   float x0 = 0.f, x1 = 0.f;
   const bool act = lane < half;
-  if (act) {
-    for (int sp = 0; sp < a.splits; ++sp) {
-      const float* pr = a.part + ((size_t)sp * a.part_rows + row) * a.N + col0;
-      x0 += pr[lane];
-      x1 += pr[lane + half];
+  {
+    // all split loads in one burst at valid addresses (clamped split and lane), masked after
+    constexpr int QS = 8;
+    const int hl = act ? lane : 0;
+    float p0[QS], p1[QS];
+#pragma unroll
+    for (int sp = 0; sp < QS; ++sp) {
+      const float* pr = a.part + ((size_t)min(sp, a.splits - 1) * a.part_rows + row) * a.N + col0;
+      p0[sp] = pr[hl];
+      p1[sp] = pr[hl + half];
     }
+#pragma unroll
+    for (int sp = 0; sp < QS; ++sp) {
+      if (sp < a.splits) {
+        x0 += p0[sp];
+        x1 += p1[sp];
+      }
+    }
+    if (!act) x0 = x1 = 0.f;
   }
   T* dst;
   int gain_kind;   // 0 = q, 1 = k, 2 = v
@@ -817,20 +832,30 @@ hipError_t launch_embed_pre(bool bf, const RowArgs& a, int rows, hipStream_t st)
   }
   return hipGetLastError();
 }
-template <int NV>
+template <int NV, int MS>
 static void launch_pp(bool bf, const RowArgs& a, int rows, hipStream_t st) {
-  if (bf) hipLaunchKernelGGL((post_pre_kernel<bf16, NV>), dim3(rows), dim3(PP_T), 0, st, a);
-  else hipLaunchKernelGGL((post_pre_kernel<float, NV>), dim3(rows), dim3(PP_T), 0, st, a);
+  if (bf) hipLaunchKernelGGL((post_pre_kernel<bf16, NV, MS>), dim3(rows), dim3(PP_T), 0, st, a);
+  else hipLaunchKernelGGL((post_pre_kernel<float, NV, MS>), dim3(rows), dim3(PP_T), 0, st, a);
+}
+template <int NV>
+static void launch_pp_s(bool bf, const RowArgs& a, int rows, hipStream_t st) {
+  if (a.splits <= 1) launch_pp<NV, 1>(bf, a, rows, st);
+  else if (a.splits <= 2) launch_pp<NV, 2>(bf, a, rows, st);
+  else if (a.splits <= 3) launch_pp<NV, 3>(bf, a, rows, st);
+  else if (a.splits <= 4) launch_pp<NV, 4>(bf, a, rows, st);
+  else if (a.splits <= 6) launch_pp<NV, 6>(bf, a, rows, st);
+  else launch_pp<NV, PP_MAXS>(bf, a, rows, st);
 }
 hipError_t launch_post_pre(bool bf, const RowArgs& a, int rows, hipStream_t st) {
   if (a.splits > PP_MAXS || a.d % 4) return hipErrorInvalidValue;
   const int v = (a.d + 4 * PP_T - 1) / (4 * PP_T);
-  if (v <= 1) launch_pp<1>(bf, a, rows, st);
-  else if (v <= 2) launch_pp<2>(bf, a, rows, st);
+  if (v <= 1) launch_pp_s<1>(bf, a, rows, st);
+  else if (v <= 2) launch_pp_s<2>(bf, a, rows, st);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 hipError_t launch_qkv_post(bool bf, const QkvArgs& a, int rows, hipStream_t st) {
+  if (a.splits < 1 || a.splits > 8) return hipErrorInvalidValue;
   DFL_T_DISPATCH(bf, qkv_post_kernel, dim3(rows, a.nh + 2 * a.nkv), dim3(64), st, a);
   return hipGetLastError();
 }
