@@ -163,3 +163,32 @@ def test_mid_bf16_two_blocks_k8_ragged_inject(H):
         case.inject(seq_ids, pos, start_pos=(Ls == [0, 0]))
         Ls = [Ls[0] + n0, Ls[1] + n1]
     _check(H, case, seq_ids, anchors=[12, 8190])
+
+
+def _same_topk_without_logits(case, seq_ids, anchors, res):
+    """The launch without full logits (a separate kernel instantiation) gives the same top-16."""
+    plain = case.draft(seq_ids, anchors, logits=False)
+    assert np.array_equal(plain["topk_ids"], res["topk_ids"])
+    assert np.array_equal(plain["topk_logits"], res["topk_logits"])
+
+
+def test_mid_bf16_big_tiles_ragged_vocab(H):
+    """12 sequences at K=16 (192 rows: the 256 x 256 lm_head tiles, rows past 192 idle) and a
+    vocabulary of 8000 (not a multiple of the 128- or 256-column tiles: the last tile reads
+    clamped weight rows whose columns the epilogue must skip)."""
+    cfg = MID.replace(vocab=8000, mask_id=7999, name="mid_bf16_v8000")
+    case = H.Case(cfg, max_seqs=12, max_batch=12, max_inject_rows=160)
+    seq_ids = list(range(12))
+    rng = np.random.default_rng(3)
+    spans = [(0, int(L)) for L in rng.integers(1, 150, size=12)]
+    anchors = rng.integers(0, cfg.vocab - 1, size=12).tolist()
+    res = _full_check(H, case, seq_ids, spans, anchors, mode_names=("viterbi",))
+    _same_topk_without_logits(case, seq_ids, anchors, res)
+
+
+def test_mid_bf16_lm_head_wave_kernel_without_logits(H):
+    """Batch 1, K=16 (the independent-wave lm_head): top-16 with and without full logits."""
+    case = H.Case(MID, max_seqs=2, max_batch=1, max_inject_rows=64)
+    _prefill(case, [1], [(0, 50)])
+    res = _check(H, case, [1], [123], mode_names=("viterbi",))
+    _same_topk_without_logits(case, [1], [123], res)
