@@ -238,13 +238,20 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
       if (LOGITS && my_row < Mv) {
         for (int c = 0; c < CPT; ++c) store_logit(p, my_row, n0 + q * 64 + cb + c, ep[lrow][cb + c]);
       }
+      // threshold: the better of the 16th entries of the row's lists (a value below another
+      // list's 16th entry has 16 better values in that list and cannot reach the row's top 16)
+      float tv = top.v[TOPK - 1];
+      int ti = top.id[TOPK - 1];
+      if (TPR == 2) {   // the partner thread of the row is lane ^ 1
+        const float pv = dpp_f<0xB1>(tv);
+        const int pi = dpp_i<0xB1>(ti);
+        if (cand_better(pv, pi, tv, ti)) { tv = pv; ti = pi; }
+      }
       if (row_live) {
-        // which of the thread's columns beat its current 16th entry; then one push per such
-        // column, so a wave runs as many pushes as its busiest lane needs (not one per column
-        // that any lane needs)
+        // which of the thread's columns beat the threshold; then one push per such column, so
+        // a wave runs as many pushes as its busiest lane needs (not one per column that any
+        // lane needs)
         const int cg = n0 + q * 64 + cb;         // global column of the thread's first value
-        const float tv = top.v[TOPK - 1];
-        const int ti = top.id[TOPK - 1];
         unsigned mask = 0;
 #pragma unroll
         for (int c4 = 0; c4 < CPT / 4; ++c4) {

@@ -259,18 +259,47 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
       const f32x4 p1v = *reinterpret_cast<const f32x4*>(&dv[0][4 * qa]);
       const f32x4 p2v = *reinterpret_cast<const f32x4*>(&dv[1][4 * qa]);
       const f32x4 sv = *reinterpret_cast<const f32x4*>(&S[t - 1][bi][4 * qa]);
-      float s1 = NEG_INF, s2 = NEG_INF;
-      int c1 = 255, c2 = 255;
+      // A predecessor's rank-1 extension always beats its rank-2 one (same pair term, better
+      // or equal partial score, smaller code), so the best two of the 32 candidates are: the
+      // best rank-1 extension b, and the better of the second-best rank-1 extension s and the
+      // rank-2 extension w of b's predecessor.  Each lane summarises its four predecessors as
+      // (b, s, w); the quad merges summaries.  An absent path enters as (-inf, 255).
+      float bs = NEG_INF, ss = NEG_INF, ws = NEG_INF;
+      int bc = 255, sc = 255, wc = 255;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ai = 4 * qa + i;
-        // candidates in code order 2 ai (rank 1), 2 ai + 1 (rank 2); an absent path enters as
-        // (-inf, 255), which never beats a list entry, i.e. it is skipped
-        top2_push(s1, c1, s2, c2, p1v[i] + sv[i], p1v[i] != NEG_INF ? 2 * ai : 255);
-        top2_push(s1, c1, s2, c2, p2v[i] + sv[i], p2v[i] != NEG_INF ? 2 * ai + 1 : 255);
+        const float v1 = p1v[i] + sv[i], v2 = p2v[i] + sv[i];
+        const int c1 = p1v[i] != NEG_INF ? 2 * ai : 255, c2 = p2v[i] != NEG_INF ? 2 * ai + 1 : 255;
+        const bool top = vit_better(v1, c1, bs, bc);
+        const bool sec = !top && vit_better(v1, c1, ss, sc);
+        ss = top ? bs : (sec ? v1 : ss);
+        sc = top ? bc : (sec ? c1 : sc);
+        ws = top ? v2 : ws;
+        wc = top ? c2 : wc;
+        bs = top ? v1 : bs;
+        bc = top ? c1 : bc;
       }
-      top2_quad<0xB1>(s1, c1, s2, c2);
-      top2_quad<0x4E>(s1, c1, s2, c2);
+      auto merge = [&](float obs, int obc, float oss, int osc, float ows, int owc) {
+        const bool theirs = vit_better(obs, obc, bs, bc);
+        // the loser's best competes with the winner's second
+        const float ls = theirs ? bs : obs, ws2 = theirs ? oss : ss;
+        const int lc = theirs ? bc : obc, wsc = theirs ? osc : sc;
+        const bool lb = vit_better(ls, lc, ws2, wsc);
+        ss = lb ? ls : ws2;
+        sc = lb ? lc : wsc;
+        ws = theirs ? ows : ws;
+        wc = theirs ? owc : wc;
+        bs = theirs ? obs : bs;
+        bc = theirs ? obc : bc;
+      };
+      merge(quad_perm_f<0xB1>(bs), quad_perm_i<0xB1>(bc), quad_perm_f<0xB1>(ss), quad_perm_i<0xB1>(sc),
+            quad_perm_f<0xB1>(ws), quad_perm_i<0xB1>(wc));
+      merge(quad_perm_f<0x4E>(bs), quad_perm_i<0x4E>(bc), quad_perm_f<0x4E>(ss), quad_perm_i<0x4E>(sc),
+            quad_perm_f<0x4E>(ws), quad_perm_i<0x4E>(wc));
+      const bool wsec = vit_better(ws, wc, ss, sc);
+      const float s1 = bs, s2 = wsec ? ws : ss;
+      const int c1 = bc, c2 = wsec ? wc : sc;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
