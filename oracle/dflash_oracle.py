@@ -25,6 +25,10 @@ What it computes, and where the pages say so:
   incoherent": S_t(a, b) = U_t(b) + < A(a) * H(h_t), B(b) >.
 * Greedy verification -- "Architecture", section "Speculative Decoding Context" and the
   sequence diagram: accept the longest valid prefix plus one bonus token.
+* Sampling walk and rejection-sampling verification -- "Architecture", section "Problem 1"
+  (sampling draws from the same pair scores; rejection sampling restores the exact target
+  distribution), flowchart "Verification" and section "Speculative Decoding Context"
+  (rejection sampling makes the scheme lossless).
 
 Readings taken where the pages are silent (each also listed in the design notes):
 RMSNorm over the whole concatenation then the fc projection, no bias; K/V of the
@@ -364,6 +368,73 @@ def verify_greedy(draft, target):
         n += 1
     committed = draft[:n] + [target[n]] + [-1] * (K - 1 - n)
     return n, np.array(committed, dtype=np.int64), target[n]
+
+
+# --------------------------------------------------------------------------------------
+# sampling walk and rejection-sampling verification
+# --------------------------------------------------------------------------------------
+
+def inverse_cdf(weights, u):
+    """Smallest index i with u * sum(weights) < sum(weights[:i + 1]) (u in [0, 1)); the last
+    index with positive weight if rounding leaves none."""
+    w = np.asarray(weights, dtype=F64)
+    c = np.cumsum(w)
+    target = u * c[-1]
+    hit = np.nonzero(target < c)[0]
+    if hit.size:
+        return int(hit[0])
+    return int(np.nonzero(w > 0)[0][-1])
+
+
+def sample_walk(S, uniforms, temperature):
+    """Sampling walk over the candidate lattice.  At slot t the candidate b is drawn from the
+    conditional distribution q_t(b) = softmax_b(S_t(a, b) / T) given the previous pick a (the
+    anchor for slot 1), by inverse CDF in candidate order with the supplied uniform u_t.
+
+    Returns (idx [K-1], q_path [K-1] = q_t(picked), q_cand [K-1][16] = q_t over the slot's
+    candidates given the previous pick)."""
+    idx, q_path, q_cand = [], [], []
+    a = 0
+    for t, St in enumerate(S):
+        z = np.asarray(St[a], dtype=F64) / temperature
+        q = np.exp(z - z.max())
+        q /= q.sum()
+        b = inverse_cdf(q, float(uniforms[t]))
+        idx.append(b)
+        q_path.append(q[b])
+        q_cand.append(q)
+        a = b
+    return np.array(idx), np.array(q_path), np.array(q_cand)
+
+
+def verify_rejection(draft, q_path, cand_ids, q_cand, target_probs, u_accept, u_resample):
+    """Rejection-sampling verification of one block (speculative sampling).
+
+    draft d_1..d_{K-1} with the drafter's probabilities q_i(d_i) (q_path) and its full
+    distribution at slot i, q_i(v) = q_cand[i-1][j] for v = cand_ids[i-1][j], else 0;
+    target_probs [K][V]: p_i for slot i at row i-1, the bonus distribution p_K at row K-1.
+    Draft i is accepted iff u_i < p_i(d_i) / q_i(d_i), in order, up to the first rejection.
+    At a rejection at slot i the committed token is drawn from r(v) = max(0, p_i(v) - q_i(v))
+    (normalised); if every draft is accepted a bonus token is drawn from p_K.  Both draws use
+    u_resample by inverse CDF in token order.  Returns (n, committed [K] padded with -1,
+    next_anchor) like verify_greedy."""
+    draft = [int(x) for x in draft]
+    K = len(draft) + 1
+    p = np.asarray(target_probs, dtype=F64)
+    n = 0
+    while n < K - 1 and u_accept[n] * q_path[n] < p[n, draft[n]]:
+        n += 1
+    if n < K - 1:
+        r = p[n].copy()
+        for j, v in enumerate(cand_ids[n]):
+            r[int(v)] = max(0.0, p[n, int(v)] - float(q_cand[n][j]))
+        if r.sum() <= 0:
+            r = p[n].copy()
+    else:
+        r = p[K - 1].copy()
+    tok = inverse_cdf(r, float(u_resample))
+    committed = draft[:n] + [tok] + [-1] * (K - 1 - n)
+    return n, np.array(committed, dtype=np.int64), tok
 
 
 def expected_tau(match_probs):

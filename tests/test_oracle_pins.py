@@ -498,3 +498,121 @@ def test_synthetic_inputs_are_deterministic():
     assert np.array_equal(s1[2], s2[0])
     gains = a["layers"][0]["attn_norm"].values
     assert abs(gains.mean() - 1.0) < 0.01 and gains.std() > 0.01
+
+
+# --------------------------------------------------------------------------------------
+# sampling walk and rejection-sampling verification
+# --------------------------------------------------------------------------------------
+
+def _softmax(z):
+    e = np.exp(z - np.max(z))
+    return e / e.sum()
+
+
+def test_inverse_cdf_boundaries():
+    w = np.array([0.0, 0.25, 0.0, 0.5, 0.25])
+    assert O.inverse_cdf(w, 0.0) == 1          # first index with positive weight
+    assert O.inverse_cdf(w, 0.2499) == 1
+    assert O.inverse_cdf(w, 0.25) == 3         # the boundary belongs to the next interval
+    assert O.inverse_cdf(w, 0.7499) == 3
+    assert O.inverse_cdf(w, 0.75) == 4
+    assert O.inverse_cdf(w, 0.999999) == 4
+
+
+def test_sample_walk_joint_distribution():
+    """Empirical joint distribution of two sampled picks equals softmax(S_1/T) x softmax(S_2[b1]/T)."""
+    rng = np.random.default_rng(11)
+    T = 0.7
+    S = [rng.normal(size=(1, 4)), rng.normal(size=(4, 4)) * 1.5]
+    exact = np.outer(_softmax(S[0][0] / T), np.ones(4)) * np.stack([_softmax(S[1][a] / T) for a in range(4)])
+    N = 40000
+    U = rng.random((N, 2))
+    counts = np.zeros((4, 4))
+    for u in U:
+        idx, qp, qc = O.sample_walk(S, u, T)
+        counts[idx[0], idx[1]] += 1
+    emp = counts / N
+    sigma = np.sqrt(exact * (1 - exact) / N)
+    assert np.all(np.abs(emp - exact) < 5 * sigma + 1e-12)
+    # the reported probabilities are the conditionals used for the draw
+    idx, qp, qc = O.sample_walk(S, [0.3, 0.8], T)
+    assert np.allclose(qc[0], _softmax(S[0][0] / T)) and np.allclose(qc[1], _softmax(S[1][idx[0]] / T))
+    assert qp[0] == qc[0][idx[0]] and qp[1] == qc[1][idx[1]]
+
+
+def test_sample_walk_temperature_limits():
+    rng = np.random.default_rng(5)
+    S = [rng.normal(size=(1, 16))] + [rng.normal(size=(16, 16)) for _ in range(4)]
+    # a very low temperature reduces sampling to the greedy walk (any uniform)
+    greedy_idx, _, _ = O.greedy_walk(S)
+    for u in ([0.01] * 5, [0.5] * 5, [0.99] * 5):
+        idx, _, _ = O.sample_walk(S, u, 1e-4)
+        assert list(idx) == list(greedy_idx)
+    # a very high temperature makes every candidate equally likely: u picks floor(16 u)
+    idx, qp, _ = O.sample_walk(S, [0.0, 0.07, 0.5, 0.93, 0.999], 1e6)
+    assert list(idx) == [0, 1, 8, 14, 15]
+    assert np.allclose(qp, 1 / 16, rtol=1e-4)
+
+
+def _drafter_and_target():
+    """Tiny vocabulary: slot 1 and slot 2 candidates with fixed drafter probabilities (slot 2's
+    independent of the slot-1 pick here), and target distributions for slots 1, 2 and the bonus."""
+    cand = np.array([[0, 2, 4], [1, 2, 5]])
+    q = np.array([[0.5, 0.3, 0.2], [0.6, 0.25, 0.15]])
+    p = np.array([[0.10, 0.05, 0.40, 0.15, 0.20, 0.10],
+                  [0.05, 0.30, 0.05, 0.20, 0.15, 0.25],
+                  [0.30, 0.10, 0.10, 0.10, 0.20, 0.20]])
+    return cand, q, p
+
+
+def test_rejection_verification_is_lossless():
+    """Whatever the drafter proposes, the committed tokens follow the target: the first one is
+    distributed as p_1; the second (given the first draft was accepted) as p_2; the third
+    (given both were accepted) as the bonus distribution p_3."""
+    cand, q, p = _drafter_and_target()
+    rng = np.random.default_rng(7)
+    N = 60000
+    first = np.zeros(6)
+    second = np.zeros(6)
+    third = np.zeros(6)
+    n1 = n2 = 0
+    for _ in range(N):
+        j1 = O.inverse_cdf(q[0], rng.random())
+        j2 = O.inverse_cdf(q[1], rng.random())
+        draft = [cand[0][j1], cand[1][j2]]
+        n, com, nxt = O.verify_rejection(draft, [q[0][j1], q[1][j2]], cand, q, p, rng.random(2), rng.random())
+        first[com[0]] += 1
+        if n >= 1:
+            second[com[1]] += 1
+            n1 += 1
+        if n == 2:
+            third[com[2]] += 1
+            n2 += 1
+        assert nxt == com[n]
+    for emp, cnt, target in ((first / N, N, p[0]), (second / n1, n1, p[1]), (third / n2, n2, p[2])):
+        sigma = np.sqrt(target * (1 - target) / cnt)
+        assert np.all(np.abs(emp - target) < 5 * sigma)
+    # acceptance rate of slot 1 = sum_v min(p_1(v), q_1(v)) (the overlap of the two)
+    overlap = sum(min(p[0][v], q[0][j]) for j, v in enumerate(cand[0]))
+    assert abs(n1 / N - overlap) < 5 * math.sqrt(overlap * (1 - overlap) / N)
+
+
+def test_rejection_verification_special_cases():
+    cand, q, p = _drafter_and_target()
+    # target equal to the drafter on slot 1: the draft is always accepted
+    p_eq = p.copy()
+    p_eq[0] = 0.0
+    p_eq[0][cand[0]] = q[0]
+    for u in (0.0, 0.5, 0.999999):
+        n, com, _ = O.verify_rejection([cand[0][1], cand[1][0]], [q[0][1], q[1][0]], cand, q, p_eq, [u, 0.0], 0.3)
+        assert n >= 1
+    # a draft the target gives zero probability is always rejected, never re-drawn
+    p_z = p.copy()
+    p_z[0][4] = 0.0
+    p_z[0] /= p_z[0].sum()
+    for u_res in np.linspace(0, 0.999, 25):
+        n, com, _ = O.verify_rejection([4, 1], [q[0][2], q[1][0]], cand, q, p_z, [0.0, 0.0], u_res)
+        assert n == 0 and com[0] != 4 and list(com[1:]) == [-1, -1]
+    # all accepted: the bonus comes from the last row
+    n, com, nxt = O.verify_rejection([0, 1], [q[0][0], q[1][0]], cand, q, p, [0.0, 0.0], 0.0)
+    assert n == 2 and list(com) == [0, 1, 0] and nxt == 0
