@@ -73,6 +73,11 @@ def lib():
                                          c_void_p]),
         "dflash_select_path": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                          c_void_p, c_void_p, c_void_p]),
+        "dflash_select_sample": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p,
+                                           c_void_p, c_void_p, c_void_p, c_void_p]),
+        "dflash_verify_rejection": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p]),
         "dflash_verify_greedy": (c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                            c_void_p, c_void_p]),
         "dflash_synth_target_argmax": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_float, c_uint64, c_void_p,
@@ -93,7 +98,8 @@ def lib():
 
 EXPORTED = ("dflash_config_check", "dflash_kv_cache_bytes", "dflash_kv_cache_layout", "dflash_workspace_bytes",
             "dflash_create", "dflash_destroy", "dflash_reset_seqs", "dflash_inject_kv", "dflash_draft_block",
-            "dflash_select_path", "dflash_verify_greedy", "dflash_synth_target_argmax", "dflash_timing_enable",
+            "dflash_select_path", "dflash_select_sample", "dflash_verify_rejection", "dflash_verify_greedy",
+            "dflash_synth_target_argmax", "dflash_timing_enable",
             "dflash_timing_read", "dflash_get_device_error", "dflash_status_string", "dflash_last_error")
 
 
@@ -147,6 +153,13 @@ def dflash_verify_greedy(n_seq, block_size, draft_ids, target_argmax, n_accepted
     check("dflash_verify_greedy", lib().dflash_verify_greedy(
         n_seq, block_size, ptr(draft_ids), ptr(target_argmax), ptr(n_accepted), ptr(n_commit), ptr(committed),
         ptr(next_anchor), stream))
+
+
+def dflash_verify_rejection(n_seq, block_size, vocab, draft_ids, q_path, topk_ids, q_cand, target_probs, u_accept,
+                            u_resample, n_accepted, n_commit, committed, next_anchor, stream=None):
+    check("dflash_verify_rejection", lib().dflash_verify_rejection(
+        n_seq, block_size, vocab, ptr(draft_ids), ptr(q_path), ptr(topk_ids), ptr(q_cand), ptr(target_probs),
+        ptr(u_accept), ptr(u_resample), ptr(n_accepted), ptr(n_commit), ptr(committed), ptr(next_anchor), stream))
 
 
 def dflash_synth_target_argmax(n_seq, block_size, vocab, draft_ids, match_prob, seed, counter, target_argmax,
@@ -236,6 +249,13 @@ class Drafter:
         check("dflash_select_path", lib().dflash_select_path(self.h, anchor_ids.numel(), ptr(anchor_ids),
                                                              ptr(topk_ids), ptr(topk_logits), ptr(h_final), mode,
                                                              ptr(path_ids), ptr(path_score), ptr(margin), stream))
+
+    def dflash_select_sample(self, anchor_ids, topk_ids, topk_logits, h_final, temperature, uniforms, path_ids, q_path,
+                             q_cand=None, stream=None):
+        check("dflash_select_sample", lib().dflash_select_sample(self.h, anchor_ids.numel(), ptr(anchor_ids),
+                                                                 ptr(topk_ids), ptr(topk_logits), ptr(h_final),
+                                                                 float(temperature), ptr(uniforms), ptr(path_ids),
+                                                                 ptr(q_path), ptr(q_cand), stream))
 
     def dflash_timing_enable(self, capacity):
         check("dflash_timing_enable", lib().dflash_timing_enable(self.h, capacity))

@@ -683,8 +683,45 @@ dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t*
   if (!anchor_ids || !topk_ids || !topk_logits || !h_final || !path_ids)
     return fail(DFLASH_E_INVALID, "NULL anchor_ids, topk_ids, topk_logits, h_final or path_ids");
   SelectArgs sa{c->block_size, c->hidden, c->sel_rank, (int)mode, c->vocab, dev_err(H), anchor_ids, topk_ids,
-                topk_logits, h_final, H->g_A, H->g_B, H->g_WH, path_ids, path_score, margin};
+                topk_logits, h_final, H->g_A, H->g_B, H->g_WH, path_ids, path_score, margin,
+                1.0f, nullptr, nullptr, nullptr};
   HIP_TRY(launch_select(bf(c), sa, n_seq, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_select_sample(dflash_handle* h, int32_t n_seq, const int32_t* anchor_ids, const int32_t* topk_ids,
+                                   const float* topk_logits, const float* h_final, float temperature,
+                                   const float* uniforms, int32_t* path_ids, float* q_path, float* q_cand,
+                                   void* stream) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  const dflash_config* c = &H->cfg;
+  if (n_seq < 1 || n_seq > H->max_batch) return fail(DFLASH_E_SHAPE, "n_seq %d outside [1, max_batch=%d]", n_seq, H->max_batch);
+  if (!(temperature >= 1e-6f && temperature <= 1e6f)) return fail(DFLASH_E_INVALID, "temperature must be in [1e-6, 1e6]");
+  if (!anchor_ids || !topk_ids || !topk_logits || !h_final || !uniforms || !path_ids || !q_path)
+    return fail(DFLASH_E_INVALID, "NULL anchor_ids, topk_ids, topk_logits, h_final, uniforms, path_ids or q_path");
+  SelectArgs sa{c->block_size, c->hidden, c->sel_rank, 2, c->vocab, dev_err(H), anchor_ids, topk_ids,
+                topk_logits, h_final, H->g_A, H->g_B, H->g_WH, path_ids, nullptr, nullptr,
+                1.0f / temperature, uniforms, q_path, q_cand};
+  HIP_TRY(launch_select(bf(c), sa, n_seq, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_verify_rejection(int32_t n_seq, int32_t block_size, int32_t vocab, const int32_t* draft_ids,
+                                      const float* q_path, const int32_t* topk_ids, const float* q_cand,
+                                      const float* target_probs, const float* u_accept, const float* u_resample,
+                                      int32_t* n_accepted, int32_t* n_commit, int32_t* committed, int32_t* next_anchor,
+                                      void* stream) {
+  if (n_seq < 0) return fail(DFLASH_E_INVALID, "n_seq must be >= 0");
+  if (block_size < 2 || block_size > 64) return fail(DFLASH_E_INVALID, "block_size must be in [2, 64]");
+  if (vocab < 2) return fail(DFLASH_E_INVALID, "vocab must be >= 2");
+  if (n_seq == 0) return DFLASH_OK;
+  if (!draft_ids || !q_path || !topk_ids || !q_cand || !target_probs || !u_accept || !u_resample || !n_accepted ||
+      !committed || !next_anchor)
+    return fail(DFLASH_E_INVALID, "NULL input or output pointer");
+  RejectArgs ra{n_seq, block_size, vocab, draft_ids, q_path, topk_ids, q_cand, target_probs, u_accept, u_resample,
+                n_accepted, n_commit, committed, next_anchor};
+  HIP_TRY(launch_verify_rejection(ra, (hipStream_t)stream));
   return DFLASH_OK;
 }
 

@@ -141,7 +141,7 @@ struct AttnArgs {
 };
 
 struct SelectArgs {
-  int K, d, r, mode, vocab;
+  int K, d, r, mode, vocab;   // mode 0 = Viterbi, 1 = greedy, 2 = sampling walk
   int* dev_err;
   const int* anchor;
   const int* topk_ids;
@@ -153,6 +153,26 @@ struct SelectArgs {
   int* path;
   float* score;
   float* margin;
+  // sampling walk only
+  float inv_temp;
+  const float* uniforms;  // [n_seq][K-1]
+  float* q_path;          // [n_seq][K-1]
+  float* q_cand;          // [n_seq][K-1][16] or null
+};
+
+struct RejectArgs {
+  int n_seq, K, V;
+  const int* draft;        // [n_seq][K-1]
+  const float* q_path;     // [n_seq][K-1]
+  const int* cand;         // [n_seq][K-1][16]
+  const float* q_cand;     // [n_seq][K-1][16]
+  const float* p;          // [n_seq][K][V]
+  const float* u_accept;   // [n_seq][K-1]
+  const float* u_resample; // [n_seq]
+  int* n_acc;
+  int* n_commit;
+  int* committed;          // [n_seq][K]
+  int* next_anchor;
 };
 
 struct VerifyArgs {
@@ -188,6 +208,7 @@ hipError_t launch_topk_merge(const MergeArgs& a, int out_rows, hipStream_t st);
 hipError_t launch_attention(bool bf, const AttnArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_select(bool bf, const SelectArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
+hipError_t launch_verify_rejection(const RejectArgs& a, hipStream_t st);
 hipError_t launch_synth(const SynthArgs& a, hipStream_t st);
 
 }  // namespace dfl

@@ -340,6 +340,37 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
       if (a.score) a.score[b] = s1;
       if (a.margin) a.margin[b] = s1 - s2;
     }
+  } else if (a.mode == 2) {
+    // sampling walk: at slot t, q(b) = softmax_b(S_t(a, b) / T) over the 16 candidates given
+    // the previous pick a; the pick is the first b (candidate order) whose inclusive
+    // cumulative probability exceeds u_t times the total
+    int ai = 0;
+    const bool in = lane < TOPK;
+    for (int t = 1; t < K; ++t) {
+      const float z = in ? S[t - 1][lane][ai] * a.inv_temp : NEG_INF;
+      const float mx = wave_max(z);
+      const float e = in ? __expf(z - mx) : 0.f;
+      const float q = e / wave_sum(e);
+      float c = q;
+#pragma unroll
+      for (int o = 1; o < TOPK; o <<= 1) {
+        const float y = __shfl_up(c, o, WAVE);
+        if (lane >= o) c += y;
+      }
+      const float total = __shfl(c, TOPK - 1, WAVE);
+      const float u = a.uniforms[(size_t)b * (K - 1) + t - 1];
+      const unsigned long long hit = __ballot(in && u * total < c);
+      const unsigned long long pos = __ballot(in && q > 0.f);
+      const int pick = hit ? __builtin_ctzll(hit) : 63 - __builtin_clzll(pos);
+      const float qp = __shfl(q, pick, WAVE);
+      const size_t o = (size_t)b * (K - 1) + t - 1;
+      if (lane == 0) {
+        a.path[o] = cid[t - 1][pick];
+        a.q_path[o] = qp;
+      }
+      if (a.q_cand && in) a.q_cand[o * TOPK + lane] = q;
+      ai = pick;
+    }
   } else {
     // greedy: from the current candidate, the best successor (ties to the smaller index)
     int ai = 0;
@@ -388,6 +419,120 @@ __global__ void verify_kernel(VerifyArgs a) {
   a.next_anchor[b] = tg[n];
 }
 
+// Rejection-sampling verification ("Architecture", section "Speculative Decoding Context" and
+// flowchart "Verification": rejection sampling keeps the scheme lossless).  One workgroup per
+// sequence.  Draft i is accepted iff u_i * q_i(d_i) < p_i(d_i), in order; at the first
+// rejection the committed token is drawn from r(v) = max(0, p_i(v) - q_i(v)) (q_i is zero
+// outside the slot's 16 candidates, so r = p except at those), and if every draft is accepted
+// from the bonus row p_K.  The draw is an inverse CDF in token order: every thread sums a
+// contiguous chunk of the vocabulary, the chunk prefix sums locate the chunk holding
+// u * sum(r), and its thread scans it.
+__global__ __launch_bounds__(256) void verify_rejection_kernel(RejectArgs a) {
+  __shared__ float part[256], pref[256];
+  __shared__ int cs_id[TOPK];
+  __shared__ float cs_min[TOPK];
+  __shared__ int s_n, s_chunk, s_pass;
+  __shared__ float s_total;
+  const int b = blockIdx.x, tid = threadIdx.x, K = a.K, V = a.V;
+  bool acc = false;
+  if (tid < K - 1) {
+    const size_t o = (size_t)b * (K - 1) + tid;
+    const int d = a.draft[o];
+    const bool ok = d >= 0 && d < V;
+    const float pd = a.p[((size_t)b * K + tid) * V + (ok ? d : 0)];
+    acc = ok && a.u_accept[o] * a.q_path[o] < pd;
+  }
+  if (tid < 64) {
+    const unsigned long long rej = __ballot(tid < K - 1 && !acc);
+    if (tid == 0) s_n = rej ? __builtin_ctzll(rej) : K - 1;
+  }
+  if (tid == 0) s_chunk = 256;
+  __syncthreads();
+  const int n = s_n;
+  const float* pr = a.p + ((size_t)b * K + n) * V;      // slot n+1's row, or the bonus row
+  const float ur = a.u_resample[b];
+  // candidates of the rejected slot with the weight min(p, q) they lose (none for the bonus)
+  if (tid < TOPK) {
+    int id = 0x7fffffff;
+    float m = 0.f;
+    if (n < K - 1) {
+      const size_t o = ((size_t)b * (K - 1) + n) * TOPK + tid;
+      const int c = a.cand[o];
+      if (c >= 0 && c < V) {
+        id = c;
+        m = fminf(pr[c], a.q_cand[o]);
+      }
+    }
+    cs_id[tid] = id;
+    cs_min[tid] = m;
+  }
+  __syncthreads();
+  const int C = (V + 255) / 256, v0 = min(V, tid * C), v1 = min(V, v0 + C);
+  // two passes at most: if the residual has no mass (rounding), draw from p itself
+  for (int pass = 0; pass < 2; ++pass) {
+    float sum = 0.f;
+    for (int v = v0; v < v1; ++v) sum += pr[v];
+    if (pass == 0)
+#pragma unroll
+      for (int j = 0; j < TOPK; ++j)
+        if (cs_id[j] >= v0 && cs_id[j] < v1) sum -= cs_min[j];
+    part[tid] = sum;
+    __syncthreads();
+    if (tid == 0) {
+      float run = 0.f;
+      for (int t = 0; t < 256; ++t) {
+        pref[t] = run;
+        run += part[t];
+      }
+      s_total = run;
+      s_pass = pass;
+    }
+    __syncthreads();
+    if (s_total > 0.f || pass == 1) break;
+    __syncthreads();
+  }
+  const bool corrected = s_pass == 0;   // the candidates' min(p, q) was taken out
+  const float target = ur * s_total;
+  if (target < pref[tid] + part[tid] && part[tid] > 0.f) atomicMin(&s_chunk, tid);
+  __syncthreads();
+  int chunk = s_chunk;
+  if (tid == 0) {
+    if (chunk == 256) {   // rounding left no chunk: the last one with mass
+      chunk = 0;
+      for (int t = 255; t >= 0; --t)
+        if (part[t] > 0.f) { chunk = t; break; }
+    }
+    const int c0 = min(V, chunk * C), c1 = min(V, c0 + C);
+    // the chunk's candidates, ascending by id
+    int lid[TOPK];
+    float lmin[TOPK];
+    int cnt = 0;
+    if (corrected)
+      for (int j = 0; j < TOPK; ++j)
+        if (cs_id[j] >= c0 && cs_id[j] < c1) {
+          int k = cnt++;
+          while (k > 0 && lid[k - 1] > cs_id[j]) { lid[k] = lid[k - 1]; lmin[k] = lmin[k - 1]; --k; }
+          lid[k] = cs_id[j];
+          lmin[k] = cs_min[j];
+        }
+    float run = pref[chunk];
+    int tok = -1, last = c0, k = 0;
+    for (int v = c0; v < c1; ++v) {
+      float w = pr[v];
+      if (k < cnt && lid[k] == v) w -= lmin[k++];
+      if (w > 0.f) last = v;
+      run += w;
+      if (target < run && w > 0.f) { tok = v; break; }
+    }
+    if (tok < 0) tok = last;
+    const size_t o = (size_t)b * K;
+    for (int i = 0; i < K; ++i) a.committed[o + i] = i < n ? a.draft[(size_t)b * (K - 1) + i] : (i == n ? tok : -1);
+    a.n_acc[b] = n;
+    if (a.n_commit) a.n_commit[b] = n + 1;
+    a.next_anchor[b] = tok;
+  }
+}
+
 // splitmix64 (Steele, Lea and Flood's SplitMix generator; constants as published by Vigna).
 __device__ __forceinline__ unsigned long long splitmix64(unsigned long long x) {
   unsigned long long z = x + 0x9E3779B97F4A7C15ull;
@@ -423,6 +568,11 @@ hipError_t launch_select(bool bf, const SelectArgs& a, int n_seq, hipStream_t st
 }
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(verify_kernel, dim3((a.n_seq + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_verify_rejection(const RejectArgs& a, hipStream_t st) {
+  if (a.K < 2 || a.K > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(verify_rejection_kernel, dim3(a.n_seq), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_synth(const SynthArgs& a, hipStream_t st) {

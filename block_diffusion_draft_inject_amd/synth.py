@@ -272,3 +272,59 @@ def target_for_tau(draft: np.ndarray, tau: np.ndarray, alt: np.ndarray, last: np
     idx = np.arange(km1)[None, :]
     match = idx < (np.asarray(tau)[:, None] - 1)
     return stand_in_target(draft, match, alt, last, vocab)
+
+
+# ------------------------------------------------------------------------------ sampling stages
+
+def lattice(cfg: DraftConfig, n: int, tag: int = 0):
+    """A candidate lattice as the lm_head stage hands it to the selector, drawn directly.
+
+    Returns (topk_ids [n][K-1][16] int32, distinct per slot, in [0, V-2]; topk_logits
+    [n][K-1][16] float32, descending: a N(8, 2) head minus cumulative Exp(mean 0.4) gaps, the
+    shape of a peaked lm_head row's top 16; h_final [n][K][hidden] float32 ~ N(0, 1), the
+    spread of a final-normed hidden row)."""
+    K, d = cfg.block_size, cfg.hidden
+    g = rng(cfg.seed, "lattice", tag, n, K, d)
+    ids = np.empty((n, K - 1, 16), dtype=np.int32)
+    for b in range(n):
+        for t in range(K - 1):
+            ids[b, t] = g.choice(cfg.vocab - 1, size=16, replace=False)
+    head = g.normal(8.0, 2.0, size=(n, K - 1, 1))
+    gaps = g.exponential(0.4, size=(n, K - 1, 16))
+    gaps[..., 0] = 0.0
+    logits = (head - np.cumsum(gaps, axis=-1)).astype(np.float32)
+    h_final = g.standard_normal((n, K, d), dtype=np.float32)
+    return ids, logits, h_final
+
+
+def sampling_uniforms(cfg: DraftConfig, n: int, tag: int = 0):
+    """Uniform [0, 1) draws of one sampled cycle: (walk [n][K-1], accept [n][K-1], resample [n]),
+    float32."""
+    K = cfg.block_size
+    g = rng(cfg.seed, "uniforms", tag, n, K)
+    walk = g.random((n, K - 1), dtype=np.float32)
+    acc = g.random((n, K - 1), dtype=np.float32)
+    res = g.random(n, dtype=np.float32)
+    return walk, acc, res
+
+
+def target_probs(cfg: DraftConfig, cand_ids: np.ndarray, tag: int = 0, cand_mass: float = 0.7) -> np.ndarray:
+    """Stand-in target distributions for one block, [n][K][V] float32, rows summing to 1.
+
+    Row i-1 (slot i) puts about cand_mass on the drafter's 16 candidates of slot i (Gamma(1)
+    weights) and the rest on the whole vocabulary (Gamma(0.05) weights: a few tokens hold most
+    of it); the bonus row K-1 has only the vocabulary-wide part."""
+    cand_ids = np.asarray(cand_ids)
+    n, km1, _ = cand_ids.shape
+    V = cfg.vocab
+    g = rng(cfg.seed, "target_probs", tag, n, km1 + 1, V)
+    out = np.empty((n, km1 + 1, V), dtype=np.float64)
+    for b in range(n):
+        for i in range(km1 + 1):
+            bg = g.gamma(0.05, size=V)
+            bg *= (1.0 - cand_mass if i < km1 else 1.0) / bg.sum()
+            if i < km1:
+                c = g.gamma(1.0, size=16)
+                bg[cand_ids[b, i]] += cand_mass * c / c.sum()
+            out[b, i] = bg
+    return out.astype(np.float32)

@@ -202,6 +202,39 @@ DFLASH_API dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, con
                                  const float* topk_logits, const float* h_final, dflash_select_mode mode,
                                  int32_t* path_ids, float* path_score, float* margin, void* stream);
 
+/* (3s) Sampling walk over the same lattice ("Architecture", section "Problem 1 -- Independent
+ * picks are incoherent": sampling draws from the same pair scores).  At slot t the pick b is
+ * drawn from q_t(b) = softmax_b(S_t(a, b) / temperature) over the slot's 16 candidates given
+ * the previous pick a (the anchor for slot 1): the first b, in candidate order, whose
+ * cumulative probability exceeds uniforms[t-1] times the total.  uniforms [n_seq][K-1] in
+ * [0, 1) are the caller's random numbers.  Outputs: path_ids [n_seq][K-1]; q_path
+ * [n_seq][K-1] = q_t(pick); q_cand [n_seq][K-1][16] = q_t over the candidates (may be NULL;
+ * dflash_verify_rejection needs it).  Device pointers; temperature in [1e-6, 1e6] (the walk's
+ * picks are the greedy walk's as it goes to 0). */
+DFLASH_API dflash_status dflash_select_sample(dflash_handle* h, int32_t n_seq, const int32_t* anchor_ids, const int32_t* topk_ids,
+                                   const float* topk_logits, const float* h_final, float temperature,
+                                   const float* uniforms, int32_t* path_ids, float* q_path, float* q_cand,
+                                   void* stream);
+
+/* (4s) Rejection-sampling verification ("Architecture", section "Speculative Decoding Context"
+ * and flowchart "Verification": rejection sampling restores the exact target distribution).
+ * draft_ids [n_seq][K-1] with the drafter's q_path [n_seq][K-1] and its distribution at every
+ * slot, q_cand [n_seq][K-1][16] over topk_ids [n_seq][K-1][16] (zero elsewhere), as written by
+ * dflash_select_sample; target_probs [n_seq][K][vocab]: row i-1 = the target's distribution for
+ * slot i, row K-1 = the bonus distribution.  Draft i is accepted iff
+ * u_accept[i-1] * q_path[i-1] < p_i(d_i), in order, up to the first rejection.  The committed
+ * token after the accepted prefix is drawn with u_resample [n_seq] (inverse CDF in token
+ * order) from max(0, p_i - q_i) normalised at a rejection at slot i, else from the bonus row.
+ * Rows of target_probs need not be normalised; where max(0, p_i - q_i) has no positive mass the
+ * token is drawn from p_i itself.  A slot's 16 candidate ids are distinct; a draft id outside
+ * [0, vocab) counts as rejected.  Outputs as dflash_verify_greedy (n_commit may be NULL).
+ * 2 <= block_size <= 64; one workgroup per sequence. */
+DFLASH_API dflash_status dflash_verify_rejection(int32_t n_seq, int32_t block_size, int32_t vocab, const int32_t* draft_ids,
+                                      const float* q_path, const int32_t* topk_ids, const float* q_cand,
+                                      const float* target_probs, const float* u_accept, const float* u_resample,
+                                      int32_t* n_accepted, int32_t* n_commit, int32_t* committed, int32_t* next_anchor,
+                                      void* stream);
+
 /* (4) Greedy longest-prefix verification ("Architecture", section "Speculative Decoding
  * Context" and the sequence diagram's last step: accepted prefix + 1 bonus token).
  * draft_ids [n_seq][K-1] = d_1..d_{K-1}; target_argmax [n_seq][K] = g_0..g_{K-1} (g_i is the

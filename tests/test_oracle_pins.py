@@ -616,3 +616,11 @@ def test_rejection_verification_special_cases():
     # all accepted: the bonus comes from the last row
     n, com, nxt = O.verify_rejection([0, 1], [q[0][0], q[1][0]], cand, q, p, [0.0, 0.0], 0.0)
     assert n == 2 and list(com) == [0, 1, 0] and nxt == 0
+    # an unnormalised slot-1 row that q covers everywhere: max(0, p - q) has no mass, so the token is
+    # drawn from p_1 itself (mass 0.1 on token 0, 0.2 on token 4: u < 1/3 gives 0, above gives 4)
+    p_u = p.copy()
+    p_u[0] = 0.0
+    p_u[0][0], p_u[0][4] = 0.1, 0.2
+    for u_res, want in ((0.0, 0), (0.3333, 0), (0.3334, 4), (0.99, 4)):
+        n, com, nxt = O.verify_rejection([2, 1], [q[0][1], q[1][0]], cand, q, p_u, [0.5, 0.0], u_res)
+        assert n == 0 and nxt == want and list(com) == [want, -1, -1]
