@@ -386,19 +386,38 @@ def inverse_cdf(weights, u):
     return int(np.nonzero(w > 0)[0][-1])
 
 
-def sample_walk(S, uniforms, temperature):
+def nucleus(q, top_p):
+    """Top-p truncation of a distribution: rank the entries by probability (descending, ties to
+    the lower index), keep every entry whose preceding mass in that ranking is below top_p (so
+    the entry that crosses top_p stays), zero the rest and renormalise.  top_p >= 1 keeps all."""
+    q = np.asarray(q, dtype=F64)
+    if top_p >= 1.0:
+        return q / q.sum()
+    order = sorted(range(len(q)), key=lambda i: (-q[i], i))
+    keep = np.zeros(len(q), dtype=bool)
+    before = 0.0
+    for i in order:
+        if before < top_p:
+            keep[i] = True
+        before += q[i]
+    r = np.where(keep, q, 0.0)
+    return r / r.sum()
+
+
+def sample_walk(S, uniforms, temperature, top_p=1.0):
     """Sampling walk over the candidate lattice.  At slot t the candidate b is drawn from the
     conditional distribution q_t(b) = softmax_b(S_t(a, b) / T) given the previous pick a (the
-    anchor for slot 1), by inverse CDF in candidate order with the supplied uniform u_t.
+    anchor for slot 1), cut to its top-p nucleus (nucleus()), by inverse CDF in candidate order
+    with the supplied uniform u_t.
 
     Returns (idx [K-1], q_path [K-1] = q_t(picked), q_cand [K-1][16] = q_t over the slot's
-    candidates given the previous pick)."""
+    candidates given the previous pick, after the cut)."""
     idx, q_path, q_cand = [], [], []
     a = 0
     for t, St in enumerate(S):
         z = np.asarray(St[a], dtype=F64) / temperature
         q = np.exp(z - z.max())
-        q /= q.sum()
+        q = nucleus(q / q.sum(), top_p)
         b = inverse_cdf(q, float(uniforms[t]))
         idx.append(b)
         q_path.append(q[b])

@@ -554,6 +554,41 @@ def test_sample_walk_temperature_limits():
     assert np.allclose(qp, 1 / 16, rtol=1e-4)
 
 
+def test_nucleus_closed_forms():
+    """Top-p by hand: keep the most probable entries until their mass reaches top_p (the entry
+    that crosses it stays), ties ranked by index, then renormalise."""
+    q = np.array([0.1, 0.5, 0.3, 0.1])
+    assert np.allclose(O.nucleus(q, 0.75), [0, 0.625, 0.375, 0])      # 0.5 < 0.75 -> 0.3 stays
+    assert np.allclose(O.nucleus(q, 0.4), [0, 1, 0, 0])               # the top entry alone reaches 0.4
+    assert np.allclose(O.nucleus(q, 0.85), [0.1, 0.5, 0.3, 0] / np.float64(0.9))   # tie 0.1/0.1 -> index 0
+    assert np.allclose(O.nucleus(q, 1.0), q)
+    t = np.array([0.3, 0.3, 0.2, 0.2])
+    assert np.allclose(O.nucleus(t, 0.5), [0.5, 0.5, 0, 0])
+    assert np.allclose(O.nucleus(t, 0.65), [0.375, 0.375, 0.25, 0])
+    assert np.allclose(O.nucleus(t, 1e-9), [1, 0, 0, 0])
+
+
+def test_sample_walk_top_p():
+    rng = np.random.default_rng(9)
+    S = [rng.normal(size=(1, 16)) * 2] + [rng.normal(size=(16, 16)) * 2 for _ in range(3)]
+    # a vanishing nucleus keeps only the most probable successor: the greedy walk, q = 1
+    g, _, _ = O.greedy_walk(S)
+    for u in (0.0, 0.5, 0.999):
+        idx, qp, qc = O.sample_walk(S, [u] * 4, 1.0, top_p=1e-9)
+        assert list(idx) == list(g) and np.allclose(qp, 1.0)
+    # the picks never leave the nucleus, and the reported q is the cut distribution
+    U = rng.random((2000, 4))
+    for u in U[:200]:
+        idx, qp, qc = O.sample_walk(S, u, 0.8, top_p=0.6)
+        for t in range(4):
+            assert qc[t][idx[t]] > 0 and qp[t] == qc[t][idx[t]] and abs(qc[t].sum() - 1) < 1e-12
+    # first pick: empirical distribution equals the cut distribution
+    want = O.nucleus(np.exp(S[0][0] / 0.8 - np.max(S[0][0] / 0.8)) / np.exp(S[0][0] / 0.8 - np.max(S[0][0] / 0.8)).sum(),
+                     0.6)
+    counts = np.bincount([O.sample_walk(S, u, 0.8, top_p=0.6)[0][0] for u in U], minlength=16) / len(U)
+    assert np.all(np.abs(counts - want) < 5 * np.sqrt(want * (1 - want) / len(U)) + 1e-12)
+
+
 def _drafter_and_target():
     """Tiny vocabulary: slot 1 and slot 2 candidates with fixed drafter probabilities (slot 2's
     independent of the slot-1 pick here), and target distributions for slots 1, 2 and the bonus."""
