@@ -73,8 +73,8 @@ def lib():
                                          c_void_p]),
         "dflash_select_path": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                          c_void_p, c_void_p, c_void_p]),
-        "dflash_select_sample": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p,
-                                           c_void_p, c_void_p, c_void_p, c_void_p]),
+        "dflash_select_sample": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_float,
+                                           c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_verify_rejection": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                               c_void_p]),
@@ -250,12 +250,12 @@ class Drafter:
                                                              ptr(topk_ids), ptr(topk_logits), ptr(h_final), mode,
                                                              ptr(path_ids), ptr(path_score), ptr(margin), stream))
 
-    def dflash_select_sample(self, anchor_ids, topk_ids, topk_logits, h_final, temperature, uniforms, path_ids, q_path,
-                             q_cand=None, stream=None):
+    def dflash_select_sample(self, anchor_ids, topk_ids, topk_logits, h_final, temperature, top_p, uniforms, path_ids,
+                             q_path, q_cand=None, stream=None):
         check("dflash_select_sample", lib().dflash_select_sample(self.h, anchor_ids.numel(), ptr(anchor_ids),
                                                                  ptr(topk_ids), ptr(topk_logits), ptr(h_final),
-                                                                 float(temperature), ptr(uniforms), ptr(path_ids),
-                                                                 ptr(q_path), ptr(q_cand), stream))
+                                                                 float(temperature), float(top_p), ptr(uniforms),
+                                                                 ptr(path_ids), ptr(q_path), ptr(q_cand), stream))
 
     def dflash_timing_enable(self, capacity):
         check("dflash_timing_enable", lib().dflash_timing_enable(self.h, capacity))

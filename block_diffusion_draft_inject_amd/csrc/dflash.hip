@@ -684,25 +684,26 @@ dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t*
     return fail(DFLASH_E_INVALID, "NULL anchor_ids, topk_ids, topk_logits, h_final or path_ids");
   SelectArgs sa{c->block_size, c->hidden, c->sel_rank, (int)mode, c->vocab, dev_err(H), anchor_ids, topk_ids,
                 topk_logits, h_final, H->g_A, H->g_B, H->g_WH, path_ids, path_score, margin,
-                1.0f, nullptr, nullptr, nullptr};
+                1.0f, 1.0f, nullptr, nullptr, nullptr};
   HIP_TRY(launch_select(bf(c), sa, n_seq, (hipStream_t)stream));
   return DFLASH_OK;
 }
 
 dflash_status dflash_select_sample(dflash_handle* h, int32_t n_seq, const int32_t* anchor_ids, const int32_t* topk_ids,
                                    const float* topk_logits, const float* h_final, float temperature,
-                                   const float* uniforms, int32_t* path_ids, float* q_path, float* q_cand,
-                                   void* stream) {
+                                   float top_p, const float* uniforms, int32_t* path_ids, float* q_path,
+                                   float* q_cand, void* stream) {
   Handle* H = as_handle(h);
   if (!H) return fail(DFLASH_E_STATE, "not a live handle");
   const dflash_config* c = &H->cfg;
   if (n_seq < 1 || n_seq > H->max_batch) return fail(DFLASH_E_SHAPE, "n_seq %d outside [1, max_batch=%d]", n_seq, H->max_batch);
   if (!(temperature >= 1e-6f && temperature <= 1e6f)) return fail(DFLASH_E_INVALID, "temperature must be in [1e-6, 1e6]");
+  if (!(top_p > 0.f && top_p <= 1.f)) return fail(DFLASH_E_INVALID, "top_p must be in (0, 1]");
   if (!anchor_ids || !topk_ids || !topk_logits || !h_final || !uniforms || !path_ids || !q_path)
     return fail(DFLASH_E_INVALID, "NULL anchor_ids, topk_ids, topk_logits, h_final, uniforms, path_ids or q_path");
   SelectArgs sa{c->block_size, c->hidden, c->sel_rank, 2, c->vocab, dev_err(H), anchor_ids, topk_ids,
                 topk_logits, h_final, H->g_A, H->g_B, H->g_WH, path_ids, nullptr, nullptr,
-                1.0f / temperature, uniforms, q_path, q_cand};
+                1.0f / temperature, top_p, uniforms, q_path, q_cand};
   HIP_TRY(launch_select(bf(c), sa, n_seq, (hipStream_t)stream));
   return DFLASH_OK;
 }

@@ -155,6 +155,7 @@ struct SelectArgs {
   float* margin;
   // sampling walk only
   float inv_temp;
+  float top_p;            // nucleus cut, >= 1 keeps all 16
   const float* uniforms;  // [n_seq][K-1]
   float* q_path;          // [n_seq][K-1]
   float* q_cand;          // [n_seq][K-1][16] or null

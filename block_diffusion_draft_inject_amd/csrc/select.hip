@@ -342,15 +342,28 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     }
   } else if (a.mode == 2) {
     // sampling walk: at slot t, q(b) = softmax_b(S_t(a, b) / T) over the 16 candidates given
-    // the previous pick a; the pick is the first b (candidate order) whose inclusive
-    // cumulative probability exceeds u_t times the total
+    // the previous pick a, cut to its top-p nucleus; the pick is the first b (candidate order)
+    // whose inclusive cumulative probability exceeds u_t times the total
     int ai = 0;
     const bool in = lane < TOPK;
+    const bool cut = a.top_p < 1.f;
     for (int t = 1; t < K; ++t) {
       const float z = in ? S[t - 1][lane][ai] * a.inv_temp : NEG_INF;
       const float mx = wave_max(z);
       const float e = in ? __expf(z - mx) : 0.f;
-      const float q = e / wave_sum(e);
+      float q = e / wave_sum(e);
+      if (cut) {
+        // mass ranked ahead of this candidate (probability descending, ties to the lower
+        // index); the candidate stays while that mass is below top_p
+        float before = 0.f;
+#pragma unroll
+        for (int j = 0; j < TOPK; ++j) {
+          const float qj = __shfl(q, j, WAVE);
+          if (qj > q || (qj == q && j < lane)) before += qj;
+        }
+        const float kept = (in && before < a.top_p) ? q : 0.f;
+        q = kept / wave_sum(kept);
+      }
       float c = q;
 #pragma unroll
       for (int o = 1; o < TOPK; o <<= 1) {

@@ -205,16 +205,18 @@ DFLASH_API dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, con
 /* (3s) Sampling walk over the same lattice ("Architecture", section "Problem 1 -- Independent
  * picks are incoherent": sampling draws from the same pair scores).  At slot t the pick b is
  * drawn from q_t(b) = softmax_b(S_t(a, b) / temperature) over the slot's 16 candidates given
- * the previous pick a (the anchor for slot 1): the first b, in candidate order, whose
+ * the previous pick a (the anchor for slot 1), cut to its top-p nucleus when top_p < 1 (rank
+ * by probability, ties to the lower candidate index; a candidate stays while the mass ranked
+ * ahead of it is below top_p; renormalise): the first b, in candidate order, whose
  * cumulative probability exceeds uniforms[t-1] times the total.  uniforms [n_seq][K-1] in
  * [0, 1) are the caller's random numbers.  Outputs: path_ids [n_seq][K-1]; q_path
- * [n_seq][K-1] = q_t(pick); q_cand [n_seq][K-1][16] = q_t over the candidates (may be NULL;
+ * [n_seq][K-1] = q_t(pick); q_cand [n_seq][K-1][16] = q_t over the candidates after the cut (may be NULL;
  * dflash_verify_rejection needs it).  Device pointers; temperature in [1e-6, 1e6] (the walk's
- * picks are the greedy walk's as it goes to 0). */
+ * picks are the greedy walk's as it goes to 0); top_p in (0, 1]. */
 DFLASH_API dflash_status dflash_select_sample(dflash_handle* h, int32_t n_seq, const int32_t* anchor_ids, const int32_t* topk_ids,
                                    const float* topk_logits, const float* h_final, float temperature,
-                                   const float* uniforms, int32_t* path_ids, float* q_path, float* q_cand,
-                                   void* stream);
+                                   float top_p, const float* uniforms, int32_t* path_ids, float* q_path,
+                                   float* q_cand, void* stream);
 
 /* (4s) Rejection-sampling verification ("Architecture", section "Speculative Decoding Context"
  * and flowchart "Verification": rejection sampling restores the exact target distribution).

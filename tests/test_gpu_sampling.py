@@ -48,15 +48,39 @@ def stable_uniform(decide, u):
     raise AssertionError("no stable uniform")
 
 
-def guarded_walk_uniforms(S, u, temperature):
+def guarded_walk_uniforms(S, u, temperature, top_p=1.0):
     u = np.asarray(u, dtype=np.float64).copy()
     for t in range(len(S)):
         def decide(x, t=t):
             v = u.copy()
             v[t] = x
-            return int(O.sample_walk(S, v, temperature)[0][t])
+            return int(O.sample_walk(S, v, temperature, top_p)[0][t])
         u[t] = stable_uniform(decide, float(u[t]))
     return u.astype(np.float32)
+
+
+def nucleus_is_stable(S, u, temperature, top_p, eps=1e-4):
+    """The oracle's walk keeps the same picks and the same cut when top_p moves by +-eps, so no
+    candidate's preceding mass sits within fp32 rounding of top_p."""
+    idx, _, qc = O.sample_walk(S, u, temperature, top_p)
+    for tp in (top_p - eps, min(1.0, top_p + eps)):
+        i2, _, q2 = O.sample_walk(S, u, temperature, tp)
+        if not np.array_equal(idx, i2) or not np.array_equal(qc > 0, q2 > 0):
+            return False
+    return True
+
+
+def guarded_inputs(S_all, u_raw, temperature, top_p):
+    """Uniforms kept off the CDF boundaries, and a top_p within 2e-3 of the asked one that no
+    walk's cut sits near."""
+    if top_p >= 1.0:
+        return np.stack([guarded_walk_uniforms(S, u, temperature) for S, u in zip(S_all, u_raw)]), 1.0
+    for k in range(20):
+        tp = top_p + (k + 1) // 2 * 1e-4 * (1 if k % 2 else -1)
+        u = np.stack([guarded_walk_uniforms(S, v, temperature, tp) for S, v in zip(S_all, u_raw)])
+        if all(nucleus_is_stable(S, v, temperature, tp) for S, v in zip(S_all, u)):
+            return u, tp
+    raise AssertionError("no stable top_p near the asked one")
 
 
 def _lattice_case(H, cfg, n, tag):
@@ -66,37 +90,45 @@ def _lattice_case(H, cfg, n, tag):
     return case, ids, logits, hf, anchors
 
 
-def _sample_on_gpu(case, anchors, ids, logits, hf, temperature, u_walk, want_q_cand=True):
+def _sample_on_gpu(case, anchors, ids, logits, hf, temperature, u_walk, want_q_cand=True, top_p=1.0):
     torch = case.torch
     n, km1 = len(anchors), ids.shape[1]
     path = torch.full((n, km1), -7, dtype=torch.int32, device="cuda")
     qp = torch.full((n, km1), -1.0, dtype=torch.float32, device="cuda")
     qc = torch.full((n, km1, 16), -1.0, dtype=torch.float32, device="cuda") if want_q_cand else None
     case.d.dflash_select_sample(case.tensor(anchors), case.tensor(ids), case.tensor(logits), case.tensor(hf),
-                                temperature, case.tensor(u_walk), path, qp, qc)
+                                temperature, top_p, case.tensor(u_walk), path, qp, qc)
     torch.cuda.synchronize()
     return path.cpu().numpy(), qp.cpu().numpy(), (None if qc is None else qc.cpu().numpy())
 
 
-@pytest.mark.parametrize("cfg,temperature", [(MID, 1.0), (MID, 0.6), (synth.WORKLOADS["tiny_fp32"], 1.7)],
-                         ids=["mid_bf16_T1", "mid_bf16_T0.6", "tiny_fp32_T1.7"])
-def test_sampling_walk_matches_oracle(H, cfg, temperature):
+@pytest.mark.parametrize("cfg,temperature,top_p",
+                         [(MID, 1.0, 1.0), (MID, 0.6, 1.0), (synth.WORKLOADS["tiny_fp32"], 1.7, 1.0),
+                          (MID, 1.0, 0.95), (MID, 0.7, 0.5), (synth.WORKLOADS["tiny_fp32"], 2.5, 0.8)],
+                         ids=["mid_bf16_T1", "mid_bf16_T0.6", "tiny_fp32_T1.7", "mid_bf16_T1_p0.95",
+                              "mid_bf16_T0.7_p0.5", "tiny_fp32_T2.5_p0.8"])
+def test_sampling_walk_matches_oracle(H, cfg, temperature, top_p):
     n = 8
     case, ids, logits, hf, anchors = _lattice_case(H, cfg, n, tag=1)
     u_raw, _, _ = synth.sampling_uniforms(cfg, n, tag=1)
     S_all = [O.pair_scores(cfg, case.W64, int(anchors[b]), ids[b], logits[b], hf[b]) for b in range(n)]
-    u = np.stack([guarded_walk_uniforms(S_all[b], u_raw[b], temperature) for b in range(n)])
-    path, qp, qc = _sample_on_gpu(case, anchors, ids, logits, hf, temperature, u)
-    _, _, qc_none = _sample_on_gpu(case, anchors, ids, logits, hf, temperature, u, want_q_cand=False)
+    u, top_p = guarded_inputs(S_all, u_raw, temperature, top_p)
+    path, qp, qc = _sample_on_gpu(case, anchors, ids, logits, hf, temperature, u, top_p=top_p)
+    _, _, qc_none = _sample_on_gpu(case, anchors, ids, logits, hf, temperature, u, want_q_cand=False, top_p=top_p)
     assert qc_none is None
+    n_cut = 0
     for b in range(n):
-        idx, q_path, q_cand = O.sample_walk(S_all[b], u[b], temperature)
+        idx, q_path, q_cand = O.sample_walk(S_all[b], u[b], temperature, top_p)
+        n_cut += int(np.sum(q_cand == 0))
         want = ids[b][np.arange(cfg.block_size - 1), idx]
         assert np.array_equal(path[b], want), (b, path[b], want)
         np.testing.assert_allclose(qp[b], q_path, atol=Q_TOL, rtol=0)
         np.testing.assert_allclose(qc[b], q_cand, atol=Q_TOL, rtol=0)
-    H.log(f"[sample] {cfg.name} T={temperature}: {n} walks equal, "
-          f"max |q err| {np.max(np.abs(qc - np.stack([O.sample_walk(S_all[b], u[b], temperature)[2] for b in range(n)]))):.2e}")
+    if top_p < 1.0:
+        assert n_cut > 0            # the cut removed candidates somewhere
+    want_qc = np.stack([O.sample_walk(S_all[b], u[b], temperature, top_p)[2] for b in range(n)])
+    H.log(f"[sample] {cfg.name} T={temperature} top_p={top_p}: {n} walks equal, {n_cut} candidates cut, "
+          f"max |q err| {np.max(np.abs(qc - want_qc)):.2e}")
 
 
 def test_sampling_walk_cold_temperature_is_greedy(H):
@@ -114,7 +146,7 @@ def test_sampling_walk_cold_temperature_is_greedy(H):
             assert np.all(qp[b] > 0.99)
 
 
-def test_select_sample_rejects_bad_temperature(H):
+def test_select_sample_rejects_bad_temperature_and_top_p(H):
     import torch
     cfg, n = MID, 1
     case, ids, logits, hf, anchors = _lattice_case(H, cfg, n, tag=3)
@@ -122,6 +154,9 @@ def test_select_sample_rejects_bad_temperature(H):
     for T in (0.0, -1.0, float("inf"), float("nan")):
         with pytest.raises(B.DflashError):
             _sample_on_gpu(case, anchors, ids, logits, hf, T, u)
+    for p in (0.0, -0.5, 1.5, float("nan")):
+        with pytest.raises(B.DflashError):
+            _sample_on_gpu(case, anchors, ids, logits, hf, 1.0, u, top_p=p)
 
 
 # ------------------------------------------------------------------------------ rejection verification
