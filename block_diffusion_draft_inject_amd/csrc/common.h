@@ -159,6 +159,23 @@ struct Top16 {
       id[i] = up ? iu : (b[i] ? idx : id[i]);
     }
   }
+  // The same for a list fed by a column stream in ascending order: idx is larger than every
+  // id in the list, so on equal values the candidate ranks last and "beats" is a plain value
+  // comparison (one compare per entry instead of three).
+  __device__ __forceinline__ void push_asc(float val, int idx) {
+    if (!(val > v[TOPK - 1])) return;
+    bool b[TOPK];
+#pragma unroll
+    for (int i = 0; i < TOPK; ++i) b[i] = val > v[i];
+#pragma unroll
+    for (int i = TOPK - 1; i >= 0; --i) {
+      const bool up = i > 0 && b[i > 0 ? i - 1 : 0];
+      const float vu = v[i > 0 ? i - 1 : 0];
+      const int iu = id[i > 0 ? i - 1 : 0];
+      v[i] = up ? vu : (b[i] ? val : v[i]);
+      id[i] = up ? iu : (b[i] ? idx : id[i]);
+    }
+  }
 };
 
 }  // namespace dfl

@@ -467,10 +467,12 @@ __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
 
 // ---------------------------------------------------------------------------------------
 // lm_head + top-16, at most 16 rows, K <= 2048 (K a multiple of 512): independent waves.
-// The workgroup copies the activation rows (hi and lo planes) into LDS once; then every wave
-// streams whole 16-column fragments (wave w of the grid takes fragments w, w + waves, ...) over
-// all of K in batches of 4 chunks of 64, three batches in rotation, the prefetch running on
-// into the next fragment.  No workgroup barrier in the main loop: a wave waits only for its own
+// The lm_head input is bf16 (the final norm writes bf16(h_f) and a zero lo plane), so only
+// the hi plane is read.  The workgroup copies the activation rows into LDS once (64 KiB); then
+// every wave streams whole 16-column fragments (wave w of the grid takes fragments w,
+// w + waves, ...) over all of K in batches of LW_CH chunks of 64, LW_NB batches in rotation,
+// the prefetch running on into the next fragment.  (Two workgroups per CU, with smaller
+// batches to fit 128 VGPRs, measured 8-10% slower than one with deep batches.)  No workgroup barrier in the main loop: a wave waits only for its own
 // loads.  (Handing fragments out through one device-wide counter was far slower: the ~13k
 // increments of one address serialise.)  Each wave keeps, per row, 4 lane lists of the
 // running top-16 (one per column quarter); at the end a row's 32 lists are merged by one
@@ -480,43 +482,45 @@ constexpr int LW_W = 8;             // waves per workgroup
 constexpr int LW_KMAX = 2048;
 constexpr int LW_LD = LW_KMAX + 8;  // LDS row stride (bf16): rows fall in distinct bank groups
 
-constexpr size_t LW_SMEM = (size_t)2 * 16 * LW_LD * 2 + (size_t)LW_W * 16 * 17 * 4;   // 137 KiB
+constexpr int LW_GROUPS = 256;      // workgroups: one per CU (two per CU measured slower)
+constexpr size_t LW_SMEM = (size_t)16 * LW_LD * 2 + (size_t)LW_W * 16 * 17 * 4;   // 73 KiB
+static_assert(2 * 16 * 32 * (TOPK + 1) * 4 <= LW_SMEM, "the merge lists overlay the activation rows");
 
+constexpr int LW_CH = 4;            // chunks of 64 k per batch
+constexpr int LW_NB = 3;            // batches in rotation (LW_NB - 1 in flight)
 struct LwBatch {
-  u32x4 b[4][2];                    // 4 chunks x (k halves 0..31 / 32..63 of the chunk)
+  u32x4 b[LW_CH][2];                // LW_CH chunks x (k halves 0..31 / 32..63 of the chunk)
 };
 
 __device__ __forceinline__ void lw_load(LwBatch& x, const bf16* row, int k0, int kg) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < LW_CH; ++c) {
     const bf16* q = row + k0 + c * 64 + kg * 8;
     x.b[c][0] = *reinterpret_cast<const u32x4*>(q);
     x.b[c][1] = *reinterpret_cast<const u32x4*>(q + 32);
   }
 }
 
-// hi and lo activation planes accumulate separately: two independent MFMA chains
-__device__ __forceinline__ void lw_mma(const LwBatch& x, const bf16 (*sa)[16][LW_LD], int k0, int li, int kg,
-                                       f32x4& acc_h, f32x4& acc_l) {
+// the two k halves of each chunk accumulate separately: two independent MFMA chains
+__device__ __forceinline__ void lw_mma(const LwBatch& x, const bf16 (*sa)[LW_LD], int k0, int li, int kg,
+                                       f32x4& acc0, f32x4& acc1) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = k0 + c * 64 + h * 32 + kg * 8;
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sa[0][li][k]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&sa[1][li][k]);
-      acc_h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(x.b[c][h]), acc_h, 0, 0, 0);
-      acc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, as_bf16x8(x.b[c][h]), acc_l, 0, 0, 0);
-    }
+  for (int c = 0; c < LW_CH; ++c) {
+    const int k = k0 + c * 64 + kg * 8;
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sa[li][k]);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sa[li][k + 32]);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(x.b[c][0]), acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(x.b[c][1]), acc1, 0, 0, 0);
+  }
 }
 
 // LOGITS: the full logits are written too (a global store in the fragment loop; kept out of
 // the instantiation without them, where it would make the compiler's load waits coarser)
 template <bool LOGITS>
-__global__ __launch_bounds__(LW_W * 64) void lmhead_topk_wave(GemmParams p) {
+__global__ __launch_bounds__(LW_W * 64, 2) void lmhead_topk_wave(GemmParams p) {
   __shared__ __align__(16) unsigned char lw_smem[LW_SMEM];
-  bf16 (*sa)[16][LW_LD] = reinterpret_cast<bf16 (*)[16][LW_LD]>(lw_smem);                 // [plane][row][k]
-  float (*fb)[16][17] = reinterpret_cast<float (*)[16][17]>(lw_smem + 2 * 16 * LW_LD * 2);   // [wave][row][col]
+  bf16 (*sa)[LW_LD] = reinterpret_cast<bf16 (*)[LW_LD]>(lw_smem);                         // [row][k]
+  float (*fb)[16][17] = reinterpret_cast<float (*)[16][17]>(lw_smem + 16 * LW_LD * 2);    // [wave][row][col]
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, kg = lane >> 4;
   const int Mv = rows_valid(p);
@@ -524,29 +528,29 @@ __global__ __launch_bounds__(LW_W * 64) void lmhead_topk_wave(GemmParams p) {
   if (Mv <= 0) return;   // uniform
   // activation rows -> LDS (rows >= Mv zero), 16-byte pieces, all loads issued in one burst at
   // always-valid addresses and masked afterwards
-  // thread t copies the 16-byte piece t % 256 of plane-rows t / 256, t / 256 + 2, ... (32 plane-rows)
+  // thread t copies the 16-byte piece t % 256 of rows t / 256, t / 256 + 2, ... (16 rows)
   {
     static_assert(LW_KMAX / 8 == 256 && LW_W * 64 == 512, "piece mapping assumes 256 pieces a row, 512 threads");
     const int v = tid & 255, q0 = tid >> 8;
     const bool vok = v < K / 8;
     const int vc = min(v, K / 8 - 1);
-    u32x4 x[16];
+    u32x4 x[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int q = q0 + 2 * i, pl = q >> 4, r = q & 15;
-      x[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(p.A) + (pl ? p.a_plane : 0) +
-                                             (size_t)min(r, Mv - 1) * p.lda + vc * 8);
+    for (int i = 0; i < 8; ++i) {
+      const int r = q0 + 2 * i;
+      x[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(p.A) + (size_t)min(r, Mv - 1) * p.lda +
+                                             vc * 8);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int q = q0 + 2 * i, pl = q >> 4, r = q & 15;
+    for (int i = 0; i < 8; ++i) {
+      const int r = q0 + 2 * i;
       const u32x4 z = {0u, 0u, 0u, 0u};
-      if (vok) *reinterpret_cast<u32x4*>(&sa[pl][r][v * 8]) = r < Mv ? x[i] : z;
+      if (vok) *reinterpret_cast<u32x4*>(&sa[r][v * 8]) = r < Mv ? x[i] : z;
     }
   }
   __syncthreads();
   const int nfrag = (p.N + 15) / 16;
-  const int ncb = K / 256;                        // batches of 4 chunks per fragment (even)
+  const int ncb = K / (64 * LW_CH);               // batches per fragment
   const int TW = gridDim.x * LW_W;
   const int my_row = lane >> 2, my_sub = lane & 3;   // epilogue: lane handles row my_row, cols 4 sub..+3
   const bool row_live = my_row < Mv && (my_row % p.block) != 0;
@@ -571,51 +575,50 @@ __global__ __launch_bounds__(LW_W * 64) void lmhead_topk_wave(GemmParams p) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int col = f * 16 + my_sub * 4 + c;
-        if (col < p.N) top.push(fb[wave][my_row][my_sub * 4 + c], col);
+        if (col < p.N) top.push_asc(fb[wave][my_row][my_sub * 4 + c], col);   // a lane's columns ascend
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  // this wave's batches, fragment by fragment; the load cursor runs two batches ahead of the
+  // this wave's batches, fragment by fragment; the load cursor runs LW_NB - 1 batches ahead of the
   // compute cursor, over fragment boundaries (loads past the end read clamped, valid rows)
   const int f0 = blockIdx.x * LW_W + wave;
   // rounded up to whole rotations: a padded batch belongs to a fragment this wave never
   // finishes (or to one past the end, whose columns the epilogue skips), so it changes nothing
-  const int T = ((f0 < nfrag ? (nfrag - 1 - f0) / TW + 1 : 0) * ncb + 2) / 3 * 3;
+  const int T = ((f0 < nfrag ? (nfrag - 1 - f0) / TW + 1 : 0) * ncb + LW_NB - 1) / LW_NB * LW_NB;
   int lf = f0, lcb = 0;
   auto issue = [&](LwBatch& b) {
-    lw_load(b, rowp(lf), lcb * 256, kg);
+    lw_load(b, rowp(lf), lcb * 64 * LW_CH, kg);
     if (++lcb == ncb) { lcb = 0; lf += TW; }
   };
   int cf = f0, ccb = 0;
-  f32x4 acc_h = {0.f, 0.f, 0.f, 0.f}, acc_l = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   auto step = [&](const LwBatch& b) {
-    lw_mma(b, sa, ccb * 256, li, kg, acc_h, acc_l);
+    lw_mma(b, sa, ccb * 64 * LW_CH, li, kg, acc0, acc1);
     if (++ccb == ncb) {
-      epilogue(cf, acc_h + acc_l);
-      acc_h = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc_l = f32x4{0.f, 0.f, 0.f, 0.f};
+      epilogue(cf, acc0 + acc1);
+      acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
       ccb = 0;
       cf += TW;
     }
   };
-  LwBatch b0, b1, b2;
-  issue(b0);
-  __builtin_amdgcn_sched_barrier(0);   // b0's loads strictly before b1's: the in-order wait counts rely on it
-  issue(b1);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int t = 0; t < T; t += 3) {
-    issue(b2);
+  // batch i's loads strictly before batch i+1's: the compiler's in-order wait counts rely on it
+  LwBatch b[LW_NB];
+#pragma unroll
+  for (int i = 0; i + 1 < LW_NB; ++i) {
+    issue(b[i]);
     __builtin_amdgcn_sched_barrier(0);
-    step(b0);
-    issue(b0);
-    __builtin_amdgcn_sched_barrier(0);
-    step(b1);
-    issue(b1);
-    __builtin_amdgcn_sched_barrier(0);
-    step(b2);
+  }
+  for (int t = 0; t < T; t += LW_NB) {
+#pragma unroll
+    for (int i = 0; i < LW_NB; ++i) {
+      issue(b[(i + LW_NB - 1) % LW_NB]);
+      __builtin_amdgcn_sched_barrier(0);
+      step(b[i]);
+    }
   }
   // merge: a row's 32 lane lists (4 lanes x 8 waves) go through LDS to one half-wave (wave w
   // takes rows 2w and 2w + 1), which extracts the row's best 16 in 16 rounds of a 32-lane
@@ -730,7 +733,7 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
       while (pl.slc < 4 && SW * 64 * pl.slc < K) pl.slc *= 2;
       if (mode == GEMM_TOPK && K >= 512 && K % 512 == 0 && K <= LW_KMAX) {
         pl.kind = 4;
-        pl.groups = 256;
+        pl.groups = LW_GROUPS;
         pl.grid = dim3(pl.groups, 1, 1);
         return pl;
       }

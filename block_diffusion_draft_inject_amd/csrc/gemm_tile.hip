@@ -1,4 +1,5 @@
-// Tiled MFMA GEMM for many rows (more than 64): C = A_hi W^T + A_lo W^T over bf16 operands.
+// Tiled MFMA GEMM for many rows (more than 64): C = A_hi W^T + A_lo W^T over bf16 operands
+// (PL = 2 activation planes), or C = A_hi W^T (PL = 1: the lm_head, whose input is bf16).
 //
 // A workgroup of WGM x WGN waves computes a BM x BN output tile (each wave BM/WGM x BN/WGN)
 // over k-steps of 32.  Operands travel global -> LDS by the LDS-DMA form of the global load
@@ -23,13 +24,15 @@ constexpr int MK = 32;   // k per step
 // chunk order inside a row of a 16-row block: logical chunk c of row r sits in slot c ^ swz(r)
 __device__ __forceinline__ int tile_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-template <int BM, int BN, int WGM, int WGN, int S>
+template <int BM, int BN, int WGM, int WGN, int S, int PL = 2>
 struct TileCfg {
   static constexpr int NW = WGM * WGN, NT = NW * 64; // waves, threads
   static constexpr int WM = BM / WGM, WN = BN / WGN; // wave tile
   static constexpr int FM = WM / 16, FN = WN / 16;   // MFMA fragments per wave
-  static constexpr int BA = BM / 16, BB = BN / 16;   // 1 KiB blocks per stage: A hi, A lo (BA each), B (BB)
-  static constexpr int NBLK = 2 * BA + BB;
+  static constexpr int BA = BM / 16, BB = BN / 16;   // 1 KiB blocks per stage: A hi (, A lo) (BA each), B (BB)
+  static constexpr int PLc = PL;
+  static_assert(PL == 1 || PL == 2, "activation planes");
+  static constexpr int NBLK = PL * BA + BB;
   static constexpr int STAGE = NBLK * 1024;
   static constexpr int D = NBLK / NW;                // LDS-DMA instructions per wave per stage
   static constexpr int LDS = S * STAGE;
@@ -82,12 +85,12 @@ __device__ __forceinline__ void tile_src(const GemmParams& p, int m0, int n0, in
       const int r = min(m0 + b * 16 + r16, Mv - 1);
       s.base[q] = ahi;
       s.voff[q] = (unsigned)(((size_t)r * p.lda + kc * 8) * 2);
-    } else if (T::NW * q < 2 * T::BA) {            // A lo
+    } else if (T::NW * q < T::PLc * T::BA) {       // A lo
       const int r = min(m0 + (b - T::BA) * 16 + r16, Mv - 1);
       s.base[q] = alo;
       s.voff[q] = (unsigned)(((size_t)r * p.lda + kc * 8) * 2);
     } else {                                       // weight rows
-      const int n = min(n0 + (b - 2 * T::BA) * 16 + r16, p.N - 1);
+      const int n = min(n0 + (b - T::PLc * T::BA) * 16 + r16, p.N - 1);
       s.addr[q] = reinterpret_cast<const char*>(brow_ptr(p, n) + kc * 8);
     }
   }
@@ -98,7 +101,7 @@ __device__ __forceinline__ void tile_issue(const TileSrc<T>& s, unsigned lds_sta
 #pragma unroll
   for (int q = 0; q < T::D; ++q) {
     const unsigned lds = lds_stage + (T::NW * q + wave) * 1024;
-    if (T::NW * q < 2 * T::BA) dma16(lds, s.voff[q], s.base[q] + (size_t)c * MK * 2);
+    if (T::NW * q < T::PLc * T::BA) dma16(lds, s.voff[q], s.base[q] + (size_t)c * MK * 2);
     else dma16v(lds, s.addr[q] + (size_t)c * MK * 2);
   }
 }
@@ -109,15 +112,18 @@ __device__ __forceinline__ void tile_mma(const unsigned char* stage, int wm, int
   bf16x8 b[T::FN];
 #pragma unroll
   for (int j = 0; j < T::FN; ++j)
-    b[j] = *reinterpret_cast<const bf16x8*>(stage + (2 * T::BA + wn * T::FN + j) * 1024 + lo);
+    b[j] = *reinterpret_cast<const bf16x8*>(stage + (T::PLc * T::BA + wn * T::FN + j) * 1024 + lo);
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
     const bf16x8 ah = *reinterpret_cast<const bf16x8*>(stage + (wm * T::FM + i) * 1024 + lo);
-    const bf16x8 al = *reinterpret_cast<const bf16x8*>(stage + (T::BA + wm * T::FM + i) * 1024 + lo);
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b[j], acc[i][j], 0, 0, 0);
+    if constexpr (T::PLc == 2) {
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(stage + (T::BA + wm * T::FM + i) * 1024 + lo);
 #pragma unroll
-    for (int j = 0; j < T::FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < T::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b[j], acc[i][j], 0, 0, 0);
+    }
   }
 }
 
@@ -160,6 +166,53 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, unsigned char* sme
     tile_mma<T>(smem + st * T::STAGE, wm, wn, lo, acc);
     st = (st + 1 == S) ? 0 : st + 1;
     sl = (sl + 1 == S) ? 0 : sl + 1;
+  }
+}
+
+// The same over all k-steps [0, nk), nk even, with four stages used as two pairs: the loads of
+// k-steps 2j+2 and 2j+3 go out together (each operand row's two adjacent 64-byte segments back
+// to back) while steps 2j and 2j+1 are multiplied, so a workgroup meets at one barrier per two
+// k-steps.  (Measured on the 256 x 256 bf16-input tile: 2540 cycles per k-step against 3050
+// for the four-stage rotation, whose load rate is the same.)
+template <class T>
+__device__ __forceinline__ void tile_issue_pair(const TileSrc<T>& s, unsigned st_a, unsigned st_b, int wave, int c) {
+#pragma unroll
+  for (int q = 0; q < T::D; ++q) {
+    const unsigned la = st_a + (T::NW * q + wave) * 1024, lb = st_b + (T::NW * q + wave) * 1024;
+    if (T::NW * q < T::PLc * T::BA) {
+      dma16(la, s.voff[q], s.base[q] + (size_t)c * MK * 2);
+      dma16(lb, s.voff[q], s.base[q] + (size_t)(c + 1) * MK * 2);
+    } else {
+      dma16v(la, s.addr[q] + (size_t)c * MK * 2);
+      dma16v(lb, s.addr[q] + (size_t)(c + 1) * MK * 2);
+    }
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void tile_run_pairs(const GemmParams& p, unsigned char* smem, int m0, int n0, int Mv,
+                                               int nk, f32x4 (&acc)[T::FM][T::FN]) {
+  static_assert(T::Sc == 4, "two pairs of stages");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / T::WGNc, wn = wave % T::WGNc, li = lane & 15, kg = lane >> 4;
+  TileSrc<T> src;
+  tile_src<T>(p, m0, n0, Mv, wave, lane, src);
+  const unsigned lo = li * 64 + ((kg ^ tile_swz(li)) << 4);
+  const unsigned sbase = lds_addr(smem);
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int np = nk / 2;
+  tile_issue_pair<T>(src, sbase, sbase + T::STAGE, wave, 0);
+  for (int j = 0; j < np; ++j) {
+    // pair j has landed for every wave, and every wave is done with pair j - 1's stages
+    wait_barrier<0>();
+    const int cur = (j & 1) * 2, nxt = 2 - cur;
+    if (j + 1 < np) tile_issue_pair<T>(src, sbase + nxt * T::STAGE, sbase + (nxt + 1) * T::STAGE, wave, 2 * j + 2);
+    tile_mma<T>(smem + cur * T::STAGE, wm, wn, lo, acc);
+    tile_mma<T>(smem + (cur + 1) * T::STAGE, wm, wn, lo, acc);
   }
 }
 
@@ -218,7 +271,12 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int n0 = t * BN;
     f32x4 acc[T::FM][T::FN];
-    tile_run<T>(p, smem, m0, n0, Mv, 0, nk, acc);
+    if constexpr (T::Sc == 4) {
+      if (nk % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, nk, acc);
+      else tile_run<T>(p, smem, m0, n0, Mv, 0, nk, acc);
+    } else {
+      tile_run<T>(p, smem, m0, n0, Mv, 0, nk, acc);
+    }
     wait_barrier<0>();   // every wave is done reading the stages; the epilogue buffer overlays them
 #pragma unroll
     for (int q = 0; q < BN / 64; ++q) {
@@ -239,14 +297,11 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
         for (int c = 0; c < CPT; ++c) store_logit(p, my_row, n0 + q * 64 + cb + c, ep[lrow][cb + c]);
       }
       // threshold: the better of the 16th entries of the row's lists (a value below another
-      // list's 16th entry has 16 better values in that list and cannot reach the row's top 16)
+      // list's 16th entry has 16 better values in that list and cannot reach the row's top 16).
+      // Every id in either list comes from an earlier pass, so it is smaller than the columns
+      // of this pass: a column beats an entry exactly when its value is larger.
       float tv = top.v[TOPK - 1];
-      int ti = top.id[TOPK - 1];
-      if (TPR == 2) {   // the partner thread of the row is lane ^ 1
-        const float pv = dpp_f<0xB1>(tv);
-        const int pi = dpp_i<0xB1>(ti);
-        if (cand_better(pv, pi, tv, ti)) { tv = pv; ti = pi; }
-      }
+      if (TPR == 2) tv = fmaxf(tv, dpp_f<0xB1>(tv));   // the partner thread of the row is lane ^ 1
       if (row_live) {
         // which of the thread's columns beat the threshold; then one push per such column, so
         // a wave runs as many pushes as its busiest lane needs (not one per column that any
@@ -259,13 +314,13 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int col = cg + c4 * 4 + e;
-            mask |= (unsigned)(col < p.N && cand_better(v[e], col, tv, ti)) << (c4 * 4 + e);
+            mask |= (unsigned)(col < p.N && v[e] > tv) << (c4 * 4 + e);
           }
         }
         while (mask) {
           const int c = __builtin_ctz(mask);
           mask &= mask - 1;
-          top.push(ep[lrow][cb + c], cg + c);
+          top.push_asc(ep[lrow][cb + c], cg + c);   // a thread's columns ascend
         }
       }
       wait_barrier<0>();
@@ -294,20 +349,24 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
 
 // Tile configurations: 0 = 128 x 128 (2 x 2 waves, 3 stages, two workgroups per CU),
 // 1 = 256 x 256 (4 x 2 waves of 64 x 128, two waves per SIMD, 3 stages, one workgroup per CU).
+// The lm_head variants read the hi plane only; with half the bytes per stage the big tile
+// keeps four stages in flight.
 using TileSmall = TileCfg<128, 128, 2, 2, 3>;
 using TileBig = TileCfg<256, 256, 4, 2, 3>;
+using TileSmallHi = TileCfg<128, 128, 2, 2, 3, 1>;
+using TileBigHi = TileCfg<256, 256, 4, 2, 4, 1>;
 
 hipError_t tile_launch(const GemmPlan& pl, int mode, const GemmParams& p, hipStream_t st) {
   if (p.K % MK) return hipErrorInvalidValue;
   if (mode == GEMM_TOPK) {
     if (pl.mt) {
-      const dim3 blk(TileBig::NT);
-      if (p.logits) hipLaunchKernelGGL((lmhead_topk_tile<TileBig, 1, true>), pl.grid, blk, 0, st, p);
-      else hipLaunchKernelGGL((lmhead_topk_tile<TileBig, 1, false>), pl.grid, blk, 0, st, p);
+      const dim3 blk(TileBigHi::NT);
+      if (p.logits) hipLaunchKernelGGL((lmhead_topk_tile<TileBigHi, 1, true>), pl.grid, blk, 0, st, p);
+      else hipLaunchKernelGGL((lmhead_topk_tile<TileBigHi, 1, false>), pl.grid, blk, 0, st, p);
     } else {
-      const dim3 blk(TileSmall::NT);
-      if (p.logits) hipLaunchKernelGGL((lmhead_topk_tile<TileSmall, 2, true>), pl.grid, blk, 0, st, p);
-      else hipLaunchKernelGGL((lmhead_topk_tile<TileSmall, 2, false>), pl.grid, blk, 0, st, p);
+      const dim3 blk(TileSmallHi::NT);
+      if (p.logits) hipLaunchKernelGGL((lmhead_topk_tile<TileSmallHi, 2, true>), pl.grid, blk, 0, st, p);
+      else hipLaunchKernelGGL((lmhead_topk_tile<TileSmallHi, 2, false>), pl.grid, blk, 0, st, p);
     }
   } else if (mode == GEMM_PARTIAL) {
     if (pl.mt) hipLaunchKernelGGL((gemm_tile_partial<TileBig, 1>), pl.grid, dim3(TileBig::NT), 0, st, p);

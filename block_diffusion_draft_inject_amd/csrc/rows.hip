@@ -93,6 +93,20 @@ __device__ __forceinline__ f32x4 ld4w(const void* p, size_t i) {
                  __uint_as_float(u.y & 0xffff0000u)};
   }
 }
+// Four activations at i, rounded to bf16 for a bf16 GEMM input: the hi plane holds bf16(v),
+// the lo plane zeros (fp32 drafters: v itself).
+template <typename T>
+__device__ __forceinline__ void st4_bf16_input(void* p, size_t i, size_t plane, f32x4 v) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p) + i) = v;
+  } else {
+    uint2 uh;
+    uh.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    uh.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16*>(p) + i) = uh;
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16*>(p) + i + plane) = uint2{0u, 0u};
+  }
+}
 // Four activations at i (16-byte aligned): fp32, or the hi and lo bf16 planes.
 template <typename T>
 __device__ __forceinline__ void st4_act(void* p, size_t i, size_t plane, f32x4 v) {
@@ -240,7 +254,7 @@ __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
       if (k < d) {
         const f32x4 o = hv[1][i] * r1 * g[i];
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.y) + (size_t)row * a.ldy + k) = o;
-        st4_act<T>(a.y2, (size_t)row * a.ldy + k, a.y_plane, o);
+        st4_bf16_input<T>(a.y2, (size_t)row * a.ldy + k, a.y_plane, o);   // the lm_head takes bf16(h_f)
       }
     }
     return;

@@ -45,9 +45,11 @@ Rounding points ("mode"):
   "exact"  -- everything float64.
   "bf16"   -- the drafter stores its KV cache in bf16: the context K/V written by
               injection and the block's own k/v (after per-head norm and RoPE) are rounded
-              to bf16 (nearest, ties to even).  Weights and target states are bf16 inputs;
-              every other value (activations, accumulations, softmax, logits, selector)
-              stays float64.
+              to bf16 (nearest, ties to even).  The shared lm_head is a bf16 product: its
+              input, the final-normed hidden h_f of slots 1..K-1, is rounded to bf16 too
+              (the returned h_final, which the selector reads, is not).  Weights and target
+              states are bf16 inputs; every other value (activations, accumulations,
+              softmax, logits, selector) stays float64.
 """
 from __future__ import annotations
 
@@ -240,7 +242,7 @@ def draft_block(cfg, W, cache: DraftCache, anchor, mode="bf16", block_ids=None, 
         m = s @ as64(lw["w_down"]).T
         h = h + two_tap_conv(m, lw["conv_mlp_post_w"], lw["conv_mlp_post_b"], cfg.use_conv)
     h_final = rms_norm(h, W["final_norm"], cfg.rms_eps)
-    logits = h_final[1:] @ as64(W["lm_head"]).T                 # [K-1][V]
+    logits = R(h_final[1:]) @ as64(W["lm_head"]).T              # [K-1][V]; bf16 input in mode "bf16"
     tk = cfg.topk
     ids_out = np.stack([topk_desc(row, tk) for row in logits]).astype(np.int64)
     vals_out = np.take_along_axis(logits, ids_out, axis=1)
