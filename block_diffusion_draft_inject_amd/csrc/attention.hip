@@ -69,41 +69,70 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
 #pragma unroll
   for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   const size_t cache_base = (((size_t)a.layer * a.max_seqs + ctx.sid) * a.nkv + kvh) * (size_t)a.window;
-  for (int j0 = k_begin; j0 < k_end; j0 += MK) {
+  // This thread's sixteen-byte pieces of the sub-tile at j0 (keys past the chunk read the
+  // chunk's last key, then count as zero; straight-line loads, so the compiler's wait for them
+  // sits at their first use, not at a branch join):
+  //   K: piece e = tid + 256 it is part e % 16 of key e / 16 (16 lanes read one 256-byte row);
+  //   V: piece pair u = tid + 256 it (it < 2) is part u / 32 of keys 2 (u % 32) and 2 (u % 32) + 1,
+  //      so that the transposed store writes (key, key + 1) pairs as 32-bit words, a wave's 64
+  //      lanes on 64 distinct banks.
+  auto key_off = [&](int gk, int part, bool& ctxk) {
+    ctxk = gk < ctx.n_ctx;
+    return ctxk ? (cache_base + (ctx.slot0 + gk) % a.window) * MDH + part * 8
+                : ((size_t)(b * K + gk - ctx.n_ctx) * a.nkv + kvh) * MDH + part * 8;
+  };
+  auto load_kv = [&](int j0, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
     const int nk = min(MK, k_end - j0);
-    __syncthreads();
-    // K rows -> sk[key][dim]; V rows -> svt[dim][key] (transposed for the P V operand)
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int it = 0; it < (MK * MDH / 8) / 256; ++it) {
+    for (int it = 0; it < 4; ++it) {
       const int e = tid + it * 256;
       const int key = e >> 4, part = e & 15;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key < nk) {
-        const int gk = j0 + key;
-        size_t off;
-        const bf16 *ks, *vs;
-        if (gk < ctx.n_ctx) {
-          const int slot = (ctx.slot0 + gk) % a.window;
-          off = (cache_base + slot) * MDH + part * 8;
-          ks = kc;
-          vs = vc;
-        } else {
-          const int t = gk - ctx.n_ctx;
-          off = ((size_t)(b * K + t) * a.nkv + kvh) * MDH + part * 8;
-          ks = kb;
-          vs = vb;
-        }
-        kv = *reinterpret_cast<const u32x4*>(ks + off);
-        vv = *reinterpret_cast<const u32x4*>(vs + off);
-      }
-      *reinterpret_cast<u32x4*>(&sk[key][part * 8]) = kv;
+      bool ctxk;
+      const size_t off = key_off(j0 + min(key, nk - 1), part, ctxk);
+      const u32x4 kx = *reinterpret_cast<const u32x4*>((ctxk ? kc : kb) + off);
+      kr[it] = key < nk ? kx : z;
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        svt[part * 8 + 2 * i][key] = (bf16)(vv[i] & 0xffffu);
-        svt[part * 8 + 2 * i + 1][key] = (bf16)(vv[i] >> 16);
+    for (int it = 0; it < 2; ++it) {
+      const int u = tid + it * 256;
+      const int part = u >> 5, k0 = 2 * (u & 31);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bool ctxk;
+        const size_t off = key_off(j0 + min(k0 + h, nk - 1), part, ctxk);
+        const u32x4 vx = *reinterpret_cast<const u32x4*>((ctxk ? vc : vb) + off);
+        vr[2 * it + h] = k0 + h < nk ? vx : z;
       }
     }
-    __syncthreads();
+  };
+  static_assert((MK * MDH / 8) / 256 == 4, "four pieces per thread");
+  u32x4 kr[4], vr[4];
+  if (k_begin < k_end) load_kv(k_begin, kr, vr);
+  // The barriers below wait for LDS traffic only (lds_barrier), so the next sub-tile's global
+  // loads, issued before this sub-tile's math, stay in flight across them.
+  for (int j0 = k_begin; j0 < k_end; j0 += MK) {
+    const int nk = min(MK, k_end - j0);
+    lds_barrier();   // every wave is done with the previous sub-tile's K, V and P
+    // K rows -> sk[key][dim]; V rows -> svt[dim][key] (transposed for the P V operand)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int e = tid + it * 256;
+      *reinterpret_cast<u32x4*>(&sk[e >> 4][(e & 15) * 8]) = kr[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int u = tid + it * 256;
+      const int part = u >> 5, k0 = 2 * (u & 31);
+      const u32x4 v0 = vr[2 * it], v1 = vr[2 * it + 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // word i holds dims 2i (low half) and 2i + 1 of its key
+        *reinterpret_cast<unsigned*>(&svt[part * 8 + 2 * i][k0]) = (v0[i] & 0xffffu) | (v1[i] << 16);
+        *reinterpret_cast<unsigned*>(&svt[part * 8 + 2 * i + 1][k0]) = (v0[i] >> 16) | (v1[i] & 0xffff0000u);
+      }
+    }
+    lds_barrier();
+    if (j0 + MK < k_end) load_kv(j0 + MK, kr, vr);
     // S = Q K^T for 16 rows x 64 keys (4 key fragments)
     f32x4 s[4];
 #pragma unroll
@@ -157,7 +186,7 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
         sp[w][4 * kg + j][16 * f + li] = hi;
         sl[w][4 * kg + j][16 * f + li] = f2bf(s[f][j] - bf2f(hi));
       }
-    __syncthreads();
+    lds_barrier();
     // O += P V : A = P [16 rows][64 keys], B = V^T rows (dims) x keys
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
