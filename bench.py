@@ -127,7 +127,7 @@ def algorithmic(cfg, tau_mean, n_ctx):
     fl = 2 * M * cfg.n_layers * layer_w + 2 * B * (K - 1) * V * d
     fl += cfg.n_layers * B * cfg.n_heads * K * (n_ctx + K) * cfg.head_dim * 4   # QK^T and PV
     fl += 2 * rows_inj * w_inject
-    lm_bytes = V * d * es + M * d * 4                  # weights + fp32-precision hidden rows
+    lm_bytes = V * d * es + M * d * es                 # weights + the hidden rows (bf16 input for bf16 drafters)
     return dict(bytes=bytes_, flops=fl, lm_head_bytes=lm_bytes, lm_head_flops=2 * B * (K - 1) * V * d)
 
 
