@@ -471,8 +471,6 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
   float* part = wsp<float>(H, W.part);
   SeqCtx* ctx = wsp<SeqCtx>(H, W.ctx);
   int* counters = wsp<int>(H, W.counters);
-  PlanArgs pa{n_seq, H->max_seqs, c->window, seq_ids, seq_len(H), seq_base(H), dev_err(H), ctx, counters};
-  HIP_TRY(launch_draft_plan(pa, st));
   const size_t Mmax = (size_t)H->max_batch * K;   // rows of every activation plane
   float* hA = wsp<float>(H, W.h0);
   float* hB = wsp<float>(H, W.h1);
@@ -496,7 +494,9 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
   ra.y = act_y;
   ra.ldy = d;
   ra.y_plane = Mmax * d;
+  ra.plan = PlanArgs{H->max_seqs, c->window, seq_ids, seq_len(H), seq_base(H), ctx, counters};
   HIP_TRY(launch_embed_pre(b, ra, M, st));
+  ra.plan = PlanArgs{};
   const int chunks = attn_chunks(c, n_seq);
   for (int l = 0; l < c->n_layers; ++l) {
     // q, k, v = y [W_q; W_k; W_v]^T

@@ -4,7 +4,7 @@
 
 namespace dfl {
 
-// Per-sequence context of one draft call, written by draft_plan_kernel.
+// Per-sequence context of one draft call, written by the block-embed kernel.
 struct SeqCtx {
   int sid;     // sequence id (clamped into range)
   int L;       // anchor position = current length
@@ -12,17 +12,19 @@ struct SeqCtx {
   int slot0;   // ring slot of the oldest visible position
 };
 
+// Per-call sequence plan, done by the block-embed kernel (the workgroup of each sequence's
+// slot 0 writes its SeqCtx; workgroup 0 zeroes the lm_head fragment counters).
 struct PlanArgs {
-  int n_seq, max_seqs, window;
+  int max_seqs, window;
   const int* seq_ids;
   const int* seq_len;
   const int* seq_base;
-  int* dev_err;
   SeqCtx* ctx;
   int* counters;       // lm_head work-stealing counters, zeroed here
 };
 
 struct RowArgs {
+  PlanArgs plan;       // block embed only
   int K, d, mask_id, use_conv, final_norm, splits, part_rows, ldy, vocab;
   size_t y_plane;      // activation planes of y (bf16 drafters)
   void* y2;            // final norm only: split copy of the output for the lm_head GEMM
@@ -195,7 +197,6 @@ struct SynthArgs {
   int* target;
 };
 
-hipError_t launch_draft_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_embed_pre(bool bf, const RowArgs& a, int rows, hipStream_t st);
 hipError_t launch_post_pre(bool bf, const RowArgs& a, int rows, hipStream_t st);
 hipError_t launch_qkv_post(bool bf, const QkvArgs& a, int rows, hipStream_t st);

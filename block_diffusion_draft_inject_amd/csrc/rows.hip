@@ -31,13 +31,11 @@ __device__ __forceinline__ void rope_cs(long pos, int i, int dh, double log_thet
 // Per sequence of a draft call: clamp the id, read its length and base, and derive the
 // visible context: positions max(base, L - window) .. L-1, which sit in consecutive ring
 // slots (mod window) starting at slot0.
-__global__ __launch_bounds__(256) void draft_plan_kernel(PlanArgs a) {
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b < NCOUNTERS && a.counters) a.counters[b] = 0;   // lm_head work counters of this call
-  if (b >= a.n_seq) return;
+// The sequence's attention context (ring slots of the last min(L - base, window) positions).
+__device__ __forceinline__ void plan_seq(const PlanArgs& a, int* dev_err, int b) {
   int sid = a.seq_ids[b];
   if (sid < 0 || sid >= a.max_seqs) {
-    atomicOr(a.dev_err, 1);
+    atomicOr(dev_err, 1);
     sid = 0;
   }
   const int L = a.seq_len[sid], base = a.seq_base[sid];
@@ -514,6 +512,9 @@ __global__ __launch_bounds__(PP_T) void embed_pre_kernel(RowArgs a) {
   const int row = blockIdx.x, tid = threadIdx.x;
   const int b = row / a.K, t = row % a.K;
   const int d = a.d;
+  // the call's plan (read only by later kernels of the call)
+  if (t == 0 && tid == 0) plan_seq(a.plan, a.dev_err, b);
+  if (row == 0 && tid < NCOUNTERS && a.plan.counters) a.plan.counters[tid] = 0;
   int anchor = a.anchor[b];
   if (anchor < 0 || anchor >= a.vocab) {   // out-of-range token: record and read row 0
     if (tid == 0 && t == 0) atomicOr(a.dev_err, 8);
@@ -828,10 +829,6 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
     else hipLaunchKernelGGL(KERNEL<float>, grid, block, 0, st, arg);             \
   } while (0)
 
-hipError_t launch_draft_plan(const PlanArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(draft_plan_kernel, dim3((a.n_seq + 255) / 256), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
 hipError_t launch_embed_pre(bool bf, const RowArgs& a, int rows, hipStream_t st) {
   if (a.d % 4) return hipErrorInvalidValue;
   const int v = (a.d + 4 * PP_T - 1) / (4 * PP_T);
