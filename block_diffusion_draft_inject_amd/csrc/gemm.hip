@@ -785,10 +785,7 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
       const int rt = (M + 127) / 128;
       const int ntiles = (N + 127) / 128;
       const int nk = K / 32;
-      // at most 8 splits for the layer GEMMs (their row kernels read <= 8 partials); the
-      // injection's long-K projection (its partials are summed by loops over any count) may
-      // take 16, so that its one live row tile still fills the chip
-      pl.splits = clampi(512 / (ntiles * rt), 1, clampi(nk / 8, 1, nk >= 512 ? 16 : 8));
+      pl.splits = clampi(512 / (ntiles * rt), 1, clampi(nk / 8, 1, 8));
       pl.grid = dim3(ntiles, rt, pl.splits);
     }
   }
