@@ -65,7 +65,7 @@ __device__ __forceinline__ void sel_gates(const SelectArgs& a, int b, float (*gt
   if constexpr (sizeof(T) == 2) {
     const int li = lane & 15, kg = lane >> 4;
     const int nch = d / 32;                 // 32-wide k chunks; the waves take every 4th
-    constexpr int BATCH = 16;
+    constexpr int BATCH = 8;               // 24 loads of 16 bytes in flight per lane
     for (int mt = 0; mt < (K + 15) / 16; ++mt)
       for (int nt = 0; nt < (r + 15) / 16; ++nt) {
         const float* hr = hb + (size_t)min(mt * 16 + li, K - 1) * d + kg * 8;
@@ -83,7 +83,9 @@ __device__ __forceinline__ void sel_gates(const SelectArgs& a, int b, float (*gt
           }
 #pragma unroll
           for (int u = 0; u < BATCH; ++u) {
-            if (c0 + 4 * u >= nch) break;
+            // a chunk past the end (its loads were clamped) adds zero: no branch, so that the
+            // compiler keeps the whole batch of loads ahead of the first MFMA
+            if (c0 + 4 * u >= nch) w[u] = u32x4{0u, 0u, 0u, 0u};
             u32x4 hi, lo;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {

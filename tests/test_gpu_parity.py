@@ -192,3 +192,16 @@ def test_mid_bf16_lm_head_wave_kernel_without_logits(H):
     _prefill(case, [1], [(0, 50)])
     res = _check(H, case, [1], [123], mode_names=("viterbi",))
     _same_topk_without_logits(case, [1], [123], res)
+
+
+@pytest.mark.parametrize("K,n_seq", [(16, 4), (32, 2)])
+def test_mid_bf16_selector_rank_256(H, K, n_seq):
+    """Selector rank 256, the width of the A/B token tables on the pages ("Architecture",
+    "Problem 1"), with A, B ~ N(0,1) so that the pair term decides the path; K = 32 is the
+    largest block the selector takes (with 2 query heads per KV head, so that the grouped
+    attention rows of one KV head, 2 x 32, still fit one 64-row tile)."""
+    cfg = MID.replace(sel_rank=256, block_size=K, n_kv_heads=8 // (64 // K), name=f"mid_bf16_r256_k{K}")
+    case = H.Case(cfg, max_seqs=n_seq, max_batch=n_seq, max_inject_rows=64, selector_stress=True)
+    seq_ids = list(range(n_seq))
+    spans = [(0, 30 + 17 * i) for i in seq_ids]
+    _full_check(H, case, seq_ids, spans, anchors=[11 + 1000 * i for i in seq_ids])
