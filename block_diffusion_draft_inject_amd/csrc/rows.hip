@@ -180,6 +180,9 @@ __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
         const int spc = min(sp, nsp - 1), qc = max(q, q0);
         pv[sp][q][i] = ld4f(a.part, ((size_t)spc * a.part_rows + (row - 2 + qc)) * d + kc);
       }
+  // keep the burst together: without this fence the scheduler moves some partial loads down to
+  // their additions (at 8 splits, one row slice: nine serial load round trips)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const bool in = (i * PP_T + tid) * 4 < d;
