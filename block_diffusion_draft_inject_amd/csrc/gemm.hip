@@ -771,7 +771,11 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
     // 256 x 256 tiles (one workgroup per CU) once there are more than 128 rows, else 128 x 128
     // (two per CU); the workgroups resident at once split the column tiles statically.
     // PARTIAL: 128 x 128 tiles, k-splits bring the launch to about two workgroups per CU, each
-    // split at least 8 k-steps of 32.
+    // split at least 8 k-steps of 32.  For 129..256 rows and at least 3072 columns, 256 x 128
+    // tiles (the weights streamed once, not once per 128 rows), k-splits up to about one
+    // workgroup per CU.  (Measured at 256 rows: QKV 16.6 -> 14.9 us, gate/up 39.6 -> 34.8 us; the
+    // 2048-column GEMMs, with only 16 column tiles, ran slower on the wide tile, and so did
+    // every GEMM at 512 or more rows.)
     pl.kind = 5;
     if (mode == GEMM_TOPK) {
       pl.mt = M > 128 ? 1 : 0;
@@ -781,11 +785,12 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
       pl.groups = clampi((pl.mt ? 256 : 512) / rt, 1, ntiles);
       pl.grid = dim3(pl.groups, rt, 1);
     } else {
-      pl.mt = 0;
-      const int rt = (M + 127) / 128;
+      pl.mt = (M > 128 && M <= 256 && N >= 3072) ? 2 : 0;
+      const int bm = pl.mt ? 256 : 128;
+      const int rt = (M + bm - 1) / bm;
       const int ntiles = (N + 127) / 128;
       const int nk = K / 32;
-      pl.splits = clampi(512 / (ntiles * rt), 1, clampi(nk / 8, 1, 8));
+      pl.splits = clampi((pl.mt ? 256 : 512) / (ntiles * rt), 1, clampi(nk / 8, 1, 8));
       pl.grid = dim3(ntiles, rt, pl.splits);
     }
   }

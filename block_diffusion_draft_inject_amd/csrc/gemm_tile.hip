@@ -169,10 +169,10 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, unsigned char* sme
   }
 }
 
-// The same over all k-steps [0, nk), nk even, with four stages used as two pairs: the loads of
-// k-steps 2j+2 and 2j+3 go out together (each operand row's two adjacent 64-byte segments back
-// to back) while steps 2j and 2j+1 are multiplied, so a workgroup meets at one barrier per two
-// k-steps.  (Measured on the 256 x 256 bf16-input tile: 2540 cycles per k-step against 3050
+// The same over k-steps [c0, c0 + nk), nk even, with four stages used as two pairs: the loads
+// of k-steps 2j+2 and 2j+3 go out together (each operand row's two adjacent 64-byte segments
+// back to back) while steps 2j and 2j+1 are multiplied, so a workgroup meets at one barrier per
+// two k-steps.  (Measured on the 256 x 256 bf16-input tile: 2540 cycles per k-step against 3050
 // for the four-stage rotation, whose load rate is the same.)
 template <class T>
 __device__ __forceinline__ void tile_issue_pair(const TileSrc<T>& s, unsigned st_a, unsigned st_b, int wave, int c) {
@@ -191,7 +191,7 @@ __device__ __forceinline__ void tile_issue_pair(const TileSrc<T>& s, unsigned st
 
 template <class T>
 __device__ __forceinline__ void tile_run_pairs(const GemmParams& p, unsigned char* smem, int m0, int n0, int Mv,
-                                               int nk, f32x4 (&acc)[T::FM][T::FN]) {
+                                               int c0, int nk, f32x4 (&acc)[T::FM][T::FN]) {
   static_assert(T::Sc == 4, "two pairs of stages");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -205,12 +205,12 @@ __device__ __forceinline__ void tile_run_pairs(const GemmParams& p, unsigned cha
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int np = nk / 2;
-  tile_issue_pair<T>(src, sbase, sbase + T::STAGE, wave, 0);
+  tile_issue_pair<T>(src, sbase, sbase + T::STAGE, wave, c0);
   for (int j = 0; j < np; ++j) {
     // pair j has landed for every wave, and every wave is done with pair j - 1's stages
     wait_barrier<0>();
     const int cur = (j & 1) * 2, nxt = 2 - cur;
-    if (j + 1 < np) tile_issue_pair<T>(src, sbase + nxt * T::STAGE, sbase + (nxt + 1) * T::STAGE, wave, 2 * j + 2);
+    if (j + 1 < np) tile_issue_pair<T>(src, sbase + nxt * T::STAGE, sbase + (nxt + 1) * T::STAGE, wave, c0 + 2 * j + 2);
     tile_mma<T>(smem + cur * T::STAGE, wm, wn, lo, acc);
     tile_mma<T>(smem + (cur + 1) * T::STAGE, wm, wn, lo, acc);
   }
@@ -228,7 +228,12 @@ __global__ __launch_bounds__(T::NT, OCC) void gemm_tile_partial(GemmParams p) {
   const int nk = p.K / MK, s = blockIdx.z;
   const int c0 = (int)((long)nk * s / p.splits), c1 = (int)((long)nk * (s + 1) / p.splits);
   f32x4 acc[T::FM][T::FN];
-  tile_run<T>(p, smem, m0, n0, Mv, c0, c1, acc);
+  if constexpr (T::Sc == 4) {
+    if ((c1 - c0) % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, c0, c1 - c0, acc);
+    else tile_run<T>(p, smem, m0, n0, Mv, c0, c1, acc);
+  } else {
+    tile_run<T>(p, smem, m0, n0, Mv, c0, c1, acc);
+  }
 #pragma unroll
   for (int i = 0; i < T::FM; ++i)
 #pragma unroll
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
     const int n0 = t * BN;
     f32x4 acc[T::FM][T::FN];
     if constexpr (T::Sc == 4) {
-      if (nk % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, nk, acc);
+      if (nk % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, 0, nk, acc);
       else tile_run<T>(p, smem, m0, n0, Mv, 0, nk, acc);
     } else {
       tile_run<T>(p, smem, m0, n0, Mv, 0, nk, acc);
@@ -348,11 +353,15 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
 }  // namespace
 
 // Tile configurations: 0 = 128 x 128 (2 x 2 waves, 3 stages, two workgroups per CU),
-// 1 = 256 x 256 (4 x 2 waves of 64 x 128, two waves per SIMD, 3 stages, one workgroup per CU).
+// 1 = 256 x 256 (4 x 2 waves of 64 x 128, two waves per SIMD, 3 stages, one workgroup per CU),
+// 2 = 256 x 128 (4 x 2 waves of 64 x 64, one workgroup per CU, 160 KiB of LDS: four stages used
+// as two pairs): all rows of a batch of up to 256 in one tile, so each weight tile is streamed
+// once.
 // The lm_head variants read the hi plane only; with half the bytes per stage the big tile
 // keeps four stages in flight.
 using TileSmall = TileCfg<128, 128, 2, 2, 3>;
 using TileBig = TileCfg<256, 256, 4, 2, 3>;
+using TileTall = TileCfg<256, 128, 4, 2, 4>;
 using TileSmallHi = TileCfg<128, 128, 2, 2, 3, 1>;
 using TileBigHi = TileCfg<256, 256, 4, 2, 4, 1>;
 
@@ -369,7 +378,8 @@ hipError_t tile_launch(const GemmPlan& pl, int mode, const GemmParams& p, hipStr
       else hipLaunchKernelGGL((lmhead_topk_tile<TileSmallHi, 2, false>), pl.grid, blk, 0, st, p);
     }
   } else if (mode == GEMM_PARTIAL) {
-    if (pl.mt) hipLaunchKernelGGL((gemm_tile_partial<TileBig, 1>), pl.grid, dim3(TileBig::NT), 0, st, p);
+    if (pl.mt == 2) hipLaunchKernelGGL((gemm_tile_partial<TileTall, 1>), pl.grid, dim3(TileTall::NT), 0, st, p);
+    else if (pl.mt) hipLaunchKernelGGL((gemm_tile_partial<TileBig, 1>), pl.grid, dim3(TileBig::NT), 0, st, p);
     else hipLaunchKernelGGL((gemm_tile_partial<TileSmall, 2>), pl.grid, dim3(TileSmall::NT), 0, st, p);
   } else {
     return hipErrorInvalidValue;

@@ -44,7 +44,8 @@ struct GemmPlan {
   int kind;      // 0 = skinny (17..64 rows), 2 = f32 simple, 3 = stream (<= 16 rows), 4 = lm_head
                  // waves (<= 16 rows), 5 = MFMA tiles with LDS-DMA operands (more than 64 rows)
   int slc;       // stream: 64-wide chunks per wave
-  int mt;        // skinny: row fragments (1,2,4); MFMA tiles: 0 = 128 x 128, 1 = 256 x 256
+  int mt;        // skinny: row fragments (1,2,4); MFMA tiles: 0 = 128 x 128, 1 = 256 x 256,
+                 // 2 = 256 x 128
   int splits;
   int groups;    // TOPK groups
   dim3 grid;

@@ -205,3 +205,16 @@ def test_mid_bf16_selector_rank_256(H, K, n_seq):
     seq_ids = list(range(n_seq))
     spans = [(0, 30 + 17 * i) for i in seq_ids]
     _full_check(H, case, seq_ids, spans, anchors=[11 + 1000 * i for i in seq_ids])
+
+
+def test_mid_bf16_wide_tiles_192_rows(H):
+    """12 sequences at K=16 (192 rows) with 16/4 heads and ffn 1536: the QKV (3072 columns) and
+    gate/up (3072) GEMMs take the 256 x 128 tiles with paired k-steps, the 2048-column ones
+    the 128 x 128 tiles; ragged contexts with ring wrap."""
+    cfg = MID.replace(n_heads=16, n_kv_heads=4, ffn=1536, name="mid_bf16_wide")
+    case = H.Case(cfg, max_seqs=12, max_batch=12, max_inject_rows=200)
+    seq_ids = list(range(12))
+    rng = np.random.default_rng(5)
+    spans = [(0, int(L)) for L in rng.integers(1, 160, size=12)]
+    anchors = rng.integers(0, cfg.vocab - 1, size=12).tolist()
+    _full_check(H, case, seq_ids, spans, anchors, mode_names=("viterbi",))
