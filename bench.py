@@ -293,6 +293,19 @@ def traffic_probe(steps, torch):
     log(f"[traffic-probe] {steps} cycles + 3 copies of {COPY_BYTES} bytes done")
 
 
+def mfma_probe(steps, torch):
+    """Workload for the MFMA counter passes: `steps` eager cycles of the batch-32 workload
+    (b32_k8_conv), after one warm-up cycle."""
+    from block_diffusion_draft_inject_amd import synth
+    cfg = synth.WORKLOADS["b32_k8_conv"]
+    cyc = Cycle(cfg, 0, torch, cfg.batch)
+    raw = torch.cuda.current_stream().cuda_stream
+    for _ in range(steps + 1):
+        cyc.step(raw)
+    torch.cuda.synchronize()
+    log(f"[mfma-probe] {steps + 1} eager cycles of {cfg.name} done")
+
+
 def _counter_rows(path):
     import csv
     rows = list(csv.DictReader(open(path)))
@@ -340,6 +353,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the workload of one rocprofv3 counter pass (eager cycles + calibration copy)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="run the workload of the MFMA counter passes (eager batch-32 cycles)")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the lm_head traffic record from two counter-collection CSVs (no GPU)")
     args = ap.parse_args()
@@ -358,6 +373,9 @@ def main():
     torch.cuda.set_device(0)
     if args.traffic_probe:
         traffic_probe(args.steps, torch)
+        return
+    if args.mfma_probe:
+        mfma_probe(args.steps, torch)
         return
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup}
     if not args.no_b1:
@@ -408,6 +426,25 @@ def main():
                       "mfma_frac": round(r3["mfma_frac"], 4), "hbm_frac": round(r3["hbm_frac"], 4),
                       "algorithmic_tflop_per_step": round(r3["alg"]["flops"] / 1e12, 4),
                       "lm_head_avg_ms": round(r3["lm_head_ms"], 5)}
+        # the batch-32 dominant kernel (lm_head + top-16 over 224 rows): its intensity (flops per
+        # weight byte ~ rows) is below the bf16 ridge (2500 / 8 ~ 312), so HBM bounds it; the MFMA
+        # fraction is given beside it
+        a3 = r3["alg"]
+        lm_s = r3["lm_head_ms"] * 1e-3
+        lm_tflops = a3["lm_head_flops"] / lm_s / 1e12
+        lm_gbps3 = a3["lm_head_bytes"] / lm_s / 1e9
+        ridge = MFMA_BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBPS
+        hbm_bound = a3["lm_head_flops"] / a3["lm_head_bytes"] < ridge
+        out["b32"]["roofline"] = {
+            "kernel": "lm_head GEMM + fused top-16 (lmhead_topk_tile, 256 x 256 MFMA tiles)",
+            "bound": "hbm" if hbm_bound else "mfma",
+            "achieved": round(lm_gbps3 if hbm_bound else lm_tflops, 1),
+            "peak": HBM_PEAK_GBPS if hbm_bound else MFMA_BF16_PEAK_TFLOPS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": round((lm_gbps3 / HBM_PEAK_GBPS) if hbm_bound else (lm_tflops / MFMA_BF16_PEAK_TFLOPS), 4),
+            "mfma_tflops": round(lm_tflops, 1), "mfma_frac": round(lm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None, "avg_launch_ms": round(r3["lm_head_ms"], 5),
+            "bytes_per_launch": int(a3["lm_head_bytes"]), "flops_per_launch": int(a3["lm_head_flops"])}
         del r3["cycle"]
     print(json.dumps(out), flush=True)
 
