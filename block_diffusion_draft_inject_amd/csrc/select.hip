@@ -418,20 +418,39 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   }
 }
 
-// Greedy longest-prefix verification: one thread per sequence.
-__global__ void verify_kernel(VerifyArgs a) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= a.n_seq) return;
+// Greedy longest-prefix verification: one wave per sequence, lane j on slot c0 + j of each
+// 64-slot chunk.  Every chunk's draft and target ids are loaded together; the first mismatch is
+// the lowest set bit of a ballot, so the accepted length costs one load round trip per chunk
+// instead of one per accepted token.
+__global__ __launch_bounds__(256) void verify_kernel(VerifyArgs a) {
+  const int b = (int)((blockIdx.x * blockDim.x + threadIdx.x) / WAVE);
+  const int lane = threadIdx.x & (WAVE - 1);
+  if (b >= a.n_seq) return;   // uniform over the wave
   const int K = a.K;
   const int* dr = a.draft + (size_t)b * (K - 1);
   const int* tg = a.target + (size_t)b * K;
-  int n = 0;
-  while (n < K - 1 && dr[n] == tg[n]) ++n;
   int* com = a.committed + (size_t)b * K;
-  for (int i = 0; i < K; ++i) com[i] = i < n ? dr[i] : (i == n ? tg[n] : -1);
-  a.n_acc[b] = n;
-  if (a.n_commit) a.n_commit[b] = n + 1;
-  a.next_anchor[b] = tg[n];
+  int n = K - 1;              // every draft accepted unless a chunk finds a mismatch
+  for (int c0 = 0; c0 < K - 1; c0 += WAVE) {
+    const int i = c0 + lane;
+    const bool in = i < K - 1;
+    const int d = dr[in ? i : 0], g = tg[in ? i : 0];
+    const unsigned long long miss = __ballot(in && d != g);
+    if (miss) {
+      n = c0 + __builtin_ctzll(miss);
+      break;
+    }
+  }
+  const int bonus = tg[n];
+  for (int c0 = 0; c0 < K; c0 += WAVE) {
+    const int i = c0 + lane;
+    if (i < K) com[i] = i < n ? dr[i] : (i == n ? bonus : -1);
+  }
+  if (lane == 0) {
+    a.n_acc[b] = n;
+    if (a.n_commit) a.n_commit[b] = n + 1;
+    a.next_anchor[b] = bonus;
+  }
 }
 
 // Rejection-sampling verification ("Architecture", section "Speculative Decoding Context" and
@@ -582,7 +601,9 @@ hipError_t launch_select(bool bf, const SelectArgs& a, int n_seq, hipStream_t st
   return hipGetLastError();
 }
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(verify_kernel, dim3((a.n_seq + 255) / 256), dim3(256), 0, st, a);
+  if (a.n_seq <= 0) return hipSuccess;
+  // four sequences (waves) per workgroup
+  hipLaunchKernelGGL(verify_kernel, dim3((a.n_seq + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_verify_rejection(const RejectArgs& a, hipStream_t st) {

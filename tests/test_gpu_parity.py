@@ -218,3 +218,37 @@ def test_mid_bf16_wide_tiles_192_rows(H):
     spans = [(0, int(L)) for L in rng.integers(1, 160, size=12)]
     anchors = rng.integers(0, cfg.vocab - 1, size=12).tolist()
     _full_check(H, case, seq_ids, spans, anchors, mode_names=("viterbi",))
+
+
+@pytest.mark.parametrize("K", [2, 16, 64, 65, 130])
+def test_verify_greedy_block_sizes(K):
+    """Greedy verification alone (one wave per sequence, 64-slot chunks): 37 sequences (a
+    partial last workgroup) with accepted prefixes of every length from 0 to K-1 (full
+    acceptance included), against the oracle's longest-prefix rule; then an empty batch."""
+    import torch
+    rng = np.random.default_rng(K)
+    n_seq, V = 37, 5000
+    draft = rng.integers(0, V, size=(n_seq, K - 1))
+    target = rng.integers(0, V, size=(n_seq, K))
+    for b in range(n_seq):
+        n = min(b * (K - 1) // (n_seq - 1), K - 1) if b < n_seq - 1 else K - 1
+        target[b, :n] = draft[b, :n]
+        if n < K - 1:
+            target[b, n] = (draft[b, n] + 1 + rng.integers(0, V - 1)) % V   # a different token
+    dev = lambda x: torch.tensor(x, dtype=torch.int32, device="cuda")
+    d, t = dev(draft), dev(target)
+    nacc = torch.empty(n_seq, dtype=torch.int32, device="cuda")
+    ncom = torch.empty_like(nacc)
+    nxt = torch.empty_like(nacc)
+    com = torch.empty((n_seq, K), dtype=torch.int32, device="cuda")
+    B.dflash_verify_greedy(n_seq, K, d, t, nacc, ncom, com, nxt)
+    torch.cuda.synchronize()
+    seen = set()
+    for b in range(n_seq):
+        n, c, a = O.verify_greedy(draft[b], target[b])
+        seen.add(n)
+        assert nacc[b].item() == n and ncom[b].item() == n + 1 and nxt[b].item() == a, b
+        assert np.array_equal(com[b].cpu().numpy(), c), b
+    assert 0 in seen and K - 1 in seen
+    B.dflash_verify_greedy(0, K, d, t, nacc, ncom, com, nxt)   # empty batch: a no-op
+    torch.cuda.synchronize()
