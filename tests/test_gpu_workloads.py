@@ -268,3 +268,24 @@ def test_b64_k16_long_context(H, big):
     match, alt, last = synth.match_draws(cfg, 0)
     run.select_verify(anchors, res, "viterbi", lambda p: synth.stand_in_target(p, match, alt, last, cfg.vocab))
     assert run.d.dflash_get_device_error() == 0
+
+
+def test_injection_200_rows_wide_tiles(H, big):
+    """Full-size injection of 200 rows in one call (8 sequences x 25 positions), then 176 more
+    appended: the stacked K/V projection (5120 columns, K = 2048) runs on the 256 x 128 tiles
+    with 6 k-splits of 10 or 11 k-steps, i.e. both the paired and the single-step k-loop.
+    Every injected position of every layer against the oracle."""
+    cfg = synth.WORKLOADS["b32_k8_conv"]
+    ids = list(range(8))
+    run = Run(H, big, cfg, max_seqs=8, max_batch=8, max_inject_rows=256, sampled=ids)
+    run.d.dflash_reset_seqs(run.t(np.arange(8, dtype=np.int32)))
+    run.inject(ids, [np.arange(1000 * s, 1000 * s + 25) for s in ids])
+    worst, same = H.check_kv(run, ids, max_positions=25)
+    H.log(f"[kv 200 rows] worst rel err {worst:.2e}, bit-equal {same:.4f}")
+    assert worst <= 1.0 and same >= 0.99
+    run.inject(ids, [np.arange(1000 * s + 25, 1000 * s + 25 + 22) for s in ids], start=False)
+    worst, same = H.check_kv(run, ids, max_positions=47)
+    H.log(f"[kv +176 rows] worst rel err {worst:.2e}, bit-equal {same:.4f}")
+    assert worst <= 1.0 and same >= 0.99
+    assert np.array_equal(run.lengths(ids), np.array([1000 * s + 47 for s in ids]))
+    assert run.d.dflash_get_device_error() == 0
