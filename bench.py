@@ -401,6 +401,11 @@ def main():
                                    "vocab 151936, 5 taps x 5120, K=16, batch 1, context 1024 (window 1024)",
                        "batch": 1, "block_size": 16, "context": 1024, "graph_steps": r["graph_steps"]},
             "eager_ms_per_step": round(r["eager_ms_per_step"], 4),
+            # the pages' own figures, context only: end-to-end speculative decoding with a target
+            # model (speed-up over autoregressive decoding), not a drafter-pass rate
+            "context": {"pages_end_to_end": "3.43x over autoregressive decoding at concurrency 1 and "
+                                            "1.16-1.45x at concurrency 32 (one H200, SGLang, FlashAttention 3, "
+                                            "block 8); not comparable with a drafter-pass rate"},
             "draft_tokens_per_s": round(r["draft_tokens_per_s"], 1),
             "cycle_hbm_frac": round(r["hbm_frac"], 4),
             "cycle_algorithmic_bytes": int(alg["bytes"]),
