@@ -44,7 +44,11 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// one LDS-DMA load: 64 lanes x 16 bytes from base + voff[lane] to LDS [lds, lds + 1024)
+// one LDS-DMA load: 64 lanes x 16 bytes from base + voff[lane] to LDS [lds, lds + 1024).
+// The LDS destination goes through M0, which each asm statement sets itself right before its
+// load.  The compiler warns that it cannot preserve a reserved register named as clobbered; on
+// gfx950 it keeps nothing in M0 across these kernels (ordinary LDS instructions do not use it,
+// and nothing else here issues LDS-DMA, GWS or message instructions), so nothing live is lost.
 __device__ __forceinline__ void dma16(unsigned lds, unsigned voff, const void* base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
                : "memory", "m0");
