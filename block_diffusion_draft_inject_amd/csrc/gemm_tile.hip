@@ -76,8 +76,8 @@ struct TileSrc {
 };
 
 template <class T>
-__device__ __forceinline__ void tile_src(const GemmParams& p, int m0, int n0, int Mv, int wave, int lane,
-                                         TileSrc<T>& s) {
+__device__ __forceinline__ void tile_src(const GemmParams& p, int m0, int n0, int Mv, int ncap, int wave,
+                                         int lane, TileSrc<T>& s) {
   const int r16 = lane >> 2;
   const int kc = (lane & 3) ^ tile_swz(r16);
   const char* ahi = reinterpret_cast<const char*>(p.A);
@@ -94,7 +94,7 @@ __device__ __forceinline__ void tile_src(const GemmParams& p, int m0, int n0, in
       s.base[q] = alo;
       s.voff[q] = (unsigned)(((size_t)r * p.lda + kc * 8) * 2);
     } else {                                       // weight rows
-      const int n = min(n0 + (b - T::PLc * T::BA) * 16 + r16, p.N - 1);
+      const int n = min(n0 + (b - T::PLc * T::BA) * 16 + r16, ncap - 1);   // columns past ncap re-read the last
       s.addr[q] = reinterpret_cast<const char*>(brow_ptr(p, n) + kc * 8);
     }
   }
@@ -144,14 +144,14 @@ __device__ __forceinline__ void tile_wait(int pend) {
 
 // One output tile over k-steps [c0, c1): acc = the tile's partial products.
 template <class T>
-__device__ __forceinline__ void tile_run(const GemmParams& p, unsigned char* smem, int m0, int n0, int Mv, int c0,
-                                         int c1, f32x4 (&acc)[T::FM][T::FN]) {
+__device__ __forceinline__ void tile_run(const GemmParams& p, unsigned char* smem, int m0, int n0, int Mv, int ncap,
+                                         int c0, int c1, f32x4 (&acc)[T::FM][T::FN]) {
   constexpr int S = T::Sc;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / T::WGNc, wn = wave % T::WGNc, li = lane & 15, kg = lane >> 4;
   TileSrc<T> src;
-  tile_src<T>(p, m0, n0, Mv, wave, lane, src);
+  tile_src<T>(p, m0, n0, Mv, ncap, wave, lane, src);
   const unsigned lo = li * 64 + ((kg ^ tile_swz(li)) << 4);
   const unsigned sbase = lds_addr(smem);
 #pragma unroll
@@ -195,13 +195,13 @@ __device__ __forceinline__ void tile_issue_pair(const TileSrc<T>& s, unsigned st
 
 template <class T>
 __device__ __forceinline__ void tile_run_pairs(const GemmParams& p, unsigned char* smem, int m0, int n0, int Mv,
-                                               int c0, int nk, f32x4 (&acc)[T::FM][T::FN]) {
+                                               int ncap, int c0, int nk, f32x4 (&acc)[T::FM][T::FN]) {
   static_assert(T::Sc == 4, "two pairs of stages");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / T::WGNc, wn = wave % T::WGNc, li = lane & 15, kg = lane >> 4;
   TileSrc<T> src;
-  tile_src<T>(p, m0, n0, Mv, wave, lane, src);
+  tile_src<T>(p, m0, n0, Mv, ncap, wave, lane, src);
   const unsigned lo = li * 64 + ((kg ^ tile_swz(li)) << 4);
   const unsigned sbase = lds_addr(smem);
 #pragma unroll
@@ -233,10 +233,10 @@ __global__ __launch_bounds__(T::NT, OCC) void gemm_tile_partial(GemmParams p) {
   const int c0 = (int)((long)nk * s / p.splits), c1 = (int)((long)nk * (s + 1) / p.splits);
   f32x4 acc[T::FM][T::FN];
   if constexpr (T::Sc == 4) {
-    if ((c1 - c0) % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, c0, c1 - c0, acc);
-    else tile_run<T>(p, smem, m0, n0, Mv, c0, c1, acc);
+    if ((c1 - c0) % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, p.N, c0, c1 - c0, acc);
+    else tile_run<T>(p, smem, m0, n0, Mv, p.N, c0, c1, acc);
   } else {
-    tile_run<T>(p, smem, m0, n0, Mv, c0, c1, acc);
+    tile_run<T>(p, smem, m0, n0, Mv, p.N, c0, c1, acc);
   }
 #pragma unroll
   for (int i = 0; i < T::FM; ++i)
@@ -270,21 +270,28 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
   const int Mv = rows_valid(p);
   const int m0 = blockIdx.y * BM;
   if (m0 >= Mv) return;
-  const int ntiles = (p.N + BN - 1) / BN;
+  // a contiguous range of columns per workgroup, in 16-column blocks, walked in tiles of BN: the
+  // last tile of a range is partial, its columns past the range re-read the range's last weight
+  // row (cache hits) and are skipped by the epilogue.  (Against whole tiles handed out
+  // round-robin: 960 rows, 64 workgroups per row tile, 708 -> 673 us; 224 rows unchanged, where
+  // each workgroup's partial third tile costs about as much as the whole third tile that 82 of
+  // the 256 workgroups ran before: the k-step cost there does not follow the weight bytes.)
+  const int nblk = (p.N + 15) / 16;
+  const int cbeg = (int)((long)nblk * blockIdx.x / gridDim.x) * 16;
+  const int cend = min((int)((long)nblk * (blockIdx.x + 1) / gridDim.x) * 16, p.N);
   const int nk = p.K / MK;
   const int lrow = tid / TPR, part = tid % TPR;
   const int my_row = m0 + lrow;
   const bool row_live = my_row < Mv && (my_row % p.block) != 0;
   Top16 top;
   top.init();
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int n0 = t * BN;
+  for (int n0 = cbeg; n0 < cend; n0 += BN) {
     f32x4 acc[T::FM][T::FN];
     if constexpr (T::Sc == 4) {
-      if (nk % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, 0, nk, acc);
-      else tile_run<T>(p, smem, m0, n0, Mv, 0, nk, acc);
+      if (nk % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, cend, 0, nk, acc);
+      else tile_run<T>(p, smem, m0, n0, Mv, cend, 0, nk, acc);
     } else {
-      tile_run<T>(p, smem, m0, n0, Mv, 0, nk, acc);
+      tile_run<T>(p, smem, m0, n0, Mv, cend, 0, nk, acc);
     }
     wait_barrier<0>();   // every wave is done reading the stages; the epilogue buffer overlays them
 #pragma unroll
@@ -303,7 +310,8 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
       wait_barrier<0>();
       const int cb = part * CPT;
       if (LOGITS && my_row < Mv) {
-        for (int c = 0; c < CPT; ++c) store_logit(p, my_row, n0 + q * 64 + cb + c, ep[lrow][cb + c]);
+        for (int c = 0; c < CPT; ++c)
+          if (n0 + q * 64 + cb + c < cend) store_logit(p, my_row, n0 + q * 64 + cb + c, ep[lrow][cb + c]);
       }
       // threshold: the better of the 16th entries of the row's lists (a value below another
       // list's 16th entry has 16 better values in that list and cannot reach the row's top 16).
@@ -323,7 +331,7 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int col = cg + c4 * 4 + e;
-            mask |= (unsigned)(col < p.N && v[e] > tv) << (c4 * 4 + e);
+            mask |= (unsigned)(col < cend && v[e] > tv) << (c4 * 4 + e);
           }
         }
         while (mask) {
