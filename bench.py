@@ -56,7 +56,7 @@ def device_weights(cfg, seed, torch):
 class Cycle:
     """Device buffers and the per-step call sequence of one workload."""
 
-    def __init__(self, cfg, seed, torch, B):
+    def __init__(self, cfg, seed, torch, B, max_seqs=None):
         from block_diffusion_draft_inject_amd import binding as Bd
         self.torch, self.cfg, self.Bd = torch, cfg, B
         self.Bd = Bd
@@ -64,7 +64,7 @@ class Cycle:
         K = cfg.block_size
         t0 = time.time()
         self.w = device_weights(cfg, seed, torch)
-        self.d = Bd.Drafter(cfg, self.w, max_seqs=self.n, max_batch=self.n, max_inject_rows=1024)
+        self.d = Bd.Drafter(cfg, self.w, max_seqs=max_seqs or self.n, max_batch=self.n, max_inject_rows=1024)
         g = torch.Generator(device="cuda")
         g.manual_seed(seed + 1)
         dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -109,6 +109,72 @@ class Cycle:
                                       stream=stream)
         Bd.dflash_verify_greedy(self.n, K, self.path, self.target, self.nacc, self.tau, self.committed,
                                 self.anchor, stream=stream)
+
+
+def run_overlap(torch, reps=10, graph_steps=10):
+    """Mixed prefill + decode on two streams: the b1_k16 decode cycle of one sequence on one
+    stream while a second handle, sharing the KV cache (its own workspace), injects the
+    1024-row window of another sequence (a new request's prefill) on a second stream.  Times,
+    per step, four HIP graphs of `graph_steps` steps: decode alone, prefill alone, both back to
+    back on one stream, and both overlapped (fork/join across the two streams)."""
+    from block_diffusion_draft_inject_amd import synth
+    from block_diffusion_draft_inject_amd import binding as Bd
+    cfg = synth.WORKLOADS["b1_k16"]
+    cyc = Cycle(cfg, 0, torch, cfg.batch, max_seqs=2)
+    dB = Bd.Drafter(cfg, cyc.w, max_seqs=2, max_batch=1, max_inject_rows=cfg.window, kv_from=cyc.d)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    W = cfg.window
+    pre = torch.randn((1, W, cfg.concat_width), generator=g, device="cuda").to(torch.bfloat16)
+    sid = torch.tensor([1], dtype=torch.int32, device="cuda")
+    nnew = torch.tensor([W], dtype=torch.int32, device="cuda")
+    spos = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def prefill(stream):   # restarts sequence 1 at position 0 every time: the same work each step
+        dB.dflash_inject_kv(sid, nnew, W, pre, start_pos=spos, stream=stream)
+
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    G = graph_steps
+    with torch.cuda.stream(s1):
+        for _ in range(2):
+            cyc.step(s1.cuda_stream)
+            prefill(s1.cuda_stream)
+    torch.cuda.synchronize()
+
+    def capture(kind):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s1):
+            a = torch.cuda.current_stream()
+            if kind == "overlapped":
+                fork = torch.cuda.Event()
+                fork.record(a)
+                s2.wait_event(fork)
+            for _ in range(G):
+                if kind in ("decode", "sequential", "overlapped"):
+                    cyc.step(a.cuda_stream)
+                if kind in ("prefill", "sequential"):
+                    prefill(a.cuda_stream)
+                if kind == "overlapped":
+                    prefill(s2.cuda_stream)
+            if kind == "overlapped":
+                join = torch.cuda.Event()
+                join.record(s2)
+                a.wait_event(join)
+        return graph
+
+    res = {}
+    for kind in ("decode", "prefill", "sequential", "overlapped"):
+        graph = capture(kind)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        res[kind] = (time.perf_counter() - t0) * 1e3 / (reps * G)
+        del graph
+    return res
 
 
 def algorithmic(cfg, tau_mean, n_ctx):
@@ -349,6 +415,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-b32", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true")
     ap.add_argument("--no-b1", action="store_true", help="skip the headline workload (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--traffic-probe", action="store_true",
@@ -451,6 +518,15 @@ def main():
             "traffic": None, "avg_launch_ms": round(r3["lm_head_ms"], 5),
             "bytes_per_launch": int(a3["lm_head_bytes"]), "flops_per_launch": int(a3["lm_head_flops"])}
         del r3["cycle"]
+    if not args.no_overlap:
+        torch.cuda.empty_cache()
+        ov = run_overlap(torch)
+        out["overlap"] = {
+            "workload": "b1_k16 decode cycle of one sequence on one stream + a 1024-row prefill injection of "
+                        "another sequence on a second stream (second handle, shared KV cache)",
+            "decode_ms": round(ov["decode"], 4), "prefill_ms": round(ov["prefill"], 4),
+            "sequential_ms": round(ov["sequential"], 4), "overlapped_ms": round(ov["overlapped"], 4),
+            "saved_frac": round(1 - ov["overlapped"] / ov["sequential"], 4)}
     print(json.dumps(out), flush=True)
 
 

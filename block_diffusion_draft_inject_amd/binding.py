@@ -175,7 +175,9 @@ class Drafter:
     (layers: a list of per-layer dicts).  All methods enqueue on `stream` (a raw hipStream_t
     address, None = default stream) and return immediately."""
 
-    def __init__(self, cfg, weights, max_seqs, max_batch, max_inject_rows=1024, device="cuda"):
+    def __init__(self, cfg, weights, max_seqs, max_batch, max_inject_rows=1024, device="cuda", kv_from=None):
+        """kv_from: another Drafter of the same config and max_seqs whose KV cache this handle
+        shares (each handle keeps its own workspace)."""
         import torch
         self.cfg = cfg
         self.c = make_config(cfg)
@@ -184,7 +186,12 @@ class Drafter:
         self.weights = weights  # keep alive
         self.max_seqs, self.max_batch, self.max_inject_rows = max_seqs, max_batch, max_inject_rows
         self.kv_layout = dflash_kv_cache_layout(cfg, max_seqs)
-        self.kv = torch.zeros(self.kv_layout.total_bytes, dtype=torch.uint8, device=device)
+        if kv_from is not None:
+            if kv_from.max_seqs != max_seqs or kv_from.kv_layout.total_bytes != self.kv_layout.total_bytes:
+                raise ValueError("kv_from must have the same config and max_seqs")
+            self.kv = kv_from.kv
+        else:
+            self.kv = torch.zeros(self.kv_layout.total_bytes, dtype=torch.uint8, device=device)
         nbytes = dflash_workspace_bytes(cfg, max_seqs, max_batch, max_inject_rows)
         if nbytes == 0:
             raise DflashError("dflash_workspace_bytes", -1, "invalid sizes")

@@ -154,7 +154,11 @@ DFLASH_API size_t dflash_workspace_bytes(const dflash_config* cfg, int32_t max_s
 /* Creates a handle.  kv_cache (kv_bytes) and workspace (ws_bytes) are caller-owned device
  * buffers of at least the sizes above.  The caller must zero the seq_len/seq_base/device_error
  * words of kv_cache before first use (or call dflash_reset_seqs).  Host-side only: enqueues
- * nothing. */
+ * nothing.  Calls of one handle share its workspace, so they must not overlap (one stream, or
+ * ordered by events).  Several handles, each with its own workspace, may share one kv_cache and
+ * run at the same time on different streams as long as their calls touch disjoint sequences
+ * (e.g. a prefill injection of a new sequence beside the draft cycles of running ones); they
+ * then share the device error word, which dflash_reset_seqs clears. */
 DFLASH_API dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, int32_t max_seqs,
                             int32_t max_batch, int32_t max_inject_rows, void* kv_cache, size_t kv_bytes,
                             void* workspace, size_t ws_bytes, dflash_handle** out /* host */);

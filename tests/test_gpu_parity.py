@@ -252,3 +252,52 @@ def test_verify_greedy_block_sizes(K):
     assert 0 in seen and K - 1 in seen
     B.dflash_verify_greedy(0, K, d, t, nacc, ncom, com, nxt)   # empty batch: a no-op
     torch.cuda.synchronize()
+
+
+def test_two_handles_share_kv_on_two_streams(H):
+    """A second handle on the same KV cache (its own workspace) injects a new sequence's whole
+    window on a second stream while the first handle injects accepted rows and drafts for two
+    running sequences on its stream.  Outputs and the whole KV region equal those of the same
+    calls run one after the other on one stream; the new sequence's K/V match the oracle."""
+    import torch
+    cfg = MID
+    case = H.Case(cfg, max_seqs=4, max_batch=2, max_inject_rows=64)
+    dB = B.Drafter(cfg, case.dev_w, max_seqs=4, max_batch=1, max_inject_rows=64, kv_from=case.d)
+    case.reset([0, 1, 2])
+    case.inject([0, 1], [np.arange(0, 50), np.arange(0, 30)])
+    pos2 = np.arange(100, 100 + cfg.window)
+    st2 = synth.target_states(cfg, 2, pos2)
+    states2 = case.states_tensor([st2], len(pos2))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    pool = torch.randn((2, 5, cfg.concat_width), generator=g, device="cuda").to(torch.bfloat16)
+    ids01, nnew01 = case.tensor(np.array([0, 1], np.int32)), case.tensor(np.array([3, 5], np.int32))
+    id2, nnew2 = case.tensor(np.array([2], np.int32)), case.tensor(np.array([len(pos2)], np.int32))
+    sp2 = case.tensor(np.array([pos2[0]], np.int32))
+    anchors = case.tensor(np.array([77, 4000], np.int32))
+    torch.cuda.synchronize()
+    snapshot = case.d.kv.clone()
+
+    def run(two_streams):
+        case.d.kv.copy_(snapshot)
+        out = case.d.outputs(2, logits=True)
+        torch.cuda.synchronize()
+        sa = torch.cuda.Stream()
+        sb = torch.cuda.Stream() if two_streams else sa
+        dB.dflash_inject_kv(id2, nnew2, len(pos2), states2, start_pos=sp2, stream=sb.cuda_stream)
+        case.d.dflash_inject_kv(ids01, nnew01, 5, pool, start_pos=None, stream=sa.cuda_stream)
+        case.d.dflash_draft_block(ids01, anchors, out["topk_ids"], out["topk_logits"], out["h_final"],
+                                  out["logits"], stream=sa.cuda_stream)
+        torch.cuda.synchronize()
+        return {k: v.clone() for k, v in out.items() if v is not None}, case.d.kv.clone()
+
+    seq_out, seq_kv = run(False)
+    par_out, par_kv = run(True)
+    for k in seq_out:
+        assert torch.equal(seq_out[k], par_out[k]), k
+    assert torch.equal(seq_kv, par_kv)
+    O.inject(cfg, case.W64, case.caches[2], pos2, st2.values, H.oracle_mode(cfg))
+    worst, same = H.check_kv(case, [2])
+    H.log(f"[two handles] new sequence K/V: worst rel err {worst:.2e}, bit-equal {same:.4f}")
+    assert worst <= 1.0 and same >= 0.99
+    assert case.d.dflash_get_device_error() == 0
