@@ -458,6 +458,84 @@ def verify_rejection(draft, q_path, cand_ids, q_cand, target_probs, u_accept, u_
     return n, np.array(committed, dtype=np.int64), tok
 
 
+# --------------------------------------------------------------------------------------
+# FP8 weight-only lm_head (a NEXT-step option, not part of the pages' pass)
+# --------------------------------------------------------------------------------------
+# The pages run drafts with quantised weights on one backend ("z-lab/dflash" README mirror,
+# section "MLX (Apple Silicon)": 4-bit draft weights); they fix no format.  The format here
+# is the OCP 8-bit floating point E4M3 encoding (bias 7, 3 mantissa bits, no infinities,
+# largest finite 448, subnormals m * 2^-9), one code per weight, with one power-of-two scale
+# per weight row: the row's largest magnitude maps into (224, 448].  Rounding is to the
+# nearest code, ties to even.  A row whose largest magnitude is below 2^-64 is stored as zero.
+
+E4M3_MAX = 448.0
+FP8_ZERO_ROW = 2.0 ** -64
+
+
+def fp8_row_exponent(amax):
+    """Smallest integer k with amax <= 448 * 2^k (0 for a row stored as zero)."""
+    amax = float(amax)
+    if amax < FP8_ZERO_ROW:
+        return 0
+    k = math.frexp(amax)[1] - 9
+    while amax > math.ldexp(E4M3_MAX, k):
+        k += 1
+    while amax <= math.ldexp(E4M3_MAX, k - 1):
+        k -= 1
+    return k
+
+
+def e4m3_code(x):
+    """E4M3 code (uint8) of the nearest representable value to each x (|x| <= 448, ties to
+    even).  The sign bit of x is kept, so a negative x that rounds to zero gives -0 (0x80)."""
+    x = np.asarray(x, dtype=F64)
+    a = np.abs(x)
+    assert np.all(a <= E4M3_MAX)
+    codes = np.zeros(x.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # subnormals (and zero): multiples of 2^-9; 8 * 2^-9 is the smallest normal, code 0x08
+    codes[sub] = np.rint(a[sub] * 512.0).astype(np.int64)
+    # normals: a = 2^f * mant, mant in [1, 2), f = floor(log2 a); 8 mantissa steps per binade
+    an = a[~sub]
+    f = np.frexp(an)[1] - 1
+    m = np.rint((np.ldexp(an, -f) - 1.0) * 8.0).astype(np.int64)   # 0..8
+    e = f + 7 + (m == 8)
+    m = np.where(m == 8, 0, m)
+    codes[~sub] = (e << 3) | m
+    return (codes | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def e4m3_value(codes):
+    """Value of each E4M3 code (the NaN codes 0x7F / 0xFF are not produced and not accepted)."""
+    c = np.asarray(codes).astype(np.int64)
+    assert not np.any((c & 0x7F) == 0x7F)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, np.ldexp(m.astype(F64), -9), np.ldexp(1.0 + m / 8.0, e - 7))
+    return np.where(c >> 7, -mag, mag)
+
+
+def quantize_fp8_rows(W):
+    """Per-row power-of-two scale and E4M3 codes of a weight matrix W [rows][cols] (the bf16
+    values as float64).  Returns (codes uint8 [rows][cols], scales float64 [rows] = 2^k)."""
+    W = np.asarray(W, dtype=F64)
+    codes = np.zeros(W.shape, dtype=np.uint8)
+    scales = np.ones(W.shape[0], dtype=F64)
+    for r in range(W.shape[0]):
+        amax = float(np.max(np.abs(W[r]))) if W.shape[1] else 0.0
+        if amax < FP8_ZERO_ROW:
+            codes[r] = e4m3_code(np.where(np.signbit(W[r]), -0.0, 0.0))
+            continue
+        k = fp8_row_exponent(amax)
+        scales[r] = math.ldexp(1.0, k)
+        codes[r] = e4m3_code(np.ldexp(W[r], -k))
+    return codes, scales
+
+
+def dequantize_fp8_rows(codes, scales):
+    """The weights the codes stand for: value(code) * scale of the row (exact in float64)."""
+    return e4m3_value(codes) * np.asarray(scales, dtype=F64)[:, None]
+
+
 def expected_tau(match_probs):
     """E[tau] when draft i is accepted with conditional probability r_i given all earlier
     ones were: 1 + sum_i prod_{j<=i} r_j (the bonus token always counts)."""

@@ -659,3 +659,61 @@ def test_rejection_verification_special_cases():
     for u_res, want in ((0.0, 0), (0.3333, 0), (0.3334, 4), (0.99, 4)):
         n, com, nxt = O.verify_rejection([2, 1], [q[0][1], q[1][0]], cand, q, p_u, [0.5, 0.0], u_res)
         assert n == 0 and nxt == want and list(com) == [want, -1, -1]
+
+
+# ---------------------------------------------------------------------------------------------
+# FP8 weight-only lm_head: E4M3 codes and per-row power-of-two scales
+# ---------------------------------------------------------------------------------------------
+
+def test_e4m3_codes_match_torch_float8():
+    """The oracle's E4M3 rounding equals torch's float8_e4m3fn conversion (round to nearest,
+    ties to even) on values with the bf16 significand width, on every midpoint between two
+    neighbouring codes (the ties), and on every code value itself."""
+    import torch
+    rng = np.random.default_rng(8)
+    vals = O.e4m3_value(np.array([c for c in range(256) if (c & 0x7F) != 0x7F]))
+    mids = (vals[:-1] + vals[1:]) / 2
+    mids = mids[np.abs(mids) <= 448]
+    x = rng.uniform(-448, 448, 20000) * np.exp2(-rng.integers(0, 20, 20000))
+    x = O.bf16_round(x)
+    for arr in (x, vals, mids):
+        ours = O.e4m3_code(arr)
+        ref = torch.tensor(arr, dtype=torch.float64).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(ours, ref)
+
+
+def test_e4m3_values_match_torch_float8():
+    import torch
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(O.e4m3_value(codes), ref)
+    assert O.e4m3_value(np.array([0x7E]))[0] == 448.0 and O.e4m3_value(np.array([0x01]))[0] == 2.0 ** -9
+
+
+def test_fp8_rows_scale_and_error_bound():
+    """Each row's largest magnitude lands in (224, 448] after its power-of-two scale; every
+    dequantised weight is within half a code step of the weight (relative 2^-4 for normals,
+    2^-10 absolute for subnormals, scaled); an all-zero row stays zero; signs are kept."""
+    rng = np.random.default_rng(9)
+    W = O.bf16_round(rng.normal(0, 0.02, (40, 256)))
+    W[3] = 0.0
+    W[5] *= 1e-3
+    W[7, :] = -W[7, :]
+    codes, scales = O.quantize_fp8_rows(W)
+    D = O.dequantize_fp8_rows(codes, scales)
+    for r in range(W.shape[0]):
+        amax = np.max(np.abs(W[r]))
+        if amax == 0:
+            assert np.all(D[r] == 0) and scales[r] == 1.0
+            continue
+        a = amax / scales[r]
+        assert 224 < a <= 448, (r, a)
+        x = np.abs(W[r]) / scales[r]
+        step = np.where(x >= 2.0 ** -6, np.exp2(np.floor(np.log2(np.maximum(x, 2.0 ** -6))) - 3), 2.0 ** -9)
+        assert np.all(np.abs(W[r] - D[r]) <= step / 2 * scales[r] * (1 + 1e-12)), r
+        assert np.all((np.sign(D[r]) == np.sign(W[r])) | (D[r] == 0))
+
+
+def test_fp8_row_exponent_closed_form():
+    for amax, k in ((448.0, 0), (448.5, 1), (224.0, -1), (224.0001, 0), (1.0, -8), (0.03125, -13), (0.0, 0)):
+        assert O.fp8_row_exponent(amax) == k, (amax, k)
