@@ -197,12 +197,18 @@ def algorithmic(cfg, tau_mean, n_ctx):
     return dict(bytes=bytes_, flops=fl, lm_head_bytes=lm_bytes, lm_head_flops=2 * B * (K - 1) * V * d)
 
 
-def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10):
+def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=False):
     """Times `steps` steps twice on one stream: (1) replays of a HIP graph holding
     `graph_steps` steps (the headline rate; no events inside the graph), (2) the same number of
     steps launched eagerly, each lm_head launch bracketed by HIP events on that stream (the
     kernel's duration; the eager step rate is reported too)."""
     cyc = Cycle(cfg, seed, torch, cfg.batch)
+    if fp8_lm_head:   # E4M3 codes + per-row power-of-two scales of the lm_head, made on the device
+        lm = cyc.w["lm_head"]
+        cyc.lm8 = (torch.empty(lm.shape, dtype=torch.uint8, device="cuda"),
+                   torch.empty(lm.shape[0], dtype=torch.float32, device="cuda"))
+        cyc.Bd.dflash_quantize_fp8_rows(lm, *cyc.lm8)
+        cyc.d.dflash_set_lm_head_fp8(*cyc.lm8)
     stream = torch.cuda.Stream()
     G = max(1, min(graph_steps, steps))
     while steps % G:
@@ -416,6 +422,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-b32", action="store_true")
     ap.add_argument("--no-overlap", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-lm_head variant of the headline workload")
     ap.add_argument("--no-b1", action="store_true", help="skip the headline workload (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--traffic-probe", action="store_true",
@@ -485,6 +492,20 @@ def main():
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(r["cycle"], budget_s=args.cpu_budget)
         del r["cycle"]
+        if not args.no_fp8:
+            torch.cuda.empty_cache()
+            r8 = run_workload(cfg, args.steps, args.warmup, torch, fp8_lm_head=True)
+            a8 = r8["alg"]
+            lm8_bytes = cfg.vocab * cfg.hidden + cfg.vocab * 4 + cfg.block_size * cfg.hidden * 2
+            out["fp8_lm_head"] = {
+                "workload": "b1_k16 with the lm_head as E4M3 codes and per-row power-of-two scales (weight-only; "
+                            "activations and every other weight bf16)",
+                "blocks_per_s": round(r8["blocks_per_s"], 1), "draft_tokens_per_s": round(r8["draft_tokens_per_s"], 1),
+                "ms_per_step": round(r8["ms_per_step"], 4),
+                "lm_head_avg_ms": round(r8["lm_head_ms"], 5), "lm_head_bytes": int(lm8_bytes),
+                "lm_head_gbps": round(lm8_bytes / (r8["lm_head_ms"] * 1e-3) / 1e9, 1),
+                "lm_head_hbm_frac": round(lm8_bytes / (r8["lm_head_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            del r8["cycle"], a8
     if not args.no_b32:
         c3 = synth.WORKLOADS["b32_k8_conv"]
         torch.cuda.empty_cache()

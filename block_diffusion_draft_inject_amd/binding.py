@@ -82,6 +82,8 @@ def lib():
                                            c_void_p, c_void_p]),
         "dflash_synth_target_argmax": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_float, c_uint64, c_void_p,
                                                  c_void_p, c_void_p]),
+        "dflash_quantize_fp8_rows": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
+        "dflash_set_lm_head_fp8": (c_int32, [H, c_void_p, c_void_p]),
         "dflash_timing_enable": (c_int32, [H, c_int32]),
         "dflash_timing_read": (c_int32, [H, POINTER(c_double), POINTER(c_int32)]),
         "dflash_get_device_error": (c_int32, [H, POINTER(c_int32)]),
@@ -99,7 +101,7 @@ def lib():
 EXPORTED = ("dflash_config_check", "dflash_kv_cache_bytes", "dflash_kv_cache_layout", "dflash_workspace_bytes",
             "dflash_create", "dflash_destroy", "dflash_reset_seqs", "dflash_inject_kv", "dflash_draft_block",
             "dflash_select_path", "dflash_select_sample", "dflash_verify_rejection", "dflash_verify_greedy",
-            "dflash_synth_target_argmax", "dflash_timing_enable",
+            "dflash_synth_target_argmax", "dflash_quantize_fp8_rows", "dflash_set_lm_head_fp8", "dflash_timing_enable",
             "dflash_timing_read", "dflash_get_device_error", "dflash_status_string", "dflash_last_error")
 
 
@@ -168,6 +170,13 @@ def dflash_synth_target_argmax(n_seq, block_size, vocab, draft_ids, match_prob, 
         n_seq, block_size, vocab, ptr(draft_ids), match_prob, seed, ptr(counter), ptr(target_argmax), stream))
 
 
+def dflash_quantize_fp8_rows(src, codes, row_scales, stream=None):
+    """E4M3 codes and per-row power-of-two scales of a bf16 matrix src [rows][cols] (device)."""
+    rows, cols = src.shape
+    check("dflash_quantize_fp8_rows", lib().dflash_quantize_fp8_rows(ptr(src), rows, cols, ptr(codes), ptr(row_scales),
+                                                                     stream))
+
+
 class Drafter:
     """One libdflash handle plus the caller-owned device buffers it borrows.
 
@@ -210,6 +219,11 @@ class Drafter:
                                                    max_inject_rows, self.kv.data_ptr(), self.kv.numel(),
                                                    self.ws.data_ptr(), self.ws.numel(), ctypes.byref(h)))
         self.h = h
+
+    def dflash_set_lm_head_fp8(self, codes, row_scales):
+        """Use E4M3 lm_head codes [V][d] with their row scales [V] (None, None: the bf16 lm_head)."""
+        self._lm_fp8 = (codes, row_scales)   # keep alive
+        check("dflash_set_lm_head_fp8", lib().dflash_set_lm_head_fp8(self.h, ptr(codes), ptr(row_scales)))
 
     def close(self):
         if self.h:

@@ -57,6 +57,8 @@ struct Handle {
   const void* g_A;
   const void* g_B;
   const void* g_WH;
+  const unsigned char* lm_fp8;       // E4M3 lm_head codes [V][d] (NULL: the bf16 lm_head)
+  const float* lm_fp8_scale;         // [V] per-row power-of-two scales
   std::vector<const void*> layers;   // n_layers * DFLASH_LAYER_TENSORS
   int max_seqs, max_batch, max_inject_rows;
   char* kv;
@@ -466,6 +468,9 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
   hipStream_t st = (hipStream_t)stream;
   const bool b = bf(c);
   const int K = c->block_size, d = c->hidden, M = n_seq * K;
+  if (H->lm_fp8 && gemm_plan(true, GEMM_TOPK, M, c->vocab, d).kind != 4)
+    return fail(DFLASH_E_UNSUPPORTED, "the FP8 lm_head takes at most 16 draft rows (n_seq * block_size = %d) and a "
+                "hidden size that is a multiple of 512 up to 2048", M);
   const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
   const WsLayout& W = H->wl;
   float* part = wsp<float>(H, W.part);
@@ -652,6 +657,12 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
     gl.logits = logits;
     gl.counter = counters;
     GemmPlan pl = gemm_plan(b, GEMM_TOPK, M, c->vocab, d);
+    if (H->lm_fp8) {
+      // FP8 lm_head: only the independent-wave kernel (<= 16 rows) takes it (checked up front)
+      gl.seg[0] = H->lm_fp8;
+      gl.ldb = d;                     // bytes per weight row
+      gl.row_scale = H->lm_fp8_scale;
+    }
     HIP_TRY(gemm_launch(b, pl, GEMM_TOPK, gl, st));
     if (ev1) HIP_TRY(hipEventRecord(ev1, st));
     ma.ncand = pl.groups * TOPK;
@@ -736,6 +747,24 @@ dflash_status dflash_verify_greedy(int32_t n_seq, int32_t block_size, const int3
     return fail(DFLASH_E_INVALID, "NULL draft_ids, target_argmax, n_accepted, committed or next_anchor");
   VerifyArgs va{n_seq, block_size, draft_ids, target_argmax, n_accepted, n_commit, committed, next_anchor};
   HIP_TRY(launch_verify(va, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_quantize_fp8_rows(const void* src, int32_t rows, int32_t cols, uint8_t* codes, float* row_scales,
+                                      void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 8) return fail(DFLASH_E_SHAPE, "rows must be >= 0 and cols a positive multiple of 8");
+  if (rows > 0 && (!src || !codes || !row_scales)) return fail(DFLASH_E_INVALID, "NULL src, codes or row_scales");
+  HIP_TRY(launch_quantize_fp8_rows(src, rows, cols, codes, row_scales, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t* codes, const float* row_scales) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  if (!codes != !row_scales) return fail(DFLASH_E_INVALID, "codes and row_scales must both be set or both be NULL");
+  if (codes && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "the FP8 lm_head is for bf16 drafters");
+  H->lm_fp8 = codes;
+  H->lm_fp8_scale = row_scales;
   return DFLASH_OK;
 }
 

@@ -16,6 +16,8 @@
 //    lists, merged at the end of the workgroup) over a contiguous range of column tiles and
 //    writes one partial list per (row, workgroup); the full-logit matrix is never stored
 //    unless requested for checking.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -514,10 +516,52 @@ __device__ __forceinline__ void lw_mma(const LwBatch& x, const bf16 (*sa)[LW_LD]
   }
 }
 
+// FP8 weights (row_scale set): one byte per weight, so a batch carries 8 chunks of 64 k, each a
+// single 16-byte load per lane: k = 16 kg .. 16 kg + 15 of the chunk.  The codes become bf16
+// weights code * scale in registers (v_cvt_scalef32_pk_bf16_fp8, exact: an E4M3 value times a
+// power of two fits bf16), and the two MFMA halves take k = 16 kg + 8 h .. +7; the activations
+// are read from LDS in the same k order, so the sum is unchanged.
+constexpr int LW_CH8 = 8;
+struct LwBatch8 {
+  u32x4 q[LW_CH8];
+  float s;                          // the row's scale
+};
+
+__device__ __forceinline__ void lw_load8(LwBatch8& x, const unsigned char* row, const float* scale, int k0,
+                                         int kg) {
+#pragma unroll
+  for (int c = 0; c < LW_CH8; ++c) x.q[c] = *reinterpret_cast<const u32x4*>(row + k0 + c * 64 + kg * 16);
+  x.s = *scale;
+}
+
+// eight E4M3 codes (two words, lowest byte first) -> eight bf16 values code * s
+__device__ __forceinline__ bf16x8 fp8x8_bf16(unsigned w0, unsigned w1, float s) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false));
+  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true));
+  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false));
+  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true));
+  return as_bf16x8(o);
+}
+
+__device__ __forceinline__ void lw_mma8(const LwBatch8& x, const bf16 (*sa)[LW_LD], int k0, int li, int kg,
+                                        f32x4& acc0, f32x4& acc1) {
+#pragma unroll
+  for (int c = 0; c < LW_CH8; ++c) {
+    const int k = k0 + c * 64 + kg * 16;
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sa[li][k]);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sa[li][k + 8]);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, fp8x8_bf16(x.q[c][0], x.q[c][1], x.s), acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, fp8x8_bf16(x.q[c][2], x.q[c][3], x.s), acc1, 0, 0, 0);
+  }
+}
+
 // LOGITS: the full logits are written too (a global store in the fragment loop; kept out of
 // the instantiation without them, where it would make the compiler's load waits coarser)
-template <bool LOGITS>
+template <bool LOGITS, bool FP8 = false>
 __global__ __launch_bounds__(LW_W * 64, 2) void lmhead_topk_wave(GemmParams p) {
+  using Batch = typename std::conditional<FP8, LwBatch8, LwBatch>::type;
+  constexpr int CH = FP8 ? LW_CH8 : LW_CH;
   __shared__ __align__(16) unsigned char lw_smem[LW_SMEM];
   bf16 (*sa)[LW_LD] = reinterpret_cast<bf16 (*)[LW_LD]>(lw_smem);                         // [row][k]
   float (*fb)[16][17] = reinterpret_cast<float (*)[16][17]>(lw_smem + 16 * LW_LD * 2);    // [wave][row][col]
@@ -550,16 +594,14 @@ __global__ __launch_bounds__(LW_W * 64, 2) void lmhead_topk_wave(GemmParams p) {
   }
   __syncthreads();
   const int nfrag = (p.N + 15) / 16;
-  const int ncb = K / (64 * LW_CH);               // batches per fragment
+  const int ncb = K / (64 * CH);                  // batches per fragment
   const int TW = gridDim.x * LW_W;
   const int my_row = lane >> 2, my_sub = lane & 3;   // epilogue: lane handles row my_row, cols 4 sub..+3
   const bool row_live = my_row < Mv && (my_row % p.block) != 0;
   Top16 top;
   top.init();
-  auto rowp = [&](int frag) {
-    const int n = min(min(frag, nfrag - 1) * 16 + li, p.N - 1);
-    return reinterpret_cast<const bf16*>(p.seg[0]) + (size_t)n * p.ldb;
-  };
+  auto rown = [&](int frag) { return min(min(frag, nfrag - 1) * 16 + li, p.N - 1); };
+  auto rowp = [&](int frag) { return reinterpret_cast<const bf16*>(p.seg[0]) + (size_t)rown(frag) * p.ldb; };
   // epilogue of one fragment: the wave's 16 x 16 tile through its own LDS slot; lane (row,
   // quarter) scans 4 columns into its list
   auto epilogue = [&](int f, const f32x4& acc) {
@@ -589,14 +631,21 @@ __global__ __launch_bounds__(LW_W * 64, 2) void lmhead_topk_wave(GemmParams p) {
   // finishes (or to one past the end, whose columns the epilogue skips), so it changes nothing
   const int T = ((f0 < nfrag ? (nfrag - 1 - f0) / TW + 1 : 0) * ncb + LW_NB - 1) / LW_NB * LW_NB;
   int lf = f0, lcb = 0;
-  auto issue = [&](LwBatch& b) {
-    lw_load(b, rowp(lf), lcb * 64 * LW_CH, kg);
+  auto issue = [&](Batch& b) {
+    if constexpr (FP8)
+      lw_load8(b, reinterpret_cast<const unsigned char*>(p.seg[0]) + (size_t)rown(lf) * p.ldb, p.row_scale + rown(lf),
+               lcb * 64 * CH, kg);
+    else
+      lw_load(b, rowp(lf), lcb * 64 * CH, kg);
     if (++lcb == ncb) { lcb = 0; lf += TW; }
   };
   int cf = f0, ccb = 0;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  auto step = [&](const LwBatch& b) {
-    lw_mma(b, sa, ccb * 64 * LW_CH, li, kg, acc0, acc1);
+  auto step = [&](const Batch& b) {
+    if constexpr (FP8)
+      lw_mma8(b, sa, ccb * 64 * CH, li, kg, acc0, acc1);
+    else
+      lw_mma(b, sa, ccb * 64 * CH, li, kg, acc0, acc1);
     if (++ccb == ncb) {
       epilogue(cf, acc0 + acc1);
       acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -606,7 +655,7 @@ __global__ __launch_bounds__(LW_W * 64, 2) void lmhead_topk_wave(GemmParams p) {
     }
   };
   // batch i's loads strictly before batch i+1's: the compiler's in-order wait counts rely on it
-  LwBatch b[LW_NB];
+  Batch b[LW_NB];
 #pragma unroll
   for (int i = 0; i + 1 < LW_NB; ++i) {
     issue(b[i]);
@@ -813,8 +862,13 @@ hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hi
   }
   if (pl.kind == 4) {
     if (p.seg_rows < p.N) return hipErrorInvalidValue;   // one weight segment
-    if (p.logits) hipLaunchKernelGGL(lmhead_topk_wave<true>, pl.grid, dim3(LW_W * 64), 0, st, p);
-    else hipLaunchKernelGGL(lmhead_topk_wave<false>, pl.grid, dim3(LW_W * 64), 0, st, p);
+    if (p.row_scale) {
+      if (p.logits) hipLaunchKernelGGL((lmhead_topk_wave<true, true>), pl.grid, dim3(LW_W * 64), 0, st, p);
+      else hipLaunchKernelGGL((lmhead_topk_wave<false, true>), pl.grid, dim3(LW_W * 64), 0, st, p);
+    } else {
+      if (p.logits) hipLaunchKernelGGL((lmhead_topk_wave<true, false>), pl.grid, dim3(LW_W * 64), 0, st, p);
+      else hipLaunchKernelGGL((lmhead_topk_wave<false, false>), pl.grid, dim3(LW_W * 64), 0, st, p);
+    }
     return hipGetLastError();
   }
   if (pl.kind == 3) {

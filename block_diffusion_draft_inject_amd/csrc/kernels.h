@@ -37,6 +37,8 @@ struct GemmParams {
   int groups;
   int block;
   float* logits;          // optional full logits [row/block][block-1][N] for slots >= 1
+  const float* row_scale; // FP8 lm_head (<= 16 rows): the weights are E4M3 codes [N][ldb bytes],
+                          // weight row n stands for code * row_scale[n]
   int* counter;           // TOPK skinny (17..64 rows): per-row-tile fragment counters, zero before the launch
 };
 

@@ -212,5 +212,7 @@ hipError_t launch_select(bool bf, const SelectArgs& a, int n_seq, hipStream_t st
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_verify_rejection(const RejectArgs& a, hipStream_t st);
 hipError_t launch_synth(const SynthArgs& a, hipStream_t st);
+hipError_t launch_quantize_fp8_rows(const void* src, int rows, int cols, unsigned char* codes, float* scales,
+                                    hipStream_t st);
 
 }  // namespace dfl

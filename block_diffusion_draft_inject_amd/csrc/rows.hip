@@ -918,4 +918,81 @@ hipError_t launch_topk_merge(const MergeArgs& a, int out_rows, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------ FP8 weight rows
+// E4M3 codes (OCP 8-bit floating point: bias 7, 3 mantissa bits, largest finite 448,
+// subnormals m * 2^-9) of a bf16 weight matrix, one power-of-two scale per row: the row's
+// largest magnitude a maps into (224, 448] (scale = 2^k, k the smallest integer with
+// a <= 448 * 2^k), each weight becomes the code nearest to w / 2^k (ties to even), its sign
+// kept.  Rows with a below 2^-64 are stored as zero codes with scale 1.  w / 2^k is exact
+// (a power-of-two scaling of a bf16 value) and every rounding step below is an exact
+// operation or rintf, so the codes do not depend on the order of any arithmetic.
+// One workgroup per row, 8 weights (16 bytes) per thread per step.
+__device__ __forceinline__ unsigned e4m3_code(float w, int k) {
+  const float x = ldexpf(fabsf(w), -k);
+  unsigned code;
+  if (x < 0x1p-6f) {
+    const int m = (int)rintf(x * 512.f);          // subnormal steps of 2^-9; 8 -> the smallest normal
+    code = (unsigned)m;                             // m == 8 is code 0x08 (exponent 1, mantissa 0)
+  } else {
+    int e;
+    frexpf(x, &e);                                  // x = f 2^e, f in [0.5, 1): floor(log2 x) = e - 1
+    int m = (int)rintf((ldexpf(x, 1 - e) - 1.f) * 8.f);   // 0..8
+    int E = e - 1 + 7;
+    if (m == 8) { m = 0; ++E; }
+    code = ((unsigned)E << 3) | (unsigned)m;
+  }
+  return code | ((__float_as_uint(w) >> 31) << 7);
+}
+
+__global__ __launch_bounds__(256) void quantize_fp8_rows_kernel(const bf16* src, int cols, unsigned char* codes,
+                                                                float* scales) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const bf16* row = src + (size_t)r * cols;
+  float amax = 0.f;
+  for (int c8 = tid; c8 < cols / 8; c8 += 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(row + c8 * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(v[j] << 16)), fabsf(__uint_as_float(v[j] & 0xffff0000u))));
+  }
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const bool zero = !(amax >= 0x1p-64f);
+  int k = 0;
+  if (!zero) {
+    int e;
+    frexpf(amax, &e);
+    k = e - 9;
+    while (amax > ldexpf(448.f, k)) ++k;
+    while (amax <= ldexpf(448.f, k - 1)) --k;
+  }
+  if (tid == 0) scales[r] = zero ? 1.f : ldexpf(1.f, k);
+  unsigned char* out = codes + (size_t)r * cols;
+  for (int c8 = tid; c8 < cols / 8; c8 += 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(row + c8 * 8);
+    uint2 o;
+    unsigned b[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float w0 = __uint_as_float(v[j] << 16), w1 = __uint_as_float(v[j] & 0xffff0000u);
+      b[2 * j] = zero ? ((__float_as_uint(w0) >> 31) << 7) : e4m3_code(w0, k);
+      b[2 * j + 1] = zero ? ((__float_as_uint(w1) >> 31) << 7) : e4m3_code(w1, k);
+    }
+    o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    *reinterpret_cast<uint2*>(out + c8 * 8) = o;
+  }
+}
+
+hipError_t launch_quantize_fp8_rows(const void* src, int rows, int cols, unsigned char* codes, float* scales,
+                                    hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_fp8_rows_kernel, dim3(rows), dim3(256), 0, st, reinterpret_cast<const bf16*>(src), cols,
+                     codes, scales);
+  return hipGetLastError();
+}
+
 }  // namespace dfl

@@ -251,6 +251,23 @@ DFLASH_API dflash_status dflash_verify_greedy(int32_t n_seq, int32_t block_size,
                                    const int32_t* target_argmax, int32_t* n_accepted, int32_t* n_commit,
                                    int32_t* committed, int32_t* next_anchor, void* stream);
 
+/* FP8 weight-only lm_head (an option beside the bf16 pass; the pages run drafts with quantised
+ * weights on one backend, "z-lab/dflash" README mirror, section "MLX (Apple Silicon)", and fix no
+ * format).  dflash_quantize_fp8_rows writes, for a bf16 matrix src [rows][cols] (device, cols a
+ * positive multiple of 8), the OCP FP8 E4M3 code of every weight (codes [rows][cols], device,
+ * caller-owned) and one power-of-two scale per row (row_scales [rows] fp32, device): with a the
+ * row's largest magnitude, scale = 2^k for the smallest integer k with a <= 448 * 2^k, and each
+ * code is the E4M3 value nearest to w / scale (ties to even; the sign of w kept, so -0 is 0x80).
+ * A row with a < 2^-64 gets zero codes and scale 1.  Asynchronous on stream; no allocation.
+ * dflash_set_lm_head_fp8 makes a handle's dflash_draft_block read the shared lm_head as those codes
+ * times their row scales (exact in bf16) instead of the bf16 matrix; NULL for both reverts to bf16.
+ * The codes are borrowed like the weights.  Supported by the batch-1 kernel only: a draft call with
+ * more than 16 rows (n_seq * block_size) or a hidden size that is not a multiple of 512 up to 2048
+ * then returns DFLASH_E_UNSUPPORTED. */
+DFLASH_API dflash_status dflash_quantize_fp8_rows(const void* src, int32_t rows, int32_t cols, uint8_t* codes,
+                                                  float* row_scales, void* stream);
+DFLASH_API dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t* codes, const float* row_scales);
+
 /* Benchmark workload helper, not part of the drafter: stands in for a target model's verify
  * pass.  For i = 1..K-1, g_{i-1} = d_i with probability match_prob, else a different token;
  * g_{K-1} is uniform.  Randomness: splitmix64 of (seed, *counter, sequence, slot); *counter

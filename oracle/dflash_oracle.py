@@ -518,17 +518,12 @@ def quantize_fp8_rows(W):
     """Per-row power-of-two scale and E4M3 codes of a weight matrix W [rows][cols] (the bf16
     values as float64).  Returns (codes uint8 [rows][cols], scales float64 [rows] = 2^k)."""
     W = np.asarray(W, dtype=F64)
-    codes = np.zeros(W.shape, dtype=np.uint8)
-    scales = np.ones(W.shape[0], dtype=F64)
-    for r in range(W.shape[0]):
-        amax = float(np.max(np.abs(W[r]))) if W.shape[1] else 0.0
-        if amax < FP8_ZERO_ROW:
-            codes[r] = e4m3_code(np.where(np.signbit(W[r]), -0.0, 0.0))
-            continue
-        k = fp8_row_exponent(amax)
-        scales[r] = math.ldexp(1.0, k)
-        codes[r] = e4m3_code(np.ldexp(W[r], -k))
-    return codes, scales
+    amax = np.max(np.abs(W), axis=1) if W.shape[1] else np.zeros(W.shape[0])
+    zero = amax < FP8_ZERO_ROW
+    k = np.array([fp8_row_exponent(a) for a in amax], dtype=np.int64)
+    scales = np.where(zero, 1.0, np.ldexp(1.0, k))
+    X = np.where(zero[:, None], np.where(np.signbit(W), -0.0, 0.0), np.ldexp(W, -k[:, None]))
+    return e4m3_code(X), scales
 
 
 def dequantize_fp8_rows(codes, scales):

@@ -301,3 +301,65 @@ def test_two_handles_share_kv_on_two_streams(H):
     H.log(f"[two handles] new sequence K/V: worst rel err {worst:.2e}, bit-equal {same:.4f}")
     assert worst <= 1.0 and same >= 0.99
     assert case.d.dflash_get_device_error() == 0
+
+
+def _quantize_on_gpu(lm):
+    import torch
+    codes = torch.empty(lm.shape, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(lm.shape[0], dtype=torch.float32, device="cuda")
+    B.dflash_quantize_fp8_rows(lm, codes, scales)
+    torch.cuda.synchronize()
+    return codes, scales
+
+
+def test_fp8_quantizer_matches_oracle():
+    """E4M3 codes and row scales, bit-exact against the oracle: ordinary rows, an all-zero row,
+    a row of -0, a row below the zero-row threshold, a row of large values, a row of exact ties
+    (midpoints between codes), a row with subnormal codes, alternating signs."""
+    import torch
+    rng = np.random.default_rng(21)
+    W = rng.normal(0, 0.02, (300, 512))
+    W[0] = 0.0
+    W[1] = -0.0
+    W[2] *= 1e-20
+    W[3] *= 1e6
+    vals = O.e4m3_value(np.arange(0, 0x7E, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    W[4] = np.resize(mids, 512) * 2.0 ** -10
+    W[4, 0] = 448 * 2.0 ** -10                     # the row's scale is 2^-10, the midpoints stay ties
+    W[5] = rng.normal(0, 1e-6, 512)
+    W[5, 7] = 0.4                                  # everything else lands on subnormal codes
+    W[6, ::2] = -W[6, ::2]
+    Wb = O.bf16_round(W)
+    dev = torch.tensor(Wb, dtype=torch.float32).to(torch.bfloat16).cuda()
+    codes, scales = _quantize_on_gpu(dev)
+    oc, osc = O.quantize_fp8_rows(Wb)
+    assert np.array_equal(scales.cpu().numpy(), osc.astype(np.float32))
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.all(oc[0] == 0) and np.all(oc[1] == 0x80)
+
+
+def test_mid_bf16_fp8_lm_head(H):
+    """Batch 1, K=16 with the FP8 lm_head: codes as the oracle's, logits and top-16 against the
+    oracle run with the dequantised lm_head, top-16 with and without full logits; a call with
+    more than 16 rows is refused; NULL codes restore the bf16 lm_head."""
+    import torch
+    case = H.Case(MID, max_seqs=2, max_batch=2, max_inject_rows=64)
+    _prefill(case, [1], [(0, 50)])
+    codes, scales = _quantize_on_gpu(case.dev_w["lm_head"])
+    oc, osc = O.quantize_fp8_rows(case.W64["lm_head"])
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), osc.astype(np.float32))
+    case.d.dflash_set_lm_head_fp8(codes, scales)
+    bf16_lm = case.W64["lm_head"]
+    case.W64["lm_head"] = O.dequantize_fp8_rows(oc, osc)
+    try:
+        res = _check(H, case, [1], [123], mode_names=("viterbi",))
+        _same_topk_without_logits(case, [1], [123], res)
+    finally:
+        case.W64["lm_head"] = bf16_lm
+    with pytest.raises(B.DflashError):
+        case.draft([1, 0], [123, 5])               # 32 rows
+    case.d.dflash_set_lm_head_fp8(None, None)
+    res = case.draft([1], [123], logits=True)
+    err, _ = H.check_draft(case, [1], [123], res)
+    assert err <= H.LOGIT_TOL["bf16"]

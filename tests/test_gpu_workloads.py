@@ -289,3 +289,33 @@ def test_injection_200_rows_wide_tiles(H, big):
     assert worst <= 1.0 and same >= 0.99
     assert np.array_equal(run.lengths(ids), np.array([1000 * s + 47 for s in ids]))
     assert run.d.dflash_get_device_error() == 0
+
+
+def test_b1_k16_fp8_lm_head(H, big):
+    """The b1_k16 drafter with the FP8 lm_head (151936 x 2048 E4M3 codes): codes and scales as
+    the oracle's, then a full-window draft against the oracle run with the dequantised lm_head."""
+    import torch
+    cfg = synth.WORKLOADS["b1_k16"]
+    lm = big["dev"]["lm_head"]
+    codes = torch.empty(lm.shape, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(lm.shape[0], dtype=torch.float32, device="cuda")
+    B.dflash_quantize_fp8_rows(lm, codes, scales)
+    torch.cuda.synchronize()
+    oc, osc = O.quantize_fp8_rows(big["W64"]["lm_head"])
+    assert np.array_equal(scales.cpu().numpy(), osc.astype(np.float32))
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    run = Run(H, big, cfg, max_seqs=1, max_batch=1, max_inject_rows=1024, sampled=[0])
+    run.d.dflash_set_lm_head_fp8(codes, scales)
+    bf16_lm = big["W64"]["lm_head"]
+    big["W64"]["lm_head"] = O.dequantize_fp8_rows(oc, osc)
+    del oc
+    try:
+        run.d.dflash_reset_seqs(run.t(np.zeros(1, dtype=np.int32)))
+        run.inject([0], [_window(cfg.context[0], cfg.window)])
+        anchors = synth.anchors(cfg).tolist()
+        res = run.draft([0], anchors)
+        run.own_logit_topk(res)
+        run.compare_sampled([0], anchors, res)
+    finally:
+        big["W64"]["lm_head"] = bf16_lm
+    assert run.d.dflash_get_device_error() == 0
