@@ -342,7 +342,7 @@ def recorded_traffic(workload):
 # ----------------------------------------------------------------------------- counter passes
 
 COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
-LM_KERNEL = "lmhead_topk_wave<false>"   # lm_head + top-16 at batch 1 (independent waves, no full-logit store)
+LM_KERNEL = "lmhead_topk_wave<false, false>"   # lm_head + top-16 at batch 1 (independent waves, bf16 weights, no full-logit store)
 
 
 def traffic_probe(steps, torch):
