@@ -489,7 +489,8 @@ constexpr size_t LW_SMEM = (size_t)16 * LW_LD * 2 + (size_t)LW_W * 16 * 17 * 4; 
 static_assert(2 * 16 * 32 * (TOPK + 1) * 4 <= LW_SMEM, "the merge lists overlay the activation rows");
 
 constexpr int LW_CH = 4;            // chunks of 64 k per batch
-constexpr int LW_NB = 3;            // batches in rotation (LW_NB - 1 in flight)
+constexpr int LW_NB = 4;            // batches in rotation (LW_NB - 1 in flight; 3 measured 1.5% slower,
+                                    // 5 no faster and spills in the FP8 and full-logit kernels)
 struct LwBatch {
   u32x4 b[LW_CH][2];                // LW_CH chunks x (k halves 0..31 / 32..63 of the chunk)
 };
