@@ -197,7 +197,7 @@ def algorithmic(cfg, tau_mean, n_ctx):
     return dict(bytes=bytes_, flops=fl, lm_head_bytes=lm_bytes, lm_head_flops=2 * B * (K - 1) * V * d)
 
 
-def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=False):
+def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=False, fp8_mlp=False):
     """Times `steps` steps twice on one stream: (1) replays of a HIP graph holding
     `graph_steps` steps (the headline rate; no events inside the graph), (2) the same number of
     steps launched eagerly, each lm_head launch bracketed by HIP events on that stream (the
@@ -209,6 +209,17 @@ def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=
                    torch.empty(lm.shape[0], dtype=torch.float32, device="cuda"))
         cyc.Bd.dflash_quantize_fp8_rows(lm, *cyc.lm8)
         cyc.d.dflash_set_lm_head_fp8(*cyc.lm8)
+    if fp8_mlp:       # E4M3 codes of every layer's stacked [gate; up] and down matrices
+        cyc.mlp8 = []
+        for l, lw in enumerate(cyc.w["layers"]):
+            out = []
+            for mat in (torch.cat([lw["w_gate"], lw["w_up"]]).contiguous(), lw["w_down"]):
+                out += [torch.empty(mat.shape, dtype=torch.uint8, device="cuda"),
+                        torch.empty(mat.shape[0], dtype=torch.float32, device="cuda")]
+                cyc.Bd.dflash_quantize_fp8_rows(mat, out[-2], out[-1])
+            cyc.d.dflash_set_mlp_fp8(l, *out)
+            cyc.mlp8.append(out)
+        torch.cuda.synchronize()
     stream = torch.cuda.Stream()
     G = max(1, min(graph_steps, steps))
     while steps % G:
@@ -506,6 +517,14 @@ def main():
                 "lm_head_gbps": round(lm8_bytes / (r8["lm_head_ms"] * 1e-3) / 1e9, 1),
                 "lm_head_hbm_frac": round(lm8_bytes / (r8["lm_head_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
             del r8["cycle"], a8
+            torch.cuda.empty_cache()
+            r9 = run_workload(cfg, args.steps, args.warmup, torch, fp8_lm_head=True, fp8_mlp=True)
+            out["fp8_lm_head_mlp"] = {
+                "workload": "b1_k16 with E4M3 codes (per-row power-of-two scales) for the lm_head and every layer's "
+                            "gate/up and down matrices (weight-only; activations and the other weights bf16)",
+                "blocks_per_s": round(r9["blocks_per_s"], 1), "draft_tokens_per_s": round(r9["draft_tokens_per_s"], 1),
+                "ms_per_step": round(r9["ms_per_step"], 4)}
+            del r9["cycle"]
     if not args.no_b32:
         c3 = synth.WORKLOADS["b32_k8_conv"]
         torch.cuda.empty_cache()

@@ -84,6 +84,7 @@ def lib():
                                                  c_void_p, c_void_p]),
         "dflash_quantize_fp8_rows": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
         "dflash_set_lm_head_fp8": (c_int32, [H, c_void_p, c_void_p]),
+        "dflash_set_mlp_fp8": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_timing_enable": (c_int32, [H, c_int32]),
         "dflash_timing_read": (c_int32, [H, POINTER(c_double), POINTER(c_int32)]),
         "dflash_get_device_error": (c_int32, [H, POINTER(c_int32)]),
@@ -101,7 +102,8 @@ def lib():
 EXPORTED = ("dflash_config_check", "dflash_kv_cache_bytes", "dflash_kv_cache_layout", "dflash_workspace_bytes",
             "dflash_create", "dflash_destroy", "dflash_reset_seqs", "dflash_inject_kv", "dflash_draft_block",
             "dflash_select_path", "dflash_select_sample", "dflash_verify_rejection", "dflash_verify_greedy",
-            "dflash_synth_target_argmax", "dflash_quantize_fp8_rows", "dflash_set_lm_head_fp8", "dflash_timing_enable",
+            "dflash_synth_target_argmax", "dflash_quantize_fp8_rows", "dflash_set_lm_head_fp8", "dflash_set_mlp_fp8",
+            "dflash_timing_enable",
             "dflash_timing_read", "dflash_get_device_error", "dflash_status_string", "dflash_last_error")
 
 
@@ -224,6 +226,15 @@ class Drafter:
         """Use E4M3 lm_head codes [V][d] with their row scales [V] (None, None: the bf16 lm_head)."""
         self._lm_fp8 = (codes, row_scales)   # keep alive
         check("dflash_set_lm_head_fp8", lib().dflash_set_lm_head_fp8(self.h, ptr(codes), ptr(row_scales)))
+
+    def dflash_set_mlp_fp8(self, layer, gate_up_codes, gate_up_scales, down_codes, down_scales):
+        """Use E4M3 codes for layer's MLP: stacked [gate; up] [2 ffn][d] and down [d][ffn], with row
+        scales (all None: the bf16 matrices)."""
+        if not hasattr(self, "_mlp_fp8"):
+            self._mlp_fp8 = {}
+        self._mlp_fp8[layer] = (gate_up_codes, gate_up_scales, down_codes, down_scales)   # keep alive
+        check("dflash_set_mlp_fp8", lib().dflash_set_mlp_fp8(self.h, layer, ptr(gate_up_codes), ptr(gate_up_scales),
+                                                             ptr(down_codes), ptr(down_scales)))
 
     def close(self):
         if self.h:

@@ -59,6 +59,11 @@ struct Handle {
   const void* g_WH;
   const unsigned char* lm_fp8;       // E4M3 lm_head codes [V][d] (NULL: the bf16 lm_head)
   const float* lm_fp8_scale;         // [V] per-row power-of-two scales
+  struct Fp8Mlp {                    // per layer: E4M3 [gate; up] [2 ffn][d] and down [d][ffn] codes
+    const unsigned char *gu, *dn;    // with their row scales (NULL: the bf16 matrices)
+    const float *gu_s, *dn_s;
+  };
+  std::vector<Fp8Mlp> mlp_fp8;
   std::vector<const void*> layers;   // n_layers * DFLASH_LAYER_TENSORS
   int max_seqs, max_batch, max_inject_rows;
   char* kv;
@@ -468,6 +473,12 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
   hipStream_t st = (hipStream_t)stream;
   const bool b = bf(c);
   const int K = c->block_size, d = c->hidden, M = n_seq * K;
+  bool any_mlp_fp8 = false;
+  for (const auto& m : H->mlp_fp8) any_mlp_fp8 |= m.gu != nullptr;
+  if (any_mlp_fp8 && (gemm_plan(true, GEMM_SWIGLU, M, 2 * c->ffn, d).kind != 3 ||
+                      gemm_plan(true, GEMM_PARTIAL, M, d, c->ffn).kind != 3))
+    return fail(DFLASH_E_UNSUPPORTED, "FP8 MLP weights take at most 16 draft rows (n_seq * block_size = %d) and a "
+                "hidden size of at most 2048", M);
   if (H->lm_fp8 && gemm_plan(true, GEMM_TOPK, M, c->vocab, d).kind != 4)
     return fail(DFLASH_E_UNSUPPORTED, "the FP8 lm_head takes at most 16 draft rows (n_seq * block_size = %d) and a "
                 "hidden size that is a multiple of 512 up to 2048", M);
@@ -591,6 +602,14 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
     gg.out = act_s;
     gg.out_plane = Mmax * c->ffn;
     gg.part = part;
+    const Handle::Fp8Mlp* m8 = (size_t)l < H->mlp_fp8.size() && H->mlp_fp8[l].gu ? &H->mlp_fp8[l] : nullptr;
+    if (m8) {   // one stacked [gate; up] segment of E4M3 codes (checked up front: the stream kernel)
+      gg.seg[0] = m8->gu;
+      gg.seg[1] = nullptr;
+      gg.seg_rows = 2 * c->ffn;
+      gg.ldb = d;
+      gg.row_scale = m8->gu_s;
+    }
     if (b && M <= 64) {
       GemmPlan pg = gemm_plan(b, GEMM_SWIGLU, M, 2 * c->ffn, d);
       HIP_TRY(gemm_launch(b, pg, GEMM_SWIGLU, gg, st));
@@ -607,6 +626,11 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
     gd.seg[0] = LW(H, l, DFLASH_L_W_DOWN);
     gd.seg_rows = d;
     gd.part = part;
+    if (m8) {
+      gd.seg[0] = m8->dn;
+      gd.ldb = c->ffn;
+      gd.row_scale = m8->dn_s;
+    }
     GemmPlan pd = gemm_plan(b, GEMM_PARTIAL, M, d, c->ffn);
     HIP_TRY(gemm_launch(b, pd, GEMM_PARTIAL, gd, st));
     RowArgs rm = ra;
@@ -765,6 +789,19 @@ dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t* codes, con
   if (codes && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "the FP8 lm_head is for bf16 drafters");
   H->lm_fp8 = codes;
   H->lm_fp8_scale = row_scales;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_set_mlp_fp8(dflash_handle* h, int32_t layer, const uint8_t* gate_up_codes,
+                                const float* gate_up_scales, const uint8_t* down_codes, const float* down_scales) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  if (layer < 0 || layer >= H->cfg.n_layers) return fail(DFLASH_E_INVALID, "layer %d outside [0, n_layers)", layer);
+  const int set = !!gate_up_codes + !!gate_up_scales + !!down_codes + !!down_scales;
+  if (set != 0 && set != 4) return fail(DFLASH_E_INVALID, "all four pointers set, or all NULL");
+  if (set && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "FP8 weights are for bf16 drafters");
+  if (H->mlp_fp8.size() < (size_t)H->cfg.n_layers) H->mlp_fp8.resize(H->cfg.n_layers, Handle::Fp8Mlp{});
+  H->mlp_fp8[layer] = Handle::Fp8Mlp{gate_up_codes, down_codes, gate_up_scales, down_scales};
   return DFLASH_OK;
 }
 

@@ -28,6 +28,17 @@ namespace dfl {
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
+// FP8 weights (row_scale set): eight E4M3 codes (two words, lowest byte first) -> eight bf16
+// values code * s, exact (an E4M3 value times a power of two fits bf16)
+__device__ __forceinline__ bf16x8 fp8x8_bf16(unsigned w0, unsigned w1, float s) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false));
+  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true));
+  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false));
+  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true));
+  return as_bf16x8(o);
+}
+
 // ---------------------------------------------------------------------------------------
 // skinny: accumulate one wave tile of (16*MT rows) x (16*NF cols) over chunks
 // c = c0, c0 + cstep, ... < c1 (chunk = 64 k values).  Software-pipelined: the loads of the
@@ -291,6 +302,14 @@ template <int SLC, int NF>
 struct StreamBuf {
   u32x4 b[SLC][NF][2];
 };
+// FP8 weights: one 16-byte load per lane per 64-k chunk, k = 16 kg .. 16 kg + 15 (the MFMA
+// halves take k = 16 kg + 8 h .. +7; the activations are held in the same k order), plus the
+// lane's row scale.  One weight segment (stacked copies for QKV-like and gate/up matrices).
+template <int SLC, int NF>
+struct StreamBuf8 {
+  u32x4 q[SLC][NF];
+  float s[NF];
+};
 
 // SWIGLU fragments interleave the two halves: lanes li < 8 take gate rows 8f .. 8f + 7, lanes
 // li >= 8 the matching up rows half + 8f .. (so the epilogue pairs lane li with lane li + 8).
@@ -328,6 +347,43 @@ __device__ __forceinline__ void stream_load(StreamBuf<SLC, NF>& x, const GemmPar
   }
 }
 
+template <int SLC, int NF, bool GLU>
+__device__ __forceinline__ void stream_load8(StreamBuf8<SLC, NF>& x, const GemmParams& p, int ncols, int f, int kw,
+                                             int kg, int li) {
+#pragma unroll
+  for (int nf = 0; nf < NF; ++nf) {
+    int n;
+    if (GLU) {
+      const int g0 = f * 8, j = min(g0 + (li & 7), ncols - 1) - g0;
+      n = (li < 8 ? g0 : p.half + g0) + j;
+    } else {
+      n = min(f * 16 + li, ncols - 1) + nf * p.half;
+    }
+    const unsigned char* row = reinterpret_cast<const unsigned char*>(p.seg[0]) + (size_t)n * p.ldb;
+#pragma unroll
+    for (int c = 0; c < SLC; ++c) x.q[c][nf] = *reinterpret_cast<const u32x4*>(row + min(kw + c * 64, p.K - 64) + kg * 16);
+    x.s[nf] = p.row_scale[n];
+  }
+}
+
+template <int SLC, int NF>
+__device__ __forceinline__ void stream_mma8(const StreamBuf8<SLC, NF>& x, const u32x4 (&ah)[SLC][2],
+                                            const u32x4 (&al)[SLC][2], f32x4 (&acc)[NF]) {
+#pragma unroll
+  for (int nf = 0; nf < NF; ++nf) acc[nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < SLC; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) {
+        const bf16x8 w = h == 0 ? fp8x8_bf16(x.q[c][nf][0], x.q[c][nf][1], x.s[nf])
+                                : fp8x8_bf16(x.q[c][nf][2], x.q[c][nf][3], x.s[nf]);
+        acc[nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah[c][h]), w, acc[nf], 0, 0, 0);
+        acc[nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al[c][h]), w, acc[nf], 0, 0, 0);
+      }
+}
+
 template <int SLC, int NF>
 __device__ __forceinline__ void stream_mma(const StreamBuf<SLC, NF>& x, const u32x4 (&ah)[SLC][2],
                                            const u32x4 (&al)[SLC][2], f32x4 (&acc)[NF]) {
@@ -344,9 +400,11 @@ __device__ __forceinline__ void stream_mma(const StreamBuf<SLC, NF>& x, const u3
       }
 }
 
-template <int SLC, int MODE, bool LOOP>
+template <int SLC, int MODE, bool LOOP, bool FP8 = false>
 __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
   constexpr int NF = 1;
+  static_assert(!(FP8 && MODE == GEMM_TOPK), "the FP8 lm_head is the wave kernel");
+  using Buf = typename std::conditional<FP8, StreamBuf8<SLC, NF>, StreamBuf<SLC, NF>>::type;
   constexpr bool GLU = MODE == GEMM_SWIGLU;
   constexpr int RED_FLOATS = 2 * NF * SW * 4 * 64;
   constexpr int MRG = (MODE == GEMM_TOPK) ? 4 * 64 * (TOPK + 1) : 0;   // lane lists for the final merge
@@ -370,13 +428,15 @@ __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
 #pragma unroll
     for (int c = 0; c < SLC; ++c) {
       const bool ok = li < Mv && kw + c * 64 < p.K;
-      const int k = min(kw + c * 64, p.K - 64) + kg * 8;
+      // bf16 weights: halves k = 32 h + 8 kg .. +7; FP8 weights: k = 16 kg + 8 h .. +7
+      const int k = min(kw + c * 64, p.K - 64) + kg * (FP8 ? 16 : 8);
+      constexpr int HO = FP8 ? 8 : 32;
       const bf16* qh = arow + k;
       const bf16* ql = arow + p.a_plane + k;
       ah[c][0] = ok ? *reinterpret_cast<const u32x4*>(qh) : z;
-      ah[c][1] = ok ? *reinterpret_cast<const u32x4*>(qh + 32) : z;
+      ah[c][1] = ok ? *reinterpret_cast<const u32x4*>(qh + HO) : z;
       al[c][0] = ok ? *reinterpret_cast<const u32x4*>(ql) : z;
-      al[c][1] = ok ? *reinterpret_cast<const u32x4*>(ql + 32) : z;
+      al[c][1] = ok ? *reinterpret_cast<const u32x4*>(ql + HO) : z;
     }
   }
   const int row = 4 * kg + wave;                        // epilogue row of waves 0..3
@@ -413,33 +473,41 @@ __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
   };
   f32x4 acc[NF];
   int f = blockIdx.x;
+  auto load = [&](Buf& x, int fr) {
+    if constexpr (FP8) stream_load8<SLC, NF, GLU>(x, p, ncols, fr, kw, kg, li);
+    else stream_load<SLC, NF, GLU>(x, p, ncols, fr, kw, kg, li);
+  };
+  auto mma = [&](const Buf& x) {
+    if constexpr (FP8) stream_mma8(x, ah, al, acc);
+    else stream_mma(x, ah, al, acc);
+  };
   if (!LOOP) {
     // one fragment for this workgroup
-    StreamBuf<SLC, NF> x;
-    stream_load<SLC, NF, GLU>(x, p, ncols, f, kw, kg, li);
-    stream_mma(x, ah, al, acc);
+    Buf x;
+    load(x, f);
+    mma(x);
     finish(acc, 0, f);
   } else {
     // ping-pong: the next fragment's loads are issued before this one's MFMAs (the scheduling
     // barrier keeps the compiler from sinking them towards their use); loads past the last
     // fragment are clamped to it and never used
     const int G = gridDim.x;
-    StreamBuf<SLC, NF> x, y;
+    Buf x, y;
     int buf = 0;
-    stream_load<SLC, NF, GLU>(x, p, ncols, f, kw, kg, li);
+    load(x, f);
     while (true) {
       const int fy = f + G;
-      stream_load<SLC, NF, GLU>(y, p, ncols, min(fy, nfrag - 1), kw, kg, li);
+      load(y, min(fy, nfrag - 1));
       __builtin_amdgcn_sched_barrier(0);
-      stream_mma(x, ah, al, acc);
+      mma(x);
       finish(acc, buf, f);
       if (fy >= nfrag) break;
       f = fy;
       buf ^= 1;
       const int fx = f + G;
-      stream_load<SLC, NF, GLU>(x, p, ncols, min(fx, nfrag - 1), kw, kg, li);
+      load(x, min(fx, nfrag - 1));
       __builtin_amdgcn_sched_barrier(0);
-      stream_mma(y, ah, al, acc);
+      mma(y);
       finish(acc, buf, f);
       if (fx >= nfrag) break;
       f = fx;
@@ -533,16 +601,6 @@ __device__ __forceinline__ void lw_load8(LwBatch8& x, const unsigned char* row, 
 #pragma unroll
   for (int c = 0; c < LW_CH8; ++c) x.q[c] = *reinterpret_cast<const u32x4*>(row + k0 + c * 64 + kg * 16);
   x.s = *scale;
-}
-
-// eight E4M3 codes (two words, lowest byte first) -> eight bf16 values code * s
-__device__ __forceinline__ bf16x8 fp8x8_bf16(unsigned w0, unsigned w1, float s) {
-  u32x4 o;
-  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false));
-  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true));
-  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false));
-  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true));
-  return as_bf16x8(o);
 }
 
 __device__ __forceinline__ void lw_mma8(const LwBatch8& x, const bf16 (*sa)[LW_LD], int k0, int li, int kg,
@@ -878,14 +936,21 @@ hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hi
     const int ncols = (mode == GEMM_SWIGLU) ? p.half : p.N;
     const int nfrag = (mode == GEMM_SWIGLU) ? (ncols + 7) / 8 : (ncols + 15) / 16;
     const bool loop = (int)pl.grid.x < nfrag;
-#define DFL_STREAM_MODE(SLC, MODE)                                                                    \
-  if (loop) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, true>), pl.grid, sb, 0, st, p);         \
-  else hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, false>), pl.grid, sb, 0, st, p);
+    if (p.row_scale && (mode == GEMM_TOPK || p.seg_rows < (mode == GEMM_SWIGLU ? 2 * p.half : p.N)))
+      return hipErrorInvalidValue;   // FP8 weights: PARTIAL / SWIGLU over one weight segment
+#define DFL_STREAM_MODE(SLC, MODE, F8)                                                                \
+  if (loop) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, true, F8>), pl.grid, sb, 0, st, p);     \
+  else hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, false, F8>), pl.grid, sb, 0, st, p);
 #define DFL_STREAM(SLC)                                                                               \
   if (pl.slc == SLC) {                                                                                \
-    if (mode == GEMM_TOPK) { DFL_STREAM_MODE(SLC, GEMM_TOPK) }                                        \
-    else if (mode == GEMM_SWIGLU) { DFL_STREAM_MODE(SLC, GEMM_SWIGLU) }                               \
-    else { DFL_STREAM_MODE(SLC, GEMM_PARTIAL) }                                                       \
+    if (mode == GEMM_TOPK) { DFL_STREAM_MODE(SLC, GEMM_TOPK, false) }                                 \
+    else if (mode == GEMM_SWIGLU) {                                                                   \
+      if (p.row_scale) { DFL_STREAM_MODE(SLC, GEMM_SWIGLU, true) }                                    \
+      else { DFL_STREAM_MODE(SLC, GEMM_SWIGLU, false) }                                               \
+    } else {                                                                                          \
+      if (p.row_scale) { DFL_STREAM_MODE(SLC, GEMM_PARTIAL, true) }                                   \
+      else { DFL_STREAM_MODE(SLC, GEMM_PARTIAL, false) }                                              \
+    }                                                                                                 \
   }
     DFL_STREAM(1)
     DFL_STREAM(2)

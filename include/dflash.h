@@ -267,6 +267,14 @@ DFLASH_API dflash_status dflash_verify_greedy(int32_t n_seq, int32_t block_size,
 DFLASH_API dflash_status dflash_quantize_fp8_rows(const void* src, int32_t rows, int32_t cols, uint8_t* codes,
                                                   float* row_scales, void* stream);
 DFLASH_API dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t* codes, const float* row_scales);
+/* The same for one layer's MLP: gate_up_codes [2*ffn][d] are the codes of the stacked matrix
+ * [W_gate; W_up] (gate rows first), down_codes [d][ffn] those of W_down, each with its row scales
+ * (as written by dflash_quantize_fp8_rows); all four NULL reverts the layer to its bf16 matrices.
+ * Borrowed like the weights.  Batch-1 kernels only: a draft call with more than 16 rows, or a
+ * hidden size above 2048, then returns DFLASH_E_UNSUPPORTED. */
+DFLASH_API dflash_status dflash_set_mlp_fp8(dflash_handle* h, int32_t layer, const uint8_t* gate_up_codes,
+                                            const float* gate_up_scales, const uint8_t* down_codes,
+                                            const float* down_scales);
 
 /* Benchmark workload helper, not part of the drafter: stands in for a target model's verify
  * pass.  For i = 1..K-1, g_{i-1} = d_i with probability match_prob, else a different token;

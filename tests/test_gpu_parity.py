@@ -363,3 +363,58 @@ def test_mid_bf16_fp8_lm_head(H):
     res = case.draft([1], [123], logits=True)
     err, _ = H.check_draft(case, [1], [123], res)
     assert err <= H.LOGIT_TOL["bf16"]
+
+
+def _fp8_drafter(case, mlp=True, lm_head=True):
+    """Quantises the MLP matrices of every layer (stacked [gate; up], down) and the lm_head on the
+    GPU, checks the codes against the oracle's, installs them, and returns float64 weights for the
+    oracle with those matrices dequantised."""
+    import copy
+    import torch
+    W = copy.copy(case.W64)
+    W["layers"] = [dict(lw) for lw in case.W64["layers"]]
+    keep = []
+    if mlp:
+        for l, lw in enumerate(case.dev_w["layers"]):
+            gu, gus = _quantize_on_gpu(torch.cat([lw["w_gate"], lw["w_up"]]).contiguous())
+            dn, dns = _quantize_on_gpu(lw["w_down"])
+            for name, codes, scales, rows in (("w_gate", gu, gus, slice(0, case.cfg.ffn)),
+                                              ("w_up", gu, gus, slice(case.cfg.ffn, 2 * case.cfg.ffn)),
+                                              ("w_down", dn, dns, slice(None))):
+                oc, osc = O.quantize_fp8_rows(case.W64["layers"][l][name])
+                assert np.array_equal(codes[rows].cpu().numpy(), oc), (l, name)
+                assert np.array_equal(scales[rows].cpu().numpy(), osc.astype(np.float32)), (l, name)
+                W["layers"][l][name] = O.dequantize_fp8_rows(oc, osc)
+            case.d.dflash_set_mlp_fp8(l, gu, gus, dn, dns)
+            keep += [gu, gus, dn, dns]
+    if lm_head:
+        codes, scales = _quantize_on_gpu(case.dev_w["lm_head"])
+        oc, osc = O.quantize_fp8_rows(case.W64["lm_head"])
+        assert np.array_equal(codes.cpu().numpy(), oc)
+        case.d.dflash_set_lm_head_fp8(codes, scales)
+        W["lm_head"] = O.dequantize_fp8_rows(oc, osc)
+    return W
+
+
+def test_mid_bf16_fp8_mlp_and_lm_head(H):
+    """Batch 1, K=16 with FP8 MLP weights in both layers (stacked gate/up through the SwiGLU
+    streaming kernel, down through the k-split one) and the FP8 lm_head, against the oracle run
+    with those matrices dequantised; more than 16 rows are refused; NULL restores bf16."""
+    case = H.Case(MID, max_seqs=2, max_batch=2, max_inject_rows=64)
+    _prefill(case, [1], [(0, 50)])
+    W8 = _fp8_drafter(case)
+    W64 = case.W64
+    case.W64 = W8
+    try:
+        res = _check(H, case, [1], [321], mode_names=("viterbi",))
+        _same_topk_without_logits(case, [1], [321], res)
+    finally:
+        case.W64 = W64
+    with pytest.raises(B.DflashError):
+        case.draft([1, 0], [321, 5])
+    for l in range(MID.n_layers):
+        case.d.dflash_set_mlp_fp8(l, None, None, None, None)
+    case.d.dflash_set_lm_head_fp8(None, None)
+    res = case.draft([1], [321], logits=True)
+    err, _ = H.check_draft(case, [1], [321], res)
+    assert err <= H.LOGIT_TOL["bf16"]

@@ -319,3 +319,41 @@ def test_b1_k16_fp8_lm_head(H, big):
     finally:
         big["W64"]["lm_head"] = bf16_lm
     assert run.d.dflash_get_device_error() == 0
+
+
+def test_b1_k16_fp8_mlp(H, big):
+    """The b1_k16 drafter with FP8 MLP weights in all 5 layers (stacked gate/up 12288 x 2048,
+    down 2048 x 6144): codes as the oracle's, then a full-window draft against the oracle run
+    with those matrices dequantised."""
+    import copy
+    import torch
+    cfg = synth.WORKLOADS["b1_k16"]
+    run = Run(H, big, cfg, max_seqs=1, max_batch=1, max_inject_rows=1024, sampled=[0])
+    W8 = copy.copy(big["W64"])
+    W8["layers"] = [dict(lw) for lw in big["W64"]["layers"]]
+    keep = []
+    for l, lw in enumerate(big["dev"]["layers"]):
+        out = []
+        for mat in (torch.cat([lw["w_gate"], lw["w_up"]]).contiguous(), lw["w_down"]):
+            codes = torch.empty(mat.shape, dtype=torch.uint8, device="cuda")
+            scales = torch.empty(mat.shape[0], dtype=torch.float32, device="cuda")
+            B.dflash_quantize_fp8_rows(mat, codes, scales)
+            out += [codes, scales]
+        torch.cuda.synchronize()
+        for name, codes, scales, rows in (("w_gate", out[0], out[1], slice(0, cfg.ffn)),
+                                          ("w_up", out[0], out[1], slice(cfg.ffn, 2 * cfg.ffn)),
+                                          ("w_down", out[2], out[3], slice(None))):
+            oc, osc = O.quantize_fp8_rows(big["W64"]["layers"][l][name])
+            assert np.array_equal(codes[rows].cpu().numpy(), oc), (l, name)
+            assert np.array_equal(scales[rows].cpu().numpy(), osc.astype(np.float32)), (l, name)
+            W8["layers"][l][name] = O.dequantize_fp8_rows(oc, osc)
+        run.d.dflash_set_mlp_fp8(l, *out)
+        keep += out
+    run.W64 = W8
+    run.d.dflash_reset_seqs(run.t(np.zeros(1, dtype=np.int32)))
+    run.inject([0], [_window(cfg.context[0], cfg.window)])
+    anchors = synth.anchors(cfg).tolist()
+    res = run.draft([0], anchors)
+    run.own_logit_topk(res)
+    run.compare_sampled([0], anchors, res)
+    assert run.d.dflash_get_device_error() == 0
