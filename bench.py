@@ -197,7 +197,8 @@ def algorithmic(cfg, tau_mean, n_ctx):
     return dict(bytes=bytes_, flops=fl, lm_head_bytes=lm_bytes, lm_head_flops=2 * B * (K - 1) * V * d)
 
 
-def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=False, fp8_mlp=False):
+def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=False, fp8_mlp=False,
+                 fp8_attn_inject=False):
     """Times `steps` steps twice on one stream: (1) replays of a HIP graph holding
     `graph_steps` steps (the headline rate; no events inside the graph), (2) the same number of
     steps launched eagerly, each lm_head launch bracketed by HIP events on that stream (the
@@ -219,6 +220,22 @@ def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=
                 cyc.Bd.dflash_quantize_fp8_rows(mat, out[-2], out[-1])
             cyc.d.dflash_set_mlp_fp8(l, *out)
             cyc.mlp8.append(out)
+        torch.cuda.synchronize()
+
+    def codes_of(mats):
+        m = torch.cat(mats).contiguous()
+        c = (torch.empty(m.shape, dtype=torch.uint8, device="cuda"),
+             torch.empty(m.shape[0], dtype=torch.float32, device="cuda"))
+        cyc.Bd.dflash_quantize_fp8_rows(m, *c)
+        return c
+    if fp8_attn_inject:   # stacked [wq; wk; wv] and wo per layer; W_fc and the stacked [wk; wv] of every layer
+        cyc.attn8 = []    # (the prefill above was injected with the bf16 weights: FP8 injection takes <= 16 rows)
+        for l, lw in enumerate(cyc.w["layers"]):
+            q8, o8 = codes_of([lw["wq"], lw["wk"], lw["wv"]]), codes_of([lw["wo"]])
+            cyc.d.dflash_set_attn_fp8(l, *q8, *o8)
+            cyc.attn8.append((q8, o8))
+        cyc.inj8 = (codes_of([cyc.w["fc"]]), codes_of([t for lw in cyc.w["layers"] for t in (lw["wk"], lw["wv"])]))
+        cyc.d.dflash_set_inject_fp8(*cyc.inj8[0], *cyc.inj8[1])
         torch.cuda.synchronize()
     stream = torch.cuda.Stream()
     G = max(1, min(graph_steps, steps))
@@ -525,6 +542,14 @@ def main():
                 "blocks_per_s": round(r9["blocks_per_s"], 1), "draft_tokens_per_s": round(r9["draft_tokens_per_s"], 1),
                 "ms_per_step": round(r9["ms_per_step"], 4)}
             del r9["cycle"]
+            torch.cuda.empty_cache()
+            r10 = run_workload(cfg, args.steps, args.warmup, torch, fp8_lm_head=True, fp8_mlp=True, fp8_attn_inject=True)
+            out["fp8_all_gemms"] = {
+                "workload": "b1_k16 with E4M3 codes (per-row power-of-two scales) for every weight GEMM of the cycle: "
+                            "injection fc and K/V, QKV, O, gate/up, down, lm_head (weight-only; activations bf16)",
+                "blocks_per_s": round(r10["blocks_per_s"], 1), "draft_tokens_per_s": round(r10["draft_tokens_per_s"], 1),
+                "ms_per_step": round(r10["ms_per_step"], 4)}
+            del r10["cycle"]
     if not args.no_b32:
         c3 = synth.WORKLOADS["b32_k8_conv"]
         torch.cuda.empty_cache()

@@ -85,6 +85,8 @@ def lib():
         "dflash_quantize_fp8_rows": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
         "dflash_set_lm_head_fp8": (c_int32, [H, c_void_p, c_void_p]),
         "dflash_set_mlp_fp8": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "dflash_set_attn_fp8": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "dflash_set_inject_fp8": (c_int32, [H, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_timing_enable": (c_int32, [H, c_int32]),
         "dflash_timing_read": (c_int32, [H, POINTER(c_double), POINTER(c_int32)]),
         "dflash_get_device_error": (c_int32, [H, POINTER(c_int32)]),
@@ -103,7 +105,7 @@ EXPORTED = ("dflash_config_check", "dflash_kv_cache_bytes", "dflash_kv_cache_lay
             "dflash_create", "dflash_destroy", "dflash_reset_seqs", "dflash_inject_kv", "dflash_draft_block",
             "dflash_select_path", "dflash_select_sample", "dflash_verify_rejection", "dflash_verify_greedy",
             "dflash_synth_target_argmax", "dflash_quantize_fp8_rows", "dflash_set_lm_head_fp8", "dflash_set_mlp_fp8",
-            "dflash_timing_enable",
+            "dflash_set_attn_fp8", "dflash_set_inject_fp8", "dflash_timing_enable",
             "dflash_timing_read", "dflash_get_device_error", "dflash_status_string", "dflash_last_error")
 
 
@@ -235,6 +237,20 @@ class Drafter:
         self._mlp_fp8[layer] = (gate_up_codes, gate_up_scales, down_codes, down_scales)   # keep alive
         check("dflash_set_mlp_fp8", lib().dflash_set_mlp_fp8(self.h, layer, ptr(gate_up_codes), ptr(gate_up_scales),
                                                              ptr(down_codes), ptr(down_scales)))
+
+    def dflash_set_attn_fp8(self, layer, qkv_codes, qkv_scales, o_codes, o_scales):
+        """Use E4M3 codes for layer's stacked [wq; wk; wv] and wo (all None: bf16)."""
+        if not hasattr(self, "_attn_fp8"):
+            self._attn_fp8 = {}
+        self._attn_fp8[layer] = (qkv_codes, qkv_scales, o_codes, o_scales)   # keep alive
+        check("dflash_set_attn_fp8", lib().dflash_set_attn_fp8(self.h, layer, ptr(qkv_codes), ptr(qkv_scales),
+                                                               ptr(o_codes), ptr(o_scales)))
+
+    def dflash_set_inject_fp8(self, fc_codes, fc_scales, kv_codes, kv_scales):
+        """Use E4M3 codes for W_fc and the stacked per-layer [wk; wv] (all None: bf16)."""
+        self._inj_fp8 = (fc_codes, fc_scales, kv_codes, kv_scales)   # keep alive
+        check("dflash_set_inject_fp8", lib().dflash_set_inject_fp8(self.h, ptr(fc_codes), ptr(fc_scales),
+                                                                   ptr(kv_codes), ptr(kv_scales)))
 
     def close(self):
         if self.h:

@@ -64,6 +64,13 @@ struct Handle {
     const float *gu_s, *dn_s;
   };
   std::vector<Fp8Mlp> mlp_fp8;
+  struct Fp8Attn {                   // per layer: E4M3 [wq; wk; wv] [qw + 2 kvw][d] and wo [d][qw] codes
+    const unsigned char *qkv, *o;
+    const float *qkv_s, *o_s;
+  };
+  std::vector<Fp8Attn> attn_fp8;
+  const unsigned char *inj_fc8, *inj_kv8;   // injection: fc [d][concat], K/V stack [L (wk, wv)][d] codes
+  const float *inj_fc8_s, *inj_kv8_s;
   std::vector<const void*> layers;   // n_layers * DFLASH_LAYER_TENSORS
   int max_seqs, max_batch, max_inject_rows;
   char* kv;
@@ -409,6 +416,13 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
   ia.meta_pos = wsp<int>(H, H->wl.meta_pos);
   HIP_TRY(launch_inject_plan(ia, st));
   const long long max_rows = (long long)n_seq * max_new;
+  if (H->inj_fc8) {
+    const int pr = (int)(max_rows < Ri ? max_rows : Ri);
+    if (pr > 0 && (gemm_plan(true, GEMM_PARTIAL, pr, d, concat).kind != 3 ||
+                   gemm_plan(true, GEMM_PARTIAL, pr, c->n_layers * 2 * c->n_kv_heads * c->head_dim, d).kind != 3))
+      return fail(DFLASH_E_UNSUPPORTED, "FP8 injection weights take at most 16 rows per call (n_seq * max_new = %lld); "
+                  "inject longer spans with the bf16 weights", max_rows);
+  }
   float* part = wsp<float>(H, H->wl.part);
   for (long long r0 = 0; r0 < max_rows; r0 += Ri) {
     const int rows = (int)((max_rows - r0) < Ri ? (max_rows - r0) : Ri);
@@ -423,6 +437,11 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
     g1.seg[0] = H->g_fc;
     g1.seg_rows = d;
     g1.part = part;
+    if (H->inj_fc8) {
+      g1.seg[0] = H->inj_fc8;
+      g1.ldb = concat;
+      g1.row_scale = H->inj_fc8_s;
+    }
     GemmPlan p1 = gemm_plan(b, GEMM_PARTIAL, rows, d, concat);
     HIP_TRY(gemm_launch(b, p1, GEMM_PARTIAL, g1, st));
     const size_t c_plane = (size_t)H->max_inject_rows * d;
@@ -439,6 +458,12 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
     }
     g2.seg_rows = kvw;
     g2.part = part;
+    if (H->inj_kv8) {   // the stacked codes in the same row order: layer l's wk rows, then its wv rows
+      g2.seg[0] = H->inj_kv8;
+      g2.seg_rows = Nkv;
+      g2.ldb = d;
+      g2.row_scale = H->inj_kv8_s;
+    }
     GemmPlan p2 = gemm_plan(b, GEMM_PARTIAL, rows, Nkv, d);
     HIP_TRY(gemm_launch(b, p2, GEMM_PARTIAL, g2, st));
     KvPostArgs ka{};
@@ -479,6 +504,13 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
                       gemm_plan(true, GEMM_PARTIAL, M, d, c->ffn).kind != 3))
     return fail(DFLASH_E_UNSUPPORTED, "FP8 MLP weights take at most 16 draft rows (n_seq * block_size = %d) and a "
                 "hidden size of at most 2048", M);
+  bool any_attn_fp8 = false;
+  for (const auto& a8 : H->attn_fp8) any_attn_fp8 |= a8.qkv != nullptr;
+  if (any_attn_fp8 && (gemm_plan(true, GEMM_PARTIAL, M, c->n_heads * c->head_dim + 2 * c->n_kv_heads * c->head_dim,
+                                 d).kind != 3 ||
+                       gemm_plan(true, GEMM_PARTIAL, M, d, c->n_heads * c->head_dim).kind != 3))
+    return fail(DFLASH_E_UNSUPPORTED, "FP8 attention projections take at most 16 draft rows (n_seq * block_size = %d)",
+                M);
   if (H->lm_fp8 && gemm_plan(true, GEMM_TOPK, M, c->vocab, d).kind != 4)
     return fail(DFLASH_E_UNSUPPORTED, "the FP8 lm_head takes at most 16 draft rows (n_seq * block_size = %d) and a "
                 "hidden size that is a multiple of 512 up to 2048", M);
@@ -525,6 +557,13 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
     gq.seg[G + 1] = LW(H, l, DFLASH_L_WV);
     gq.seg_rows = kvw;
     gq.part = part;
+    const Handle::Fp8Attn* a8 = (size_t)l < H->attn_fp8.size() && H->attn_fp8[l].qkv ? &H->attn_fp8[l] : nullptr;
+    if (a8) {   // one stacked [wq; wk; wv] segment of E4M3 codes (checked up front: the stream kernel)
+      gq.seg[0] = a8->qkv;
+      gq.seg_rows = qw + 2 * kvw;
+      gq.ldb = d;
+      gq.row_scale = a8->qkv_s;
+    }
     GemmPlan pq = gemm_plan(b, GEMM_PARTIAL, M, qw + 2 * kvw, d);
     HIP_TRY(gemm_launch(b, pq, GEMM_PARTIAL, gq, st));
     QkvArgs qa{};
@@ -575,6 +614,11 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
     go.seg[0] = LW(H, l, DFLASH_L_WO);
     go.seg_rows = d;
     go.part = part;
+    if (a8) {
+      go.seg[0] = a8->o;
+      go.ldb = qw;
+      go.row_scale = a8->o_s;
+    }
     GemmPlan po = gemm_plan(b, GEMM_PARTIAL, M, d, qw);
     HIP_TRY(gemm_launch(b, po, GEMM_PARTIAL, go, st));
     RowArgs rp = ra;
@@ -802,6 +846,33 @@ dflash_status dflash_set_mlp_fp8(dflash_handle* h, int32_t layer, const uint8_t*
   if (set && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "FP8 weights are for bf16 drafters");
   if (H->mlp_fp8.size() < (size_t)H->cfg.n_layers) H->mlp_fp8.resize(H->cfg.n_layers, Handle::Fp8Mlp{});
   H->mlp_fp8[layer] = Handle::Fp8Mlp{gate_up_codes, down_codes, gate_up_scales, down_scales};
+  return DFLASH_OK;
+}
+
+dflash_status dflash_set_attn_fp8(dflash_handle* h, int32_t layer, const uint8_t* qkv_codes, const float* qkv_scales,
+                                 const uint8_t* o_codes, const float* o_scales) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  if (layer < 0 || layer >= H->cfg.n_layers) return fail(DFLASH_E_INVALID, "layer %d outside [0, n_layers)", layer);
+  const int set = !!qkv_codes + !!qkv_scales + !!o_codes + !!o_scales;
+  if (set != 0 && set != 4) return fail(DFLASH_E_INVALID, "all four pointers set, or all NULL");
+  if (set && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "FP8 weights are for bf16 drafters");
+  if (H->attn_fp8.size() < (size_t)H->cfg.n_layers) H->attn_fp8.resize(H->cfg.n_layers, Handle::Fp8Attn{});
+  H->attn_fp8[layer] = Handle::Fp8Attn{qkv_codes, o_codes, qkv_scales, o_scales};
+  return DFLASH_OK;
+}
+
+dflash_status dflash_set_inject_fp8(dflash_handle* h, const uint8_t* fc_codes, const float* fc_scales,
+                                   const uint8_t* kv_codes, const float* kv_scales) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  const int set = !!fc_codes + !!fc_scales + !!kv_codes + !!kv_scales;
+  if (set != 0 && set != 4) return fail(DFLASH_E_INVALID, "all four pointers set, or all NULL");
+  if (set && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "FP8 weights are for bf16 drafters");
+  H->inj_fc8 = fc_codes;
+  H->inj_fc8_s = fc_scales;
+  H->inj_kv8 = kv_codes;
+  H->inj_kv8_s = kv_scales;
   return DFLASH_OK;
 }
 

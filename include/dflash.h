@@ -275,6 +275,18 @@ DFLASH_API dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t*
 DFLASH_API dflash_status dflash_set_mlp_fp8(dflash_handle* h, int32_t layer, const uint8_t* gate_up_codes,
                                             const float* gate_up_scales, const uint8_t* down_codes,
                                             const float* down_scales);
+/* The same for one layer's attention projections: qkv_codes [n_heads*head_dim + 2*n_kv_heads*head_dim][d]
+ * are the codes of the stacked [W_q; W_k; W_v], o_codes [d][n_heads*head_dim] those of W_o.  Batch-1
+ * kernels only, as above. */
+DFLASH_API dflash_status dflash_set_attn_fp8(dflash_handle* h, int32_t layer, const uint8_t* qkv_codes,
+                                             const float* qkv_scales, const uint8_t* o_codes, const float* o_scales);
+/* The same for the injection: fc_codes [d][n_taps*target_hidden] (W_fc) and kv_codes
+ * [n_layers*2*n_kv_heads*head_dim][d], the stacked [W_k^0; W_v^0; W_k^1; W_v^1; ...].  An injection
+ * call whose rows (n_seq * max_new, or max_inject_rows per pass) exceed 16 then returns
+ * DFLASH_E_UNSUPPORTED before enqueueing anything: inject long spans (a prefill) with the bf16
+ * weights, i.e. before this call or after clearing it (all NULL). */
+DFLASH_API dflash_status dflash_set_inject_fp8(dflash_handle* h, const uint8_t* fc_codes, const float* fc_scales,
+                                               const uint8_t* kv_codes, const float* kv_scales);
 
 /* Benchmark workload helper, not part of the drafter: stands in for a target model's verify
  * pass.  For i = 1..K-1, g_{i-1} = d_i with probability match_prob, else a different token;

@@ -185,6 +185,7 @@ def check_kv(case, seq_ids, sample_layers=None, max_positions=64):
                         bound = 2.0 ** -7 * np.abs(ref) + 1e-2 * rms
                     else:
                         bound = np.full(ref.shape, 1e-5 * rms)
+                    assert np.all(np.isfinite(got)), (s, l, kind, p)   # NaN would slip past max()
                     ratio = np.abs(got - ref) / bound
                     if float(np.max(ratio)) > 1.0:
                         i = np.unravel_index(int(np.argmax(ratio)), ratio.shape)

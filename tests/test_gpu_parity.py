@@ -365,15 +365,49 @@ def test_mid_bf16_fp8_lm_head(H):
     assert err <= H.LOGIT_TOL["bf16"]
 
 
-def _fp8_drafter(case, mlp=True, lm_head=True):
-    """Quantises the MLP matrices of every layer (stacked [gate; up], down) and the lm_head on the
-    GPU, checks the codes against the oracle's, installs them, and returns float64 weights for the
-    oracle with those matrices dequantised."""
+def _fp8_stacked(case, W, mats, names_rows):
+    """GPU codes of the row-stacked device matrices `mats`; each (layer or None, name, rows) block
+    checked against the oracle's codes of that matrix and replaced in W by its dequantised form."""
+    import torch
+    codes, scales = _quantize_on_gpu(torch.cat(mats).contiguous() if len(mats) > 1 else mats[0])
+    for layer, name, rows in names_rows:
+        src = case.W64["layers"][layer][name] if layer is not None else case.W64[name]
+        oc, osc = O.quantize_fp8_rows(src)
+        assert np.array_equal(codes[rows].cpu().numpy(), oc), (layer, name)
+        assert np.array_equal(scales[rows].cpu().numpy(), osc.astype(np.float32)), (layer, name)
+        if layer is not None:
+            W["layers"][layer][name] = O.dequantize_fp8_rows(oc, osc)
+        else:
+            W[name] = O.dequantize_fp8_rows(oc, osc)
+    return codes, scales
+
+
+def _fp8_drafter(case, mlp=True, lm_head=True, attn=False, inject=False):
+    """Quantises the MLP matrices of every layer (stacked [gate; up], down), optionally the
+    attention projections (stacked [wq; wk; wv], wo) and the injection matrices (fc, the stacked
+    per-layer [wk; wv]), and the lm_head on the GPU, checks the codes against the oracle's,
+    installs them, and returns float64 weights for the oracle with those matrices dequantised."""
     import copy
     import torch
+    cfg = case.cfg
     W = copy.copy(case.W64)
     W["layers"] = [dict(lw) for lw in case.W64["layers"]]
     keep = []
+    qw, kvw = cfg.q_width, cfg.kv_width
+    if attn:
+        for l, lw in enumerate(case.dev_w["layers"]):
+            q8 = _fp8_stacked(case, W, [lw["wq"], lw["wk"], lw["wv"]],
+                              [(l, "wq", slice(0, qw)), (l, "wk", slice(qw, qw + kvw)), (l, "wv", slice(qw + kvw, None))])
+            o8 = _fp8_stacked(case, W, [lw["wo"]], [(l, "wo", slice(None))])
+            case.d.dflash_set_attn_fp8(l, *q8, *o8)
+    if inject:
+        fc8 = _fp8_stacked(case, W, [case.dev_w["fc"]], [(None, "fc", slice(None))])
+        mats, blocks = [], []
+        for l, lw in enumerate(case.dev_w["layers"]):
+            mats += [lw["wk"], lw["wv"]]
+            blocks += [(l, "wk", slice(2 * l * kvw, (2 * l + 1) * kvw)), (l, "wv", slice((2 * l + 1) * kvw, (2 * l + 2) * kvw))]
+        kv8 = _fp8_stacked(case, W, mats, blocks)
+        case.d.dflash_set_inject_fp8(*fc8, *kv8)
     if mlp:
         for l, lw in enumerate(case.dev_w["layers"]):
             gu, gus = _quantize_on_gpu(torch.cat([lw["w_gate"], lw["w_up"]]).contiguous())
@@ -418,3 +452,22 @@ def test_mid_bf16_fp8_mlp_and_lm_head(H):
     res = case.draft([1], [321], logits=True)
     err, _ = H.check_draft(case, [1], [321], res)
     assert err <= H.LOGIT_TOL["bf16"]
+
+
+def test_mid_bf16_fp8_every_gemm(H):
+    """FP8 codes for every weight GEMM of a batch-1 cycle: injection (fc, stacked K/V), attention
+    projections (stacked QKV, O), MLP and lm_head.  A prefill injected with the bf16 weights, then
+    an injection of 5 rows with the FP8 ones, then a draft, each against the oracle run with the
+    same matrices (dequantised where FP8); an injection of more than 16 rows is refused."""
+    case = H.Case(MID, max_seqs=2, max_batch=2, max_inject_rows=64)
+    _prefill(case, [1], [(0, 50)])
+    W64 = case.W64
+    case.W64 = _fp8_drafter(case, mlp=True, lm_head=True, attn=True, inject=True)
+    try:
+        case.inject([1], [np.arange(50, 55)], start_pos=False)
+        res = _check(H, case, [1], [77], mode_names=("viterbi",))
+        _same_topk_without_logits(case, [1], [77], res)
+        with pytest.raises(B.DflashError):
+            case.inject([1], [np.arange(55, 75)], start_pos=False)
+    finally:
+        case.W64 = W64
