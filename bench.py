@@ -348,9 +348,15 @@ def cpu_baseline(cyc, budget_s=20.0, max_cycles=10000):
 
 # ----------------------------------------------------------------------------- traffic record
 
-def kernel_hash():
+# sources of each workload's lm_head kernel (and its launch planning): a traffic record holds
+# only while these are unchanged
+HASH_FILES = {"b1_k16": ("gemm.hip", "common.h", "kernels.h"),
+              "b32_k8_conv": ("gemm.hip", "gemm_tile.hip", "common.h", "kernels.h")}
+
+
+def kernel_hash(workload="b1_k16"):
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h", "kernels.h"):
+    for f in HASH_FILES[workload]:
         h.update(open(os.path.join(ROOT, "block_diffusion_draft_inject_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -362,7 +368,7 @@ def recorded_traffic(workload):
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
-    if rec.get("kernel_hash") != kernel_hash():
+    if rec.get("kernel_hash") != kernel_hash(workload):
         return None
     return rec.get("bytes_per_launch")
 
@@ -371,14 +377,16 @@ def recorded_traffic(workload):
 
 COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
 LM_KERNEL = "lmhead_topk_wave<false, false>"   # lm_head + top-16 at batch 1 (independent waves, bf16 weights, no full-logit store)
+LM_KERNELS = {"b1_k16": LM_KERNEL,
+              "b32_k8_conv": "lmhead_topk_tile<"}   # batch 32: 256 x 256 MFMA tiles
 
 
-def traffic_probe(steps, torch):
+def traffic_probe(steps, torch, workload="b1_k16"):
     """Workload for one rocprofv3 counter pass: `steps` eager cycles of the headline workload,
     then a plain elementwise copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES) three
     times.  The copy's FETCH_SIZE / WRITE_SIZE readings give the counters' scale."""
     from block_diffusion_draft_inject_amd import synth
-    cfg = synth.WORKLOADS["b1_k16"]
+    cfg = synth.WORKLOADS[workload]
     cyc = Cycle(cfg, 0, torch, cfg.batch)
     raw = torch.cuda.current_stream().cuda_stream
     for _ in range(steps):
@@ -422,7 +430,7 @@ def traffic_record(fetch_csv, write_csv, workload="b1_k16"):
     res = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = [r for r in _counter_rows(path) if r[2] == name]
-        lm = [v for _, k, _, v in rows if LM_KERNEL in k]
+        lm = [v for _, k, _, v in rows if LM_KERNELS[workload] in k]
         copies = sorted([(i, v) for i, k, _, v in rows if "elementwise" in k])[-3:]
         if not lm or len(copies) < 3:
             raise SystemExit(f"{path}: no lm_head dispatches or fewer than 3 copy dispatches")
@@ -430,7 +438,7 @@ def traffic_record(fetch_csv, write_csv, workload="b1_k16"):
         scale = COPY_BYTES / (copy_kib * 1024.0)
         res[name] = dict(kib_per_launch=sum(lm) / len(lm), launches=len(lm), copy_kib=copy_kib, scale=scale)
     f, w = res["FETCH_SIZE"], res["WRITE_SIZE"]
-    rec = dict(kernel=LM_KERNEL, workload=workload, kernel_hash=kernel_hash(),
+    rec = dict(kernel=LM_KERNELS[workload], workload=workload, kernel_hash=kernel_hash(workload),
                fetch=f, write=w, copy_bytes=COPY_BYTES,
                bytes_per_launch=int(round(f["kib_per_launch"] * 1024 * f["scale"]
                                           + w["kib_per_launch"] * 1024 * w["scale"])))
@@ -459,9 +467,11 @@ def main():
                     help="run the workload of the MFMA counter passes (eager batch-32 cycles)")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the lm_head traffic record from two counter-collection CSVs (no GPU)")
+    ap.add_argument("--traffic-workload", default="b1_k16", choices=sorted(LM_KERNELS),
+                    help="workload of --traffic-probe / --traffic-record")
     args = ap.parse_args()
     if args.traffic_record:
-        traffic_record(*args.traffic_record)
+        traffic_record(*args.traffic_record, workload=args.traffic_workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the drafter pass shards by sequence with no exchange, "
@@ -474,7 +484,7 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     if args.traffic_probe:
-        traffic_probe(args.steps, torch)
+        traffic_probe(args.steps, torch, args.traffic_workload)
         return
     if args.mfma_probe:
         mfma_probe(args.steps, torch)
@@ -580,7 +590,7 @@ def main():
             "unit": "GB/s" if hbm_bound else "TFLOP/s",
             "frac": round((lm_gbps3 / HBM_PEAK_GBPS) if hbm_bound else (lm_tflops / MFMA_BF16_PEAK_TFLOPS), 4),
             "mfma_tflops": round(lm_tflops, 1), "mfma_frac": round(lm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None, "avg_launch_ms": round(r3["lm_head_ms"], 5),
+            "traffic": recorded_traffic("b32_k8_conv"), "avg_launch_ms": round(r3["lm_head_ms"], 5),
             "bytes_per_launch": int(a3["lm_head_bytes"]), "flops_per_launch": int(a3["lm_head_flops"])}
         del r3["cycle"]
     if not args.no_overlap:
