@@ -223,6 +223,10 @@ dflash_status check_cfg(const dflash_config* c) {
     if (c->ffn % 128 || qw % 64 || (c->n_taps * c->target_hidden) % 64)
       return fail(DFLASH_E_UNSUPPORTED, "bf16 GEMMs need ffn a multiple of 128, n_heads*head_dim and the concat width multiples of 64");
     if (qw % kvw) return fail(DFLASH_E_UNSUPPORTED, "n_heads*head_dim must be a multiple of n_kv_heads*head_dim");
+    // the O and down projections feed the sublayer epilogue, which sums at most 8 k-splits: the
+    // streaming plan reaches 8 splits of 2048 at K = 16384
+    if (c->ffn > 16384 || qw > 16384)
+      return fail(DFLASH_E_UNSUPPORTED, "bf16 drafters need ffn and n_heads*head_dim <= 16384");
     if ((qw / kvw) + 2 > MAX_SEG || 2 * c->n_layers > MAX_SEG) return fail(DFLASH_E_UNSUPPORTED, "too many weight segments");
   } else {
     if (256 % R || c->head_dim % (256 / R)) return fail(DFLASH_E_UNSUPPORTED, "fp32 attention needs 256 %% R == 0 and head_dim %% (256/R) == 0");
@@ -414,8 +418,8 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
   ia.ubar_plane = (size_t)H->max_inject_rows * concat;
   ia.meta_seq = wsp<int>(H, H->wl.meta_seq);
   ia.meta_pos = wsp<int>(H, H->wl.meta_pos);
-  HIP_TRY(launch_inject_plan(ia, st));
   const long long max_rows = (long long)n_seq * max_new;
+  // host-checkable refusal before anything is enqueued (the plan kernel advances seq_len)
   if (H->inj_fc8) {
     const int pr = (int)(max_rows < Ri ? max_rows : Ri);
     if (pr > 0 && (gemm_plan(true, GEMM_PARTIAL, pr, d, concat).kind != 3 ||
@@ -423,6 +427,7 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
       return fail(DFLASH_E_UNSUPPORTED, "FP8 injection weights take at most 16 rows per call (n_seq * max_new = %lld); "
                   "inject longer spans with the bf16 weights", max_rows);
   }
+  HIP_TRY(launch_inject_plan(ia, st));
   float* part = wsp<float>(H, H->wl.part);
   for (long long r0 = 0; r0 < max_rows; r0 += Ri) {
     const int rows = (int)((max_rows - r0) < Ri ? (max_rows - r0) : Ri);

@@ -139,7 +139,7 @@ typedef struct dflash_handle dflash_handle;
  * block_size <= 64; block_size 2..32; topk 16; sel_rank a multiple of 8 in [8, 256]; the concat
  * width n_taps*target_hidden a multiple of 8 (of 64 for bf16) and at most 65536 (bf16) or 32768
  * (fp32); bf16 drafters need head_dim 128, ffn a multiple of 128 and n_heads*head_dim a multiple
- * of 64. */
+ * of 64, both at most 16384. */
 DFLASH_API dflash_status dflash_config_check(const dflash_config* cfg);
 
 /* Size of the caller-owned KV cache buffer for `max_seqs` sequences (0 on invalid input). */

@@ -38,6 +38,10 @@ def test_config_check_accepts_workloads_and_rejects_bad_shapes():
     assert B.dflash_config_check(base.replace(n_kv_heads=3)) == -3
     assert B.dflash_config_check(base.replace(block_size=32)) == -3        # 4 heads/group * 32 > 64
     assert B.dflash_config_check(base.replace(mask_id=151936)) == -1
+    # the O and down projections' k-splits must fit the sublayer epilogue (K <= 16384)
+    assert B.dflash_config_check(base.replace(ffn=16384)) == 0
+    assert B.dflash_config_check(base.replace(ffn=16384 + 128)) == -3
+    assert B.dflash_config_check(base.replace(n_heads=132, n_kv_heads=4)) == -3   # 132 x 128 > 16384
     assert B.lib().dflash_config_check(None) == -1
     assert b"NULL" in B.lib().dflash_last_error()
 
@@ -114,3 +118,21 @@ def test_status_strings():
     L = B.lib()
     for s in (0, -1, -2, -3, -4, -5):
         assert L.dflash_status_string(s)
+
+
+def test_fp8_injection_refusal_precedes_any_device_work():
+    """With FP8 injection weights installed, an injection of more than 16 rows is refused before
+    anything is enqueued (the plan kernel, which advances the sequence lengths, included): on a
+    handle over never-dereferenced fake device addresses the call returns -3 instead of touching
+    the device."""
+    cfg = synth.WORKLOADS["b1_k16"]
+    st, h, keep, kvb, wsb = _fake_handle(cfg, max_seqs=4, max_batch=1, rows=64)
+    assert st == 0, B.lib().dflash_last_error()
+    L = B.lib()
+    fake = 0x5000
+    assert L.dflash_set_inject_fp8(h, fake, fake, fake, fake) == 0
+    assert L.dflash_inject_kv(h, 1, fake, None, fake, 17, fake, None) == -3
+    assert b"16 rows" in L.dflash_last_error()
+    assert L.dflash_inject_kv(h, 2, fake, None, fake, 9, fake, None) == -3      # 18 rows over two sequences
+    assert L.dflash_set_inject_fp8(h, None, None, None, None) == 0
+    assert L.dflash_destroy(h) == 0

@@ -467,7 +467,14 @@ def test_mid_bf16_fp8_every_gemm(H):
         case.inject([1], [np.arange(50, 55)], start_pos=False)
         res = _check(H, case, [1], [77], mode_names=("viterbi",))
         _same_topk_without_logits(case, [1], [77], res)
-        with pytest.raises(B.DflashError):
+        _, _, sl, sb = case.d.kv_views()
+        before = (sl[:2].cpu().tolist(), sb[:2].cpu().tolist())
+        with pytest.raises(B.DflashError) as e:
             case.inject([1], [np.arange(55, 75)], start_pos=False)
+        assert e.value.status == -3
+        import torch
+        torch.cuda.synchronize()
+        # refused before anything was enqueued: the sequence lengths did not move
+        assert (sl[:2].cpu().tolist(), sb[:2].cpu().tolist()) == before and before[0][1] == 55
     finally:
         case.W64 = W64
