@@ -174,6 +174,9 @@ def run_overlap(torch, reps=10, graph_steps=10):
         torch.cuda.synchronize()
         res[kind] = (time.perf_counter() - t0) * 1e3 / (reps * G)
         del graph
+    torch.cuda.synchronize()
+    dB.close()
+    cyc.d.close()
     return res
 
 
@@ -294,6 +297,8 @@ def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=
     res["hbm_frac"] = alg["bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS
     res["mfma_frac"] = alg["flops"] / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
     res["cycle"] = cyc
+    del graph
+    torch.cuda.synchronize()
     return res
 
 
@@ -596,6 +601,7 @@ def main():
     if not args.no_overlap:
         torch.cuda.empty_cache()
         ov = run_overlap(torch)
+        _release(torch)
         out["overlap"] = {
             "workload": "b1_k16 decode cycle of one sequence on one stream + a 1024-row prefill injection of "
                         "another sequence on a second stream (second handle, shared KV cache)",
@@ -603,6 +609,18 @@ def main():
             "sequential_ms": round(ov["sequential"], 4), "overlapped_ms": round(ov["overlapped"], 4),
             "saved_frac": round(1 - ov["overlapped"] / ov["sequential"], 4)}
     print(json.dumps(out), flush=True)
+    _release(torch)
+
+
+def _release(torch):
+    """Frees every graph, handle and device buffer of the run while the HIP runtime is fully up,
+    so that nothing of ours is left for interpreter finalisation (where objects die in no fixed
+    order, possibly after the runtime or a profiler attached to it has begun to shut down)."""
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -202,15 +202,47 @@ def check_kv(case, seq_ids, sample_layers=None, max_positions=64):
     return worst, same / max(1, tot)
 
 
-def check_draft(case, seq_ids, anchors, res, band=TIE_BAND, oracles=None):
+class SwapCount:
+    """Top-16 set differences against the oracle, split by how far the candidate's oracle logit
+    lies from the oracle's 16th value: within the 1e-3 tie band, or beyond it but within twice
+    the row's measured logit error (two candidates closer than the logit error can swap)."""
+
+    def __init__(self):
+        self.rows = self.rows_swapped = self.tie = self.wide = 0
+        self.max_gap = 0.0
+
+    def add_row(self, gset, oset, o_logits, kth, row_err, band=TIE_BAND):
+        self.rows += 1
+        if gset == oset:
+            return
+        self.rows_swapped += 1
+        for i in gset ^ oset:
+            gap = abs(o_logits[i] - kth)
+            assert gap <= band + 2 * row_err, ("top-16 set", i, gap, row_err)
+            self.max_gap = max(self.max_gap, gap)
+            if gap <= band:
+                self.tie += 1
+            else:
+                self.wide += 1
+
+    def __str__(self):
+        return (f"{self.rows} rows, {self.rows_swapped} with a set difference: {self.tie} ids within the 1e-3 tie "
+                f"band, {self.wide} beyond it (largest gap {self.max_gap:.2e})")
+
+
+WIDE_SWAP_ROWS = 0.02    # at most this fraction of rows may hold a swap beyond the 1e-3 band
+
+
+def check_draft(case, seq_ids, anchors, res, band=TIE_BAND, oracles=None, swaps_out=None):
     """Logits, then top-16: bitwise equal to the exact top-16 of the GPU's own logits, and equal
     as a set to the oracle's up to near-ties.  A candidate may enter or leave the set only if its
     oracle logit is within `band` + 2 * (that row's max |GPU - oracle| logit error) of the
-    oracle's 16th value: two candidates closer than the logit error can legitimately swap."""
+    oracle's 16th value: two candidates closer than the logit error can legitimately swap.  The
+    differences beyond the 1e-3 band are counted and held to WIDE_SWAP_ROWS of the rows."""
     cfg = case.cfg
     errs = []
     o_all = []
-    swaps = 0
+    sc = SwapCount() if swaps_out is None else swaps_out
     for b, (s, a) in enumerate(zip(seq_ids, anchors)):
         o = oracles[b] if oracles is not None else O.draft_block(cfg, case.W64, case.caches[int(s)], int(a),
                                                                   oracle_mode(cfg))
@@ -232,17 +264,13 @@ def check_draft(case, seq_ids, anchors, res, band=TIE_BAND, oracles=None):
             errs.append(float(row_err.max()))
         for t in range(cfg.block_size - 1):
             gset, oset = set(res["topk_ids"][b, t].tolist()), set(o["topk_ids"][t].tolist())
-            if gset != oset:
-                swaps += 1
-                kth = o["topk_logits"][t][-1]
-                for i in gset ^ oset:
-                    gap = abs(o["logits"][t][i] - kth)
-                    assert gap <= band + 2 * row_err[t], ("top-16 set", b, t, i, gap, row_err[t])
+            sc.add_row(gset, oset, o["logits"][t], o["topk_logits"][t][-1], row_err[t], band)
         slot_err = np.max(np.abs(res["h_final"][b] - o["h_final"]), axis=1)
         hf_err = float(slot_err.max())
         assert hf_err < 0.1, ("h_final", b, hf_err, "per slot", np.round(slot_err, 4).tolist())
     err = max(errs) if errs else 0.0
-    log(f"[draft] {cfg.name}: max |logit err| {err:.3e}, rows with a near-tie swap in the top-16 set: {swaps}")
+    log(f"[draft] {cfg.name}: max |logit err| {err:.3e}; top-16 vs oracle: {sc}")
+    assert sc.wide <= max(1, WIDE_SWAP_ROWS * sc.rows), str(sc)
     return err, o_all
 
 

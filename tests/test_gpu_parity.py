@@ -300,6 +300,34 @@ def test_two_handles_share_kv_on_two_streams(H):
     worst, same = H.check_kv(case, [2])
     H.log(f"[two handles] new sequence K/V: worst rel err {worst:.2e}, bit-equal {same:.4f}")
     assert worst <= 1.0 and same >= 0.99
+    # the two-stream drafts against the oracle: the running sequences took pool rows 0..2 (seq 0,
+    # positions 50..52) and 0..4 (seq 1, positions 30..34) before drafting
+    pool64 = pool.float().cpu().numpy().astype(np.float64)
+    for i, (s, L0, n) in enumerate(((0, 50, 3), (1, 30, 5))):
+        O.inject(cfg, case.W64, case.caches[s], np.arange(L0, L0 + n), pool64[i, :n], H.oracle_mode(cfg))
+    worst, same = H.check_kv(case, [0, 1])
+    assert worst <= 1.0 and same >= 0.99
+    res = {k: v.cpu().numpy() for k, v in par_out.items()}
+    err, _ = H.check_draft(case, [0, 1], [77, 4000], res)
+    H.log(f"[two handles] two-stream drafts vs oracle: max |logit err| {err:.2e}")
+    assert err <= H.LOGIT_TOL["bf16"]
+    assert case.d.dflash_get_device_error() == 0
+
+
+def test_mid_bf16_empty_context_mfma_attention(H):
+    """Fresh sequences with no injected context (L = 0: the block attends to itself only, so every
+    split-KV chunk past the first is empty) beside sequences with 1 and 63 context positions, on
+    the MFMA attention of bf16 drafters, batch 1 (16 rows) and batch 3 (48 rows)."""
+    case = H.Case(MID, max_seqs=4, max_batch=3, max_inject_rows=64)
+    case.reset([0, 1, 2])
+    case.inject([1, 2], [np.arange(0, 1), np.arange(0, 63)])
+    res = case.draft([0], [5], logits=True)
+    err, _ = H.check_draft(case, [0], [5], res)
+    assert err <= H.LOGIT_TOL["bf16"]
+    res = case.draft([1, 0, 2], [9, 4000, 123], logits=True)
+    err, _ = H.check_draft(case, [1, 0, 2], [9, 4000, 123], res)
+    H.log(f"[empty context] max |logit err| {err:.2e}")
+    assert err <= H.LOGIT_TOL["bf16"]
     assert case.d.dflash_get_device_error() == 0
 
 
