@@ -44,6 +44,8 @@ class DraftConfig:
     window: int = 1024
     topk: int = 16
     use_conv: bool = True
+    conv_group: int = 0           # 0: scalar conv taps per position; G > 0: per-channel taps, one
+                                  # correction per G channels (conv weights [2 d/G][d], bases [2][d])
     rms_eps: float = 1e-6
     rope_theta: float = 10000.0
     weight_std: float = 0.02
@@ -158,14 +160,15 @@ LAYER_TENSORS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "mlp_n
 
 def layer_shapes(cfg: DraftConfig) -> dict:
     d, f = cfg.hidden, cfg.ffn
+    cw, cb = ((2 * d // cfg.conv_group, d), (2, d)) if cfg.conv_group else ((2, d), (2,))
     return {
         "attn_norm": (d,), "wq": (cfg.q_width, d), "wk": (cfg.kv_width, d), "wv": (cfg.kv_width, d),
         "q_norm": (cfg.head_dim,), "k_norm": (cfg.head_dim,), "wo": (d, cfg.q_width),
         "mlp_norm": (d,), "w_gate": (f, d), "w_up": (f, d), "w_down": (d, f),
-        "conv_attn_pre_w": (2, d), "conv_attn_pre_b": (2,),
-        "conv_attn_post_w": (2, d), "conv_attn_post_b": (2,),
-        "conv_mlp_pre_w": (2, d), "conv_mlp_pre_b": (2,),
-        "conv_mlp_post_w": (2, d), "conv_mlp_post_b": (2,),
+        "conv_attn_pre_w": cw, "conv_attn_pre_b": cb,
+        "conv_attn_post_w": cw, "conv_attn_post_b": cb,
+        "conv_mlp_pre_w": cw, "conv_mlp_pre_b": cb,
+        "conv_mlp_post_w": cw, "conv_mlp_post_b": cb,
     }
 
 

@@ -18,7 +18,9 @@ What it computes, and where the pages say so:
   the anchor, slots 1..K-1 start as MASK, attention non-causal inside the block).
 * Two-tap dynamic convolution -- "Architecture", section "Problem 2 -- Suffix decay
   is local": Conv(x)_t = k_t0 * x_t + k_t1 * x_{t-1}, around every attention and MLP
-  sublayer, the first position reading the last verified token.
+  sublayer, the first position reading the last verified token.  Two forms: the configs'
+  scalar taps per position, and the page's per-channel coefficients (a learned base per
+  channel plus a correction from the current row shared per 16 channels).
 * Shared lm_head and top-16 candidates -- "Architecture", flowchart "Drafter" and the
   sequence diagram "One Cycle, Step by Step".
 * Path selector -- "Architecture", section "Problem 1 -- Independent picks are
@@ -138,6 +140,39 @@ def two_tap_conv(x, w, b, use_conv=True):
     return k[:, 0:1] * x + k[:, 1:2] * prev
 
 
+def two_tap_conv_grouped(x, base, wc, group):
+    """Per-channel (depthwise) two-tap conv over the rows of one block (x: [K][d]):
+    Conv(x)_t = k_t0 * x_t + k_t1 * x_{t-1} with coefficient vectors k_tj in R^d,
+
+        k_tj[c] = sigmoid(base_j[c] + corr_tj[c // group]),   corr_tj = W_j x_t in R^(d / group),
+
+    a learned base kernel per channel and tap plus a correction from the current row shared by
+    each run of `group` consecutive channels ("Architecture", section "Problem 2 -- Suffix decay
+    is local": one correction per 16 channels).  base: [2][d]; wc: [2 * d / group][d], tap 0's
+    correction rows first.  Slot 0 has no predecessor inside the block: x_{-1} = 0."""
+    x = as64(x)
+    d = x.shape[1]
+    ng = d // group
+    corr = x @ as64(wc).T                                            # [K][2 * ng]
+    base = as64(base)
+    k0 = sigmoid(base[0][None, :] + np.repeat(corr[:, :ng], group, axis=1))
+    k1 = sigmoid(base[1][None, :] + np.repeat(corr[:, ng:], group, axis=1))
+    prev = np.zeros_like(x)
+    prev[1:] = x[:-1]
+    return k0 * x + k1 * prev
+
+
+def sublayer_conv(cfg, x, w, b):
+    """The conv of one sublayer boundary in the drafter's configured form: none, the scalar
+    per-position taps (w: [2][d], b: [2]) or the per-channel form (cfg.conv_group > 0: w is the
+    correction matrix [2 d / G][d], b the base kernel [2][d])."""
+    if not cfg.use_conv:
+        return as64(x)
+    if getattr(cfg, "conv_group", 0):
+        return two_tap_conv_grouped(x, b, w, cfg.conv_group)
+    return two_tap_conv(x, w, b, True)
+
+
 def topk_desc(values, k):
     """Indices of the k largest values, ordered by (value descending, index ascending)."""
     values = as64(values)
@@ -220,7 +255,7 @@ def draft_block(cfg, W, cache: DraftCache, anchor, mode="bf16", block_ids=None, 
     for l, lw in enumerate(W["layers"]):
         # attention sublayer
         z = rms_norm(h, lw["attn_norm"], cfg.rms_eps)
-        y = two_tap_conv(z, lw["conv_attn_pre_w"], lw["conv_attn_pre_b"], cfg.use_conv)
+        y = sublayer_conv(cfg, z, lw["conv_attn_pre_w"], lw["conv_attn_pre_b"])
         q = (y @ as64(lw["wq"]).T).reshape(K, nh, dh)
         k = (y @ as64(lw["wk"]).T).reshape(K, nkv, dh)
         v = (y @ as64(lw["wv"]).T).reshape(K, nkv, dh)
@@ -234,13 +269,13 @@ def draft_block(cfg, W, cache: DraftCache, anchor, mode="bf16", block_ids=None, 
             keys, vals = k, v
         o = _attention(q, keys, vals, nkv).reshape(K, nh * dh)
         a = o @ as64(lw["wo"]).T
-        h = h + two_tap_conv(a, lw["conv_attn_post_w"], lw["conv_attn_post_b"], cfg.use_conv)
+        h = h + sublayer_conv(cfg, a, lw["conv_attn_post_w"], lw["conv_attn_post_b"])
         # feed-forward sublayer
         z = rms_norm(h, lw["mlp_norm"], cfg.rms_eps)
-        y = two_tap_conv(z, lw["conv_mlp_pre_w"], lw["conv_mlp_pre_b"], cfg.use_conv)
+        y = sublayer_conv(cfg, z, lw["conv_mlp_pre_w"], lw["conv_mlp_pre_b"])
         s = silu(y @ as64(lw["w_gate"]).T) * (y @ as64(lw["w_up"]).T)
         m = s @ as64(lw["w_down"]).T
-        h = h + two_tap_conv(m, lw["conv_mlp_post_w"], lw["conv_mlp_post_b"], cfg.use_conv)
+        h = h + sublayer_conv(cfg, m, lw["conv_mlp_post_w"], lw["conv_mlp_post_b"])
     h_final = rms_norm(h, W["final_norm"], cfg.rms_eps)
     logits = R(h_final[1:]) @ as64(W["lm_head"]).T              # [K-1][V]; bf16 input in mode "bf16"
     tk = cfg.topk

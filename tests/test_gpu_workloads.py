@@ -116,7 +116,7 @@ class Run:
         err = max(errs) if errs else 0.0
         H.log(f"[{cfg.name}] sampled sequences {self.sampled}: max |logit err| {err:.3e}; top-16 vs oracle: {sc}")
         assert err <= H.LOGIT_TOL["bf16"]
-        assert sc.wide <= max(1, H.WIDE_SWAP_ROWS * sc.rows), str(sc)
+        assert sc.ok(), str(sc)
         self.swaps = sc
         return err
 
