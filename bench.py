@@ -93,6 +93,8 @@ class Cycle:
         self.nacc = torch.empty(self.n, dtype=torch.int32, device="cuda")
         self.committed = torch.empty((self.n, K), dtype=torch.int32, device="cuda")
         self.counter = torch.zeros(1, dtype=torch.int64, device="cuda")
+        # stand-in target: the 0.7 match rule, or (incremental workload) tau uniform on {1..K}
+        self.match = -1.0 if cfg.tau_uniform else (0.7 if cfg.match_prob is None else cfg.match_prob)
         torch.cuda.synchronize()
         log(f"[bench] {cfg.name}: setup {time.time() - t0:.1f}s")
 
@@ -105,7 +107,7 @@ class Cycle:
                              stream=stream)
         d.dflash_select_path(self.anchor, o["topk_ids"], o["topk_logits"], o["h_final"], Bd.SELECT_VITERBI,
                              self.path, self.score, self.margin, stream=stream)
-        Bd.dflash_synth_target_argmax(self.n, K, cfg.vocab, self.path, 0.7, 12345, self.counter, self.target,
+        Bd.dflash_synth_target_argmax(self.n, K, cfg.vocab, self.path, self.match, 12345, self.counter, self.target,
                                       stream=stream)
         Bd.dflash_verify_greedy(self.n, K, self.path, self.target, self.nacc, self.tau, self.committed,
                                 self.anchor, stream=stream)
@@ -187,13 +189,16 @@ def algorithmic(cfg, tau_mean, n_ctx):
     qw, kvw = cfg.q_width, cfg.kv_width
     es = 2 if cfg.dtype == "bf16" else 4
     layer_w = (qw * d + 2 * kvw * d + d * qw + 3 * f * d)
-    w_block = cfg.n_layers * layer_w + V * d            # backbone + lm_head
+    # the four convs of a layer: [2][d] weights and 2 biases, or (per-channel form) a [2 d/G][d]
+    # correction matrix and a [2][d] base each
+    conv_w = 4 * ((2 * d // cfg.conv_group) * d + 2 * d if cfg.conv_group else 2 * d + 2) if cfg.use_conv else 0
+    w_block = cfg.n_layers * (layer_w + conv_w) + V * d            # backbone + lm_head
     w_inject = d * cfg.concat_width + cfg.n_layers * 2 * kvw * d
     rows_inj = B * tau_mean
     kv_read = cfg.n_layers * B * 2 * n_ctx * kvw * es
     bytes_ = (w_block + w_inject) * es + kv_read + rows_inj * cfg.concat_width * es
     M = B * K
-    fl = 2 * M * cfg.n_layers * layer_w + 2 * B * (K - 1) * V * d
+    fl = 2 * M * cfg.n_layers * (layer_w + conv_w) + 2 * B * (K - 1) * V * d
     fl += cfg.n_layers * B * cfg.n_heads * K * (n_ctx + K) * cfg.head_dim * 4   # QK^T and PV
     fl += 2 * rows_inj * w_inject
     lm_bytes = V * d * es + M * d * es                 # weights + the hidden rows (bf16 input for bf16 drafters)
@@ -302,14 +307,63 @@ def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=
     return res
 
 
+def batched_record(wname, desc, r):
+    """Sub-record of a batched workload: rates, the cycle's fractions of both peaks, and the roofline
+    of its dominant kernel, the lm_head + top-16 tile (its intensity is its row count in flops per
+    weight byte: below the bf16 ridge of ~312 the bound is HBM, above it MFMA; the other fraction is
+    given beside it)."""
+    a = r["alg"]
+    lm_s = r["lm_head_ms"] * 1e-3
+    lm_tflops = a["lm_head_flops"] / lm_s / 1e12
+    lm_gbps = a["lm_head_bytes"] / lm_s / 1e9
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBPS
+    hbm_bound = a["lm_head_flops"] / a["lm_head_bytes"] < ridge
+    rec = {"workload": desc,
+           "blocks_per_s": round(r["blocks_per_s"], 1),
+           "draft_tokens_per_s": round(r["draft_tokens_per_s"], 1),
+           "ms_per_step": round(r["ms_per_step"], 4),
+           "eager_ms_per_step": round(r["eager_ms_per_step"], 4),
+           "mfma_frac": round(r["mfma_frac"], 4), "hbm_frac": round(r["hbm_frac"], 4),
+           "algorithmic_tflop_per_step": round(a["flops"] / 1e12, 4),
+           "algorithmic_gbytes_per_step": round(a["bytes"] / 1e9, 4),
+           "tau_mean_last": round(r["tau_last"], 3),
+           "lm_head_avg_ms": round(r["lm_head_ms"], 5)}
+    rec["roofline"] = {
+        "kernel": "lm_head GEMM + fused top-16 (lmhead_topk_tile, 256 x 256 MFMA tiles)",
+        "bound": "hbm" if hbm_bound else "mfma",
+        "achieved": round(lm_gbps if hbm_bound else lm_tflops, 1),
+        "peak": HBM_PEAK_GBPS if hbm_bound else MFMA_BF16_PEAK_TFLOPS,
+        "unit": "GB/s" if hbm_bound else "TFLOP/s",
+        "frac": round((lm_gbps / HBM_PEAK_GBPS) if hbm_bound else (lm_tflops / MFMA_BF16_PEAK_TFLOPS), 4),
+        "mfma_tflops": round(lm_tflops, 1), "mfma_frac": round(lm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "hbm_gbps": round(lm_gbps, 1), "hbm_frac": round(lm_gbps / HBM_PEAK_GBPS, 4),
+        "traffic": recorded_traffic(wname) if wname in HASH_FILES else None,
+        "avg_launch_ms": round(r["lm_head_ms"], 5),
+        "bytes_per_launch": int(a["lm_head_bytes"]), "flops_per_launch": int(a["lm_head_flops"])}
+    return rec
+
+
 # ----------------------------------------------------------------------------- cpu baseline
 
 def cpu_baseline(cyc, budget_s=20.0, max_cycles=10000):
     """The CPU oracle (as it stands) running the same drafter cycle on the host cores, on a
-    bounded sample: prefill of the same context, then cycles until the time budget is spent."""
+    bounded sample: prefill of the same context, then cycles until the time budget is spent; once
+    with the BLAS pool on every core this process may run on, once on one thread."""
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores, user_api="blas"):
+        res = _cpu_cycles(cyc, budget_s, max_cycles, cores)
+    with threadpool_limits(limits=1, user_api="blas"):
+        one = _cpu_cycles(cyc, budget_s / 2, max_cycles, 1)
+    res["value_1thread"] = one["value"]
+    res["sample"] += f"; one thread: {one['n']} cycles in {one['el']:.1f}s"
+    for r in (res,):
+        r.pop("n"), r.pop("el")
+    return res
+
+
+def _cpu_cycles(cyc, budget_s, max_cycles, threads):
     import numpy as np
-    import torch
-    from threadpoolctl import threadpool_info
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle import dflash_oracle as O
     from block_diffusion_draft_inject_amd import synth
@@ -345,8 +399,7 @@ def cpu_baseline(cyc, budget_s=20.0, max_cycles=10000):
         if time.perf_counter() - t0 > budget_s:
             break
     el = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return dict(value=n / el, unit="blocks/s", cores=int(threads), kind="oracle",
+    return dict(value=n / el, unit="blocks/s", cores=int(threads), kind="oracle", n=n, el=el,
                 sample=f"{cfg.name}: one sequence (context {L}), {n} full cycles (inject tau, draft, Viterbi "
                        f"select, verify) in {el:.1f}s, float64 NumPy, BLAS threads {threads}")
 
@@ -462,6 +515,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-b32", action="store_true")
+    ap.add_argument("--no-c4", action="store_true", help="skip b32_k16_incremental")
+    ap.add_argument("--no-c5", action="store_true", help="skip b64_k16_long")
+    ap.add_argument("--no-pc", action="store_true", help="skip the per-channel conv leg")
     ap.add_argument("--no-overlap", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-lm_head variant of the headline workload")
     ap.add_argument("--no-b1", action="store_true", help="skip the headline workload (profiling runs)")
@@ -565,39 +621,34 @@ def main():
                 "blocks_per_s": round(r10["blocks_per_s"], 1), "draft_tokens_per_s": round(r10["draft_tokens_per_s"], 1),
                 "ms_per_step": round(r10["ms_per_step"], 4)}
             del r10["cycle"]
-    if not args.no_b32:
-        c3 = synth.WORKLOADS["b32_k8_conv"]
+    batched = [("b32", "b32_k8_conv", args.no_b32,
+                "b32_k8_conv: same drafter, K=8, batch 32, contexts U[512,4096] (window 1024), two-tap conv, "
+                "0.7 match rule"),
+               ("b32_k16", "b32_k16_incremental", args.no_c4,
+                "b32_k16_incremental: same drafter, K=16, batch 32, 2048-token prefixes (ring of 1024), every "
+                "cycle injects the tau ~ U{1..16} committed tokens' target states, tau from the stand-in target"),
+               ("b64", "b64_k16_long", args.no_c5,
+                "b64_k16_long: same drafter, K=16, batch 64, context 32768 each (the last 1024 positions "
+                "injected and attended), 0.7 match rule")]
+    for key, wname, skip, desc in batched:
+        if skip:
+            continue
         torch.cuda.empty_cache()
-        r3 = run_workload(c3, args.steps, args.warmup, torch)
-        out["b32"] = {"workload": "b32_k8_conv: same drafter, K=8, batch 32, contexts U[512,4096] (window 1024), "
-                                  "two-tap conv, 0.7 match rule",
-                      "blocks_per_s": round(r3["blocks_per_s"], 1),
-                      "draft_tokens_per_s": round(r3["draft_tokens_per_s"], 1),
-                      "ms_per_step": round(r3["ms_per_step"], 4),
-                      "eager_ms_per_step": round(r3["eager_ms_per_step"], 4),
-                      "mfma_frac": round(r3["mfma_frac"], 4), "hbm_frac": round(r3["hbm_frac"], 4),
-                      "algorithmic_tflop_per_step": round(r3["alg"]["flops"] / 1e12, 4),
-                      "lm_head_avg_ms": round(r3["lm_head_ms"], 5)}
-        # the batch-32 dominant kernel (lm_head + top-16 over 224 rows): its intensity (flops per
-        # weight byte ~ rows) is below the bf16 ridge (2500 / 8 ~ 312), so HBM bounds it; the MFMA
-        # fraction is given beside it
-        a3 = r3["alg"]
-        lm_s = r3["lm_head_ms"] * 1e-3
-        lm_tflops = a3["lm_head_flops"] / lm_s / 1e12
-        lm_gbps3 = a3["lm_head_bytes"] / lm_s / 1e9
-        ridge = MFMA_BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBPS
-        hbm_bound = a3["lm_head_flops"] / a3["lm_head_bytes"] < ridge
-        out["b32"]["roofline"] = {
-            "kernel": "lm_head GEMM + fused top-16 (lmhead_topk_tile, 256 x 256 MFMA tiles)",
-            "bound": "hbm" if hbm_bound else "mfma",
-            "achieved": round(lm_gbps3 if hbm_bound else lm_tflops, 1),
-            "peak": HBM_PEAK_GBPS if hbm_bound else MFMA_BF16_PEAK_TFLOPS,
-            "unit": "GB/s" if hbm_bound else "TFLOP/s",
-            "frac": round((lm_gbps3 / HBM_PEAK_GBPS) if hbm_bound else (lm_tflops / MFMA_BF16_PEAK_TFLOPS), 4),
-            "mfma_tflops": round(lm_tflops, 1), "mfma_frac": round(lm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": recorded_traffic("b32_k8_conv"), "avg_launch_ms": round(r3["lm_head_ms"], 5),
-            "bytes_per_launch": int(a3["lm_head_bytes"]), "flops_per_launch": int(a3["lm_head_flops"])}
-        del r3["cycle"]
+        rb = run_workload(synth.WORKLOADS[wname], args.steps, args.warmup, torch)
+        out[key] = batched_record(wname, desc, rb)
+        del rb["cycle"]
+        _release(torch)
+    if not args.no_pc:
+        torch.cuda.empty_cache()
+        cpc = synth.WORKLOADS["b1_k16"].replace(conv_group=16, name="b1_k16_pc16")
+        rp = run_workload(cpc, args.steps, args.warmup, torch)
+        out["per_channel_conv"] = {
+            "workload": "b1_k16 with the pages' per-channel conv (base per channel + correction per 16 channels: "
+                        "a 256 x 2048 correction GEMM before each of the 20 convs of the cycle)",
+            "blocks_per_s": round(rp["blocks_per_s"], 1), "draft_tokens_per_s": round(rp["draft_tokens_per_s"], 1),
+            "ms_per_step": round(rp["ms_per_step"], 4), "cycle_hbm_frac": round(rp["hbm_frac"], 4)}
+        del rp["cycle"]
+        _release(torch)
     if not args.no_overlap:
         torch.cuda.empty_cache()
         ov = run_overlap(torch)

@@ -28,7 +28,7 @@ class dflash_config(Structure):
     _fields_ = [(n, c_int32) for n in ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab",
                                        "n_taps", "target_hidden", "block_size", "window", "topk", "sel_rank",
                                        "mask_id", "use_conv")] + [
-        ("rms_eps", c_float), ("rope_theta", c_float), ("dtype", c_int32)]
+        ("rms_eps", c_float), ("rope_theta", c_float), ("dtype", c_int32), ("conv_group", c_int32)]
 
 
 class dflash_weights(Structure):
@@ -122,7 +122,7 @@ def make_config(cfg) -> dflash_config:
         head_dim=cfg.head_dim, ffn=cfg.ffn, vocab=cfg.vocab, n_taps=cfg.n_taps, target_hidden=cfg.target_hidden,
         block_size=cfg.block_size, window=cfg.window, topk=cfg.topk, sel_rank=cfg.sel_rank, mask_id=cfg.mask_id,
         use_conv=int(bool(cfg.use_conv)), rms_eps=cfg.rms_eps, rope_theta=cfg.rope_theta,
-        dtype=DFLASH_BF16 if cfg.dtype == "bf16" else DFLASH_F32)
+        dtype=DFLASH_BF16 if cfg.dtype == "bf16" else DFLASH_F32, conv_group=int(getattr(cfg, "conv_group", 0)))
 
 
 def ptr(t) -> int | None:

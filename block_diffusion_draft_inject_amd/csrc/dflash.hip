@@ -39,7 +39,7 @@ size_t esize(const dflash_config* c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 
 // Workspace regions (byte offsets), a pure function of (config, max_batch, max_inject_rows).
 struct WsLayout {
-  size_t h0, h1, act_y, act_o, act_s, qb, hsplit, kb, vb, ctx, part, o_part, m_part, l_part, tk_val, tk_id;
+  size_t h0, h1, act_y, act_o, act_s, qb, hsplit, kb, vb, act_a, act_z, ctx, part, o_part, m_part, l_part, tk_val, tk_id;
   size_t ubar, cbuf, meta_seq, meta_pos, row_off, row_start, row_skip, total, counters;
   size_t bytes;
   size_t part_floats;
@@ -83,6 +83,8 @@ struct Handle {
 };
 
 bool bf(const dflash_config* c) { return c->dtype == DFLASH_BF16; }
+// the pages' per-channel conv: coefficients from a base per channel plus a correction per conv_group channels
+bool per_channel_conv(const dflash_config* c) { return c->use_conv && c->conv_group > 0; }
 
 int attn_chunks(const dflash_config* c, int n_seq) {
   const int max_chunks = (c->window + c->block_size + 63) / 64;
@@ -111,6 +113,7 @@ size_t draft_part_floats(const dflash_config* c, int n_seq) {
   if (b && M <= 64) upd(GEMM_SWIGLU, 2 * c->ffn, d);
   else upd(GEMM_PARTIAL, 2 * c->ffn, d);
   upd(GEMM_PARTIAL, d, c->ffn);
+  if (per_channel_conv(c)) upd(GEMM_PARTIAL, 2 * d / c->conv_group, d);   // conv corrections
   if (!b) {
     size_t f = (size_t)M * c->vocab;   // fp32 path keeps full logits
     if (f > mx) mx = f;
@@ -152,6 +155,9 @@ WsLayout ws_layout(const dflash_config* c, int max_batch, int max_inject_rows, i
   L.hsplit = take(M * d * 4);
   L.kb = take(M * kvw * es);
   L.vb = take(M * kvw * es);
+  // per-channel conv: the sublayer output a and the normed rows z as GEMM operands
+  L.act_a = per_channel_conv(c) ? take(M * d * 4) : 0;
+  L.act_z = per_channel_conv(c) ? take(M * d * 4) : 0;
   L.ctx = take((size_t)max_batch * sizeof(SeqCtx));
   size_t pf = 0;
   int chmax = 1;
@@ -217,6 +223,9 @@ dflash_status check_cfg(const dflash_config* c) {
   if (c->n_taps * c->target_hidden > (c->dtype == DFLASH_BF16 ? 65536 : 32768))
     return fail(DFLASH_E_UNSUPPORTED, "n_taps*target_hidden must be <= 65536 (bf16) or 32768 (fp32)");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 1.f)) return fail(DFLASH_E_INVALID, "rms_eps >= 0 and rope_theta > 1 required");
+  if (c->conv_group < 0) return fail(DFLASH_E_INVALID, "conv_group must be >= 0");
+  if (c->conv_group > 0 && (c->hidden % c->conv_group || c->conv_group % 4))
+    return fail(DFLASH_E_UNSUPPORTED, "conv_group must divide hidden and be a multiple of 4");
   if (c->dtype == DFLASH_BF16) {
     if (c->head_dim != 128) return fail(DFLASH_E_UNSUPPORTED, "bf16 attention needs head_dim 128");
     const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
@@ -548,7 +557,63 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
   ra.ldy = d;
   ra.y_plane = Mmax * d;
   ra.plan = PlanArgs{H->max_seqs, c->window, seq_ids, seq_len(H), seq_base(H), ctx, counters};
-  HIP_TRY(launch_embed_pre(b, ra, M, st));
+  // Per-channel conv: each conv takes a correction GEMM (rows x [2 d/G][d]) on its input first.
+  // A post-conv runs as: reduce the sublayer's k-split partials into activation planes a, the
+  // correction GEMM on a, then the residual + post-conv + RMSNorm kernel, which writes z; a
+  // pre-conv as: the correction GEMM on z, then the conv itself, which writes the GEMM input y.
+  const bool pc = per_channel_conv(c);
+  const int Ncorr = pc ? 2 * d / c->conv_group : 0;
+  char* act_a = H->ws + W.act_a;
+  char* act_z = H->ws + W.act_z;
+  auto pc_corr = [&](const char* x, const void* wc, int& splits) -> dflash_status {
+    GemmParams gc = gemm_base(x, d, M, Ncorr, d);
+    gc.a_plane = Mmax * d;
+    gc.seg[0] = wc;
+    gc.seg_rows = Ncorr;
+    gc.part = part;
+    GemmPlan pl = gemm_plan(b, GEMM_PARTIAL, M, Ncorr, d);
+    HIP_TRY(gemm_launch(b, pl, GEMM_PARTIAL, gc, st));
+    splits = pl.splits;
+    return DFLASH_OK;
+  };
+  auto pc_pre = [&](const void* wc, const void* base) -> dflash_status {
+    int sp = 1;
+    dflash_status s2 = pc_corr(act_z, wc, sp);
+    if (s2 != DFLASH_OK) return s2;
+    PcArgs pa{};
+    pa.K = K; pa.d = d; pa.G = c->conv_group; pa.splits = sp; pa.part_rows = M; pa.ldo = d;
+    pa.plane = Mmax * d;
+    pa.x = act_z; pa.part = part; pa.base = base; pa.out = act_y;
+    HIP_TRY(launch_conv_apply(b, pa, M, st));
+    return DFLASH_OK;
+  };
+  auto pc_post = [&](int splits, float* h_in, float* h_out, const void* wc, const void* base, const void* gain,
+                     bool final) -> dflash_status {
+    ReduceArgs rd{M, d, splits, M, Mmax * d, nullptr, 0, part, act_a};
+    HIP_TRY(launch_reduce_store(b, rd, st));
+    int sp = 1;
+    dflash_status s2 = pc_corr(act_a, wc, sp);
+    if (s2 != DFLASH_OK) return s2;
+    PcArgs pa{};
+    pa.K = K; pa.d = d; pa.G = c->conv_group; pa.splits = sp; pa.part_rows = M; pa.ldo = d;
+    pa.plane = Mmax * d; pa.eps = c->rms_eps;
+    pa.h_in = h_in; pa.h_out = h_out; pa.x = act_a; pa.part = part; pa.base = base; pa.gain = gain;
+    pa.final_norm = final ? 1 : 0;
+    pa.out = final ? (void*)h_final : (void*)act_z;
+    pa.out2 = final ? (void*)(H->ws + W.hsplit) : nullptr;
+    HIP_TRY(launch_post_pre_pc(b, pa, M, st));
+    return DFLASH_OK;
+  };
+  if (pc) {   // h = E[x], z = RMSNorm(h) (the embed kernel without its conv), then the pre-conv
+    RowArgs re = ra;
+    re.use_conv = 0;
+    re.y = act_z;
+    HIP_TRY(launch_embed_pre(b, re, M, st));
+    dflash_status s2 = pc_pre(LW(H, 0, DFLASH_L_CONV_ATTN_PRE_W), LW(H, 0, DFLASH_L_CONV_ATTN_PRE_B));
+    if (s2 != DFLASH_OK) return s2;
+  } else {
+    HIP_TRY(launch_embed_pre(b, ra, M, st));
+  }
   ra.plan = PlanArgs{};
   const int chunks = attn_chunks(c, n_seq);
   for (int l = 0; l < c->n_layers; ++l) {
@@ -640,7 +705,13 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
     rp.final_norm = 0;
     rp.y = act_y;
     rp.ldy = d;
-    HIP_TRY(launch_post_pre(b, rp, M, st));
+    if (pc) {
+      dflash_status s2 = pc_post(po.splits, hA, hB, rp.post_w, rp.post_b, rp.pre_gain, false);
+      if (s2 == DFLASH_OK) s2 = pc_pre(rp.pre_w, rp.pre_b);
+      if (s2 != DFLASH_OK) return s2;
+    } else {
+      HIP_TRY(launch_post_pre(b, rp, M, st));
+    }
     // s = silu(y W_gate^T) * (y W_up^T)
     GemmParams gg = gemm_base(act_y, d, M, 2 * c->ffn, d);
     gg.a_plane = Mmax * d;
@@ -704,7 +775,14 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
       rm.y2 = H->ws + W.hsplit;
       rm.ldy = d;
     }
-    HIP_TRY(launch_post_pre(b, rm, M, st));
+    if (pc) {
+      const bool last = l + 1 == c->n_layers;
+      dflash_status s2 = pc_post(pd.splits, hB, hA, rm.post_w, rm.post_b, rm.pre_gain, last);
+      if (s2 == DFLASH_OK && !last) s2 = pc_pre(rm.pre_w, rm.pre_b);
+      if (s2 != DFLASH_OK) return s2;
+    } else {
+      HIP_TRY(launch_post_pre(b, rm, M, st));
+    }
   }
   // shared lm_head + top-16 per draft slot
   GemmParams gl = gemm_base(b ? (const void*)(H->ws + W.hsplit) : (const void*)h_final, d, M, c->vocab, d);
@@ -886,7 +964,8 @@ dflash_status dflash_synth_target_argmax(int32_t n_seq, int32_t block_size, int3
                                          void* stream) {
   if (n_seq < 0 || n_seq > 1024) return fail(DFLASH_E_SHAPE, "n_seq must be 0..1024");
   if (block_size < 2 || vocab < 2) return fail(DFLASH_E_INVALID, "block_size and vocab must be >= 2");
-  if (!(match_prob >= 0.f && match_prob <= 1.f)) return fail(DFLASH_E_INVALID, "match_prob must be in [0, 1]");
+  if (!((match_prob >= 0.f && match_prob <= 1.f) || match_prob == -1.f))
+    return fail(DFLASH_E_INVALID, "match_prob must be in [0, 1], or -1");
   if (n_seq == 0) return DFLASH_OK;
   if (!draft_ids || !counter || !target_argmax) return fail(DFLASH_E_INVALID, "NULL draft_ids, counter or target_argmax");
   SynthArgs a{n_seq, block_size, vocab, match_prob, (unsigned long long)seed, reinterpret_cast<long long*>(counter),

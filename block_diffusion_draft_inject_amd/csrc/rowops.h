@@ -197,7 +197,25 @@ struct SynthArgs {
   int* target;
 };
 
+// Per-channel two-tap conv (conv_group G > 0): coefficient vectors k_tj[c] = sigmoid(base_j[c] +
+// corr_tj[c / G]), corr_t = W_c x_t in R^(2 d / G) given as k-split GEMM partials.
+struct PcArgs {
+  int K, d, G, splits, part_rows, final_norm, ldo;
+  size_t plane;        // activation planes of x and out (bf16 drafters)
+  float eps;
+  const float* h_in;   // post-conv + norm only: residual in/out
+  float* h_out;
+  const void* x;       // conv input rows (activation planes): the sublayer output a, or the normed z
+  const float* part;   // corrections [splits][part_rows][2 d / G], tap 0's groups first
+  const void* base;    // [2][d]
+  const void* gain;    // RMSNorm gain (post-conv + norm only)
+  void* out;           // z planes / y planes / final: h_final fp32
+  void* out2;          // final only: the lm_head's bf16 input rows
+};
+
 hipError_t launch_embed_pre(bool bf, const RowArgs& a, int rows, hipStream_t st);
+hipError_t launch_post_pre_pc(bool bf, const PcArgs& a, int rows, hipStream_t st);
+hipError_t launch_conv_apply(bool bf, const PcArgs& a, int rows, hipStream_t st);
 hipError_t launch_post_pre(bool bf, const RowArgs& a, int rows, hipStream_t st);
 hipError_t launch_qkv_post(bool bf, const QkvArgs& a, int rows, hipStream_t st);
 hipError_t launch_swiglu(bool bf, const SwigluArgs& a, hipStream_t st);

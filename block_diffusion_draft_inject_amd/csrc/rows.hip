@@ -281,6 +281,128 @@ __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------ per-channel conv
+// The page's form of the two-tap conv ("Architecture", section "Problem 2 -- Suffix decay is
+// local"): Conv(x)_t = k_t0 (.) x_t + k_t1 (.) x_{t-1} with per-channel coefficients
+// k_tj[c] = sigmoid(base_j[c] + corr_tj[c / G]), a learned base kernel per channel plus a correction
+// W_c x_t from the current row shared by each run of G channels.  The corrections come from a
+// GEMM launched before (k-split partials, summed here in split order); a thread's 4 consecutive
+// channels share one group (G % 4 == 0).
+
+// Four activations at i: fp32, or the sum of the hi and lo bf16 planes.
+template <typename T>
+__device__ __forceinline__ f32x4 ld4_act(const void* p, size_t i, size_t plane) {
+  if constexpr (sizeof(T) == 4) {
+    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + i);
+  } else {
+    const uint2 h = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16*>(p) + i);
+    const uint2 l = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16*>(p) + i + plane);
+    return f32x4{__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xffff0000u), __uint_as_float(h.y << 16),
+                 __uint_as_float(h.y & 0xffff0000u)} +
+           f32x4{__uint_as_float(l.x << 16), __uint_as_float(l.x & 0xffff0000u), __uint_as_float(l.y << 16),
+                 __uint_as_float(l.y & 0xffff0000u)};
+  }
+}
+
+constexpr int PC_MAXS = 8;   // correction k-splits summed (the planner keeps it <= 8)
+
+// corr_t0 and corr_t1 of the group holding channel k of row `row` (all split loads in one burst)
+__device__ __forceinline__ void pc_corr(const PcArgs& a, int row, int k, float& c0, float& c1) {
+  const int ng = a.d / a.G, N = 2 * ng, grp = k / a.G;
+  float p0[PC_MAXS], p1[PC_MAXS];
+#pragma unroll
+  for (int s = 0; s < PC_MAXS; ++s) {
+    const float* pr = a.part + ((size_t)min(s, a.splits - 1) * a.part_rows + row) * N;
+    p0[s] = pr[grp];
+    p1[s] = pr[ng + grp];
+  }
+  c0 = c1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < PC_MAXS; ++s)
+    if (s < a.splits) {
+      c0 += p0[s];
+      c1 += p1[s];
+    }
+}
+
+__device__ __forceinline__ f32x4 sig4(f32x4 b, float c) {
+  return f32x4{sigmoidf_(b[0] + c), sigmoidf_(b[1] + c), sigmoidf_(b[2] + c), sigmoidf_(b[3] + c)};
+}
+
+// Sublayer epilogue with the per-channel post-conv: h_out[t] = h_in[t] + k_t0 (.) a_t + k_t1 (.) a_{t-1}
+// (a = x, the reduced sublayer output), then z = RMSNorm(h_out[t]) * gain -> out (activation
+// planes), or, final: out = h_f (fp32) and out2 = bf16(h_f) for the lm_head.
+template <typename T, int NV>
+__global__ __launch_bounds__(PP_T) void post_pre_pc_kernel(PcArgs a) {
+  __shared__ float red[(PP_T / 64) * 1];
+  const int row = blockIdx.x, tid = threadIdx.x, t = row % a.K, d = a.d;
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 h[NV], xt[NV], xq[NV], b0[NV], b1[NV], g[NV];
+  float c0[NV], c1[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int k = (i * PP_T + tid) * 4;
+    const int kc = k < d ? k : 0;
+    h[i] = ld4f(a.h_in, (size_t)row * d + kc);
+    xt[i] = ld4_act<T>(a.x, (size_t)row * d + kc, a.plane);
+    xq[i] = ld4_act<T>(a.x, (size_t)(t >= 1 ? row - 1 : row) * d + kc, a.plane);
+    b0[i] = ld4w<T>(a.base, kc);
+    b1[i] = ld4w<T>(a.base, (size_t)d + kc);
+    g[i] = ld4w<T>(a.gain, kc);
+    pc_corr(a, row, kc, c0[i], c1[i]);
+  }
+  float ss[1] = {0.f};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int k = (i * PP_T + tid) * 4;
+    if (k >= d) { h[i] = z4; continue; }
+    const f32x4 k0 = sig4(b0[i], c0[i]), k1 = sig4(b1[i], c1[i]);
+    h[i] += k0 * xt[i] + (t >= 1 ? k1 * xq[i] : z4);
+    *reinterpret_cast<f32x4*>(a.h_out + (size_t)row * d + k) = h[i];
+    ss[0] += dot4(h[i], h[i]);
+  }
+  block_sum<1, PP_T>(ss, red);
+  const float r = rsqrtf(ss[0] / d + a.eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int k = (i * PP_T + tid) * 4;
+    if (k >= d) continue;
+    const f32x4 o = h[i] * r * g[i];
+    if (a.final_norm) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + (size_t)row * a.ldo + k) = o;
+      st4_bf16_input<T>(a.out2, (size_t)row * a.ldo + k, a.plane, o);   // the lm_head takes bf16(h_f)
+    } else {
+      st4_act<T>(a.out, (size_t)row * a.ldo + k, a.plane, o);
+    }
+  }
+}
+
+// Pre-conv: y_t = k_t0 (.) z_t + k_t1 (.) z_{t-1} (z = x, the normed rows) -> out (activation planes).
+template <typename T, int NV>
+__global__ __launch_bounds__(PP_T) void conv_apply_kernel(PcArgs a) {
+  const int row = blockIdx.x, tid = threadIdx.x, t = row % a.K, d = a.d;
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 xt[NV], xq[NV], b0[NV], b1[NV];
+  float c0[NV], c1[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int k = (i * PP_T + tid) * 4;
+    const int kc = k < d ? k : 0;
+    xt[i] = ld4_act<T>(a.x, (size_t)row * d + kc, a.plane);
+    xq[i] = ld4_act<T>(a.x, (size_t)(t >= 1 ? row - 1 : row) * d + kc, a.plane);
+    b0[i] = ld4w<T>(a.base, kc);
+    b1[i] = ld4w<T>(a.base, (size_t)d + kc);
+    pc_corr(a, row, kc, c0[i], c1[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int k = (i * PP_T + tid) * 4;
+    if (k >= d) continue;
+    const f32x4 y = sig4(b0[i], c0[i]) * xt[i] + (t >= 1 ? sig4(b1[i], c1[i]) * xq[i] : z4);
+    st4_act<T>(a.out, (size_t)row * a.ldo + k, a.plane, y);
+  }
+}
+
 // ------------------------------------------------------------------------ q/k/v post
 // One wave per (row, head).  Heads 0..nh-1 are q, nh..nh+nkv-1 k, then v.  Lane l holds
 // elements l and l + dh/2, which is exactly a rotate-half RoPE pair.
@@ -866,6 +988,34 @@ hipError_t launch_post_pre(bool bf, const RowArgs& a, int rows, hipStream_t st) 
   if (v <= 1) launch_pp_s<1>(bf, a, rows, st);
   else if (v <= 2) launch_pp_s<2>(bf, a, rows, st);
   else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+hipError_t launch_post_pre_pc(bool bf, const PcArgs& a, int rows, hipStream_t st) {
+  if (a.d % 4 || a.G % 4 || a.d % a.G || a.splits < 1 || a.splits > PC_MAXS) return hipErrorInvalidValue;
+  const int v = (a.d + 4 * PP_T - 1) / (4 * PP_T);
+  if (v <= 1) {
+    if (bf) hipLaunchKernelGGL((post_pre_pc_kernel<bf16, 1>), dim3(rows), dim3(PP_T), 0, st, a);
+    else hipLaunchKernelGGL((post_pre_pc_kernel<float, 1>), dim3(rows), dim3(PP_T), 0, st, a);
+  } else if (v <= 2) {
+    if (bf) hipLaunchKernelGGL((post_pre_pc_kernel<bf16, 2>), dim3(rows), dim3(PP_T), 0, st, a);
+    else hipLaunchKernelGGL((post_pre_pc_kernel<float, 2>), dim3(rows), dim3(PP_T), 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+hipError_t launch_conv_apply(bool bf, const PcArgs& a, int rows, hipStream_t st) {
+  if (a.d % 4 || a.G % 4 || a.d % a.G || a.splits < 1 || a.splits > PC_MAXS) return hipErrorInvalidValue;
+  const int v = (a.d + 4 * PP_T - 1) / (4 * PP_T);
+  if (v <= 1) {
+    if (bf) hipLaunchKernelGGL((conv_apply_kernel<bf16, 1>), dim3(rows), dim3(PP_T), 0, st, a);
+    else hipLaunchKernelGGL((conv_apply_kernel<float, 1>), dim3(rows), dim3(PP_T), 0, st, a);
+  } else if (v <= 2) {
+    if (bf) hipLaunchKernelGGL((conv_apply_kernel<bf16, 2>), dim3(rows), dim3(PP_T), 0, st, a);
+    else hipLaunchKernelGGL((conv_apply_kernel<float, 2>), dim3(rows), dim3(PP_T), 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 hipError_t launch_qkv_post(bool bf, const QkvArgs& a, int rows, hipStream_t st) {

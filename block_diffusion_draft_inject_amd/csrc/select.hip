@@ -584,13 +584,16 @@ __global__ __launch_bounds__(1024) void synth_target_kernel(SynthArgs a) {
   if (b >= a.n_seq) return;
   const int K = a.K;
   const unsigned long long key = a.seed ^ ((unsigned long long)ctr << 24) ^ ((unsigned long long)b << 8);
+  // p < 0: committed tokens tau uniform on {1..K} (drafts 1..tau-1 match, draft tau does not)
+  const int tau = a.p < 0.f ? 1 + (int)(splitmix64(key ^ 0xABCDull) % (unsigned long long)K) : K;
   for (int i = 1; i < K; ++i) {
     const unsigned long long h1 = splitmix64(key ^ (unsigned long long)(2 * i));
     const unsigned long long h2 = splitmix64(key ^ (unsigned long long)(2 * i + 1));
     const float u = (float)(h1 >> 40) * (1.0f / 16777216.0f);
     const int di = a.draft[(size_t)b * (K - 1) + i - 1];
     const int alt = (int)(1 + h2 % (unsigned long long)(a.vocab - 1));
-    a.target[(size_t)b * K + i - 1] = (u < a.p) ? di : (int)(((long long)di + alt) % a.vocab);
+    const bool match = a.p < 0.f ? i < tau : u < a.p;
+    a.target[(size_t)b * K + i - 1] = match ? di : (int)(((long long)di + alt) % a.vocab);
   }
   a.target[(size_t)b * K + K - 1] = (int)(splitmix64(key ^ 0xFFFFull) % (unsigned long long)a.vocab);
 }

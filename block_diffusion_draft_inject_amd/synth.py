@@ -204,6 +204,15 @@ def make_weights(cfg: DraftConfig, selector_stress: bool = False) -> dict:
     return w
 
 
+def conv_tensors(cfg: DraftConfig) -> list:
+    """The conv parameters of every layer alone (the same draws make_weights makes for them), so
+    that drafters differing only in conv form can share every other tensor."""
+    s = cfg.weight_std
+    shapes = layer_shapes(cfg)
+    return [{n: _normal(cfg, ("layer", l, n), shp, s) for n, shp in shapes.items() if n.startswith("conv_")}
+            for l in range(cfg.n_layers)]
+
+
 def target_states(cfg: DraftConfig, seq: int, positions) -> Tensor:
     """Tapped target hidden states, N(0,1), one row of n_taps*target_hidden per (seq, position).
 

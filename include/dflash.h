@@ -73,13 +73,21 @@ typedef enum { DFLASH_SELECT_VITERBI = 0, DFLASH_SELECT_GREEDY = 1 } dflash_sele
  *  - sel_rank r: width of the selector's A/B token tables and context gate.
  *  - use_conv: 1 = two-tap dynamic convolution around every attention and MLP sublayer
  *    ("Architecture", section "Problem 2 -- Suffix decay is local").
- *  - rope_theta: rotary base for the rotate-half RoPE applied after the per-head q/k norm. */
+ *  - rope_theta: rotary base for the rotate-half RoPE applied after the per-head q/k norm.
+ *  - conv_group: form of the conv coefficients.  0: one scalar per tap and position,
+ *    k_t = sigmoid(W_c x_t + b_c) in R^2 (the conv weight of a sublayer is [2][d], its bias [2]).
+ *    G > 0: per-channel (depthwise) coefficients ("Architecture", section "Problem 2": a learned
+ *    base kernel per channel plus a small correction from the current hidden state shared per
+ *    16 channels), k_tj[c] = sigmoid(base_j[c] + (W_c x_t)[j d/G + c/G]): the conv weight is the
+ *    correction matrix [2 d/G][d] and the "bias" the base kernel [2][d].  G must divide hidden
+ *    and be a multiple of 4; G = hidden with a constant base row is the scalar form. */
 typedef struct {
   int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
   int32_t n_taps, target_hidden;
   int32_t block_size, window, topk, sel_rank, mask_id, use_conv;
   float rms_eps, rope_theta;
   dflash_dtype dtype;
+  int32_t conv_group;
 } dflash_config;
 
 /* Per-layer weight tensors, in this order, in dflash_weights.layers[l * DFLASH_LAYER_TENSORS + i]. */
@@ -96,7 +104,7 @@ typedef enum {
   DFLASH_L_W_UP,            /* [ffn][d]                                                       */
   DFLASH_L_W_DOWN,          /* [d][ffn]                                                       */
   DFLASH_L_CONV_ATTN_PRE_W, /* [2][d]  conv taps k_t = sigmoid(W x_t + b): before attention   */
-  DFLASH_L_CONV_ATTN_PRE_B, /* [2]                                                            */
+  DFLASH_L_CONV_ATTN_PRE_B, /* [2]     (conv_group G > 0: W is [2 d/G][d], b is [2][d])       */
   DFLASH_L_CONV_ATTN_POST_W,/* [2][d]  after attention (on the O-projection output)           */
   DFLASH_L_CONV_ATTN_POST_B,/* [2]                                                            */
   DFLASH_L_CONV_MLP_PRE_W,  /* [2][d]  before the MLP                                          */
@@ -290,7 +298,8 @@ DFLASH_API dflash_status dflash_set_inject_fp8(dflash_handle* h, const uint8_t* 
 
 /* Benchmark workload helper, not part of the drafter: stands in for a target model's verify
  * pass.  For i = 1..K-1, g_{i-1} = d_i with probability match_prob, else a different token;
- * g_{K-1} is uniform.  Randomness: splitmix64 of (seed, *counter, sequence, slot); *counter
+ * g_{K-1} is uniform.  match_prob = -1 instead draws the committed count tau uniform on {1..K}
+ * and matches exactly drafts 1..tau-1 (greedy verification then commits tau tokens).  Randomness: splitmix64 of (seed, *counter, sequence, slot); *counter
  * (device int64) is incremented once per call.  Runs as one workgroup: n_seq <= 1024. */
 DFLASH_API dflash_status dflash_synth_target_argmax(int32_t n_seq, int32_t block_size, int32_t vocab, const int32_t* draft_ids,
                                          float match_prob, uint64_t seed, int64_t* counter,

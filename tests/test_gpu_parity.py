@@ -506,3 +506,22 @@ def test_mid_bf16_fp8_every_gemm(H):
         assert (sl[:2].cpu().tolist(), sb[:2].cpu().tolist()) == before and before[0][1] == 55
     finally:
         case.W64 = W64
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_per_channel_conv(H, dtype):
+    """The pages' per-channel two-tap conv (one correction per 16 channels): the fp32 tiny drafter
+    (16 groups), and the mid bf16 drafter (32 groups) at batch 1 (16 rows: the streaming GEMMs for
+    the corrections) and batch 12 (192 rows: the tile GEMMs), against the oracle."""
+    if dtype == "f32":
+        cfg = synth.WORKLOADS["tiny_fp32"].replace(conv_group=16, name="tiny_fp32_pc16")
+        case = H.Case(cfg, max_seqs=1, max_batch=1, max_inject_rows=128)
+        _full_check(H, case, [0], [(0, 128)], synth.anchors(cfg).tolist())
+        return
+    cfg = MID.replace(conv_group=16, name="mid_bf16_pc16")
+    case = H.Case(cfg, max_seqs=12, max_batch=12, max_inject_rows=256)
+    _full_check(H, case, [3], [(0, 50)], anchors=[77])
+    rng = np.random.default_rng(9)
+    seq_ids = list(range(12))
+    spans = [(0, int(L)) for L in rng.integers(1, 120, size=12)]
+    _full_check(H, case, seq_ids, spans, rng.integers(0, cfg.vocab - 1, size=12).tolist(), mode_names=("viterbi",))

@@ -419,3 +419,36 @@ def test_b1_k16_fp8_attention_and_injection(H, big):
     run.own_logit_topk(res)
     run.compare_sampled([0], anchors, res)
     assert run.d.dflash_get_device_error() == 0
+
+
+def test_b1_k16_per_channel_conv(H, big):
+    """The b1_k16 drafter with the pages' per-channel conv (a base per channel and a correction per
+    16 channels: 20 correction matrices of 256 x 2048): full-window injection and a draft against
+    the oracle, every sequence check of the bf16 workloads."""
+    import copy
+    import torch
+    cfg = synth.WORKLOADS["b1_k16"].replace(conv_group=16, name="b1_k16_pc16")
+    convs = synth.conv_tensors(cfg)
+    dev = dict(big["dev"])
+    dev["layers"] = [dict(lw) for lw in big["dev"]["layers"]]
+    W = copy.copy(big["W64"])
+    W["layers"] = [dict(lw) for lw in big["W64"]["layers"]]
+    for l, cl in enumerate(convs):
+        for n, t in cl.items():
+            dev["layers"][l][n] = torch.from_numpy(np.ascontiguousarray(t.storage).view(np.int16)).cuda().view(
+                torch.bfloat16)
+            W["layers"][l][n] = t.values.astype(np.float64)
+    run = Run(H, dict(big, dev=dev, W64=W), cfg, max_seqs=1, max_batch=1, max_inject_rows=1024, sampled=[0])
+    run.d.dflash_reset_seqs(run.t(np.zeros(1, dtype=np.int32)))
+    run.inject([0], [_window(cfg.context[0], cfg.window)])
+    for cyc in range(2):
+        anchors = synth.anchors(cfg, cyc).tolist()
+        res = run.draft([0], anchors)
+        run.own_logit_topk(res)
+        run.compare_sampled([0], anchors, res)
+        match, alt, last = synth.match_draws(cfg, cyc)
+        _, ncom = run.select_verify(anchors, res, "viterbi",
+                                    lambda p: synth.stand_in_target(p, match, alt, last, cfg.vocab))
+        L = int(run.lengths([0])[0])
+        run.inject([0], [np.arange(L, L + int(ncom[0]))], start=False)
+    assert run.d.dflash_get_device_error() == 0
