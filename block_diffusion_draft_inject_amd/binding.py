@@ -71,6 +71,8 @@ def lib():
         "dflash_inject_kv": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
         "dflash_draft_block": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_void_p]),
+        "dflash_draft_block_static": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                c_void_p, c_void_p]),
         "dflash_select_path": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                          c_void_p, c_void_p, c_void_p]),
         "dflash_select_sample": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_float,
@@ -103,7 +105,7 @@ def lib():
 
 EXPORTED = ("dflash_config_check", "dflash_kv_cache_bytes", "dflash_kv_cache_layout", "dflash_workspace_bytes",
             "dflash_create", "dflash_destroy", "dflash_reset_seqs", "dflash_inject_kv", "dflash_draft_block",
-            "dflash_select_path", "dflash_select_sample", "dflash_verify_rejection", "dflash_verify_greedy",
+            "dflash_draft_block_static", "dflash_select_path", "dflash_select_sample", "dflash_verify_rejection", "dflash_verify_greedy",
             "dflash_synth_target_argmax", "dflash_quantize_fp8_rows", "dflash_set_lm_head_fp8", "dflash_set_mlp_fp8",
             "dflash_set_attn_fp8", "dflash_set_inject_fp8", "dflash_timing_enable",
             "dflash_timing_read", "dflash_get_device_error", "dflash_status_string", "dflash_last_error")
@@ -291,6 +293,11 @@ class Drafter:
         check("dflash_draft_block", lib().dflash_draft_block(self.h, seq_ids.numel(), ptr(seq_ids), ptr(anchor_ids),
                                                              ptr(topk_ids), ptr(topk_logits), ptr(h_final),
                                                              ptr(logits), stream))
+
+    def dflash_draft_block_static(self, seq_ids, anchor_ids, topk_ids, topk_logits, h_final, logits=None, stream=None):
+        check("dflash_draft_block_static", lib().dflash_draft_block_static(
+            self.h, seq_ids.numel(), ptr(seq_ids), ptr(anchor_ids), ptr(topk_ids), ptr(topk_logits), ptr(h_final),
+            ptr(logits), stream))
 
     def dflash_select_path(self, anchor_ids, topk_ids, topk_logits, h_final, mode, path_ids, path_score=None,
                            margin=None, stream=None):

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <vector>
 
 #include "../../include/dflash.h"
@@ -16,6 +17,14 @@
 using namespace dfl;
 
 static thread_local char g_err[512] = "";
+
+// Scratch of dflash_draft_block_static (the allocation-free draft): one copy per GPU the library
+// runs on, alive until the process ends.  Host code uses its device address from
+// hipGetSymbolAddress (kept per device in g_scratch), never the array's name.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[STATIC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+static std::atomic<void*> g_scratch[MAX_DEVICES];
 
 static dflash_status fail(dflash_status s, const char* fmt, ...) {
   va_list ap;
@@ -265,6 +274,8 @@ Handle* as_handle(dflash_handle* h) {
 
 template <typename P>
 P* wsp(Handle* H, size_t off) { return reinterpret_cast<P*>(H->ws + off); }
+template <typename P>
+P* wsp(char* ws, size_t off) { return reinterpret_cast<P*>(ws + off); }
 
 const void* LW(Handle* H, int l, int t) { return H->layers[(size_t)l * DFLASH_LAYER_TENSORS + t]; }
 
@@ -283,6 +294,334 @@ GemmParams gemm_base(const void* A, int lda, int M, int N, int K) {
   p.ldb = K;
   p.block = 1;
   return p;
+}
+
+// One draft pass over the workspace at `ws` with regions `W`, whose activation planes hold `Mmax`
+// rows.  Host checks of the FP8 row limits come first (before anything is enqueued).
+dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, int32_t n_seq, const int32_t* seq_ids,
+                         const int32_t* anchor_ids, int32_t* topk_ids, float* topk_logits, float* h_final,
+                         float* logits, hipStream_t st) {
+  const dflash_config* c = &H->cfg;
+  const bool b = bf(c);
+  const int K = c->block_size, d = c->hidden, M = n_seq * K;
+  bool any_mlp_fp8 = false;
+  for (const auto& m : H->mlp_fp8) any_mlp_fp8 |= m.gu != nullptr;
+  if (any_mlp_fp8 && (gemm_plan(true, GEMM_SWIGLU, M, 2 * c->ffn, d).kind != 3 ||
+                      gemm_plan(true, GEMM_PARTIAL, M, d, c->ffn).kind != 3))
+    return fail(DFLASH_E_UNSUPPORTED, "FP8 MLP weights take at most 16 draft rows (n_seq * block_size = %d) and a "
+                "hidden size of at most 2048", M);
+  bool any_attn_fp8 = false;
+  for (const auto& a8 : H->attn_fp8) any_attn_fp8 |= a8.qkv != nullptr;
+  if (any_attn_fp8 && (gemm_plan(true, GEMM_PARTIAL, M, c->n_heads * c->head_dim + 2 * c->n_kv_heads * c->head_dim,
+                                 d).kind != 3 ||
+                       gemm_plan(true, GEMM_PARTIAL, M, d, c->n_heads * c->head_dim).kind != 3))
+    return fail(DFLASH_E_UNSUPPORTED, "FP8 attention projections take at most 16 draft rows (n_seq * block_size = %d)",
+                M);
+  if (H->lm_fp8 && gemm_plan(true, GEMM_TOPK, M, c->vocab, d).kind != 4)
+    return fail(DFLASH_E_UNSUPPORTED, "the FP8 lm_head takes at most 16 draft rows (n_seq * block_size = %d) and a "
+                "hidden size that is a multiple of 512 up to 2048", M);
+  const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
+  float* part = wsp<float>(ws, W.part);
+  SeqCtx* ctx = wsp<SeqCtx>(ws, W.ctx);
+  int* counters = wsp<int>(ws, W.counters);
+  float* hA = wsp<float>(ws, W.h0);
+  float* hB = wsp<float>(ws, W.h1);
+  char* act_y = ws + W.act_y;
+  char* act_o = ws + W.act_o;
+  char* act_s = ws + W.act_s;
+  RowArgs ra{};
+  ra.K = K;
+  ra.d = d;
+  ra.mask_id = c->mask_id;
+  ra.use_conv = c->use_conv;
+  ra.eps = c->rms_eps;
+  ra.anchor = anchor_ids;
+  ra.vocab = c->vocab;
+  ra.dev_err = dev_err(H);
+  ra.embed = H->g_embed;
+  ra.h_out = hA;
+  ra.pre_gain = LW(H, 0, DFLASH_L_ATTN_NORM);
+  ra.pre_w = LW(H, 0, DFLASH_L_CONV_ATTN_PRE_W);
+  ra.pre_b = LW(H, 0, DFLASH_L_CONV_ATTN_PRE_B);
+  ra.y = act_y;
+  ra.ldy = d;
+  ra.y_plane = Mmax * d;
+  ra.plan = PlanArgs{H->max_seqs, c->window, seq_ids, seq_len(H), seq_base(H), ctx, counters};
+  // Per-channel conv: each conv takes a correction GEMM (rows x [2 d/G][d]) on its input first.
+  // A post-conv runs as: reduce the sublayer's k-split partials into activation planes a, the
+  // correction GEMM on a, then the residual + post-conv + RMSNorm kernel, which writes z; a
+  // pre-conv as: the correction GEMM on z, then the conv itself, which writes the GEMM input y.
+  const bool pc = per_channel_conv(c);
+  const int Ncorr = pc ? 2 * d / c->conv_group : 0;
+  char* act_a = ws + W.act_a;
+  char* act_z = ws + W.act_z;
+  auto pc_corr = [&](const char* x, const void* wc, int& splits) -> dflash_status {
+    GemmParams gc = gemm_base(x, d, M, Ncorr, d);
+    gc.a_plane = Mmax * d;
+    gc.seg[0] = wc;
+    gc.seg_rows = Ncorr;
+    gc.part = part;
+    GemmPlan pl = gemm_plan(b, GEMM_PARTIAL, M, Ncorr, d);
+    HIP_TRY(gemm_launch(b, pl, GEMM_PARTIAL, gc, st));
+    splits = pl.splits;
+    return DFLASH_OK;
+  };
+  auto pc_pre = [&](const void* wc, const void* base) -> dflash_status {
+    int sp = 1;
+    dflash_status s2 = pc_corr(act_z, wc, sp);
+    if (s2 != DFLASH_OK) return s2;
+    PcArgs pa{};
+    pa.K = K; pa.d = d; pa.G = c->conv_group; pa.splits = sp; pa.part_rows = M; pa.ldo = d;
+    pa.plane = Mmax * d;
+    pa.x = act_z; pa.part = part; pa.base = base; pa.out = act_y;
+    HIP_TRY(launch_conv_apply(b, pa, M, st));
+    return DFLASH_OK;
+  };
+  auto pc_post = [&](int splits, float* h_in, float* h_out, const void* wc, const void* base, const void* gain,
+                     bool final) -> dflash_status {
+    ReduceArgs rd{M, d, splits, M, Mmax * d, nullptr, 0, part, act_a};
+    HIP_TRY(launch_reduce_store(b, rd, st));
+    int sp = 1;
+    dflash_status s2 = pc_corr(act_a, wc, sp);
+    if (s2 != DFLASH_OK) return s2;
+    PcArgs pa{};
+    pa.K = K; pa.d = d; pa.G = c->conv_group; pa.splits = sp; pa.part_rows = M; pa.ldo = d;
+    pa.plane = Mmax * d; pa.eps = c->rms_eps;
+    pa.h_in = h_in; pa.h_out = h_out; pa.x = act_a; pa.part = part; pa.base = base; pa.gain = gain;
+    pa.final_norm = final ? 1 : 0;
+    pa.out = final ? (void*)h_final : (void*)act_z;
+    pa.out2 = final ? (void*)(ws + W.hsplit) : nullptr;
+    HIP_TRY(launch_post_pre_pc(b, pa, M, st));
+    return DFLASH_OK;
+  };
+  if (pc) {   // h = E[x], z = RMSNorm(h) (the embed kernel without its conv), then the pre-conv
+    RowArgs re = ra;
+    re.use_conv = 0;
+    re.y = act_z;
+    HIP_TRY(launch_embed_pre(b, re, M, st));
+    dflash_status s2 = pc_pre(LW(H, 0, DFLASH_L_CONV_ATTN_PRE_W), LW(H, 0, DFLASH_L_CONV_ATTN_PRE_B));
+    if (s2 != DFLASH_OK) return s2;
+  } else {
+    HIP_TRY(launch_embed_pre(b, ra, M, st));
+  }
+  ra.plan = PlanArgs{};
+  const int chunks = attn_chunks(c, n_seq);
+  for (int l = 0; l < c->n_layers; ++l) {
+    // q, k, v = y [W_q; W_k; W_v]^T
+    const int G = qw / kvw;
+    GemmParams gq = gemm_base(act_y, d, M, qw + 2 * kvw, d);
+    gq.a_plane = Mmax * d;
+    for (int i = 0; i < G; ++i)
+      gq.seg[i] = reinterpret_cast<const char*>(LW(H, l, DFLASH_L_WQ)) + (size_t)i * kvw * d * esize(c);
+    gq.seg[G] = LW(H, l, DFLASH_L_WK);
+    gq.seg[G + 1] = LW(H, l, DFLASH_L_WV);
+    gq.seg_rows = kvw;
+    gq.part = part;
+    const Handle::Fp8Attn* a8 = (size_t)l < H->attn_fp8.size() && H->attn_fp8[l].qkv ? &H->attn_fp8[l] : nullptr;
+    if (a8) {   // one stacked [wq; wk; wv] segment of E4M3 codes (checked up front: the stream kernel)
+      gq.seg[0] = a8->qkv;
+      gq.seg_rows = qw + 2 * kvw;
+      gq.ldb = d;
+      gq.row_scale = a8->qkv_s;
+    }
+    GemmPlan pq = gemm_plan(b, GEMM_PARTIAL, M, qw + 2 * kvw, d);
+    HIP_TRY(gemm_launch(b, pq, GEMM_PARTIAL, gq, st));
+    QkvArgs qa{};
+    qa.K = K;
+    qa.nh = c->n_heads;
+    qa.nkv = c->n_kv_heads;
+    qa.dh = c->head_dim;
+    qa.N = qw + 2 * kvw;
+    qa.splits = pq.splits;
+    qa.part_rows = M;
+    qa.eps = c->rms_eps;
+    qa.log_theta = log((double)c->rope_theta);
+    qa.ctx = ctx;
+    qa.part = part;
+    qa.q_gain = LW(H, l, DFLASH_L_Q_NORM);
+    qa.k_gain = LW(H, l, DFLASH_L_K_NORM);
+    qa.q = ws + W.qb;
+    qa.q_plane = Mmax * qw;
+    qa.k = ws + W.kb;
+    qa.v = ws + W.vb;
+    HIP_TRY(launch_qkv_post(b, qa, M, st));
+    AttnArgs aa{};
+    aa.K = K;
+    aa.nh = c->n_heads;
+    aa.nkv = c->n_kv_heads;
+    aa.dh = c->head_dim;
+    aa.window = c->window;
+    aa.max_seqs = H->max_seqs;
+    aa.chunks = chunks;
+    aa.layer = l;
+    aa.scale = 1.0f / sqrtf((float)c->head_dim);
+    aa.ctx = ctx;
+    aa.q = qa.q;
+    aa.kb = qa.k;
+    aa.vb = qa.v;
+    aa.kcache = H->kv + H->kvl.k_offset;
+    aa.vcache = H->kv + H->kvl.v_offset;
+    aa.o_part = wsp<float>(ws, W.o_part);
+    aa.m_part = wsp<float>(ws, W.m_part);
+    aa.l_part = wsp<float>(ws, W.l_part);
+    aa.o = act_o;
+    aa.q_plane = Mmax * qw;
+    aa.o_plane = Mmax * qw;
+    HIP_TRY(launch_attention(b, aa, n_seq, st));
+    // a = o W_o^T
+    GemmParams go = gemm_base(act_o, qw, M, d, qw);
+    go.a_plane = Mmax * qw;
+    go.seg[0] = LW(H, l, DFLASH_L_WO);
+    go.seg_rows = d;
+    go.part = part;
+    if (a8) {
+      go.seg[0] = a8->o;
+      go.ldb = qw;
+      go.row_scale = a8->o_s;
+    }
+    GemmPlan po = gemm_plan(b, GEMM_PARTIAL, M, d, qw);
+    HIP_TRY(gemm_launch(b, po, GEMM_PARTIAL, go, st));
+    RowArgs rp = ra;
+    rp.h_in = hA;
+    rp.h_out = hB;
+    rp.part = part;
+    rp.splits = po.splits;
+    rp.part_rows = M;
+    rp.post_w = LW(H, l, DFLASH_L_CONV_ATTN_POST_W);
+    rp.post_b = LW(H, l, DFLASH_L_CONV_ATTN_POST_B);
+    rp.pre_gain = LW(H, l, DFLASH_L_MLP_NORM);
+    rp.pre_w = LW(H, l, DFLASH_L_CONV_MLP_PRE_W);
+    rp.pre_b = LW(H, l, DFLASH_L_CONV_MLP_PRE_B);
+    rp.final_norm = 0;
+    rp.y = act_y;
+    rp.ldy = d;
+    if (pc) {
+      dflash_status s2 = pc_post(po.splits, hA, hB, rp.post_w, rp.post_b, rp.pre_gain, false);
+      if (s2 == DFLASH_OK) s2 = pc_pre(rp.pre_w, rp.pre_b);
+      if (s2 != DFLASH_OK) return s2;
+    } else {
+      HIP_TRY(launch_post_pre(b, rp, M, st));
+    }
+    // s = silu(y W_gate^T) * (y W_up^T)
+    GemmParams gg = gemm_base(act_y, d, M, 2 * c->ffn, d);
+    gg.a_plane = Mmax * d;
+    gg.seg[0] = LW(H, l, DFLASH_L_W_GATE);
+    gg.seg[1] = LW(H, l, DFLASH_L_W_UP);
+    gg.seg_rows = c->ffn;
+    gg.half = c->ffn;
+    gg.out = act_s;
+    gg.out_plane = Mmax * c->ffn;
+    gg.part = part;
+    const Handle::Fp8Mlp* m8 = (size_t)l < H->mlp_fp8.size() && H->mlp_fp8[l].gu ? &H->mlp_fp8[l] : nullptr;
+    if (m8) {   // one stacked [gate; up] segment of E4M3 codes (checked up front: the stream kernel)
+      gg.seg[0] = m8->gu;
+      gg.seg[1] = nullptr;
+      gg.seg_rows = 2 * c->ffn;
+      gg.ldb = d;
+      gg.row_scale = m8->gu_s;
+    }
+    if (b && M <= 64) {
+      GemmPlan pg = gemm_plan(b, GEMM_SWIGLU, M, 2 * c->ffn, d);
+      HIP_TRY(gemm_launch(b, pg, GEMM_SWIGLU, gg, st));
+    } else {
+      gg.half = 0;
+      GemmPlan pg = gemm_plan(b, GEMM_PARTIAL, M, 2 * c->ffn, d);
+      HIP_TRY(gemm_launch(b, pg, GEMM_PARTIAL, gg, st));
+      SwigluArgs sa{M, c->ffn, pg.splits, M, Mmax * c->ffn, part, act_s};
+      HIP_TRY(launch_swiglu(b, sa, st));
+    }
+    // m = s W_down^T
+    GemmParams gd = gemm_base(act_s, c->ffn, M, d, c->ffn);
+    gd.a_plane = Mmax * c->ffn;
+    gd.seg[0] = LW(H, l, DFLASH_L_W_DOWN);
+    gd.seg_rows = d;
+    gd.part = part;
+    if (m8) {
+      gd.seg[0] = m8->dn;
+      gd.ldb = c->ffn;
+      gd.row_scale = m8->dn_s;
+    }
+    GemmPlan pd = gemm_plan(b, GEMM_PARTIAL, M, d, c->ffn);
+    HIP_TRY(gemm_launch(b, pd, GEMM_PARTIAL, gd, st));
+    RowArgs rm = ra;
+    rm.h_in = hB;
+    rm.h_out = hA;
+    rm.part = part;
+    rm.splits = pd.splits;
+    rm.part_rows = M;
+    rm.post_w = LW(H, l, DFLASH_L_CONV_MLP_POST_W);
+    rm.post_b = LW(H, l, DFLASH_L_CONV_MLP_POST_B);
+    if (l + 1 < c->n_layers) {
+      rm.pre_gain = LW(H, l + 1, DFLASH_L_ATTN_NORM);
+      rm.pre_w = LW(H, l + 1, DFLASH_L_CONV_ATTN_PRE_W);
+      rm.pre_b = LW(H, l + 1, DFLASH_L_CONV_ATTN_PRE_B);
+      rm.final_norm = 0;
+      rm.y = act_y;
+      rm.ldy = d;
+    } else {
+      rm.pre_gain = H->g_fnorm;
+      rm.final_norm = 1;
+      rm.y = h_final;
+      rm.y2 = ws + W.hsplit;
+      rm.ldy = d;
+    }
+    if (pc) {
+      const bool last = l + 1 == c->n_layers;
+      dflash_status s2 = pc_post(pd.splits, hB, hA, rm.post_w, rm.post_b, rm.pre_gain, last);
+      if (s2 == DFLASH_OK && !last) s2 = pc_pre(rm.pre_w, rm.pre_b);
+      if (s2 != DFLASH_OK) return s2;
+    } else {
+      HIP_TRY(launch_post_pre(b, rm, M, st));
+    }
+  }
+  // shared lm_head + top-16 per draft slot
+  GemmParams gl = gemm_base(b ? (const void*)(ws + W.hsplit) : (const void*)h_final, d, M, c->vocab, d);
+  gl.a_plane = Mmax * d;
+  gl.seg[0] = H->g_lm;
+  gl.seg_rows = c->vocab;
+  gl.block = K;
+  MergeArgs ma{};
+  ma.K = K;
+  ma.out_ids = topk_ids;
+  ma.out_vals = topk_logits;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (H->t_cap > 0) {
+    ev0 = H->t_ev[2 * H->t_next];
+    ev1 = H->t_ev[2 * H->t_next + 1];
+    H->t_next = (H->t_next + 1) % H->t_cap;
+    if (H->t_count < H->t_cap) H->t_count++;
+    HIP_TRY(hipEventRecord(ev0, st));
+  }
+  if (b) {
+    gl.tk_val = wsp<float>(ws, W.tk_val);
+    gl.tk_id = wsp<int>(ws, W.tk_id);
+    gl.logits = logits;
+    gl.counter = counters;
+    GemmPlan pl = gemm_plan(b, GEMM_TOPK, M, c->vocab, d);
+    if (H->lm_fp8) {
+      // FP8 lm_head: only the independent-wave kernel (<= 16 rows) takes it (checked up front)
+      gl.seg[0] = H->lm_fp8;
+      gl.ldb = d;                     // bytes per weight row
+      gl.row_scale = H->lm_fp8_scale;
+    }
+    HIP_TRY(gemm_launch(b, pl, GEMM_TOPK, gl, st));
+    if (ev1) HIP_TRY(hipEventRecord(ev1, st));
+    ma.ncand = pl.groups * TOPK;
+    ma.vals = gl.tk_val;
+    ma.ids = gl.tk_id;
+  } else {
+    gl.part = part;
+    GemmPlan pl = gemm_plan(b, GEMM_PARTIAL, M, c->vocab, d);
+    HIP_TRY(gemm_launch(b, pl, GEMM_PARTIAL, gl, st));
+    if (ev1) HIP_TRY(hipEventRecord(ev1, st));
+    ma.ncand = c->vocab;
+    ma.vals = part;
+    ma.ids = nullptr;
+    ma.logits_out = logits;
+  }
+  ma.counters = counters;
+  HIP_TRY(launch_topk_merge(ma, n_seq * (K - 1), st));
+  return DFLASH_OK;
 }
 
 }  // namespace
@@ -510,328 +849,34 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t*
   if (!seq_ids || !anchor_ids || !topk_ids || !topk_logits || !h_final)
     return fail(DFLASH_E_INVALID, "NULL seq_ids, anchor_ids, topk_ids, topk_logits or h_final");
   hipStream_t st = (hipStream_t)stream;
-  const bool b = bf(c);
-  const int K = c->block_size, d = c->hidden, M = n_seq * K;
-  bool any_mlp_fp8 = false;
-  for (const auto& m : H->mlp_fp8) any_mlp_fp8 |= m.gu != nullptr;
-  if (any_mlp_fp8 && (gemm_plan(true, GEMM_SWIGLU, M, 2 * c->ffn, d).kind != 3 ||
-                      gemm_plan(true, GEMM_PARTIAL, M, d, c->ffn).kind != 3))
-    return fail(DFLASH_E_UNSUPPORTED, "FP8 MLP weights take at most 16 draft rows (n_seq * block_size = %d) and a "
-                "hidden size of at most 2048", M);
-  bool any_attn_fp8 = false;
-  for (const auto& a8 : H->attn_fp8) any_attn_fp8 |= a8.qkv != nullptr;
-  if (any_attn_fp8 && (gemm_plan(true, GEMM_PARTIAL, M, c->n_heads * c->head_dim + 2 * c->n_kv_heads * c->head_dim,
-                                 d).kind != 3 ||
-                       gemm_plan(true, GEMM_PARTIAL, M, d, c->n_heads * c->head_dim).kind != 3))
-    return fail(DFLASH_E_UNSUPPORTED, "FP8 attention projections take at most 16 draft rows (n_seq * block_size = %d)",
-                M);
-  if (H->lm_fp8 && gemm_plan(true, GEMM_TOPK, M, c->vocab, d).kind != 4)
-    return fail(DFLASH_E_UNSUPPORTED, "the FP8 lm_head takes at most 16 draft rows (n_seq * block_size = %d) and a "
-                "hidden size that is a multiple of 512 up to 2048", M);
-  const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
-  const WsLayout& W = H->wl;
-  float* part = wsp<float>(H, W.part);
-  SeqCtx* ctx = wsp<SeqCtx>(H, W.ctx);
-  int* counters = wsp<int>(H, W.counters);
-  const size_t Mmax = (size_t)H->max_batch * K;   // rows of every activation plane
-  float* hA = wsp<float>(H, W.h0);
-  float* hB = wsp<float>(H, W.h1);
-  char* act_y = H->ws + W.act_y;
-  char* act_o = H->ws + W.act_o;
-  char* act_s = H->ws + W.act_s;
-  RowArgs ra{};
-  ra.K = K;
-  ra.d = d;
-  ra.mask_id = c->mask_id;
-  ra.use_conv = c->use_conv;
-  ra.eps = c->rms_eps;
-  ra.anchor = anchor_ids;
-  ra.vocab = c->vocab;
-  ra.dev_err = dev_err(H);
-  ra.embed = H->g_embed;
-  ra.h_out = hA;
-  ra.pre_gain = LW(H, 0, DFLASH_L_ATTN_NORM);
-  ra.pre_w = LW(H, 0, DFLASH_L_CONV_ATTN_PRE_W);
-  ra.pre_b = LW(H, 0, DFLASH_L_CONV_ATTN_PRE_B);
-  ra.y = act_y;
-  ra.ldy = d;
-  ra.y_plane = Mmax * d;
-  ra.plan = PlanArgs{H->max_seqs, c->window, seq_ids, seq_len(H), seq_base(H), ctx, counters};
-  // Per-channel conv: each conv takes a correction GEMM (rows x [2 d/G][d]) on its input first.
-  // A post-conv runs as: reduce the sublayer's k-split partials into activation planes a, the
-  // correction GEMM on a, then the residual + post-conv + RMSNorm kernel, which writes z; a
-  // pre-conv as: the correction GEMM on z, then the conv itself, which writes the GEMM input y.
-  const bool pc = per_channel_conv(c);
-  const int Ncorr = pc ? 2 * d / c->conv_group : 0;
-  char* act_a = H->ws + W.act_a;
-  char* act_z = H->ws + W.act_z;
-  auto pc_corr = [&](const char* x, const void* wc, int& splits) -> dflash_status {
-    GemmParams gc = gemm_base(x, d, M, Ncorr, d);
-    gc.a_plane = Mmax * d;
-    gc.seg[0] = wc;
-    gc.seg_rows = Ncorr;
-    gc.part = part;
-    GemmPlan pl = gemm_plan(b, GEMM_PARTIAL, M, Ncorr, d);
-    HIP_TRY(gemm_launch(b, pl, GEMM_PARTIAL, gc, st));
-    splits = pl.splits;
-    return DFLASH_OK;
-  };
-  auto pc_pre = [&](const void* wc, const void* base) -> dflash_status {
-    int sp = 1;
-    dflash_status s2 = pc_corr(act_z, wc, sp);
-    if (s2 != DFLASH_OK) return s2;
-    PcArgs pa{};
-    pa.K = K; pa.d = d; pa.G = c->conv_group; pa.splits = sp; pa.part_rows = M; pa.ldo = d;
-    pa.plane = Mmax * d;
-    pa.x = act_z; pa.part = part; pa.base = base; pa.out = act_y;
-    HIP_TRY(launch_conv_apply(b, pa, M, st));
-    return DFLASH_OK;
-  };
-  auto pc_post = [&](int splits, float* h_in, float* h_out, const void* wc, const void* base, const void* gain,
-                     bool final) -> dflash_status {
-    ReduceArgs rd{M, d, splits, M, Mmax * d, nullptr, 0, part, act_a};
-    HIP_TRY(launch_reduce_store(b, rd, st));
-    int sp = 1;
-    dflash_status s2 = pc_corr(act_a, wc, sp);
-    if (s2 != DFLASH_OK) return s2;
-    PcArgs pa{};
-    pa.K = K; pa.d = d; pa.G = c->conv_group; pa.splits = sp; pa.part_rows = M; pa.ldo = d;
-    pa.plane = Mmax * d; pa.eps = c->rms_eps;
-    pa.h_in = h_in; pa.h_out = h_out; pa.x = act_a; pa.part = part; pa.base = base; pa.gain = gain;
-    pa.final_norm = final ? 1 : 0;
-    pa.out = final ? (void*)h_final : (void*)act_z;
-    pa.out2 = final ? (void*)(H->ws + W.hsplit) : nullptr;
-    HIP_TRY(launch_post_pre_pc(b, pa, M, st));
-    return DFLASH_OK;
-  };
-  if (pc) {   // h = E[x], z = RMSNorm(h) (the embed kernel without its conv), then the pre-conv
-    RowArgs re = ra;
-    re.use_conv = 0;
-    re.y = act_z;
-    HIP_TRY(launch_embed_pre(b, re, M, st));
-    dflash_status s2 = pc_pre(LW(H, 0, DFLASH_L_CONV_ATTN_PRE_W), LW(H, 0, DFLASH_L_CONV_ATTN_PRE_B));
-    if (s2 != DFLASH_OK) return s2;
-  } else {
-    HIP_TRY(launch_embed_pre(b, ra, M, st));
+  return draft_impl(H, H->ws, H->wl, (size_t)H->max_batch * c->block_size, n_seq, seq_ids, anchor_ids, topk_ids,
+                    topk_logits, h_final, logits, st);
+}
+
+dflash_status dflash_draft_block_static(dflash_handle* h, int32_t n_seq, const int32_t* seq_ids, const int32_t* anchor_ids,
+                                        int32_t* topk_ids, float* topk_logits, float* h_final, float* logits,
+                                        void* stream) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  const dflash_config* c = &H->cfg;
+  if (n_seq < 1 || n_seq > 4096) return fail(DFLASH_E_SHAPE, "n_seq %d outside [1, 4096]", n_seq);
+  if (!seq_ids || !anchor_ids || !topk_ids || !topk_logits || !h_final)
+    return fail(DFLASH_E_INVALID, "NULL seq_ids, anchor_ids, topk_ids, topk_logits or h_final");
+  // the draft's regions laid out for exactly n_seq sequences (injection regions at their minimum)
+  const WsLayout wl = ws_layout(c, n_seq, 1, 1);
+  if (wl.bytes > STATIC_SCRATCH_BYTES)
+    return fail(DFLASH_E_SHAPE, "a draft of %d sequences needs %zu bytes of scratch; the static scratch holds %zu",
+                n_seq, wl.bytes, STATIC_SCRATCH_BYTES);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(DFLASH_E_UNSUPPORTED, "device %d: at most %d devices", dev, MAX_DEVICES);
+  void* base = g_scratch[dev].load(std::memory_order_acquire);
+  if (!base) {   // first call on this device: the array's address there (two racing first calls agree)
+    HIP_TRY(hipGetSymbolAddress(&base, HIP_SYMBOL(scratch)));
+    g_scratch[dev].store(base, std::memory_order_release);
   }
-  ra.plan = PlanArgs{};
-  const int chunks = attn_chunks(c, n_seq);
-  for (int l = 0; l < c->n_layers; ++l) {
-    // q, k, v = y [W_q; W_k; W_v]^T
-    const int G = qw / kvw;
-    GemmParams gq = gemm_base(act_y, d, M, qw + 2 * kvw, d);
-    gq.a_plane = Mmax * d;
-    for (int i = 0; i < G; ++i)
-      gq.seg[i] = reinterpret_cast<const char*>(LW(H, l, DFLASH_L_WQ)) + (size_t)i * kvw * d * esize(c);
-    gq.seg[G] = LW(H, l, DFLASH_L_WK);
-    gq.seg[G + 1] = LW(H, l, DFLASH_L_WV);
-    gq.seg_rows = kvw;
-    gq.part = part;
-    const Handle::Fp8Attn* a8 = (size_t)l < H->attn_fp8.size() && H->attn_fp8[l].qkv ? &H->attn_fp8[l] : nullptr;
-    if (a8) {   // one stacked [wq; wk; wv] segment of E4M3 codes (checked up front: the stream kernel)
-      gq.seg[0] = a8->qkv;
-      gq.seg_rows = qw + 2 * kvw;
-      gq.ldb = d;
-      gq.row_scale = a8->qkv_s;
-    }
-    GemmPlan pq = gemm_plan(b, GEMM_PARTIAL, M, qw + 2 * kvw, d);
-    HIP_TRY(gemm_launch(b, pq, GEMM_PARTIAL, gq, st));
-    QkvArgs qa{};
-    qa.K = K;
-    qa.nh = c->n_heads;
-    qa.nkv = c->n_kv_heads;
-    qa.dh = c->head_dim;
-    qa.N = qw + 2 * kvw;
-    qa.splits = pq.splits;
-    qa.part_rows = M;
-    qa.eps = c->rms_eps;
-    qa.log_theta = log((double)c->rope_theta);
-    qa.ctx = ctx;
-    qa.part = part;
-    qa.q_gain = LW(H, l, DFLASH_L_Q_NORM);
-    qa.k_gain = LW(H, l, DFLASH_L_K_NORM);
-    qa.q = H->ws + W.qb;
-    qa.q_plane = Mmax * qw;
-    qa.k = H->ws + W.kb;
-    qa.v = H->ws + W.vb;
-    HIP_TRY(launch_qkv_post(b, qa, M, st));
-    AttnArgs aa{};
-    aa.K = K;
-    aa.nh = c->n_heads;
-    aa.nkv = c->n_kv_heads;
-    aa.dh = c->head_dim;
-    aa.window = c->window;
-    aa.max_seqs = H->max_seqs;
-    aa.chunks = chunks;
-    aa.layer = l;
-    aa.scale = 1.0f / sqrtf((float)c->head_dim);
-    aa.ctx = ctx;
-    aa.q = qa.q;
-    aa.kb = qa.k;
-    aa.vb = qa.v;
-    aa.kcache = H->kv + H->kvl.k_offset;
-    aa.vcache = H->kv + H->kvl.v_offset;
-    aa.o_part = wsp<float>(H, W.o_part);
-    aa.m_part = wsp<float>(H, W.m_part);
-    aa.l_part = wsp<float>(H, W.l_part);
-    aa.o = act_o;
-    aa.q_plane = Mmax * qw;
-    aa.o_plane = Mmax * qw;
-    HIP_TRY(launch_attention(b, aa, n_seq, st));
-    // a = o W_o^T
-    GemmParams go = gemm_base(act_o, qw, M, d, qw);
-    go.a_plane = Mmax * qw;
-    go.seg[0] = LW(H, l, DFLASH_L_WO);
-    go.seg_rows = d;
-    go.part = part;
-    if (a8) {
-      go.seg[0] = a8->o;
-      go.ldb = qw;
-      go.row_scale = a8->o_s;
-    }
-    GemmPlan po = gemm_plan(b, GEMM_PARTIAL, M, d, qw);
-    HIP_TRY(gemm_launch(b, po, GEMM_PARTIAL, go, st));
-    RowArgs rp = ra;
-    rp.h_in = hA;
-    rp.h_out = hB;
-    rp.part = part;
-    rp.splits = po.splits;
-    rp.part_rows = M;
-    rp.post_w = LW(H, l, DFLASH_L_CONV_ATTN_POST_W);
-    rp.post_b = LW(H, l, DFLASH_L_CONV_ATTN_POST_B);
-    rp.pre_gain = LW(H, l, DFLASH_L_MLP_NORM);
-    rp.pre_w = LW(H, l, DFLASH_L_CONV_MLP_PRE_W);
-    rp.pre_b = LW(H, l, DFLASH_L_CONV_MLP_PRE_B);
-    rp.final_norm = 0;
-    rp.y = act_y;
-    rp.ldy = d;
-    if (pc) {
-      dflash_status s2 = pc_post(po.splits, hA, hB, rp.post_w, rp.post_b, rp.pre_gain, false);
-      if (s2 == DFLASH_OK) s2 = pc_pre(rp.pre_w, rp.pre_b);
-      if (s2 != DFLASH_OK) return s2;
-    } else {
-      HIP_TRY(launch_post_pre(b, rp, M, st));
-    }
-    // s = silu(y W_gate^T) * (y W_up^T)
-    GemmParams gg = gemm_base(act_y, d, M, 2 * c->ffn, d);
-    gg.a_plane = Mmax * d;
-    gg.seg[0] = LW(H, l, DFLASH_L_W_GATE);
-    gg.seg[1] = LW(H, l, DFLASH_L_W_UP);
-    gg.seg_rows = c->ffn;
-    gg.half = c->ffn;
-    gg.out = act_s;
-    gg.out_plane = Mmax * c->ffn;
-    gg.part = part;
-    const Handle::Fp8Mlp* m8 = (size_t)l < H->mlp_fp8.size() && H->mlp_fp8[l].gu ? &H->mlp_fp8[l] : nullptr;
-    if (m8) {   // one stacked [gate; up] segment of E4M3 codes (checked up front: the stream kernel)
-      gg.seg[0] = m8->gu;
-      gg.seg[1] = nullptr;
-      gg.seg_rows = 2 * c->ffn;
-      gg.ldb = d;
-      gg.row_scale = m8->gu_s;
-    }
-    if (b && M <= 64) {
-      GemmPlan pg = gemm_plan(b, GEMM_SWIGLU, M, 2 * c->ffn, d);
-      HIP_TRY(gemm_launch(b, pg, GEMM_SWIGLU, gg, st));
-    } else {
-      gg.half = 0;
-      GemmPlan pg = gemm_plan(b, GEMM_PARTIAL, M, 2 * c->ffn, d);
-      HIP_TRY(gemm_launch(b, pg, GEMM_PARTIAL, gg, st));
-      SwigluArgs sa{M, c->ffn, pg.splits, M, Mmax * c->ffn, part, act_s};
-      HIP_TRY(launch_swiglu(b, sa, st));
-    }
-    // m = s W_down^T
-    GemmParams gd = gemm_base(act_s, c->ffn, M, d, c->ffn);
-    gd.a_plane = Mmax * c->ffn;
-    gd.seg[0] = LW(H, l, DFLASH_L_W_DOWN);
-    gd.seg_rows = d;
-    gd.part = part;
-    if (m8) {
-      gd.seg[0] = m8->dn;
-      gd.ldb = c->ffn;
-      gd.row_scale = m8->dn_s;
-    }
-    GemmPlan pd = gemm_plan(b, GEMM_PARTIAL, M, d, c->ffn);
-    HIP_TRY(gemm_launch(b, pd, GEMM_PARTIAL, gd, st));
-    RowArgs rm = ra;
-    rm.h_in = hB;
-    rm.h_out = hA;
-    rm.part = part;
-    rm.splits = pd.splits;
-    rm.part_rows = M;
-    rm.post_w = LW(H, l, DFLASH_L_CONV_MLP_POST_W);
-    rm.post_b = LW(H, l, DFLASH_L_CONV_MLP_POST_B);
-    if (l + 1 < c->n_layers) {
-      rm.pre_gain = LW(H, l + 1, DFLASH_L_ATTN_NORM);
-      rm.pre_w = LW(H, l + 1, DFLASH_L_CONV_ATTN_PRE_W);
-      rm.pre_b = LW(H, l + 1, DFLASH_L_CONV_ATTN_PRE_B);
-      rm.final_norm = 0;
-      rm.y = act_y;
-      rm.ldy = d;
-    } else {
-      rm.pre_gain = H->g_fnorm;
-      rm.final_norm = 1;
-      rm.y = h_final;
-      rm.y2 = H->ws + W.hsplit;
-      rm.ldy = d;
-    }
-    if (pc) {
-      const bool last = l + 1 == c->n_layers;
-      dflash_status s2 = pc_post(pd.splits, hB, hA, rm.post_w, rm.post_b, rm.pre_gain, last);
-      if (s2 == DFLASH_OK && !last) s2 = pc_pre(rm.pre_w, rm.pre_b);
-      if (s2 != DFLASH_OK) return s2;
-    } else {
-      HIP_TRY(launch_post_pre(b, rm, M, st));
-    }
-  }
-  // shared lm_head + top-16 per draft slot
-  GemmParams gl = gemm_base(b ? (const void*)(H->ws + W.hsplit) : (const void*)h_final, d, M, c->vocab, d);
-  gl.a_plane = Mmax * d;
-  gl.seg[0] = H->g_lm;
-  gl.seg_rows = c->vocab;
-  gl.block = K;
-  MergeArgs ma{};
-  ma.K = K;
-  ma.out_ids = topk_ids;
-  ma.out_vals = topk_logits;
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  if (H->t_cap > 0) {
-    ev0 = H->t_ev[2 * H->t_next];
-    ev1 = H->t_ev[2 * H->t_next + 1];
-    H->t_next = (H->t_next + 1) % H->t_cap;
-    if (H->t_count < H->t_cap) H->t_count++;
-    HIP_TRY(hipEventRecord(ev0, st));
-  }
-  if (b) {
-    gl.tk_val = wsp<float>(H, W.tk_val);
-    gl.tk_id = wsp<int>(H, W.tk_id);
-    gl.logits = logits;
-    gl.counter = counters;
-    GemmPlan pl = gemm_plan(b, GEMM_TOPK, M, c->vocab, d);
-    if (H->lm_fp8) {
-      // FP8 lm_head: only the independent-wave kernel (<= 16 rows) takes it (checked up front)
-      gl.seg[0] = H->lm_fp8;
-      gl.ldb = d;                     // bytes per weight row
-      gl.row_scale = H->lm_fp8_scale;
-    }
-    HIP_TRY(gemm_launch(b, pl, GEMM_TOPK, gl, st));
-    if (ev1) HIP_TRY(hipEventRecord(ev1, st));
-    ma.ncand = pl.groups * TOPK;
-    ma.vals = gl.tk_val;
-    ma.ids = gl.tk_id;
-  } else {
-    gl.part = part;
-    GemmPlan pl = gemm_plan(b, GEMM_PARTIAL, M, c->vocab, d);
-    HIP_TRY(gemm_launch(b, pl, GEMM_PARTIAL, gl, st));
-    if (ev1) HIP_TRY(hipEventRecord(ev1, st));
-    ma.ncand = c->vocab;
-    ma.vals = part;
-    ma.ids = nullptr;
-    ma.logits_out = logits;
-  }
-  ma.counters = counters;
-  HIP_TRY(launch_topk_merge(ma, n_seq * (K - 1), st));
-  return DFLASH_OK;
+  return draft_impl(H, reinterpret_cast<char*>(base), wl, (size_t)n_seq * c->block_size, n_seq, seq_ids, anchor_ids,
+                    topk_ids, topk_logits, h_final, logits, (hipStream_t)stream);
 }
 
 dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t* anchor_ids, const int32_t* topk_ids,

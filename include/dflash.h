@@ -203,6 +203,23 @@ DFLASH_API dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const
 DFLASH_API dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seq, const int32_t* seq_ids, const int32_t* anchor_ids,
                                  int32_t* topk_ids, float* topk_logits, float* h_final, float* logits, void* stream);
 
+/* Allocation-free variant of dflash_draft_block, for callers that cannot allocate device memory or
+ * hand out a workspace per call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The same pass, arguments and outputs; every scratch buffer of the pass
+ * (activations, GEMM k-split partials, attention partials, top-16 partial lists, work counters)
+ * lives in the library's own static device array of 32 MiB on the current device instead of the
+ * handle's workspace (the KV cache is still the handle's).  The current device must be the one
+ * the stream, the handle's buffers and the outputs belong to.  The array is shared by every call
+ * on that GPU and keeps the last call's contents (the pass itself zeroes what must start at zero),
+ * so calls that overlap in time on one GPU -- several streams, several handles, several threads --
+ * race on it: the caller must serialise them.  n_seq is limited by the array's size, not by the
+ * handle's max_batch: dflash_workspace_bytes(cfg, 1, n_seq, 1) must not exceed 32 MiB (4 sequences
+ * at block 16 and hidden 2048, 8 at block 8); a larger call returns DFLASH_E_SHAPE before anything
+ * is enqueued.  No call allocates or frees device memory. */
+DFLASH_API dflash_status dflash_draft_block_static(dflash_handle* h, int32_t n_seq, const int32_t* seq_ids,
+                                                   const int32_t* anchor_ids, int32_t* topk_ids, float* topk_logits,
+                                                   float* h_final, float* logits, void* stream);
+
 /* (3) Path selection over the candidate lattice ("Architecture", section "Problem 1 --
  * Independent picks are incoherent"): S_t(a, b) = U_t(b) + sum_j A[a,j] * H_t[j] * B[b,j] with
  * U_t the drafter logit, H_t = sigmoid(W_H h_final[t]); slot 1's predecessor is the anchor.
