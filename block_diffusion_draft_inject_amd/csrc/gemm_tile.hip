@@ -45,17 +45,16 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 }
 
 // one LDS-DMA load: 64 lanes x 16 bytes from base + voff[lane] to LDS [lds, lds + 1024).
-// The LDS destination goes through M0, which each asm statement sets itself right before its
-// load.  The compiler warns that it cannot preserve a reserved register named as clobbered; on
-// gfx950 it keeps nothing in M0 across these kernels (ordinary LDS instructions do not use it,
-// and nothing else here issues LDS-DMA, GWS or message instructions), so nothing live is lost.
+// The LDS destination goes through M0, passed as an input operand bound to M0 ("{m0}"): the
+// compiler loads it there itself and knows the statement reads it.  It does not look inside the
+// statement for the wait state an LDS-DMA load needs after an M0 write, so the statement starts
+// with one (s_nop 0).
 __device__ __forceinline__ void dma16(unsigned lds, unsigned voff, const void* base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
-               : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
 // the same from a per-lane 64-bit address
 __device__ __forceinline__ void dma16v(unsigned lds, const void* addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(addr) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "{m0}"(lds) : "memory");
 }
 
 // wait until at most N of this wave's loads are outstanding and its LDS reads are done, then
