@@ -400,7 +400,11 @@ __device__ __forceinline__ void stream_mma(const StreamBuf<SLC, NF>& x, const u3
       }
 }
 
-template <int SLC, int MODE, bool LOOP, bool FP8 = false>
+// Fragments of a workgroup: x, x + G, x + 2G, ... (G = gridDim.x).  NB = 1: one fragment.
+// RING = false: exactly NB fragments per workgroup (G divides the fragment count), all NB loaded
+// at once and then multiplied and reduced in order.  RING = true: NB buffers in rotation, the
+// loads of the next NB - 1 fragments in flight while one is multiplied and reduced.
+template <int SLC, int MODE, int NB, bool RING, bool FP8 = false>
 __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
   constexpr int NF = 1;
   static_assert(!(FP8 && MODE == GEMM_TOPK), "the FP8 lm_head is the wave kernel");
@@ -481,37 +485,57 @@ __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
     if constexpr (FP8) stream_mma8(x, ah, al, acc);
     else stream_mma(x, ah, al, acc);
   };
-  if (!LOOP) {
+  const int G = gridDim.x;
+  if constexpr (NB == 1) {
     // one fragment for this workgroup
     Buf x;
     load(x, f);
     mma(x);
     finish(acc, 0, f);
+  } else if constexpr (!RING) {
+    // all NB fragments requested at once (the whole share of the weight stream in flight), then
+    // multiplied and reduced in the order they were requested; the in-order wait counts let each
+    // one start as soon as its own loads are in
+    Buf b[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      load(b[i], min(f + i * G, nfrag - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      mma(b[i]);
+      finish(acc, i & 1, f + i * G);
+    }
   } else {
-    // ping-pong: the next fragment's loads are issued before this one's MFMAs (the scheduling
-    // barrier keeps the compiler from sinking them towards their use); loads past the last
-    // fragment are clamped to it and never used
-    const int G = gridDim.x;
-    Buf x, y;
+    // ring: the load cursor runs NB - 1 fragments ahead of the compute cursor (the scheduling
+    // barrier keeps the compiler from sinking loads towards their use).  The fragment count is
+    // padded to whole rounds; a padded round loads the last fragment again (cache hits) and
+    // computes nothing (the test is uniform over the workgroup)
+    const int nf = (nfrag - 1 - (int)blockIdx.x) / G + 1;
+    const int T = (nf + NB - 1) / NB * NB;
+    Buf b[NB];
+    int lf = f;
+#pragma unroll
+    for (int i = 0; i + 1 < NB; ++i) {
+      load(b[i], min(lf, nfrag - 1));
+      lf += G;
+      __builtin_amdgcn_sched_barrier(0);
+    }
     int buf = 0;
-    load(x, f);
-    while (true) {
-      const int fy = f + G;
-      load(y, min(fy, nfrag - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      mma(x);
-      finish(acc, buf, f);
-      if (fy >= nfrag) break;
-      f = fy;
-      buf ^= 1;
-      const int fx = f + G;
-      load(x, min(fx, nfrag - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      mma(y);
-      finish(acc, buf, f);
-      if (fx >= nfrag) break;
-      f = fx;
-      buf ^= 1;
+    for (int t = 0; t < T; t += NB) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        load(b[(i + NB - 1) % NB], min(lf, nfrag - 1));
+        lf += G;
+        __builtin_amdgcn_sched_barrier(0);
+        if (f < nfrag) {
+          mma(b[i]);
+          finish(acc, buf, f);
+          buf ^= 1;
+        }
+        f += G;
+      }
     }
   }
   if (MODE != GEMM_TOPK || !epi) return;
@@ -911,6 +935,24 @@ size_t gemm_part_floats(const GemmPlan& pl, int mode, int M, int N) {
   return (size_t)pl.splits * M * N;
 }
 
+// streaming kernel with nb fragments per workgroup requested at once (nb = 0: a ring of the most
+// buffers the slice's registers allow: 3 of 4 chunks, 4 of 1 or 2; nb = -2: a ring of 2)
+template <int SLC, int MODE, bool F8>
+static void launch_stream(const GemmPlan& pl, int nb, const GemmParams& p, hipStream_t st) {
+  constexpr int NBR = SLC == 4 ? 3 : 4;
+  const dim3 sb(SW * 64);
+  if (nb == 1) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 1, false, F8>), pl.grid, sb, 0, st, p);
+  else if (nb == 2) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 2, false, F8>), pl.grid, sb, 0, st, p);
+  else if (nb == 3) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 3, false, F8>), pl.grid, sb, 0, st, p);
+  else if (nb == -2) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 2, true, F8>), pl.grid, sb, 0, st, p);
+  else if constexpr (NBR >= 4) {
+    if (nb == 4) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 4, false, F8>), pl.grid, sb, 0, st, p);
+    else hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, NBR, true, F8>), pl.grid, sb, 0, st, p);
+  } else {
+    hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, NBR, true, F8>), pl.grid, sb, 0, st, p);
+  }
+}
+
 hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hipStream_t st) {
   p.splits = pl.splits;
   p.groups = pl.groups;
@@ -932,31 +974,32 @@ hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hi
   }
   if (pl.kind == 3) {
     if ((p.seg_rows % 16 && p.seg_rows < p.N) || p.half % 8) return hipErrorInvalidValue;
-    const dim3 sb(SW * 64);
     const int ncols = (mode == GEMM_SWIGLU) ? p.half : p.N;
     const int nfrag = (mode == GEMM_SWIGLU) ? (ncols + 7) / 8 : (ncols + 15) / 16;
-    const bool loop = (int)pl.grid.x < nfrag;
+    // fragments per workgroup: all at once when every workgroup has the same few, else a ring;
+    // 4 chunks per wave leave registers for a ring of 3 (or, when 3 would pad the rounds and 2
+    // does not, of 2: fc at K = 25600 has 8 fragments per workgroup, 27.7 us with 3, 25 with 2)
+    const int G = (int)pl.grid.x, nf = (nfrag + G - 1) / G;
+    const int nbmax = pl.slc == 4 ? 3 : 4;
+    int nb = nf == 1 ? 1 : (nfrag % G == 0 && nf <= nbmax ? nf : 0);   // 0: ring of nbmax
+    if (nb == 0 && pl.slc == 4 && nfrag % G == 0 && nf % 3 && nf % 2 == 0) nb = -2;   // ring of 2
     if (p.row_scale && (mode == GEMM_TOPK || p.seg_rows < (mode == GEMM_SWIGLU ? 2 * p.half : p.N)))
       return hipErrorInvalidValue;   // FP8 weights: PARTIAL / SWIGLU over one weight segment
-#define DFL_STREAM_MODE(SLC, MODE, F8)                                                                \
-  if (loop) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, true, F8>), pl.grid, sb, 0, st, p);     \
-  else hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, false, F8>), pl.grid, sb, 0, st, p);
 #define DFL_STREAM(SLC)                                                                               \
   if (pl.slc == SLC) {                                                                                \
-    if (mode == GEMM_TOPK) { DFL_STREAM_MODE(SLC, GEMM_TOPK, false) }                                 \
+    if (mode == GEMM_TOPK) launch_stream<SLC, GEMM_TOPK, false>(pl, nb, p, st);                       \
     else if (mode == GEMM_SWIGLU) {                                                                   \
-      if (p.row_scale) { DFL_STREAM_MODE(SLC, GEMM_SWIGLU, true) }                                    \
-      else { DFL_STREAM_MODE(SLC, GEMM_SWIGLU, false) }                                               \
+      if (p.row_scale) launch_stream<SLC, GEMM_SWIGLU, true>(pl, nb, p, st);                          \
+      else launch_stream<SLC, GEMM_SWIGLU, false>(pl, nb, p, st);                                     \
     } else {                                                                                          \
-      if (p.row_scale) { DFL_STREAM_MODE(SLC, GEMM_PARTIAL, true) }                                   \
-      else { DFL_STREAM_MODE(SLC, GEMM_PARTIAL, false) }                                              \
+      if (p.row_scale) launch_stream<SLC, GEMM_PARTIAL, true>(pl, nb, p, st);                         \
+      else launch_stream<SLC, GEMM_PARTIAL, false>(pl, nb, p, st);                                    \
     }                                                                                                 \
   }
     DFL_STREAM(1)
     DFL_STREAM(2)
     DFL_STREAM(4)
 #undef DFL_STREAM
-#undef DFL_STREAM_MODE
     return hipGetLastError();
   }
   if (pl.kind == 0) {
