@@ -113,6 +113,119 @@ class Cycle:
                                 self.anchor, stream=stream)
 
 
+class BatchCycle:
+    """One batch of sequences (ids first .. first + n - 1) on a drafter handle: its own anchors,
+    committed counts and outputs, and the per-step call sequence of the cycle (as Cycle.step)."""
+
+    def __init__(self, cfg, d, first, n, torch, g):
+        from block_diffusion_draft_inject_amd import binding as Bd
+        self.cfg, self.d, self.n, self.Bd = cfg, d, n, Bd
+        K = cfg.block_size
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        self.seq_ids = torch.arange(first, first + n, dtype=torch.int32, device="cuda")
+        self.pool = torch.randn((n, K, cfg.concat_width), generator=g, device="cuda").to(dt)
+        self.anchor = torch.randint(0, cfg.vocab - 1, (n,), generator=g, device="cuda", dtype=torch.int32)
+        self.tau = torch.zeros(n, dtype=torch.int32, device="cuda")
+        self.out = d.outputs(n, logits=False)
+        self.path = torch.empty((n, K - 1), dtype=torch.int32, device="cuda")
+        self.score = torch.empty(n, dtype=torch.float32, device="cuda")
+        self.margin = torch.empty(n, dtype=torch.float32, device="cuda")
+        self.target = torch.empty((n, K), dtype=torch.int32, device="cuda")
+        self.nacc = torch.empty(n, dtype=torch.int32, device="cuda")
+        self.committed = torch.empty((n, K), dtype=torch.int32, device="cuda")
+        self.counter = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+    def step(self, stream):
+        cfg, d, Bd, K = self.cfg, self.d, self.Bd, self.cfg.block_size
+        d.dflash_inject_kv(self.seq_ids, self.tau, K, self.pool, start_pos=None, stream=stream)
+        o = self.out
+        d.dflash_draft_block(self.seq_ids, self.anchor, o["topk_ids"], o["topk_logits"], o["h_final"], None,
+                             stream=stream)
+        d.dflash_select_path(self.anchor, o["topk_ids"], o["topk_logits"], o["h_final"], Bd.SELECT_VITERBI,
+                             self.path, self.score, self.margin, stream=stream)
+        Bd.dflash_synth_target_argmax(self.n, K, cfg.vocab, self.path, 0.7, 12345, self.counter, self.target,
+                                      stream=stream)
+        Bd.dflash_verify_greedy(self.n, K, self.path, self.target, self.nacc, self.tau, self.committed,
+                                self.anchor, stream=stream)
+
+
+def run_pipeline(torch, wname="b32_k8_conv", reps=10, graph_steps=10):
+    """Two-batch pipeline: the sequences of a batched workload split into two halves, each half's
+    cycle (inject its committed tokens -> draft -> select -> stand-in target -> verify, tau kept on
+    the device) on its own handle (shared weights and KV cache) and its own stream, so that one
+    half's injection runs beside the other half's draft and selection.  Times, per step of all
+    sequences, HIP graphs of `graph_steps` steps: the whole batch on one handle and stream; the two
+    halves one after the other on one stream; the two halves on two streams (fork/join)."""
+    from block_diffusion_draft_inject_amd import synth
+    from block_diffusion_draft_inject_amd import binding as Bd
+    cfg = synth.WORKLOADS[wname]
+    n, h = cfg.batch, cfg.batch // 2
+    w = device_weights(cfg, 0, torch)
+    d_all = Bd.Drafter(cfg, w, max_seqs=n, max_batch=n, max_inject_rows=1024)
+    d_lo = Bd.Drafter(cfg, w, max_seqs=n, max_batch=h, max_inject_rows=1024, kv_from=d_all)
+    d_hi = Bd.Drafter(cfg, w, max_seqs=n, max_batch=n - h, max_inject_rows=1024, kv_from=d_all)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    L = synth.context_lengths(cfg)
+    first = [max(0, int(l) - cfg.window) for l in L]
+    nrow = [int(l) - f for l, f in zip(L, first)]
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    pre = torch.randn((n, max(nrow), cfg.concat_width), generator=g, device="cuda").to(dt)
+    ids = torch.arange(n, dtype=torch.int32, device="cuda")
+    d_all.dflash_reset_seqs(ids)
+    d_all.dflash_inject_kv(ids, torch.tensor(nrow, dtype=torch.int32, device="cuda"), max(nrow), pre,
+                           start_pos=torch.tensor(first, dtype=torch.int32, device="cuda"))
+    whole = BatchCycle(cfg, d_all, 0, n, torch, g)
+    lo = BatchCycle(cfg, d_lo, 0, h, torch, g)
+    hi = BatchCycle(cfg, d_hi, h, n - h, torch, g)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        for _ in range(2):
+            whole.step(s1.cuda_stream)
+            lo.step(s1.cuda_stream)
+            hi.step(s1.cuda_stream)
+    torch.cuda.synchronize()
+    G = graph_steps
+
+    def capture(kind):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s1):
+            a = torch.cuda.current_stream()
+            if kind == "two_streams":
+                fork = torch.cuda.Event()
+                fork.record(a)
+                s2.wait_event(fork)
+            for _ in range(G):
+                if kind == "one_batch":
+                    whole.step(a.cuda_stream)
+                else:
+                    lo.step(a.cuda_stream)
+                    hi.step(s2.cuda_stream if kind == "two_streams" else a.cuda_stream)
+            if kind == "two_streams":
+                join = torch.cuda.Event()
+                join.record(s2)
+                a.wait_event(join)
+        return graph
+
+    res = {}
+    for kind in ("one_batch", "halves_one_stream", "two_streams"):
+        graph = capture(kind)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        res[kind] = (time.perf_counter() - t0) * 1e3 / (reps * G)
+        del graph
+    if d_all.dflash_get_device_error():
+        raise RuntimeError("device error word set in the pipeline leg")
+    for d in (d_hi, d_lo, d_all):
+        d.close()
+    return res
+
+
 def run_overlap(torch, reps=10, graph_steps=10):
     """Mixed prefill + decode on two streams: the b1_k16 decode cycle of one sequence on one
     stream while a second handle, sharing the KV cache (its own workspace), injects the
@@ -518,6 +631,7 @@ def main():
     ap.add_argument("--no-c4", action="store_true", help="skip b32_k16_incremental")
     ap.add_argument("--no-c5", action="store_true", help="skip b64_k16_long")
     ap.add_argument("--no-pc", action="store_true", help="skip the per-channel conv leg")
+    ap.add_argument("--no-pipeline", action="store_true", help="skip the two-batch two-stream pipeline leg")
     ap.add_argument("--no-overlap", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-lm_head variant of the headline workload")
     ap.add_argument("--no-b1", action="store_true", help="skip the headline workload (profiling runs)")
@@ -659,6 +773,19 @@ def main():
             "decode_ms": round(ov["decode"], 4), "prefill_ms": round(ov["prefill"], 4),
             "sequential_ms": round(ov["sequential"], 4), "overlapped_ms": round(ov["overlapped"], 4),
             "saved_frac": round(1 - ov["overlapped"] / ov["sequential"], 4)}
+    if not args.no_pipeline:
+        torch.cuda.empty_cache()
+        pp = run_pipeline(torch)
+        _release(torch)
+        out["pipeline"] = {
+            "workload": "b32_k8_conv split into two halves of 16 sequences, each half's whole cycle on its own "
+                        "handle and stream (shared weights and KV cache, tau on the device): one half's injection "
+                        "beside the other half's draft and selection",
+            "one_batch_ms": round(pp["one_batch"], 4), "halves_one_stream_ms": round(pp["halves_one_stream"], 4),
+            "two_streams_ms": round(pp["two_streams"], 4),
+            "two_streams_blocks_per_s": round(32 / (pp["two_streams"] * 1e-3), 1),
+            "saved_frac_vs_halves": round(1 - pp["two_streams"] / pp["halves_one_stream"], 4),
+            "saved_frac_vs_one_batch": round(1 - pp["two_streams"] / pp["one_batch"], 4)}
     print(json.dumps(out), flush=True)
     _release(torch)
 

@@ -525,3 +525,87 @@ def test_per_channel_conv(H, dtype):
     seq_ids = list(range(12))
     spans = [(0, int(L)) for L in rng.integers(1, 120, size=12)]
     _full_check(H, case, seq_ids, spans, rng.integers(0, cfg.vocab - 1, size=12).tolist(), mode_names=("viterbi",))
+
+
+def test_two_batch_pipeline_two_streams(H):
+    """The two-batch pipeline: four sequences split into two halves, each half's whole cycle
+    (inject its committed tokens -> draft -> select -> stand-in target -> verify, tau and the next
+    anchor kept on the device) on its own handle (shared weights and KV cache) and stream, for two
+    cycles.  Every output and the KV region equal those of the same calls on one stream, and both
+    cycles' drafts of all four sequences match the oracle (fed the tau and anchors the GPU chose)."""
+    import torch
+    cfg = MID
+    K = cfg.block_size
+    case = H.Case(cfg, max_seqs=4, max_batch=4, max_inject_rows=64)
+    halves = [(B.Drafter(cfg, case.dev_w, max_seqs=4, max_batch=2, max_inject_rows=64, kv_from=case.d), [0, 1]),
+              (B.Drafter(cfg, case.dev_w, max_seqs=4, max_batch=2, max_inject_rows=64, kv_from=case.d), [2, 3])]
+    case.reset([0, 1, 2, 3])
+    case.inject([0, 1, 2, 3], [np.arange(0, 30 + 7 * i) for i in range(4)])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    pool = torch.randn((4, K, cfg.concat_width), generator=g, device="cuda").to(torch.bfloat16)
+    pools = [pool[:2].contiguous(), pool[2:].contiguous()]
+    anchors0 = [[17, 4000], [123, 8000]]
+    torch.cuda.synchronize()
+    snapshot = case.d.kv.clone()
+
+    def run(two_streams):
+        case.d.kv.copy_(snapshot)
+        st = [torch.cuda.Stream(), None]
+        st[1] = torch.cuda.Stream() if two_streams else st[0]
+        state = []
+        for hidx, (d, ids) in enumerate(halves):
+            t = lambda x, dt=torch.int32: torch.tensor(x, dtype=dt, device="cuda")
+            state.append(dict(ids=t(ids), anchor=t(anchors0[hidx]), tau=t([0, 0]), out=None,
+                              path=torch.empty((2, K - 1), dtype=torch.int32, device="cuda"),
+                              score=torch.empty(2, device="cuda"), margin=torch.empty(2, device="cuda"),
+                              target=torch.empty((2, K), dtype=torch.int32, device="cuda"),
+                              nacc=t([0, 0]), com=torch.empty((2, K), dtype=torch.int32, device="cuda"),
+                              ctr=torch.zeros(1, dtype=torch.int64, device="cuda")))
+        records = []
+        torch.cuda.synchronize()
+        for step in range(2):
+            rec = []
+            for hidx, (d, ids) in enumerate(halves):
+                s, x = st[hidx].cuda_stream, state[hidx]
+                x["out"] = d.outputs(2, logits=True)
+                anchor_in = x["anchor"].clone()
+                d.dflash_inject_kv(x["ids"], x["tau"], K, pools[hidx], start_pos=None, stream=s)
+                o = x["out"]
+                d.dflash_draft_block(x["ids"], anchor_in, o["topk_ids"], o["topk_logits"], o["h_final"], o["logits"],
+                                     stream=s)
+                d.dflash_select_path(anchor_in, o["topk_ids"], o["topk_logits"], o["h_final"], B.SELECT_VITERBI,
+                                     x["path"], x["score"], x["margin"], stream=s)
+                B.dflash_synth_target_argmax(2, K, cfg.vocab, x["path"], 0.7, 99 + hidx, x["ctr"], x["target"],
+                                             stream=s)
+                B.dflash_verify_greedy(2, K, x["path"], x["target"], x["nacc"], x["tau"], x["com"], x["anchor"],
+                                       stream=s)
+                rec.append((anchor_in, x))
+            torch.cuda.synchronize()
+            records.append([dict(anchor=a.cpu().numpy(), tau=x["tau"].cpu().numpy(), path=x["path"].cpu().numpy(),
+                                 **{k: v.cpu().numpy() for k, v in x["out"].items()}) for a, x in rec])
+        return records, case.d.kv.clone()
+
+    seq_rec, seq_kv = run(False)
+    par_rec, par_kv = run(True)
+    assert torch.equal(seq_kv, par_kv)
+    for a, b in zip(seq_rec, par_rec):
+        for ha, hb in zip(a, b):
+            for k in ha:
+                assert np.array_equal(ha[k], hb[k]), k
+    # the oracle, teacher-forced with the GPU's tau and anchors
+    pool64 = pool.float().cpu().numpy().astype(np.float64)
+    for step, rec in enumerate(par_rec):
+        if step == 1:
+            for hidx, (_, ids) in enumerate(halves):
+                tau0 = par_rec[0][hidx]["tau"]
+                for i, sid in enumerate(ids):
+                    L0 = case.caches[sid].length
+                    O.inject(cfg, case.W64, case.caches[sid], np.arange(L0, L0 + int(tau0[i])),
+                             pool64[sid, : int(tau0[i])], H.oracle_mode(cfg))
+        for hidx, (_, ids) in enumerate(halves):
+            r = rec[hidx]
+            err, _ = H.check_draft(case, ids, r["anchor"].tolist(), r)
+            assert err <= H.LOGIT_TOL["bf16"]
+            H.log(f"[pipeline] step {step} half {hidx}: max |logit err| {err:.2e}, tau {r['tau'].tolist()}")
+    assert case.d.dflash_get_device_error() == 0
