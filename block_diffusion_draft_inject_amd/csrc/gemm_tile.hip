@@ -14,6 +14,8 @@
 // it the stage read one step earlier is free and is refilled.  The LDS-DMA loads are issued
 // from inline assembly (the compiler does not know they write LDS; the explicit waits above
 // replace its own), so the k-loop contains no other global memory access.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace dfl {
@@ -39,6 +41,9 @@ struct TileCfg {
   static constexpr int BMc = BM, BNc = BN, Sc = S, WGNc = WGN;
   static_assert(BA % NW == 0 && BB % NW == 0, "blocks per operand must split evenly over the waves");
 };
+
+__device__ __forceinline__ int ctz_(unsigned x) { return __builtin_ctz(x); }
+__device__ __forceinline__ int ctz_(unsigned long long x) { return __builtin_ctzll(x); }
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
@@ -259,6 +264,7 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
   constexpr int BM = T::BMc, BN = T::BNc;
   constexpr int TPR = T::NT / BM;                 // threads per row
   constexpr int CPT = 64 / TPR;                   // columns per thread in a 64-column pass
+  using MaskT = typename std::conditional<(CPT > 32), unsigned long long, unsigned>::type;   // one bit per column
   static_assert(T::NT % BM == 0 && CPT % 4 == 0, "row split");
   static_assert(T::LDS >= BM * 68 * 4, "epilogue buffer must fit in the stages");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS];
@@ -323,24 +329,24 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
         // a wave runs as many pushes as its busiest lane needs (not one per column that any
         // lane needs)
         const int cg = n0 + q * 64 + cb;         // global column of the thread's first value
-        unsigned mask = 0;
+        MaskT mask = 0;
 #pragma unroll
         for (int c4 = 0; c4 < CPT / 4; ++c4) {
           const f32x4 v = *reinterpret_cast<const f32x4*>(&ep[lrow][cb + c4 * 4]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int col = cg + c4 * 4 + e;
-            mask |= (unsigned)(col < cend && v[e] > tv) << (c4 * 4 + e);
+            mask |= (MaskT)(col < cend && v[e] > tv) << (c4 * 4 + e);
           }
         }
         // the next marked value is read from LDS before the current one is inserted, so the
         // read's latency overlaps the insertion (b32 lm_head 269 -> 267 us)
         if (mask) {
-          int c = __builtin_ctz(mask);
+          int c = ctz_(mask);
           mask &= mask - 1;
           float val = ep[lrow][cb + c];
           while (true) {
-            const int cn = mask ? __builtin_ctz(mask) : c;
+            const int cn = mask ? ctz_(mask) : c;
             const float vn = ep[lrow][cb + cn];
             top.push_asc(val, cg + c);   // a thread's columns ascend
             if (!mask) break;
