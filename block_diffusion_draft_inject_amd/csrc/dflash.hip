@@ -49,7 +49,7 @@ size_t esize(const dflash_config* c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
 // Workspace regions (byte offsets), a pure function of (config, max_batch, max_inject_rows).
 struct WsLayout {
   size_t h0, h1, act_y, act_o, act_s, qb, hsplit, kb, vb, act_a, act_z, ctx, part, o_part, m_part, l_part, tk_val, tk_id;
-  size_t ubar, cbuf, meta_seq, meta_pos, row_off, row_start, row_skip, total, counters;
+  size_t ubar, cbuf, meta_seq, meta_pos, row_off, row_start, row_skip, total, counters, sel_part, sel_cnt;
   size_t bytes;
   size_t part_floats;
   int chunks_max;
@@ -89,6 +89,7 @@ struct Handle {
   // timing
   int t_cap, t_next, t_count;
   std::vector<hipEvent_t> t_ev;
+  bool sel_cnt_clear = false;   // the selector's arrival counters have been zeroed on the device
 };
 
 bool bf(const dflash_config* c) { return c->dtype == DFLASH_BF16; }
@@ -205,6 +206,9 @@ WsLayout ws_layout(const dflash_config* c, int max_batch, int max_inject_rows, i
   L.row_skip = take((size_t)max_seqs * 4);
   L.total = take(4);
   L.counters = take(NCOUNTERS * 4);
+  // selector: partial pair scores per (sequence, slot, chunk of 32 ranks) and arrival counters
+  L.sel_part = take((size_t)max_batch * (K - 1) * ((c->sel_rank + 31) / 32) * TOPK * TOPK * 4);
+  L.sel_cnt = take((size_t)max_batch * 4);
   L.bytes = off;
   return L;
 }
@@ -879,6 +883,19 @@ dflash_status dflash_draft_block_static(dflash_handle* h, int32_t n_seq, const i
                     topk_ids, topk_logits, h_final, logits, (hipStream_t)stream);
 }
 
+// The selector's workspace; the first selector call of a handle zeroes its arrival counters
+// (a fill kernel on the call's stream; afterwards every launch leaves them at zero).
+static hipError_t select_prepare(Handle* H, SelectArgs& sa, hipStream_t st) {
+  sa.spart = wsp<float>(H->ws, H->wl.sel_part);
+  sa.sel_cnt = wsp<unsigned>(H->ws, H->wl.sel_cnt);
+  if (!H->sel_cnt_clear) {
+    const hipError_t e = launch_fill_u32(sa.sel_cnt, H->max_batch, 0u, st);
+    if (e != hipSuccess) return e;
+    H->sel_cnt_clear = true;
+  }
+  return hipSuccess;
+}
+
 dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t* anchor_ids, const int32_t* topk_ids,
                                  const float* topk_logits, const float* h_final, dflash_select_mode mode,
                                  int32_t* path_ids, float* path_score, float* margin, void* stream) {
@@ -892,6 +909,7 @@ dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t*
   SelectArgs sa{c->block_size, c->hidden, c->sel_rank, (int)mode, c->vocab, dev_err(H), anchor_ids, topk_ids,
                 topk_logits, h_final, H->g_A, H->g_B, H->g_WH, path_ids, path_score, margin,
                 1.0f, 1.0f, nullptr, nullptr, nullptr};
+  HIP_TRY(select_prepare(H, sa, (hipStream_t)stream));
   HIP_TRY(launch_select(bf(c), sa, n_seq, (hipStream_t)stream));
   return DFLASH_OK;
 }
@@ -911,6 +929,7 @@ dflash_status dflash_select_sample(dflash_handle* h, int32_t n_seq, const int32_
   SelectArgs sa{c->block_size, c->hidden, c->sel_rank, 2, c->vocab, dev_err(H), anchor_ids, topk_ids,
                 topk_logits, h_final, H->g_A, H->g_B, H->g_WH, path_ids, nullptr, nullptr,
                 1.0f / temperature, top_p, uniforms, q_path, q_cand};
+  HIP_TRY(select_prepare(H, sa, (hipStream_t)stream));
   HIP_TRY(launch_select(bf(c), sa, n_seq, (hipStream_t)stream));
   return DFLASH_OK;
 }

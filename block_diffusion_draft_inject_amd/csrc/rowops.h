@@ -161,6 +161,10 @@ struct SelectArgs {
   const float* uniforms;  // [n_seq][K-1]
   float* q_path;          // [n_seq][K-1]
   float* q_cand;          // [n_seq][K-1][16] or null
+  // workspace
+  float* spart;           // [n_seq][K-1][rank chunks of 32][16][16] partial pair scores
+  unsigned* sel_cnt;      // [n_seq] arrival counters: zero between launches (the last arrival resets)
+  int spw;                // slots per workgroup (set by the launcher)
 };
 
 struct RejectArgs {
@@ -227,6 +231,7 @@ hipError_t launch_reset(const ResetArgs& a, hipStream_t st);
 hipError_t launch_topk_merge(const MergeArgs& a, int out_rows, hipStream_t st);
 hipError_t launch_attention(bool bf, const AttnArgs& a, int n_seq, hipStream_t st);
 hipError_t launch_select(bool bf, const SelectArgs& a, int n_seq, hipStream_t st);
+hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t st);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
 hipError_t launch_verify_rejection(const RejectArgs& a, hipStream_t st);
 hipError_t launch_synth(const SynthArgs& a, hipStream_t st);

@@ -3,31 +3,19 @@
 // Selector ("Architecture", kb.ekarisky.com, section "Problem 1 -- Independent picks are
 // incoherent"): keep the top-16 candidates of every draft slot and score adjacent pairs,
 //   S_t(a, b) = U_t(b) + < A(a) * H(h_t), B(b) >,   H(h_t) = sigmoid(W_H h_t),
-// all pairs at once; only the walk over the precomputed scores is sequential.  One workgroup
-// per sequence.  VITERBI keeps the two best partial paths per state (so the margin to the
-// second-best complete path is exact); GREEDY follows the best successor.
+// all pairs at once; only the walk over the precomputed scores is sequential.  The gates and
+// pair scores are spread over one workgroup per (sequence, slot, chunk of 32 ranks); the last
+// of a sequence's workgroups to finish sums the rank chunks and walks.  VITERBI: a forward and
+// a backward max-plus sweep give the best path and the exact score of the second-best complete
+// path (the margin); GREEDY follows the best successor.
 #include "rowops.h"
 
 namespace dfl {
 
 constexpr int SEL_KMAX = 32;    // block size
-constexpr int SEL_RMAX = 256;   // selector rank
-constexpr int SEL_RC = 16;      // rank chunk of the predecessor rows staged in LDS
-constexpr int SEL_NP = (SEL_KMAX - 2) * TOPK + 1;   // predecessor rows: anchor + candidates of slots 1..K-2
-
-// order of Viterbi candidates: higher score, then smaller code (2 * predecessor + rank)
-__device__ __forceinline__ bool vit_better(float s1, int c1, float s2, int c2) {
-  return (s1 > s2) | ((s1 == s2) & (c1 < c2));
-}
-
-// (s1,c1) >= (s2,c2) are a sorted best-two list; insert candidate (s,c)
-__device__ __forceinline__ void top2_push(float& s1, int& c1, float& s2, int& c2, float s, int c) {
-  const bool b1 = vit_better(s, c, s1, c1), b2 = vit_better(s, c, s2, c2);
-  s2 = b1 ? s1 : (b2 ? s : s2);
-  c2 = b1 ? c1 : (b2 ? c : c2);
-  s1 = b1 ? s : s1;
-  c1 = b1 ? c : c1;
-}
+constexpr int SEL_SR = 32;      // ranks per workgroup
+constexpr int SEL_T = 512;      // threads per workgroup
+constexpr int SEL_DMAX = 4096;  // hidden size (config bound)
 
 // DPP quad permutation (lanes l ^ 1 for 0xB1, l ^ 2 for 0x4E inside each group of four)
 template <int CTRL>
@@ -37,310 +25,105 @@ __device__ __forceinline__ float quad_perm_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// merge the best-two lists of the lanes of a quad (DPP, no LDS round trip)
-template <int CTRL>
-__device__ __forceinline__ void top2_quad(float& s1, int& c1, float& s2, int& c2) {
-  const float o1 = quad_perm_f<CTRL>(s1), o2 = quad_perm_f<CTRL>(s2);
-  const int p1 = quad_perm_i<CTRL>(c1), p2 = quad_perm_i<CTRL>(c2);
-  top2_push(s1, c1, s2, c2, o1, p1);
-  top2_push(s1, c1, s2, c2, o2, p2);
-}
+// Walk state of one sequence, in LDS (the sequence's last workgroup only).
+struct SelWalk {
+  int cid[SEL_KMAX][TOPK];                    // candidate ids of slots 1..K-1
+  float S[SEL_KMAX][TOPK][TOPK];              // S[t-1][b][a]: pair scores with the logit term
+  float alpha[SEL_KMAX][TOPK];                // forward sweep, slot t at row t-1
+  float beta[SEL_KMAX][TOPK];                 // backward sweep
+  unsigned char bp1[SEL_KMAX][TOPK];          // best predecessor per (slot, state)
+  int best[SEL_KMAX];                         // the best path's state per slot
+};
 
-// merge the best-two lists of this lane and lane ^ m
-__device__ __forceinline__ void top2_xor(float& s1, int& c1, float& s2, int& c2, int m) {
-  const float o1 = __shfl_xor(s1, m, WAVE), o2 = __shfl_xor(s2, m, WAVE);
-  const int p1 = __shfl_xor(c1, m, WAVE), p2 = __shfl_xor(c2, m, WAVE);
-  top2_push(s1, c1, s2, c2, o1, p1);
-  top2_push(s1, c1, s2, c2, o2, p2);
-}
-
-// gate[t-1][j] = sigmoid(W_H[j] . h_final[b][t]) for slots t = 1..K-1, into LDS.
-// bf16 tables: one 16x16 MFMA tile per (slot tile, rank tile); the four waves split the hidden
-// dimension, h enters as bf16 hi + lo planes (two MFMAs), partial tiles are summed through LDS.
-template <typename T>
-__device__ __forceinline__ void sel_gates(const SelectArgs& a, int b, float (*gt)[SEL_RMAX], float (*red)[64][4]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = a.K, r = a.r, d = a.d;
-  const float* hb = a.h_final + (size_t)b * K * d;
-  if constexpr (sizeof(T) == 2) {
-    const int li = lane & 15, kg = lane >> 4;
-    const int nch = d / 32;                 // 32-wide k chunks; the waves take every 4th
-    constexpr int BATCH = 8;               // 24 loads of 16 bytes in flight per lane
-    for (int mt = 0; mt < (K + 15) / 16; ++mt)
-      for (int nt = 0; nt < (r + 15) / 16; ++nt) {
-        const float* hr = hb + (size_t)min(mt * 16 + li, K - 1) * d + kg * 8;
-        const bf16* wr = reinterpret_cast<const bf16*>(a.WH) + (size_t)min(nt * 16 + li, r - 1) * d + kg * 8;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int c0 = wave; c0 < nch; c0 += 4 * BATCH) {
-          f32x4 h0[BATCH], h1[BATCH];
-          u32x4 w[BATCH];
-#pragma unroll
-          for (int u = 0; u < BATCH; ++u) {     // all loads of the batch first
-            const int c = min(c0 + 4 * u, nch - 1);
-            h0[u] = *reinterpret_cast<const f32x4*>(hr + c * 32);
-            h1[u] = *reinterpret_cast<const f32x4*>(hr + c * 32 + 4);
-            w[u] = *reinterpret_cast<const u32x4*>(wr + c * 32);
-          }
-#pragma unroll
-          for (int u = 0; u < BATCH; ++u) {
-            // a chunk past the end (its loads were clamped) adds zero: no branch, so that the
-            // compiler keeps the whole batch of loads ahead of the first MFMA
-            if (c0 + 4 * u >= nch) w[u] = u32x4{0u, 0u, 0u, 0u};
-            u32x4 hi, lo;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float x0 = e < 2 ? h0[u][2 * e] : h1[u][2 * e - 4];
-              const float x1 = e < 2 ? h0[u][2 * e + 1] : h1[u][2 * e - 3];
-              const bf16 a0 = f2bf(x0), a1 = f2bf(x1);
-              hi[e] = (unsigned)a0 | ((unsigned)a1 << 16);
-              lo[e] = (unsigned)f2bf(x0 - bf2f(a0)) | ((unsigned)f2bf(x1 - bf2f(a1)) << 16);
-            }
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(hi), as_bf16x8(w[u]), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lo), as_bf16x8(w[u]), acc, 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) red[wave][lane][j] = acc[j];
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float g = red[0][lane][j] + red[1][lane][j] + red[2][lane][j] + red[3][lane][j];
-            const int t = mt * 16 + kg * 4 + j, jj = nt * 16 + li;   // D layout: row 4 kg + j, column li
-            if (t >= 1 && t < K && jj < r) gt[t - 1][jj] = sigmoidf_(g);
-          }
-        }
-        __syncthreads();
-      }
-  } else {
-    // fp32 tables: one wave per dot product
-    const float* wh = reinterpret_cast<const float*>(a.WH);
-    for (int e = wave; e < (K - 1) * r; e += 4) {
-      const int t = e / r + 1, j = e % r;
-      float acc = 0.f;
-      for (int k = lane; k < d; k += 64) acc += hb[(size_t)t * d + k] * wh[(size_t)j * d + k];
-      acc = wave_sum(acc);
-      if (lane == 0) gt[t - 1][j] = sigmoidf_(acc);
-    }
-    __syncthreads();
-  }
-}
-
-// Path selector for one sequence per workgroup.  Phases: candidates -> gates (in-kernel) ->
-// pair scores S_t(a, b) for all slots at once (one thread per (slot, successor), predecessor
-// rows staged in LDS by rank chunks) -> the sequential walk in one wave with shuffles only.
-template <typename T>
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
-  __shared__ int cid[SEL_KMAX][TOPK];
-  __shared__ float cu[SEL_KMAX][TOPK];
-  __shared__ __attribute__((aligned(16))) float gt[SEL_KMAX][SEL_RMAX];
-  __shared__ __attribute__((aligned(16))) float red[4][64][4];
-  __shared__ __attribute__((aligned(16))) float ta[SEL_NP][SEL_RC + 4];
-  __shared__ __attribute__((aligned(16))) float S[SEL_KMAX][TOPK][TOPK];   // S[t-1][b][a]
-  __shared__ unsigned char bp1[SEL_KMAX][TOPK], bp2[SEL_KMAX][TOPK];
-  __shared__ __attribute__((aligned(16))) float dv[2][TOPK];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = a.K, r = a.r;
-  int anchor = a.anchor[b];
-  if (anchor < 0 || anchor >= a.vocab) {   // out-of-range token: record and read row 0
-    if (tid == 0) atomicOr(a.dev_err, 8);
-    anchor = 0;
-  }
-  const int ncand = (K - 1) * TOPK, npred = (K - 2) * TOPK + 1;
-  for (int e = tid; e < ncand; e += 256) {
-    int id = a.topk_ids[(size_t)b * ncand + e];
-    if (id < 0 || id >= a.vocab) {         // out-of-range candidate: record and read row 0
-      atomicOr(a.dev_err, 16);
-      id = 0;
-    }
-    cid[e / TOPK][e % TOPK] = id;
-    cu[e / TOPK][e % TOPK] = a.topk_logits[(size_t)b * ncand + e];
-  }
-  __syncthreads();
-  // pair scores: thread (t, bi) for t = 1..K-1 (two passes cover K up to 32), accumulated over
-  // rank chunks of SEL_RC.  The first chunk's table loads are issued before the gate phase so
-  // that their latency overlaps it.
-  constexpr int VE = 16 / sizeof(T);
-  constexpr int VPR = SEL_RC / VE;                      // 16-byte vectors per row chunk
-  constexpr int XA = (SEL_NP * VPR + 255) / 256;        // predecessor vectors per thread
-  float acc[2][TOPK];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int i = 0; i < TOPK; ++i) acc[q][i] = 0.f;
-  u32x4 xa[XA], xb[2][VPR];
-  auto issue = [&](int r0) {
-    const int nv = min(SEL_RC, r - r0) / VE;           // rank is a multiple of 8
-#pragma unroll
-    for (int u = 0; u < XA; ++u) {
-      const int e = tid + 256 * u, row = e / VPR, v = e % VPR;
-      const bool ok = row < npred && v < nv;
-      const int ci = max(min(row, npred - 1) - 1, 0);  // candidate index of predecessor row >= 1
-      const int tok = row == 0 ? anchor : cid[ci / TOPK][ci % TOPK];
-      xa[u] = ok ? reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.A) + (size_t)tok * r + r0)[v]
-                 : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = min(tid + 256 * q, ncand - 1);
-      const u32x4* brow = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.B) +
-                                                         (size_t)cid[e / TOPK][e % TOPK] * r + r0);
-#pragma unroll
-      for (int v = 0; v < VPR; ++v) xb[q][v] = v < nv ? brow[v] : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto consume = [&](int r0) {
-    const int rc = min(SEL_RC, r - r0);
-#pragma unroll
-    for (int u = 0; u < XA; ++u) {
-      const int e = tid + 256 * u, row = e / VPR, v = e % VPR;
-      if (row < npred) {
-        const T* xe = reinterpret_cast<const T*>(&xa[u]);
-#pragma unroll
-        for (int j = 0; j < VE; ++j) ta[row][v * VE + j] = v * VE < rc ? ldv(xe, j) : 0.f;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = tid + 256 * q;
-      if (e >= ncand) break;
-      const int t = e / TOPK + 1;
-      float gb[SEL_RC];
-#pragma unroll
-      for (int j = 0; j < SEL_RC; ++j)
-        gb[j] = j < rc ? ldv(reinterpret_cast<const T*>(&xb[q][j / VE]), j % VE) * gt[t - 1][r0 + j] : 0.f;
-      const int p0 = t == 1 ? 0 : 1 + (t - 2) * TOPK;
-      const int na = t == 1 ? 1 : TOPK;
-#pragma unroll
-      for (int ai = 0; ai < TOPK; ++ai) {
-        if (ai >= na) break;
-        const f32x4* pa = reinterpret_cast<const f32x4*>(ta[p0 + ai]);
-        float sacc = 0.f;
-#pragma unroll
-        for (int j4 = 0; j4 < SEL_RC / 4; ++j4) {
-          const f32x4 x = pa[j4];
-          sacc += x[0] * gb[4 * j4] + x[1] * gb[4 * j4 + 1] + x[2] * gb[4 * j4 + 2] + x[3] * gb[4 * j4 + 3];
-        }
-        acc[q][ai] += sacc;
-      }
-    }
-    __syncthreads();
-  };
-  issue(0);
-  sel_gates<T>(a, b, gt, red);              // ends with a barrier: gt visible
-  consume(0);
-  for (int r0 = SEL_RC; r0 < r; r0 += SEL_RC) {
-    issue(r0);
-    consume(r0);
-  }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = tid + 256 * q;
-    if (e >= ncand) break;
-    const int t = e / TOPK + 1, bi = e % TOPK;
-#pragma unroll
-    for (int ai = 0; ai < TOPK; ++ai) S[t - 1][bi][ai] = acc[q][ai] + cu[t - 1][bi];
-  }
-  __syncthreads();
-  if (wave != 0) return;
+// The sequential walk over the summed pair scores, in wave 0 of the last workgroup.
+__device__ void sel_walk(const SelectArgs& a, int b, SelWalk& w) {
+  const int K = a.K, lane = threadIdx.x & 63;
   // ---- the walk: one wave; lane = 4 * bi + qa holds predecessors a = 4 qa .. 4 qa + 3 of state bi
   const int bi = lane >> 2, qa = lane & 3;
   if (a.mode == 0) {
-    // partial-path scores of the previous slot live in LDS (dv[0][a] = best, dv[1][a] = second);
-    // each lane reads its four predecessors with two 16-byte reads, the quad merges by DPP
-    if (lane < TOPK) {
-      dv[0][lane] = S[0][lane][0];           // slot 1: the single path anchor -> lane
-      dv[1][lane] = NEG_INF;
-    }
-    float d1 = 0.f, d2 = 0.f;
+    // Viterbi as two max-plus sweeps.  Forward: alpha_t(b) = max_a alpha_{t-1}(a) + S_t(a, b),
+    // alpha_1(b) = S_1(anchor, b), the predecessor kept per state (ties to the smaller a).
+    // Backward: beta_t(a) = max_b S_{t+1}(a, b) + beta_{t+1}(b), beta_{K-1} = 0.  The best path
+    // follows the predecessors back from the best final state (ties to the smaller state), so
+    // it is the best path of the two-best list recursion with the same order.  Every other path
+    // leaves the best one at some slot t in a state b != best_t, and the best path through
+    // (t, b) scores alpha_t(b) + beta_t(b); so the second-best complete path scores the
+    // maximum of that over the states off the best path.  Per step each lane takes four
+    // predecessors (successors) of one state; the quad merges by DPP; sweep values pass
+    // through LDS (one wave: its LDS accesses are ordered).
+    if (lane < TOPK) w.alpha[0][lane] = w.S[0][lane][0];
     for (int t = 2; t < K; ++t) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const f32x4 p1v = *reinterpret_cast<const f32x4*>(&dv[0][4 * qa]);
-      const f32x4 p2v = *reinterpret_cast<const f32x4*>(&dv[1][4 * qa]);
-      const f32x4 sv = *reinterpret_cast<const f32x4*>(&S[t - 1][bi][4 * qa]);
-      // A predecessor's rank-1 extension always beats its rank-2 one (same pair term, better
-      // or equal partial score, smaller code), so the best two of the 32 candidates are: the
-      // best rank-1 extension b, and the better of the second-best rank-1 extension s and the
-      // rank-2 extension w of b's predecessor.  Each lane summarises its four predecessors as
-      // (b, s, w); the quad merges summaries.  An absent path enters as (-inf, 255).
-      float bs = NEG_INF, ss = NEG_INF, ws = NEG_INF;
-      int bc = 255, sc = 255, wc = 255;
+      const f32x4 av = *reinterpret_cast<const f32x4*>(&w.alpha[t - 2][4 * qa]);
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(&w.S[t - 1][bi][4 * qa]);
+      float bv = av[0] + sv[0];
+      int ba = 4 * qa;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ai = 4 * qa + i;
-        const float v1 = p1v[i] + sv[i], v2 = p2v[i] + sv[i];
-        const int c1 = p1v[i] != NEG_INF ? 2 * ai : 255, c2 = p2v[i] != NEG_INF ? 2 * ai + 1 : 255;
-        const bool top = vit_better(v1, c1, bs, bc);
-        const bool sec = !top && vit_better(v1, c1, ss, sc);
-        ss = top ? bs : (sec ? v1 : ss);
-        sc = top ? bc : (sec ? c1 : sc);
-        ws = top ? v2 : ws;
-        wc = top ? c2 : wc;
-        bs = top ? v1 : bs;
-        bc = top ? c1 : bc;
+      for (int i = 1; i < 4; ++i) {
+        const float v = av[i] + sv[i];
+        ba = v > bv ? 4 * qa + i : ba;      // strictly greater: ties keep the smaller predecessor
+        bv = fmaxf(v, bv);
       }
-      auto merge = [&](float obs, int obc, float oss, int osc, float ows, int owc) {
-        const bool theirs = vit_better(obs, obc, bs, bc);
-        // the loser's best competes with the winner's second
-        const float ls = theirs ? bs : obs, ws2 = theirs ? oss : ss;
-        const int lc = theirs ? bc : obc, wsc = theirs ? osc : sc;
-        const bool lb = vit_better(ls, lc, ws2, wsc);
-        ss = lb ? ls : ws2;
-        sc = lb ? lc : wsc;
-        ws = theirs ? ows : ws;
-        wc = theirs ? owc : wc;
-        bs = theirs ? obs : bs;
-        bc = theirs ? obc : bc;
+      auto merge = [&](float ov, int oa) {
+        const bool take = (ov > bv) | ((ov == bv) & (oa < ba));
+        bv = take ? ov : bv;
+        ba = take ? oa : ba;
       };
-      merge(quad_perm_f<0xB1>(bs), quad_perm_i<0xB1>(bc), quad_perm_f<0xB1>(ss), quad_perm_i<0xB1>(sc),
-            quad_perm_f<0xB1>(ws), quad_perm_i<0xB1>(wc));
-      merge(quad_perm_f<0x4E>(bs), quad_perm_i<0x4E>(bc), quad_perm_f<0x4E>(ss), quad_perm_i<0x4E>(sc),
-            quad_perm_f<0x4E>(ws), quad_perm_i<0x4E>(wc));
-      const bool wsec = vit_better(ws, wc, ss, sc);
-      const float s1 = bs, s2 = wsec ? ws : ss;
-      const int c1 = bc, c2 = wsec ? wc : sc;
+      merge(quad_perm_f<0xB1>(bv), quad_perm_i<0xB1>(ba));
+      merge(quad_perm_f<0x4E>(bv), quad_perm_i<0x4E>(ba));
+      if (qa == 0) {
+        w.alpha[t - 1][bi] = bv;
+        w.bp1[t - 1][bi] = (unsigned char)ba;
+      }
+    }
+    // backward sweep: lane = 4 ai + qb holds state ai of slot t, successors 4 qb .. 4 qb + 3
+    if (lane < TOPK) w.beta[K - 2][lane] = 0.f;
+    for (int t = K - 2; t >= 1; --t) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (qa == 0) {
-        dv[0][bi] = s1;
-        dv[1][bi] = s2;
-        bp1[t - 1][bi] = (unsigned char)c1;
-        bp2[t - 1][bi] = (unsigned char)c2;
-      }
-      d1 = s1;
-      d2 = s2;
+      const f32x4 bn = *reinterpret_cast<const f32x4*>(&w.beta[t][4 * qa]);
+      float m = NEG_INF;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, w.S[t][4 * qa + i][bi] + bn[i]);   // S_{t+1}(bi, 4 qa + i)
+      m = fmaxf(m, quad_perm_f<0xB1>(m));
+      m = fmaxf(m, quad_perm_f<0x4E>(m));
+      if (qa == 0) w.beta[t - 1][bi] = m;
     }
-    if (K == 2) {
-      d1 = S[0][bi][0];
-      d2 = NEG_INF;
-    }
-    // best two complete paths over the states of slot K-1 (code 2 bi + rank)
-    float s1 = NEG_INF, s2 = NEG_INF;
-    int c1 = 255, c2 = 255;
-    if (qa == 0) {
-      if (d1 != NEG_INF) top2_push(s1, c1, s2, c2, d1, 2 * bi);
-      if (d2 != NEG_INF) top2_push(s1, c1, s2, c2, d2, 2 * bi + 1);
-    }
-    for (int m = 4; m < 64; m <<= 1) top2_xor(s1, c1, s2, c2, m);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // best final state (ties to the smaller state), then the path back through the predecessors
+    float s1 = lane < TOPK ? w.alpha[K - 2][lane] : NEG_INF;
+    int st = lane < TOPK ? lane : TOPK;
+    for (int m = 1; m < 64; m <<= 1) {
+      const float ov = __shfl_xor(s1, m, WAVE);
+      const int os = __shfl_xor(st, m, WAVE);
+      const bool take = (ov > s1) | ((ov == s1) & (os < st));
+      s1 = take ? ov : s1;
+      st = take ? os : st;
+    }
     if (lane == 0) {
-      int st = c1 >> 1, rank = c1 & 1;
       for (int t = K - 1; t >= 1; --t) {
-        a.path[(size_t)b * (K - 1) + t - 1] = cid[t - 1][st];
-        if (t > 1) {
-          const int code = rank == 0 ? bp1[t - 1][st] : bp2[t - 1][st];
-          st = code >> 1;
-          rank = code & 1;
-        }
+        w.best[t - 1] = st;
+        a.path[(size_t)b * (K - 1) + t - 1] = w.cid[t - 1][st];
+        if (t > 1) st = w.bp1[t - 1][st];
       }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float s2 = NEG_INF;
+    for (int e = lane; e < (K - 1) * TOPK; e += WAVE) {
+      const int tt = e / TOPK, sb = e % TOPK;
+      if (sb != w.best[tt]) s2 = fmaxf(s2, w.alpha[tt][sb] + w.beta[tt][sb]);
+    }
+    s2 = wave_max(s2);
+    if (lane == 0) {
       if (a.score) a.score[b] = s1;
-      if (a.margin) a.margin[b] = s1 - s2;
+      if (a.margin) a.margin[b] = fmaxf(s1 - s2, 0.f);
     }
   } else if (a.mode == 2) {
     // sampling walk: at slot t, q(b) = softmax_b(S_t(a, b) / T) over the 16 candidates given
@@ -350,7 +133,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     const bool in = lane < TOPK;
     const bool cut = a.top_p < 1.f;
     for (int t = 1; t < K; ++t) {
-      const float z = in ? S[t - 1][lane][ai] * a.inv_temp : NEG_INF;
+      const float z = in ? w.S[t - 1][lane][ai] * a.inv_temp : NEG_INF;
       const float mx = wave_max(z);
       const float e = in ? __expf(z - mx) : 0.f;
       float q = e / wave_sum(e);
@@ -380,7 +163,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
       const float qp = __shfl(q, pick, WAVE);
       const size_t o = (size_t)b * (K - 1) + t - 1;
       if (lane == 0) {
-        a.path[o] = cid[t - 1][pick];
+        a.path[o] = w.cid[t - 1][pick];
         a.q_path[o] = qp;
       }
       if (a.q_cand && in) a.q_cand[o * TOPK + lane] = q;
@@ -391,7 +174,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     int ai = 0;
     float total = 0.f, margin = __builtin_huge_valf();
     for (int t = 1; t < K; ++t) {
-      const float v = lane < TOPK ? S[t - 1][lane][ai] : NEG_INF;
+      const float v = lane < TOPK ? w.S[t - 1][lane][ai] : NEG_INF;
       float m1 = v;
       int i1 = lane < TOPK ? lane : 255;
       for (int m = 1; m < TOPK; m <<= 1) {
@@ -408,7 +191,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
       sec = __shfl(sec, 0, WAVE);
       margin = fminf(margin, m1 - sec);
       total += m1;
-      if (lane == 0) a.path[(size_t)b * (K - 1) + t - 1] = cid[t - 1][i1];
+      if (lane == 0) a.path[(size_t)b * (K - 1) + t - 1] = w.cid[t - 1][i1];
       ai = i1;
     }
     if (lane == 0) {
@@ -416,6 +199,294 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
       if (a.margin) a.margin[b] = margin;
     }
   }
+}
+
+// One workgroup per (group of up to SEL_SPW consecutive slots, chunk of 32 ranks) of sequence b
+// (grid x = group * chunks + chunk, y = b; a.spw slots per group: one for small batches, the
+// most parallel split, all of them for larger batches, where one workgroup per sequence needs
+// no hand-off and reads each chunk of W_H once).  Phases: (1) the gates
+// g_t[j] = sigmoid(W_H[j] . h_final[b][t]) of the group's slots for the chunk's ranks (bf16
+// tables: MFMA with slots as rows and ranks as columns, h as hi + lo planes, the eight waves
+// splitting the hidden dimension; fp32 tables: VALU dot products); (2) the chunk's share of the
+// 16 x 16 pair scores of each slot, sum_j A[pred a][j] * g_t[j] * B[cand b][j] (predecessors:
+// the anchor for t = 1, else the candidates of slot t - 1); (3) with several workgroups per
+// sequence, the shares go to the workspace and the last workgroup to finish adds them in chunk
+// order; then the logit term U_t(b) is added and the sequence's workgroup walks.
+constexpr int SEL_SPW = 16;     // most slots per workgroup (one MFMA row tile)
+constexpr int SEL_HROWS = 4;    // groups of at most this many slots stage their h rows in LDS
+
+template <typename T, bool STAGE>
+__global__ __launch_bounds__(SEL_T) void select_kernel(SelectArgs a) {
+  // LDS pool: bf16 h planes of up to SEL_HROWS slots followed by their tables, or the tables of
+  // up to SEL_SPW slots; table (slot s, side q) is [16 rows][SEL_SR + 4] floats (rows 16-byte aligned)
+  constexpr int TS_ = SEL_SR + 4;
+  constexpr int TABF = TOPK * TS_;
+  constexpr int HHB = SEL_HROWS * 2 * SEL_DMAX * 2;
+  constexpr int POOL = HHB + 2 * SEL_HROWS * TABF * 4 > 2 * SEL_SPW * TABF * 4 ? HHB + 2 * SEL_HROWS * TABF * 4
+                                                                              : 2 * SEL_SPW * TABF * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char pool[POOL];
+  __shared__ __attribute__((aligned(16))) float red[SEL_T / WAVE][SEL_SPW][SEL_SR];
+  __shared__ __attribute__((aligned(16))) float gsh[SEL_SPW][SEL_SR];
+  __shared__ int last_flag;
+  __shared__ __attribute__((aligned(16))) SelWalk sw;
+  const int K = a.K, r = a.r, d = a.d, spw = a.spw;
+  const int nrc = (r + SEL_SR - 1) / SEL_SR;
+  const int ngrp = (K - 1 + spw - 1) / spw;
+  const int b = blockIdx.y, grp = blockIdx.x / nrc, rc = blockIdx.x % nrc;
+  const int t0 = grp * spw + 1, ns = min(spw, K - t0);        // slots t0 .. t0 + ns - 1
+  const int r0 = rc * SEL_SR, nr = min(SEL_SR, r - r0);       // nr: a multiple of 8
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ncand = (K - 1) * TOPK;
+  const int* ids = a.topk_ids + (size_t)b * ncand;
+  // STAGE (bf16 tables, at most SEL_HROWS slots): h rows staged in LDS as bf16 planes
+  constexpr bool stage = STAGE && sizeof(T) == 2;
+  bf16 (*hh)[2][SEL_DMAX] = reinterpret_cast<bf16 (*)[2][SEL_DMAX]>(pool);
+  float* tab = reinterpret_cast<float*>(pool + (stage ? HHB : 0));
+  auto ta = [&](int sl, int row) { return tab + ((2 * sl) * TOPK + row) * TS_; };
+  auto tb = [&](int sl, int row) { return tab + ((2 * sl + 1) * TOPK + row) * TS_; };
+  // (a) table gathers, item e: slot e / (32 VPR), row (e / VPR) % 32 (0..15: A of the
+  // predecessors, 16..31: B of the slot's candidates), 16 bytes v = e % VPR of ranks r0 .. r0 + nr
+  constexpr int VE = 16 / sizeof(T);
+  constexpr int VPR = SEL_SR / VE;
+  constexpr int GPT = (2 * TOPK * SEL_SPW * VPR + SEL_T - 1) / SEL_T;
+  const int ng = 2 * TOPK * ns * VPR;
+  int tok[GPT];
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int e = tid + i * SEL_T, row = (e / VPR) % (2 * TOPK), t = t0 + e / (2 * TOPK * VPR);
+    tok[i] = 0;
+    if (e < ng) tok[i] = row < TOPK ? (t == 1 ? a.anchor[b] : ids[(t - 2) * TOPK + row]) : ids[(t - 1) * TOPK + row - TOPK];
+  }
+  // (b) bf16 tables: the h rows of a small group (staged in LDS below), then the W_H fragments
+  // (and, for a large group, its h fragments) of the first batch, issued before the gathers
+  constexpr int HPT = SEL_HROWS * SEL_DMAX / (4 * SEL_T);     // staged h pieces of 4 per thread
+  f32x4 hx[HPT];
+  if constexpr (stage) {
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) {
+      const int e = (i * SEL_T + tid) * 4, sl = min(e / d, ns - 1), k = e % d;
+      hx[i] = *reinterpret_cast<const f32x4*>(a.h_final + ((size_t)b * K + t0 + sl) * d + k);
+    }
+  }
+  constexpr int NWV = SEL_T / WAVE;
+  constexpr int CB = 8;                        // 32-wide k chunks per wave and batch
+  const int li = lane & 15, kg = lane >> 4;
+  const int nch = d / 32;
+  const int hrow = min(li, ns - 1);            // MFMA row li = slot t0 + li
+  u32x4 wv[CB][2];
+  f32x4 hv[CB][2];
+  const bf16* w0 = reinterpret_cast<const bf16*>(a.WH) + (size_t)min(r0 + li, r - 1) * d + kg * 8;
+  const bf16* w1 = reinterpret_cast<const bf16*>(a.WH) + (size_t)min(r0 + 16 + li, r - 1) * d + kg * 8;
+  const float* hr = a.h_final + ((size_t)b * K + t0 + hrow) * d + kg * 8;
+  auto issue = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int c = min(c0 + NWV * u, nch - 1);
+      wv[u][0] = *reinterpret_cast<const u32x4*>(w0 + c * 32);
+      wv[u][1] = *reinterpret_cast<const u32x4*>(w1 + c * 32);
+      if constexpr (!stage) {
+        hv[u][0] = *reinterpret_cast<const f32x4*>(hr + c * 32);
+        hv[u][1] = *reinterpret_cast<const f32x4*>(hr + c * 32 + 4);
+      }
+    }
+  };
+  if constexpr (sizeof(T) == 2) issue(wave);
+  u32x4 xv[GPT];
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int e = tid + i * SEL_T, row = (e / VPR) % (2 * TOPK), v = e % VPR;
+    const int t = t0 + e / (2 * TOPK * VPR);
+    xv[i] = u32x4{0u, 0u, 0u, 0u};
+    if (e < ng) {
+      int k = tok[i];
+      if (k < 0 || k >= a.vocab) {             // out-of-range token: record and read row 0
+        atomicOr(a.dev_err, (row < TOPK && t == 1) ? 8 : 16);
+        k = 0;
+      }
+      const T* base = reinterpret_cast<const T*>(row < TOPK ? a.A : a.B) + (size_t)k * r + r0;
+      if (v * VE < nr) xv[i] = reinterpret_cast<const u32x4*>(base)[v];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int e = tid + i * SEL_T, row = (e / VPR) % (2 * TOPK), v = e % VPR, sl = e / (2 * TOPK * VPR);
+    if (e < ng) {
+      float* dst = (row < TOPK ? ta(sl, row) : tb(sl, row - TOPK)) + v * VE;
+#pragma unroll
+      for (int q = 0; q < VE; ++q) dst[q] = v * VE + q < nr ? ldv(reinterpret_cast<const T*>(&xv[i]), q) : 0.f;
+    }
+  }
+  // (1) gates
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (stage) {
+#pragma unroll
+      for (int i = 0; i < HPT; ++i) {
+        const int e = (i * SEL_T + tid) * 4, sl = e / d, k = e % d;
+        if (sl < ns) {
+          uint32_t hp[2], lp[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const bf16 h0 = f2bf(hx[i][2 * q]), h1 = f2bf(hx[i][2 * q + 1]);
+            hp[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lp[q] = (uint32_t)f2bf(hx[i][2 * q] - bf2f(h0)) | ((uint32_t)f2bf(hx[i][2 * q + 1] - bf2f(h1)) << 16);
+          }
+          *reinterpret_cast<uint2*>(&hh[sl][0][k]) = make_uint2(hp[0], hp[1]);
+          *reinterpret_cast<uint2*>(&hh[sl][1][k]) = make_uint2(lp[0], lp[1]);
+        }
+      }
+    }
+    lds_barrier();
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = wave; c0 < nch; c0 += NWV * CB) {
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        // a chunk past the end (its loads were clamped) adds zero: no branch, so that the
+        // whole batch of loads stays ahead of the first MFMA
+        const bool live = c0 + NWV * u < nch;
+        const int c = min(c0 + NWV * u, nch - 1);
+        u32x4 hi, lo;
+        if constexpr (stage) {
+          hi = *reinterpret_cast<const u32x4*>(&hh[hrow][0][c * 32 + kg * 8]);
+          lo = *reinterpret_cast<const u32x4*>(&hh[hrow][1][c * 32 + kg * 8]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = e < 2 ? hv[u][0][2 * e] : hv[u][1][2 * e - 4];
+            const float x1 = e < 2 ? hv[u][0][2 * e + 1] : hv[u][1][2 * e - 3];
+            const bf16 h0 = f2bf(x0), h1 = f2bf(x1);
+            hi[e] = (unsigned)h0 | ((unsigned)h1 << 16);
+            lo[e] = (unsigned)f2bf(x0 - bf2f(h0)) | ((unsigned)f2bf(x1 - bf2f(h1)) << 16);
+          }
+        }
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const bf16x8 x0 = as_bf16x8(live ? wv[u][0] : z), x1 = as_bf16x8(live ? wv[u][1] : z);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(hi), x0, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lo), x0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(hi), x1, acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lo), x1, acc1, 0, 0, 0);
+      }
+      if (c0 + NWV * CB < nch) issue(c0 + NWV * CB);
+    }
+    // D layout: lane (li, kg) holds rows (slots) 4 kg .. 4 kg + 3 of column (rank) li
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sl = 4 * kg + j;
+      if (sl < ns) {
+        red[wave][sl][li] = acc0[j];
+        red[wave][sl][16 + li] = acc1[j];
+      }
+    }
+    lds_barrier();
+    if (tid < ns * SEL_SR) {
+      const int sl = tid / SEL_SR, j = tid % SEL_SR;
+      float g = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) g += red[w][sl][j];
+      gsh[sl][j] = j < nr ? sigmoidf_(g) : 0.f;
+    }
+  } else {
+    // fp32 tables: 16 lanes per rank, each over every 64th group of 4 k, slot by slot
+    const int j = tid >> 4, p = tid & 15;
+    const float* wr = reinterpret_cast<const float*>(a.WH) + (size_t)min(r0 + j, r - 1) * d;
+    for (int sl = 0; sl < ns; ++sl) {
+      const float* hb = a.h_final + ((size_t)b * K + t0 + sl) * d;
+      float acc = 0.f;
+      for (int k = p * 4; k < d; k += 64) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(wr + k);
+        const f32x4 h = *reinterpret_cast<const f32x4*>(hb + k);
+        acc += x[0] * h[0] + x[1] * h[1] + x[2] * h[2] + x[3] * h[3];
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m, WAVE);
+      if (p == 0) gsh[sl][j] = j < nr ? sigmoidf_(acc) : 0.f;
+    }
+  }
+  lds_barrier();
+  // (2) this chunk's share of the pair scores, item (slot sl, b, a); with one workgroup per
+  // sequence (one group, one chunk) it is the whole pair term and goes straight to the walk
+  const bool single = ngrp * nrc == 1;
+  // item (slot sl, state b, APT predecessors): B[b] * g_t in registers, dotted with APT A rows
+  // (APT = 1 for small groups: every lane busy; 4 for large ones: fewer LDS reads per score)
+  constexpr int APT = STAGE ? 1 : 4;
+  for (int e = tid; e < ns * TOPK * (TOPK / APT); e += SEL_T) {
+    const int sl = e / (TOPK * TOPK / APT), bi = (e / (TOPK / APT)) % TOPK, a0 = (e % (TOPK / APT)) * APT;
+    const int t = t0 + sl;
+    float gb[SEL_SR];
+    const float* pb = tb(sl, bi);
+#pragma unroll
+    for (int j4 = 0; j4 < SEL_SR / 4; ++j4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(pb + 4 * j4);
+      const f32x4 g = *reinterpret_cast<const f32x4*>(&gsh[sl][4 * j4]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) gb[4 * j4 + q] = x[q] * g[q];   // ranks >= nr are zero
+    }
+    float v[APT];
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+      const float* pa = ta(sl, a0 + i);
+      float acc = 0.f;
+#pragma unroll
+      for (int j4 = 0; j4 < SEL_SR / 4; ++j4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(pa + 4 * j4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc += x[q] * gb[4 * j4 + q];
+      }
+      v[i] = (t > 1 || a0 + i == 0) ? acc : 0.f;   // slot 1 has the anchor as its only predecessor
+    }
+    if (single) {
+      const float u = a.topk_logits[(size_t)b * ncand + (t - 1) * TOPK + bi];
+#pragma unroll
+      for (int i = 0; i < APT; ++i) sw.S[t - 1][bi][a0 + i] = v[i] + u;
+    } else {
+      float* o = a.spart + (((size_t)b * (K - 1) + t - 1) * nrc + rc) * (TOPK * TOPK) + bi * TOPK + a0;
+#pragma unroll
+      for (int i = 0; i < APT; ++i) o[i] = v[i];
+    }
+  }
+  if (single) {
+    if (tid < ncand) {
+      const int id = ids[tid];
+      sw.cid[tid / TOPK][tid % TOPK] = (id < 0 || id >= a.vocab) ? 0 : id;   // recorded in phase (a)
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    sel_walk(a, b, sw);
+    return;
+  }
+  // (3) the last workgroup of the sequence
+  if (!arrive_last(a.sel_cnt + b, (unsigned)(ngrp * nrc), &last_flag)) return;
+  // thread e takes pair scores e, e + SEL_T, ...: every load of a chunk is issued before any is
+  // used (one memory round trip per rank chunk, not one per element)
+  constexpr int EPT = ((SEL_KMAX - 1) * TOPK * TOPK + SEL_T - 1) / SEL_T;
+  const int ne = (K - 1) * TOPK * TOPK;
+  const float* spb = a.spart + (size_t)b * (K - 1) * nrc * (TOPK * TOPK);
+  const int id = ids[min(tid, ncand - 1)];
+  float sum[EPT], lg[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = min(tid + i * SEL_T, ne - 1), tt = e / (TOPK * TOPK);
+    lg[i] = a.topk_logits[(size_t)b * ncand + tt * TOPK + (e % (TOPK * TOPK)) / TOPK];
+    sum[i] = 0.f;
+  }
+  for (int q = 0; q < nrc; ++q) {
+    float x[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = min(tid + i * SEL_T, ne - 1), tt = e / (TOPK * TOPK);
+      x[i] = spb[((size_t)tt * nrc + q) * (TOPK * TOPK) + e % (TOPK * TOPK)];
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) sum[i] += x[i];
+  }
+  if (tid < ncand) sw.cid[tid / TOPK][tid % TOPK] = (id < 0 || id >= a.vocab) ? 0 : id;   // recorded in phase (a)
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid + i * SEL_T;
+    if (e < ne) sw.S[e / (TOPK * TOPK)][(e % (TOPK * TOPK)) / TOPK][e % TOPK] = sum[i] + lg[i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  sel_walk(a, b, sw);
 }
 
 // Greedy longest-prefix verification: one wave per sequence, lane j on slot c0 + j of each
@@ -599,8 +670,28 @@ __global__ __launch_bounds__(1024) void synth_target_kernel(SynthArgs a) {
 }
 
 hipError_t launch_select(bool bf, const SelectArgs& a, int n_seq, hipStream_t st) {
-  if (bf) hipLaunchKernelGGL(select_kernel<bf16>, dim3(n_seq), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(select_kernel<float>, dim3(n_seq), dim3(256), 0, st, a);
+  if (a.K < 2 || a.K > SEL_KMAX || a.r < 8 || a.r > 256 || a.r % 8 || a.d < 64 || a.d > SEL_DMAX || a.d % 64 ||
+      !a.spart || !a.sel_cnt)
+    return hipErrorInvalidValue;
+  // slots per workgroup: one for small batches (the most parallel split, with a hand-off to the
+  // last workgroup of each sequence), else all of them (one workgroup per sequence when the rank
+  // fits one chunk: no hand-off, each chunk of W_H read once per sequence)
+  SelectArgs g = a;
+  const int nrc = (a.r + SEL_SR - 1) / SEL_SR;
+  g.spw = (long)n_seq * (a.K - 1) * nrc <= 128 ? 1 : (a.K - 1 < SEL_SPW ? a.K - 1 : SEL_SPW);
+  const dim3 grid(((a.K - 1 + g.spw - 1) / g.spw) * nrc, n_seq);
+  if (bf && g.spw <= SEL_HROWS) hipLaunchKernelGGL((select_kernel<bf16, true>), grid, dim3(SEL_T), 0, st, g);
+  else if (bf) hipLaunchKernelGGL((select_kernel<bf16, false>), grid, dim3(SEL_T), 0, st, g);
+  else hipLaunchKernelGGL((select_kernel<float, false>), grid, dim3(SEL_T), 0, st, g);
+  return hipGetLastError();
+}
+__global__ __launch_bounds__(256) void fill_u32_kernel(unsigned* p, int n, unsigned v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n, v);
   return hipGetLastError();
 }
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {

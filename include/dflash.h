@@ -223,10 +223,12 @@ DFLASH_API dflash_status dflash_draft_block_static(dflash_handle* h, int32_t n_s
 /* (3) Path selection over the candidate lattice ("Architecture", section "Problem 1 --
  * Independent picks are incoherent"): S_t(a, b) = U_t(b) + sum_j A[a,j] * H_t[j] * B[b,j] with
  * U_t the drafter logit, H_t = sigmoid(W_H h_final[t]); slot 1's predecessor is the anchor.
- * VITERBI: the max-scoring path (2-best list Viterbi; margin = best - second-best path score).
+ * VITERBI: the max-scoring path (margin = best - second-best complete path score, exact).
  * GREEDY: follow the best successor from the anchor (margin = smallest best-minus-second gap).
  * Ties go to the smaller candidate index.  path_ids [n_seq][K-1]; path_score, margin [n_seq]
- * may be NULL. */
+ * may be NULL.  Works in the handle's workspace (partial pair scores and one arrival counter
+ * per sequence), so it must not overlap the handle's other calls; the first selector call of a
+ * handle also enqueues a small kernel that zeroes the counters (each launch leaves them zero). */
 DFLASH_API dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, const int32_t* anchor_ids, const int32_t* topk_ids,
                                  const float* topk_logits, const float* h_final, dflash_select_mode mode,
                                  int32_t* path_ids, float* path_score, float* margin, void* stream);
@@ -241,7 +243,8 @@ DFLASH_API dflash_status dflash_select_path(dflash_handle* h, int32_t n_seq, con
  * [0, 1) are the caller's random numbers.  Outputs: path_ids [n_seq][K-1]; q_path
  * [n_seq][K-1] = q_t(pick); q_cand [n_seq][K-1][16] = q_t over the candidates after the cut (may be NULL;
  * dflash_verify_rejection needs it).  Device pointers; temperature in [1e-6, 1e6] (the walk's
- * picks are the greedy walk's as it goes to 0); top_p in (0, 1]. */
+ * picks are the greedy walk's as it goes to 0); top_p in (0, 1].  Workspace use as for
+ * dflash_select_path. */
 DFLASH_API dflash_status dflash_select_sample(dflash_handle* h, int32_t n_seq, const int32_t* anchor_ids, const int32_t* topk_ids,
                                    const float* topk_logits, const float* h_final, float temperature,
                                    float top_p, const float* uniforms, int32_t* path_ids, float* q_path,
