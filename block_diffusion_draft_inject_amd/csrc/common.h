@@ -48,30 +48,6 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Hand-off from n workgroups to the one that arrives last at `counter` (device memory, zero
-// before the first of the n arrivals).  Returns true in every thread of that workgroup, which
-// then sees every global store the other n - 1 made before they arrived, and leaves the counter
-// at zero for the next launch.  The workgroups may sit on different XCDs, whose L2 caches are
-// separate: the workgroup barrier completes every wave's stores (into this XCD's L2), then
-// one agent-scope release by the counting thread writes the L2 back (one write-back per
-// workgroup, not per wave), the count itself is a system-scope atomic (performed past the
-// L2s), and the last workgroup acquires at agent scope after it (L2 invalidated).  No
-// workgroup waits for another.
-__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned n, int* flag_lds) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    const int last = prev + 1 == n;
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    *flag_lds = last;
-  }
-  __syncthreads();
-  const bool last = *flag_lds != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
-}
-
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
 // Cross-lane data movement with DPP (no LDS round trip).  Controls used: quad_perm [1,0,3,2]

@@ -142,6 +142,30 @@ struct AttnArgs {
   void* o;             // [rows][nh*dh]
 };
 
+// Hand-off from n workgroups to the one that arrives last at `counter` (device memory, zero
+// before the first of the n arrivals).  Returns true in every thread of that workgroup, which
+// then sees every global store the other n - 1 made before they arrived, and leaves the counter
+// at zero for the next launch.  The workgroups may sit on different XCDs, whose L2 caches are
+// separate: the workgroup barrier completes every wave's stores (into this XCD's L2), then
+// one agent-scope release by the counting thread writes the L2 back (one write-back per
+// workgroup, not per wave), the count itself is a system-scope atomic (performed past the
+// L2s), and the last workgroup acquires at agent scope after it (L2 invalidated).  No
+// workgroup waits for another.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned n, int* flag_lds) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int last = prev + 1 == n;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    *flag_lds = last;
+  }
+  __syncthreads();
+  const bool last = *flag_lds != 0;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
 struct SelectArgs {
   int K, d, r, mode, vocab;   // mode 0 = Viterbi, 1 = greedy, 2 = sampling walk
   int* dev_err;
