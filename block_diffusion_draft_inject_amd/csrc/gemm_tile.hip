@@ -224,16 +224,19 @@ __device__ __forceinline__ void tile_run_pairs(const GemmParams& p, unsigned cha
   }
 }
 
-// PARTIAL: grid x = column tile, y = row tile, z = k-split; part[z][row][col].
+// PARTIAL: grid x = k-split, y = column tile, z = row tile; part[split][row][col].  The split is
+// the fastest grid index: workgroups go to the eight XCDs round-robin by linear index, so with
+// eight splits each XCD takes one k-range and its L2 fetches only that slice of the activation
+// rows (every column tile of a split reads the same slice), instead of all of them.
 template <class T, int OCC>
 __global__ __launch_bounds__(T::NT, OCC) void gemm_tile_partial(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / T::WGNc, wn = wave % T::WGNc, li = lane & 15, kg = lane >> 4;
   const int Mv = rows_valid(p);
-  const int m0 = blockIdx.y * T::BMc, n0 = blockIdx.x * T::BNc;
+  const int m0 = blockIdx.z * T::BMc, n0 = blockIdx.y * T::BNc;
   if (m0 >= Mv) return;
-  const int nk = p.K / MK, s = blockIdx.z;
+  const int nk = p.K / MK, s = blockIdx.x;
   const int c0 = (int)((long)nk * s / p.splits), c1 = (int)((long)nk * (s + 1) / p.splits);
   f32x4 acc[T::FM][T::FN];
   if constexpr (T::Sc == 4) {
@@ -406,9 +409,10 @@ hipError_t tile_launch(const GemmPlan& pl, int mode, const GemmParams& p, hipStr
       else hipLaunchKernelGGL((lmhead_topk_tile<TileSmallHi, 2, false>), pl.grid, blk, 0, st, p);
     }
   } else if (mode == GEMM_PARTIAL) {
-    if (pl.mt == 2) hipLaunchKernelGGL((gemm_tile_partial<TileTall, 1>), pl.grid, dim3(TileTall::NT), 0, st, p);
-    else if (pl.mt) hipLaunchKernelGGL((gemm_tile_partial<TileBig, 1>), pl.grid, dim3(TileBig::NT), 0, st, p);
-    else hipLaunchKernelGGL((gemm_tile_partial<TileSmall, 2>), pl.grid, dim3(TileSmall::NT), 0, st, p);
+    const dim3 g(pl.grid.z, pl.grid.x, pl.grid.y);   // (split, column tile, row tile)
+    if (pl.mt == 2) hipLaunchKernelGGL((gemm_tile_partial<TileTall, 1>), g, dim3(TileTall::NT), 0, st, p);
+    else if (pl.mt) hipLaunchKernelGGL((gemm_tile_partial<TileBig, 1>), g, dim3(TileBig::NT), 0, st, p);
+    else hipLaunchKernelGGL((gemm_tile_partial<TileSmall, 2>), g, dim3(TileSmall::NT), 0, st, p);
   } else {
     return hipErrorInvalidValue;
   }
