@@ -49,10 +49,9 @@ Rounding points ("mode"):
               injection and the block's own k/v (after per-head norm and RoPE) are rounded
               to bf16 (nearest, ties to even).  The shared lm_head is a bf16 product: its
               input, the final-normed hidden h_f of slots 1..K-1, is rounded to bf16 too
-              (the returned h_final, which the selector reads, is not).  So is the input of
-              every feed-forward sublayer (the pre-convolved, normed row that enters the gate
-              and up projections).  Weights and target states are bf16 inputs; every other
-              value (activations, accumulations, softmax, logits, selector) stays float64.
+              (the returned h_final, which the selector reads, is not).  Weights and target
+              states are bf16 inputs; every other value (activations, accumulations,
+              softmax, logits, selector) stays float64.
 """
 from __future__ import annotations
 
@@ -273,7 +272,7 @@ def draft_block(cfg, W, cache: DraftCache, anchor, mode="bf16", block_ids=None, 
         h = h + sublayer_conv(cfg, a, lw["conv_attn_post_w"], lw["conv_attn_post_b"])
         # feed-forward sublayer
         z = rms_norm(h, lw["mlp_norm"], cfg.rms_eps)
-        y = R(sublayer_conv(cfg, z, lw["conv_mlp_pre_w"], lw["conv_mlp_pre_b"]))   # bf16 MLP input in mode "bf16"
+        y = sublayer_conv(cfg, z, lw["conv_mlp_pre_w"], lw["conv_mlp_pre_b"])
         s = silu(y @ as64(lw["w_gate"]).T) * (y @ as64(lw["w_up"]).T)
         m = s @ as64(lw["w_down"]).T
         h = h + sublayer_conv(cfg, m, lw["conv_mlp_post_w"], lw["conv_mlp_post_b"])
