@@ -219,8 +219,9 @@ def run_pipeline(torch, wname="b32_k8_conv", reps=10, graph_steps=10):
         torch.cuda.synchronize()
         res[kind] = (time.perf_counter() - t0) * 1e3 / (reps * G)
         del graph
-    if d_all.dflash_get_device_error():
-        raise RuntimeError("device error word set in the pipeline leg")
+    e = d_all.dflash_get_device_error()
+    if e:
+        raise RuntimeError(f"device error word {e:#x} set in the pipeline leg")
     for d in (d_hi, d_lo, d_all):
         d.close()
     return res
