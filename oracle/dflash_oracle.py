@@ -566,6 +566,79 @@ def dequantize_fp8_rows(codes, scales):
     return e4m3_value(codes) * np.asarray(scales, dtype=F64)[:, None]
 
 
+# --------------------------------------------------------------------------------------
+# MXFP4 weight-only drafts (a NEXT-step option, not part of the pages' pass)
+# --------------------------------------------------------------------------------------
+# The pages run 4-bit drafts on one backend ("z-lab/dflash" README mirror, section "MLX (Apple
+# Silicon)") and fix no format.  The format here is the OCP Microscaling MXFP4 encoding: along each
+# weight row, blocks of 32 consecutive weights share one scale 2^s, stored as an 8-bit exponent
+# byte s + 127 (E8M0); each weight is a 4-bit E2M1 element (sign bit, 2 exponent bits, 1 mantissa
+# bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).  The block's largest magnitude a sets
+# s = floor(log2 a) - 2, 2 being the exponent of the largest element magnitude 6 = 1.5 * 2^2, so a
+# lands in [4, 8) * 2^s.  Each element is the E2M1 magnitude nearest to |w| / 2^s (ties to the even
+# code, i.e. mantissa bit 0), magnitudes above 6 saturate to 6, and the sign bit is w's (so -0 is
+# code 8).  A block whose largest magnitude is below 2^-64 is stored as zero codes with scale 1.
+# Two elements per byte: element 2j in the low nibble, element 2j + 1 in the high one.
+
+E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+MX_BLOCK = 32
+MX_ZERO_BLOCK = 2.0 ** -64
+
+
+def e2m1_code(x):
+    """4-bit E2M1 code (0..15) of each x: the nearest magnitude (ties to the even code, saturating
+    at 6) with bit 3 the sign bit of x."""
+    x = np.asarray(x, dtype=F64)
+    a = np.minimum(np.abs(x), 6.0)
+    dist = np.abs(a[..., None] - E2M1_MAG)
+    nearest = dist == dist.min(axis=-1, keepdims=True)         # one code, or two at a midpoint
+    idx = np.arange(8)
+    even = np.where(nearest & (idx % 2 == 0), idx, 99).min(axis=-1)
+    code = np.where(even < 99, even, np.where(nearest, idx, 99).min(axis=-1))
+    return code | (np.signbit(x).astype(np.int64) << 3)
+
+
+def e2m1_value(codes):
+    """Value of each 4-bit E2M1 code."""
+    c = np.asarray(codes).astype(np.int64)
+    mag = E2M1_MAG[c & 7]
+    return np.where(c & 8, -mag, mag)
+
+
+def mx_block_exponent(amax):
+    """s = floor(log2 amax) - 2 for one block (0 for a block stored as zero)."""
+    amax = float(amax)
+    if amax < MX_ZERO_BLOCK:
+        return 0
+    return math.frexp(amax)[1] - 3          # frexp: amax = m 2^e, m in [0.5, 1): floor(log2) = e - 1
+
+
+def quantize_mxfp4_rows(W):
+    """MXFP4 codes and block scales of W [rows][cols] (cols a multiple of 32; the bf16 values as
+    float64).  Returns (codes uint8 [rows][cols/2], element 2j in the low nibble of byte j;
+    scale bytes uint8 [rows][cols/32] = s + 127)."""
+    W = np.asarray(W, dtype=F64)
+    rows, cols = W.shape
+    assert cols % MX_BLOCK == 0
+    blocks = W.reshape(rows, cols // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(blocks), axis=-1)
+    s = np.array([[mx_block_exponent(a) for a in r] for r in amax], dtype=np.int64).reshape(amax.shape)
+    assert np.all((s + 127 >= 1) & (s + 127 <= 254))
+    codes = e2m1_code(np.ldexp(blocks, -s[..., None])).reshape(rows, cols)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (s + 127).astype(np.uint8)
+
+
+def dequantize_mxfp4_rows(packed, scale_bytes):
+    """The weights MXFP4 codes stand for: value(element) * 2^(scale byte - 127), exact in float64."""
+    packed = np.asarray(packed).astype(np.int64)
+    rows = packed.shape[0]
+    codes = np.stack([packed & 15, packed >> 4], axis=-1).reshape(rows, -1)
+    cols = codes.shape[1]
+    sc = np.ldexp(1.0, np.asarray(scale_bytes).astype(np.int64) - 127)      # [rows][cols/32]
+    return (e2m1_value(codes).reshape(rows, cols // MX_BLOCK, MX_BLOCK) * sc[..., None]).reshape(rows, cols)
+
+
 def expected_tau(match_probs):
     """E[tau] when draft i is accepted with conditional probability r_i given all earlier
     ones were: 1 + sum_i prod_{j<=i} r_j (the bonus token always counts)."""
