@@ -320,7 +320,7 @@ def algorithmic(cfg, tau_mean, n_ctx):
 
 
 def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=False, fp8_mlp=False,
-                 fp8_attn_inject=False):
+                 fp8_attn_inject=False, mxfp4_lm_head=False):
     """Times `steps` steps twice on one stream: (1) replays of a HIP graph holding
     `graph_steps` steps (the headline rate; no events inside the graph), (2) the same number of
     steps launched eagerly, each lm_head launch bracketed by HIP events on that stream (the
@@ -332,6 +332,12 @@ def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=
                    torch.empty(lm.shape[0], dtype=torch.float32, device="cuda"))
         cyc.Bd.dflash_quantize_fp8_rows(lm, *cyc.lm8)
         cyc.d.dflash_set_lm_head_fp8(*cyc.lm8)
+    if mxfp4_lm_head:   # MXFP4 codes + block scale bytes of the lm_head, made on the device
+        lm = cyc.w["lm_head"]
+        cyc.lm4 = (torch.empty((lm.shape[0], lm.shape[1] // 2), dtype=torch.uint8, device="cuda"),
+                   torch.empty((lm.shape[0], lm.shape[1] // 32), dtype=torch.uint8, device="cuda"))
+        cyc.Bd.dflash_quantize_mxfp4_rows(lm, *cyc.lm4)
+        cyc.d.dflash_set_lm_head_mxfp4(*cyc.lm4)
     if fp8_mlp:       # E4M3 codes of every layer's stacked [gate; up] and down matrices
         cyc.mlp8 = []
         for l, lw in enumerate(cyc.w["layers"]):
@@ -736,6 +742,27 @@ def main():
                 "blocks_per_s": round(r10["blocks_per_s"], 1), "draft_tokens_per_s": round(r10["draft_tokens_per_s"], 1),
                 "ms_per_step": round(r10["ms_per_step"], 4)}
             del r10["cycle"]
+            torch.cuda.empty_cache()
+            r11 = run_workload(cfg, args.steps, args.warmup, torch, mxfp4_lm_head=True)
+            lm4_bytes = cfg.vocab * cfg.hidden // 2 + cfg.vocab * cfg.hidden // 32 + cfg.block_size * cfg.hidden * 2
+            out["mxfp4_lm_head"] = {
+                "workload": "b1_k16 with the lm_head as MXFP4 (E2M1 codes, one power-of-two scale byte per 32 "
+                            "weights; weight-only; activations and every other weight bf16)",
+                "blocks_per_s": round(r11["blocks_per_s"], 1), "draft_tokens_per_s": round(r11["draft_tokens_per_s"], 1),
+                "ms_per_step": round(r11["ms_per_step"], 4),
+                "lm_head_avg_ms": round(r11["lm_head_ms"], 5), "lm_head_bytes": int(lm4_bytes),
+                "lm_head_gbps": round(lm4_bytes / (r11["lm_head_ms"] * 1e-3) / 1e9, 1),
+                "lm_head_hbm_frac": round(lm4_bytes / (r11["lm_head_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            del r11["cycle"]
+            torch.cuda.empty_cache()
+            r12 = run_workload(cfg, args.steps, args.warmup, torch, mxfp4_lm_head=True, fp8_mlp=True,
+                               fp8_attn_inject=True)
+            out["mxfp4_lm_head_fp8_rest"] = {
+                "workload": "b1_k16 with the lm_head as MXFP4 and every other weight GEMM of the cycle as E4M3 "
+                            "codes (weight-only; activations bf16)",
+                "blocks_per_s": round(r12["blocks_per_s"], 1), "draft_tokens_per_s": round(r12["draft_tokens_per_s"], 1),
+                "ms_per_step": round(r12["ms_per_step"], 4)}
+            del r12["cycle"]
     batched = [("b32", "b32_k8_conv", args.no_b32,
                 "b32_k8_conv: same drafter, K=8, batch 32, contexts U[512,4096] (window 1024), two-tap conv, "
                 "0.7 match rule"),

@@ -86,6 +86,8 @@ def lib():
                                                  c_void_p, c_void_p]),
         "dflash_quantize_fp8_rows": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
         "dflash_set_lm_head_fp8": (c_int32, [H, c_void_p, c_void_p]),
+        "dflash_quantize_mxfp4_rows": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
+        "dflash_set_lm_head_mxfp4": (c_int32, [H, c_void_p, c_void_p]),
         "dflash_set_mlp_fp8": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_set_attn_fp8": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_set_inject_fp8": (c_int32, [H, c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -107,6 +109,7 @@ EXPORTED = ("dflash_config_check", "dflash_kv_cache_bytes", "dflash_kv_cache_lay
             "dflash_create", "dflash_destroy", "dflash_reset_seqs", "dflash_inject_kv", "dflash_draft_block",
             "dflash_draft_block_static", "dflash_select_path", "dflash_select_sample", "dflash_verify_rejection", "dflash_verify_greedy",
             "dflash_synth_target_argmax", "dflash_quantize_fp8_rows", "dflash_set_lm_head_fp8", "dflash_set_mlp_fp8",
+            "dflash_quantize_mxfp4_rows", "dflash_set_lm_head_mxfp4",
             "dflash_set_attn_fp8", "dflash_set_inject_fp8", "dflash_timing_enable",
             "dflash_timing_read", "dflash_get_device_error", "dflash_status_string", "dflash_last_error")
 
@@ -170,6 +173,13 @@ def dflash_verify_rejection(n_seq, block_size, vocab, draft_ids, q_path, topk_id
         ptr(u_accept), ptr(u_resample), ptr(n_accepted), ptr(n_commit), ptr(committed), ptr(next_anchor), stream))
 
 
+def dflash_quantize_mxfp4_rows(src, codes, scales, stream=None):
+    """MXFP4 codes [rows][cols/2] (uint8) and block scale bytes [rows][cols/32] (uint8) of a bf16 matrix."""
+    rows, cols = src.shape
+    check("dflash_quantize_mxfp4_rows", lib().dflash_quantize_mxfp4_rows(ptr(src), rows, cols, ptr(codes), ptr(scales),
+                                                                         stream))
+
+
 def dflash_synth_target_argmax(n_seq, block_size, vocab, draft_ids, match_prob, seed, counter, target_argmax,
                                stream=None):
     check("dflash_synth_target_argmax", lib().dflash_synth_target_argmax(
@@ -230,6 +240,12 @@ class Drafter:
         """Use E4M3 lm_head codes [V][d] with their row scales [V] (None, None: the bf16 lm_head)."""
         self._lm_fp8 = (codes, row_scales)   # keep alive
         check("dflash_set_lm_head_fp8", lib().dflash_set_lm_head_fp8(self.h, ptr(codes), ptr(row_scales)))
+
+    def dflash_set_lm_head_mxfp4(self, codes, scales):
+        """Use MXFP4 codes [vocab][hidden/2] with block scale bytes [vocab][hidden/32] for the lm_head
+        (None, None: back to bf16)."""
+        self._lm_fp4 = (codes, scales)   # keep alive
+        check("dflash_set_lm_head_mxfp4", lib().dflash_set_lm_head_mxfp4(self.h, ptr(codes), ptr(scales)))
 
     def dflash_set_mlp_fp8(self, layer, gate_up_codes, gate_up_scales, down_codes, down_scales):
         """Use E4M3 codes for layer's MLP: stacked [gate; up] [2 ffn][d] and down [d][ffn], with row

@@ -68,6 +68,8 @@ struct Handle {
   const void* g_WH;
   const unsigned char* lm_fp8;       // E4M3 lm_head codes [V][d] (NULL: the bf16 lm_head)
   const float* lm_fp8_scale;         // [V] per-row power-of-two scales
+  const unsigned char* lm_fp4;       // MXFP4 lm_head codes [V][d/2] (NULL: not in use)
+  const unsigned char* lm_fp4_scale; // [V][d/32] block scale bytes
   struct Fp8Mlp {                    // per layer: E4M3 [gate; up] [2 ffn][d] and down [d][ffn] codes
     const unsigned char *gu, *dn;    // with their row scales (NULL: the bf16 matrices)
     const float *gu_s, *dn_s;
@@ -321,9 +323,9 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
                        gemm_plan(true, GEMM_PARTIAL, M, d, c->n_heads * c->head_dim).kind != 3))
     return fail(DFLASH_E_UNSUPPORTED, "FP8 attention projections take at most 16 draft rows (n_seq * block_size = %d)",
                 M);
-  if (H->lm_fp8 && gemm_plan(true, GEMM_TOPK, M, c->vocab, d).kind != 4)
-    return fail(DFLASH_E_UNSUPPORTED, "the FP8 lm_head takes at most 16 draft rows (n_seq * block_size = %d) and a "
-                "hidden size that is a multiple of 512 up to 2048", M);
+  if ((H->lm_fp8 || H->lm_fp4) && gemm_plan(true, GEMM_TOPK, M, c->vocab, d).kind != 4)
+    return fail(DFLASH_E_UNSUPPORTED, "the FP8 / MXFP4 lm_head takes at most 16 draft rows (n_seq * block_size = %d) "
+                "and a hidden size that is a multiple of 512 up to 2048", M);
   const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
   float* part = wsp<float>(ws, W.part);
   SeqCtx* ctx = wsp<SeqCtx>(ws, W.ctx);
@@ -602,7 +604,12 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
     gl.logits = logits;
     gl.counter = counters;
     GemmPlan pl = gemm_plan(b, GEMM_TOPK, M, c->vocab, d);
-    if (H->lm_fp8) {
+    if (H->lm_fp4) {
+      // MXFP4 lm_head: only the independent-wave kernel (<= 16 rows) takes it (checked up front)
+      gl.seg[0] = H->lm_fp4;
+      gl.ldb = d / 2;                 // bytes per weight row
+      gl.blk_scale = H->lm_fp4_scale;
+    } else if (H->lm_fp8) {
       // FP8 lm_head: only the independent-wave kernel (<= 16 rows) takes it (checked up front)
       gl.seg[0] = H->lm_fp8;
       gl.ldb = d;                     // bytes per weight row
@@ -980,6 +987,26 @@ dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t* codes, con
   if (codes && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "the FP8 lm_head is for bf16 drafters");
   H->lm_fp8 = codes;
   H->lm_fp8_scale = row_scales;
+  if (codes) H->lm_fp4 = H->lm_fp4_scale = nullptr;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_quantize_mxfp4_rows(const void* src, int32_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                                         void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32) return fail(DFLASH_E_INVALID, "rows >= 0 and cols a positive multiple of 32 required");
+  if (rows > 0 && (!src || !codes || !scales)) return fail(DFLASH_E_INVALID, "NULL src, codes or scales");
+  HIP_TRY(launch_quantize_mxfp4_rows(src, rows, cols, codes, scales, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_set_lm_head_mxfp4(dflash_handle* h, const uint8_t* codes, const uint8_t* scales) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  if (!codes != !scales) return fail(DFLASH_E_INVALID, "codes and scales must both be set or both be NULL");
+  if (codes && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "the MXFP4 lm_head is for bf16 drafters");
+  H->lm_fp4 = codes;
+  H->lm_fp4_scale = scales;
+  if (codes) H->lm_fp8 = nullptr, H->lm_fp8_scale = nullptr;
   return DFLASH_OK;
 }
 

@@ -639,12 +639,56 @@ __device__ __forceinline__ void lw_mma8(const LwBatch8& x, const bf16 (*sa)[LW_L
   }
 }
 
+// MXFP4 weights (blk_scale set): codes [N][K/2] bytes, element 2j in the low nibble of byte j,
+// and one scale byte E per 32 weights of a row ([N][K/32]), the block's weights being
+// code value * 2^(E - 127).  A batch is LW_CH4 chunks of 128 k: lane (li, kg) loads the 16 code
+// bytes of k = 32 kg .. 32 kg + 31 of each chunk (one block) and the 16 scale bytes of the batch's
+// blocks.  Word m of a lane's 16 bytes becomes eight bf16 weights (v_cvt_scalef32_pk_bf16_fp4,
+// exact: an E2M1 value times a power of two fits bf16) and feeds the MFMA over k = 32 kg + 8 m ..
+// + 7 of the chunk; the activations are read from LDS in that k order, so the sum is unchanged.
+constexpr int LW_CH4 = 4;
+struct LwBatch4 {
+  u32x4 q[LW_CH4];
+  u32x4 sc;                         // scale bytes of the batch's 16 blocks (chunk c, lane group kg: byte 4c + kg)
+};
+
+__device__ __forceinline__ void lw_load4(LwBatch4& x, const unsigned char* row, const unsigned char* srow, int k0,
+                                         int kg) {
+#pragma unroll
+  for (int c = 0; c < LW_CH4; ++c) x.q[c] = *reinterpret_cast<const u32x4*>(row + (k0 + 128 * c) / 2 + 16 * kg);
+  x.sc = *reinterpret_cast<const u32x4*>(srow + k0 / 32);
+}
+
+__device__ __forceinline__ bf16x8 fp4x8_bf16(unsigned w, float s) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+  return as_bf16x8(o);
+}
+
+__device__ __forceinline__ void lw_mma4(const LwBatch4& x, const bf16 (*sa)[LW_LD], int k0, int li, int kg,
+                                        f32x4& acc0, f32x4& acc1) {
+#pragma unroll
+  for (int c = 0; c < LW_CH4; ++c) {
+    const float s = __uint_as_float(((x.sc[c] >> (8 * kg)) & 0xFFu) << 23);   // 2^(E - 127), E >= 1
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sa[li][k0 + 128 * c + 32 * kg + 8 * m]);
+      const bf16x8 w = fp4x8_bf16(x.q[c][m], s);
+      if (m & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc1, 0, 0, 0);
+      else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc0, 0, 0, 0);
+    }
+  }
+}
+
 // LOGITS: the full logits are written too (a global store in the fragment loop; kept out of
 // the instantiation without them, where it would make the compiler's load waits coarser)
-template <bool LOGITS, bool FP8 = false>
+template <bool LOGITS, bool FP8 = false, bool FP4 = false>
 __global__ __launch_bounds__(LW_W * 64, 2) void lmhead_topk_wave(GemmParams p) {
-  using Batch = typename std::conditional<FP8, LwBatch8, LwBatch>::type;
-  constexpr int CH = FP8 ? LW_CH8 : LW_CH;
+  using Batch = typename std::conditional<FP4, LwBatch4, typename std::conditional<FP8, LwBatch8, LwBatch>::type>::type;
+  constexpr int KPB = FP4 ? 128 * LW_CH4 : 64 * (FP8 ? LW_CH8 : LW_CH);   // k per batch
   __shared__ __align__(16) unsigned char lw_smem[LW_SMEM];
   bf16 (*sa)[LW_LD] = reinterpret_cast<bf16 (*)[LW_LD]>(lw_smem);                         // [row][k]
   float (*fb)[16][17] = reinterpret_cast<float (*)[16][17]>(lw_smem + 16 * LW_LD * 2);    // [wave][row][col]
@@ -677,7 +721,7 @@ __global__ __launch_bounds__(LW_W * 64, 2) void lmhead_topk_wave(GemmParams p) {
   }
   __syncthreads();
   const int nfrag = (p.N + 15) / 16;
-  const int ncb = K / (64 * CH);                  // batches per fragment
+  const int ncb = K / KPB;                        // batches per fragment
   const int TW = gridDim.x * LW_W;
   const int my_row = lane >> 2, my_sub = lane & 3;   // epilogue: lane handles row my_row, cols 4 sub..+3
   const bool row_live = my_row < Mv && (my_row % p.block) != 0;
@@ -715,20 +759,25 @@ __global__ __launch_bounds__(LW_W * 64, 2) void lmhead_topk_wave(GemmParams p) {
   const int T = ((f0 < nfrag ? (nfrag - 1 - f0) / TW + 1 : 0) * ncb + LW_NB - 1) / LW_NB * LW_NB;
   int lf = f0, lcb = 0;
   auto issue = [&](Batch& b) {
-    if constexpr (FP8)
+    if constexpr (FP4)
+      lw_load4(b, reinterpret_cast<const unsigned char*>(p.seg[0]) + (size_t)rown(lf) * p.ldb,
+               p.blk_scale + (size_t)rown(lf) * (K / 32), lcb * KPB, kg);
+    else if constexpr (FP8)
       lw_load8(b, reinterpret_cast<const unsigned char*>(p.seg[0]) + (size_t)rown(lf) * p.ldb, p.row_scale + rown(lf),
-               lcb * 64 * CH, kg);
+               lcb * KPB, kg);
     else
-      lw_load(b, rowp(lf), lcb * 64 * CH, kg);
+      lw_load(b, rowp(lf), lcb * KPB, kg);
     if (++lcb == ncb) { lcb = 0; lf += TW; }
   };
   int cf = f0, ccb = 0;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   auto step = [&](const Batch& b) {
-    if constexpr (FP8)
-      lw_mma8(b, sa, ccb * 64 * CH, li, kg, acc0, acc1);
+    if constexpr (FP4)
+      lw_mma4(b, sa, ccb * KPB, li, kg, acc0, acc1);
+    else if constexpr (FP8)
+      lw_mma8(b, sa, ccb * KPB, li, kg, acc0, acc1);
     else
-      lw_mma(b, sa, ccb * 64 * CH, li, kg, acc0, acc1);
+      lw_mma(b, sa, ccb * KPB, li, kg, acc0, acc1);
     if (++ccb == ncb) {
       epilogue(cf, acc0 + acc1);
       acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -963,7 +1012,10 @@ hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hi
   }
   if (pl.kind == 4) {
     if (p.seg_rows < p.N) return hipErrorInvalidValue;   // one weight segment
-    if (p.row_scale) {
+    if (p.blk_scale) {
+      if (p.logits) hipLaunchKernelGGL((lmhead_topk_wave<true, false, true>), pl.grid, dim3(LW_W * 64), 0, st, p);
+      else hipLaunchKernelGGL((lmhead_topk_wave<false, false, true>), pl.grid, dim3(LW_W * 64), 0, st, p);
+    } else if (p.row_scale) {
       if (p.logits) hipLaunchKernelGGL((lmhead_topk_wave<true, true>), pl.grid, dim3(LW_W * 64), 0, st, p);
       else hipLaunchKernelGGL((lmhead_topk_wave<false, true>), pl.grid, dim3(LW_W * 64), 0, st, p);
     } else {

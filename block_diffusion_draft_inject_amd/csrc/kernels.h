@@ -40,6 +40,8 @@ struct GemmParams {
   const float* row_scale; // FP8 lm_head (<= 16 rows): the weights are E4M3 codes [N][ldb bytes],
                           // weight row n stands for code * row_scale[n]
   int* counter;           // TOPK skinny (17..64 rows): per-row-tile fragment counters, zero before the launch
+  const unsigned char* blk_scale;  // MXFP4 lm_head (<= 16 rows): the weights are E2M1 codes [N][K/2 bytes], with
+                                   // scale byte E [N][K/32] per 32 weights standing for 2^(E - 127)
 };
 
 struct GemmPlan {

@@ -261,5 +261,7 @@ hipError_t launch_verify_rejection(const RejectArgs& a, hipStream_t st);
 hipError_t launch_synth(const SynthArgs& a, hipStream_t st);
 hipError_t launch_quantize_fp8_rows(const void* src, int rows, int cols, unsigned char* codes, float* scales,
                                     hipStream_t st);
+hipError_t launch_quantize_mxfp4_rows(const void* src, int rows, int cols, unsigned char* codes, unsigned char* scales,
+                                      hipStream_t st);
 
 }  // namespace dfl

@@ -1137,6 +1137,65 @@ __global__ __launch_bounds__(256) void quantize_fp8_rows_kernel(const bf16* src,
   }
 }
 
+// MXFP4 (OCP Microscaling): blocks of 32 consecutive weights of a row share a scale 2^s, stored as
+// the byte s + 127, with s = floor(log2 a) - 2 for the block's largest magnitude a (a in [4, 8) 2^s);
+// each weight is the 4-bit E2M1 code of the magnitude nearest to |w| / 2^s among 0, 0.5, 1, 1.5, 2,
+// 3, 4, 6 (ties to the even code, beyond 6 saturating), with the sign of w as bit 3.  A block with
+// a < 2^-64 is stored as signed zeros with scale byte 127.  Two codes per byte, element 2j in the
+// low nibble.  One thread per block; |w| / 2^s is exact (a bf16 value times a power of two).
+__device__ __forceinline__ unsigned e2m1_code(float w, int s) {
+  const float a = fabsf(ldexpf(w, -s));
+  // code = number of midpoints below a; at a midpoint the even neighbour (the lower one for
+  // 0.25, 1.25, 2.5, 5; the upper one for 0.75, 1.75, 3.5)
+  const unsigned c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.f);
+  return c | ((__float_as_uint(w) >> 31) << 3);
+}
+
+__global__ __launch_bounds__(256) void quantize_mxfp4_rows_kernel(const bf16* src, int rows, int cols,
+                                                                  unsigned char* codes, unsigned char* scales) {
+  const int nb = cols / 32;
+  const long blk = (long)blockIdx.x * 256 + threadIdx.x;
+  if (blk >= (long)rows * nb) return;
+  const long r = blk / nb;
+  const int b = (int)(blk % nb);
+  const u32x4* p = reinterpret_cast<const u32x4*>(src + r * cols + (long)b * 32);
+  u32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = p[i];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(v[i][j] << 16)), fabsf(__uint_as_float(v[i][j] & 0xffff0000u))));
+  const bool zero = !(amax >= 0x1p-64f);
+  const int s = zero ? 0 : (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 2;   // floor(log2 a) - 2
+  scales[blk] = (unsigned char)(s + 127);
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {   // word i: elements 8i .. 8i + 7 of the block
+    unsigned w = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float w0 = __uint_as_float(v[i][j] << 16), w1 = __uint_as_float(v[i][j] & 0xffff0000u);
+      w |= (e2m1_code(w0, s) | (e2m1_code(w1, s) << 4)) << (8 * j);
+    }
+    o[i] = w;
+  }
+  // 32 codes = 16 bytes: word i of o covers bytes 4i .. 4i + 3, i.e. elements 8i .. 8i + 7
+  *reinterpret_cast<uint2*>(codes + r * (cols / 2) + (long)b * 16) = make_uint2(o[0], o[1]);
+  *reinterpret_cast<uint2*>(codes + r * (cols / 2) + (long)b * 16 + 8) = make_uint2(o[2], o[3]);
+}
+
+hipError_t launch_quantize_mxfp4_rows(const void* src, int rows, int cols, unsigned char* codes, unsigned char* scales,
+                                      hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const long n = (long)rows * (cols / 32);
+  hipLaunchKernelGGL(quantize_mxfp4_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const bf16*>(src), rows, cols, codes, scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_fp8_rows(const void* src, int rows, int cols, unsigned char* codes, float* scales,
                                     hipStream_t st) {
   if (rows <= 0) return hipSuccess;

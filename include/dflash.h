@@ -294,7 +294,23 @@ DFLASH_API dflash_status dflash_verify_greedy(int32_t n_seq, int32_t block_size,
  * then returns DFLASH_E_UNSUPPORTED. */
 DFLASH_API dflash_status dflash_quantize_fp8_rows(const void* src, int32_t rows, int32_t cols, uint8_t* codes,
                                                   float* row_scales, void* stream);
-DFLASH_API dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t* codes, const float* row_scales);
+DFLASH_API dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t* codes, const float* row_scales);   /* clears an MXFP4 lm_head */
+/* MXFP4 weight-only lm_head (4-bit weights, as in the pages' 4-bit drafts on one backend, "z-lab/dflash"
+ * README mirror, section "MLX (Apple Silicon)"; the format is the OCP Microscaling MXFP4 encoding).
+ * dflash_quantize_mxfp4_rows writes, for a bf16 matrix src [rows][cols] (device, 16-byte aligned,
+ * cols a positive multiple of 32), per block of 32 consecutive weights of a row one scale byte
+ * E = s + 127 (scales [rows][cols/32], device) with s = floor(log2 a) - 2 for the block's largest
+ * magnitude a, and per weight the 4-bit E2M1 code of the magnitude nearest to |w| / 2^s among
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 (ties to the even code, larger magnitudes saturating to 6) with the
+ * sign of w as bit 3 (codes [rows][cols/2], device, 8-byte aligned: weight 2j in the low nibble of
+ * byte j).  A block with a < 2^-64 is stored as signed zeros with E = 127.  Asynchronous on stream;
+ * no allocation.  dflash_set_lm_head_mxfp4 makes a handle's dflash_draft_block read the shared
+ * lm_head as those codes, each standing for value(code) * 2^(E - 127) (exact in bf16), instead of the
+ * bf16 matrix (and instead of an FP8 lm_head, which it clears); NULL for both reverts to bf16.
+ * Borrowed like the weights.  Batch-1 kernel only, with the same limits as the FP8 lm_head. */
+DFLASH_API dflash_status dflash_quantize_mxfp4_rows(const void* src, int32_t rows, int32_t cols, uint8_t* codes,
+                                                    uint8_t* scales, void* stream);
+DFLASH_API dflash_status dflash_set_lm_head_mxfp4(dflash_handle* h, const uint8_t* codes, const uint8_t* scales);
 /* The same for one layer's MLP: gate_up_codes [2*ffn][d] are the codes of the stacked matrix
  * [W_gate; W_up] (gate rows first), down_codes [d][ffn] those of W_down, each with its row scales
  * (as written by dflash_quantize_fp8_rows); all four NULL reverts the layer to its bf16 matrices.

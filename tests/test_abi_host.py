@@ -111,6 +111,12 @@ def test_create_validates_before_any_device_call():
     assert L.dflash_synth_target_argmax(2000, 8, 100, fake, 0.7, 0, fake, fake, None) == -2
     assert L.dflash_synth_target_argmax(2, 8, 100, fake, 1.5, 0, fake, fake, None) == -1
     assert L.dflash_timing_enable(h, -1) == -1
+    assert L.dflash_quantize_mxfp4_rows(fake, 4, 48, fake, fake, None) == -1            # cols not a multiple of 32
+    assert L.dflash_quantize_mxfp4_rows(None, 4, 64, fake, fake, None) == -1
+    assert L.dflash_quantize_mxfp4_rows(None, 0, 64, None, None, None) == 0             # nothing to do
+    assert L.dflash_set_lm_head_mxfp4(h, fake, None) == -1
+    assert L.dflash_set_lm_head_mxfp4(h, fake, fake) == -3                              # fp32 drafter
+    assert L.dflash_set_lm_head_mxfp4(h, None, None) == 0
     assert L.dflash_destroy(h) == 0
 
 

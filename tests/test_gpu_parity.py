@@ -393,6 +393,66 @@ def test_mid_bf16_fp8_lm_head(H):
     assert err <= H.LOGIT_TOL["bf16"]
 
 
+def _quantize_mxfp4_on_gpu(lm):
+    import torch
+    rows, cols = lm.shape
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
+    B.dflash_quantize_mxfp4_rows(lm, codes, scales)
+    torch.cuda.synchronize()
+    return codes, scales
+
+
+def test_mxfp4_quantizer_matches_oracle():
+    """MXFP4 codes and block scale bytes, bit-exact against the oracle: ordinary rows, rows spanning
+    many binades, an all-zero row, a row of -0, a row below the zero-block threshold, a row of exact
+    midpoints between E2M1 magnitudes (ties), a row of values that saturate, alternating signs."""
+    import torch
+    rng = np.random.default_rng(22)
+    W = rng.normal(0, 0.02, (200, 512))
+    W[:20] *= np.exp(rng.normal(0, 3, (20, 1)))
+    W[20] = 0.0
+    W[21] = -0.0
+    W[22] *= 1e-22
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    W[23] = np.resize(np.concatenate([mids, -mids]), 512) * 2.0 ** -9
+    W[23, ::32] = 4.0 * 2.0 ** -9                 # every block's exponent is -9: the midpoints stay ties
+    W[24] = np.resize([7.9, 6.5, -7.0, 6.0], 512) * 2.0 ** -4
+    W[25, ::2] = -W[25, ::2]
+    Wb = O.bf16_round(W)
+    dev = torch.tensor(Wb, dtype=torch.float32).to(torch.bfloat16).cuda()
+    codes, scales = _quantize_mxfp4_on_gpu(dev)
+    oc, osc = O.quantize_mxfp4_rows(Wb)
+    assert np.array_equal(scales.cpu().numpy(), osc)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.all(oc[20] == 0) and np.all(oc[21] == 0x88)
+
+
+def test_mid_bf16_mxfp4_lm_head(H):
+    """Batch 1, K=16 with the MXFP4 lm_head: codes as the oracle's, logits and top-16 against the
+    oracle run with the dequantised lm_head, top-16 with and without full logits; a call with more
+    than 16 rows is refused; setting the FP8 lm_head replaces it; NULL restores the bf16 lm_head."""
+    case = H.Case(MID, max_seqs=2, max_batch=2, max_inject_rows=64)
+    _prefill(case, [1], [(0, 50)])
+    codes, scales = _quantize_mxfp4_on_gpu(case.dev_w["lm_head"])
+    oc, osc = O.quantize_mxfp4_rows(case.W64["lm_head"])
+    assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), osc)
+    case.d.dflash_set_lm_head_mxfp4(codes, scales)
+    bf16_lm = case.W64["lm_head"]
+    case.W64["lm_head"] = O.dequantize_mxfp4_rows(oc, osc)
+    try:
+        res = _check(H, case, [1], [123], mode_names=("viterbi",))
+        _same_topk_without_logits(case, [1], [123], res)
+    finally:
+        case.W64["lm_head"] = bf16_lm
+    with pytest.raises(B.DflashError):
+        case.draft([1, 0], [123, 5])               # 32 rows
+    case.d.dflash_set_lm_head_mxfp4(None, None)
+    res = case.draft([1], [123], logits=True)
+    err, _ = H.check_draft(case, [1], [123], res)
+    assert err <= H.LOGIT_TOL["bf16"]
+
+
 def _fp8_stacked(case, W, mats, names_rows):
     """GPU codes of the row-stacked device matrices `mats`; each (layer or None, name, rows) block
     checked against the oracle's codes of that matrix and replaced in W by its dequantised form."""

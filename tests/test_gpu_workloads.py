@@ -322,6 +322,38 @@ def test_b1_k16_fp8_lm_head(H, big):
     assert run.d.dflash_get_device_error() == 0
 
 
+def test_b1_k16_mxfp4_lm_head(H, big):
+    """The b1_k16 drafter with the MXFP4 lm_head (151936 x 2048 E2M1 codes, a scale byte per 32):
+    codes and scales as the oracle's, then a full-window draft against the oracle run with the
+    dequantised lm_head."""
+    import torch
+    cfg = synth.WORKLOADS["b1_k16"]
+    lm = big["dev"]["lm_head"]
+    rows, cols = lm.shape
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
+    B.dflash_quantize_mxfp4_rows(lm, codes, scales)
+    torch.cuda.synchronize()
+    oc, osc = O.quantize_mxfp4_rows(big["W64"]["lm_head"])
+    assert np.array_equal(scales.cpu().numpy(), osc)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    run = Run(H, big, cfg, max_seqs=1, max_batch=1, max_inject_rows=1024, sampled=[0])
+    run.d.dflash_set_lm_head_mxfp4(codes, scales)
+    bf16_lm = big["W64"]["lm_head"]
+    big["W64"]["lm_head"] = O.dequantize_mxfp4_rows(oc, osc)
+    del oc
+    try:
+        run.d.dflash_reset_seqs(run.t(np.zeros(1, dtype=np.int32)))
+        run.inject([0], [_window(cfg.context[0], cfg.window)])
+        anchors = synth.anchors(cfg).tolist()
+        res = run.draft([0], anchors)
+        run.own_logit_topk(res)
+        run.compare_sampled([0], anchors, res)
+    finally:
+        big["W64"]["lm_head"] = bf16_lm
+    assert run.d.dflash_get_device_error() == 0
+
+
 def test_b1_k16_fp8_mlp(H, big):
     """The b1_k16 drafter with FP8 MLP weights in all 5 layers (stacked gate/up 12288 x 2048,
     down 2048 x 6144): codes as the oracle's, then a full-window draft against the oracle run
