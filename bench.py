@@ -320,7 +320,7 @@ def algorithmic(cfg, tau_mean, n_ctx):
 
 
 def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=False, fp8_mlp=False,
-                 fp8_attn_inject=False, mxfp4_lm_head=False):
+                 fp8_attn_inject=False, mxfp4_lm_head=False, mxfp4_mlp=False):
     """Times `steps` steps twice on one stream: (1) replays of a HIP graph holding
     `graph_steps` steps (the headline rate; no events inside the graph), (2) the same number of
     steps launched eagerly, each lm_head launch bracketed by HIP events on that stream (the
@@ -348,6 +348,18 @@ def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=
                 cyc.Bd.dflash_quantize_fp8_rows(mat, out[-2], out[-1])
             cyc.d.dflash_set_mlp_fp8(l, *out)
             cyc.mlp8.append(out)
+        torch.cuda.synchronize()
+    if mxfp4_mlp:     # MXFP4 codes + block scale bytes of every layer's stacked [gate; up] and down matrices
+        cyc.mlp4 = []
+        for l, lw in enumerate(cyc.w["layers"]):
+            out = []
+            for mat in (torch.cat([lw["w_gate"], lw["w_up"]]).contiguous(), lw["w_down"]):
+                r, c = mat.shape
+                out += [torch.empty((r, c // 2), dtype=torch.uint8, device="cuda"),
+                        torch.empty((r, c // 32), dtype=torch.uint8, device="cuda")]
+                cyc.Bd.dflash_quantize_mxfp4_rows(mat, out[-2], out[-1])
+            cyc.d.dflash_set_mlp_mxfp4(l, *out)
+            cyc.mlp4.append(out)
         torch.cuda.synchronize()
 
     def codes_of(mats):
@@ -763,6 +775,15 @@ def main():
                 "blocks_per_s": round(r12["blocks_per_s"], 1), "draft_tokens_per_s": round(r12["draft_tokens_per_s"], 1),
                 "ms_per_step": round(r12["ms_per_step"], 4)}
             del r12["cycle"]
+            torch.cuda.empty_cache()
+            r13 = run_workload(cfg, args.steps, args.warmup, torch, mxfp4_lm_head=True, mxfp4_mlp=True,
+                               fp8_attn_inject=True)
+            out["mxfp4_lm_head_mlp_fp8_rest"] = {
+                "workload": "b1_k16 with the lm_head and every layer's gate/up and down matrices as MXFP4, the "
+                            "attention projections and the injection as E4M3 codes (weight-only; activations bf16)",
+                "blocks_per_s": round(r13["blocks_per_s"], 1), "draft_tokens_per_s": round(r13["draft_tokens_per_s"], 1),
+                "ms_per_step": round(r13["ms_per_step"], 4)}
+            del r13["cycle"]
     batched = [("b32", "b32_k8_conv", args.no_b32,
                 "b32_k8_conv: same drafter, K=8, batch 32, contexts U[512,4096] (window 1024), two-tap conv, "
                 "0.7 match rule"),

@@ -89,6 +89,7 @@ def lib():
         "dflash_quantize_mxfp4_rows": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
         "dflash_set_lm_head_mxfp4": (c_int32, [H, c_void_p, c_void_p]),
         "dflash_set_mlp_fp8": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "dflash_set_mlp_mxfp4": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_set_attn_fp8": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_set_inject_fp8": (c_int32, [H, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_timing_enable": (c_int32, [H, c_int32]),
@@ -109,7 +110,7 @@ EXPORTED = ("dflash_config_check", "dflash_kv_cache_bytes", "dflash_kv_cache_lay
             "dflash_create", "dflash_destroy", "dflash_reset_seqs", "dflash_inject_kv", "dflash_draft_block",
             "dflash_draft_block_static", "dflash_select_path", "dflash_select_sample", "dflash_verify_rejection", "dflash_verify_greedy",
             "dflash_synth_target_argmax", "dflash_quantize_fp8_rows", "dflash_set_lm_head_fp8", "dflash_set_mlp_fp8",
-            "dflash_quantize_mxfp4_rows", "dflash_set_lm_head_mxfp4",
+            "dflash_quantize_mxfp4_rows", "dflash_set_lm_head_mxfp4", "dflash_set_mlp_mxfp4",
             "dflash_set_attn_fp8", "dflash_set_inject_fp8", "dflash_timing_enable",
             "dflash_timing_read", "dflash_get_device_error", "dflash_status_string", "dflash_last_error")
 
@@ -255,6 +256,16 @@ class Drafter:
         self._mlp_fp8[layer] = (gate_up_codes, gate_up_scales, down_codes, down_scales)   # keep alive
         check("dflash_set_mlp_fp8", lib().dflash_set_mlp_fp8(self.h, layer, ptr(gate_up_codes), ptr(gate_up_scales),
                                                              ptr(down_codes), ptr(down_scales)))
+
+    def dflash_set_mlp_mxfp4(self, layer, gate_up_codes, gate_up_scales, down_codes, down_scales):
+        """Use MXFP4 codes for layer's MLP: stacked [gate; up] [2 ffn][d/2] and down [d][ffn/2], with
+        block scale bytes [rows][cols/32] (all None: the bf16 matrices)."""
+        if not hasattr(self, "_mlp_fp8"):
+            self._mlp_fp8 = {}
+        self._mlp_fp8[layer] = (gate_up_codes, gate_up_scales, down_codes, down_scales)   # keep alive
+        check("dflash_set_mlp_mxfp4", lib().dflash_set_mlp_mxfp4(self.h, layer, ptr(gate_up_codes),
+                                                                 ptr(gate_up_scales), ptr(down_codes),
+                                                                 ptr(down_scales)))
 
     def dflash_set_attn_fp8(self, layer, qkv_codes, qkv_scales, o_codes, o_scales):
         """Use E4M3 codes for layer's stacked [wq; wk; wv] and wo (all None: bf16)."""

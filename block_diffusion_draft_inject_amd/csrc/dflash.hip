@@ -70,11 +70,12 @@ struct Handle {
   const float* lm_fp8_scale;         // [V] per-row power-of-two scales
   const unsigned char* lm_fp4;       // MXFP4 lm_head codes [V][d/2] (NULL: not in use)
   const unsigned char* lm_fp4_scale; // [V][d/32] block scale bytes
-  struct Fp8Mlp {                    // per layer: E4M3 [gate; up] [2 ffn][d] and down [d][ffn] codes
-    const unsigned char *gu, *dn;    // with their row scales (NULL: the bf16 matrices)
-    const float *gu_s, *dn_s;
+  struct QuantMlp {                  // per layer: [gate; up] [2 ffn][d] and down [d][ffn] as E4M3 codes
+    const unsigned char *gu, *dn;    // with row scales, or MXFP4 codes (half the bytes) with block
+    const float *gu_s, *dn_s;        // scale bytes [rows][cols / 32] (NULL gu: the bf16 matrices)
+    const unsigned char *gu_b, *dn_b;
   };
-  std::vector<Fp8Mlp> mlp_fp8;
+  std::vector<QuantMlp> mlp_q;
   struct Fp8Attn {                   // per layer: E4M3 [wq; wk; wv] [qw + 2 kvw][d] and wo [d][qw] codes
     const unsigned char *qkv, *o;
     const float *qkv_s, *o_s;
@@ -310,12 +311,12 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
   const dflash_config* c = &H->cfg;
   const bool b = bf(c);
   const int K = c->block_size, d = c->hidden, M = n_seq * K;
-  bool any_mlp_fp8 = false;
-  for (const auto& m : H->mlp_fp8) any_mlp_fp8 |= m.gu != nullptr;
-  if (any_mlp_fp8 && (gemm_plan(true, GEMM_SWIGLU, M, 2 * c->ffn, d).kind != 3 ||
-                      gemm_plan(true, GEMM_PARTIAL, M, d, c->ffn).kind != 3))
-    return fail(DFLASH_E_UNSUPPORTED, "FP8 MLP weights take at most 16 draft rows (n_seq * block_size = %d) and a "
-                "hidden size of at most 2048", M);
+  bool any_mlp_q = false;
+  for (const auto& m : H->mlp_q) any_mlp_q |= m.gu != nullptr;
+  if (any_mlp_q && (gemm_plan(true, GEMM_SWIGLU, M, 2 * c->ffn, d).kind != 3 ||
+                    gemm_plan(true, GEMM_PARTIAL, M, d, c->ffn).kind != 3))
+    return fail(DFLASH_E_UNSUPPORTED, "FP8 / MXFP4 MLP weights take at most 16 draft rows (n_seq * block_size = %d) "
+                "and a hidden size of at most 2048", M);
   bool any_attn_fp8 = false;
   for (const auto& a8 : H->attn_fp8) any_attn_fp8 |= a8.qkv != nullptr;
   if (any_attn_fp8 && (gemm_plan(true, GEMM_PARTIAL, M, c->n_heads * c->head_dim + 2 * c->n_kv_heads * c->head_dim,
@@ -518,13 +519,14 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
     gg.out = act_s;
     gg.out_plane = Mmax * c->ffn;
     gg.part = part;
-    const Handle::Fp8Mlp* m8 = (size_t)l < H->mlp_fp8.size() && H->mlp_fp8[l].gu ? &H->mlp_fp8[l] : nullptr;
-    if (m8) {   // one stacked [gate; up] segment of E4M3 codes (checked up front: the stream kernel)
-      gg.seg[0] = m8->gu;
+    const Handle::QuantMlp* mq = (size_t)l < H->mlp_q.size() && H->mlp_q[l].gu ? &H->mlp_q[l] : nullptr;
+    if (mq) {   // one stacked [gate; up] segment of codes (checked up front: the stream kernel)
+      gg.seg[0] = mq->gu;
       gg.seg[1] = nullptr;
       gg.seg_rows = 2 * c->ffn;
-      gg.ldb = d;
-      gg.row_scale = m8->gu_s;
+      gg.ldb = mq->gu_b ? d / 2 : d;
+      gg.row_scale = mq->gu_s;
+      gg.blk_scale = mq->gu_b;
     }
     if (b && M <= 64) {
       GemmPlan pg = gemm_plan(b, GEMM_SWIGLU, M, 2 * c->ffn, d);
@@ -542,10 +544,11 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
     gd.seg[0] = LW(H, l, DFLASH_L_W_DOWN);
     gd.seg_rows = d;
     gd.part = part;
-    if (m8) {
-      gd.seg[0] = m8->dn;
-      gd.ldb = c->ffn;
-      gd.row_scale = m8->dn_s;
+    if (mq) {
+      gd.seg[0] = mq->dn;
+      gd.ldb = mq->dn_b ? c->ffn / 2 : c->ffn;
+      gd.row_scale = mq->dn_s;
+      gd.blk_scale = mq->dn_b;
     }
     GemmPlan pd = gemm_plan(b, GEMM_PARTIAL, M, d, c->ffn);
     HIP_TRY(gemm_launch(b, pd, GEMM_PARTIAL, gd, st));
@@ -1018,8 +1021,24 @@ dflash_status dflash_set_mlp_fp8(dflash_handle* h, int32_t layer, const uint8_t*
   const int set = !!gate_up_codes + !!gate_up_scales + !!down_codes + !!down_scales;
   if (set != 0 && set != 4) return fail(DFLASH_E_INVALID, "all four pointers set, or all NULL");
   if (set && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "FP8 weights are for bf16 drafters");
-  if (H->mlp_fp8.size() < (size_t)H->cfg.n_layers) H->mlp_fp8.resize(H->cfg.n_layers, Handle::Fp8Mlp{});
-  H->mlp_fp8[layer] = Handle::Fp8Mlp{gate_up_codes, down_codes, gate_up_scales, down_scales};
+  if (H->mlp_q.size() < (size_t)H->cfg.n_layers) H->mlp_q.resize(H->cfg.n_layers, Handle::QuantMlp{});
+  H->mlp_q[layer] = Handle::QuantMlp{gate_up_codes, down_codes, gate_up_scales, down_scales, nullptr, nullptr};
+  return DFLASH_OK;
+}
+
+dflash_status dflash_set_mlp_mxfp4(dflash_handle* h, int32_t layer, const uint8_t* gate_up_codes,
+                                   const uint8_t* gate_up_scales, const uint8_t* down_codes,
+                                   const uint8_t* down_scales) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  if (layer < 0 || layer >= H->cfg.n_layers) return fail(DFLASH_E_INVALID, "layer %d outside [0, n_layers)", layer);
+  const int set = !!gate_up_codes + !!gate_up_scales + !!down_codes + !!down_scales;
+  if (set != 0 && set != 4) return fail(DFLASH_E_INVALID, "all four pointers set, or all NULL");
+  if (set && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "MXFP4 weights are for bf16 drafters");
+  if (set && (H->cfg.hidden % 128 || H->cfg.ffn % 128))
+    return fail(DFLASH_E_UNSUPPORTED, "MXFP4 MLP weights need hidden and ffn sizes that are multiples of 128");
+  if (H->mlp_q.size() < (size_t)H->cfg.n_layers) H->mlp_q.resize(H->cfg.n_layers, Handle::QuantMlp{});
+  H->mlp_q[layer] = Handle::QuantMlp{gate_up_codes, down_codes, nullptr, nullptr, gate_up_scales, down_scales};
   return DFLASH_OK;
 }
 

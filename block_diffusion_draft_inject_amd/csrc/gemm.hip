@@ -39,6 +39,17 @@ __device__ __forceinline__ bf16x8 fp8x8_bf16(unsigned w0, unsigned w1, float s) 
   return as_bf16x8(o);
 }
 
+// MXFP4 weights (blk_scale set): one word of eight E2M1 codes (element 2j in the low nibble of
+// byte j) -> eight bf16 values code * s, s = 2^(E - 127) of the codes' block, exact
+__device__ __forceinline__ bf16x8 fp4x8_bf16(unsigned w, float s) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+  return as_bf16x8(o);
+}
+
 // ---------------------------------------------------------------------------------------
 // skinny: accumulate one wave tile of (16*MT rows) x (16*NF cols) over chunks
 // c = c0, c0 + cstep, ... < c1 (chunk = 64 k values).  Software-pipelined: the loads of the
@@ -310,6 +321,18 @@ struct StreamBuf8 {
   u32x4 q[SLC][NF];
   float s[NF];
 };
+// MXFP4 weights.  Slices of 2 or 4 chunks are read as 128-k super-chunks: lane (li, kg) loads 16
+// bytes, the 32 codes of block k = 32 kg .. 32 kg + 31 of its row, and that block's scale byte
+// (one load per row and 64 bytes per row per instruction, as for FP8).  A one-chunk slice keeps the
+// FP8 order: 8 bytes per lane, k = 16 kg .. 16 kg + 15, half a block.
+template <int SLC, int NF>
+struct StreamBuf4 {
+  static constexpr bool WIDE = SLC >= 2;
+  static constexpr int NC = WIDE ? SLC / 2 : SLC;
+  u32x4 q[NC][NF];   // WIDE: four words, else words 0 and 1
+  unsigned e[NC][NF];   // the block's scale byte, as loaded (turned into a float only at its use,
+                        // so that no wait for it lands between the loads of the ring)
+};
 
 // SWIGLU fragments interleave the two halves: lanes li < 8 take gate rows 8f .. 8f + 7, lanes
 // li >= 8 the matching up rows half + 8f .. (so the epilogue pairs lane li with lane li + 8).
@@ -366,6 +389,62 @@ __device__ __forceinline__ void stream_load8(StreamBuf8<SLC, NF>& x, const GemmP
   }
 }
 
+template <int SLC, int NF, bool GLU>
+__device__ __forceinline__ void stream_load4(StreamBuf4<SLC, NF>& x, const GemmParams& p, int ncols, int f, int kw,
+                                             int kg, int li) {
+#pragma unroll
+  for (int nf = 0; nf < NF; ++nf) {
+    int n;
+    if (GLU) {
+      const int g0 = f * 8, j = min(g0 + (li & 7), ncols - 1) - g0;
+      n = (li < 8 ? g0 : p.half + g0) + j;
+    } else {
+      n = min(f * 16 + li, ncols - 1) + nf * p.half;
+    }
+    const unsigned char* row = reinterpret_cast<const unsigned char*>(p.seg[0]) + (size_t)n * p.ldb;
+    const unsigned char* srow = p.blk_scale + (size_t)n * (p.K / 32);
+    if constexpr (StreamBuf4<SLC, NF>::WIDE) {
+#pragma unroll
+      for (int c = 0; c < SLC / 2; ++c) {
+        const int k = min(kw + c * 128, p.K - 128) + kg * 32;
+        x.q[c][nf] = *reinterpret_cast<const u32x4*>(row + k / 2);
+        x.e[c][nf] = srow[k / 32];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < SLC; ++c) {
+        const int k = min(kw + c * 64, p.K - 64) + kg * 16;
+        const uint2 w = *reinterpret_cast<const uint2*>(row + k / 2);
+        x.q[c][nf][0] = w.x;
+        x.q[c][nf][1] = w.y;
+        x.e[c][nf] = srow[k / 32];
+      }
+    }
+  }
+}
+
+template <int SLC, int NF>
+__device__ __forceinline__ void stream_mma4(const StreamBuf4<SLC, NF>& x, const u32x4 (&ah)[SLC][2],
+                                            const u32x4 (&al)[SLC][2], f32x4 (&acc)[NF]) {
+  // activation chunk c, half h holds k = (WIDE) 128 (c / 2) + 32 kg + 16 (c % 2) + 8 h .. +7, so
+  // word j of super-chunk cc (codes 8 j .. 8 j + 7 of the block) meets chunk 2 cc + j / 2, half j % 2
+  constexpr bool WIDE = StreamBuf4<SLC, NF>::WIDE;
+#pragma unroll
+  for (int nf = 0; nf < NF; ++nf) acc[nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < SLC; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) {
+        const unsigned word = WIDE ? x.q[c / 2][nf][2 * (c % 2) + h] : x.q[c][nf][h];
+        const float sc = __uint_as_float((WIDE ? x.e[c / 2][nf] : x.e[c][nf]) << 23);   // 2^(E - 127), E >= 1
+        const bf16x8 w = fp4x8_bf16(word, sc);
+        acc[nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah[c][h]), w, acc[nf], 0, 0, 0);
+        acc[nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al[c][h]), w, acc[nf], 0, 0, 0);
+      }
+}
+
 template <int SLC, int NF>
 __device__ __forceinline__ void stream_mma8(const StreamBuf8<SLC, NF>& x, const u32x4 (&ah)[SLC][2],
                                             const u32x4 (&al)[SLC][2], f32x4 (&acc)[NF]) {
@@ -404,11 +483,14 @@ __device__ __forceinline__ void stream_mma(const StreamBuf<SLC, NF>& x, const u3
 // RING = false: exactly NB fragments per workgroup (G divides the fragment count), all NB loaded
 // at once and then multiplied and reduced in order.  RING = true: NB buffers in rotation, the
 // loads of the next NB - 1 fragments in flight while one is multiplied and reduced.
-template <int SLC, int MODE, int NB, bool RING, bool FP8 = false>
+// WF: the weight format, 0 bf16, 1 E4M3 codes with row scales, 2 MXFP4 codes with block scales.
+template <int SLC, int MODE, int NB, bool RING, int WF = 0>
 __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
   constexpr int NF = 1;
-  static_assert(!(FP8 && MODE == GEMM_TOPK), "the FP8 lm_head is the wave kernel");
-  using Buf = typename std::conditional<FP8, StreamBuf8<SLC, NF>, StreamBuf<SLC, NF>>::type;
+  static_assert(!(WF && MODE == GEMM_TOPK), "the FP8 / MXFP4 lm_head is the wave kernel");
+  using Buf = typename std::conditional<
+      WF == 2, StreamBuf4<SLC, NF>,
+      typename std::conditional<WF == 1, StreamBuf8<SLC, NF>, StreamBuf<SLC, NF>>::type>::type;
   constexpr bool GLU = MODE == GEMM_SWIGLU;
   constexpr int RED_FLOATS = 2 * NF * SW * 4 * 64;
   constexpr int MRG = (MODE == GEMM_TOPK) ? 4 * 64 * (TOPK + 1) : 0;   // lane lists for the final merge
@@ -431,10 +513,14 @@ __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int c = 0; c < SLC; ++c) {
-      const bool ok = li < Mv && kw + c * 64 < p.K;
-      // bf16 weights: halves k = 32 h + 8 kg .. +7; FP8 weights: k = 16 kg + 8 h .. +7
-      const int k = min(kw + c * 64, p.K - 64) + kg * (FP8 ? 16 : 8);
-      constexpr int HO = FP8 ? 8 : 32;
+      // bf16 weights: halves k = 32 h + 8 kg .. +7; FP8 and MXFP4 weights: k = 16 kg + 8 h .. +7;
+      // MXFP4 over 2 or 4 chunks: chunk pairs form 128-k super-chunks, k = 32 kg + 16 (c % 2) + 8 h
+      constexpr bool W4 = WF == 2 && SLC >= 2;
+      const int c0 = W4 ? kw + (c / 2) * 128 : kw + c * 64;
+      const bool ok = li < Mv && c0 < p.K;
+      const int k = W4 ? min(c0, p.K - 128) + kg * 32 + (c % 2) * 16
+                       : min(c0, p.K - 64) + kg * (WF ? 16 : 8);
+      constexpr int HO = WF ? 8 : 32;
       const bf16* qh = arow + k;
       const bf16* ql = arow + p.a_plane + k;
       ah[c][0] = ok ? *reinterpret_cast<const u32x4*>(qh) : z;
@@ -478,11 +564,13 @@ __global__ __launch_bounds__(SW * 64) void gemm_stream_kernel(GemmParams p) {
   f32x4 acc[NF];
   int f = blockIdx.x;
   auto load = [&](Buf& x, int fr) {
-    if constexpr (FP8) stream_load8<SLC, NF, GLU>(x, p, ncols, fr, kw, kg, li);
+    if constexpr (WF == 2) stream_load4<SLC, NF, GLU>(x, p, ncols, fr, kw, kg, li);
+    else if constexpr (WF == 1) stream_load8<SLC, NF, GLU>(x, p, ncols, fr, kw, kg, li);
     else stream_load<SLC, NF, GLU>(x, p, ncols, fr, kw, kg, li);
   };
   auto mma = [&](const Buf& x) {
-    if constexpr (FP8) stream_mma8(x, ah, al, acc);
+    if constexpr (WF == 2) stream_mma4(x, ah, al, acc);
+    else if constexpr (WF == 1) stream_mma8(x, ah, al, acc);
     else stream_mma(x, ah, al, acc);
   };
   const int G = gridDim.x;
@@ -657,15 +745,6 @@ __device__ __forceinline__ void lw_load4(LwBatch4& x, const unsigned char* row, 
 #pragma unroll
   for (int c = 0; c < LW_CH4; ++c) x.q[c] = *reinterpret_cast<const u32x4*>(row + (k0 + 128 * c) / 2 + 16 * kg);
   x.sc = *reinterpret_cast<const u32x4*>(srow + k0 / 32);
-}
-
-__device__ __forceinline__ bf16x8 fp4x8_bf16(unsigned w, float s) {
-  u32x4 o;
-  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
-  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
-  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
-  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
-  return as_bf16x8(o);
 }
 
 __device__ __forceinline__ void lw_mma4(const LwBatch4& x, const bf16 (*sa)[LW_LD], int k0, int li, int kg,
@@ -986,19 +1065,19 @@ size_t gemm_part_floats(const GemmPlan& pl, int mode, int M, int N) {
 
 // streaming kernel with nb fragments per workgroup requested at once (nb = 0: a ring of the most
 // buffers the slice's registers allow: 3 of 4 chunks, 4 of 1 or 2; nb = -2: a ring of 2)
-template <int SLC, int MODE, bool F8>
+template <int SLC, int MODE, int WF>
 static void launch_stream(const GemmPlan& pl, int nb, const GemmParams& p, hipStream_t st) {
   constexpr int NBR = SLC == 4 ? 3 : 4;
   const dim3 sb(SW * 64);
-  if (nb == 1) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 1, false, F8>), pl.grid, sb, 0, st, p);
-  else if (nb == 2) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 2, false, F8>), pl.grid, sb, 0, st, p);
-  else if (nb == 3) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 3, false, F8>), pl.grid, sb, 0, st, p);
-  else if (nb == -2) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 2, true, F8>), pl.grid, sb, 0, st, p);
+  if (nb == 1) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 1, false, WF>), pl.grid, sb, 0, st, p);
+  else if (nb == 2) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 2, false, WF>), pl.grid, sb, 0, st, p);
+  else if (nb == 3) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 3, false, WF>), pl.grid, sb, 0, st, p);
+  else if (nb == -2) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 2, true, WF>), pl.grid, sb, 0, st, p);
   else if constexpr (NBR >= 4) {
-    if (nb == 4) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 4, false, F8>), pl.grid, sb, 0, st, p);
-    else hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, NBR, true, F8>), pl.grid, sb, 0, st, p);
+    if (nb == 4) hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, 4, false, WF>), pl.grid, sb, 0, st, p);
+    else hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, NBR, true, WF>), pl.grid, sb, 0, st, p);
   } else {
-    hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, NBR, true, F8>), pl.grid, sb, 0, st, p);
+    hipLaunchKernelGGL((gemm_stream_kernel<SLC, MODE, NBR, true, WF>), pl.grid, sb, 0, st, p);
   }
 }
 
@@ -1035,17 +1114,21 @@ hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hi
     const int nbmax = pl.slc == 4 ? 3 : 4;
     int nb = nf == 1 ? 1 : (nfrag % G == 0 && nf <= nbmax ? nf : 0);   // 0: ring of nbmax
     if (nb == 0 && pl.slc == 4 && nfrag % G == 0 && nf % 3 && nf % 2 == 0) nb = -2;   // ring of 2
-    if (p.row_scale && (mode == GEMM_TOPK || p.seg_rows < (mode == GEMM_SWIGLU ? 2 * p.half : p.N)))
-      return hipErrorInvalidValue;   // FP8 weights: PARTIAL / SWIGLU over one weight segment
+    const int wf = p.blk_scale ? 2 : (p.row_scale ? 1 : 0);
+    if (wf && (mode == GEMM_TOPK || p.seg_rows < (mode == GEMM_SWIGLU ? 2 * p.half : p.N)))
+      return hipErrorInvalidValue;   // FP8 / MXFP4 weights: PARTIAL / SWIGLU over one weight segment
+    if (wf == 2 && p.K % (pl.slc >= 2 ? 128 : 64)) return hipErrorInvalidValue;
 #define DFL_STREAM(SLC)                                                                               \
   if (pl.slc == SLC) {                                                                                \
-    if (mode == GEMM_TOPK) launch_stream<SLC, GEMM_TOPK, false>(pl, nb, p, st);                       \
+    if (mode == GEMM_TOPK) launch_stream<SLC, GEMM_TOPK, 0>(pl, nb, p, st);                           \
     else if (mode == GEMM_SWIGLU) {                                                                   \
-      if (p.row_scale) launch_stream<SLC, GEMM_SWIGLU, true>(pl, nb, p, st);                          \
-      else launch_stream<SLC, GEMM_SWIGLU, false>(pl, nb, p, st);                                     \
+      if (wf == 2) launch_stream<SLC, GEMM_SWIGLU, 2>(pl, nb, p, st);                                 \
+      else if (wf == 1) launch_stream<SLC, GEMM_SWIGLU, 1>(pl, nb, p, st);                            \
+      else launch_stream<SLC, GEMM_SWIGLU, 0>(pl, nb, p, st);                                         \
     } else {                                                                                          \
-      if (p.row_scale) launch_stream<SLC, GEMM_PARTIAL, true>(pl, nb, p, st);                         \
-      else launch_stream<SLC, GEMM_PARTIAL, false>(pl, nb, p, st);                                    \
+      if (wf == 2) launch_stream<SLC, GEMM_PARTIAL, 2>(pl, nb, p, st);                                \
+      else if (wf == 1) launch_stream<SLC, GEMM_PARTIAL, 1>(pl, nb, p, st);                           \
+      else launch_stream<SLC, GEMM_PARTIAL, 0>(pl, nb, p, st);                                        \
     }                                                                                                 \
   }
     DFL_STREAM(1)

@@ -319,6 +319,14 @@ DFLASH_API dflash_status dflash_set_lm_head_mxfp4(dflash_handle* h, const uint8_
 DFLASH_API dflash_status dflash_set_mlp_fp8(dflash_handle* h, int32_t layer, const uint8_t* gate_up_codes,
                                             const float* gate_up_scales, const uint8_t* down_codes,
                                             const float* down_scales);
+/* The same for one layer's MLP in MXFP4: gate_up_codes [2*ffn][d/2] and down_codes [d][ffn/2] as
+ * written by dflash_quantize_mxfp4_rows, with their block scale bytes gate_up_scales [2*ffn][d/32]
+ * and down_scales [d][ffn/32].  Replaces the layer's FP8 MLP weights if any (and
+ * dflash_set_mlp_fp8 replaces these); all four NULL reverts the layer to bf16.  hidden and ffn must
+ * be multiples of 128 (else DFLASH_E_UNSUPPORTED); batch-1 limits as for FP8. */
+DFLASH_API dflash_status dflash_set_mlp_mxfp4(dflash_handle* h, int32_t layer, const uint8_t* gate_up_codes,
+                                              const uint8_t* gate_up_scales, const uint8_t* down_codes,
+                                              const uint8_t* down_scales);
 /* The same for one layer's attention projections: qkv_codes [n_heads*head_dim + 2*n_kv_heads*head_dim][d]
  * are the codes of the stacked [W_q; W_k; W_v], o_codes [d][n_heads*head_dim] those of W_o.  Batch-1
  * kernels only, as above. */

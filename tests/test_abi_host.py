@@ -117,6 +117,10 @@ def test_create_validates_before_any_device_call():
     assert L.dflash_set_lm_head_mxfp4(h, fake, None) == -1
     assert L.dflash_set_lm_head_mxfp4(h, fake, fake) == -3                              # fp32 drafter
     assert L.dflash_set_lm_head_mxfp4(h, None, None) == 0
+    assert L.dflash_set_mlp_mxfp4(h, 0, fake, fake, fake, None) == -1                  # three of four set
+    assert L.dflash_set_mlp_mxfp4(h, 9, None, None, None, None) == -1                  # no such layer
+    assert L.dflash_set_mlp_mxfp4(h, 0, fake, fake, fake, fake) == -3                  # fp32 drafter
+    assert L.dflash_set_mlp_mxfp4(h, 0, None, None, None, None) == 0
     assert L.dflash_destroy(h) == 0
 
 

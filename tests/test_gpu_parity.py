@@ -568,6 +568,61 @@ def test_mid_bf16_fp8_every_gemm(H):
         case.W64 = W64
 
 
+# hidden 1024: the gate/up slices are two 64-k chunks (one 128-k MXFP4 super-chunk); ffn 4608:
+# the down projection takes 5 k-splits of 1024, the last half past the end of K
+MID_WIDE_MLP = synth.DraftConfig(name="mid_bf16_wide_mlp", n_layers=2, hidden=1024, n_heads=8, n_kv_heads=2,
+                                 head_dim=128, ffn=4608, vocab=8192, n_taps=2, target_hidden=512, block_size=16,
+                                 sel_rank=16, mask_id=8191, dtype="bf16", batch=8, window=64)
+
+
+@pytest.mark.parametrize("cfg", [MID, MID_WIDE_MLP], ids=["one_chunk_slices", "super_chunks"])
+def test_mid_bf16_mxfp4_mlp(H, cfg):
+    """Batch 1, K=16 with MXFP4 MLP weights in both layers (stacked gate/up through the SwiGLU
+    streaming kernel, down through the k-split one), with one-chunk slices (hidden 512, ffn 1024)
+    and with 128-k super-chunks (hidden 1024, ffn 4608): codes and block scales as the oracle's,
+    then a draft against the oracle run with those matrices dequantised; FP8 MLP weights set
+    afterwards replace them; more than 16 rows are refused; NULL restores bf16."""
+    import copy
+    import torch
+    case = H.Case(cfg, max_seqs=2, max_batch=2, max_inject_rows=64)
+    _prefill(case, [1], [(0, 50)])
+    W4 = copy.copy(case.W64)
+    W4["layers"] = [dict(lw) for lw in case.W64["layers"]]
+    keep = []
+    for l, lw in enumerate(case.dev_w["layers"]):
+        gu, gus = _quantize_mxfp4_on_gpu(torch.cat([lw["w_gate"], lw["w_up"]]).contiguous())
+        dn, dns = _quantize_mxfp4_on_gpu(lw["w_down"])
+        for name, codes, scales, rows in (("w_gate", gu, gus, slice(0, cfg.ffn)),
+                                          ("w_up", gu, gus, slice(cfg.ffn, 2 * cfg.ffn)),
+                                          ("w_down", dn, dns, slice(None))):
+            oc, osc = O.quantize_mxfp4_rows(case.W64["layers"][l][name])
+            assert np.array_equal(codes[rows].cpu().numpy(), oc), (l, name)
+            assert np.array_equal(scales[rows].cpu().numpy(), osc), (l, name)
+            W4["layers"][l][name] = O.dequantize_mxfp4_rows(oc, osc)
+        case.d.dflash_set_mlp_mxfp4(l, gu, gus, dn, dns)
+        keep += [gu, gus, dn, dns]
+    W64 = case.W64
+    case.W64 = W4
+    try:
+        res = _check(H, case, [1], [222], mode_names=("viterbi",))
+        _same_topk_without_logits(case, [1], [222], res)
+    finally:
+        case.W64 = W64
+    with pytest.raises(B.DflashError):
+        case.draft([1, 0], [222, 5])               # 32 rows
+    W8 = _fp8_drafter(case, mlp=True, lm_head=False)   # replaces the MXFP4 MLP weights
+    case.W64 = W8
+    try:
+        _check(H, case, [1], [222], mode_names=("viterbi",))
+    finally:
+        case.W64 = W64
+    for l in range(cfg.n_layers):
+        case.d.dflash_set_mlp_mxfp4(l, None, None, None, None)
+    res = case.draft([1], [222], logits=True)
+    err, _ = H.check_draft(case, [1], [222], res)
+    assert err <= H.LOGIT_TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_per_channel_conv(H, dtype):
     """The pages' per-channel two-tap conv (one correction per 16 channels): the fp32 tiny drafter

@@ -392,6 +392,45 @@ def test_b1_k16_fp8_mlp(H, big):
     assert run.d.dflash_get_device_error() == 0
 
 
+def test_b1_k16_mxfp4_mlp(H, big):
+    """The b1_k16 drafter with MXFP4 MLP weights in all 5 layers (stacked gate/up 12288 x 2048,
+    down 2048 x 6144): codes and block scales as the oracle's, then a full-window draft against the
+    oracle run with those matrices dequantised."""
+    import copy
+    import torch
+    cfg = synth.WORKLOADS["b1_k16"]
+    run = Run(H, big, cfg, max_seqs=1, max_batch=1, max_inject_rows=1024, sampled=[0])
+    W4 = copy.copy(big["W64"])
+    W4["layers"] = [dict(lw) for lw in big["W64"]["layers"]]
+    keep = []
+    for l, lw in enumerate(big["dev"]["layers"]):
+        out = []
+        for mat in (torch.cat([lw["w_gate"], lw["w_up"]]).contiguous(), lw["w_down"]):
+            rows, cols = mat.shape
+            codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
+            scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
+            B.dflash_quantize_mxfp4_rows(mat, codes, scales)
+            out += [codes, scales]
+        torch.cuda.synchronize()
+        for name, codes, scales, rows in (("w_gate", out[0], out[1], slice(0, cfg.ffn)),
+                                          ("w_up", out[0], out[1], slice(cfg.ffn, 2 * cfg.ffn)),
+                                          ("w_down", out[2], out[3], slice(None))):
+            oc, osc = O.quantize_mxfp4_rows(big["W64"]["layers"][l][name])
+            assert np.array_equal(codes[rows].cpu().numpy(), oc), (l, name)
+            assert np.array_equal(scales[rows].cpu().numpy(), osc), (l, name)
+            W4["layers"][l][name] = O.dequantize_mxfp4_rows(oc, osc)
+        run.d.dflash_set_mlp_mxfp4(l, *out)
+        keep += out
+    run.W64 = W4
+    run.d.dflash_reset_seqs(run.t(np.zeros(1, dtype=np.int32)))
+    run.inject([0], [_window(cfg.context[0], cfg.window)])
+    anchors = synth.anchors(cfg).tolist()
+    res = run.draft([0], anchors)
+    run.own_logit_topk(res)
+    run.compare_sampled([0], anchors, res)
+    assert run.d.dflash_get_device_error() == 0
+
+
 def _codes(mat):
     import torch
     codes = torch.empty(mat.shape, dtype=torch.uint8, device="cuda")
