@@ -801,6 +801,22 @@ def main():
         out[key] = batched_record(wname, desc, rb)
         del rb["cycle"]
         _release(torch)
+    if not args.no_b32 and not args.no_fp8:
+        torch.cuda.empty_cache()
+        rb = run_workload(synth.WORKLOADS["b32_k8_conv"], args.steps, args.warmup, torch, fp8_lm_head=True,
+                          fp8_mlp=True, fp8_attn_inject=True)
+        lm8_bytes = rb["alg"]["lm_head_bytes"] - synth.WORKLOADS["b32_k8_conv"].vocab * \
+            synth.WORKLOADS["b32_k8_conv"].hidden   # one byte per lm_head weight instead of two
+        out["b32_fp8_all_gemms"] = {
+            "workload": "b32_k8_conv with E4M3 codes (per-row power-of-two scales) for every weight GEMM of the "
+                        "cycle: injection fc and K/V, QKV, O, gate/up, down, lm_head (weight-only; activations bf16; "
+                        "the LDS tile kernels stage 16 rows x 64 k of codes per 1 KiB block)",
+            "blocks_per_s": round(rb["blocks_per_s"], 1), "draft_tokens_per_s": round(rb["draft_tokens_per_s"], 1),
+            "ms_per_step": round(rb["ms_per_step"], 4), "lm_head_avg_ms": round(rb["lm_head_ms"], 5),
+            "lm_head_bytes": int(lm8_bytes),
+            "lm_head_gbps": round(lm8_bytes / (rb["lm_head_ms"] * 1e-3) / 1e9, 1)}
+        del rb["cycle"]
+        _release(torch)
     if not args.no_pc:
         torch.cuda.empty_cache()
         cpc = synth.WORKLOADS["b1_k16"].replace(conv_group=16, name="b1_k16_pc16")

@@ -311,22 +311,22 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
   const dflash_config* c = &H->cfg;
   const bool b = bf(c);
   const int K = c->block_size, d = c->hidden, M = n_seq * K;
-  bool any_mlp_q = false;
-  for (const auto& m : H->mlp_q) any_mlp_q |= m.gu != nullptr;
-  if (any_mlp_q && (gemm_plan(true, GEMM_SWIGLU, M, 2 * c->ffn, d).kind != 3 ||
-                    gemm_plan(true, GEMM_PARTIAL, M, d, c->ffn).kind != 3))
-    return fail(DFLASH_E_UNSUPPORTED, "FP8 / MXFP4 MLP weights take at most 16 draft rows (n_seq * block_size = %d) "
+  // E4M3 weights run in every GEMM kernel but the batch-1 streaming top-16 one (the lm_head of
+  // at most 16 rows takes the independent-wave kernel, hidden a multiple of 512 up to 2048);
+  // MXFP4 weights only in the batch-1 streaming and independent-wave kernels
+  bool any_mlp_fp4 = false;
+  for (const auto& m : H->mlp_q) any_mlp_fp4 |= m.gu_b != nullptr;
+  if (any_mlp_fp4 && (gemm_plan(true, GEMM_SWIGLU, M, 2 * c->ffn, d).kind != 3 ||
+                      gemm_plan(true, GEMM_PARTIAL, M, d, c->ffn).kind != 3))
+    return fail(DFLASH_E_UNSUPPORTED, "MXFP4 MLP weights take at most 16 draft rows (n_seq * block_size = %d) "
                 "and a hidden size of at most 2048", M);
-  bool any_attn_fp8 = false;
-  for (const auto& a8 : H->attn_fp8) any_attn_fp8 |= a8.qkv != nullptr;
-  if (any_attn_fp8 && (gemm_plan(true, GEMM_PARTIAL, M, c->n_heads * c->head_dim + 2 * c->n_kv_heads * c->head_dim,
-                                 d).kind != 3 ||
-                       gemm_plan(true, GEMM_PARTIAL, M, d, c->n_heads * c->head_dim).kind != 3))
-    return fail(DFLASH_E_UNSUPPORTED, "FP8 attention projections take at most 16 draft rows (n_seq * block_size = %d)",
-                M);
-  if ((H->lm_fp8 || H->lm_fp4) && gemm_plan(true, GEMM_TOPK, M, c->vocab, d).kind != 4)
-    return fail(DFLASH_E_UNSUPPORTED, "the FP8 / MXFP4 lm_head takes at most 16 draft rows (n_seq * block_size = %d) "
+  const int lm_kind = gemm_plan(true, GEMM_TOPK, M, c->vocab, d).kind;
+  if (H->lm_fp4 && lm_kind != 4)
+    return fail(DFLASH_E_UNSUPPORTED, "the MXFP4 lm_head takes at most 16 draft rows (n_seq * block_size = %d) "
                 "and a hidden size that is a multiple of 512 up to 2048", M);
+  if (H->lm_fp8 && lm_kind == 3)
+    return fail(DFLASH_E_UNSUPPORTED, "with at most 16 draft rows the FP8 lm_head needs a hidden size that is a "
+                "multiple of 512 up to 2048 (n_seq * block_size = %d)", M);
   const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
   float* part = wsp<float>(ws, W.part);
   SeqCtx* ctx = wsp<SeqCtx>(ws, W.ctx);
@@ -425,7 +425,7 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
     gq.seg_rows = kvw;
     gq.part = part;
     const Handle::Fp8Attn* a8 = (size_t)l < H->attn_fp8.size() && H->attn_fp8[l].qkv ? &H->attn_fp8[l] : nullptr;
-    if (a8) {   // one stacked [wq; wk; wv] segment of E4M3 codes (checked up front: the stream kernel)
+    if (a8) {   // one stacked [wq; wk; wv] segment of E4M3 codes
       gq.seg[0] = a8->qkv;
       gq.seg_rows = qw + 2 * kvw;
       gq.ldb = d;
@@ -520,7 +520,7 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
     gg.out_plane = Mmax * c->ffn;
     gg.part = part;
     const Handle::QuantMlp* mq = (size_t)l < H->mlp_q.size() && H->mlp_q[l].gu ? &H->mlp_q[l] : nullptr;
-    if (mq) {   // one stacked [gate; up] segment of codes (checked up front: the stream kernel)
+    if (mq) {   // one stacked [gate; up] segment of codes (MXFP4: checked up front, the stream kernel)
       gg.seg[0] = mq->gu;
       gg.seg[1] = nullptr;
       gg.seg_rows = 2 * c->ffn;
@@ -613,7 +613,7 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
       gl.ldb = d / 2;                 // bytes per weight row
       gl.blk_scale = H->lm_fp4_scale;
     } else if (H->lm_fp8) {
-      // FP8 lm_head: only the independent-wave kernel (<= 16 rows) takes it (checked up front)
+      // FP8 lm_head: every top-16 kernel but the batch-1 streaming one (checked up front)
       gl.seg[0] = H->lm_fp8;
       gl.ldb = d;                     // bytes per weight row
       gl.row_scale = H->lm_fp8_scale;
@@ -781,14 +781,6 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
   ia.meta_seq = wsp<int>(H, H->wl.meta_seq);
   ia.meta_pos = wsp<int>(H, H->wl.meta_pos);
   const long long max_rows = (long long)n_seq * max_new;
-  // host-checkable refusal before anything is enqueued (the plan kernel advances seq_len)
-  if (H->inj_fc8) {
-    const int pr = (int)(max_rows < Ri ? max_rows : Ri);
-    if (pr > 0 && (gemm_plan(true, GEMM_PARTIAL, pr, d, concat).kind != 3 ||
-                   gemm_plan(true, GEMM_PARTIAL, pr, c->n_layers * 2 * c->n_kv_heads * c->head_dim, d).kind != 3))
-      return fail(DFLASH_E_UNSUPPORTED, "FP8 injection weights take at most 16 rows per call (n_seq * max_new = %lld); "
-                  "inject longer spans with the bf16 weights", max_rows);
-  }
   HIP_TRY(launch_inject_plan(ia, st));
   float* part = wsp<float>(H, H->wl.part);
   for (long long r0 = 0; r0 < max_rows; r0 += Ri) {

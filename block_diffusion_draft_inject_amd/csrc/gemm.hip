@@ -28,17 +28,6 @@ namespace dfl {
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
-// FP8 weights (row_scale set): eight E4M3 codes (two words, lowest byte first) -> eight bf16
-// values code * s, exact (an E4M3 value times a power of two fits bf16)
-__device__ __forceinline__ bf16x8 fp8x8_bf16(unsigned w0, unsigned w1, float s) {
-  u32x4 o;
-  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false));
-  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true));
-  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false));
-  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true));
-  return as_bf16x8(o);
-}
-
 // MXFP4 weights (blk_scale set): one word of eight E2M1 codes (element 2j in the low nibble of
 // byte j) -> eight bf16 values code * s, s = 2^(E - 127) of the codes' block, exact
 __device__ __forceinline__ bf16x8 fp4x8_bf16(unsigned w, float s) {
@@ -65,18 +54,23 @@ struct SkinnyBatch {
 
 // Loads chunks c and c + cstep; both indices are clamped to clast so the loads are always
 // issued (no branch around them: the compiler then keeps exact vmcnt counts and the next
-// batch stays in flight while the current one is multiplied).
-template <int MT, int NF>
+// batch stays in flight while the current one is multiplied).  F8: weight rows of E4M3 codes,
+// one 16-byte load per lane and chunk (k = 16 kg .. 16 kg + 15, the same k as the two bf16 halves).
+template <int MT, int NF, bool F8 = false>
 __device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NF>& x, const bf16* const (&arow)[MT], size_t a_plane,
-                                            const bf16* const (&brow)[NF], int kg, int c, int cstep, int clast) {
+                                            const void* const (&brow)[NF], int kg, int c, int cstep, int clast) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int k = min(c + u * cstep, clast) * 64 + kg * 16;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const u32x4* q = reinterpret_cast<const u32x4*>(brow[f] + k);
-      x.b[u][f][0] = q[0];
-      x.b[u][f][1] = q[1];
+      if constexpr (F8) {
+        x.b[u][f][0] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(brow[f]) + k);
+      } else {
+        const u32x4* q = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(brow[f]) + k);
+        x.b[u][f][0] = q[0];
+        x.b[u][f][1] = q[1];
+      }
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -90,47 +84,64 @@ __device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NF>& x, const bf16* 
   }
 }
 
-template <int MT, int NF>
-__device__ __forceinline__ void skinny_mma(const SkinnyBatch<MT, NF>& x, bool two, f32x4 (&acc)[MT][NF]) {
+template <int MT, int NF, bool F8 = false>
+__device__ __forceinline__ void skinny_mma(const SkinnyBatch<MT, NF>& x, bool two, const float (&bs)[NF],
+                                           f32x4 (&acc)[MT][NF]) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     if (u == 1 && !two) break;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 w = F8 ? fp8x8_bf16(x.b[u][f][0][2 * h], x.b[u][f][0][2 * h + 1], bs[f]) : as_bf16x8(x.b[u][f][h]);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.ah[u][m][h]), as_bf16x8(x.b[u][f][h]), acc[m][f], 0, 0, 0);
-          acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.al[u][m][h]), as_bf16x8(x.b[u][f][h]), acc[m][f], 0, 0, 0);
+        for (int m = 0; m < MT; ++m) {
+          acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.ah[u][m][h]), w, acc[m][f], 0, 0, 0);
+          acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.al[u][m][h]), w, acc[m][f], 0, 0, 0);
         }
+      }
   }
 }
 
-template <int MT, int NF>
-__device__ __forceinline__ void skinny_acc(const bf16* const (&arow)[MT], size_t a_plane, const bf16* const (&brow)[NF],
-                                           int kg, int c0, int c1, int cstep, f32x4 (&acc)[MT][NF]) {
+// bs: F8, the row scale of each weight row (unused for bf16 weights)
+template <int MT, int NF, bool F8 = false>
+__device__ __forceinline__ void skinny_acc(const bf16* const (&arow)[MT], size_t a_plane, const void* const (&brow)[NF],
+                                           const float (&bs)[NF], int kg, int c0, int c1, int cstep,
+                                           f32x4 (&acc)[MT][NF]) {
   if (c0 >= c1) return;
   const int clast = c0 + (c1 - 1 - c0) / cstep * cstep;   // last chunk this wave owns
   SkinnyBatch<MT, NF> x, y;
   int c = c0;
-  skinny_load(x, arow, a_plane, brow, kg, c, cstep, clast);
+  skinny_load<MT, NF, F8>(x, arow, a_plane, brow, kg, c, cstep, clast);
   while (true) {
     const int cy = c + 2 * cstep;
-    skinny_load(y, arow, a_plane, brow, kg, cy, cstep, clast);
-    skinny_mma(x, c + cstep < c1, acc);
+    skinny_load<MT, NF, F8>(y, arow, a_plane, brow, kg, cy, cstep, clast);
+    skinny_mma<MT, NF, F8>(x, c + cstep < c1, bs, acc);
     if (cy >= c1) break;
     const int cx = cy + 2 * cstep;
-    skinny_load(x, arow, a_plane, brow, kg, cx, cstep, clast);
-    skinny_mma(y, cy + cstep < c1, acc);
+    skinny_load<MT, NF, F8>(x, arow, a_plane, brow, kg, cx, cstep, clast);
+    skinny_mma<MT, NF, F8>(y, cy + cstep < c1, bs, acc);
     if (cx >= c1) break;
     c = cx;
   }
 }
 
+// weight row n (bf16 segments, or one segment of E4M3 codes) and its scale
+template <bool F8>
+__device__ __forceinline__ const void* wrow_ptr(const GemmParams& p, int n, float& scale) {
+  if constexpr (F8) {
+    scale = p.row_scale[n];
+    return reinterpret_cast<const unsigned char*>(p.seg[0]) + (size_t)n * p.ldb;
+  } else {
+    scale = 1.f;
+    return brow_ptr(p, n);
+  }
+}
+
 // PARTIAL (NF=1) and SWIGLU (NF=2: gate and up fragment of the same 16 output columns).
 // grid: x = column tile (16 output columns), y = row tile (16*MT rows), z = k-split.
-template <int MT, int MODE>
+template <int MT, int MODE, bool F8 = false>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
   constexpr int NF = (MODE == GEMM_SWIGLU) ? 2 : 1;
   __shared__ float red[3][MT][NF][4][64];
@@ -146,12 +157,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
     const int r = min(m0 + m * 16 + li, Mv - 1);
     arow[m] = reinterpret_cast<const bf16*>(p.A) + (size_t)r * p.lda;
   }
-  const bf16* brow[NF];
+  const void* brow[NF];
+  float bs[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     int n = ncol0 + li + f * p.half;     // SWIGLU: f=1 reads the up rows at offset `half`
     n = min(n, p.N - 1);
-    brow[f] = brow_ptr(p, n);
+    brow[f] = wrow_ptr<F8>(p, n, bs[f]);
   }
   const int nchunks = p.K / 64;
   const int s = blockIdx.z;
@@ -161,7 +173,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  skinny_acc<MT, NF>(arow, p.a_plane, brow, kg, c0 + wave, c1, 4, acc);
+  skinny_acc<MT, NF, F8>(arow, p.a_plane, brow, bs, kg, c0 + wave, c1, 4, acc);
   // reduce the 4 waves' k-slices
   if (wave > 0) {
 #pragma unroll
@@ -204,7 +216,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
 // 9496 fragments of a 151936-word vocabulary divide.  Each row's candidates are kept by
 // 64/(16*MT) lanes in private sorted top-16 lists, merged at the end of the workgroup; one
 // partial list per (row, workgroup) is written.  grid: x = workgroups, y = row tile.
-template <int MT>
+template <int MT, bool F8 = false>
 __global__ __launch_bounds__(256) void lmhead_topk_skinny(GemmParams p) {
   constexpr int R = 16 * MT;
   constexpr int LPR = 64 / R;          // lanes per row within a wave: 4, 2, 1
@@ -237,11 +249,12 @@ __global__ __launch_bounds__(256) void lmhead_topk_skinny(GemmParams p) {
     f = __shfl(f, 0, WAVE);
     if (f >= nfrag) break;
     const int col = f * 16 + li;
-    const bf16* brow[1] = {brow_ptr(p, min(col, p.N - 1))};
+    float bs[1];
+    const void* brow[1] = {wrow_ptr<F8>(p, min(col, p.N - 1), bs[0])};
     f32x4 acc[MT][1];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    skinny_acc<MT, 1>(arow, p.a_plane, brow, kg, 0, nchunks, 1, acc);
+    skinny_acc<MT, 1, F8>(arow, p.a_plane, brow, bs, kg, 0, nchunks, 1, acc);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -1145,19 +1158,29 @@ hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hi
     return hipGetLastError();
   }
   if (pl.kind == 0) {
-    if (mode == GEMM_TOPK) {
-      if (pl.mt == 1) hipLaunchKernelGGL(lmhead_topk_skinny<1>, pl.grid, blk, 0, st, p);
-      else if (pl.mt == 2) hipLaunchKernelGGL(lmhead_topk_skinny<2>, pl.grid, blk, 0, st, p);
-      else hipLaunchKernelGGL(lmhead_topk_skinny<4>, pl.grid, blk, 0, st, p);
-    } else if (mode == GEMM_SWIGLU) {
-      if (pl.mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<1, GEMM_SWIGLU>), pl.grid, blk, 0, st, p);
-      else if (pl.mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<2, GEMM_SWIGLU>), pl.grid, blk, 0, st, p);
-      else hipLaunchKernelGGL((gemm_skinny_kernel<4, GEMM_SWIGLU>), pl.grid, blk, 0, st, p);
-    } else {
-      if (pl.mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<1, GEMM_PARTIAL>), pl.grid, blk, 0, st, p);
-      else if (pl.mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<2, GEMM_PARTIAL>), pl.grid, blk, 0, st, p);
-      else hipLaunchKernelGGL((gemm_skinny_kernel<4, GEMM_PARTIAL>), pl.grid, blk, 0, st, p);
+    if (p.blk_scale) return hipErrorInvalidValue;   // MXFP4: batch-1 kernels only
+    if (p.row_scale && p.seg_rows < (mode == GEMM_SWIGLU ? 2 * p.half : p.N))
+      return hipErrorInvalidValue;                  // E4M3 weights: one segment
+#define DFL_SKINNY(F8)                                                                                \
+    if (mode == GEMM_TOPK) {                                                                          \
+      if (pl.mt == 1) hipLaunchKernelGGL((lmhead_topk_skinny<1, F8>), pl.grid, blk, 0, st, p);        \
+      else if (pl.mt == 2) hipLaunchKernelGGL((lmhead_topk_skinny<2, F8>), pl.grid, blk, 0, st, p);   \
+      else hipLaunchKernelGGL((lmhead_topk_skinny<4, F8>), pl.grid, blk, 0, st, p);                   \
+    } else if (mode == GEMM_SWIGLU) {                                                                 \
+      if (pl.mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<1, GEMM_SWIGLU, F8>), pl.grid, blk, 0, st, p);      \
+      else if (pl.mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<2, GEMM_SWIGLU, F8>), pl.grid, blk, 0, st, p); \
+      else hipLaunchKernelGGL((gemm_skinny_kernel<4, GEMM_SWIGLU, F8>), pl.grid, blk, 0, st, p);                 \
+    } else {                                                                                          \
+      if (pl.mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<1, GEMM_PARTIAL, F8>), pl.grid, blk, 0, st, p);      \
+      else if (pl.mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<2, GEMM_PARTIAL, F8>), pl.grid, blk, 0, st, p); \
+      else hipLaunchKernelGGL((gemm_skinny_kernel<4, GEMM_PARTIAL, F8>), pl.grid, blk, 0, st, p);                 \
     }
+    if (p.row_scale) {
+      DFL_SKINNY(true)
+    } else {
+      DFL_SKINNY(false)
+    }
+#undef DFL_SKINNY
     return hipGetLastError();
   }
   if (pl.kind == 5) return tile_launch(pl, mode, p, st);

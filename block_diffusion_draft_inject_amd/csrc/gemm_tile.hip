@@ -39,6 +39,34 @@ struct TileCfg {
   static constexpr int D = NBLK / NW;                // LDS-DMA instructions per wave per stage
   static constexpr int LDS = S * STAGE;
   static constexpr int BMc = BM, BNc = BN, Sc = S, WGNc = WGN;
+  static constexpr int WF = 0;                       // bf16 weights
+  static_assert(BA % NW == 0 && BB % NW == 0, "blocks per operand must split evenly over the waves");
+};
+
+// E4M3 weights (row_scale set).  One byte per weight, so a 1 KiB LDS-DMA block holds 16 weight
+// rows x 64 k, two k-steps: the k-steps go in pairs.  A pair buffer holds the activation blocks of
+// both steps (as for bf16 weights) and one weight block per 16 columns covering both steps; NP
+// pair buffers rotate, NP - 1 pairs in flight while one is multiplied.  The four 16-byte pieces
+// (16 k each) of a weight row sit in the same row-dependent XOR order as the bf16 chunks; a lane
+// takes the 8 codes of its MFMA operand (k = 32 s + 8 kg .. + 7 of step s of the pair) with one
+// 8-byte LDS read and widens them to bf16 (exact).  The row scale multiplies the finished
+// column: the scales are powers of two, so this equals multiplying by the scaled weights.
+template <int BM, int BN, int WGM, int WGN, int NP, int PL = 2>
+struct Tile8Cfg {
+  static constexpr int NW = WGM * WGN, NT = NW * 64;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int FM = WM / 16, FN = WN / 16;
+  static constexpr int BA = BM / 16, BB = BN / 16;
+  static constexpr int PLc = PL;
+  static constexpr int NBLK = 2 * PL * BA + BB;          // blocks per pair buffer
+  static constexpr int PAIR = NBLK * 1024;
+  static constexpr int QA = PL * BA / NW, QB = BB / NW;   // per wave and pair: 2 QA activation, QB weight DMAs
+  static constexpr int D2 = 2 * QA + QB;
+  static constexpr int LDS = NP * PAIR;
+  static constexpr int BMc = BM, BNc = BN, NPc = NP, WGNc = WGN;
+  static constexpr int WF = 1;
+  static_assert(PL == 1 || PL == 2, "activation planes");
+  static_assert(NP >= 2 && NP <= 3, "pair buffers");
   static_assert(BA % NW == 0 && BB % NW == 0, "blocks per operand must split evenly over the waves");
 };
 
@@ -224,6 +252,111 @@ __device__ __forceinline__ void tile_run_pairs(const GemmParams& p, unsigned cha
   }
 }
 
+template <class T>
+struct Tile8Src {
+  const char* base[T::QA];
+  unsigned voff[T::QA];
+  const unsigned char* addr[T::QB];
+};
+
+template <class T>
+__device__ __forceinline__ void tile8_src(const GemmParams& p, int m0, int n0, int Mv, int ncap, int wave, int lane,
+                                          Tile8Src<T>& s) {
+  const int r16 = lane >> 2;
+  const int kc = (lane & 3) ^ tile_swz(r16);
+  const char* ahi = reinterpret_cast<const char*>(p.A);
+  const char* alo = reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.A) + p.a_plane);
+#pragma unroll
+  for (int q = 0; q < T::QA; ++q) {
+    const int b = T::NW * q + wave;                // activation block of a step: hi rows, then lo rows
+    const bool hi = T::NW * q < T::BA;
+    const int r = min(m0 + (hi ? b : b - T::BA) * 16 + r16, Mv - 1);
+    s.base[q] = hi ? ahi : alo;
+    s.voff[q] = (unsigned)(((size_t)r * p.lda + kc * 8) * 2);
+  }
+#pragma unroll
+  for (int q = 0; q < T::QB; ++q) {
+    const int n = min(n0 + (T::NW * q + wave) * 16 + r16, ncap - 1);   // columns past ncap re-read the last
+    s.addr[q] = reinterpret_cast<const unsigned char*>(p.seg[0]) + (size_t)n * p.ldb + kc * 16;
+  }
+}
+
+// the pair of k-steps c, c + 1 into the pair buffer at LDS address `pb`
+template <class T>
+__device__ __forceinline__ void tile8_issue(const Tile8Src<T>& s, unsigned pb, int wave, int c) {
+#pragma unroll
+  for (int q = 0; q < T::QA; ++q) {
+    dma16(pb + (T::NW * q + wave) * 1024, s.voff[q], s.base[q] + (size_t)c * MK * 2);
+    dma16(pb + (T::PLc * T::BA + T::NW * q + wave) * 1024, s.voff[q], s.base[q] + (size_t)(c + 1) * MK * 2);
+  }
+#pragma unroll
+  for (int q = 0; q < T::QB; ++q) dma16v(pb + (2 * T::PLc * T::BA + T::NW * q + wave) * 1024, s.addr[q] + (size_t)c * MK);
+}
+
+// step st (0, 1) of the pair in `pair`: lo = the lane's activation offset in a block, lb = its
+// weight offset for this step
+template <class T>
+__device__ __forceinline__ void tile8_mma(const unsigned char* pair, int st, int wm, int wn, unsigned lo, unsigned lb,
+                                          f32x4 (&acc)[T::FM][T::FN]) {
+  bf16x8 b[T::FN];
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) {
+    const uint2 w = *reinterpret_cast<const uint2*>(pair + (2 * T::PLc * T::BA + wn * T::FN + j) * 1024 + lb);
+    b[j] = fp8x8_bf16(w.x, w.y, 1.f);
+  }
+  const unsigned char* a = pair + st * T::PLc * T::BA * 1024;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(a + (wm * T::FM + i) * 1024 + lo);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b[j], acc[i][j], 0, 0, 0);
+    if constexpr (T::PLc == 2) {
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(a + (T::BA + wm * T::FM + i) * 1024 + lo);
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+// One output tile over the k-step pairs starting at step c0 (even), np pairs: acc = the tile's
+// partial products (before the row scales).
+template <class T>
+__device__ __forceinline__ void tile8_run(const GemmParams& p, unsigned char* smem, int m0, int n0, int Mv, int ncap,
+                                          int c0, int np, f32x4 (&acc)[T::FM][T::FN]) {
+  constexpr int NP = T::NPc;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / T::WGNc, wn = wave % T::WGNc, li = lane & 15, kg = lane >> 4;
+  Tile8Src<T> src;
+  tile8_src<T>(p, m0, n0, Mv, ncap, wave, lane, src);
+  const unsigned lo = li * 64 + ((kg ^ tile_swz(li)) << 4);
+  const unsigned lb0 = li * 64 + (((kg >> 1) ^ tile_swz(li)) << 4) + (kg & 1) * 8;
+  const unsigned lb1 = li * 64 + (((2 + (kg >> 1)) ^ tile_swz(li)) << 4) + (kg & 1) * 8;
+  const unsigned sbase = lds_addr(smem);
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q + 1 < NP; ++q)
+    if (q < np) tile8_issue<T>(src, sbase + q * T::PAIR, wave, c0 + 2 * q);
+  int cur = 0;   // buffer of pair j
+  for (int j = 0; j < np; ++j) {
+    // pair j has landed for every wave (later pairs may still be in flight), and every wave is
+    // done with pair j - 1's buffer
+    if (NP >= 3 && j + 1 < np) wait_barrier<T::D2>();
+    else wait_barrier<0>();
+    if (j + NP - 1 < np) {
+      const int nb = cur == 0 ? NP - 1 : cur - 1;
+      tile8_issue<T>(src, sbase + nb * T::PAIR, wave, c0 + 2 * (j + NP - 1));
+    }
+    tile8_mma<T>(smem + cur * T::PAIR, 0, wm, wn, lo, lb0, acc);
+    tile8_mma<T>(smem + cur * T::PAIR, 1, wm, wn, lo, lb1, acc);
+    cur = cur + 1 == NP ? 0 : cur + 1;
+  }
+}
+
 // PARTIAL: grid x = k-split, y = column tile, z = row tile; part[split][row][col].  The split is
 // the fastest grid index: workgroups go to the eight XCDs round-robin by linear index, so with
 // eight splits each XCD takes one k-range and its L2 fetches only that slice of the activation
@@ -237,13 +370,25 @@ __global__ __launch_bounds__(T::NT, OCC) void gemm_tile_partial(GemmParams p) {
   const int m0 = blockIdx.z * T::BMc, n0 = blockIdx.y * T::BNc;
   if (m0 >= Mv) return;
   const int nk = p.K / MK, s = blockIdx.x;
-  const int c0 = (int)((long)nk * s / p.splits), c1 = (int)((long)nk * (s + 1) / p.splits);
   f32x4 acc[T::FM][T::FN];
-  if constexpr (T::Sc == 4) {
-    if ((c1 - c0) % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, p.N, c0, c1 - c0, acc);
-    else tile_run<T>(p, smem, m0, n0, Mv, p.N, c0, c1, acc);
+  float sc[T::FN];   // E4M3: the row scale of each of the lane's columns
+  if constexpr (T::WF == 1) {
+    // whole pairs of k-steps per split (K is a multiple of 64)
+    const int np = nk / 2;
+    const int p0 = (int)((long)np * s / p.splits), p1 = (int)((long)np * (s + 1) / p.splits);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) sc[j] = p.row_scale[min(n0 + wn * T::WN + j * 16 + li, p.N - 1)];
+    tile8_run<T>(p, smem, m0, n0, Mv, p.N, 2 * p0, p1 - p0, acc);
   } else {
-    tile_run<T>(p, smem, m0, n0, Mv, p.N, c0, c1, acc);
+    const int c0 = (int)((long)nk * s / p.splits), c1 = (int)((long)nk * (s + 1) / p.splits);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) sc[j] = 1.f;
+    if constexpr (T::Sc == 4) {
+      if ((c1 - c0) % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, p.N, c0, c1 - c0, acc);
+      else tile_run<T>(p, smem, m0, n0, Mv, p.N, c0, c1, acc);
+    } else {
+      tile_run<T>(p, smem, m0, n0, Mv, p.N, c0, c1, acc);
+    }
   }
 #pragma unroll
   for (int i = 0; i < T::FM; ++i)
@@ -253,7 +398,7 @@ __global__ __launch_bounds__(T::NT, OCC) void gemm_tile_partial(GemmParams p) {
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + wm * T::WM + i * 16 + kg * 4 + r;
         const int col = n0 + wn * T::WN + j * 16 + li;
-        if (row < Mv && col < p.N) p.part[((size_t)s * p.M + row) * p.N + col] = acc[i][j][r];
+        if (row < Mv && col < p.N) p.part[((size_t)s * p.M + row) * p.N + col] = acc[i][j][r] * sc[j];
       }
 }
 
@@ -295,7 +440,18 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
   top.init();
   for (int n0 = cbeg; n0 < cend; n0 += BN) {
     f32x4 acc[T::FM][T::FN];
-    if constexpr (T::Sc == 4) {
+    if constexpr (T::WF == 1) {
+      // E4M3: the row scales of the lane's columns (read after the k-loop: held across it, they
+      // pushed the 256 x 256 tile past its registers)
+      tile8_run<T>(p, smem, m0, n0, Mv, cend, 0, nk / 2, acc);
+      float sc[T::FN];
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) sc[j] = p.row_scale[min(n0 + wn * T::WN + j * 16 + li, p.N - 1)];
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) acc[i][j] *= sc[j];
+    } else if constexpr (T::Sc == 4) {
       if (nk % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, cend, 0, nk, acc);
       else tile_run<T>(p, smem, m0, n0, Mv, cend, 0, nk, acc);
     } else {
@@ -395,9 +551,35 @@ using TileBig = TileCfg<256, 256, 4, 2, 3>;
 using TileTall = TileCfg<256, 128, 4, 2, 4>;
 using TileSmallHi = TileCfg<128, 128, 2, 2, 3, 1>;
 using TileBigHi = TileCfg<256, 256, 4, 2, 4, 1>;
+// E4M3 weights: pair buffers of 40 / 72 KiB (layer GEMMs, two each) and 24 / 48 KiB (lm_head,
+// three each)
+using TileSmall8 = Tile8Cfg<128, 128, 2, 2, 2>;
+using TileTall8 = Tile8Cfg<256, 128, 4, 2, 2>;
+using TileSmallHi8 = Tile8Cfg<128, 128, 2, 2, 3, 1>;
+using TileBigHi8 = Tile8Cfg<256, 256, 4, 2, 3, 1>;
 
 hipError_t tile_launch(const GemmPlan& pl, int mode, const GemmParams& p, hipStream_t st) {
   if (p.K % MK) return hipErrorInvalidValue;
+  if (p.row_scale) {   // E4M3 weights: one segment, whole pairs of k-steps
+    if (p.K % (2 * MK) || p.seg_rows < p.N || p.blk_scale) return hipErrorInvalidValue;
+    if (mode == GEMM_TOPK) {
+      if (pl.mt) {
+        if (p.logits) hipLaunchKernelGGL((lmhead_topk_tile<TileBigHi8, 1, true>), pl.grid, dim3(TileBigHi8::NT), 0, st, p);
+        else hipLaunchKernelGGL((lmhead_topk_tile<TileBigHi8, 1, false>), pl.grid, dim3(TileBigHi8::NT), 0, st, p);
+      } else {
+        if (p.logits) hipLaunchKernelGGL((lmhead_topk_tile<TileSmallHi8, 2, true>), pl.grid, dim3(TileSmallHi8::NT), 0, st, p);
+        else hipLaunchKernelGGL((lmhead_topk_tile<TileSmallHi8, 2, false>), pl.grid, dim3(TileSmallHi8::NT), 0, st, p);
+      }
+    } else if (mode == GEMM_PARTIAL) {
+      const dim3 g(pl.grid.z, pl.grid.x, pl.grid.y);
+      if (pl.mt == 2) hipLaunchKernelGGL((gemm_tile_partial<TileTall8, 1>), g, dim3(TileTall8::NT), 0, st, p);
+      else if (pl.mt == 0) hipLaunchKernelGGL((gemm_tile_partial<TileSmall8, 2>), g, dim3(TileSmall8::NT), 0, st, p);
+      else return hipErrorInvalidValue;
+    } else {
+      return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (mode == GEMM_TOPK) {
     if (pl.mt) {
       const dim3 blk(TileBigHi::NT);

@@ -55,6 +55,17 @@ struct GemmPlan {
   dim3 grid;
 };
 
+// FP8 weights (row_scale set): eight E4M3 codes (two words, lowest byte first) -> eight bf16
+// values code * s, exact (an E4M3 value times a power of two fits bf16)
+__device__ __forceinline__ bf16x8 fp8x8_bf16(unsigned w0, unsigned w1, float s) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false));
+  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true));
+  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false));
+  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true));
+  return as_bf16x8(o);
+}
+
 // Row n of the segmented weight matrix.
 __device__ __forceinline__ const bf16* brow_ptr(const GemmParams& p, int n) {
   const int s = n / p.seg_rows;

@@ -289,9 +289,11 @@ DFLASH_API dflash_status dflash_verify_greedy(int32_t n_seq, int32_t block_size,
  * A row with a < 2^-64 gets zero codes and scale 1.  Asynchronous on stream; no allocation.
  * dflash_set_lm_head_fp8 makes a handle's dflash_draft_block read the shared lm_head as those codes
  * times their row scales (exact in bf16) instead of the bf16 matrix; NULL for both reverts to bf16.
- * The codes are borrowed like the weights.  Supported by the batch-1 kernel only: a draft call with
- * more than 16 rows (n_seq * block_size) or a hidden size that is not a multiple of 512 up to 2048
- * then returns DFLASH_E_UNSUPPORTED. */
+ * The codes are borrowed like the weights.  Every batch size: at most 16 draft rows
+ * (n_seq * block_size) the independent-wave kernel widens the codes in registers, 17..64 rows the
+ * skinny MFMA kernel, more rows the LDS tile kernels (each 1 KiB LDS-DMA block 16 rows x 64 k of
+ * codes); with at most 16 rows the hidden size must be a multiple of 512 up to 2048, else the call
+ * returns DFLASH_E_UNSUPPORTED. */
 DFLASH_API dflash_status dflash_quantize_fp8_rows(const void* src, int32_t rows, int32_t cols, uint8_t* codes,
                                                   float* row_scales, void* stream);
 DFLASH_API dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t* codes, const float* row_scales);   /* clears an MXFP4 lm_head */
@@ -307,15 +309,16 @@ DFLASH_API dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t*
  * no allocation.  dflash_set_lm_head_mxfp4 makes a handle's dflash_draft_block read the shared
  * lm_head as those codes, each standing for value(code) * 2^(E - 127) (exact in bf16), instead of the
  * bf16 matrix (and instead of an FP8 lm_head, which it clears); NULL for both reverts to bf16.
- * Borrowed like the weights.  Batch-1 kernel only, with the same limits as the FP8 lm_head. */
+ * Borrowed like the weights.  Batch-1 kernel only: a draft call with more than 16 rows, or a
+ * hidden size that is not a multiple of 512 up to 2048, returns DFLASH_E_UNSUPPORTED. */
 DFLASH_API dflash_status dflash_quantize_mxfp4_rows(const void* src, int32_t rows, int32_t cols, uint8_t* codes,
                                                     uint8_t* scales, void* stream);
 DFLASH_API dflash_status dflash_set_lm_head_mxfp4(dflash_handle* h, const uint8_t* codes, const uint8_t* scales);
 /* The same for one layer's MLP: gate_up_codes [2*ffn][d] are the codes of the stacked matrix
  * [W_gate; W_up] (gate rows first), down_codes [d][ffn] those of W_down, each with its row scales
  * (as written by dflash_quantize_fp8_rows); all four NULL reverts the layer to its bf16 matrices.
- * Borrowed like the weights.  Batch-1 kernels only: a draft call with more than 16 rows, or a
- * hidden size above 2048, then returns DFLASH_E_UNSUPPORTED. */
+ * Borrowed like the weights.  Every batch size (the streaming, skinny and tile GEMM kernels all
+ * take E4M3 codes). */
 DFLASH_API dflash_status dflash_set_mlp_fp8(dflash_handle* h, int32_t layer, const uint8_t* gate_up_codes,
                                             const float* gate_up_scales, const uint8_t* down_codes,
                                             const float* down_scales);
@@ -323,20 +326,19 @@ DFLASH_API dflash_status dflash_set_mlp_fp8(dflash_handle* h, int32_t layer, con
  * written by dflash_quantize_mxfp4_rows, with their block scale bytes gate_up_scales [2*ffn][d/32]
  * and down_scales [d][ffn/32].  Replaces the layer's FP8 MLP weights if any (and
  * dflash_set_mlp_fp8 replaces these); all four NULL reverts the layer to bf16.  hidden and ffn must
- * be multiples of 128 (else DFLASH_E_UNSUPPORTED); batch-1 limits as for FP8. */
+ * be multiples of 128 (else DFLASH_E_UNSUPPORTED).  Batch-1 kernels only: a draft call with more
+ * than 16 rows, or a hidden size above 2048, returns DFLASH_E_UNSUPPORTED. */
 DFLASH_API dflash_status dflash_set_mlp_mxfp4(dflash_handle* h, int32_t layer, const uint8_t* gate_up_codes,
                                               const uint8_t* gate_up_scales, const uint8_t* down_codes,
                                               const uint8_t* down_scales);
 /* The same for one layer's attention projections: qkv_codes [n_heads*head_dim + 2*n_kv_heads*head_dim][d]
- * are the codes of the stacked [W_q; W_k; W_v], o_codes [d][n_heads*head_dim] those of W_o.  Batch-1
- * kernels only, as above. */
+ * are the codes of the stacked [W_q; W_k; W_v], o_codes [d][n_heads*head_dim] those of W_o.  Every
+ * batch size. */
 DFLASH_API dflash_status dflash_set_attn_fp8(dflash_handle* h, int32_t layer, const uint8_t* qkv_codes,
                                              const float* qkv_scales, const uint8_t* o_codes, const float* o_scales);
 /* The same for the injection: fc_codes [d][n_taps*target_hidden] (W_fc) and kv_codes
- * [n_layers*2*n_kv_heads*head_dim][d], the stacked [W_k^0; W_v^0; W_k^1; W_v^1; ...].  An injection
- * call whose rows (n_seq * max_new, or max_inject_rows per pass) exceed 16 then returns
- * DFLASH_E_UNSUPPORTED before enqueueing anything: inject long spans (a prefill) with the bf16
- * weights, i.e. before this call or after clearing it (all NULL). */
+ * [n_layers*2*n_kv_heads*head_dim][d], the stacked [W_k^0; W_v^0; W_k^1; W_v^1; ...].  Every
+ * injection size, a prefill included. */
 DFLASH_API dflash_status dflash_set_inject_fp8(dflash_handle* h, const uint8_t* fc_codes, const float* fc_scales,
                                                const uint8_t* kv_codes, const float* kv_scales);
 

@@ -368,12 +368,13 @@ def test_fp8_quantizer_matches_oracle():
 
 
 def test_mid_bf16_fp8_lm_head(H):
-    """Batch 1, K=16 with the FP8 lm_head: codes as the oracle's, logits and top-16 against the
-    oracle run with the dequantised lm_head, top-16 with and without full logits; a call with
-    more than 16 rows is refused; NULL codes restore the bf16 lm_head."""
+    """K=16 with the FP8 lm_head: codes as the oracle's, logits and top-16 against the oracle run
+    with the dequantised lm_head, top-16 with and without full logits, at batch 1 (the
+    independent-wave kernel) and batch 2 (32 rows: the skinny kernel); NULL codes restore the
+    bf16 lm_head."""
     import torch
     case = H.Case(MID, max_seqs=2, max_batch=2, max_inject_rows=64)
-    _prefill(case, [1], [(0, 50)])
+    _prefill(case, [1, 0], [(0, 50), (0, 37)])
     codes, scales = _quantize_on_gpu(case.dev_w["lm_head"])
     oc, osc = O.quantize_fp8_rows(case.W64["lm_head"])
     assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), osc.astype(np.float32))
@@ -383,10 +384,10 @@ def test_mid_bf16_fp8_lm_head(H):
     try:
         res = _check(H, case, [1], [123], mode_names=("viterbi",))
         _same_topk_without_logits(case, [1], [123], res)
+        res = _check(H, case, [1, 0], [123, 5], mode_names=("viterbi",))   # 32 rows
+        _same_topk_without_logits(case, [1, 0], [123, 5], res)
     finally:
         case.W64["lm_head"] = bf16_lm
-    with pytest.raises(B.DflashError):
-        case.draft([1, 0], [123, 5])               # 32 rows
     case.d.dflash_set_lm_head_fp8(None, None)
     res = case.draft([1], [123], logits=True)
     err, _ = H.check_draft(case, [1], [123], res)
@@ -519,21 +520,21 @@ def _fp8_drafter(case, mlp=True, lm_head=True, attn=False, inject=False):
 
 
 def test_mid_bf16_fp8_mlp_and_lm_head(H):
-    """Batch 1, K=16 with FP8 MLP weights in both layers (stacked gate/up through the SwiGLU
-    streaming kernel, down through the k-split one) and the FP8 lm_head, against the oracle run
-    with those matrices dequantised; more than 16 rows are refused; NULL restores bf16."""
+    """K=16 with FP8 MLP weights in both layers and the FP8 lm_head, against the oracle run with
+    those matrices dequantised: batch 1 (stacked gate/up through the SwiGLU streaming kernel, down
+    through the k-split one) and batch 2 (the skinny SwiGLU and k-split kernels); NULL restores
+    bf16."""
     case = H.Case(MID, max_seqs=2, max_batch=2, max_inject_rows=64)
-    _prefill(case, [1], [(0, 50)])
+    _prefill(case, [1, 0], [(0, 50), (0, 61)])
     W8 = _fp8_drafter(case)
     W64 = case.W64
     case.W64 = W8
     try:
         res = _check(H, case, [1], [321], mode_names=("viterbi",))
         _same_topk_without_logits(case, [1], [321], res)
+        _check(H, case, [1, 0], [321, 5], mode_names=("viterbi",))
     finally:
         case.W64 = W64
-    with pytest.raises(B.DflashError):
-        case.draft([1, 0], [321, 5])
     for l in range(MID.n_layers):
         case.d.dflash_set_mlp_fp8(l, None, None, None, None)
     case.d.dflash_set_lm_head_fp8(None, None)
@@ -545,8 +546,9 @@ def test_mid_bf16_fp8_mlp_and_lm_head(H):
 def test_mid_bf16_fp8_every_gemm(H):
     """FP8 codes for every weight GEMM of a batch-1 cycle: injection (fc, stacked K/V), attention
     projections (stacked QKV, O), MLP and lm_head.  A prefill injected with the bf16 weights, then
-    an injection of 5 rows with the FP8 ones, then a draft, each against the oracle run with the
-    same matrices (dequantised where FP8); an injection of more than 16 rows is refused."""
+    an injection of 5 rows with the FP8 ones (the streaming kernels), a draft, and an injection of
+    20 rows (the skinny kernels), each against the oracle run with the same matrices (dequantised
+    where FP8)."""
     case = H.Case(MID, max_seqs=2, max_batch=2, max_inject_rows=64)
     _prefill(case, [1], [(0, 50)])
     W64 = case.W64
@@ -555,15 +557,34 @@ def test_mid_bf16_fp8_every_gemm(H):
         case.inject([1], [np.arange(50, 55)], start_pos=False)
         res = _check(H, case, [1], [77], mode_names=("viterbi",))
         _same_topk_without_logits(case, [1], [77], res)
-        _, _, sl, sb = case.d.kv_views()
-        before = (sl[:2].cpu().tolist(), sb[:2].cpu().tolist())
-        with pytest.raises(B.DflashError) as e:
-            case.inject([1], [np.arange(55, 75)], start_pos=False)
-        assert e.value.status == -3
-        import torch
-        torch.cuda.synchronize()
-        # refused before anything was enqueued: the sequence lengths did not move
-        assert (sl[:2].cpu().tolist(), sb[:2].cpu().tolist()) == before and before[0][1] == 55
+        case.inject([1], [np.arange(55, 75)], start_pos=False)
+        _check(H, case, [1], [78], mode_names=("viterbi",))
+    finally:
+        case.W64 = W64
+
+
+@pytest.mark.parametrize("wide,n_seq", [(False, 5), (True, 10)], ids=["80_rows", "160_rows_wide_mlp"])
+def test_fp8_every_gemm_tiles(H, wide, n_seq):
+    """E4M3 codes for every weight GEMM at more than 64 rows (the LDS-DMA tile kernels, codes
+    staged 16 rows x 64 k per 1 KiB block): 5 sequences at K=16 (80 rows: 128 x 128 layer tiles,
+    the 128 x 128 lm_head tile) and 10 at hidden 1024 / ffn 4608 (160 rows: the 256 x 128 tile for
+    gate/up, the 256 x 256 lm_head tile).  Ragged contexts injected with the bf16 weights, then one
+    injection of up to 12 rows per sequence with the FP8 ones (tile kernels again), then a draft,
+    against the oracle run with the same matrices (dequantised where FP8)."""
+    cfg = MID_WIDE_MLP if wide else MID
+    case = H.Case(cfg, max_seqs=n_seq, max_batch=n_seq, max_inject_rows=128)
+    seq_ids = list(range(n_seq))
+    rng = np.random.default_rng(40 + n_seq)
+    lens = [int(L) for L in rng.integers(20, 90, size=n_seq)]
+    _prefill(case, seq_ids, [(0, L) for L in lens])
+    W64 = case.W64
+    case.W64 = _fp8_drafter(case, mlp=True, lm_head=True, attn=True, inject=True)
+    try:
+        adds = [np.arange(L, L + int(a)) for L, a in zip(lens, rng.integers(1, 13, size=n_seq))]
+        case.inject(seq_ids, adds, start_pos=False)
+        anchors = rng.integers(0, cfg.vocab - 1, size=n_seq).tolist()
+        res = _check(H, case, seq_ids, anchors, mode_names=("viterbi",))
+        _same_topk_without_logits(case, seq_ids, anchors, res)
     finally:
         case.W64 = W64
 

@@ -492,6 +492,70 @@ def test_b1_k16_fp8_attention_and_injection(H, big):
     assert run.d.dflash_get_device_error() == 0
 
 
+def test_b32_k8_fp8_every_gemm(H, big):
+    """Batch 32, K=8 (256 draft rows) with E4M3 codes for every weight GEMM: the layer GEMMs on
+    the 256 x 128 and 128 x 128 tiles, the lm_head on the 256 x 256 tile, and an injection of 4 new
+    rows per sequence (128 rows: W_fc with K = 25600 and the stacked K/V on the tiles); codes
+    checked against the oracle's; K/V and drafts of sampled sequences against the oracle run with
+    the dequantised matrices (the contexts injected before with the bf16 weights)."""
+    import copy
+    import torch
+    cfg = synth.WORKLOADS["b32_k8_conv"]
+    Ls = synth.context_lengths(cfg)
+    sampled = [int(np.argmin(Ls)), int(np.argmax(Ls)), 11]
+    run = Run(H, big, cfg, max_seqs=32, max_batch=32, max_inject_rows=4096, sampled=sampled)
+    ids = list(range(32))
+    run.d.dflash_reset_seqs(run.t(np.arange(32, dtype=np.int32)))
+    run.inject(ids, [_window(int(L), cfg.window) for L in Ls])
+    W8 = copy.copy(big["W64"])
+    W8["layers"] = [dict(lw) for lw in big["W64"]["layers"]]
+    keep = []
+
+    def q(mat, names_rows, layer):
+        """GPU codes of `mat`; each (name, rows) block checked against the oracle's codes of that
+        matrix and replaced in W8 by its dequantised form."""
+        codes, scales = _codes(mat)
+        for name, rows in names_rows:
+            src = big["W64"][name] if layer is None else big["W64"]["layers"][layer][name]
+            oc, osc = O.quantize_fp8_rows(src)
+            assert np.array_equal(codes[rows].cpu().numpy(), oc), (layer, name)
+            assert np.array_equal(scales[rows].cpu().numpy(), osc.astype(np.float32)), (layer, name)
+            if layer is None:
+                W8[name] = O.dequantize_fp8_rows(oc, osc)
+            else:
+                W8["layers"][layer][name] = O.dequantize_fp8_rows(oc, osc)
+        keep.append((codes, scales))
+        return codes, scales
+
+    qw, kvw, ffn = cfg.q_width, cfg.kv_width, cfg.ffn
+    for l, lw in enumerate(big["dev"]["layers"]):
+        q8 = q(torch.cat([lw["wq"], lw["wk"], lw["wv"]]).contiguous(),
+               [("wq", slice(0, qw)), ("wk", slice(qw, qw + kvw)), ("wv", slice(qw + kvw, None))], l)
+        o8 = q(lw["wo"], [("wo", slice(None))], l)
+        run.d.dflash_set_attn_fp8(l, *q8, *o8)
+        gu = q(torch.cat([lw["w_gate"], lw["w_up"]]).contiguous(),
+               [("w_gate", slice(0, ffn)), ("w_up", slice(ffn, None))], l)
+        dn = q(lw["w_down"], [("w_down", slice(None))], l)
+        run.d.dflash_set_mlp_fp8(l, *gu, *dn)
+    fc8 = q(big["dev"]["fc"], [("fc", slice(None))], None)
+    # the stacked injection K/V codes are the per-matrix ones (the quantiser works row by row)
+    kv8 = _codes(torch.cat([t for lw in big["dev"]["layers"] for t in (lw["wk"], lw["wv"])]).contiguous())
+    keep.append(kv8)
+    run.d.dflash_set_inject_fp8(*fc8, *kv8)
+    lm8 = q(big["dev"]["lm_head"], [("lm_head", slice(None))], None)
+    run.d.dflash_set_lm_head_fp8(*lm8)
+    run.W64 = W8
+    run.inject(ids, [np.arange(int(L), int(L) + 4) for L in Ls], start=False)
+    worst, same = H.check_kv(run, sampled, max_positions=64)
+    H.log(f"[b32_k8 fp8] K/V of sampled sequences: worst rel err {worst:.2e}, bit-equal {same:.4f}")
+    assert worst <= 1.0 and same >= 0.99
+    anchors = synth.anchors(cfg).tolist()
+    res = run.draft(ids, anchors)
+    run.own_logit_topk(res)
+    run.compare_sampled(ids, anchors, res)
+    assert run.d.dflash_get_device_error() == 0
+
+
 def test_b1_k16_per_channel_conv(H, big):
     """The b1_k16 drafter with the pages' per-channel conv (a base per channel and a correction per
     16 channels: 20 correction matrices of 256 x 2048): full-window injection and a draft against
