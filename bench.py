@@ -566,7 +566,7 @@ def recorded_traffic(workload):
 # ----------------------------------------------------------------------------- counter passes
 
 COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
-LM_KERNEL = "lmhead_topk_wave<false, false>"   # lm_head + top-16 at batch 1 (independent waves, bf16 weights, no full-logit store)
+LM_KERNEL = "lmhead_topk_wave<false, false, false>"   # lm_head + top-16 at batch 1 (independent waves, bf16 weights, no full-logit store)
 LM_KERNELS = {"b1_k16": LM_KERNEL,
               "b32_k8_conv": "lmhead_topk_tile<"}   # batch 32: 256 x 256 MFMA tiles
 
