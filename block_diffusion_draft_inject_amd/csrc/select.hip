@@ -36,11 +36,12 @@ struct SelWalk {
 };
 
 // The sequential walk over the summed pair scores, in wave 0 of the last workgroup.
-__device__ void sel_walk(const SelectArgs& a, int b, SelWalk& w) {
+// Viterbi sweeps, one per wave: wave 0 the forward sweep (with predecessors), wave 1 the backward
+// sweep; they read only the pair scores, so they run side by side.
+__device__ void sel_sweeps(const SelectArgs& a, SelWalk& w, int role) {
   const int K = a.K, lane = threadIdx.x & 63;
-  // ---- the walk: one wave; lane = 4 * bi + qa holds predecessors a = 4 qa .. 4 qa + 3 of state bi
   const int bi = lane >> 2, qa = lane & 3;
-  if (a.mode == 0) {
+  if (role == 0) {
     // Viterbi as two max-plus sweeps.  Forward: alpha_t(b) = max_a alpha_{t-1}(a) + S_t(a, b),
     // alpha_1(b) = S_1(anchor, b), the predecessor kept per state (ties to the smaller a).
     // Backward: beta_t(a) = max_b S_{t+1}(a, b) + beta_{t+1}(b), beta_{K-1} = 0.  The best path
@@ -78,6 +79,7 @@ __device__ void sel_walk(const SelectArgs& a, int b, SelWalk& w) {
         w.bp1[t - 1][bi] = (unsigned char)ba;
       }
     }
+  } else {
     // backward sweep: lane = 4 ai + qb holds state ai of slot t, successors 4 qb .. 4 qb + 3
     if (lane < TOPK) w.beta[K - 2][lane] = 0.f;
     for (int t = K - 2; t >= 1; --t) {
@@ -92,9 +94,14 @@ __device__ void sel_walk(const SelectArgs& a, int b, SelWalk& w) {
       m = fmaxf(m, quad_perm_f<0x4E>(m));
       if (qa == 0) w.beta[t - 1][bi] = m;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+__device__ void sel_walk(const SelectArgs& a, int b, SelWalk& w) {
+  const int K = a.K, lane = threadIdx.x & 63;
+  // ---- the walk: one wave; lane = 4 * bi + qa holds predecessors a = 4 qa .. 4 qa + 3 of state bi
+  if (a.mode == 0) {
+    // after sel_sweeps (both sweeps in LDS, a workgroup barrier between):
     // best final state (ties to the smaller state), then the path back through the predecessors
     float s1 = lane < TOPK ? w.alpha[K - 2][lane] : NEG_INF;
     int st = lane < TOPK ? lane : TOPK;
@@ -449,6 +456,10 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(SelectArgs a) {
       sw.cid[tid / TOPK][tid % TOPK] = (id < 0 || id >= a.vocab) ? 0 : id;   // recorded in phase (a)
     }
     __syncthreads();
+    if (a.mode == 0) {
+      if (wave < 2) sel_sweeps(a, sw, wave);
+      __syncthreads();
+    }
     if (wave != 0) return;
     sel_walk(a, b, sw);
     return;
@@ -485,6 +496,10 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(SelectArgs a) {
     if (e < ne) sw.S[e / (TOPK * TOPK)][(e % (TOPK * TOPK)) / TOPK][e % TOPK] = sum[i] + lg[i];
   }
   __syncthreads();
+  if (a.mode == 0) {
+    if (wave < 2) sel_sweeps(a, sw, wave);
+    __syncthreads();
+  }
   if (wave != 0) return;
   sel_walk(a, b, sw);
 }
