@@ -406,14 +406,18 @@ __global__ __launch_bounds__(T::NT, OCC) void gemm_tile_partial(GemmParams p) {
 // ...), y = row tile.  After each tile its logits pass through LDS 64 columns at a time; TPR
 // threads share a row (64 / TPR columns each) and keep running top-16 lists: a thread first
 // marks the columns that beat its list's 16th entry, then inserts only those.  The lists of a
-// row are merged at the end into one partial list per (row, workgroup).
+// row are merged at the end into one partial list per (row, workgroup).  The 256-row tile keeps
+// one list per row, on its first 256 threads (one wave per SIMD): a list of n random columns
+// takes about 16 + 16 ln(n / 16) insertions, so splitting a row over two lists adds insertions
+// that the SIMDs, not the waves, pay for (224 rows: 282 -> 269 us; 960 rows: 711 -> 668 us).
 template <class T, int OCC, bool LOGITS>
 __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
   constexpr int BM = T::BMc, BN = T::BNc;
-  constexpr int TPR = T::NT / BM;                 // threads per row
+  constexpr int TPR = BM >= 256 ? 1 : T::NT / BM;   // threads per row in the epilogue
+  constexpr int EPT = BM * TPR;                   // epilogue threads (the first EPT of the workgroup)
   constexpr int CPT = 64 / TPR;                   // columns per thread in a 64-column pass
   using MaskT = typename std::conditional<(CPT > 32), unsigned long long, unsigned>::type;   // one bit per column
-  static_assert(T::NT % BM == 0 && CPT % 4 == 0, "row split");
+  static_assert(T::NT % BM == 0 && EPT <= T::NT && CPT % 4 == 0, "row split");
   static_assert(T::LDS >= BM * 68 * 4, "epilogue buffer must fit in the stages");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS];
   float (*ep)[68] = reinterpret_cast<float (*)[68]>(smem);
@@ -433,9 +437,10 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
   const int cbeg = (int)((long)nblk * blockIdx.x / gridDim.x) * 16;
   const int cend = min((int)((long)nblk * (blockIdx.x + 1) / gridDim.x) * 16, p.N);
   const int nk = p.K / MK;
-  const int lrow = tid / TPR, part = tid % TPR;
+  const bool ep_thr = tid < EPT;
+  const int lrow = ep_thr ? tid / TPR : 0, part = tid % TPR;
   const int my_row = m0 + lrow;
-  const bool row_live = my_row < Mv && (my_row % p.block) != 0;
+  const bool row_live = ep_thr && my_row < Mv && (my_row % p.block) != 0;
   Top16 top;
   top.init();
   for (int n0 = cbeg; n0 < cend; n0 += BN) {
@@ -473,7 +478,7 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
       }
       wait_barrier<0>();
       const int cb = part * CPT;
-      if (LOGITS && my_row < Mv) {
+      if (LOGITS && ep_thr && my_row < Mv) {
         for (int c = 0; c < CPT; ++c)
           if (n0 + q * 64 + cb + c < cend) store_logit(p, my_row, n0 + q * 64 + cb + c, ep[lrow][cb + c]);
       }
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
     }
     wait_barrier<0>();
   }
-  if (part == 0 && my_row < Mv) store_partial(p, my_row, blockIdx.x, top);
+  if (ep_thr && part == 0 && my_row < Mv) store_partial(p, my_row, blockIdx.x, top);
 }
 
 }  // namespace
