@@ -10,8 +10,8 @@
 // chip at small batch; each chunk writes an unnormalised partial output with its running max
 // and sum, and attn_combine merges them (log-sum-exp).
 //
-// bf16 path: Q K^T and P V on v_mfma_f32_16x16x32_bf16 (each wave owns 16 query rows); Q and P
-// enter as sums of two bf16 terms (hi + lo), K and V are the bf16 cache values, running sums
+// bf16 path: K Q^T and V^T P^T on v_mfma_f32_16x16x32_bf16 (each wave owns 16 query rows); Q and
+// P enter as sums of two bf16 terms (hi + lo), K and V are the bf16 cache values, running sums
 // stay fp32.  fp32 path: VALU.
 #include "rowops.h"
 
@@ -31,11 +31,17 @@ __device__ __forceinline__ bf16x8 bits_bf16x8(u32x4 v) { return __builtin_bit_ca
 constexpr int MK = 64;          // keys per sub-tile
 constexpr int MDH = 128;        // head_dim of the MFMA path
 
+// Each wave computes S^T = K Q^T for its 16 query rows, i.e. the MFMA takes the keys as its A
+// operand and the queries as B: lane (li, kg) then holds the scores of query row li for the keys
+// 16 f + 4 kg + r of each 16-key fragment f.  A row's softmax is in-lane plus two exchanges
+// across the lane groups kg, and P goes straight from registers into O^T += V^T P^T as the B
+// operand (each lane's eight k-slots of a 32-key block are the keys it already holds, and the
+// V^T operand is read from LDS in the same key order), so P never passes through LDS; O^T leaves
+// lane (li, kg) with dims 16 n + 4 kg + r of query row li, scaled by that row's own softmax
+// factor.
 __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sk[MK][MDH + 8];
   __shared__ __attribute__((aligned(16))) bf16 svt[MDH][MK + 8];
-  __shared__ __attribute__((aligned(16))) bf16 sp[4][16][MK + 8];
-  __shared__ __attribute__((aligned(16))) bf16 sl[4][16][MK + 8];
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, li = lane & 15, kg = lane >> 4;
   const int K = a.K, G = a.nh / a.nkv, R = G * K;
@@ -45,11 +51,15 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
   const int k_begin = min(c * ck, n_keys), k_end = min(k_begin + ck, n_keys);
   const size_t pidx = ((size_t)b * a.nkv + kvh) * a.chunks + c;
   const bf16* q = reinterpret_cast<const bf16*>(a.q);
-  const bf16* kb = reinterpret_cast<const bf16*>(a.kb);
-  const bf16* vb = reinterpret_cast<const bf16*>(a.vb);
-  const bf16* kc = reinterpret_cast<const bf16*>(a.kcache);
-  const bf16* vc = reinterpret_cast<const bf16*>(a.vcache);
-  // this wave's 16 query rows as MFMA A fragments (row = 16w + li, dims ks*32 + kg*8 .. +8),
+  // this (layer, sequence, KV head)'s rings, and its block keys (key n_ctx + t at row t * nkv)
+  const size_t cache_base = (((size_t)a.layer * a.max_seqs + ctx.sid) * a.nkv + kvh) * (size_t)a.window * MDH;
+  const bf16* kc = reinterpret_cast<const bf16*>(a.kcache) + cache_base;
+  const bf16* vc = reinterpret_cast<const bf16*>(a.vcache) + cache_base;
+  const size_t blk_base = ((size_t)b * K * a.nkv + kvh) * MDH;
+  const bf16* kb = reinterpret_cast<const bf16*>(a.kb) + blk_base;
+  const bf16* vb = reinterpret_cast<const bf16*>(a.vb) + blk_base;
+  const int blk_stride = a.nkv * MDH;
+  // this wave's 16 query rows as the B operand of S^T (query 16w + li, dims ks*32 + kg*8 .. +8),
   // hi and lo planes
   const int qrow = 16 * w + li;
   u32x4 qa[4], ql[4];
@@ -62,36 +72,37 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
       ql[ks] = (qrow < R) ? *reinterpret_cast<const u32x4*>(qp + a.q_plane + ks * 32 + kg * 8) : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  float m[4], l[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) { m[j] = NEG_INF; l[j] = 0.f; }
-  f32x4 acc[8];
+  float m = NEG_INF, l = 0.f;   // query row 16w + li (the same in its four lanes)
+  f32x4 acc[8];                 // O^T: acc[n][r] = O[row 16w + li][dim 16n + 4kg + r]
 #pragma unroll
   for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const size_t cache_base = (((size_t)a.layer * a.max_seqs + ctx.sid) * a.nkv + kvh) * (size_t)a.window;
-  // This thread's sixteen-byte pieces of the sub-tile at j0 (keys past the chunk read the
-  // chunk's last key, then count as zero; straight-line loads, so the compiler's wait for them
-  // sits at their first use, not at a branch join):
+  // This thread's sixteen-byte pieces of the sub-tile at j0.  Keys past the chunk read the
+  // chunk's last key and are used as loaded: their scores are set to -inf, so P is zero there
+  // and the (finite) values drop out.  Nothing touches a loaded register before its LDS store in
+  // the next iteration, so the loads stay in flight across this sub-tile's math (a select on a
+  // loaded value would make the compiler wait for it right there):
   //   K: piece e = tid + 256 it is part e % 16 of key e / 16 (16 lanes read one 256-byte row);
   //   V: piece pair u = tid + 256 it (it < 2) is part u / 32 of keys 2 (u % 32) and 2 (u % 32) + 1,
   //      so that the transposed store writes (key, key + 1) pairs as 32-bit words, a wave's 64
   //      lanes on 64 distinct banks.
-  auto key_off = [&](int gk, int part, bool& ctxk) {
-    ctxk = gk < ctx.n_ctx;
-    return ctxk ? (cache_base + (ctx.slot0 + gk) % a.window) * MDH + part * 8
-                : ((size_t)(b * K + gk - ctx.n_ctx) * a.nkv + kvh) * MDH + part * 8;
+  // A context key j0 + key sits in ring slot s0 + key (mod window), s0 the sub-tile's first slot;
+  // s0 < window and j0 + key < n_ctx <= window, so one subtraction reduces it.
+  auto key_off = [&](int j0, int s0, int key, int part, bool& ctxk) {
+    ctxk = j0 + key < ctx.n_ctx;
+    int s = s0 + key;
+    s = s >= a.window ? s - a.window : s;
+    return ctxk ? s * MDH + part * 8 : (j0 + key - ctx.n_ctx) * blk_stride + part * 8;
   };
   auto load_kv = [&](int j0, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
     const int nk = min(MK, k_end - j0);
-    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int s0 = (ctx.slot0 + j0) % a.window;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int e = tid + it * 256;
       const int key = e >> 4, part = e & 15;
       bool ctxk;
-      const size_t off = key_off(j0 + min(key, nk - 1), part, ctxk);
-      const u32x4 kx = *reinterpret_cast<const u32x4*>((ctxk ? kc : kb) + off);
-      kr[it] = key < nk ? kx : z;
+      const int off = key_off(j0, s0, min(key, nk - 1), part, ctxk);
+      kr[it] = *reinterpret_cast<const u32x4*>((ctxk ? kc : kb) + off);
     }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -100,9 +111,8 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         bool ctxk;
-        const size_t off = key_off(j0 + min(k0 + h, nk - 1), part, ctxk);
-        const u32x4 vx = *reinterpret_cast<const u32x4*>((ctxk ? vc : vb) + off);
-        vr[2 * it + h] = k0 + h < nk ? vx : z;
+        const int off = key_off(j0, s0, min(k0 + h, nk - 1), part, ctxk);
+        vr[2 * it + h] = *reinterpret_cast<const u32x4*>((ctxk ? vc : vb) + off);
       }
     }
   };
@@ -113,8 +123,8 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
   // loads, issued before this sub-tile's math, stay in flight across them.
   for (int j0 = k_begin; j0 < k_end; j0 += MK) {
     const int nk = min(MK, k_end - j0);
-    lds_barrier();   // every wave is done with the previous sub-tile's K, V and P
-    // K rows -> sk[key][dim]; V rows -> svt[dim][key] (transposed for the P V operand)
+    lds_barrier();   // every wave is done with the previous sub-tile's K and V
+    // K rows -> sk[key][dim]; V rows -> svt[dim][key] (transposed for the V^T operand)
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int e = tid + it * 256;
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
     }
     lds_barrier();
     if (j0 + MK < k_end) load_kv(j0 + MK, kr, vr);
-    // S = Q K^T for 16 rows x 64 keys (4 key fragments)
+    // S^T = K Q^T: s[f][r] = score of query row li and key 16f + 4kg + r
     f32x4 s[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -141,75 +151,70 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sk[16 * f + li][ks * 32 + kg * 8]);
-        s[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_bf16x8(qa[ks]), kf, s[f], 0, 0, 0);
-        s[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_bf16x8(ql[ks]), kf, s[f], 0, 0, 0);
+        s[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, bits_bf16x8(qa[ks]), s[f], 0, 0, 0);
+        s[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, bits_bf16x8(ql[ks]), s[f], 0, 0, 0);
       }
     }
-    // online softmax; lane holds rows 4*kg + j, key 16f + li
-    float alpha[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float mx = NEG_INF;
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const float v = (16 * f + li < nk) ? s[f][j] * a.scale : NEG_INF;
-        s[f][j] = v;
-        mx = fmaxf(mx, v);
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-      const float mn = fmaxf(m[j], mx);
-      alpha[j] = (m[j] == NEG_INF) ? 0.f : __expf(m[j] - mn);
-      float sum = 0.f;
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const float p = (s[f][j] == NEG_INF) ? 0.f : __expf(s[f][j] - mn);
-        s[f][j] = p;
-        sum += p;
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
-      l[j] = l[j] * alpha[j] + sum;
-      m[j] = mn;
-    }
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[n][j] *= alpha[j];
-    // P is split into two bf16 terms, P = hi + lo with hi = bf16(P), lo = bf16(P - hi), and both
-    // are multiplied with V: the product then carries ~16 mantissa bits of P instead of 8.
+    // online softmax of the row: its 64 keys are 16 per lane in the lanes li + 16 kg
+    float mx = NEG_INF;
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16 hi = f2bf(s[f][j]);
-        sp[w][4 * kg + j][16 * f + li] = hi;
-        sl[w][4 * kg + j][16 * f + li] = f2bf(s[f][j] - bf2f(hi));
+      for (int r = 0; r < 4; ++r) {
+        const float v = (16 * f + 4 * kg + r < nk) ? s[f][r] * a.scale : NEG_INF;
+        s[f][r] = v;
+        mx = fmaxf(mx, v);
       }
-    lds_barrier();
-    // O += P V : A = P [16 rows][64 keys], B = V^T rows (dims) x keys
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);
+    const float alpha = (m == NEG_INF) ? 0.f : __expf(m - mn);
+    float sum = 0.f;
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = (s[f][r] == NEG_INF) ? 0.f : __expf(s[f][r] - mn);
+        s[f][r] = p;
+        sum += p;
+      }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    l = l * alpha + sum;
+    m = mn;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+    // O^T += V^T P^T over two 32-key blocks: the lane's k-slots 0-3 are keys 32 k2 + 4 kg + r
+    // (fragment 2 k2), slots 4-7 keys 32 k2 + 16 + 4 kg + r (fragment 2 k2 + 1).  P is split
+    // into two bf16 terms, P = hi + lo with hi = bf16(P), lo = bf16(P - hi), and both are
+    // multiplied with V: the product then carries ~16 mantissa bits of P instead of 8.
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
-      const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&sp[w][li][k2 * 32 + kg * 8]);
-      const bf16x8 pl = *reinterpret_cast<const bf16x8*>(&sl[w][li][k2 * 32 + kg * 8]);
+      bf16x8 ph, pl;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float p = s[2 * k2 + r / 4][r % 4];
+        const bf16 hi = f2bf(p);
+        ph[r] = __builtin_bit_cast(__bf16, hi);
+        pl[r] = __builtin_bit_cast(__bf16, f2bf(p - bf2f(hi)));
+      }
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&svt[16 * n + li][k2 * 32 + kg * 8]);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vf, acc[n], 0, 0, 0);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf, acc[n], 0, 0, 0);
+        const uint2 v0 = *reinterpret_cast<const uint2*>(&svt[16 * n + li][32 * k2 + 4 * kg]);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(&svt[16 * n + li][32 * k2 + 16 + 4 * kg]);
+        const bf16x8 vf = bits_bf16x8(u32x4{v0.x, v0.y, v1.x, v1.y});
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph, acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl, acc[n], 0, 0, 0);
       }
     }
   }
+  if (qrow < R) {
+    float* op = a.o_part + (pidx * R + qrow) * MDH;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 16 * w + 4 * kg + j;
-    if (r >= R) continue;
-    float* op = a.o_part + (pidx * R + r) * MDH;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) op[16 * n + li] = acc[n][j];
-    if (li == 0) {
-      a.m_part[pidx * R + r] = m[j];
-      a.l_part[pidx * R + r] = l[j];
+    for (int n = 0; n < 8; ++n) *reinterpret_cast<f32x4*>(op + 16 * n + 4 * kg) = acc[n];
+    if (kg == 0) {
+      a.m_part[pidx * R + qrow] = m;
+      a.l_part[pidx * R + qrow] = l;
     }
   }
 }
