@@ -62,6 +62,7 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
   // this wave's 16 query rows as the B operand of S^T (query 16w + li, dims ks*32 + kg*8 .. +8),
   // hi and lo planes
   const int qrow = 16 * w + li;
+  const bool has_rows = __builtin_amdgcn_readfirstlane(16 * w) < R;   // wave-uniform
   u32x4 qa[4], ql[4];
   {
     const int g = qrow / K, t = qrow % K;
@@ -143,6 +144,8 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma(AttnArgs a) {
     }
     lds_barrier();
     if (j0 + MK < k_end) load_kv(j0 + MK, kr, vr);
+    // a wave past the R query rows (R = 32 at block size 8) only loads and stores K and V
+    if (!has_rows) continue;
     // S^T = K Q^T: s[f][r] = score of query row li and key 16f + 4kg + r
     f32x4 s[4];
 #pragma unroll
@@ -329,74 +332,82 @@ __global__ __launch_bounds__(256) void attn_chunk_valu(AttnArgs a) {
 }
 
 // Merge the chunks of one query row: o = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c.
-// One workgroup of 128 threads per (row, KV head, sequence); chunk maxima and sums are read by
-// one thread each, and every thread then issues its chunk loads eight at a time.
-template <typename T>
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
-  __shared__ float wgt[256];
-  __shared__ float red[2];
-  __shared__ float s_den;
-  const int r = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+// One wave per (row, KV head, sequence), blockDim / 64 rows per workgroup (four, or one when
+// there are few rows, so that they spread over more CUs) and no workgroup barrier:
+// lane j reads the maxima and sums of chunks j, j + 64, ... (M and the denominator are wave
+// reductions), the chunk weights go through the wave's own LDS row, and lane j accumulates dims
+// j and j + 64 over the chunks in order, the loads of CB chunks at a time (8 when there are at
+// most 8 chunks, else 32: the 17 chunks of a batch-1 pass in one round trip, not three).
+template <typename T, int CB>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  constexpr int CMAX = 256;   // chunks per (sequence, KV head), at most
+  __shared__ float wts[4][CMAX];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int kvh = blockIdx.y, b = blockIdx.z;
   const int K = a.K, dh = a.dh, G = a.nh / a.nkv, R = G * K;
+  const int r = blockIdx.x * (blockDim.x >> 6) + wv;
+  if (r >= R) return;   // the whole wave: the reductions below need all 64 lanes
   const size_t base = ((size_t)b * a.nkv + kvh) * a.chunks;
   const int nc = a.chunks;
-  // the first CB chunks' partial outputs are loaded in the same burst as the maxima and sums
-  constexpr int CB = 32;
-  const size_t cstride = (size_t)R * dh;
-  const float* op = a.o_part + (base * R + r) * dh + min(tid, dh - 1);
-  float x[CB];
+  float mc[CMAX / 64], lc[CMAX / 64];
+  float M = NEG_INF;
 #pragma unroll
-  for (int u = 0; u < CB; ++u) x[u] = op[(size_t)min(u, nc - 1) * cstride];
-  float mc[2], lc[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = min(tid + 128 * u, nc - 1);
-    mc[u] = a.m_part[(base + c) * R + r];
-    lc[u] = a.l_part[(base + c) * R + r];
-    if (tid + 128 * u >= nc) { mc[u] = NEG_INF; lc[u] = 0.f; }
+  for (int g = 0; g < CMAX / 64; ++g) {
+    const int c = g * 64 + lane;
+    mc[g] = c < nc ? a.m_part[(base + c) * R + r] : NEG_INF;
+    lc[g] = c < nc ? a.l_part[(base + c) * R + r] : 0.f;
+    M = fmaxf(M, mc[g]);
   }
-  float M = wave_max(fmaxf(mc[0], mc[1]));
-  if ((tid & 63) == 0) red[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(red[0], red[1]);
+  M = wave_max(M);
   float den = 0.f;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + 128 * u;
-    const float w = (mc[u] == NEG_INF) ? 0.f : __expf(mc[u] - M);
-    if (c < nc) wgt[c] = w;
-    den += w * lc[u];
+  for (int g = 0; g < CMAX / 64; ++g) {
+    const float w = (mc[g] == NEG_INF) ? 0.f : __expf(mc[g] - M);
+    wts[wv][g * 64 + lane] = w;
+    den += w * lc[g];
   }
   den = wave_sum(den);
-  __syncthreads();
-  if ((tid & 63) == 0) red[tid >> 6] = den;
-  __syncthreads();
-  if (tid == 0) s_den = red[0] + red[1];
-  __syncthreads();
-  if (tid >= dh) return;
-  float num = 0.f;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const size_t cstride = (size_t)R * dh;
+  const float* op = a.o_part + (base * R + r) * dh;
+  const int d0 = min(lane, dh - 1), d1 = min(lane + 64, dh - 1);
+  float n0 = 0.f, n1 = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += CB) {
+    float x0[CB], x1[CB];
 #pragma unroll
-  for (int u = 0; u < CB; ++u) num += (u < nc) ? wgt[u] * x[u] : 0.f;
-  for (int c0 = CB; c0 < nc; c0 += 8) {
-    float y[8];
+    for (int u = 0; u < CB; ++u) {
+      const size_t co = (size_t)min(c0 + u, nc - 1) * cstride;
+      x0[u] = op[co + d0];
+      x1[u] = op[co + d1];
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) y[u] = (c0 + u < nc) ? op[(size_t)(c0 + u) * cstride] : 0.f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) num += (c0 + u < nc) ? wgt[c0 + u] * y[u] : 0.f;
+    for (int u = 0; u < CB; ++u) {
+      const float w = c0 + u < nc ? wts[wv][c0 + u] : 0.f;
+      n0 += w * x0[u];
+      n1 += w * x1[u];
+    }
   }
   const int g = r / K, t = r % K, h = kvh * G + g;
-  st_act(reinterpret_cast<T*>(a.o), ((size_t)(b * K + t) * a.nh + h) * dh + tid, a.o_plane, num / s_den);
+  const size_t orow = ((size_t)(b * K + t) * a.nh + h) * dh;
+  if (lane < dh) st_act(reinterpret_cast<T*>(a.o), orow + lane, a.o_plane, n0 / den);
+  if (lane + 64 < dh) st_act(reinterpret_cast<T*>(a.o), orow + lane + 64, a.o_plane, n1 / den);
 }
 
 hipError_t launch_attention(bool bf, const AttnArgs& a, int n_seq, hipStream_t st) {
   const int R = (a.nh / a.nkv) * a.K;
-  const dim3 g1(a.chunks, a.nkv, n_seq), g2(R, a.nkv, n_seq);
+  if (a.chunks > 256 || a.dh > 128) return hipErrorInvalidValue;
+  const int rpw = (long)R * a.nkv * n_seq >= 1024 ? 4 : 1;   // combine: rows (waves) per workgroup
+  const dim3 g1(a.chunks, a.nkv, n_seq), g2((R + rpw - 1) / rpw, a.nkv, n_seq);
   if (bf) {
     hipLaunchKernelGGL(attn_chunk_mfma, g1, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(attn_combine_kernel<bf16>, g2, dim3(128), 0, st, a);
+    if (a.chunks <= 8) hipLaunchKernelGGL((attn_combine_kernel<bf16, 8>), g2, dim3(64 * rpw), 0, st, a);
+    else hipLaunchKernelGGL((attn_combine_kernel<bf16, 32>), g2, dim3(64 * rpw), 0, st, a);
   } else {
     hipLaunchKernelGGL(attn_chunk_valu, g1, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(attn_combine_kernel<float>, g2, dim3(128), 0, st, a);
+    if (a.chunks <= 8) hipLaunchKernelGGL((attn_combine_kernel<float, 8>), g2, dim3(64 * rpw), 0, st, a);
+    else hipLaunchKernelGGL((attn_combine_kernel<float, 32>), g2, dim3(64 * rpw), 0, st, a);
   }
   return hipGetLastError();
 }
