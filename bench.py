@@ -817,6 +817,18 @@ def main():
             "lm_head_gbps": round(lm8_bytes / (rb["lm_head_ms"] * 1e-3) / 1e9, 1)}
         del rb["cycle"]
         _release(torch)
+        torch.cuda.empty_cache()
+        rb = run_workload(synth.WORKLOADS["b32_k8_conv"], args.steps, args.warmup, torch, mxfp4_lm_head=True,
+                          mxfp4_mlp=True)
+        out["b32_mxfp4_lm_head_mlp"] = {
+            "workload": "b32_k8_conv with MXFP4 codes (32-weight blocks, E8M0 scales) for the lm_head and every "
+                        "layer's MLP (weight-only; activations bf16): above 16 rows these run on the skinny "
+                        "kernels (codes streamed into registers over row tiles of 64 rows), the other GEMMs on the "
+                        "bf16 tiles",
+            "blocks_per_s": round(rb["blocks_per_s"], 1), "draft_tokens_per_s": round(rb["draft_tokens_per_s"], 1),
+            "ms_per_step": round(rb["ms_per_step"], 4), "lm_head_avg_ms": round(rb["lm_head_ms"], 5)}
+        del rb["cycle"]
+        _release(torch)
     if not args.no_pc:
         torch.cuda.empty_cache()
         cpc = synth.WORKLOADS["b1_k16"].replace(conv_group=16, name="b1_k16_pc16")

@@ -126,6 +126,10 @@ size_t draft_part_floats(const dflash_config* c, int n_seq) {
   if (b && M <= 64) upd(GEMM_SWIGLU, 2 * c->ffn, d);
   else upd(GEMM_PARTIAL, 2 * c->ffn, d);
   upd(GEMM_PARTIAL, d, c->ffn);
+  if (b) {   // an MXFP4 down projection runs on the skinny kernels at any row count
+    size_t f = gemm_part_floats(gemm_plan_skinny(GEMM_PARTIAL, M, d, c->ffn), GEMM_PARTIAL, M, d);
+    if (f > mx) mx = f;
+  }
   if (per_channel_conv(c)) upd(GEMM_PARTIAL, 2 * d / c->conv_group, d);   // conv corrections
   if (!b) {
     size_t f = (size_t)M * c->vocab;   // fp32 path keeps full logits
@@ -144,9 +148,13 @@ size_t inject_part_floats(const dflash_config* c, int rows) {
   return a > e ? a : e;
 }
 
+// partial top-16 lists per row: the most any top-16 kernel may write (a quantised lm_head can
+// run on the skinny kernels instead of the plain plan's)
 int topk_groups(const dflash_config* c, int n_seq) {
-  GemmPlan pl = gemm_plan(true, GEMM_TOPK, n_seq * c->block_size, c->vocab, c->hidden);
-  return pl.groups;
+  const int M = n_seq * c->block_size;
+  const int g0 = gemm_plan(true, GEMM_TOPK, M, c->vocab, c->hidden).groups;
+  const int g1 = gemm_plan_skinny(GEMM_TOPK, M, c->vocab, c->hidden).groups;
+  return g0 > g1 ? g0 : g1;
 }
 
 WsLayout ws_layout(const dflash_config* c, int max_batch, int max_inject_rows, int max_seqs) {
@@ -311,22 +319,14 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
   const dflash_config* c = &H->cfg;
   const bool b = bf(c);
   const int K = c->block_size, d = c->hidden, M = n_seq * K;
-  // E4M3 weights run in every GEMM kernel but the batch-1 streaming top-16 one (the lm_head of
-  // at most 16 rows takes the independent-wave kernel, hidden a multiple of 512 up to 2048);
-  // MXFP4 weights only in the batch-1 streaming and independent-wave kernels
-  bool any_mlp_fp4 = false;
-  for (const auto& m : H->mlp_q) any_mlp_fp4 |= m.gu_b != nullptr;
-  if (any_mlp_fp4 && (gemm_plan(true, GEMM_SWIGLU, M, 2 * c->ffn, d).kind != 3 ||
-                      gemm_plan(true, GEMM_PARTIAL, M, d, c->ffn).kind != 3))
-    return fail(DFLASH_E_UNSUPPORTED, "MXFP4 MLP weights take at most 16 draft rows (n_seq * block_size = %d) "
-                "and a hidden size of at most 2048", M);
-  const int lm_kind = gemm_plan(true, GEMM_TOPK, M, c->vocab, d).kind;
-  if (H->lm_fp4 && lm_kind != 4)
-    return fail(DFLASH_E_UNSUPPORTED, "the MXFP4 lm_head takes at most 16 draft rows (n_seq * block_size = %d) "
-                "and a hidden size that is a multiple of 512 up to 2048", M);
-  if (H->lm_fp8 && lm_kind == 3)
-    return fail(DFLASH_E_UNSUPPORTED, "with at most 16 draft rows the FP8 lm_head needs a hidden size that is a "
-                "multiple of 512 up to 2048 (n_seq * block_size = %d)", M);
+  // E4M3 and MXFP4 weights: each GEMM takes the plain plan's kernel when that kernel takes the
+  // format, else the skinny kernels (gemm_plan_wf).  A skinny top-16 pass keeps one work counter
+  // per row tile of 64 rows.
+  const int lm_wf = H->lm_fp4 ? 2 : (H->lm_fp8 ? 1 : 0);
+  const GemmPlan lm_plan = gemm_plan_wf(b, b ? GEMM_TOPK : GEMM_PARTIAL, M, c->vocab, d, lm_wf);
+  if (b && lm_plan.kind == 0 && (int)lm_plan.grid.y > NCOUNTERS)
+    return fail(DFLASH_E_UNSUPPORTED, "a quantised lm_head on the skinny kernels takes at most %d draft rows "
+                "(n_seq * block_size = %d)", NCOUNTERS * 64, M);
   const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
   float* part = wsp<float>(ws, W.part);
   SeqCtx* ctx = wsp<SeqCtx>(ws, W.ctx);
@@ -528,8 +528,10 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
       gg.row_scale = mq->gu_s;
       gg.blk_scale = mq->gu_b;
     }
-    if (b && M <= 64) {
-      GemmPlan pg = gemm_plan(b, GEMM_SWIGLU, M, 2 * c->ffn, d);
+    const int mwf = mq ? (mq->gu_b ? 2 : 1) : 0;
+    if (b && (M <= 64 || mwf == 2)) {   // the SwiGLU epilogue inside the GEMM (MXFP4: skinny at any M)
+      GemmPlan pg = M <= 64 ? gemm_plan_wf(b, GEMM_SWIGLU, M, 2 * c->ffn, d, mwf)
+                            : gemm_plan_skinny(GEMM_SWIGLU, M, 2 * c->ffn, d);
       HIP_TRY(gemm_launch(b, pg, GEMM_SWIGLU, gg, st));
     } else {
       gg.half = 0;
@@ -550,7 +552,7 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
       gd.row_scale = mq->dn_s;
       gd.blk_scale = mq->dn_b;
     }
-    GemmPlan pd = gemm_plan(b, GEMM_PARTIAL, M, d, c->ffn);
+    GemmPlan pd = gemm_plan_wf(b, GEMM_PARTIAL, M, d, c->ffn, mwf);
     HIP_TRY(gemm_launch(b, pd, GEMM_PARTIAL, gd, st));
     RowArgs rm = ra;
     rm.h_in = hB;
@@ -606,14 +608,12 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
     gl.tk_id = wsp<int>(ws, W.tk_id);
     gl.logits = logits;
     gl.counter = counters;
-    GemmPlan pl = gemm_plan(b, GEMM_TOPK, M, c->vocab, d);
-    if (H->lm_fp4) {
-      // MXFP4 lm_head: only the independent-wave kernel (<= 16 rows) takes it (checked up front)
+    const GemmPlan& pl = lm_plan;
+    if (H->lm_fp4) {   // MXFP4 lm_head: the independent-wave kernel (<= 16 rows) or the skinny ones
       gl.seg[0] = H->lm_fp4;
       gl.ldb = d / 2;                 // bytes per weight row
       gl.blk_scale = H->lm_fp4_scale;
-    } else if (H->lm_fp8) {
-      // FP8 lm_head: every top-16 kernel but the batch-1 streaming one (checked up front)
+    } else if (H->lm_fp8) {   // FP8 lm_head: every top-16 kernel but the batch-1 streaming one
       gl.seg[0] = H->lm_fp8;
       gl.ldb = d;                     // bytes per weight row
       gl.row_scale = H->lm_fp8_scale;

@@ -50,21 +50,30 @@ struct SkinnyBatch {
   u32x4 ah[2][MT][2];   // activation hi plane
   u32x4 al[2][MT][2];   // activation lo plane
   u32x4 b[2][NF][2];
+  unsigned e[2][NF];    // MXFP4: the scale byte of the lane's block, kept as loaded
 };
 
 // Loads chunks c and c + cstep; both indices are clamped to clast so the loads are always
 // issued (no branch around them: the compiler then keeps exact vmcnt counts and the next
-// batch stays in flight while the current one is multiplied).  F8: weight rows of E4M3 codes,
-// one 16-byte load per lane and chunk (k = 16 kg .. 16 kg + 15, the same k as the two bf16 halves).
-template <int MT, int NF, bool F8 = false>
+// batch stays in flight while the current one is multiplied).  Weight formats WF: 0 bf16;
+// 1 E4M3 codes, one 16-byte load per lane and chunk (k = 16 kg .. 16 kg + 15, the same k as the
+// two bf16 halves); 2 MXFP4 codes, one 8-byte load per lane and chunk (the same 16 k, element 2j
+// in the low nibble of byte j) and the scale byte of the 32-k block holding them (srow).
+template <int MT, int NF, int WF = 0>
 __device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NF>& x, const bf16* const (&arow)[MT], size_t a_plane,
-                                            const void* const (&brow)[NF], int kg, int c, int cstep, int clast) {
+                                            const void* const (&brow)[NF], const unsigned char* const (&srow)[NF],
+                                            int kg, int c, int cstep, int clast) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int k = min(c + u * cstep, clast) * 64 + kg * 16;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      if constexpr (F8) {
+      if constexpr (WF == 2) {
+        const uint2 q = *reinterpret_cast<const uint2*>(reinterpret_cast<const unsigned char*>(brow[f]) + k / 2);
+        x.b[u][f][0][0] = q.x;
+        x.b[u][f][0][1] = q.y;
+        x.e[u][f] = srow[f][k / 32];
+      } else if constexpr (WF == 1) {
         x.b[u][f][0] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(brow[f]) + k);
       } else {
         const u32x4* q = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(brow[f]) + k);
@@ -84,7 +93,7 @@ __device__ __forceinline__ void skinny_load(SkinnyBatch<MT, NF>& x, const bf16* 
   }
 }
 
-template <int MT, int NF, bool F8 = false>
+template <int MT, int NF, int WF = 0>
 __device__ __forceinline__ void skinny_mma(const SkinnyBatch<MT, NF>& x, bool two, const float (&bs)[NF],
                                            f32x4 (&acc)[MT][NF]) {
 #pragma unroll
@@ -94,7 +103,10 @@ __device__ __forceinline__ void skinny_mma(const SkinnyBatch<MT, NF>& x, bool tw
     for (int f = 0; f < NF; ++f)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const bf16x8 w = F8 ? fp8x8_bf16(x.b[u][f][0][2 * h], x.b[u][f][0][2 * h + 1], bs[f]) : as_bf16x8(x.b[u][f][h]);
+        bf16x8 w;
+        if constexpr (WF == 2) w = fp4x8_bf16(x.b[u][f][0][h], __uint_as_float(x.e[u][f] << 23));   // 2^(E - 127)
+        else if constexpr (WF == 1) w = fp8x8_bf16(x.b[u][f][0][2 * h], x.b[u][f][0][2 * h + 1], bs[f]);
+        else w = as_bf16x8(x.b[u][f][h]);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.ah[u][m][h]), w, acc[m][f], 0, 0, 0);
@@ -104,44 +116,49 @@ __device__ __forceinline__ void skinny_mma(const SkinnyBatch<MT, NF>& x, bool tw
   }
 }
 
-// bs: F8, the row scale of each weight row (unused for bf16 weights)
-template <int MT, int NF, bool F8 = false>
+// bs: E4M3, the row scale of each weight row; srow: MXFP4, each weight row's scale bytes
+template <int MT, int NF, int WF = 0>
 __device__ __forceinline__ void skinny_acc(const bf16* const (&arow)[MT], size_t a_plane, const void* const (&brow)[NF],
-                                           const float (&bs)[NF], int kg, int c0, int c1, int cstep,
-                                           f32x4 (&acc)[MT][NF]) {
+                                           const unsigned char* const (&srow)[NF], const float (&bs)[NF], int kg,
+                                           int c0, int c1, int cstep, f32x4 (&acc)[MT][NF]) {
   if (c0 >= c1) return;
   const int clast = c0 + (c1 - 1 - c0) / cstep * cstep;   // last chunk this wave owns
   SkinnyBatch<MT, NF> x, y;
   int c = c0;
-  skinny_load<MT, NF, F8>(x, arow, a_plane, brow, kg, c, cstep, clast);
+  skinny_load<MT, NF, WF>(x, arow, a_plane, brow, srow, kg, c, cstep, clast);
   while (true) {
     const int cy = c + 2 * cstep;
-    skinny_load<MT, NF, F8>(y, arow, a_plane, brow, kg, cy, cstep, clast);
-    skinny_mma<MT, NF, F8>(x, c + cstep < c1, bs, acc);
+    skinny_load<MT, NF, WF>(y, arow, a_plane, brow, srow, kg, cy, cstep, clast);
+    skinny_mma<MT, NF, WF>(x, c + cstep < c1, bs, acc);
     if (cy >= c1) break;
     const int cx = cy + 2 * cstep;
-    skinny_load<MT, NF, F8>(x, arow, a_plane, brow, kg, cx, cstep, clast);
-    skinny_mma<MT, NF, F8>(y, cy + cstep < c1, bs, acc);
+    skinny_load<MT, NF, WF>(x, arow, a_plane, brow, srow, kg, cx, cstep, clast);
+    skinny_mma<MT, NF, WF>(y, cy + cstep < c1, bs, acc);
     if (cx >= c1) break;
     c = cx;
   }
 }
 
-// weight row n (bf16 segments, or one segment of E4M3 codes) and its scale
-template <bool F8>
-__device__ __forceinline__ const void* wrow_ptr(const GemmParams& p, int n, float& scale) {
-  if constexpr (F8) {
+// weight row n (bf16 segments, or one segment of E4M3 or MXFP4 codes, ldb bytes a row) and its
+// scale (E4M3) or scale bytes (MXFP4: K / 32 a row)
+template <int WF>
+__device__ __forceinline__ const void* wrow_ptr(const GemmParams& p, int n, float& scale, const unsigned char*& srow) {
+  scale = 1.f;
+  srow = nullptr;
+  if constexpr (WF == 2) {
+    srow = p.blk_scale + (size_t)n * (p.K / 32);
+    return reinterpret_cast<const unsigned char*>(p.seg[0]) + (size_t)n * p.ldb;
+  } else if constexpr (WF == 1) {
     scale = p.row_scale[n];
     return reinterpret_cast<const unsigned char*>(p.seg[0]) + (size_t)n * p.ldb;
   } else {
-    scale = 1.f;
     return brow_ptr(p, n);
   }
 }
 
 // PARTIAL (NF=1) and SWIGLU (NF=2: gate and up fragment of the same 16 output columns).
 // grid: x = column tile (16 output columns), y = row tile (16*MT rows), z = k-split.
-template <int MT, int MODE, bool F8 = false>
+template <int MT, int MODE, int WF = 0>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
   constexpr int NF = (MODE == GEMM_SWIGLU) ? 2 : 1;
   __shared__ float red[3][MT][NF][4][64];
@@ -158,12 +175,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
     arow[m] = reinterpret_cast<const bf16*>(p.A) + (size_t)r * p.lda;
   }
   const void* brow[NF];
+  const unsigned char* srow[NF];
   float bs[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     int n = ncol0 + li + f * p.half;     // SWIGLU: f=1 reads the up rows at offset `half`
     n = min(n, p.N - 1);
-    brow[f] = wrow_ptr<F8>(p, n, bs[f]);
+    brow[f] = wrow_ptr<WF>(p, n, bs[f], srow[f]);
   }
   const int nchunks = p.K / 64;
   const int s = blockIdx.z;
@@ -173,7 +191,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  skinny_acc<MT, NF, F8>(arow, p.a_plane, brow, bs, kg, c0 + wave, c1, 4, acc);
+  skinny_acc<MT, NF, WF>(arow, p.a_plane, brow, srow, bs, kg, c0 + wave, c1, 4, acc);
   // reduce the 4 waves' k-slices
   if (wave > 0) {
 #pragma unroll
@@ -216,7 +234,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
 // 9496 fragments of a 151936-word vocabulary divide.  Each row's candidates are kept by
 // 64/(16*MT) lanes in private sorted top-16 lists, merged at the end of the workgroup; one
 // partial list per (row, workgroup) is written.  grid: x = workgroups, y = row tile.
-template <int MT, bool F8 = false>
+template <int MT, int WF = 0>
 __global__ __launch_bounds__(256) void lmhead_topk_skinny(GemmParams p) {
   constexpr int R = 16 * MT;
   constexpr int LPR = 64 / R;          // lanes per row within a wave: 4, 2, 1
@@ -250,11 +268,12 @@ __global__ __launch_bounds__(256) void lmhead_topk_skinny(GemmParams p) {
     if (f >= nfrag) break;
     const int col = f * 16 + li;
     float bs[1];
-    const void* brow[1] = {wrow_ptr<F8>(p, min(col, p.N - 1), bs[0])};
+    const unsigned char* srow[1];
+    const void* brow[1] = {wrow_ptr<WF>(p, min(col, p.N - 1), bs[0], srow[0])};
     f32x4 acc[MT][1];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    skinny_acc<MT, 1, F8>(arow, p.a_plane, brow, bs, kg, 0, nchunks, 1, acc);
+    skinny_acc<MT, 1, WF>(arow, p.a_plane, brow, srow, bs, kg, 0, nchunks, 1, acc);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -977,6 +996,38 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------------------
 static int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// The skinny kernels (weights streamed into registers, row tiles of up to 64 rows): the plan
+// for 17..64 rows, and for any row count whose weight format the other kernels do not take.
+GemmPlan gemm_plan_skinny(int mode, int M, int N, int K) {
+  GemmPlan pl{};
+  pl.splits = 1;
+  pl.groups = 1;
+  pl.kind = 0;
+  const int nchunks = K / 64;
+  pl.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  const int rt = (M + 16 * pl.mt - 1) / (16 * pl.mt);
+  if (mode == GEMM_TOPK) {
+    const int nfrag = (N + 15) / 16;
+    pl.groups = clampi(512 / rt, 1, (nfrag + 3) / 4);   // = resident workgroups (2 per CU)
+    pl.grid = dim3(pl.groups, rt, 1);
+  } else {
+    const int ncols = (mode == GEMM_SWIGLU) ? N / 2 : N;
+    const int ct = (ncols + 15) / 16;
+    if (mode == GEMM_PARTIAL) pl.splits = clampi((768 + ct * rt - 1) / (ct * rt), 1, clampi(nchunks / 4, 1, 8));
+    pl.grid = dim3(ct, rt, pl.splits);
+  }
+  return pl;
+}
+
+GemmPlan gemm_plan_wf(bool bf16, int mode, int M, int N, int K, int wf) {
+  GemmPlan pl = gemm_plan(bf16, mode, M, N, K);
+  if (!bf16 || wf == 0) return pl;
+  // which kernels take E4M3 (1) and MXFP4 (2) weights: the skinny and the independent-wave ones
+  // both; the streaming ones both but in their top-16 form; the tiles E4M3 only
+  const bool takes = pl.kind == 0 || pl.kind == 4 || (pl.kind == 3 && mode != GEMM_TOPK) || (pl.kind == 5 && wf == 1);
+  return takes ? pl : gemm_plan_skinny(mode, M, N, K);
+}
+
 GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
   GemmPlan pl{};
   pl.splits = 1;
@@ -986,7 +1037,6 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
     pl.grid = dim3((N + 63) / 64, (M + 3) / 4, 1);
     return pl;
   }
-  const int nchunks = K / 64;
   if (M <= 16) {
     // stream kernel: slice = SW waves x slc chunks of 64; full K in one workgroup for the
     // nonlinear epilogues, k-splits for PARTIAL
@@ -1033,19 +1083,7 @@ GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K) {
     }
   }
   if (M <= 64) {
-    pl.kind = 0;
-    pl.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    const int rt = (M + 16 * pl.mt - 1) / (16 * pl.mt);
-    if (mode == GEMM_TOPK) {
-      const int nfrag = (N + 15) / 16;
-      pl.groups = clampi(512 / rt, 1, (nfrag + 3) / 4);   // = resident workgroups (2 per CU)
-      pl.grid = dim3(pl.groups, rt, 1);
-    } else {
-      const int ncols = (mode == GEMM_SWIGLU) ? N / 2 : N;
-      const int ct = (ncols + 15) / 16;
-      if (mode == GEMM_PARTIAL) pl.splits = clampi((768 + ct * rt - 1) / (ct * rt), 1, clampi(nchunks / 4, 1, 8));
-      pl.grid = dim3(ct, rt, pl.splits);
-    }
+    return gemm_plan_skinny(mode, M, N, K);
   } else {
     // MFMA tiles with LDS-DMA operands (K is a multiple of 32 for every bf16 drafter).  TOPK:
     // 256 x 256 tiles (one workgroup per CU) once there are more than 128 rows, else 128 x 128
@@ -1158,27 +1196,29 @@ hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hi
     return hipGetLastError();
   }
   if (pl.kind == 0) {
-    if (p.blk_scale) return hipErrorInvalidValue;   // MXFP4: batch-1 kernels only
-    if (p.row_scale && p.seg_rows < (mode == GEMM_SWIGLU ? 2 * p.half : p.N))
-      return hipErrorInvalidValue;                  // E4M3 weights: one segment
-#define DFL_SKINNY(F8)                                                                                \
+    if ((p.row_scale || p.blk_scale) && p.seg_rows < (mode == GEMM_SWIGLU ? 2 * p.half : p.N))
+      return hipErrorInvalidValue;                  // E4M3 / MXFP4 weights: one segment
+    if (p.blk_scale && p.K % 64) return hipErrorInvalidValue;
+#define DFL_SKINNY(WF)                                                                                \
     if (mode == GEMM_TOPK) {                                                                          \
-      if (pl.mt == 1) hipLaunchKernelGGL((lmhead_topk_skinny<1, F8>), pl.grid, blk, 0, st, p);        \
-      else if (pl.mt == 2) hipLaunchKernelGGL((lmhead_topk_skinny<2, F8>), pl.grid, blk, 0, st, p);   \
-      else hipLaunchKernelGGL((lmhead_topk_skinny<4, F8>), pl.grid, blk, 0, st, p);                   \
+      if (pl.mt == 1) hipLaunchKernelGGL((lmhead_topk_skinny<1, WF>), pl.grid, blk, 0, st, p);        \
+      else if (pl.mt == 2) hipLaunchKernelGGL((lmhead_topk_skinny<2, WF>), pl.grid, blk, 0, st, p);   \
+      else hipLaunchKernelGGL((lmhead_topk_skinny<4, WF>), pl.grid, blk, 0, st, p);                   \
     } else if (mode == GEMM_SWIGLU) {                                                                 \
-      if (pl.mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<1, GEMM_SWIGLU, F8>), pl.grid, blk, 0, st, p);      \
-      else if (pl.mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<2, GEMM_SWIGLU, F8>), pl.grid, blk, 0, st, p); \
-      else hipLaunchKernelGGL((gemm_skinny_kernel<4, GEMM_SWIGLU, F8>), pl.grid, blk, 0, st, p);                 \
+      if (pl.mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<1, GEMM_SWIGLU, WF>), pl.grid, blk, 0, st, p);      \
+      else if (pl.mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<2, GEMM_SWIGLU, WF>), pl.grid, blk, 0, st, p); \
+      else hipLaunchKernelGGL((gemm_skinny_kernel<4, GEMM_SWIGLU, WF>), pl.grid, blk, 0, st, p);                 \
     } else {                                                                                          \
-      if (pl.mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<1, GEMM_PARTIAL, F8>), pl.grid, blk, 0, st, p);      \
-      else if (pl.mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<2, GEMM_PARTIAL, F8>), pl.grid, blk, 0, st, p); \
-      else hipLaunchKernelGGL((gemm_skinny_kernel<4, GEMM_PARTIAL, F8>), pl.grid, blk, 0, st, p);                 \
+      if (pl.mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<1, GEMM_PARTIAL, WF>), pl.grid, blk, 0, st, p);      \
+      else if (pl.mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<2, GEMM_PARTIAL, WF>), pl.grid, blk, 0, st, p); \
+      else hipLaunchKernelGGL((gemm_skinny_kernel<4, GEMM_PARTIAL, WF>), pl.grid, blk, 0, st, p);                 \
     }
-    if (p.row_scale) {
-      DFL_SKINNY(true)
+    if (p.blk_scale) {
+      DFL_SKINNY(2)
+    } else if (p.row_scale) {
+      DFL_SKINNY(1)
     } else {
-      DFL_SKINNY(false)
+      DFL_SKINNY(0)
     }
 #undef DFL_SKINNY
     return hipGetLastError();

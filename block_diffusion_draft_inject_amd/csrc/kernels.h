@@ -97,6 +97,11 @@ __device__ __forceinline__ void store_partial(const GemmParams& p, int row, int 
 
 // Chooses the launch shape; deterministic in (dtype, mode, M, N, K).
 GemmPlan gemm_plan(bool bf16, int mode, int M, int N, int K);
+// The skinny kernels' plan for any M (row tiles of up to 64 rows).
+GemmPlan gemm_plan_skinny(int mode, int M, int N, int K);
+// gemm_plan for weights in format wf (0 bf16, 1 E4M3, 2 MXFP4): the same plan when its kernel
+// takes that format, else the skinny plan (every format).
+GemmPlan gemm_plan_wf(bool bf16, int mode, int M, int N, int K, int wf);
 // Bytes of partial output the plan writes (PARTIAL) or top-k partial entries (TOPK).
 size_t gemm_part_floats(const GemmPlan& pl, int mode, int M, int N);
 hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hipStream_t st);

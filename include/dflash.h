@@ -290,10 +290,9 @@ DFLASH_API dflash_status dflash_verify_greedy(int32_t n_seq, int32_t block_size,
  * dflash_set_lm_head_fp8 makes a handle's dflash_draft_block read the shared lm_head as those codes
  * times their row scales (exact in bf16) instead of the bf16 matrix; NULL for both reverts to bf16.
  * The codes are borrowed like the weights.  Every batch size: at most 16 draft rows
- * (n_seq * block_size) the independent-wave kernel widens the codes in registers, 17..64 rows the
- * skinny MFMA kernel, more rows the LDS tile kernels (each 1 KiB LDS-DMA block 16 rows x 64 k of
- * codes); with at most 16 rows the hidden size must be a multiple of 512 up to 2048, else the call
- * returns DFLASH_E_UNSUPPORTED. */
+ * (n_seq * block_size) the independent-wave kernel widens the codes in registers (hidden a
+ * multiple of 512 up to 2048; other hidden sizes take the skinny kernel), 17..64 rows the skinny
+ * MFMA kernel, more rows the LDS tile kernels (each 1 KiB LDS-DMA block 16 rows x 64 k of codes). */
 DFLASH_API dflash_status dflash_quantize_fp8_rows(const void* src, int32_t rows, int32_t cols, uint8_t* codes,
                                                   float* row_scales, void* stream);
 DFLASH_API dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t* codes, const float* row_scales);   /* clears an MXFP4 lm_head */
@@ -309,8 +308,11 @@ DFLASH_API dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t*
  * no allocation.  dflash_set_lm_head_mxfp4 makes a handle's dflash_draft_block read the shared
  * lm_head as those codes, each standing for value(code) * 2^(E - 127) (exact in bf16), instead of the
  * bf16 matrix (and instead of an FP8 lm_head, which it clears); NULL for both reverts to bf16.
- * Borrowed like the weights.  Batch-1 kernel only: a draft call with more than 16 rows, or a
- * hidden size that is not a multiple of 512 up to 2048, returns DFLASH_E_UNSUPPORTED. */
+ * Borrowed like the weights.  Every batch size: at most 16 draft rows the independent-wave kernel
+ * (hidden a multiple of 512 up to 2048), otherwise the skinny kernels, which stream the codes into
+ * registers over row tiles of up to 64 rows (each weight tile read once per row tile) and keep one
+ * work counter per row tile: a draft call of more than 4096 rows on them returns
+ * DFLASH_E_UNSUPPORTED before anything is enqueued. */
 DFLASH_API dflash_status dflash_quantize_mxfp4_rows(const void* src, int32_t rows, int32_t cols, uint8_t* codes,
                                                     uint8_t* scales, void* stream);
 DFLASH_API dflash_status dflash_set_lm_head_mxfp4(dflash_handle* h, const uint8_t* codes, const uint8_t* scales);
@@ -326,8 +328,10 @@ DFLASH_API dflash_status dflash_set_mlp_fp8(dflash_handle* h, int32_t layer, con
  * written by dflash_quantize_mxfp4_rows, with their block scale bytes gate_up_scales [2*ffn][d/32]
  * and down_scales [d][ffn/32].  Replaces the layer's FP8 MLP weights if any (and
  * dflash_set_mlp_fp8 replaces these); all four NULL reverts the layer to bf16.  hidden and ffn must
- * be multiples of 128 (else DFLASH_E_UNSUPPORTED).  Batch-1 kernels only: a draft call with more
- * than 16 rows, or a hidden size above 2048, returns DFLASH_E_UNSUPPORTED. */
+ * be multiples of 128 (else DFLASH_E_UNSUPPORTED).  Every batch size: at most 16 draft rows the
+ * streaming kernels (the skinny ones where the streaming plan does not apply), more rows the
+ * skinny kernels over row tiles of up to 64 rows, with the SwiGLU epilogue inside the gate/up
+ * GEMM at every row count. */
 DFLASH_API dflash_status dflash_set_mlp_mxfp4(dflash_handle* h, int32_t layer, const uint8_t* gate_up_codes,
                                               const uint8_t* gate_up_scales, const uint8_t* down_codes,
                                               const uint8_t* down_scales);

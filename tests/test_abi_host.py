@@ -130,22 +130,19 @@ def test_status_strings():
         assert L.dflash_status_string(s)
 
 
-def test_mxfp4_refusal_precedes_any_device_work():
-    """MXFP4 weights run in the batch-1 kernels only: with MXFP4 MLP weights or an MXFP4 lm_head
-    installed, a draft of more than 16 rows is refused before anything is enqueued; on a handle
-    over never-dereferenced fake device addresses the call returns -3 instead of touching the
-    device.  (E4M3 weights run at every batch size: nothing to refuse.)"""
+def test_quantised_lm_head_row_limit_precedes_any_device_work():
+    """MXFP4 (and E4M3) weights run at every row count; a quantised lm_head that the plan puts on
+    the skinny top-16 kernels keeps one work counter per 64-row tile, 64 counters in all, so a
+    draft of more than 4096 rows with the MXFP4 lm_head is refused before anything is enqueued: on
+    a handle over never-dereferenced fake device addresses the call returns -3 instead of touching
+    the device.  MXFP4 MLP weights alone have no such limit."""
     cfg = synth.WORKLOADS["b1_k16"]
-    st, h, keep, kvb, wsb = _fake_handle(cfg, max_seqs=4, max_batch=2, rows=64)
+    st, h, keep, kvb, wsb = _fake_handle(cfg, max_seqs=260, max_batch=257, rows=64)
     assert st == 0, B.lib().dflash_last_error()
     L = B.lib()
     fake = 0x5000
-    assert L.dflash_set_mlp_mxfp4(h, 0, fake, fake, fake, fake) == 0
-    assert L.dflash_draft_block(h, 2, fake, fake, fake, fake, fake, None, None) == -3     # 32 rows
-    assert b"16 draft rows" in L.dflash_last_error()
-    assert L.dflash_set_mlp_mxfp4(h, 0, None, None, None, None) == 0
     assert L.dflash_set_lm_head_mxfp4(h, fake, fake) == 0
-    assert L.dflash_draft_block(h, 2, fake, fake, fake, fake, fake, None, None) == -3
-    assert b"16 draft rows" in L.dflash_last_error()
+    assert L.dflash_draft_block(h, 257, fake, fake, fake, fake, fake, None, None) == -3     # 4112 rows
+    assert b"4096 draft rows" in L.dflash_last_error()
     assert L.dflash_set_lm_head_mxfp4(h, None, None) == 0
     assert L.dflash_destroy(h) == 0

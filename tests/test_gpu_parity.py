@@ -430,9 +430,9 @@ def test_mxfp4_quantizer_matches_oracle():
 
 
 def test_mid_bf16_mxfp4_lm_head(H):
-    """Batch 1, K=16 with the MXFP4 lm_head: codes as the oracle's, logits and top-16 against the
-    oracle run with the dequantised lm_head, top-16 with and without full logits; a call with more
-    than 16 rows is refused; setting the FP8 lm_head replaces it; NULL restores the bf16 lm_head."""
+    """Batch 1, K=16 with the MXFP4 lm_head (the independent-wave kernel): codes as the oracle's,
+    logits and top-16 against the oracle run with the dequantised lm_head, top-16 with and without
+    full logits; NULL restores the bf16 lm_head.  (More rows: test_mxfp4_above_16_rows.)"""
     case = H.Case(MID, max_seqs=2, max_batch=2, max_inject_rows=64)
     _prefill(case, [1], [(0, 50)])
     codes, scales = _quantize_mxfp4_on_gpu(case.dev_w["lm_head"])
@@ -446,8 +446,6 @@ def test_mid_bf16_mxfp4_lm_head(H):
         _same_topk_without_logits(case, [1], [123], res)
     finally:
         case.W64["lm_head"] = bf16_lm
-    with pytest.raises(B.DflashError):
-        case.draft([1, 0], [123, 5])               # 32 rows
     case.d.dflash_set_lm_head_mxfp4(None, None)
     res = case.draft([1], [123], logits=True)
     err, _ = H.check_draft(case, [1], [123], res)
@@ -602,7 +600,7 @@ def test_mid_bf16_mxfp4_mlp(H, cfg):
     streaming kernel, down through the k-split one), with one-chunk slices (hidden 512, ffn 1024)
     and with 128-k super-chunks (hidden 1024, ffn 4608): codes and block scales as the oracle's,
     then a draft against the oracle run with those matrices dequantised; FP8 MLP weights set
-    afterwards replace them; more than 16 rows are refused; NULL restores bf16."""
+    afterwards replace them; NULL restores bf16.  (More rows: test_mxfp4_above_16_rows.)"""
     import copy
     import torch
     case = H.Case(cfg, max_seqs=2, max_batch=2, max_inject_rows=64)
@@ -629,8 +627,6 @@ def test_mid_bf16_mxfp4_mlp(H, cfg):
         _same_topk_without_logits(case, [1], [222], res)
     finally:
         case.W64 = W64
-    with pytest.raises(B.DflashError):
-        case.draft([1, 0], [222, 5])               # 32 rows
     W8 = _fp8_drafter(case, mlp=True, lm_head=False)   # replaces the MXFP4 MLP weights
     case.W64 = W8
     try:
@@ -745,3 +741,63 @@ def test_two_batch_pipeline_two_streams(H):
             assert err <= H.LOGIT_TOL["bf16"]
             H.log(f"[pipeline] step {step} half {hidx}: max |logit err| {err:.2e}, tau {r['tau'].tolist()}")
     assert case.d.dflash_get_device_error() == 0
+
+
+def _mxfp4_drafter(case, mlp=True, lm_head=True):
+    """Quantises the MLP matrices of every layer (stacked [gate; up], down) and the lm_head to MXFP4
+    on the GPU, checks codes and block scales against the oracle's, installs them, and returns
+    float64 weights for the oracle with those matrices dequantised."""
+    import copy
+    import torch
+    cfg = case.cfg
+    W = copy.copy(case.W64)
+    W["layers"] = [dict(lw) for lw in case.W64["layers"]]
+    if mlp:
+        for l, lw in enumerate(case.dev_w["layers"]):
+            gu, gus = _quantize_mxfp4_on_gpu(torch.cat([lw["w_gate"], lw["w_up"]]).contiguous())
+            dn, dns = _quantize_mxfp4_on_gpu(lw["w_down"])
+            for name, codes, scales, rows in (("w_gate", gu, gus, slice(0, cfg.ffn)),
+                                              ("w_up", gu, gus, slice(cfg.ffn, 2 * cfg.ffn)),
+                                              ("w_down", dn, dns, slice(None))):
+                oc, osc = O.quantize_mxfp4_rows(case.W64["layers"][l][name])
+                assert np.array_equal(codes[rows].cpu().numpy(), oc), (l, name)
+                assert np.array_equal(scales[rows].cpu().numpy(), osc), (l, name)
+                W["layers"][l][name] = O.dequantize_mxfp4_rows(oc, osc)
+            case.d.dflash_set_mlp_mxfp4(l, gu, gus, dn, dns)
+    if lm_head:
+        codes, scales = _quantize_mxfp4_on_gpu(case.dev_w["lm_head"])
+        oc, osc = O.quantize_mxfp4_rows(case.W64["lm_head"])
+        assert np.array_equal(codes.cpu().numpy(), oc) and np.array_equal(scales.cpu().numpy(), osc)
+        case.d.dflash_set_lm_head_mxfp4(codes, scales)
+        W["lm_head"] = O.dequantize_mxfp4_rows(oc, osc)
+    return W
+
+
+@pytest.mark.parametrize("wide,n_seq", [(False, 2), (False, 5), (True, 10)],
+                         ids=["32_rows", "80_rows", "160_rows_wide"])
+def test_mxfp4_above_16_rows(H, wide, n_seq):
+    """MXFP4 lm_head and MLP weights above 16 draft rows run on the skinny kernels (weights into
+    registers, row tiles of up to 64 rows): 2 sequences at K=16 (32 rows, tiles of 32), 5 (80 rows,
+    two row tiles) and 10 at hidden 1024 / ffn 4608 (160 rows, three row tiles, the SwiGLU epilogue
+    in the GEMM at more than 64 rows).  Ragged contexts, then a draft against the oracle run with
+    the dequantised matrices, top-16 with and without full logits; NULL restores bf16."""
+    cfg = MID_WIDE_MLP if wide else MID
+    case = H.Case(cfg, max_seqs=n_seq, max_batch=n_seq, max_inject_rows=128)
+    seq_ids = list(range(n_seq))
+    rng = np.random.default_rng(70 + n_seq)
+    lens = [int(L) for L in rng.integers(20, 90, size=n_seq)]
+    _prefill(case, seq_ids, [(0, L) for L in lens])
+    W64 = case.W64
+    case.W64 = _mxfp4_drafter(case)
+    anchors = rng.integers(0, cfg.vocab - 1, size=n_seq).tolist()
+    try:
+        res = _check(H, case, seq_ids, anchors, mode_names=("viterbi",))
+        _same_topk_without_logits(case, seq_ids, anchors, res)
+    finally:
+        case.W64 = W64
+    case.d.dflash_set_lm_head_mxfp4(None, None)
+    for l in range(cfg.n_layers):
+        case.d.dflash_set_mlp_mxfp4(l, None, None, None, None)
+    res = case.draft(seq_ids, anchors, logits=True)
+    err, _ = H.check_draft(case, seq_ids, anchors, res)
+    assert err <= H.LOGIT_TOL["bf16"]

@@ -587,3 +587,55 @@ def test_b1_k16_per_channel_conv(H, big):
         L = int(run.lengths([0])[0])
         run.inject([0], [np.arange(L, L + int(ncom[0]))], start=False)
     assert run.d.dflash_get_device_error() == 0
+
+
+def test_b32_k8_mxfp4_lm_head_and_mlp(H, big):
+    """Batch 32, K=8 (256 draft rows) with MXFP4 codes for the lm_head and every layer's MLP: these
+    run on the skinny kernels (row tiles of 64; the SwiGLU epilogue inside the gate/up GEMM), the
+    other GEMMs on the bf16 tiles; codes and block scales checked against the oracle's; drafts of
+    sampled sequences against the oracle run with the dequantised matrices."""
+    import copy
+    import torch
+    cfg = synth.WORKLOADS["b32_k8_conv"]
+    Ls = synth.context_lengths(cfg)
+    sampled = [int(np.argmin(Ls)), int(np.argmax(Ls)), 11]
+    run = Run(H, big, cfg, max_seqs=32, max_batch=32, max_inject_rows=4096, sampled=sampled)
+    ids = list(range(32))
+    run.d.dflash_reset_seqs(run.t(np.arange(32, dtype=np.int32)))
+    run.inject(ids, [_window(int(L), cfg.window) for L in Ls])
+    W4 = copy.copy(big["W64"])
+    W4["layers"] = [dict(lw) for lw in big["W64"]["layers"]]
+    keep = []
+
+    def q4(mat, names_rows, layer):
+        rows, cols = mat.shape
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
+        B.dflash_quantize_mxfp4_rows(mat, codes, scales)
+        torch.cuda.synchronize()
+        for name, rs in names_rows:
+            src = big["W64"][name] if layer is None else big["W64"]["layers"][layer][name]
+            oc, osc = O.quantize_mxfp4_rows(src)
+            assert np.array_equal(codes[rs].cpu().numpy(), oc), (layer, name)
+            assert np.array_equal(scales[rs].cpu().numpy(), osc), (layer, name)
+            if layer is None:
+                W4[name] = O.dequantize_mxfp4_rows(oc, osc)
+            else:
+                W4["layers"][layer][name] = O.dequantize_mxfp4_rows(oc, osc)
+        keep.append((codes, scales))
+        return codes, scales
+
+    ffn = cfg.ffn
+    for l, lw in enumerate(big["dev"]["layers"]):
+        gu = q4(torch.cat([lw["w_gate"], lw["w_up"]]).contiguous(),
+                [("w_gate", slice(0, ffn)), ("w_up", slice(ffn, None))], l)
+        dn = q4(lw["w_down"], [("w_down", slice(None))], l)
+        run.d.dflash_set_mlp_mxfp4(l, *gu, *dn)
+    lm4 = q4(big["dev"]["lm_head"], [("lm_head", slice(None))], None)
+    run.d.dflash_set_lm_head_mxfp4(*lm4)
+    run.W64 = W4
+    anchors = synth.anchors(cfg).tolist()
+    res = run.draft(ids, anchors)
+    run.own_logit_topk(res)
+    run.compare_sampled(ids, anchors, res)
+    assert run.d.dflash_get_device_error() == 0
