@@ -320,13 +320,14 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
   const bool b = bf(c);
   const int K = c->block_size, d = c->hidden, M = n_seq * K;
   // E4M3 and MXFP4 weights: each GEMM takes the plain plan's kernel when that kernel takes the
-  // format, else the skinny kernels (gemm_plan_wf).  A skinny top-16 pass keeps one work counter
-  // per row tile of 64 rows.
+  // format, else the skinny kernels (gemm_plan_wf: a quantised top-16 GEMM of at most 16 rows that
+  // the streaming kernel would take; MXFP4 tiles with more than 2048 k a workgroup).  A skinny
+  // top-16 pass keeps one work counter per row tile of 64 rows.
   const int lm_wf = H->lm_fp4 ? 2 : (H->lm_fp8 ? 1 : 0);
   const GemmPlan lm_plan = gemm_plan_wf(b, b ? GEMM_TOPK : GEMM_PARTIAL, M, c->vocab, d, lm_wf);
   if (b && lm_plan.kind == 0 && (int)lm_plan.grid.y > NCOUNTERS)
-    return fail(DFLASH_E_UNSUPPORTED, "a quantised lm_head on the skinny kernels takes at most %d draft rows "
-                "(n_seq * block_size = %d)", NCOUNTERS * 64, M);
+    return fail(DFLASH_E_UNSUPPORTED, "an MXFP4 lm_head with a hidden size above 2048 runs on the skinny kernels, "
+                "which take at most %d draft rows (n_seq * block_size = %d)", NCOUNTERS * 64, M);
   const int qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
   float* part = wsp<float>(ws, W.part);
   SeqCtx* ctx = wsp<SeqCtx>(ws, W.ctx);
@@ -529,13 +530,12 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
       gg.blk_scale = mq->gu_b;
     }
     const int mwf = mq ? (mq->gu_b ? 2 : 1) : 0;
-    if (b && (M <= 64 || mwf == 2)) {   // the SwiGLU epilogue inside the GEMM (MXFP4: skinny at any M)
-      GemmPlan pg = M <= 64 ? gemm_plan_wf(b, GEMM_SWIGLU, M, 2 * c->ffn, d, mwf)
-                            : gemm_plan_skinny(GEMM_SWIGLU, M, 2 * c->ffn, d);
+    if (b && M <= 64) {   // the SwiGLU epilogue inside the GEMM
+      GemmPlan pg = gemm_plan_wf(b, GEMM_SWIGLU, M, 2 * c->ffn, d, mwf);
       HIP_TRY(gemm_launch(b, pg, GEMM_SWIGLU, gg, st));
     } else {
       gg.half = 0;
-      GemmPlan pg = gemm_plan(b, GEMM_PARTIAL, M, 2 * c->ffn, d);
+      GemmPlan pg = gemm_plan_wf(b, GEMM_PARTIAL, M, 2 * c->ffn, d, mwf);
       HIP_TRY(gemm_launch(b, pg, GEMM_PARTIAL, gg, st));
       SwigluArgs sa{M, c->ffn, pg.splits, M, Mmax * c->ffn, part, act_s};
       HIP_TRY(launch_swiglu(b, sa, st));

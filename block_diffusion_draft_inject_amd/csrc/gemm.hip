@@ -28,16 +28,6 @@ namespace dfl {
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
-// MXFP4 weights (blk_scale set): one word of eight E2M1 codes (element 2j in the low nibble of
-// byte j) -> eight bf16 values code * s, s = 2^(E - 127) of the codes' block, exact
-__device__ __forceinline__ bf16x8 fp4x8_bf16(unsigned w, float s) {
-  u32x4 o;
-  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
-  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
-  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
-  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
-  return as_bf16x8(o);
-}
 
 // ---------------------------------------------------------------------------------------
 // skinny: accumulate one wave tile of (16*MT rows) x (16*NF cols) over chunks
@@ -1022,9 +1012,12 @@ GemmPlan gemm_plan_skinny(int mode, int M, int N, int K) {
 GemmPlan gemm_plan_wf(bool bf16, int mode, int M, int N, int K, int wf) {
   GemmPlan pl = gemm_plan(bf16, mode, M, N, K);
   if (!bf16 || wf == 0) return pl;
-  // which kernels take E4M3 (1) and MXFP4 (2) weights: the skinny and the independent-wave ones
-  // both; the streaming ones both but in their top-16 form; the tiles E4M3 only
-  const bool takes = pl.kind == 0 || pl.kind == 4 || (pl.kind == 3 && mode != GEMM_TOPK) || (pl.kind == 5 && wf == 1);
+  // which kernels take E4M3 (1) and MXFP4 (2) weights: the skinny, independent-wave and tile ones
+  // both (the MXFP4 tiles at most TILE4_MAX_STEPS k-steps a workgroup); the streaming ones both
+  // but in their top-16 form
+  const int tile_steps = 2 * ((K / 64 + pl.splits - 1) / pl.splits);
+  const bool takes = pl.kind == 0 || pl.kind == 4 || (pl.kind == 3 && mode != GEMM_TOPK) ||
+                     (pl.kind == 5 && (wf == 1 || tile_steps <= TILE4_MAX_STEPS));
   return takes ? pl : gemm_plan_skinny(mode, M, N, K);
 }
 

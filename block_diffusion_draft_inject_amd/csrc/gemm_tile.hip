@@ -70,6 +70,40 @@ struct Tile8Cfg {
   static_assert(BA % NW == 0 && BB % NW == 0, "blocks per operand must split evenly over the waves");
 };
 
+// MXFP4 weights (blk_scale set).  Half a byte per weight, so a pair of k-steps (64 k) of a weight
+// row is 32 bytes of codes and a 1 KiB LDS-DMA block holds 32 weight rows x 64 k (lane l: row l/2,
+// one k-step of it per 16-byte half).  A pair buffer holds the activation blocks of both steps
+// (as for bf16 weights) and one code block per 32 columns; where there are fewer code blocks than
+// waves, only the first waves issue them (two pair buffers then, every pair waited for in full).
+// The two halves of a code row are swapped on bit 3 of the row, so that the 4-byte operand reads
+// of 16 rows x 4 lane groups fall in 64 distinct banks.  The block scales (one byte per row and
+// k-step: a block is 32 k) of the tile's columns sit in LDS as [step][column] bytes, staged for
+// the workgroup's whole k-range (at most SEG k-steps) before its k-loop; each operand word of
+// eight codes is widened with its block's scale (v_cvt_scalef32_pk_bf16_fp4, exact), so nothing
+// is scaled after the sum.
+template <int BM, int BN, int WGM, int WGN, int NP, int PL = 2>
+struct Tile4Cfg {
+  static constexpr int NW = WGM * WGN, NT = NW * 64;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int FM = WM / 16, FN = WN / 16;
+  static constexpr int BA = BM / 16, BC = BN / 32;
+  static constexpr int PLc = PL;
+  static constexpr int NBLK = 2 * PL * BA + BC;          // blocks per pair buffer
+  static constexpr int PAIR = NBLK * 1024;
+  static constexpr bool CG = BC < NW;                     // code blocks issued by waves < BC only
+  static constexpr int QA = PL * BA / NW, QC = CG ? 1 : BC / NW;
+  static constexpr int D2 = 2 * QA + QC;
+  static constexpr int SEG = TILE4_MAX_STEPS;             // k-steps of block scales a workgroup stages
+  static constexpr int SCL = SEG * BN;                    // their bytes
+  static constexpr int LDS = NP * PAIR + SCL;
+  static constexpr int EPB = NP * PAIR;                   // bytes an epilogue may overlay
+  static constexpr int BMc = BM, BNc = BN, NPc = NP, WGNc = WGN;
+  static constexpr int WF = 2;
+  static_assert(PL == 1 || PL == 2, "activation planes");
+  static_assert(NP >= 2 && NP <= 3 && (NP == 2 || !CG), "pair buffers");
+  static_assert(BA % NW == 0 && (BC % NW == 0 || NW % BC == 0), "blocks per operand must split over the waves");
+};
+
 __device__ __forceinline__ int ctz_(unsigned x) { return __builtin_ctz(x); }
 __device__ __forceinline__ int ctz_(unsigned long long x) { return __builtin_ctzll(x); }
 
@@ -357,6 +391,150 @@ __device__ __forceinline__ void tile8_run(const GemmParams& p, unsigned char* sm
   }
 }
 
+template <class T>
+struct Tile4Src {
+  const char* base[T::QA];
+  unsigned voff[T::QA];
+  const unsigned char* addr[T::QC];
+};
+
+// half (k-step of a pair) stored at 16-byte position half ^ ((row >> 3) & 1) of a code row
+__device__ __forceinline__ int tile4_swz(int row) { return (row >> 3) & 1; }
+
+template <class T>
+__device__ __forceinline__ void tile4_src(const GemmParams& p, int m0, int n0, int Mv, int ncap, int wave, int lane,
+                                          Tile4Src<T>& s) {
+  const int r16 = lane >> 2;
+  const int kc = (lane & 3) ^ tile_swz(r16);
+  const char* ahi = reinterpret_cast<const char*>(p.A);
+  const char* alo = reinterpret_cast<const char*>(reinterpret_cast<const bf16*>(p.A) + p.a_plane);
+#pragma unroll
+  for (int q = 0; q < T::QA; ++q) {
+    const int b = T::NW * q + wave;                // activation block of a step: hi rows, then lo rows
+    const bool hi = T::NW * q < T::BA;
+    const int r = min(m0 + (hi ? b : b - T::BA) * 16 + r16, Mv - 1);
+    s.base[q] = hi ? ahi : alo;
+    s.voff[q] = (unsigned)(((size_t)r * p.lda + kc * 8) * 2);
+  }
+  const int r32 = lane >> 1;                       // row of the lane in a code block
+  const int half = (lane & 1) ^ tile4_swz(r32);   // the k-step its LDS position holds
+#pragma unroll
+  for (int q = 0; q < T::QC; ++q) {
+    const int b = T::CG ? min(wave, T::BC - 1) : T::NW * q + wave;
+    const int n = min(n0 + b * 32 + r32, ncap - 1);   // columns past ncap re-read the last
+    s.addr[q] = reinterpret_cast<const unsigned char*>(p.seg[0]) + (size_t)n * p.ldb + half * 16;
+  }
+}
+
+// the pair of k-steps c, c + 1 (c even) into the pair buffer at LDS address `pb`
+template <class T>
+__device__ __forceinline__ void tile4_issue(const Tile4Src<T>& s, unsigned pb, int wave, int c) {
+#pragma unroll
+  for (int q = 0; q < T::QA; ++q) {
+    dma16(pb + (T::NW * q + wave) * 1024, s.voff[q], s.base[q] + (size_t)c * MK * 2);
+    dma16(pb + (T::PLc * T::BA + T::NW * q + wave) * 1024, s.voff[q], s.base[q] + (size_t)(c + 1) * MK * 2);
+  }
+  if (!T::CG || wave < T::BC) {                    // wave-uniform
+#pragma unroll
+    for (int q = 0; q < T::QC; ++q) {
+      const int b = T::CG ? wave : T::NW * q + wave;
+      dma16v(pb + (2 * T::PLc * T::BA + b) * 1024, s.addr[q] + (size_t)c * (MK / 2));
+    }
+  }
+}
+
+// The block scales of columns [n0, n0 + BN) (clamped to ncap - 1) for k-steps [c, c + ns), ns <=
+// SEG, into scl[step][column] (every wave is done with the previous ones: the caller's barrier;
+// no LDS-DMA load is in flight, so the compiler's own waits for these loads are exact).
+template <class T>
+__device__ __forceinline__ void tile4_scales(const GemmParams& p, unsigned char* scl, int n0, int ncap, int c, int ns) {
+  constexpr int PER = T::SEG * T::BNc / T::NT;     // bytes per thread, 8 loads in flight at a time
+  static_assert(PER % 8 == 0, "scale bytes per thread");
+  const int kb = p.K / 32;
+  const int col = threadIdx.x % T::BNc, st0 = threadIdx.x / T::BNc;
+  constexpr int SST = T::NT / T::BNc;              // steps apart of a thread's successive bytes
+  const unsigned char* src = p.blk_scale + (size_t)min(n0 + col, ncap - 1) * kb + c;
+#pragma unroll 1
+  for (int i0 = 0; i0 < PER; i0 += 8) {
+    unsigned char v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = src[min(st0 + (i0 + i) * SST, ns - 1)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int st = st0 + (i0 + i) * SST;
+      if (st < ns) scl[st * T::BNc + col] = v[i];
+    }
+  }
+}
+
+// step st (0, 1) of the pair in `pair`: lo = the lane's activation offset in a block; scl_st the
+// scale row of this step
+template <class T>
+__device__ __forceinline__ void tile4_mma(const unsigned char* pair, int st, int wm, int wn, unsigned lo, int li, int kg,
+                                          const unsigned char* scl_st, f32x4 (&acc)[T::FM][T::FN]) {
+  bf16x8 b[T::FN];
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) {
+    const int col = wn * T::WN + j * 16 + li;      // column of the tile
+    const int r = col & 31;                        // its row in code block col / 32
+    const unsigned w = *reinterpret_cast<const unsigned*>(
+        pair + (2 * T::PLc * T::BA + (col >> 5)) * 1024 + r * 32 + ((st ^ tile4_swz(r)) << 4) + kg * 4);
+    b[j] = fp4x8_bf16(w, __uint_as_float((unsigned)scl_st[col] << 23));   // 2^(E - 127)
+  }
+  const unsigned char* a = pair + st * T::PLc * T::BA * 1024;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(a + (wm * T::FM + i) * 1024 + lo);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b[j], acc[i][j], 0, 0, 0);
+    if constexpr (T::PLc == 2) {
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(a + (T::BA + wm * T::FM + i) * 1024 + lo);
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+// One output tile over the k-step pairs starting at step c0 (even), np pairs, 2 np <= SEG: the
+// block scales of those steps are staged first, then acc = the tile's sums.
+template <class T>
+__device__ __forceinline__ void tile4_run(const GemmParams& p, unsigned char* smem, int m0, int n0, int Mv, int ncap,
+                                          int c0, int np, f32x4 (&acc)[T::FM][T::FN]) {
+  constexpr int NP = T::NPc;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / T::WGNc, wn = wave % T::WGNc, li = lane & 15, kg = lane >> 4;
+  unsigned char* scl = smem + NP * T::PAIR;
+  wait_barrier<0>();                               // every wave is done with the LDS of the last tile
+  tile4_scales<T>(p, scl, n0, ncap, c0, 2 * np);
+  Tile4Src<T> src;
+  tile4_src<T>(p, m0, n0, Mv, ncap, wave, lane, src);
+  const unsigned lo = li * 64 + ((kg ^ tile_swz(li)) << 4);
+  const unsigned sbase = lds_addr(smem);
+#pragma unroll
+  for (int q = 0; q + 1 < NP; ++q)
+    if (q < np) tile4_issue<T>(src, sbase + q * T::PAIR, wave, c0 + 2 * q);
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int cur = 0;   // buffer of pair j
+  for (int j = 0; j < np; ++j) {
+    // pair j has landed for every wave (later pairs may still be in flight), every wave is done
+    // with pair j - 1's buffer, and (first pass) the scales are in LDS
+    if (NP >= 3 && j + 1 < np) wait_barrier<T::D2>();
+    else wait_barrier<0>();
+    if (j + NP - 1 < np) {
+      const int nb = cur == 0 ? NP - 1 : cur - 1;
+      tile4_issue<T>(src, sbase + nb * T::PAIR, wave, c0 + 2 * (j + NP - 1));
+    }
+    tile4_mma<T>(smem + cur * T::PAIR, 0, wm, wn, lo, li, kg, scl + (2 * j) * T::BNc, acc);
+    tile4_mma<T>(smem + cur * T::PAIR, 1, wm, wn, lo, li, kg, scl + (2 * j + 1) * T::BNc, acc);
+    cur = cur + 1 == NP ? 0 : cur + 1;
+  }
+}
+
 // PARTIAL: grid x = k-split, y = column tile, z = row tile; part[split][row][col].  The split is
 // the fastest grid index: workgroups go to the eight XCDs round-robin by linear index, so with
 // eight splits each XCD takes one k-range and its L2 fetches only that slice of the activation
@@ -379,6 +557,13 @@ __global__ __launch_bounds__(T::NT, OCC) void gemm_tile_partial(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) sc[j] = p.row_scale[min(n0 + wn * T::WN + j * 16 + li, p.N - 1)];
     tile8_run<T>(p, smem, m0, n0, Mv, p.N, 2 * p0, p1 - p0, acc);
+  } else if constexpr (T::WF == 2) {
+    // MXFP4: whole pairs of k-steps per split, the block scales applied inside
+    const int np = nk / 2;
+    const int p0 = (int)((long)np * s / p.splits), p1 = (int)((long)np * (s + 1) / p.splits);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) sc[j] = 1.f;
+    tile4_run<T>(p, smem, m0, n0, Mv, p.N, 2 * p0, p1 - p0, acc);
   } else {
     const int c0 = (int)((long)nk * s / p.splits), c1 = (int)((long)nk * (s + 1) / p.splits);
 #pragma unroll
@@ -456,6 +641,8 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
       for (int i = 0; i < T::FM; ++i)
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) acc[i][j] *= sc[j];
+    } else if constexpr (T::WF == 2) {
+      tile4_run<T>(p, smem, m0, n0, Mv, cend, 0, nk / 2, acc);
     } else if constexpr (T::Sc == 4) {
       if (nk % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, cend, 0, nk, acc);
       else tile_run<T>(p, smem, m0, n0, Mv, cend, 0, nk, acc);
@@ -562,9 +749,37 @@ using TileSmall8 = Tile8Cfg<128, 128, 2, 2, 2>;
 using TileTall8 = Tile8Cfg<256, 128, 4, 2, 2>;
 using TileSmallHi8 = Tile8Cfg<128, 128, 2, 2, 3, 1>;
 using TileBigHi8 = Tile8Cfg<256, 256, 4, 2, 3, 1>;
+// MXFP4 weights: pair buffers of 36 / 68 KiB (layer GEMMs, two each; the 256 x 128 tile's four
+// code blocks issued by waves 0-3) and 20 / 40 KiB (lm_head, three each), plus 8 / 16 KiB of
+// staged block scales
+using TileSmall4 = Tile4Cfg<128, 128, 2, 2, 2>;
+using TileTall4 = Tile4Cfg<256, 128, 4, 2, 2>;
+using TileSmallHi4 = Tile4Cfg<128, 128, 2, 2, 3, 1>;
+using TileBigHi4 = Tile4Cfg<256, 256, 4, 2, 3, 1>;
 
 hipError_t tile_launch(const GemmPlan& pl, int mode, const GemmParams& p, hipStream_t st) {
   if (p.K % MK) return hipErrorInvalidValue;
+  if (p.blk_scale) {   // MXFP4 weights: one segment, whole pairs of k-steps, at most SEG k-steps a workgroup
+    if (p.K % (2 * MK) || p.seg_rows < p.N || p.row_scale) return hipErrorInvalidValue;
+    if (2 * ((p.K / MK / 2 + pl.splits - 1) / pl.splits) > TILE4_MAX_STEPS) return hipErrorInvalidValue;
+    if (mode == GEMM_TOPK) {
+      if (pl.mt) {
+        if (p.logits) hipLaunchKernelGGL((lmhead_topk_tile<TileBigHi4, 1, true>), pl.grid, dim3(TileBigHi4::NT), 0, st, p);
+        else hipLaunchKernelGGL((lmhead_topk_tile<TileBigHi4, 1, false>), pl.grid, dim3(TileBigHi4::NT), 0, st, p);
+      } else {
+        if (p.logits) hipLaunchKernelGGL((lmhead_topk_tile<TileSmallHi4, 2, true>), pl.grid, dim3(TileSmallHi4::NT), 0, st, p);
+        else hipLaunchKernelGGL((lmhead_topk_tile<TileSmallHi4, 2, false>), pl.grid, dim3(TileSmallHi4::NT), 0, st, p);
+      }
+    } else if (mode == GEMM_PARTIAL) {
+      const dim3 g(pl.grid.z, pl.grid.x, pl.grid.y);
+      if (pl.mt == 2) hipLaunchKernelGGL((gemm_tile_partial<TileTall4, 1>), g, dim3(TileTall4::NT), 0, st, p);
+      else if (pl.mt == 0) hipLaunchKernelGGL((gemm_tile_partial<TileSmall4, 2>), g, dim3(TileSmall4::NT), 0, st, p);
+      else return hipErrorInvalidValue;
+    } else {
+      return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (p.row_scale) {   // E4M3 weights: one segment, whole pairs of k-steps
     if (p.K % (2 * MK) || p.seg_rows < p.N || p.blk_scale) return hipErrorInvalidValue;
     if (mode == GEMM_TOPK) {

@@ -66,6 +66,17 @@ __device__ __forceinline__ bf16x8 fp8x8_bf16(unsigned w0, unsigned w1, float s) 
   return as_bf16x8(o);
 }
 
+// MXFP4 weights (blk_scale set): one word of eight E2M1 codes (element 2j in the low nibble of
+// byte j) -> eight bf16 values code * s, s = 2^(E - 127) of the codes' block, exact
+__device__ __forceinline__ bf16x8 fp4x8_bf16(unsigned w, float s) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+  o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+  o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+  o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+  return as_bf16x8(o);
+}
+
 // Row n of the segmented weight matrix.
 __device__ __forceinline__ const bf16* brow_ptr(const GemmParams& p, int n) {
   const int s = n / p.seg_rows;
@@ -107,5 +118,7 @@ size_t gemm_part_floats(const GemmPlan& pl, int mode, int M, int N);
 hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hipStream_t st);
 // Tiled MFMA kernels for more than 64 rows (pl.kind 5; pl.mt selects the tile shape).
 hipError_t tile_launch(const GemmPlan& pl, int mode, const GemmParams& p, hipStream_t st);
+// k-steps of 32 (2048 k) an MXFP4 tile workgroup takes at most (its block scales staged in LDS)
+constexpr int TILE4_MAX_STEPS = 64;
 
 }  // namespace dfl

@@ -309,10 +309,11 @@ DFLASH_API dflash_status dflash_set_lm_head_fp8(dflash_handle* h, const uint8_t*
  * lm_head as those codes, each standing for value(code) * 2^(E - 127) (exact in bf16), instead of the
  * bf16 matrix (and instead of an FP8 lm_head, which it clears); NULL for both reverts to bf16.
  * Borrowed like the weights.  Every batch size: at most 16 draft rows the independent-wave kernel
- * (hidden a multiple of 512 up to 2048), otherwise the skinny kernels, which stream the codes into
- * registers over row tiles of up to 64 rows (each weight tile read once per row tile) and keep one
- * work counter per row tile: a draft call of more than 4096 rows on them returns
- * DFLASH_E_UNSUPPORTED before anything is enqueued. */
+ * (hidden a multiple of 512 up to 2048), 17..64 rows the skinny kernel (codes streamed into
+ * registers), more rows the LDS tile kernels (each 1 KiB LDS-DMA block 32 rows x 64 k of codes,
+ * the block scales of a tile staged in LDS) when the hidden size is at most 2048, else the skinny
+ * kernels over row tiles of 64 rows, which keep one work counter per row tile: such a draft call
+ * of more than 4096 rows returns DFLASH_E_UNSUPPORTED before anything is enqueued. */
 DFLASH_API dflash_status dflash_quantize_mxfp4_rows(const void* src, int32_t rows, int32_t cols, uint8_t* codes,
                                                     uint8_t* scales, void* stream);
 DFLASH_API dflash_status dflash_set_lm_head_mxfp4(dflash_handle* h, const uint8_t* codes, const uint8_t* scales);
@@ -329,9 +330,9 @@ DFLASH_API dflash_status dflash_set_mlp_fp8(dflash_handle* h, int32_t layer, con
  * and down_scales [d][ffn/32].  Replaces the layer's FP8 MLP weights if any (and
  * dflash_set_mlp_fp8 replaces these); all four NULL reverts the layer to bf16.  hidden and ffn must
  * be multiples of 128 (else DFLASH_E_UNSUPPORTED).  Every batch size: at most 16 draft rows the
- * streaming kernels (the skinny ones where the streaming plan does not apply), more rows the
- * skinny kernels over row tiles of up to 64 rows, with the SwiGLU epilogue inside the gate/up
- * GEMM at every row count. */
+ * streaming kernels (the skinny ones where the streaming plan does not apply), 17..64 rows the
+ * skinny kernels, more rows the LDS tile kernels (the skinny ones over row tiles of 64 rows where
+ * a tile workgroup's k-range would exceed 2048). */
 DFLASH_API dflash_status dflash_set_mlp_mxfp4(dflash_handle* h, int32_t layer, const uint8_t* gate_up_codes,
                                               const uint8_t* gate_up_scales, const uint8_t* down_codes,
                                               const uint8_t* down_scales);

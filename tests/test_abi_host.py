@@ -131,18 +131,18 @@ def test_status_strings():
 
 
 def test_quantised_lm_head_row_limit_precedes_any_device_work():
-    """MXFP4 (and E4M3) weights run at every row count; a quantised lm_head that the plan puts on
-    the skinny top-16 kernels keeps one work counter per 64-row tile, 64 counters in all, so a
-    draft of more than 4096 rows with the MXFP4 lm_head is refused before anything is enqueued: on
-    a handle over never-dereferenced fake device addresses the call returns -3 instead of touching
-    the device.  MXFP4 MLP weights alone have no such limit."""
-    cfg = synth.WORKLOADS["b1_k16"]
+    """MXFP4 (and E4M3) weights run at every row count.  The MXFP4 tiles stage the block scales of
+    at most 2048 k per workgroup, so an MXFP4 lm_head over a wider hidden size runs on the skinny
+    top-16 kernels, which keep one work counter per 64-row tile, 64 counters in all: a draft of
+    more than 4096 rows with it is refused before anything is enqueued (on a handle over
+    never-dereferenced fake device addresses the call returns -3 instead of touching the device)."""
+    cfg = synth.WORKLOADS["b1_k16"].replace(hidden=2560, name="b1_k16_h2560")
     st, h, keep, kvb, wsb = _fake_handle(cfg, max_seqs=260, max_batch=257, rows=64)
     assert st == 0, B.lib().dflash_last_error()
     L = B.lib()
     fake = 0x5000
     assert L.dflash_set_lm_head_mxfp4(h, fake, fake) == 0
     assert L.dflash_draft_block(h, 257, fake, fake, fake, fake, fake, None, None) == -3     # 4112 rows
-    assert b"4096 draft rows" in L.dflash_last_error()
+    assert b"4096 draft rows" in L.dflash_last_error(), L.dflash_last_error()
     assert L.dflash_set_lm_head_mxfp4(h, None, None) == 0
     assert L.dflash_destroy(h) == 0

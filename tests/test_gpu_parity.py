@@ -776,11 +776,12 @@ def _mxfp4_drafter(case, mlp=True, lm_head=True):
 @pytest.mark.parametrize("wide,n_seq", [(False, 2), (False, 5), (True, 10)],
                          ids=["32_rows", "80_rows", "160_rows_wide"])
 def test_mxfp4_above_16_rows(H, wide, n_seq):
-    """MXFP4 lm_head and MLP weights above 16 draft rows run on the skinny kernels (weights into
-    registers, row tiles of up to 64 rows): 2 sequences at K=16 (32 rows, tiles of 32), 5 (80 rows,
-    two row tiles) and 10 at hidden 1024 / ffn 4608 (160 rows, three row tiles, the SwiGLU epilogue
-    in the GEMM at more than 64 rows).  Ragged contexts, then a draft against the oracle run with
-    the dequantised matrices, top-16 with and without full logits; NULL restores bf16."""
+    """MXFP4 lm_head and MLP weights above 16 draft rows: 2 sequences at K=16 (32 rows: the skinny
+    kernels, codes streamed into registers), 5 (80 rows: the 128 x 128 LDS tiles, codes staged 32
+    rows x 64 k per 1 KiB block, block scales in LDS) and 10 at hidden 1024 / ffn 4608 (160 rows:
+    the 256 x 128 tile for gate/up, whose four code blocks come from waves 0-3, and the 256 x 256
+    lm_head tile).  Ragged contexts, then a draft against the oracle run with the dequantised
+    matrices, top-16 with and without full logits; NULL restores bf16."""
     cfg = MID_WIDE_MLP if wide else MID
     case = H.Case(cfg, max_seqs=n_seq, max_batch=n_seq, max_inject_rows=128)
     seq_ids = list(range(n_seq))

@@ -590,10 +590,10 @@ def test_b1_k16_per_channel_conv(H, big):
 
 
 def test_b32_k8_mxfp4_lm_head_and_mlp(H, big):
-    """Batch 32, K=8 (256 draft rows) with MXFP4 codes for the lm_head and every layer's MLP: these
-    run on the skinny kernels (row tiles of 64; the SwiGLU epilogue inside the gate/up GEMM), the
-    other GEMMs on the bf16 tiles; codes and block scales checked against the oracle's; drafts of
-    sampled sequences against the oracle run with the dequantised matrices."""
+    """Batch 32, K=8 (256 draft rows) with MXFP4 codes for the lm_head and every layer's MLP, on the
+    LDS tile kernels (the 256 x 256 lm_head tile, the 256 x 128 gate/up tile, the 128 x 128 down
+    tile with 8 k-splits); codes and block scales checked against the oracle's; drafts of sampled
+    sequences against the oracle run with the dequantised matrices."""
     import copy
     import torch
     cfg = synth.WORKLOADS["b32_k8_conv"]
