@@ -320,7 +320,7 @@ def algorithmic(cfg, tau_mean, n_ctx):
 
 
 def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=False, fp8_mlp=False,
-                 fp8_attn_inject=False, mxfp4_lm_head=False, mxfp4_mlp=False):
+                 fp8_attn_inject=False, mxfp4_lm_head=False, mxfp4_mlp=False, mxfp4_attn_inject=False):
     """Times `steps` steps twice on one stream: (1) replays of a HIP graph holding
     `graph_steps` steps (the headline rate; no events inside the graph), (2) the same number of
     steps launched eagerly, each lm_head launch bracketed by HIP events on that stream (the
@@ -376,6 +376,23 @@ def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=
             cyc.attn8.append((q8, o8))
         cyc.inj8 = (codes_of([cyc.w["fc"]]), codes_of([t for lw in cyc.w["layers"] for t in (lw["wk"], lw["wv"])]))
         cyc.d.dflash_set_inject_fp8(*cyc.inj8[0], *cyc.inj8[1])
+        torch.cuda.synchronize()
+
+    def codes4_of(mats):
+        m = torch.cat(mats).contiguous()
+        r, c = m.shape
+        q = (torch.empty((r, c // 2), dtype=torch.uint8, device="cuda"),
+             torch.empty((r, c // 32), dtype=torch.uint8, device="cuda"))
+        cyc.Bd.dflash_quantize_mxfp4_rows(m, *q)
+        return q
+    if mxfp4_attn_inject:   # the same matrices as MXFP4 codes + block scale bytes
+        cyc.attn4 = []
+        for l, lw in enumerate(cyc.w["layers"]):
+            q4, o4 = codes4_of([lw["wq"], lw["wk"], lw["wv"]]), codes4_of([lw["wo"]])
+            cyc.d.dflash_set_attn_mxfp4(l, *q4, *o4)
+            cyc.attn4.append((q4, o4))
+        cyc.inj4 = (codes4_of([cyc.w["fc"]]), codes4_of([t for lw in cyc.w["layers"] for t in (lw["wk"], lw["wv"])]))
+        cyc.d.dflash_set_inject_mxfp4(*cyc.inj4[0], *cyc.inj4[1])
         torch.cuda.synchronize()
     stream = torch.cuda.Stream()
     G = max(1, min(graph_steps, steps))
@@ -784,6 +801,16 @@ def main():
                 "blocks_per_s": round(r13["blocks_per_s"], 1), "draft_tokens_per_s": round(r13["draft_tokens_per_s"], 1),
                 "ms_per_step": round(r13["ms_per_step"], 4)}
             del r13["cycle"]
+            _release(torch)
+            torch.cuda.empty_cache()
+            r14 = run_workload(cfg, args.steps, args.warmup, torch, mxfp4_lm_head=True, mxfp4_mlp=True,
+                               mxfp4_attn_inject=True)
+            out["mxfp4_all_gemms"] = {
+                "workload": "b1_k16 with every weight GEMM as MXFP4 (injection fc and K/V, QKV, O, gate/up, down, "
+                            "lm_head; weight-only, activations bf16)",
+                "blocks_per_s": round(r14["blocks_per_s"], 1), "draft_tokens_per_s": round(r14["draft_tokens_per_s"], 1),
+                "ms_per_step": round(r14["ms_per_step"], 4)}
+            del r14["cycle"]
     batched = [("b32", "b32_k8_conv", args.no_b32,
                 "b32_k8_conv: same drafter, K=8, batch 32, contexts U[512,4096] (window 1024), two-tap conv, "
                 "0.7 match rule"),
@@ -819,12 +846,12 @@ def main():
         _release(torch)
         torch.cuda.empty_cache()
         rb = run_workload(synth.WORKLOADS["b32_k8_conv"], args.steps, args.warmup, torch, mxfp4_lm_head=True,
-                          mxfp4_mlp=True)
-        out["b32_mxfp4_lm_head_mlp"] = {
-            "workload": "b32_k8_conv with MXFP4 codes (32-weight blocks, E8M0 scales) for the lm_head and every "
-                        "layer's MLP (weight-only; activations bf16): above 16 rows these run on the skinny "
-                        "kernels (codes streamed into registers over row tiles of 64 rows), the other GEMMs on the "
-                        "bf16 tiles",
+                          mxfp4_mlp=True, mxfp4_attn_inject=True)
+        out["b32_mxfp4_all_gemms"] = {
+            "workload": "b32_k8_conv with MXFP4 codes (32-weight blocks, E8M0 scales) for every weight GEMM of the "
+                        "cycle: injection fc and K/V, QKV, O, gate/up, down, lm_head (weight-only; activations bf16; "
+                        "the LDS tile kernels stage 32 rows x 64 k of codes per 1 KiB block and the block scales "
+                        "in LDS)",
             "blocks_per_s": round(rb["blocks_per_s"], 1), "draft_tokens_per_s": round(rb["draft_tokens_per_s"], 1),
             "ms_per_step": round(rb["ms_per_step"], 4), "lm_head_avg_ms": round(rb["lm_head_ms"], 5)}
         del rb["cycle"]

@@ -92,6 +92,8 @@ def lib():
         "dflash_set_mlp_mxfp4": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_set_attn_fp8": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_set_inject_fp8": (c_int32, [H, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "dflash_set_attn_mxfp4": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "dflash_set_inject_mxfp4": (c_int32, [H, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_timing_enable": (c_int32, [H, c_int32]),
         "dflash_timing_read": (c_int32, [H, POINTER(c_double), POINTER(c_int32)]),
         "dflash_get_device_error": (c_int32, [H, POINTER(c_int32)]),
@@ -111,7 +113,8 @@ EXPORTED = ("dflash_config_check", "dflash_kv_cache_bytes", "dflash_kv_cache_lay
             "dflash_draft_block_static", "dflash_select_path", "dflash_select_sample", "dflash_verify_rejection", "dflash_verify_greedy",
             "dflash_synth_target_argmax", "dflash_quantize_fp8_rows", "dflash_set_lm_head_fp8", "dflash_set_mlp_fp8",
             "dflash_quantize_mxfp4_rows", "dflash_set_lm_head_mxfp4", "dflash_set_mlp_mxfp4",
-            "dflash_set_attn_fp8", "dflash_set_inject_fp8", "dflash_timing_enable",
+            "dflash_set_attn_fp8", "dflash_set_inject_fp8", "dflash_set_attn_mxfp4", "dflash_set_inject_mxfp4",
+            "dflash_timing_enable",
             "dflash_timing_read", "dflash_get_device_error", "dflash_status_string", "dflash_last_error")
 
 
@@ -280,6 +283,20 @@ class Drafter:
         self._inj_fp8 = (fc_codes, fc_scales, kv_codes, kv_scales)   # keep alive
         check("dflash_set_inject_fp8", lib().dflash_set_inject_fp8(self.h, ptr(fc_codes), ptr(fc_scales),
                                                                    ptr(kv_codes), ptr(kv_scales)))
+
+    def dflash_set_attn_mxfp4(self, layer, qkv_codes, qkv_scales, o_codes, o_scales):
+        """Use MXFP4 codes and block scale bytes for layer's stacked [wq; wk; wv] and wo (all None: bf16)."""
+        if not hasattr(self, "_attn_fp8"):
+            self._attn_fp8 = {}
+        self._attn_fp8[layer] = (qkv_codes, qkv_scales, o_codes, o_scales)   # keep alive
+        check("dflash_set_attn_mxfp4", lib().dflash_set_attn_mxfp4(self.h, layer, ptr(qkv_codes), ptr(qkv_scales),
+                                                                   ptr(o_codes), ptr(o_scales)))
+
+    def dflash_set_inject_mxfp4(self, fc_codes, fc_scales, kv_codes, kv_scales):
+        """Use MXFP4 codes and block scale bytes for W_fc and the stacked per-layer [wk; wv] (all None: bf16)."""
+        self._inj_fp8 = (fc_codes, fc_scales, kv_codes, kv_scales)   # keep alive
+        check("dflash_set_inject_mxfp4", lib().dflash_set_inject_mxfp4(self.h, ptr(fc_codes), ptr(fc_scales),
+                                                                       ptr(kv_codes), ptr(kv_scales)))
 
     def close(self):
         if self.h:

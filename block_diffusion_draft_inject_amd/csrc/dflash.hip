@@ -76,13 +76,15 @@ struct Handle {
     const unsigned char *gu_b, *dn_b;
   };
   std::vector<QuantMlp> mlp_q;
-  struct Fp8Attn {                   // per layer: E4M3 [wq; wk; wv] [qw + 2 kvw][d] and wo [d][qw] codes
-    const unsigned char *qkv, *o;
+  struct QuantAttn {                 // per layer: quantised [wq; wk; wv] (qw + 2 kvw rows) and wo (d rows):
+    const unsigned char *qkv, *o;      // codes; E4M3 with row scales, or MXFP4 with block scale bytes
     const float *qkv_s, *o_s;
+    const unsigned char *qkv_b, *o_b;
   };
-  std::vector<Fp8Attn> attn_fp8;
+  std::vector<QuantAttn> attn_q;
   const unsigned char *inj_fc8, *inj_kv8;   // injection: fc [d][concat], K/V stack [L (wk, wv)][d] codes
-  const float *inj_fc8_s, *inj_kv8_s;
+  const float *inj_fc8_s, *inj_kv8_s;       // E4M3 row scales, or
+  const unsigned char *inj_fc_b, *inj_kv_b; // MXFP4 block scale bytes
   std::vector<const void*> layers;   // n_layers * DFLASH_LAYER_TENSORS
   int max_seqs, max_batch, max_inject_rows;
   char* kv;
@@ -425,14 +427,16 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
     gq.seg[G + 1] = LW(H, l, DFLASH_L_WV);
     gq.seg_rows = kvw;
     gq.part = part;
-    const Handle::Fp8Attn* a8 = (size_t)l < H->attn_fp8.size() && H->attn_fp8[l].qkv ? &H->attn_fp8[l] : nullptr;
-    if (a8) {   // one stacked [wq; wk; wv] segment of E4M3 codes
+    const Handle::QuantAttn* a8 = (size_t)l < H->attn_q.size() && H->attn_q[l].qkv ? &H->attn_q[l] : nullptr;
+    const int awf = a8 ? (a8->qkv_b ? 2 : 1) : 0;
+    if (a8) {   // one stacked [wq; wk; wv] segment of E4M3 or MXFP4 codes
       gq.seg[0] = a8->qkv;
       gq.seg_rows = qw + 2 * kvw;
-      gq.ldb = d;
+      gq.ldb = awf == 2 ? d / 2 : d;
       gq.row_scale = a8->qkv_s;
+      gq.blk_scale = a8->qkv_b;
     }
-    GemmPlan pq = gemm_plan(b, GEMM_PARTIAL, M, qw + 2 * kvw, d);
+    GemmPlan pq = gemm_plan_wf(b, GEMM_PARTIAL, M, qw + 2 * kvw, d, awf);
     HIP_TRY(gemm_launch(b, pq, GEMM_PARTIAL, gq, st));
     QkvArgs qa{};
     qa.K = K;
@@ -484,10 +488,11 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
     go.part = part;
     if (a8) {
       go.seg[0] = a8->o;
-      go.ldb = qw;
+      go.ldb = awf == 2 ? qw / 2 : qw;
       go.row_scale = a8->o_s;
+      go.blk_scale = a8->o_b;
     }
-    GemmPlan po = gemm_plan(b, GEMM_PARTIAL, M, d, qw);
+    GemmPlan po = gemm_plan_wf(b, GEMM_PARTIAL, M, d, qw, awf);
     HIP_TRY(gemm_launch(b, po, GEMM_PARTIAL, go, st));
     RowArgs rp = ra;
     rp.h_in = hA;
@@ -796,12 +801,14 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
     g1.seg[0] = H->g_fc;
     g1.seg_rows = d;
     g1.part = part;
+    const int iwf = H->inj_fc8 ? (H->inj_fc_b ? 2 : 1) : 0;
     if (H->inj_fc8) {
       g1.seg[0] = H->inj_fc8;
-      g1.ldb = concat;
+      g1.ldb = iwf == 2 ? concat / 2 : concat;
       g1.row_scale = H->inj_fc8_s;
+      g1.blk_scale = H->inj_fc_b;
     }
-    GemmPlan p1 = gemm_plan(b, GEMM_PARTIAL, rows, d, concat);
+    GemmPlan p1 = gemm_plan_wf(b, GEMM_PARTIAL, rows, d, concat, iwf);
     HIP_TRY(gemm_launch(b, p1, GEMM_PARTIAL, g1, st));
     const size_t c_plane = (size_t)H->max_inject_rows * d;
     ReduceArgs ra{rows, d, p1.splits, rows, c_plane, ia.total, (int)r0, part, H->ws + H->wl.cbuf};
@@ -820,10 +827,11 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
     if (H->inj_kv8) {   // the stacked codes in the same row order: layer l's wk rows, then its wv rows
       g2.seg[0] = H->inj_kv8;
       g2.seg_rows = Nkv;
-      g2.ldb = d;
+      g2.ldb = iwf == 2 ? d / 2 : d;
       g2.row_scale = H->inj_kv8_s;
+      g2.blk_scale = H->inj_kv_b;
     }
-    GemmPlan p2 = gemm_plan(b, GEMM_PARTIAL, rows, Nkv, d);
+    GemmPlan p2 = gemm_plan_wf(b, GEMM_PARTIAL, rows, Nkv, d, iwf);
     HIP_TRY(gemm_launch(b, p2, GEMM_PARTIAL, g2, st));
     KvPostArgs ka{};
     ka.N = Nkv;
@@ -1042,8 +1050,23 @@ dflash_status dflash_set_attn_fp8(dflash_handle* h, int32_t layer, const uint8_t
   const int set = !!qkv_codes + !!qkv_scales + !!o_codes + !!o_scales;
   if (set != 0 && set != 4) return fail(DFLASH_E_INVALID, "all four pointers set, or all NULL");
   if (set && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "FP8 weights are for bf16 drafters");
-  if (H->attn_fp8.size() < (size_t)H->cfg.n_layers) H->attn_fp8.resize(H->cfg.n_layers, Handle::Fp8Attn{});
-  H->attn_fp8[layer] = Handle::Fp8Attn{qkv_codes, o_codes, qkv_scales, o_scales};
+  if (H->attn_q.size() < (size_t)H->cfg.n_layers) H->attn_q.resize(H->cfg.n_layers, Handle::QuantAttn{});
+  H->attn_q[layer] = Handle::QuantAttn{qkv_codes, o_codes, qkv_scales, o_scales, nullptr, nullptr};
+  return DFLASH_OK;
+}
+
+dflash_status dflash_set_attn_mxfp4(dflash_handle* h, int32_t layer, const uint8_t* qkv_codes, const uint8_t* qkv_scales,
+                                    const uint8_t* o_codes, const uint8_t* o_scales) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  if (layer < 0 || layer >= H->cfg.n_layers) return fail(DFLASH_E_INVALID, "layer %d outside [0, n_layers)", layer);
+  const int set = !!qkv_codes + !!qkv_scales + !!o_codes + !!o_scales;
+  if (set != 0 && set != 4) return fail(DFLASH_E_INVALID, "all four pointers set, or all NULL");
+  if (set && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "MXFP4 weights are for bf16 drafters");
+  if (set && (H->cfg.hidden % 128 || (H->cfg.n_heads * H->cfg.head_dim) % 128))
+    return fail(DFLASH_E_UNSUPPORTED, "MXFP4 attention weights need hidden and n_heads*head_dim multiples of 128");
+  if (H->attn_q.size() < (size_t)H->cfg.n_layers) H->attn_q.resize(H->cfg.n_layers, Handle::QuantAttn{});
+  H->attn_q[layer] = Handle::QuantAttn{qkv_codes, o_codes, nullptr, nullptr, qkv_scales, o_scales};
   return DFLASH_OK;
 }
 
@@ -1058,6 +1081,24 @@ dflash_status dflash_set_inject_fp8(dflash_handle* h, const uint8_t* fc_codes, c
   H->inj_fc8_s = fc_scales;
   H->inj_kv8 = kv_codes;
   H->inj_kv8_s = kv_scales;
+  H->inj_fc_b = H->inj_kv_b = nullptr;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_set_inject_mxfp4(dflash_handle* h, const uint8_t* fc_codes, const uint8_t* fc_scales,
+                                      const uint8_t* kv_codes, const uint8_t* kv_scales) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  const int set = !!fc_codes + !!fc_scales + !!kv_codes + !!kv_scales;
+  if (set != 0 && set != 4) return fail(DFLASH_E_INVALID, "all four pointers set, or all NULL");
+  if (set && !bf(&H->cfg)) return fail(DFLASH_E_UNSUPPORTED, "MXFP4 weights are for bf16 drafters");
+  if (set && (H->cfg.hidden % 128 || (H->cfg.n_taps * H->cfg.target_hidden) % 128))
+    return fail(DFLASH_E_UNSUPPORTED, "MXFP4 injection weights need hidden and n_taps*target_hidden multiples of 128");
+  H->inj_fc8 = fc_codes;
+  H->inj_kv8 = kv_codes;
+  H->inj_fc8_s = H->inj_kv8_s = nullptr;
+  H->inj_fc_b = fc_scales;
+  H->inj_kv_b = kv_scales;
   return DFLASH_OK;
 }
 

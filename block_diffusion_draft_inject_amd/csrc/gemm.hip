@@ -1013,11 +1013,10 @@ GemmPlan gemm_plan_wf(bool bf16, int mode, int M, int N, int K, int wf) {
   GemmPlan pl = gemm_plan(bf16, mode, M, N, K);
   if (!bf16 || wf == 0) return pl;
   // which kernels take E4M3 (1) and MXFP4 (2) weights: the skinny, independent-wave and tile ones
-  // both (the MXFP4 tiles at most TILE4_MAX_STEPS k-steps a workgroup); the streaming ones both
-  // but in their top-16 form
-  const int tile_steps = 2 * ((K / 64 + pl.splits - 1) / pl.splits);
+  // both (the MXFP4 lm_head tiles at most TILE4_MAX_STEPS k-steps); the streaming ones both but in
+  // their top-16 form
   const bool takes = pl.kind == 0 || pl.kind == 4 || (pl.kind == 3 && mode != GEMM_TOPK) ||
-                     (pl.kind == 5 && (wf == 1 || tile_steps <= TILE4_MAX_STEPS));
+                     (pl.kind == 5 && (wf == 1 || mode != GEMM_TOPK || K / 32 <= TILE4_MAX_STEPS));
   return takes ? pl : gemm_plan_skinny(mode, M, N, K);
 }
 

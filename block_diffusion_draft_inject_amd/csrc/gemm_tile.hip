@@ -78,9 +78,8 @@ struct Tile8Cfg {
 // The two halves of a code row are swapped on bit 3 of the row, so that the 4-byte operand reads
 // of 16 rows x 4 lane groups fall in 64 distinct banks.  The block scales (one byte per row and
 // k-step: a block is 32 k) of the tile's columns sit in LDS as [step][column] bytes, staged for
-// the workgroup's whole k-range (at most SEG k-steps) before its k-loop; each operand word of
-// eight codes is widened with its block's scale (v_cvt_scalef32_pk_bf16_fp4, exact), so nothing
-// is scaled after the sum.
+// up to SEG k-steps before the k-loop over them; each operand word of eight codes is widened with
+// its block's scale (v_cvt_scalef32_pk_bf16_fp4, exact), so nothing is scaled after the sum.
 template <int BM, int BN, int WGM, int WGN, int NP, int PL = 2>
 struct Tile4Cfg {
   static constexpr int NW = WGM * WGN, NT = NW * 64;
@@ -93,7 +92,7 @@ struct Tile4Cfg {
   static constexpr bool CG = BC < NW;                     // code blocks issued by waves < BC only
   static constexpr int QA = PL * BA / NW, QC = CG ? 1 : BC / NW;
   static constexpr int D2 = 2 * QA + QC;
-  static constexpr int SEG = TILE4_MAX_STEPS;             // k-steps of block scales a workgroup stages
+  static constexpr int SEG = TILE4_MAX_STEPS;             // k-steps of block scales staged at once
   static constexpr int SCL = SEG * BN;                    // their bytes
   static constexpr int LDS = NP * PAIR + SCL;
   static constexpr int EPB = NP * PAIR;                   // bytes an epilogue may overlay
@@ -444,25 +443,31 @@ __device__ __forceinline__ void tile4_issue(const Tile4Src<T>& s, unsigned pb, i
 }
 
 // The block scales of columns [n0, n0 + BN) (clamped to ncap - 1) for k-steps [c, c + ns), ns <=
-// SEG, into scl[step][column] (every wave is done with the previous ones: the caller's barrier;
-// no LDS-DMA load is in flight, so the compiler's own waits for these loads are exact).
-template <class T>
+// SEG, into scl[step][column] (every wave is done with the previous ones: the caller's barrier).
+// The compiler counts only its own loads, so its wait for these also waits for any LDS-DMA load
+// issued before them; it never waits for fewer.
+template <class T, int BURST>
 __device__ __forceinline__ void tile4_scales(const GemmParams& p, unsigned char* scl, int n0, int ncap, int c, int ns) {
-  constexpr int PER = T::SEG * T::BNc / T::NT;     // bytes per thread, 8 loads in flight at a time
-  static_assert(PER % 8 == 0, "scale bytes per thread");
-  const int kb = p.K / 32;
-  const int col = threadIdx.x % T::BNc, st0 = threadIdx.x / T::BNc;
-  constexpr int SST = T::NT / T::BNc;              // steps apart of a thread's successive bytes
-  const unsigned char* src = p.blk_scale + (size_t)min(n0 + col, ncap - 1) * kb + c;
+  // TPC threads per column, each SPT consecutive steps; the two scale bytes of a pair of steps are
+  // one 2-byte load (c and K / 32 are even), BURST loads in flight at a time, only the bursts the
+  // segment reaches, each load clamped to the segment's last pair (the bytes past ns are not
+  // stored)
+  constexpr int TPC = T::NT / T::BNc, SPT = T::SEG / TPC;
+  static_assert(T::NT % T::BNc == 0 && SPT % 2 == 0 && (SPT / 2) % BURST == 0, "scale bytes per thread");
+  const int col = threadIdx.x % T::BNc, s0 = (threadIdx.x / T::BNc) * SPT;
+  const unsigned short* src = reinterpret_cast<const unsigned short*>(
+      p.blk_scale + (size_t)min(n0 + col, ncap - 1) * (p.K / 32) + c);
+  const int lastp = (ns - 1) / 2;
 #pragma unroll 1
-  for (int i0 = 0; i0 < PER; i0 += 8) {
-    unsigned char v[8];
+  for (int i0 = 0; i0 < SPT / 2 && s0 + 2 * i0 < ns; i0 += BURST) {
+    unsigned short v[BURST];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = src[min(st0 + (i0 + i) * SST, ns - 1)];
+    for (int i = 0; i < BURST; ++i) v[i] = src[min(s0 / 2 + i0 + i, lastp)];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int st = st0 + (i0 + i) * SST;
-      if (st < ns) scl[st * T::BNc + col] = v[i];
+    for (int i = 0; i < BURST; ++i) {
+      const int st = s0 + 2 * (i0 + i);
+      if (st < ns) scl[st * T::BNc + col] = (unsigned char)(v[i] & 0xFF);
+      if (st + 1 < ns) scl[(st + 1) * T::BNc + col] = (unsigned char)(v[i] >> 8);
     }
   }
 }
@@ -496,9 +501,12 @@ __device__ __forceinline__ void tile4_mma(const unsigned char* pair, int st, int
   }
 }
 
-// One output tile over the k-step pairs starting at step c0 (even), np pairs, 2 np <= SEG: the
-// block scales of those steps are staged first, then acc = the tile's sums.
-template <class T>
+// One output tile over the k-step pairs starting at step c0 (even), np pairs: acc = the tile's
+// sums.  The block scales of up to SEG k-steps are staged in LDS before the pairs that use them:
+// once, when 2 np <= SEG (the lm_head tiles require it), else per segment of SEG k-steps (SEGS:
+// the partial-sum tiles, whose registers leave room for the accumulators across the segment
+// loop; in the 256 x 256 lm_head tile the same loop spilled them).
+template <class T, bool SEGS>
 __device__ __forceinline__ void tile4_run(const GemmParams& p, unsigned char* smem, int m0, int n0, int Mv, int ncap,
                                           int c0, int np, f32x4 (&acc)[T::FM][T::FN]) {
   constexpr int NP = T::NPc;
@@ -506,32 +514,57 @@ __device__ __forceinline__ void tile4_run(const GemmParams& p, unsigned char* sm
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / T::WGNc, wn = wave % T::WGNc, li = lane & 15, kg = lane >> 4;
   unsigned char* scl = smem + NP * T::PAIR;
-  wait_barrier<0>();                               // every wave is done with the LDS of the last tile
-  tile4_scales<T>(p, scl, n0, ncap, c0, 2 * np);
-  Tile4Src<T> src;
-  tile4_src<T>(p, m0, n0, Mv, ncap, wave, lane, src);
   const unsigned lo = li * 64 + ((kg ^ tile_swz(li)) << 4);
   const unsigned sbase = lds_addr(smem);
-#pragma unroll
-  for (int q = 0; q + 1 < NP; ++q)
-    if (q < np) tile4_issue<T>(src, sbase + q * T::PAIR, wave, c0 + 2 * q);
-#pragma unroll
-  for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int cur = 0;   // buffer of pair j
-  for (int j = 0; j < np; ++j) {
-    // pair j has landed for every wave (later pairs may still be in flight), every wave is done
-    // with pair j - 1's buffer, and (first pass) the scales are in LDS
-    if (NP >= 3 && j + 1 < np) wait_barrier<T::D2>();
-    else wait_barrier<0>();
-    if (j + NP - 1 < np) {
-      const int nb = cur == 0 ? NP - 1 : cur - 1;
-      tile4_issue<T>(src, sbase + nb * T::PAIR, wave, c0 + 2 * (j + NP - 1));
+  // the pairs [g0, g0 + gn) of the range, their first NP - 1 already in flight and the scales of
+  // their steps staged
+  auto pairs = [&](const Tile4Src<T>& src, int g0, int gn) {
+    const int cg = c0 + 2 * g0;
+    int cur = 0;   // buffer of pair j
+    for (int j = 0; j < gn; ++j) {
+      // pair j has landed for every wave (later pairs may still be in flight), every wave is done
+      // with pair j - 1's buffer, and (first pass) the scales are in LDS
+      if (NP >= 3 && j + 1 < gn) wait_barrier<T::D2>();
+      else wait_barrier<0>();
+      if (j + NP - 1 < gn) {
+        const int nb = cur == 0 ? NP - 1 : cur - 1;
+        tile4_issue<T>(src, sbase + nb * T::PAIR, wave, cg + 2 * (j + NP - 1));
+      }
+      tile4_mma<T>(smem + cur * T::PAIR, 0, wm, wn, lo, li, kg, scl + (2 * j) * T::BNc, acc);
+      tile4_mma<T>(smem + cur * T::PAIR, 1, wm, wn, lo, li, kg, scl + (2 * j + 1) * T::BNc, acc);
+      cur = cur + 1 == NP ? 0 : cur + 1;
     }
-    tile4_mma<T>(smem + cur * T::PAIR, 0, wm, wn, lo, li, kg, scl + (2 * j) * T::BNc, acc);
-    tile4_mma<T>(smem + cur * T::PAIR, 1, wm, wn, lo, li, kg, scl + (2 * j + 1) * T::BNc, acc);
-    cur = cur + 1 == NP ? 0 : cur + 1;
+  };
+  // The first pairs' loads go out before the scales are staged, so both travel in one round trip
+  // (the compiler counts only its own loads: its wait for the scale loads also waits for the pairs
+  // issued before them, never for fewer).
+  Tile4Src<T> src;
+  tile4_src<T>(p, m0, n0, Mv, ncap, wave, lane, src);
+  if constexpr (!SEGS) {
+    wait_barrier<0>();                             // every wave is done with the LDS of the last tile
+#pragma unroll
+    for (int q = 0; q + 1 < NP; ++q)
+      if (q < np) tile4_issue<T>(src, sbase + q * T::PAIR, wave, c0 + 2 * q);
+    tile4_scales<T, 8>(p, scl, n0, ncap, c0, 2 * np);   // before the accumulators are live
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    pairs(src, 0, np);
+  } else {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g0 = 0; g0 < np; g0 += T::SEG / 2) {
+      const int gn = min(T::SEG / 2, np - g0);
+      wait_barrier<0>();                           // every wave is done with the previous segment
+#pragma unroll
+      for (int q = 0; q + 1 < NP; ++q)
+        if (q < gn) tile4_issue<T>(src, sbase + q * T::PAIR, wave, c0 + 2 * (g0 + q));
+      tile4_scales<T, T::SEG / (2 * (T::NT / T::BNc))>(p, scl, n0, ncap, c0 + 2 * g0, 2 * gn);
+      pairs(src, g0, gn);
+    }
   }
 }
 
@@ -563,7 +596,7 @@ __global__ __launch_bounds__(T::NT, OCC) void gemm_tile_partial(GemmParams p) {
     const int p0 = (int)((long)np * s / p.splits), p1 = (int)((long)np * (s + 1) / p.splits);
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) sc[j] = 1.f;
-    tile4_run<T>(p, smem, m0, n0, Mv, p.N, 2 * p0, p1 - p0, acc);
+    tile4_run<T, true>(p, smem, m0, n0, Mv, p.N, 2 * p0, p1 - p0, acc);
   } else {
     const int c0 = (int)((long)nk * s / p.splits), c1 = (int)((long)nk * (s + 1) / p.splits);
 #pragma unroll
@@ -642,7 +675,7 @@ __global__ __launch_bounds__(T::NT, OCC) void lmhead_topk_tile(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) acc[i][j] *= sc[j];
     } else if constexpr (T::WF == 2) {
-      tile4_run<T>(p, smem, m0, n0, Mv, cend, 0, nk / 2, acc);
+      tile4_run<T, false>(p, smem, m0, n0, Mv, cend, 0, nk / 2, acc);
     } else if constexpr (T::Sc == 4) {
       if (nk % 2 == 0) tile_run_pairs<T>(p, smem, m0, n0, Mv, cend, 0, nk, acc);
       else tile_run<T>(p, smem, m0, n0, Mv, cend, 0, nk, acc);
@@ -761,7 +794,7 @@ hipError_t tile_launch(const GemmPlan& pl, int mode, const GemmParams& p, hipStr
   if (p.K % MK) return hipErrorInvalidValue;
   if (p.blk_scale) {   // MXFP4 weights: one segment, whole pairs of k-steps, at most SEG k-steps a workgroup
     if (p.K % (2 * MK) || p.seg_rows < p.N || p.row_scale) return hipErrorInvalidValue;
-    if (2 * ((p.K / MK / 2 + pl.splits - 1) / pl.splits) > TILE4_MAX_STEPS) return hipErrorInvalidValue;
+    if (mode == GEMM_TOPK && p.K / MK > TILE4_MAX_STEPS) return hipErrorInvalidValue;
     if (mode == GEMM_TOPK) {
       if (pl.mt) {
         if (p.logits) hipLaunchKernelGGL((lmhead_topk_tile<TileBigHi4, 1, true>), pl.grid, dim3(TileBigHi4::NT), 0, st, p);

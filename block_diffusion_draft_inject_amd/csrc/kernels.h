@@ -118,7 +118,8 @@ size_t gemm_part_floats(const GemmPlan& pl, int mode, int M, int N);
 hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hipStream_t st);
 // Tiled MFMA kernels for more than 64 rows (pl.kind 5; pl.mt selects the tile shape).
 hipError_t tile_launch(const GemmPlan& pl, int mode, const GemmParams& p, hipStream_t st);
-// k-steps of 32 (2048 k) an MXFP4 tile workgroup takes at most (its block scales staged in LDS)
+// k-steps of 32 (2048 k) whose MXFP4 block scales a tile stages in LDS at once; the MXFP4 lm_head
+// tiles take at most this many (hidden <= 2048)
 constexpr int TILE4_MAX_STEPS = 64;
 
 }  // namespace dfl

@@ -346,6 +346,21 @@ DFLASH_API dflash_status dflash_set_attn_fp8(dflash_handle* h, int32_t layer, co
  * injection size, a prefill included. */
 DFLASH_API dflash_status dflash_set_inject_fp8(dflash_handle* h, const uint8_t* fc_codes, const float* fc_scales,
                                                const uint8_t* kv_codes, const float* kv_scales);
+/* MXFP4 forms of the last two (the 4-bit reading of the same passage; codes and block scale bytes
+ * as written by dflash_quantize_mxfp4_rows: qkv_codes [n_heads*head_dim + 2*n_kv_heads*head_dim][d/2]
+ * with qkv_scales [..][d/32], o_codes [d][n_heads*head_dim/2] with o_scales [d][n_heads*head_dim/32];
+ * fc_codes [d][n_taps*target_hidden/2] with fc_scales [d][n_taps*target_hidden/32], kv_codes
+ * [n_layers*2*n_kv_heads*head_dim][d/2] with kv_scales [..][d/32]).  Each replaces the FP8 weights
+ * of the same GEMMs and is replaced by them; all four NULL reverts to bf16.  Borrowed like the
+ * weights.  The widths these GEMMs read along k (hidden, n_heads*head_dim, n_taps*target_hidden)
+ * must be multiples of 128, else DFLASH_E_UNSUPPORTED.  Every batch and injection size: the
+ * streaming kernels at most 16 rows, the skinny ones 17..64, the LDS tile kernels above (their
+ * block scales staged in LDS 2048 k at a time). */
+DFLASH_API dflash_status dflash_set_attn_mxfp4(dflash_handle* h, int32_t layer, const uint8_t* qkv_codes,
+                                               const uint8_t* qkv_scales, const uint8_t* o_codes,
+                                               const uint8_t* o_scales);
+DFLASH_API dflash_status dflash_set_inject_mxfp4(dflash_handle* h, const uint8_t* fc_codes, const uint8_t* fc_scales,
+                                                 const uint8_t* kv_codes, const uint8_t* kv_scales);
 
 /* Benchmark workload helper, not part of the drafter: stands in for a target model's verify
  * pass.  For i = 1..K-1, g_{i-1} = d_i with probability match_prob, else a different token;

@@ -121,6 +121,13 @@ def test_create_validates_before_any_device_call():
     assert L.dflash_set_mlp_mxfp4(h, 9, None, None, None, None) == -1                  # no such layer
     assert L.dflash_set_mlp_mxfp4(h, 0, fake, fake, fake, fake) == -3                  # fp32 drafter
     assert L.dflash_set_mlp_mxfp4(h, 0, None, None, None, None) == 0
+    assert L.dflash_set_attn_mxfp4(h, 0, fake, fake, None, fake) == -1                 # three of four set
+    assert L.dflash_set_attn_mxfp4(h, -1, None, None, None, None) == -1                # no such layer
+    assert L.dflash_set_attn_mxfp4(h, 0, fake, fake, fake, fake) == -3                 # fp32 drafter
+    assert L.dflash_set_attn_mxfp4(h, 0, None, None, None, None) == 0
+    assert L.dflash_set_inject_mxfp4(h, fake, None, fake, fake) == -1
+    assert L.dflash_set_inject_mxfp4(h, fake, fake, fake, fake) == -3                  # fp32 drafter
+    assert L.dflash_set_inject_mxfp4(h, None, None, None, None) == 0
     assert L.dflash_destroy(h) == 0
 
 
@@ -146,3 +153,21 @@ def test_quantised_lm_head_row_limit_precedes_any_device_work():
     assert b"4096 draft rows" in L.dflash_last_error(), L.dflash_last_error()
     assert L.dflash_set_lm_head_mxfp4(h, None, None) == 0
     assert L.dflash_destroy(h) == 0
+
+
+def test_mxfp4_setters_check_the_k_widths():
+    """The MXFP4 attention and injection setters refuse, before anything is used, k widths that are
+    not multiples of 128 (the streaming kernels read MXFP4 codes 128 k at a time): a drafter whose
+    concatenated target width is 5 x 5184 = 25920 (a multiple of 64, as bf16 drafters need, but not
+    of 128); the same setters succeed at 5 x 5120."""
+    L = B.lib()
+    fake = 0x5000
+    for th, want in ((5184, -3), (5120, 0)):
+        cfg = synth.WORKLOADS["b1_k16"].replace(target_hidden=th, name=f"b1_k16_t{th}")
+        st, h, keep, kvb, wsb = _fake_handle(cfg)
+        assert st == 0, L.dflash_last_error()
+        assert L.dflash_set_inject_mxfp4(h, fake, fake, fake, fake) == want, L.dflash_last_error()
+        assert L.dflash_set_attn_mxfp4(h, 0, fake, fake, fake, fake) == 0
+        assert L.dflash_set_inject_mxfp4(h, None, None, None, None) == 0
+        assert L.dflash_set_attn_mxfp4(h, 0, None, None, None, None) == 0
+        assert L.dflash_destroy(h) == 0

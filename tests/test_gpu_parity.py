@@ -743,15 +743,50 @@ def test_two_batch_pipeline_two_streams(H):
     assert case.d.dflash_get_device_error() == 0
 
 
-def _mxfp4_drafter(case, mlp=True, lm_head=True):
-    """Quantises the MLP matrices of every layer (stacked [gate; up], down) and the lm_head to MXFP4
-    on the GPU, checks codes and block scales against the oracle's, installs them, and returns
-    float64 weights for the oracle with those matrices dequantised."""
+def _mxfp4_stacked(case, W, mats, names_rows):
+    """GPU MXFP4 codes and block scales of the row-stacked device matrices `mats`; each (layer or
+    None, name, rows) block checked against the oracle's of that matrix and replaced in W by its
+    dequantised form."""
+    import torch
+    codes, scales = _quantize_mxfp4_on_gpu(torch.cat(mats).contiguous() if len(mats) > 1 else mats[0])
+    for layer, name, rows in names_rows:
+        src = case.W64["layers"][layer][name] if layer is not None else case.W64[name]
+        oc, osc = O.quantize_mxfp4_rows(src)
+        assert np.array_equal(codes[rows].cpu().numpy(), oc), (layer, name)
+        assert np.array_equal(scales[rows].cpu().numpy(), osc), (layer, name)
+        if layer is not None:
+            W["layers"][layer][name] = O.dequantize_mxfp4_rows(oc, osc)
+        else:
+            W[name] = O.dequantize_mxfp4_rows(oc, osc)
+    return codes, scales
+
+
+def _mxfp4_drafter(case, mlp=True, lm_head=True, attn=False, inject=False):
+    """Quantises the MLP matrices of every layer (stacked [gate; up], down), the lm_head, and
+    optionally the attention projections (stacked [wq; wk; wv], wo) and the injection matrices (fc,
+    the stacked per-layer [wk; wv]) to MXFP4 on the GPU, checks codes and block scales against the
+    oracle's, installs them, and returns float64 weights for the oracle with those matrices
+    dequantised."""
     import copy
     import torch
     cfg = case.cfg
     W = copy.copy(case.W64)
     W["layers"] = [dict(lw) for lw in case.W64["layers"]]
+    qw, kvw = cfg.q_width, cfg.kv_width
+    if attn:
+        for l, lw in enumerate(case.dev_w["layers"]):
+            q4 = _mxfp4_stacked(case, W, [lw["wq"], lw["wk"], lw["wv"]],
+                                [(l, "wq", slice(0, qw)), (l, "wk", slice(qw, qw + kvw)), (l, "wv", slice(qw + kvw, None))])
+            o4 = _mxfp4_stacked(case, W, [lw["wo"]], [(l, "wo", slice(None))])
+            case.d.dflash_set_attn_mxfp4(l, *q4, *o4)
+    if inject:
+        fc4 = _mxfp4_stacked(case, W, [case.dev_w["fc"]], [(None, "fc", slice(None))])
+        mats, blocks = [], []
+        for l, lw in enumerate(case.dev_w["layers"]):
+            mats += [lw["wk"], lw["wv"]]
+            blocks += [(l, "wk", slice(2 * l * kvw, (2 * l + 1) * kvw)), (l, "wv", slice((2 * l + 1) * kvw, (2 * l + 2) * kvw))]
+        kv4 = _mxfp4_stacked(case, W, mats, blocks)
+        case.d.dflash_set_inject_mxfp4(*fc4, *kv4)
     if mlp:
         for l, lw in enumerate(case.dev_w["layers"]):
             gu, gus = _quantize_mxfp4_on_gpu(torch.cat([lw["w_gate"], lw["w_up"]]).contiguous())
@@ -802,3 +837,29 @@ def test_mxfp4_above_16_rows(H, wide, n_seq):
     res = case.draft(seq_ids, anchors, logits=True)
     err, _ = H.check_draft(case, seq_ids, anchors, res)
     assert err <= H.LOGIT_TOL["bf16"]
+
+
+@pytest.mark.parametrize("wide,n_seq", [(False, 1), (False, 2), (False, 5), (True, 10)],
+                         ids=["16_rows", "32_rows", "80_rows", "160_rows_wide"])
+def test_mxfp4_every_gemm(H, wide, n_seq):
+    """MXFP4 codes for every weight GEMM (injection fc and stacked K/V, QKV, O, gate/up, down,
+    lm_head): 16 draft rows (the streaming kernels and the independent-wave lm_head), 32 (skinny),
+    80 and 160 (LDS tiles; the 160-row case at hidden 1024 / ffn 4608).  Ragged contexts injected
+    with the bf16 weights, then one injection of up to 12 rows per sequence with the MXFP4 ones,
+    then a draft, against the oracle run with the same matrices (dequantised where MXFP4)."""
+    cfg = MID_WIDE_MLP if wide else MID
+    case = H.Case(cfg, max_seqs=n_seq, max_batch=n_seq, max_inject_rows=128)
+    seq_ids = list(range(n_seq))
+    rng = np.random.default_rng(90 + n_seq)
+    lens = [int(L) for L in rng.integers(20, 90, size=n_seq)]
+    _prefill(case, seq_ids, [(0, L) for L in lens])
+    W64 = case.W64
+    case.W64 = _mxfp4_drafter(case, mlp=True, lm_head=True, attn=True, inject=True)
+    try:
+        adds = [np.arange(L, L + int(a)) for L, a in zip(lens, rng.integers(1, 13, size=n_seq))]
+        case.inject(seq_ids, adds, start_pos=False)
+        anchors = rng.integers(0, cfg.vocab - 1, size=n_seq).tolist()
+        res = _check(H, case, seq_ids, anchors, mode_names=("viterbi",))
+        _same_topk_without_logits(case, seq_ids, anchors, res)
+    finally:
+        case.W64 = W64

@@ -589,20 +589,12 @@ def test_b1_k16_per_channel_conv(H, big):
     assert run.d.dflash_get_device_error() == 0
 
 
-def test_b32_k8_mxfp4_lm_head_and_mlp(H, big):
-    """Batch 32, K=8 (256 draft rows) with MXFP4 codes for the lm_head and every layer's MLP, on the
-    LDS tile kernels (the 256 x 256 lm_head tile, the 256 x 128 gate/up tile, the 128 x 128 down
-    tile with 8 k-splits); codes and block scales checked against the oracle's; drafts of sampled
-    sequences against the oracle run with the dequantised matrices."""
+def _mxfp4_weights(big, cfg, run, attn=True, inject=True, mlp=True, lm_head=True):
+    """MXFP4 codes and block scales of the chosen weight groups, made on the GPU, checked against
+    the oracle's, installed on run's handle; returns (oracle weights with those matrices
+    dequantised, the device tensors to keep alive)."""
     import copy
     import torch
-    cfg = synth.WORKLOADS["b32_k8_conv"]
-    Ls = synth.context_lengths(cfg)
-    sampled = [int(np.argmin(Ls)), int(np.argmax(Ls)), 11]
-    run = Run(H, big, cfg, max_seqs=32, max_batch=32, max_inject_rows=4096, sampled=sampled)
-    ids = list(range(32))
-    run.d.dflash_reset_seqs(run.t(np.arange(32, dtype=np.int32)))
-    run.inject(ids, [_window(int(L), cfg.window) for L in Ls])
     W4 = copy.copy(big["W64"])
     W4["layers"] = [dict(lw) for lw in big["W64"]["layers"]]
     keep = []
@@ -625,15 +617,74 @@ def test_b32_k8_mxfp4_lm_head_and_mlp(H, big):
         keep.append((codes, scales))
         return codes, scales
 
-    ffn = cfg.ffn
+    qw, kvw, ffn = cfg.q_width, cfg.kv_width, cfg.ffn
     for l, lw in enumerate(big["dev"]["layers"]):
-        gu = q4(torch.cat([lw["w_gate"], lw["w_up"]]).contiguous(),
-                [("w_gate", slice(0, ffn)), ("w_up", slice(ffn, None))], l)
-        dn = q4(lw["w_down"], [("w_down", slice(None))], l)
-        run.d.dflash_set_mlp_mxfp4(l, *gu, *dn)
-    lm4 = q4(big["dev"]["lm_head"], [("lm_head", slice(None))], None)
-    run.d.dflash_set_lm_head_mxfp4(*lm4)
+        if attn:
+            q = q4(torch.cat([lw["wq"], lw["wk"], lw["wv"]]).contiguous(),
+                   [("wq", slice(0, qw)), ("wk", slice(qw, qw + kvw)), ("wv", slice(qw + kvw, None))], l)
+            o = q4(lw["wo"], [("wo", slice(None))], l)
+            run.d.dflash_set_attn_mxfp4(l, *q, *o)
+        if mlp:
+            gu = q4(torch.cat([lw["w_gate"], lw["w_up"]]).contiguous(),
+                    [("w_gate", slice(0, ffn)), ("w_up", slice(ffn, None))], l)
+            dn = q4(lw["w_down"], [("w_down", slice(None))], l)
+            run.d.dflash_set_mlp_mxfp4(l, *gu, *dn)
+    if inject:
+        fc = q4(big["dev"]["fc"], [("fc", slice(None))], None)
+        # the stacked injection K/V codes are the per-matrix ones (the quantiser works row by row)
+        kv = q4(torch.cat([t for lw in big["dev"]["layers"] for t in (lw["wk"], lw["wv"])]).contiguous(),
+                [], None)
+        run.d.dflash_set_inject_mxfp4(*fc, *kv)
+    if lm_head:
+        lm = q4(big["dev"]["lm_head"], [("lm_head", slice(None))], None)
+        run.d.dflash_set_lm_head_mxfp4(*lm)
+    return W4, keep
+
+
+def test_b1_k16_mxfp4_every_gemm(H, big):
+    """The b1_k16 drafter with MXFP4 codes for every weight GEMM: the 1024-row window injected
+    with them (W_fc of K = 25600 on the LDS tiles, its block scales staged 2048 k at a time, and the
+    stacked K/V), every layer's K/V against the oracle, then 5 more rows (the streaming kernels)
+    and a full-window draft (the streaming kernels and the independent-wave lm_head) against the
+    oracle run with the dequantised matrices."""
+    cfg = synth.WORKLOADS["b1_k16"]
+    run = Run(H, big, cfg, max_seqs=1, max_batch=1, max_inject_rows=1024, sampled=[0])
+    W4, keep = _mxfp4_weights(big, cfg, run)
     run.W64 = W4
+    run.d.dflash_reset_seqs(run.t(np.zeros(1, dtype=np.int32)))
+    run.inject([0], [_window(cfg.context[0], cfg.window)])
+    worst, same = H.check_kv(run, [0], max_positions=1024)
+    H.log(f"[b1_k16 mxfp4 injection] K/V of every layer: worst rel err {worst:.2e}, bit-equal {same:.4f}")
+    assert worst <= 1.0 and same >= 0.99
+    L = cfg.context[0]
+    run.inject([0], [np.arange(L, L + 5)], start=False)
+    anchors = synth.anchors(cfg).tolist()
+    res = run.draft([0], anchors)
+    run.own_logit_topk(res)
+    run.compare_sampled([0], anchors, res)
+    assert run.d.dflash_get_device_error() == 0
+
+
+def test_b32_k8_mxfp4_every_gemm(H, big):
+    """Batch 32, K=8 (256 draft rows) with MXFP4 codes for every weight GEMM, on the LDS tile
+    kernels (the 256 x 256 lm_head tile, the 256 x 128 QKV and gate/up tiles, the 128 x 128 O and
+    down tiles with 8 k-splits) and an injection of 4 new rows per sequence with them (128 rows,
+    W_fc with K = 25600 on the tiles); codes and block scales checked against the oracle's; K/V and
+    drafts of sampled sequences against the oracle run with the dequantised matrices (the
+    contexts injected before with the bf16 weights)."""
+    cfg = synth.WORKLOADS["b32_k8_conv"]
+    Ls = synth.context_lengths(cfg)
+    sampled = [int(np.argmin(Ls)), int(np.argmax(Ls)), 11]
+    run = Run(H, big, cfg, max_seqs=32, max_batch=32, max_inject_rows=4096, sampled=sampled)
+    ids = list(range(32))
+    run.d.dflash_reset_seqs(run.t(np.arange(32, dtype=np.int32)))
+    run.inject(ids, [_window(int(L), cfg.window) for L in Ls])
+    W4, keep = _mxfp4_weights(big, cfg, run)
+    run.W64 = W4
+    run.inject(ids, [np.arange(int(L), int(L) + 4) for L in Ls], start=False)
+    worst, same = H.check_kv(run, sampled, max_positions=64)
+    H.log(f"[b32_k8 mxfp4] K/V of sampled sequences: worst rel err {worst:.2e}, bit-equal {same:.4f}")
+    assert worst <= 1.0 and same >= 0.99
     anchors = synth.anchors(cfg).tolist()
     res = run.draft(ids, anchors)
     run.own_logit_topk(res)
