@@ -178,6 +178,8 @@ def run_pipeline(torch, wname="b32_k8_conv", reps=10, graph_steps=10):
     whole = BatchCycle(cfg, d_all, 0, n, torch, g)
     lo = BatchCycle(cfg, d_lo, 0, h, torch, g)
     hi = BatchCycle(cfg, d_hi, h, n - h, torch, g)
+    # the set-up above ran on the default stream; the side streams do not wait for it
+    torch.cuda.synchronize()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     with torch.cuda.stream(s1):
         for _ in range(2):
@@ -245,6 +247,7 @@ def run_overlap(torch, reps=10, graph_steps=10):
     sid = torch.tensor([1], dtype=torch.int32, device="cuda")
     nnew = torch.tensor([W], dtype=torch.int32, device="cuda")
     spos = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()   # the side streams below do not wait for the default stream's set-up
 
     def prefill(stream):   # restarts sequence 1 at position 0 every time: the same work each step
         dB.dflash_inject_kv(sid, nnew, W, pre, start_pos=spos, stream=stream)
@@ -394,6 +397,7 @@ def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=
         cyc.inj4 = (codes4_of([cyc.w["fc"]]), codes4_of([t for lw in cyc.w["layers"] for t in (lw["wk"], lw["wv"])]))
         cyc.d.dflash_set_inject_mxfp4(*cyc.inj4[0], *cyc.inj4[1])
         torch.cuda.synchronize()
+    torch.cuda.synchronize()   # weight codes were made on the default stream, which `stream` does not wait for
     stream = torch.cuda.Stream()
     G = max(1, min(graph_steps, steps))
     while steps % G:
