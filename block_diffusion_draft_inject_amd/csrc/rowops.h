@@ -142,6 +142,16 @@ struct AttnArgs {
   void* o;             // [rows][nh*dh]
 };
 
+// Row handled by workgroup b of a launch of n one-row workgroups.  A launch deals its workgroups
+// to the eight XCDs round-robin (workgroup b to XCD b mod 8); this gives each XCD one contiguous
+// range of rows (XCD x: rows x*q + min(x, r) onwards, q = n / 8, r = n mod 8), so that a row
+// reading its neighbours' inputs (the two-tap conv reads rows t-1 and t-2) finds them in the
+// L2 of its own XCD, where the neighbours' workgroups fetched them.  A bijection for every n.
+__device__ __forceinline__ int xcd_row(int b, int n) {
+  const int x = b & 7, q = n >> 3, r = n & 7;
+  return x * q + min(x, r) + (b >> 3);
+}
+
 // Hand-off from n workgroups to the one that arrives last at `counter` (device memory, zero
 // before the first of the n arrivals).  Returns true in every thread of that workgroup, which
 // then sees every global store the other n - 1 made before they arrived, and leaves the counter

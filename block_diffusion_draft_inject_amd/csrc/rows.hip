@@ -133,7 +133,7 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a
 template <typename T, int NV, int MS>
 __global__ __launch_bounds__(PP_T) void post_pre_kernel(RowArgs a) {
   __shared__ float red[8 * 4];
-  const int row = blockIdx.x, tid = threadIdx.x;
+  const int row = xcd_row(blockIdx.x, gridDim.x), tid = threadIdx.x;
   const int t = row % a.K;
   const int d = a.d;
   const bool conv = a.use_conv != 0;
@@ -335,7 +335,7 @@ __device__ __forceinline__ f32x4 sig4(f32x4 b, float c) {
 template <typename T, int NV>
 __global__ __launch_bounds__(PP_T) void post_pre_pc_kernel(PcArgs a) {
   __shared__ float red[(PP_T / 64) * 1];
-  const int row = blockIdx.x, tid = threadIdx.x, t = row % a.K, d = a.d;
+  const int row = xcd_row(blockIdx.x, gridDim.x), tid = threadIdx.x, t = row % a.K, d = a.d;
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 h[NV], xt[NV], xq[NV], b0[NV], b1[NV], g[NV];
   float c0[NV], c1[NV];
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(PP_T) void post_pre_pc_kernel(PcArgs a) {
 // Pre-conv: y_t = k_t0 (.) z_t + k_t1 (.) z_{t-1} (z = x, the normed rows) -> out (activation planes).
 template <typename T, int NV>
 __global__ __launch_bounds__(PP_T) void conv_apply_kernel(PcArgs a) {
-  const int row = blockIdx.x, tid = threadIdx.x, t = row % a.K, d = a.d;
+  const int row = xcd_row(blockIdx.x, gridDim.x), tid = threadIdx.x, t = row % a.K, d = a.d;
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 xt[NV], xq[NV], b0[NV], b1[NV];
   float c0[NV], c1[NV];
@@ -812,10 +812,14 @@ __device__ __forceinline__ void wave_best_dpp(float& v, int& id) {
 
 // List mode with at most 256 lists: thread t holds list t (sorted).  Each wave extracts its
 // own best 16 in 16 rounds of a wave-wide arg-best (the winning lane shifts its list by one),
-// the four wave results go through LDS, and wave 0 extracts the final 16 from those 64.
+// the four wave results go through LDS, and wave 0 places each of those 64 by its rank: lane
+// (l, i) holds entry i of wave l's sorted list, and its rank is i plus the entries of the
+// other three lists that beat it; ranks below 16 are the output slots.  (Ids are distinct, so
+// real candidates get distinct ranks; padding entries all equal (-inf, none) and those that
+// collide write the same value, covering every slot after the real ones.)
 __global__ __launch_bounds__(256) void topk_merge_lists_kernel(MergeArgs a) {
-  __shared__ float wv[4][TOPK];
-  __shared__ int wi[4][TOPK];
+  __shared__ __attribute__((aligned(16))) float wv[4][TOPK];
+  __shared__ __attribute__((aligned(16))) int wi[4][TOPK];
   const int orow = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = orow / (a.K - 1), t = orow % (a.K - 1) + 1;
   if (orow == 0 && tid < NCOUNTERS && a.counters) a.counters[tid] = 0;
@@ -853,21 +857,18 @@ __global__ __launch_bounds__(256) void topk_merge_lists_kernel(MergeArgs a) {
   }
   __syncthreads();
   if (w != 0) return;
-  float cv = wv[lane >> 4][lane & 15];
-  int ci = wi[lane >> 4][lane & 15];
-  float ov = NEG_INF;
-  int oi = ID_NONE;
-#pragma unroll 1
-  for (int r = 0; r < TOPK; ++r) {
-    float bv = cv;
-    int bi = ci;
-    wave_best_dpp(bv, bi);
-    if (lane == r) { ov = bv; oi = bi; }
-    if (ci == bi && cv == bv) { cv = NEG_INF; ci = ID_NONE; }
+  const int l = lane >> 4, i = lane & (TOPK - 1);
+  const float cv = wv[l][i];
+  const int ci = wi[l][i];
+  int rank = i;
+#pragma unroll
+  for (int o = 1; o < 4; ++o) {
+    const int l2 = (l + o) & 3;
+    rank += count_better(wv[l2], wi[l2], cv, ci);
   }
-  if (lane < TOPK) {
-    a.out_ids[(size_t)orow * TOPK + lane] = oi;
-    a.out_vals[(size_t)orow * TOPK + lane] = ov;
+  if (rank < TOPK) {
+    a.out_ids[(size_t)orow * TOPK + rank] = ci;
+    a.out_vals[(size_t)orow * TOPK + rank] = cv;
   }
 }
 
