@@ -492,6 +492,52 @@ __global__ __launch_bounds__(256) void swiglu_kernel(SwigluArgs a) {
   st_act(reinterpret_cast<T*>(a.out), m * a.f + j, a.out_plane, g / (1.f + __expf(-g)) * u);
 }
 
+// Four consecutive outputs of one row per thread (f a multiple of 4).  Every split's gate and up
+// vectors are requested before any is summed: the split index is clamped so that each load is
+// unconditional, and absent splits are masked afterwards (a load under a condition would be
+// waited for inside it).  The sums run in split order from zero, as in the one-element form, so
+// the results are the same bits; each plane takes one 8-byte (bf16) or 16-byte (fp32) store.
+__device__ __forceinline__ void st_act4(bf16* p, size_t i, size_t plane, const float (&v)[4]) {
+  unsigned hw[2], lw[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bf16 h0 = f2bf(v[2 * h]), h1 = f2bf(v[2 * h + 1]);
+    const bf16 l0 = f2bf(v[2 * h] - bf2f(h0)), l1 = f2bf(v[2 * h + 1] - bf2f(h1));
+    hw[h] = (unsigned)h0 | ((unsigned)h1 << 16);
+    lw[h] = (unsigned)l0 | ((unsigned)l1 << 16);
+  }
+  *reinterpret_cast<uint2*>(p + i) = make_uint2(hw[0], hw[1]);
+  *reinterpret_cast<uint2*>(p + i + plane) = make_uint2(lw[0], lw[1]);
+}
+__device__ __forceinline__ void st_act4(float* p, size_t i, size_t, const float (&v)[4]) {
+  *reinterpret_cast<f32x4*>(p + i) = f32x4{v[0], v[1], v[2], v[3]};
+}
+template <typename T, int MS>
+__global__ __launch_bounds__(256) void swiglu4_kernel(SwigluArgs a) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (size_t)a.M * a.f) return;
+  const size_t m = i / a.f, j = i % a.f;
+  f32x4 g[MS], u[MS];
+#pragma unroll
+  for (int sp = 0; sp < MS; ++sp) {
+    const float* pr = a.part + ((size_t)min(sp, a.splits - 1) * a.part_rows + m) * (2 * a.f) + j;
+    g[sp] = *reinterpret_cast<const f32x4*>(pr);
+    u[sp] = *reinterpret_cast<const f32x4*>(pr + a.f);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sp = 0; sp < MS; ++sp)
+    if (sp < a.splits) {
+      gs += g[sp];
+      us += u[sp];
+    }
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = gs[e] / (1.f + __expf(-gs[e])) * us[e];
+  st_act4(reinterpret_cast<T*>(a.out), m * a.f + j, a.out_plane, v);
+}
+
 // ------------------------------------------------------------------------ sum partials -> T
 template <typename T>
 __global__ __launch_bounds__(256) void reduce_store_kernel(ReduceArgs a) {
@@ -1024,9 +1070,23 @@ hipError_t launch_qkv_post(bool bf, const QkvArgs& a, int rows, hipStream_t st) 
   DFL_T_DISPATCH(bf, qkv_post_kernel, dim3(rows, a.nh + 2 * a.nkv), dim3(64), st, a);
   return hipGetLastError();
 }
+template <int MS>
+static void launch_swiglu4(bool bf, const SwigluArgs& a, hipStream_t st) {
+  const size_t n4 = (size_t)a.M * a.f / 4;
+  const dim3 grid((unsigned)((n4 + 255) / 256));
+  if (bf) hipLaunchKernelGGL((swiglu4_kernel<bf16, MS>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((swiglu4_kernel<float, MS>), grid, dim3(256), 0, st, a);
+}
 hipError_t launch_swiglu(bool bf, const SwigluArgs& a, hipStream_t st) {
   const size_t n = (size_t)a.M * a.f;
-  DFL_T_DISPATCH(bf, swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st, a);
+  if (a.splits < 1) return hipErrorInvalidValue;
+  // the four-wide form needs whole vectors of one row and 16-byte aligned partial rows; the
+  // output planes are then 8-byte aligned (plane = a multiple of f)
+  const bool v4 = a.f % 4 == 0 && a.out_plane % 4 == 0 && a.splits <= 8;
+  if (v4 && a.splits <= 2) launch_swiglu4<2>(bf, a, st);
+  else if (v4 && a.splits <= 4) launch_swiglu4<4>(bf, a, st);
+  else if (v4) launch_swiglu4<8>(bf, a, st);
+  else DFL_T_DISPATCH(bf, swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st, a);
   return hipGetLastError();
 }
 hipError_t launch_reduce_store(bool bf, const ReduceArgs& a, hipStream_t st) {
