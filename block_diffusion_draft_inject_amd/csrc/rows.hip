@@ -549,6 +549,26 @@ __global__ __launch_bounds__(256) void reduce_store_kernel(ReduceArgs a) {
   st_act(reinterpret_cast<T*>(a.out), i, a.out_plane, acc);
 }
 
+// Four consecutive outputs per thread (N a multiple of 4), the splits' loads unconditional and
+// requested before the sums, summed in split order from zero (the same bits as above).
+template <typename T, int MS>
+__global__ __launch_bounds__(256) void reduce_store4_kernel(ReduceArgs a) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int Mv = a.m_dev ? max(0, min(a.M, *a.m_dev - a.m_off)) : a.M;
+  if (i >= (size_t)Mv * a.N) return;
+  f32x4 p[MS];
+#pragma unroll
+  for (int sp = 0; sp < MS; ++sp)
+    p[sp] = *reinterpret_cast<const f32x4*>(a.part + (size_t)min(sp, a.splits - 1) * a.part_rows * a.N + i);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sp = 0; sp < MS; ++sp)
+    if (sp < a.splits) acc += p[sp];
+  const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+  st_act4(reinterpret_cast<T*>(a.out), i, a.out_plane, v);
+}
+
 // ------------------------------------------------------------------------ injection
 // One workgroup: per-sequence row offsets of this call (exclusive scan of the projected row
 // counts), and the sequences' length update.  Of n rows for one sequence only the last
@@ -1089,9 +1109,21 @@ hipError_t launch_swiglu(bool bf, const SwigluArgs& a, hipStream_t st) {
   else DFL_T_DISPATCH(bf, swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st, a);
   return hipGetLastError();
 }
+template <int MS>
+static void launch_reduce_store4(bool bf, const ReduceArgs& a, hipStream_t st) {
+  const size_t n4 = (size_t)a.M * a.N / 4;
+  const dim3 grid((unsigned)((n4 + 255) / 256));
+  if (bf) hipLaunchKernelGGL((reduce_store4_kernel<bf16, MS>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((reduce_store4_kernel<float, MS>), grid, dim3(256), 0, st, a);
+}
 hipError_t launch_reduce_store(bool bf, const ReduceArgs& a, hipStream_t st) {
   const size_t n = (size_t)a.M * a.N;
-  DFL_T_DISPATCH(bf, reduce_store_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st, a);
+  if (a.splits < 1) return hipErrorInvalidValue;
+  const bool v4 = a.N % 4 == 0 && a.out_plane % 4 == 0 && a.splits <= 8;
+  if (v4 && a.splits <= 2) launch_reduce_store4<2>(bf, a, st);
+  else if (v4 && a.splits <= 4) launch_reduce_store4<4>(bf, a, st);
+  else if (v4) launch_reduce_store4<8>(bf, a, st);
+  else DFL_T_DISPATCH(bf, reduce_store_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st, a);
   return hipGetLastError();
 }
 hipError_t launch_inject_plan(const InjectArgs& a, hipStream_t st) {
