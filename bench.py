@@ -323,12 +323,15 @@ def algorithmic(cfg, tau_mean, n_ctx):
 
 
 def run_workload(cfg, steps, warmup, torch, seed=0, graph_steps=10, fp8_lm_head=False, fp8_mlp=False,
-                 fp8_attn_inject=False, mxfp4_lm_head=False, mxfp4_mlp=False, mxfp4_attn_inject=False):
+                 fp8_attn_inject=False, mxfp4_lm_head=False, mxfp4_mlp=False, mxfp4_attn_inject=False,
+                 blocked_weights=False):
     """Times `steps` steps twice on one stream: (1) replays of a HIP graph holding
     `graph_steps` steps (the headline rate; no events inside the graph), (2) the same number of
     steps launched eagerly, each lm_head launch bracketed by HIP events on that stream (the
     kernel's duration; the eager step rate is reported too)."""
     cyc = Cycle(cfg, seed, torch, cfg.batch)
+    if blocked_weights:
+        set_blocked_weights(cyc, torch)
     if fp8_lm_head:   # E4M3 codes + per-row power-of-two scales of the lm_head, made on the device
         lm = cyc.w["lm_head"]
         cyc.lm8 = (torch.empty(lm.shape, dtype=torch.uint8, device="cuda"),
@@ -592,6 +595,23 @@ LM_KERNELS = {"b1_k16": LM_KERNEL,
               "b32_k8_conv": "lmhead_topk_tile<"}   # batch 32: 256 x 256 MFMA tiles
 
 
+BLOCKED_NAMES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
+def set_blocked_weights(cyc, torch):
+    """16-row-blocked copies (made on the device) of the lm_head, W_fc and every layer matrix,
+    registered with the cycle's handle: the batched GEMMs' MFMA tiles then read those (same results)."""
+    def blk(t):
+        out = torch.empty_like(t)
+        cyc.Bd.dflash_block_weights(t, out)
+        return out
+    w = cyc.w
+    cyc.blocked = {"lm_head": blk(w["lm_head"]), "fc": blk(w["fc"]),
+                   "layers": [{n: blk(lw[n]) for n in BLOCKED_NAMES} for lw in w["layers"]]}
+    cyc.d.dflash_set_blocked_weights(cyc.blocked)
+    torch.cuda.synchronize()
+
+
 def traffic_probe(steps, torch, workload="b1_k16"):
     """Workload for one rocprofv3 counter pass: `steps` eager cycles of the headline workload,
     then a plain elementwise copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES) three
@@ -599,6 +619,8 @@ def traffic_probe(steps, torch, workload="b1_k16"):
     from block_diffusion_draft_inject_amd import synth
     cfg = synth.WORKLOADS[workload]
     cyc = Cycle(cfg, 0, torch, cfg.batch)
+    if cfg.batch > 1:   # as the bench's batched legs run
+        set_blocked_weights(cyc, torch)
     raw = torch.cuda.current_stream().cuda_stream
     for _ in range(steps):
         cyc.step(raw)
@@ -824,14 +846,22 @@ def main():
                ("b64", "b64_k16_long", args.no_c5,
                 "b64_k16_long: same drafter, K=16, batch 64, context 32768 each (the last 1024 positions "
                 "injected and attended), 0.7 match rule")]
+    blk_note = ("; the bf16 weights also held as 16-row-blocked copies (dflash_set_blocked_weights) for the "
+                "MFMA tile GEMMs, which then read one contiguous KiB per weight load (same results)")
     for key, wname, skip, desc in batched:
         if skip:
             continue
         torch.cuda.empty_cache()
-        rb = run_workload(synth.WORKLOADS[wname], args.steps, args.warmup, torch)
-        out[key] = batched_record(wname, desc, rb)
+        rb = run_workload(synth.WORKLOADS[wname], args.steps, args.warmup, torch, blocked_weights=True)
+        out[key] = batched_record(wname, desc + blk_note, rb)
         del rb["cycle"]
         _release(torch)
+        if key == "b32":   # the same workload on the row-major weights alone
+            torch.cuda.empty_cache()
+            rr = run_workload(synth.WORKLOADS[wname], args.steps, args.warmup, torch)
+            out[key]["row_major_weights_ms_per_step"] = round(rr["ms_per_step"], 4)
+            del rr["cycle"]
+            _release(torch)
     if not args.no_b32 and not args.no_fp8:
         torch.cuda.empty_cache()
         rb = run_workload(synth.WORKLOADS["b32_k8_conv"], args.steps, args.warmup, torch, fp8_lm_head=True,

@@ -94,6 +94,8 @@ def lib():
         "dflash_set_inject_fp8": (c_int32, [H, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_set_attn_mxfp4": (c_int32, [H, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
         "dflash_set_inject_mxfp4": (c_int32, [H, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "dflash_block_weights": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_void_p]),
+        "dflash_set_blocked_weights": (c_int32, [H, POINTER(dflash_weights)]),
         "dflash_timing_enable": (c_int32, [H, c_int32]),
         "dflash_timing_read": (c_int32, [H, POINTER(c_double), POINTER(c_int32)]),
         "dflash_get_device_error": (c_int32, [H, POINTER(c_int32)]),
@@ -114,7 +116,7 @@ EXPORTED = ("dflash_config_check", "dflash_kv_cache_bytes", "dflash_kv_cache_lay
             "dflash_synth_target_argmax", "dflash_quantize_fp8_rows", "dflash_set_lm_head_fp8", "dflash_set_mlp_fp8",
             "dflash_quantize_mxfp4_rows", "dflash_set_lm_head_mxfp4", "dflash_set_mlp_mxfp4",
             "dflash_set_attn_fp8", "dflash_set_inject_fp8", "dflash_set_attn_mxfp4", "dflash_set_inject_mxfp4",
-            "dflash_timing_enable",
+            "dflash_block_weights", "dflash_set_blocked_weights", "dflash_timing_enable",
             "dflash_timing_read", "dflash_get_device_error", "dflash_status_string", "dflash_last_error")
 
 
@@ -175,6 +177,12 @@ def dflash_verify_rejection(n_seq, block_size, vocab, draft_ids, q_path, topk_id
     check("dflash_verify_rejection", lib().dflash_verify_rejection(
         n_seq, block_size, vocab, ptr(draft_ids), ptr(q_path), ptr(topk_ids), ptr(q_cand), ptr(target_probs),
         ptr(u_accept), ptr(u_resample), ptr(n_accepted), ptr(n_commit), ptr(committed), ptr(next_anchor), stream))
+
+
+def dflash_block_weights(src, dst, stream=None):
+    """16-row-blocked copy (same size, bf16) of a row-major bf16 matrix [rows][cols] into dst."""
+    rows, cols = src.shape
+    check("dflash_block_weights", lib().dflash_block_weights(ptr(src), rows, cols, ptr(dst), stream))
 
 
 def dflash_quantize_mxfp4_rows(src, codes, scales, stream=None):
@@ -291,6 +299,30 @@ class Drafter:
         self._attn_fp8[layer] = (qkv_codes, qkv_scales, o_codes, o_scales)   # keep alive
         check("dflash_set_attn_mxfp4", lib().dflash_set_attn_mxfp4(self.h, layer, ptr(qkv_codes), ptr(qkv_scales),
                                                                    ptr(o_codes), ptr(o_scales)))
+
+    def dflash_set_blocked_weights(self, blocked):
+        """Register blocked copies (dflash_block_weights) of the bf16 weight matrices: a dict with
+        optional "lm_head", "fc" and "layers" (one dict per layer with any of wq, wk, wv, wo, w_gate,
+        w_up, w_down); None removes them."""
+        if blocked is None:
+            self._blocked = None
+            check("dflash_set_blocked_weights", lib().dflash_set_blocked_weights(self.h, None))
+            return
+        bw = dflash_weights()
+        for name in ("lm_head", "fc"):
+            if blocked.get(name) is not None:
+                setattr(bw, name, blocked[name].data_ptr())
+        keep = [bw]
+        if blocked.get("layers") is not None:
+            if len(blocked["layers"]) != self.c.n_layers:
+                raise ValueError("blocked['layers'] needs one dict per layer")
+            flat = [(lw[n].data_ptr() if lw.get(n) is not None else None) for lw in blocked["layers"]
+                    for n in LAYER_TENSORS]
+            arr = (c_void_p * len(flat))(*flat)
+            bw.layers = ctypes.cast(arr, POINTER(c_void_p))
+            keep.append(arr)
+        self._blocked = (blocked, keep)   # keep alive
+        check("dflash_set_blocked_weights", lib().dflash_set_blocked_weights(self.h, ctypes.byref(bw)))
 
     def dflash_set_inject_mxfp4(self, fc_codes, fc_scales, kv_codes, kv_scales):
         """Use MXFP4 codes and block scale bytes for W_fc and the stacked per-layer [wk; wv] (all None: bf16)."""

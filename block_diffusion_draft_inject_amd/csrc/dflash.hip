@@ -86,6 +86,10 @@ struct Handle {
   const float *inj_fc8_s, *inj_kv8_s;       // E4M3 row scales, or
   const unsigned char *inj_fc_b, *inj_kv_b; // MXFP4 block scale bytes
   std::vector<const void*> layers;   // n_layers * DFLASH_LAYER_TENSORS
+  // 16-row-blocked copies of the bf16 weight matrices for the MFMA tiles (NULL: row-major only)
+  const void* blk_lm = nullptr;
+  const void* blk_fc = nullptr;
+  std::vector<const void*> blk_layers;   // empty, or n_layers * DFLASH_LAYER_TENSORS
   int max_seqs, max_batch, max_inject_rows;
   char* kv;
   dflash_kv_layout kvl;
@@ -295,6 +299,23 @@ template <typename P>
 P* wsp(char* ws, size_t off) { return reinterpret_cast<P*>(ws + off); }
 
 const void* LW(Handle* H, int l, int t) { return H->layers[(size_t)l * DFLASH_LAYER_TENSORS + t]; }
+const void* LWB(Handle* H, int l, int t) {
+  return H->blk_layers.empty() ? nullptr : H->blk_layers[(size_t)l * DFLASH_LAYER_TENSORS + t];
+}
+
+// Points a GEMM that runs on the bf16 MFMA tiles at the 16-row-blocked weight copies: segment i
+// moves from its matrix base[i] to the same byte offset in that matrix's copy blk[i] (a 16-row
+// group takes the same bytes in both forms).  Nothing changes unless the plan runs the bf16 tiles,
+// the segments hold whole 16-row groups and every segment's matrix has a copy.
+void use_blocked(GemmParams& g, const GemmPlan& pl, int nseg, const void* const* base, const void* const* blk) {
+  if (pl.kind != 5 || g.row_scale || g.blk_scale || g.seg_rows % 16 || g.ldb % 32) return;
+  for (int i = 0; i < nseg; ++i)
+    if (!blk[i]) return;
+  for (int i = 0; i < nseg; ++i)
+    g.seg[i] = reinterpret_cast<const char*>(blk[i]) +
+               (reinterpret_cast<const char*>(g.seg[i]) - reinterpret_cast<const char*>(base[i]));
+  g.b_blocked = 1;
+}
 
 int* seq_len(Handle* H) { return reinterpret_cast<int*>(H->kv + H->kvl.seq_len_offset); }
 int* seq_base(Handle* H) { return reinterpret_cast<int*>(H->kv + H->kvl.seq_base_offset); }
@@ -437,6 +458,13 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
       gq.blk_scale = a8->qkv_b;
     }
     GemmPlan pq = gemm_plan_wf(b, GEMM_PARTIAL, M, qw + 2 * kvw, d, awf);
+    if (!a8) {
+      const void *qb[MAX_SEG], *qk[MAX_SEG];
+      for (int i = 0; i < G; ++i) { qb[i] = LW(H, l, DFLASH_L_WQ); qk[i] = LWB(H, l, DFLASH_L_WQ); }
+      qb[G] = LW(H, l, DFLASH_L_WK); qk[G] = LWB(H, l, DFLASH_L_WK);
+      qb[G + 1] = LW(H, l, DFLASH_L_WV); qk[G + 1] = LWB(H, l, DFLASH_L_WV);
+      use_blocked(gq, pq, G + 2, qb, qk);
+    }
     HIP_TRY(gemm_launch(b, pq, GEMM_PARTIAL, gq, st));
     QkvArgs qa{};
     qa.K = K;
@@ -493,6 +521,10 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
       go.blk_scale = a8->o_b;
     }
     GemmPlan po = gemm_plan_wf(b, GEMM_PARTIAL, M, d, qw, awf);
+    if (!a8) {
+      const void *ob = LW(H, l, DFLASH_L_WO), *ok = LWB(H, l, DFLASH_L_WO);
+      use_blocked(go, po, 1, &ob, &ok);
+    }
     HIP_TRY(gemm_launch(b, po, GEMM_PARTIAL, go, st));
     RowArgs rp = ra;
     rp.h_in = hA;
@@ -541,6 +573,11 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
     } else {
       gg.half = 0;
       GemmPlan pg = gemm_plan_wf(b, GEMM_PARTIAL, M, 2 * c->ffn, d, mwf);
+      if (!mq) {
+        const void* gb[2] = {LW(H, l, DFLASH_L_W_GATE), LW(H, l, DFLASH_L_W_UP)};
+        const void* gk[2] = {LWB(H, l, DFLASH_L_W_GATE), LWB(H, l, DFLASH_L_W_UP)};
+        use_blocked(gg, pg, 2, gb, gk);
+      }
       HIP_TRY(gemm_launch(b, pg, GEMM_PARTIAL, gg, st));
       SwigluArgs sa{M, c->ffn, pg.splits, M, Mmax * c->ffn, part, act_s};
       HIP_TRY(launch_swiglu(b, sa, st));
@@ -558,6 +595,10 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
       gd.blk_scale = mq->dn_b;
     }
     GemmPlan pd = gemm_plan_wf(b, GEMM_PARTIAL, M, d, c->ffn, mwf);
+    if (!mq) {
+      const void *db = LW(H, l, DFLASH_L_W_DOWN), *dk = LWB(H, l, DFLASH_L_W_DOWN);
+      use_blocked(gd, pd, 1, &db, &dk);
+    }
     HIP_TRY(gemm_launch(b, pd, GEMM_PARTIAL, gd, st));
     RowArgs rm = ra;
     rm.h_in = hB;
@@ -622,6 +663,8 @@ dflash_status draft_impl(Handle* H, char* ws, const WsLayout& W, size_t Mmax, in
       gl.seg[0] = H->lm_fp8;
       gl.ldb = d;                     // bytes per weight row
       gl.row_scale = H->lm_fp8_scale;
+    } else {
+      use_blocked(gl, pl, 1, &H->g_lm, &H->blk_lm);
     }
     HIP_TRY(gemm_launch(b, pl, GEMM_TOPK, gl, st));
     if (ev1) HIP_TRY(hipEventRecord(ev1, st));
@@ -809,6 +852,7 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
       g1.blk_scale = H->inj_fc_b;
     }
     GemmPlan p1 = gemm_plan_wf(b, GEMM_PARTIAL, rows, d, concat, iwf);
+    if (!H->inj_fc8) use_blocked(g1, p1, 1, &H->g_fc, &H->blk_fc);
     HIP_TRY(gemm_launch(b, p1, GEMM_PARTIAL, g1, st));
     const size_t c_plane = (size_t)H->max_inject_rows * d;
     ReduceArgs ra{rows, d, p1.splits, rows, c_plane, ia.total, (int)r0, part, H->ws + H->wl.cbuf};
@@ -832,6 +876,14 @@ dflash_status dflash_inject_kv(dflash_handle* h, int32_t n_seq, const int32_t* s
       g2.blk_scale = H->inj_kv_b;
     }
     GemmPlan p2 = gemm_plan_wf(b, GEMM_PARTIAL, rows, Nkv, d, iwf);
+    if (!H->inj_kv8) {
+      const void *kb[MAX_SEG], *kk[MAX_SEG];
+      for (int l = 0; l < c->n_layers; ++l) {
+        kb[2 * l] = LW(H, l, DFLASH_L_WK); kk[2 * l] = LWB(H, l, DFLASH_L_WK);
+        kb[2 * l + 1] = LW(H, l, DFLASH_L_WV); kk[2 * l + 1] = LWB(H, l, DFLASH_L_WV);
+      }
+      use_blocked(g2, p2, 2 * c->n_layers, kb, kk);
+    }
     HIP_TRY(gemm_launch(b, p2, GEMM_PARTIAL, g2, st));
     KvPostArgs ka{};
     ka.N = Nkv;
@@ -980,6 +1032,48 @@ dflash_status dflash_quantize_fp8_rows(const void* src, int32_t rows, int32_t co
   if (rows < 0 || cols <= 0 || cols % 8) return fail(DFLASH_E_SHAPE, "rows must be >= 0 and cols a positive multiple of 8");
   if (rows > 0 && (!src || !codes || !row_scales)) return fail(DFLASH_E_INVALID, "NULL src, codes or row_scales");
   HIP_TRY(launch_quantize_fp8_rows(src, rows, cols, codes, row_scales, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_block_weights(const void* src, int64_t rows, int64_t cols, void* dst, void* stream) {
+  if (rows <= 0 || cols <= 0 || rows % 16 || cols % 32)
+    return fail(DFLASH_E_SHAPE, "rows must be a positive multiple of 16 and cols of 32");
+  if (!src || !dst) return fail(DFLASH_E_INVALID, "NULL src or dst");
+  if (src == dst) return fail(DFLASH_E_INVALID, "src and dst must not be the same buffer");
+  HIP_TRY(launch_block_weights(src, (long)rows, (long)cols, dst, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_set_blocked_weights(dflash_handle* h, const dflash_weights* blocked) {
+  Handle* H = as_handle(h);
+  if (!H) return fail(DFLASH_E_STATE, "not a live handle");
+  const dflash_config* c = &H->cfg;
+  if (!blocked) {
+    H->blk_lm = H->blk_fc = nullptr;
+    H->blk_layers.clear();
+    return DFLASH_OK;
+  }
+  if (!bf(c)) return fail(DFLASH_E_UNSUPPORTED, "blocked weights are for bf16 drafters");
+  const int d = c->hidden, qw = c->n_heads * c->head_dim, kvw = c->n_kv_heads * c->head_dim;
+  const int concat = c->n_taps * c->target_hidden;
+  // (rows, cols) of each matrix that may come blocked: rows a multiple of 16, cols of 32
+  auto shape_ok = [](const void* p, long rows, long cols) { return !p || (rows % 16 == 0 && cols % 32 == 0); };
+  if (!shape_ok(blocked->lm_head, c->vocab, d)) return fail(DFLASH_E_SHAPE, "a blocked lm_head needs vocab % 16 == 0");
+  if (!shape_ok(blocked->fc, d, concat)) return fail(DFLASH_E_SHAPE, "a blocked fc needs n_taps*target_hidden % 32 == 0");
+  std::vector<const void*> lay;
+  if (blocked->layers) {
+    lay.assign(blocked->layers, blocked->layers + (size_t)c->n_layers * DFLASH_LAYER_TENSORS);
+    for (int l = 0; l < c->n_layers; ++l) {
+      const void* const* t = &lay[(size_t)l * DFLASH_LAYER_TENSORS];
+      if (!shape_ok(t[DFLASH_L_WQ], qw, d) || !shape_ok(t[DFLASH_L_WK], kvw, d) || !shape_ok(t[DFLASH_L_WV], kvw, d) ||
+          !shape_ok(t[DFLASH_L_WO], d, qw) || !shape_ok(t[DFLASH_L_W_GATE], c->ffn, d) ||
+          !shape_ok(t[DFLASH_L_W_UP], c->ffn, d) || !shape_ok(t[DFLASH_L_W_DOWN], d, c->ffn))
+        return fail(DFLASH_E_SHAPE, "a blocked layer matrix needs rows % 16 == 0 and cols % 32 == 0");
+    }
+  }
+  H->blk_lm = blocked->lm_head;
+  H->blk_fc = blocked->fc;
+  H->blk_layers.swap(lay);
   return DFLASH_OK;
 }
 

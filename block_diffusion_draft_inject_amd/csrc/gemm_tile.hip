@@ -138,6 +138,7 @@ struct TileSrc {
   const char* base[T::D];
   unsigned voff[T::D];
   const char* addr[T::D];
+  unsigned bstep;   // bytes from one k-step's weight piece to the next
 };
 
 template <class T>
@@ -160,9 +161,32 @@ __device__ __forceinline__ void tile_src(const GemmParams& p, int m0, int n0, in
       s.voff[q] = (unsigned)(((size_t)r * p.lda + kc * 8) * 2);
     } else {                                       // weight rows
       const int n = min(n0 + (b - T::PLc * T::BA) * 16 + r16, ncap - 1);   // columns past ncap re-read the last
-      s.addr[q] = reinterpret_cast<const char*>(brow_ptr(p, n) + kc * 8);
+      if (p.b_blocked) {   // the lane's 16 bytes of its 16-row group's first block
+        const int sg = n / p.seg_rows, nr = n - sg * p.seg_rows;
+        s.addr[q] = reinterpret_cast<const char*>(p.seg[sg]) + (size_t)(nr >> 4) * (p.ldb / MK) * 1024 + lane * 16;
+      } else {
+        s.addr[q] = reinterpret_cast<const char*>(brow_ptr(p, n) + kc * 8);
+      }
     }
   }
+  s.bstep = p.b_blocked ? 1024u : (unsigned)(MK * 2);
+}
+
+// 16-row-blocked copy of a bf16 weight matrix [rows][cols] (rows a multiple of 16, cols of 32):
+// block (g, c) -- rows 16 g .. 16 g + 15, k = 32 c .. 32 c + 31 -- is 1 KiB at
+// dst + (g * cols / 32 + c) KiB, holding at byte 16 l the piece that lane l of a weight LDS-DMA
+// reads in the row-major form: row 16 g + l / 4, k = 32 c + 8 ((l mod 4) XOR swz(l / 4)) .. + 7.
+// A tile's weight DMA then reads one contiguous KiB per instruction, and a 16-row group's k-steps
+// follow each other; LDS receives the same bytes, so results are unchanged.  One thread per
+// 16-byte piece.
+__global__ __launch_bounds__(256) void block_weights_kernel(const bf16* src, long rows, long cols, bf16* dst) {
+  const long piece = (long)blockIdx.x * 256 + threadIdx.x;
+  if (piece >= rows * cols / 8) return;
+  const long blk = piece >> 6, steps = cols / MK;
+  const int l = (int)(piece & 63), r16 = l >> 2;
+  const long g = blk / steps, c = blk - g * steps;
+  const long r = 16 * g + r16, k = MK * c + 8 * ((l & 3) ^ tile_swz(r16));
+  *reinterpret_cast<u32x4*>(dst + piece * 8) = *reinterpret_cast<const u32x4*>(src + r * cols + k);
 }
 
 template <class T>
@@ -171,7 +195,7 @@ __device__ __forceinline__ void tile_issue(const TileSrc<T>& s, unsigned lds_sta
   for (int q = 0; q < T::D; ++q) {
     const unsigned lds = lds_stage + (T::NW * q + wave) * 1024;
     if (T::NW * q < T::PLc * T::BA) dma16(lds, s.voff[q], s.base[q] + (size_t)c * MK * 2);
-    else dma16v(lds, s.addr[q] + (size_t)c * MK * 2);
+    else dma16v(lds, s.addr[q] + (size_t)c * s.bstep);
   }
 }
 
@@ -252,8 +276,8 @@ __device__ __forceinline__ void tile_issue_pair(const TileSrc<T>& s, unsigned st
       dma16(la, s.voff[q], s.base[q] + (size_t)c * MK * 2);
       dma16(lb, s.voff[q], s.base[q] + (size_t)(c + 1) * MK * 2);
     } else {
-      dma16v(la, s.addr[q] + (size_t)c * MK * 2);
-      dma16v(lb, s.addr[q] + (size_t)(c + 1) * MK * 2);
+      dma16v(la, s.addr[q] + (size_t)c * s.bstep);
+      dma16v(lb, s.addr[q] + (size_t)(c + 1) * s.bstep);
     }
   }
 }
@@ -790,8 +814,19 @@ using TileTall4 = Tile4Cfg<256, 128, 4, 2, 2>;
 using TileSmallHi4 = Tile4Cfg<128, 128, 2, 2, 3, 1>;
 using TileBigHi4 = Tile4Cfg<256, 256, 4, 2, 3, 1>;
 
+hipError_t launch_block_weights(const void* src, long rows, long cols, void* dst, hipStream_t st) {
+  if (!src || !dst || rows <= 0 || cols <= 0 || rows % 16 || cols % MK) return hipErrorInvalidValue;
+  const long grid = (rows * cols / 8 + 255) / 256;
+  if (grid > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(block_weights_kernel, dim3((unsigned)grid), dim3(256), 0, st, reinterpret_cast<const bf16*>(src),
+                     rows, cols, reinterpret_cast<bf16*>(dst));
+  return hipGetLastError();
+}
+
 hipError_t tile_launch(const GemmPlan& pl, int mode, const GemmParams& p, hipStream_t st) {
   if (p.K % MK) return hipErrorInvalidValue;
+  // blocked bf16 weights: whole 16-row groups per segment and whole k-steps per row
+  if (p.b_blocked && (p.row_scale || p.blk_scale || p.seg_rows % 16 || p.ldb % MK)) return hipErrorInvalidValue;
   if (p.blk_scale) {   // MXFP4 weights: one segment, whole pairs of k-steps, at most SEG k-steps a workgroup
     if (p.K % (2 * MK) || p.seg_rows < p.N || p.row_scale) return hipErrorInvalidValue;
     if (mode == GEMM_TOPK && p.K / MK > TILE4_MAX_STEPS) return hipErrorInvalidValue;

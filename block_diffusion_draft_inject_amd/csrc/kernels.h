@@ -42,6 +42,8 @@ struct GemmParams {
   int* counter;           // TOPK skinny (17..64 rows): per-row-tile fragment counters, zero before the launch
   const unsigned char* blk_scale;  // MXFP4 lm_head (<= 16 rows): the weights are E2M1 codes [N][K/2 bytes], with
                                    // scale byte E [N][K/32] per 32 weights standing for 2^(E - 127)
+  int b_blocked;          // MFMA tiles with bf16 weights: seg[] point into 16-row-blocked copies
+                          // (block_weights_kernel), not row-major matrices
 };
 
 struct GemmPlan {
@@ -118,6 +120,9 @@ size_t gemm_part_floats(const GemmPlan& pl, int mode, int M, int N);
 hipError_t gemm_launch(bool bf16, const GemmPlan& pl, int mode, GemmParams p, hipStream_t st);
 // Tiled MFMA kernels for more than 64 rows (pl.kind 5; pl.mt selects the tile shape).
 hipError_t tile_launch(const GemmPlan& pl, int mode, const GemmParams& p, hipStream_t st);
+// 16-row-blocked copy of a bf16 [rows][cols] weight matrix for the MFMA tiles (rows % 16 == 0,
+// cols % 32 == 0), same size as the source
+hipError_t launch_block_weights(const void* src, long rows, long cols, void* dst, hipStream_t st);
 // k-steps of 32 (2048 k) whose MXFP4 block scales a tile stages in LDS at once; the MXFP4 lm_head
 // tiles take at most this many (hidden <= 2048)
 constexpr int TILE4_MAX_STEPS = 64;

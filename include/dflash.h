@@ -362,6 +362,31 @@ DFLASH_API dflash_status dflash_set_attn_mxfp4(dflash_handle* h, int32_t layer, 
 DFLASH_API dflash_status dflash_set_inject_mxfp4(dflash_handle* h, const uint8_t* fc_codes, const uint8_t* fc_scales,
                                                  const uint8_t* kv_codes, const uint8_t* kv_scales);
 
+/* A second layout of the bf16 weight matrices for the batched GEMMs (more than 64 rows), which run
+ * on MFMA tiles whose weight operand is loaded 16 rows x 32 k at a time.  The operations are the
+ * drafter's weight projections ("Architecture", kb.ekarisky.com, Component Breakdown); the layout
+ * is this library's own, for its tile loads, and changes no result.
+ *
+ * dflash_block_weights: writes dst, the blocked copy of src, a row-major bf16 [rows][cols] matrix
+ * (device pointers; dst is caller-owned, the same size as src and not overlapping it; rows a
+ * positive multiple of 16, cols of 32), enqueued on `stream`.  Block (g, c) -- rows 16 g .. 16 g +
+ * 15, k = 32 c .. 32 c + 31 -- is the KiB at byte offset (g * cols / 32 + c) * 1024 of dst; its
+ * 16 bytes at offset 16 l hold row r = 16 g + l / 4, k = 32 c + 8 ((l mod 4) XOR s) .. + 7, with
+ * s = ((l / 4) / 2 XOR (l / 4) / 8) mod 4.  A 16-row group therefore takes the same bytes in both
+ * forms.  Errors: DFLASH_E_SHAPE (rows or cols), DFLASH_E_INVALID (NULL or src == dst), DFLASH_E_HIP.
+ *
+ * dflash_set_blocked_weights: registers blocked copies of the handle's matrices, borrowed like the
+ * weights and holding the same values: blocked->lm_head [V][d], blocked->fc [d][n_taps *
+ * target_hidden] and, in blocked->layers (host array indexed like dflash_weights.layers), the
+ * entries DFLASH_L_WQ, WK, WV, WO, W_GATE, W_UP and W_DOWN; every other field and entry is ignored,
+ * and a NULL leaves that matrix row-major only.  A GEMM that runs on the bf16 tiles (not one whose
+ * weights are FP8 or MXFP4 codes) reads the copies when every matrix it spans has one; results are
+ * the same bits.  blocked == NULL removes them.  Errors: DFLASH_E_STATE, DFLASH_E_UNSUPPORTED (fp32
+ * drafter), DFLASH_E_SHAPE (a given matrix with rows not a multiple of 16 or cols of 32); on error
+ * nothing changes. */
+DFLASH_API dflash_status dflash_block_weights(const void* src, int64_t rows, int64_t cols, void* dst, void* stream);
+DFLASH_API dflash_status dflash_set_blocked_weights(dflash_handle* h, const dflash_weights* blocked);
+
 /* Benchmark workload helper, not part of the drafter: stands in for a target model's verify
  * pass.  For i = 1..K-1, g_{i-1} = d_i with probability match_prob, else a different token;
  * g_{K-1} is uniform.  match_prob = -1 instead draws the committed count tau uniform on {1..K}

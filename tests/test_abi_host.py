@@ -171,3 +171,54 @@ def test_mxfp4_setters_check_the_k_widths():
         assert L.dflash_set_inject_mxfp4(h, None, None, None, None) == 0
         assert L.dflash_set_attn_mxfp4(h, 0, None, None, None, None) == 0
         assert L.dflash_destroy(h) == 0
+
+
+def test_blocked_weight_entry_points_check_shapes_before_any_device_work():
+    """dflash_block_weights refuses, before launching anything, a row count that is not a multiple
+    of 16, a column count that is not a multiple of 32, NULL and src == dst.  dflash_set_blocked_weights
+    refuses an fp32 drafter and a blocked lm_head whose vocabulary is not a multiple of 16 (leaving the
+    handle as it was), takes NULL entries and clears with NULL."""
+    L = B.lib()
+    src, dst = 0x5000, 0x9000
+    assert L.dflash_block_weights(src, 15, 64, dst, None) == -2
+    assert L.dflash_block_weights(src, 16, 48, dst, None) == -2
+    assert L.dflash_block_weights(src, 0, 64, dst, None) == -2
+    assert L.dflash_block_weights(None, 16, 64, dst, None) == -1
+    assert L.dflash_block_weights(src, 16, 64, src, None) == -1
+
+    def table(cfg, lm=None, wq=None):
+        bw = B.dflash_weights()
+        bw.lm_head = lm
+        flat = (ctypes.c_void_p * (cfg.n_layers * len(B.LAYER_TENSORS)))()
+        if wq is not None:
+            for l in range(cfg.n_layers):
+                flat[l * len(B.LAYER_TENSORS) + B.LAYER_TENSORS.index("wq")] = wq
+        bw.layers = ctypes.cast(flat, ctypes.POINTER(ctypes.c_void_p))
+        return bw, flat
+
+    cfg = synth.WORKLOADS["b1_k16"]
+    st, h, keep, kvb, wsb = _fake_handle(cfg)
+    assert st == 0, L.dflash_last_error()
+    bw, flat = table(cfg, lm=0xA000, wq=0xB000)
+    assert L.dflash_set_blocked_weights(h, ctypes.byref(bw)) == 0, L.dflash_last_error()
+    bw, flat = table(cfg)          # every entry NULL: nothing blocked
+    assert L.dflash_set_blocked_weights(h, ctypes.byref(bw)) == 0
+    assert L.dflash_set_blocked_weights(h, None) == 0
+    assert L.dflash_destroy(h) == 0
+
+    ragged = cfg.replace(vocab=151930, mask_id=151929, name="b1_k16_v151930")
+    st, h, keep, kvb, wsb = _fake_handle(ragged)
+    assert st == 0, L.dflash_last_error()
+    bw, flat = table(ragged, lm=0xA000)
+    assert L.dflash_set_blocked_weights(h, ctypes.byref(bw)) == -2
+    assert b"16" in L.dflash_last_error()
+    bw, flat = table(ragged, wq=0xB000)   # the layer matrices can still be blocked
+    assert L.dflash_set_blocked_weights(h, ctypes.byref(bw)) == 0
+    assert L.dflash_destroy(h) == 0
+
+    st, h, keep, kvb, wsb = _fake_handle(synth.WORKLOADS["tiny_fp32"])
+    assert st == 0, L.dflash_last_error()
+    bw, flat = table(synth.WORKLOADS["tiny_fp32"], wq=0xB000)
+    assert L.dflash_set_blocked_weights(h, ctypes.byref(bw)) == -3
+    assert L.dflash_set_blocked_weights(h, None) == 0
+    assert L.dflash_destroy(h) == 0

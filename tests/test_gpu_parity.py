@@ -863,3 +863,75 @@ def test_mxfp4_every_gemm(H, wide, n_seq):
         _same_topk_without_logits(case, seq_ids, anchors, res)
     finally:
         case.W64 = W64
+
+
+def _blocked_copy(t):
+    import torch
+    out = torch.empty_like(t)
+    B.dflash_block_weights(t, out)
+    return out
+
+
+@pytest.mark.gpu
+def test_blocked_weights_layout_and_same_bits(H):
+    """(1) dflash_block_weights lays a bf16 [48][96] matrix out as the header defines it (the
+    definition written out here with NumPy).  (2) With blocked copies of the lm_head, W_fc and
+    every layer matrix registered, injections of 40..64 rows for 12 sequences (fc and the stacked
+    K/V on the MFMA tiles, passes of up to 200 rows) and a 192-row draft with full logits (QKV, O,
+    gate/up, down and the lm_head on the tiles) leave the same KV cache bytes and give the same
+    outputs, bit for bit, as the row-major weights.  (3) Registering the row-major matrices
+    themselves as the "blocked" copies changes the draft (same bytes, other order), so the
+    tiles did read the registered copies."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    src = torch.randn((48, 96), generator=g, device="cuda").to(torch.bfloat16)
+    dst = _blocked_copy(src)
+    torch.cuda.synchronize()
+    s = src.view(torch.int16).cpu().numpy()
+    got = dst.view(torch.int16).cpu().numpy().reshape(-1)
+    want = np.empty_like(got)
+    steps = s.shape[1] // 32
+    for grp in range(s.shape[0] // 16):
+        for c in range(steps):
+            for lane in range(64):
+                q = lane // 4
+                k = 32 * c + 8 * ((lane % 4) ^ (((q >> 1) ^ (q >> 3)) & 3))
+                off = ((grp * steps + c) * 64 + lane) * 8
+                want[off:off + 8] = s[16 * grp + q, k:k + 8]
+    assert np.array_equal(got, want)
+
+    cfg = MID.replace(n_heads=16, n_kv_heads=4, ffn=1536, name="mid_bf16_wide")
+    case = H.Case(cfg, max_seqs=12, max_batch=12, max_inject_rows=200)
+    ids = list(range(12))
+    lens = [40 + 2 * i for i in ids]
+    names = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+    blocked = {"lm_head": _blocked_copy(case.dev_w["lm_head"]), "fc": _blocked_copy(case.dev_w["fc"]),
+               "layers": [{n: _blocked_copy(lw[n]) for n in names} for lw in case.dev_w["layers"]]}
+    plain = {"lm_head": case.dev_w["lm_head"], "fc": case.dev_w["fc"],
+             "layers": [{n: lw[n] for n in names} for lw in case.dev_w["layers"]]}
+    case.reset(ids)
+    torch.cuda.synchronize()
+    snapshot = case.d.kv.clone()
+    ids_t = case.tensor(np.array(ids, np.int32))
+    anchors = case.tensor(np.array([17 + 600 * i for i in ids], np.int32))
+
+    def run():
+        case.d.kv.copy_(snapshot)
+        case.inject(ids, [np.arange(0, n) for n in lens])
+        out = case.d.outputs(12, logits=True)
+        case.d.dflash_draft_block(ids_t, anchors, out["topk_ids"], out["topk_logits"], out["h_final"], out["logits"])
+        torch.cuda.synchronize()
+        assert case.d.dflash_get_device_error() == 0
+        return {k: v.clone() for k, v in out.items() if v is not None}, case.d.kv.clone()
+
+    ref_out, ref_kv = run()
+    case.d.dflash_set_blocked_weights(blocked)
+    blk_out, blk_kv = run()
+    case.d.dflash_set_blocked_weights(plain)
+    wrong_out, _ = run()
+    case.d.dflash_set_blocked_weights(None)
+    assert torch.equal(ref_kv, blk_kv)
+    for k in ref_out:
+        assert torch.equal(ref_out[k], blk_out[k]), k
+    assert not torch.equal(ref_out["logits"], wrong_out["logits"])

@@ -223,6 +223,51 @@ def test_b32_k8_conv_ragged_contexts(H, big):
     assert run.d.dflash_get_device_error() == 0
 
 
+def test_b32_k8_blocked_weights_same_bits(H, big):
+    """b32_k8_conv at full size, as the bench's batched legs run it: with 16-row-blocked copies of
+    the lm_head, W_fc and every layer matrix registered, the window injection of the 32 sequences
+    (fc and the stacked K/V on the MFMA tiles) and the 224-row draft give the same KV cache bytes,
+    top-16 lists and h_final, bit for bit, as the row-major weights."""
+    import torch
+    cfg = synth.WORKLOADS["b32_k8_conv"]
+    Ls = synth.context_lengths(cfg)
+    run = Run(H, big, cfg, max_seqs=32, max_batch=32, max_inject_rows=4096, sampled=[0])
+    ids = list(range(32))
+    anchors = synth.anchors(cfg).tolist()
+    dev = big["dev"]
+
+    def blk(t):
+        out = torch.empty_like(t)
+        B.dflash_block_weights(t, out)
+        return out
+    names = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+    blocked = {"lm_head": blk(dev["lm_head"]), "fc": blk(dev["fc"]),
+               "layers": [{n: blk(lw[n]) for n in names} for lw in dev["layers"]]}
+
+    # one fixed set of target states for both cycles (the harness's inject draws new ones per call)
+    first = [max(0, int(L) - cfg.window) for L in Ls]
+    n_new = [int(L) - f for L, f in zip(Ls, first)]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(21)
+    states = torch.randn((32, max(n_new), cfg.concat_width), generator=g, device="cuda").to(torch.bfloat16)
+
+    def cycle():
+        run.d.dflash_reset_seqs(run.t(np.arange(32, dtype=np.int32)))
+        run.d.dflash_inject_kv(run.t(np.asarray(ids, dtype=np.int32)), run.t(np.asarray(n_new, dtype=np.int32)),
+                               max(n_new), states, start_pos=run.t(np.asarray(first, dtype=np.int32)))
+        res = run.draft(ids, anchors, logits=False)
+        return res, run.d.kv.clone()
+
+    ref, ref_kv = cycle()
+    run.d.dflash_set_blocked_weights(blocked)
+    got, got_kv = cycle()
+    run.d.dflash_set_blocked_weights(None)
+    assert run.d.dflash_get_device_error() == 0
+    assert torch.equal(ref_kv, got_kv)
+    for k in ("topk_ids", "topk_logits", "h_final"):
+        assert np.array_equal(ref[k], got[k]), k
+
+
 def test_b32_k16_incremental_64_cycles(H, big):
     """Batch 32, K=16, 2048-token prefixes, 64 cycles of draft -> select -> verify -> inject
     tau ~ U{1..16} new states into the ring; oracle comparison at cycles 0, 31 and 63."""
