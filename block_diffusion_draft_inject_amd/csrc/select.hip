@@ -661,18 +661,25 @@ __device__ __forceinline__ unsigned long long splitmix64(unsigned long long x) {
   return z ^ (z >> 31);
 }
 
+// One thread per (sequence b, slot j): slot j < K - 1 is target token i = j + 1, compared with
+// draft i; slot K - 1 is the token after the block.  Each slot's draws depend on (seed, counter,
+// b, i) alone, so the slots of a sequence are computed side by side.
 __global__ __launch_bounds__(1024) void synth_target_kernel(SynthArgs a) {
   __shared__ long long ctr;
-  const int b = threadIdx.x;
-  if (b == 0) ctr = *a.counter;
+  if (threadIdx.x == 0) ctr = *a.counter;
   __syncthreads();
-  if (b == 0) *a.counter = ctr + 1;
-  if (b >= a.n_seq) return;
+  if (threadIdx.x == 0) *a.counter = ctr + 1;
   const int K = a.K;
-  const unsigned long long key = a.seed ^ ((unsigned long long)ctr << 24) ^ ((unsigned long long)b << 8);
-  // p < 0: committed tokens tau uniform on {1..K} (drafts 1..tau-1 match, draft tau does not)
-  const int tau = a.p < 0.f ? 1 + (int)(splitmix64(key ^ 0xABCDull) % (unsigned long long)K) : K;
-  for (int i = 1; i < K; ++i) {
+  for (long t = threadIdx.x; t < (long)a.n_seq * K; t += blockDim.x) {
+    const int b = (int)(t / K), j = (int)(t - (long)b * K);
+    const unsigned long long key = a.seed ^ ((unsigned long long)ctr << 24) ^ ((unsigned long long)b << 8);
+    if (j == K - 1) {
+      a.target[(size_t)b * K + K - 1] = (int)(splitmix64(key ^ 0xFFFFull) % (unsigned long long)a.vocab);
+      continue;
+    }
+    const int i = j + 1;
+    // p < 0: committed tokens tau uniform on {1..K} (drafts 1..tau-1 match, draft tau does not)
+    const int tau = a.p < 0.f ? 1 + (int)(splitmix64(key ^ 0xABCDull) % (unsigned long long)K) : K;
     const unsigned long long h1 = splitmix64(key ^ (unsigned long long)(2 * i));
     const unsigned long long h2 = splitmix64(key ^ (unsigned long long)(2 * i + 1));
     const float u = (float)(h1 >> 40) * (1.0f / 16777216.0f);
@@ -681,7 +688,6 @@ __global__ __launch_bounds__(1024) void synth_target_kernel(SynthArgs a) {
     const bool match = a.p < 0.f ? i < tau : u < a.p;
     a.target[(size_t)b * K + i - 1] = match ? di : (int)(((long long)di + alt) % a.vocab);
   }
-  a.target[(size_t)b * K + K - 1] = (int)(splitmix64(key ^ 0xFFFFull) % (unsigned long long)a.vocab);
 }
 
 hipError_t launch_select(bool bf, const SelectArgs& a, int n_seq, hipStream_t st) {

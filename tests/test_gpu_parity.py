@@ -935,3 +935,44 @@ def test_blocked_weights_layout_and_same_bits(H):
     for k in ref_out:
         assert torch.equal(ref_out[k], blk_out[k]), k
     assert not torch.equal(ref_out["logits"], wrong_out["logits"])
+
+
+def _splitmix64(x):
+    """SplitMix64 (Steele, Lea and Flood; constants as published by Vigna), on Python integers."""
+    m = (1 << 64) - 1
+    z = (x + 0x9E3779B97F4A7C15) & m
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & m
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & m
+    return z ^ (z >> 31)
+
+
+@pytest.mark.parametrize("p", [0.7, -1.0])
+def test_synth_target_exact_draws(H, p):
+    """The stand-in target's tokens equal the rule written out from the generator's definition:
+    per (sequence b, token i) the key seed ^ (counter << 24) ^ (b << 8); draft i is kept when
+    u = (h1 >> 40) / 2^24 < p (h1 = splitmix64(key ^ 2i)), or, with p < 0, when i < tau =
+    1 + splitmix64(key ^ 0xABCD) mod K; else it becomes (draft + 1 + h2 mod (V - 1)) mod V
+    (h2 = splitmix64(key ^ (2i + 1))); the token after the block is splitmix64(key ^ 0xFFFF) mod V.
+    130 sequences x K = 8 is more slots than the kernel's 1024 threads."""
+    import torch
+    K, V, n, seed = 8, 1000, 130, 123
+    d = torch.randint(0, V, (n, K - 1), dtype=torch.int32, device="cuda")
+    ctr = torch.full((1,), 5, dtype=torch.int64, device="cuda")
+    tgt = torch.empty((n, K), dtype=torch.int32, device="cuda")
+    B.dflash_synth_target_argmax(n, K, V, d, p, seed, ctr, tgt)
+    torch.cuda.synchronize()
+    dn, got = d.cpu().numpy(), tgt.cpu().numpy()
+    want = np.empty_like(got)
+    pf = np.float32(p)
+    for b in range(n):
+        key = seed ^ (5 << 24) ^ (b << 8)
+        tau = 1 + _splitmix64(key ^ 0xABCD) % K
+        for i in range(1, K):
+            u = np.float32(_splitmix64(key ^ (2 * i)) >> 40) * np.float32(1.0 / 16777216.0)
+            alt = 1 + _splitmix64(key ^ (2 * i + 1)) % (V - 1)
+            match = (i < tau) if p < 0 else bool(u < pf)
+            di = int(dn[b, i - 1])
+            want[b, i - 1] = di if match else (di + alt) % V
+        want[b, K - 1] = _splitmix64(key ^ 0xFFFF) % V
+    assert np.array_equal(got, want)
+    assert ctr.item() == 6
